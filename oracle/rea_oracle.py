@@ -1,0 +1,297 @@
+"""Plain fp64 CPU oracle for the ReAttention hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The GPU library
+never calls it, and it shares no code, table or constant with the GPU path.
+
+What it computes, for one layer, one batch entry
+(q: [n_q][Hq][d] un-rotated queries; K, V: [Hkv][T][d] pre-RoPE cache whose
+last n_q rows belong to the queries themselves):
+
+  1. regions   global [0, G'), middle [G', T-L'), local [T-L', T), with
+               G' = min(G, T), L' = min(L, T-G')
+  2. spans     the middle cut into spans of S tokens from its start; the last
+               span may be shorter
+  3. scores    s[i,h,t] = sum_g q[i, h*g_sz+g] . K[h,t]  (no RoPE, no scale)
+  4. span      sigma_b[h,j] = sum over the block's queries i of
+     scores    max over span j's tokens t of s[i,h,t]
+  5. top-k     the min(k, n_spans) largest sigma, ties to the lower span
+               index, emitted in ascending span order
+  6. window    [0, G') ++ selected spans in order ++ [T-L', T); window row w
+               gets position w
+  7. RoPE      rotate-half rotary embedding at the window positions, for the
+               window keys and for the queries (a query sits at the window row
+               of its own key)
+  8. attention causal softmax attention over the window, scale 1/sqrt(d)
+
+Sources (the page title and the part of it each step follows):
+  * "ReAttention: Training-Free Infinite Context with Finite Attention Scope",
+    arXiv abstract (mlsanity.com page): position-agnostic top-k attention runs
+    before ordinary position-aware self-attention.
+  * the same title's research-map summary (atlas.scime.ai), section
+    "Approach": middle KV segments are chosen by the dot product of the query
+    with un-positioned keys, concatenated with the global and local caches, and
+    only then given positional embeddings, so positions stay inside the
+    pre-trained range.
+  * the same title's OpenReview discussion (paperhub.cn copy):
+      - "Decoding Phase" pseudocode: append to the cache first, score the
+        middle slice key[G:-L], top-k, concatenate global ++ recalled ++ local
+        for both K and V, attend;
+      - "Prefilling Phase" pseudocode: the same per chunk (its concat slices
+        are garbled; the decoding slices are used);
+      - the NIAH reply's hyperparameter list for LLaMA3-8B-8K: global 32,
+        span ("seg_size") 32, 127 spans, local 4096, chunk 512;
+      - the reply on token eviction: nothing is evicted and selection is
+        redone per head, layer and step.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * GQA: one selection per KV head, scoring with the sum of the group's
+    query-head logits (step 3).
+  * span reduce: max over the span's tokens (step 4); a block of queries sums
+    its queries' span maxima.
+  * ties: lower span index first (step 5).
+  * remainder: a partial last span, scored over and gathered with its real
+    length.
+  * RoPE: rotate-half pairing (c, c + d/2), inverse frequency
+    theta^(-2c/d), positions 0..W-1, angles in fp64.
+
+Arithmetic: products of bf16/fp32 inputs are exact in fp64; sums are fp64.  The
+top-k decision is made exact by recomputing, with ``fractions.Fraction``, every
+span whose fp64 score lies within 1e-9 * max|sigma| of the k-th one (fp64 error
+here is below 1e-12 relative).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+GUARD_REL = 1e-9
+
+
+# --------------------------------------------------------------------------
+# 1-2. regions and spans
+# --------------------------------------------------------------------------
+def regions(T: int, G: int, L: int):
+    """(G', L', mid_lo, mid_hi).  Global [0,G'), middle [G',T-L'), local [T-L',T)."""
+    Gp = min(G, T)
+    Lp = min(L, T - Gp)
+    return Gp, Lp, Gp, T - Lp
+
+
+def span_list(mid_lo: int, mid_hi: int, S: int):
+    """Spans [a, b) tiling the middle from its start; the last may be short."""
+    out = []
+    a = mid_lo
+    while a < mid_hi:
+        out.append((a, min(a + S, mid_hi)))
+        a += S
+    return out
+
+
+# --------------------------------------------------------------------------
+# 3-4. scores
+# --------------------------------------------------------------------------
+def token_scores(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int,
+                 mid_lo: int, mid_hi: int) -> np.ndarray:
+    """s[i, t - mid_lo] = sum_g q[i, h*g+gg] . K_h[t]  for t in the middle.
+
+    q_blk: [nb][Hq][d] fp64, K_h: [T][d] fp64.  Un-rotated, unscaled.
+    """
+    nb, _, d = q_blk.shape
+    Qh = q_blk[:, h * g:(h + 1) * g, :].reshape(nb * g, d)       # [nb*g][d]
+    Km = K_h[mid_lo:mid_hi]                                       # [N][d]
+    per_head = Qh @ Km.T                                          # [nb*g][N]
+    return per_head.reshape(nb, g, -1).sum(axis=1)                # [nb][N]
+
+
+def span_scores_from_tokens(s: np.ndarray, spans, mid_lo: int) -> np.ndarray:
+    """sigma[j] = sum_i max_{t in span j} s[i, t]; -0 canonicalised to +0."""
+    sig = np.empty(len(spans), dtype=np.float64)
+    for j, (a, b) in enumerate(spans):
+        sig[j] = s[:, a - mid_lo:b - mid_lo].max(axis=1).sum()
+    return sig + 0.0
+
+
+def exact_span_score(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int, span) -> Fraction:
+    """Exact rational value of sigma for one span (inputs are dyadic floats)."""
+    a, b = span
+    total = Fraction(0)
+    nb, _, d = q_blk.shape
+    for i in range(nb):
+        best = None
+        for t in range(a, b):
+            acc = Fraction(0)
+            for gg in range(g):
+                qv = q_blk[i, h * g + gg]
+                for c in range(d):
+                    acc += Fraction(float(qv[c])) * Fraction(float(K_h[t, c]))
+            if best is None or acc > best:
+                best = acc
+        total += best
+    return total
+
+
+# --------------------------------------------------------------------------
+# 5. top-k
+# --------------------------------------------------------------------------
+def select_topk(sigma: np.ndarray, k: int, exact_fn=None):
+    """Indices of the min(k, n) largest sigma, ties -> lower index, ascending.
+
+    `exact_fn(j)` returns the exact score of span j; it is consulted only for
+    spans whose fp64 score is within GUARD_REL * max|sigma| of the k-th one.
+    """
+    n = len(sigma)
+    kk = min(max(k, 0), n)
+    if kk == 0:
+        return []
+    if kk == n:
+        return list(range(n))
+    order = sorted(range(n), key=lambda j: (-sigma[j], j))
+    kth = sigma[order[kk - 1]]
+    tol = GUARD_REL * max(float(np.abs(sigma).max()), 1e-300)
+    band = [j for j in range(n) if abs(sigma[j] - kth) <= tol]
+    if len(band) > 1 and exact_fn is not None:
+        above = [j for j in range(n) if sigma[j] > kth + tol]
+        exact = {j: exact_fn(j) for j in band}
+        band_sorted = sorted(band, key=lambda j: (-exact[j], j))
+        chosen = above + band_sorted[:kk - len(above)]
+    else:
+        chosen = order[:kk]
+    return sorted(chosen)
+
+
+# --------------------------------------------------------------------------
+# 6-7. window and RoPE
+# --------------------------------------------------------------------------
+def window_src(T: int, Gp: int, Lp: int, spans, sel):
+    """Cache token index of every window row: global ++ selected ++ local."""
+    src = list(range(Gp))
+    for j in sel:
+        a, b = spans[j]
+        src.extend(range(a, b))
+    src.extend(range(T - Lp, T))
+    return np.array(src, dtype=np.int64)
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half RoPE in fp64.  x: [..., d]; pos broadcasts against x[..., 0]."""
+    d = x.shape[-1]
+    half = d // 2
+    inv = np.array([theta ** (-2.0 * c / d) for c in range(half)], dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    cs, sn = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cs - x2 * sn, x2 * cs + x1 * sn], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# 8. attention
+# --------------------------------------------------------------------------
+def attend_one(qv: np.ndarray, Kr: np.ndarray, V: np.ndarray, qpos: int, scale: float):
+    """softmax over window rows w <= qpos of (qv . Kr[w]) * scale, times V."""
+    n = qpos + 1
+    logits = (Kr[:n] @ qv) * scale
+    m = logits.max()
+    p = np.exp(logits - m)
+    return (p @ V[:n]) / p.sum()
+
+
+# --------------------------------------------------------------------------
+# The steps as the library exposes them
+# --------------------------------------------------------------------------
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def score_select(q, K, G, S, k, L, block_q=1, return_scores=False):
+    """Steps 1-5.  q [n_q][Hq][d], K [Hkv][T][d] (any float dtype, upcast to fp64).
+
+    Returns sel: list over blocks of list over KV heads of ascending span
+    indices (and the fp64 span scores [n_blk][Hkv][n_spans] if asked).
+    """
+    q = _f64(q)
+    K = _f64(K)
+    n_q, Hq, d = q.shape
+    Hkv, T, _ = K.shape
+    g = Hq // Hkv
+    Gp, Lp, lo, hi = regions(T, G, L)
+    spans = span_list(lo, hi, S)
+    n_blk = n_q // block_q
+    sel = []
+    scores = np.zeros((n_blk, Hkv, len(spans)), dtype=np.float64)
+    for b in range(n_blk):
+        qb = q[b * block_q:(b + 1) * block_q]
+        row = []
+        for h in range(Hkv):
+            if spans:
+                s = token_scores(qb, K[h], h, g, lo, hi)
+                sig = span_scores_from_tokens(s, spans, lo)
+            else:
+                sig = np.zeros(0)
+            scores[b, h] = sig
+            row.append(select_topk(
+                sig, k, lambda j, qb=qb, h=h: exact_span_score(qb, K[h], h, g, spans[j])))
+        sel.append(row)
+    return (sel, scores) if return_scores else sel
+
+
+def gather_rope(q, K, V, sel, G, S, L, block_q=1, theta=500000.0):
+    """Steps 6-7.  Returns (K_win, V_win, q_rot, W, qpos) with
+    K_win/V_win lists [n_blk][Hkv] of [W][d] fp64 arrays (K rotated, V plain),
+    q_rot [n_q][Hq][d] fp64, W [n_blk][Hkv], qpos [n_q][Hkv] window positions."""
+    q = _f64(q)
+    K = _f64(K)
+    V = _f64(V)
+    n_q, Hq, d = q.shape
+    Hkv, T, _ = K.shape
+    g = Hq // Hkv
+    Gp, Lp, lo, hi = regions(T, G, L)
+    spans = span_list(lo, hi, S)
+    n_blk = n_q // block_q
+    K_win, V_win = [], []
+    W = np.zeros((n_blk, Hkv), dtype=np.int64)
+    qpos = np.zeros((n_q, Hkv), dtype=np.int64)
+    q_rot = np.zeros_like(q)
+    for b in range(n_blk):
+        kr, vr = [], []
+        for h in range(Hkv):
+            src = window_src(T, Gp, Lp, spans, sel[b][h])
+            Wbh = len(src)
+            W[b, h] = Wbh
+            kr.append(rope(K[h][src], np.arange(Wbh), theta))
+            vr.append(V[h][src])
+            for i in range(b * block_q, (b + 1) * block_q):
+                p_abs = T - n_q + i
+                pos = Wbh - (T - p_abs)       # row holding the query's own key
+                qpos[i, h] = pos
+                q_rot[i, h * g:(h + 1) * g] = rope(q[i, h * g:(h + 1) * g], np.full(g, pos), theta)
+        K_win.append(kr)
+        V_win.append(vr)
+    return K_win, V_win, q_rot, W, qpos
+
+
+def window_attend(q_rot, K_win, V_win, qpos, block_q=1, scale=None):
+    """Step 8.  Returns out [n_q][Hq][d] fp64."""
+    n_q, Hq, d = q_rot.shape
+    Hkv = len(K_win[0])
+    g = Hq // Hkv
+    sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+    out = np.zeros((n_q, Hq, d), dtype=np.float64)
+    for i in range(n_q):
+        b = i // block_q
+        for hq in range(Hq):
+            h = hq // g
+            out[i, hq] = attend_one(q_rot[i, hq], K_win[b][h], V_win[b][h], int(qpos[i, h]), sc)
+    return out
+
+
+def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, return_all=False):
+    """Steps 1-8 (the fused decode/prefill step).  Returns (out, sel)."""
+    sel = score_select(q, K, G, S, k, L, block_q)
+    K_win, V_win, q_rot, W, qpos = gather_rope(q, K, V, sel, G, S, L, block_q, theta)
+    out = window_attend(q_rot, K_win, V_win, qpos, block_q, scale)
+    if return_all:
+        return dict(out=out, sel=sel, K_win=K_win, V_win=V_win, q_rot=q_rot, W=W, qpos=qpos)
+    return out, sel

@@ -1,0 +1,98 @@
+"""Second, independent coding of the ReAttention hot path in scalar Python.
+
+Every loop is written out; span scores and the top-k decision use exact
+rational arithmetic (fractions.Fraction), so on tiny inputs this is the exact
+definition.  It shares no code with oracle/ and is used to pin it.
+"""
+import math
+from fractions import Fraction
+
+
+def _rot(x, pos, theta):
+    d = len(x)
+    half = d // 2
+    y = [0.0] * d
+    for c in range(half):
+        ang = pos * (theta ** (-2.0 * c / d))
+        cs, sn = math.cos(ang), math.sin(ang)
+        y[c] = x[c] * cs - x[c + half] * sn
+        y[c + half] = x[c + half] * cs + x[c] * sn
+    return y
+
+
+def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None):
+    """q [n_q][Hq][d], K/V [Hkv][T][d] as nested lists of floats.
+
+    Returns (out [n_q][Hq][d] floats, sel [n_blk][Hkv] lists, W [n_blk][Hkv]).
+    """
+    n_q, Hq, d = len(q), len(q[0]), len(q[0][0])
+    Hkv, T = len(K), len(K[0])
+    g = Hq // Hkv
+    Gp = min(G, T)
+    Lp = min(L, T - Gp)
+    lo, hi = Gp, T - Lp
+    spans = []
+    a = lo
+    while a < hi:
+        spans.append((a, min(a + S, hi)))
+        a += S
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    out = [[[0.0] * d for _ in range(Hq)] for _ in range(n_q)]
+    sel_all, W_all = [], []
+    for b in range(n_q // block_q):
+        sel_b, W_b = [], []
+        for h in range(Hkv):
+            sig = []
+            for (a, e) in spans:
+                tot = Fraction(0)
+                for i in range(b * block_q, (b + 1) * block_q):
+                    best = None
+                    for t in range(a, e):
+                        acc = Fraction(0)
+                        for gg in range(g):
+                            for c in range(d):
+                                acc += Fraction(q[i][h * g + gg][c]) * Fraction(K[h][t][c])
+                        if best is None or acc > best:
+                            best = acc
+                    tot += best
+                sig.append(tot)
+            remaining = list(range(len(spans)))
+            chosen = []
+            for _ in range(min(k, len(spans))):
+                bj = remaining[0]
+                for j in remaining[1:]:
+                    if sig[j] > sig[bj]:      # strict: equal scores keep the lower index
+                        bj = j
+                chosen.append(bj)
+                remaining.remove(bj)
+            chosen.sort()
+            src = list(range(Gp))
+            for j in chosen:
+                src += list(range(spans[j][0], spans[j][1]))
+            src += list(range(T - Lp, T))
+            Wh = len(src)
+            krot = [_rot(K[h][src[w]], w, theta) for w in range(Wh)]
+            for i in range(b * block_q, (b + 1) * block_q):
+                pos = Wh - n_q + i
+                for gg in range(g):
+                    hq = h * g + gg
+                    qr = _rot(q[i][hq], pos, theta)
+                    logits = []
+                    for w in range(pos + 1):
+                        s = 0.0
+                        for c in range(d):
+                            s += qr[c] * krot[w][c]
+                        logits.append(s * sc)
+                    m = max(logits)
+                    p = [math.exp(x - m) for x in logits]
+                    z = sum(p)
+                    for c in range(d):
+                        acc = 0.0
+                        for w in range(pos + 1):
+                            acc += p[w] * V[h][src[w]][c]
+                        out[i][hq][c] = acc / z
+            sel_b.append(chosen)
+            W_b.append(Wh)
+        sel_all.append(sel_b)
+        W_all.append(W_b)
+    return out, sel_all, W_all
