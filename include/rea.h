@@ -1,0 +1,210 @@
+/*
+ * rea.h - C ABI of librea.so: the ReAttention hot path on AMD MI355X (gfx950).
+ *
+ * The method (ReAttention: Training-Free Infinite Context with Finite
+ * Attention Scope, arXiv 2407.15176):
+ *   1. score the un-rotated queries against the pre-RoPE keys of the middle
+ *      cache (everything between the first G and the last L tokens), reduce
+ *      token scores to span scores and keep the top-k spans
+ *      [research-map summary, "Approach"; OpenReview discussion, "Decoding
+ *      Phase" pseudocode: score = query @ key[G:-L]^T, then top-k];
+ *   2. concatenate global cache ++ selected spans (in original order) ++ local
+ *      cache into one window [same pseudocode: key_recall / value_recall];
+ *   3. apply RoPE with fresh positions 0..W-1, so the attention scope stays
+ *      inside the pre-trained range [summary, "Approach"];
+ *   4. run ordinary causal softmax attention over the window [pseudocode:
+ *      flash_attention(query, key_recall, value_recall)].
+ *
+ * Readings this library takes where the pages are silent:
+ *   - GQA: one selection per KV head; a token's score is the sum over the
+ *     head's query group of q . k.
+ *   - span score: max over the span's tokens; for a block of queries (chunked
+ *     prefill) the sum over the block's queries of those maxima.
+ *   - ties: the lower span index wins; selected spans are emitted ascending.
+ *   - the middle is cut into spans of S tokens from its start; a shorter last
+ *     span is scored over, and gathered with, its real length.
+ *   - RoPE: rotate-half pairing (c, c + d/2), inverse frequency
+ *     rope_theta^(-2c/d); a query takes the window position of its own key.
+ *
+ * Conventions
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates nothing and keeps no state between calls (apart from a
+ *     thread-local error string).  Calls are re-entrant.
+ *   - All argument validation happens on the host before any HIP call, so
+ *     every error status below is reachable on a machine without a GPU.
+ *   - Kernels are enqueued asynchronously on the caller's stream (a
+ *     hipStream_t passed as void*; NULL = the null stream).  A device fault
+ *     surfaces at the caller's next synchronisation.
+ *   - Outputs are undefined when the return value is not REA_OK.
+ *   - Sizes are in elements unless the name says bytes.
+ */
+#ifndef REA_H
+#define REA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define REA_ABI_VERSION 1
+
+typedef enum rea_status {
+    REA_OK = 0,
+    REA_EINVAL = 1,        /* null pointer, struct_size mismatch, bad hyperparameter */
+    REA_ESHAPE = 2,        /* inconsistent sizes (Hq % Hkv, n_q % block_q, strides, W_cap, ...) */
+    REA_EDTYPE = 3,        /* dtype not REA_BF16 / REA_F32 */
+    REA_EALIGN = 4,        /* a pointer or row stride is not 16-byte aligned */
+    REA_EWORKSPACE = 5,    /* workspace smaller than rea_query_sizes() asks for */
+    REA_ENODEVICE = 6,     /* no usable HIP device */
+    REA_ELAUNCH = 7,       /* a kernel launch failed (hipGetLastError) */
+    REA_EUNSUPPORTED = 8   /* valid arguments outside what this build implements */
+} rea_status;
+
+typedef enum rea_dtype {
+    REA_BF16 = 0,          /* bfloat16 storage of q, K, V */
+    REA_F32 = 1            /* float32 storage of q, K, V */
+} rea_dtype;
+
+/*
+ * One layer's problem, batch 1.
+ *
+ * q      [n_q][n_q_heads][head_dim], contiguous, un-rotated.  The queries are
+ *        the last n_q tokens of the cache (their K/V rows are already
+ *        appended, as the pseudocode appends before scoring).
+ * k, v   pre-RoPE cache: element (h, t, c) at  base[h*kv_stride_head +
+ *        t*kv_stride_tok + c],  h < n_kv_heads, t < T, c < head_dim.
+ *        16-byte aligned base and row stride.
+ * T      valid tokens, including the n_q newest ones.
+ * Query head hq reads KV head hq / (n_q_heads / n_kv_heads).
+ */
+typedef struct rea_problem {
+    uint32_t struct_size;      /* = sizeof(rea_problem) */
+    int32_t dtype;             /* rea_dtype */
+    int32_t n_q;               /* >= 1 */
+    int32_t n_q_heads;         /* Hq, multiple of n_kv_heads */
+    int32_t n_kv_heads;        /* Hkv >= 1 */
+    int32_t head_dim;          /* d: 64 or 128 */
+    int64_t T;                 /* n_q <= T < 2^31 */
+    const void *q;
+    const void *k;
+    const void *v;
+    int64_t kv_stride_head;    /* >= T * kv_stride_tok */
+    int64_t kv_stride_tok;     /* >= head_dim */
+} rea_problem;
+
+/*
+ * Hyperparameters: global size G, span size S, number of spans k, local size
+ * L [OpenReview discussion, hyperparameter list of the NIAH reply: global 32,
+ * seg_size 32, num_seg 127, local 4096 on LLaMA3-8B-8K], and the number of
+ * consecutive queries that share one selection (1 when decoding; a prefill
+ * chunk is cut into blocks of block_q queries).
+ *
+ * Regions: G' = min(G, T), L' = min(L, T - G'), middle = [G', T - L').
+ * Precondition: n_q <= L', or the middle is empty (T <= G + L).
+ */
+typedef struct rea_params {
+    uint32_t struct_size;      /* = sizeof(rea_params) */
+    int32_t G;                 /* >= 0 */
+    int32_t S;                 /* >= 1 */
+    int32_t topk;              /* >= 0 spans */
+    int32_t L;                 /* >= 0 */
+    int32_t block_q;           /* >= 1, divides n_q */
+    double rope_theta;         /* > 0 */
+    float softmax_scale;       /* <= 0 selects 1/sqrt(head_dim) */
+    int32_t reserved;          /* must be 0 */
+} rea_params;
+
+/* Derived sizes and the workspace each entry point needs. */
+typedef struct rea_sizes {
+    int64_t n_blocks;          /* n_q / block_q */
+    int64_t n_spans;           /* ceil((T - L' - G') / S) */
+    int64_t k_sel;             /* min(topk, n_spans): spans selected per (block, KV head) */
+    int64_t W_cap;             /* min(T, G' + k_sel*S + L'): the largest possible window */
+    size_t ws_score_select;    /* bytes of workspace rea_score_select needs */
+    size_t ws_window_attend;   /* bytes of workspace rea_window_attend needs */
+    size_t ws_decode_step;     /* bytes of workspace rea_decode_step needs */
+} rea_sizes;
+
+/* Optional timing hooks: hipEvent_t handles (as void*) that rea_decode_step
+ * records on its stream immediately before and after the token-scoring kernel.
+ * Either may be NULL. */
+typedef struct rea_timing {
+    void *score_begin;
+    void *score_end;
+} rea_timing;
+
+int rea_abi_version(void);
+const char *rea_status_string(int status);
+/* Detail message of the last failing call on this thread ("" if none). */
+const char *rea_last_error(void);
+
+/* Fills *out.  Host-only: validates p and a, makes no HIP call. */
+rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes *out);
+
+/*
+ * Step 1: position-agnostic span scoring and top-k selection.
+ *
+ * sel          [n_blocks][n_kv_heads][topk] int32: for block b and KV head h
+ *              the selected span indices (span j covers middle tokens
+ *              [G' + j*S, min(G' + (j+1)*S, T - L'))), strictly ascending,
+ *              padded with -1 after n_sel entries.  May be NULL if topk == 0.
+ * n_sel        [n_blocks][n_kv_heads] int32 = k_sel.
+ * span_scores  NULL, or [n_blocks][n_kv_heads][n_spans] double: sum over the
+ *              block's queries of the span's maximum token score.
+ * ws           device workspace of at least sizes.ws_score_select bytes
+ *              (256-byte aligned); contents are scratch.
+ */
+rea_status rea_score_select(const rea_problem *p, const rea_params *a,
+                            int32_t *sel, int32_t *n_sel, double *span_scores,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Steps 2-3: gather the window and apply RoPE at window positions.
+ *
+ * sel, n_sel   as produced by rea_score_select (device).
+ * k_win        [n_blocks][n_kv_heads][W_cap][head_dim] float32: row w of the
+ *              window key, rotated to position w (rows >= W untouched).
+ * v_win        [n_blocks][n_kv_heads][W_cap][head_dim], problem dtype: the
+ *              window value rows, bit-exact copies of the cache rows.
+ * q_rot        [n_q][n_q_heads][head_dim] float32: each query rotated to the
+ *              window position of its own key, W - n_q + (query index in q).
+ * W            [n_blocks][n_kv_heads] int32 window lengths.
+ * W_cap        row capacity of k_win/v_win; must be >= sizes.W_cap.
+ */
+rea_status rea_gather_rope(const rea_problem *p, const rea_params *a,
+                           const int32_t *sel, const int32_t *n_sel,
+                           float *k_win, void *v_win, float *q_rot, int32_t *W,
+                           int32_t W_cap, void *stream);
+
+/*
+ * Step 4: causal softmax attention over the window.  Query i of block b sees
+ * window rows w <= its position; logits are (q_rot . k_win[w]) * scale.
+ * out          [n_q][n_q_heads][head_dim] float32.
+ * ws           at least sizes.ws_window_attend bytes.
+ */
+rea_status rea_window_attend(const rea_problem *p, const rea_params *a,
+                             const float *q_rot, const float *k_win, const void *v_win,
+                             const int32_t *W, int32_t W_cap, float *out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Steps 1-4 in one call, no host synchronisation (window lengths stay on the
+ * device).  The decode step of one layer when n_q == block_q == 1; any
+ * n_q/block_q accepted by the three calls above is accepted here too.
+ * out          [n_q][n_q_heads][head_dim] float32.
+ * sel, n_sel   optional copies of the selection (NULL to skip).
+ * ws           at least sizes.ws_decode_step bytes.
+ * timing       optional events around the scoring kernel (NULL to skip).
+ */
+rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out,
+                           int32_t *sel, int32_t *n_sel,
+                           void *ws, size_t ws_bytes, void *stream,
+                           const rea_timing *timing);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REA_H */

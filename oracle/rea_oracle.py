@@ -107,9 +107,20 @@ def token_scores(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int,
 
 
 def span_scores_from_tokens(s: np.ndarray, spans, mid_lo: int) -> np.ndarray:
-    """sigma[j] = sum_i max_{t in span j} s[i, t]; -0 canonicalised to +0."""
+    """sigma[j] = sum_i max_{t in span j} s[i, t]; -0 canonicalised to +0.
+
+    s: [nb][N] token scores of the block's queries over the middle.  Spans of
+    full length S are reduced together through a [nb][n_full][S] view.
+    """
+    if not spans:
+        return np.zeros(0)
+    nb = s.shape[0]
+    S = spans[0][1] - spans[0][0]
+    n_full = sum(1 for (a, b) in spans if b - a == S)
     sig = np.empty(len(spans), dtype=np.float64)
-    for j, (a, b) in enumerate(spans):
+    sig[:n_full] = s[:, :n_full * S].reshape(nb, n_full, S).max(axis=2).sum(axis=0)
+    for j in range(n_full, len(spans)):
+        a, b = spans[j]
         sig[j] = s[:, a - mid_lo:b - mid_lo].max(axis=1).sum()
     return sig + 0.0
 
@@ -189,13 +200,15 @@ def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
 # --------------------------------------------------------------------------
 # 8. attention
 # --------------------------------------------------------------------------
-def attend_one(qv: np.ndarray, Kr: np.ndarray, V: np.ndarray, qpos: int, scale: float):
-    """softmax over window rows w <= qpos of (qv . Kr[w]) * scale, times V."""
-    n = qpos + 1
-    logits = (Kr[:n] @ qv) * scale
-    m = logits.max()
+def attend_rows(Q: np.ndarray, Kr: np.ndarray, V: np.ndarray, qpos: np.ndarray, scale: float):
+    """Rows of softmax attention: row r of the result is
+    sum_w softmax_w((Q[r] . Kr[w]) * scale over w <= qpos[r]) * V[w]."""
+    logits = (Q @ Kr.T) * scale                                  # [R][W]
+    w = np.arange(Kr.shape[0])
+    logits = np.where(w[None, :] <= np.asarray(qpos)[:, None], logits, -np.inf)
+    m = logits.max(axis=1, keepdims=True)
     p = np.exp(logits - m)
-    return (p @ V[:n]) / p.sum()
+    return (p @ V) / p.sum(axis=1, keepdims=True)
 
 
 # --------------------------------------------------------------------------
@@ -279,11 +292,13 @@ def window_attend(q_rot, K_win, V_win, qpos, block_q=1, scale=None):
     g = Hq // Hkv
     sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
     out = np.zeros((n_q, Hq, d), dtype=np.float64)
-    for i in range(n_q):
-        b = i // block_q
-        for hq in range(Hq):
-            h = hq // g
-            out[i, hq] = attend_one(q_rot[i, hq], K_win[b][h], V_win[b][h], int(qpos[i, h]), sc)
+    for b in range(n_q // block_q):
+        i0, i1 = b * block_q, (b + 1) * block_q
+        for h in range(Hkv):
+            Q = q_rot[i0:i1, h * g:(h + 1) * g].reshape(-1, d)     # rows (i, gg)
+            pos = np.repeat(qpos[i0:i1, h], g)
+            out[i0:i1, h * g:(h + 1) * g] = attend_rows(
+                Q, K_win[b][h], V_win[b][h], pos, sc).reshape(i1 - i0, g, d)
     return out
 
 

@@ -1,0 +1,110 @@
+"""Shared helpers for the GPU parity tests: run the library, run the oracle on
+the same generated inputs, compare."""
+import numpy as np
+import torch
+
+import oracle.rea_oracle as O
+import synth
+import top_kv_cache_amd as rea
+from synth import torch_io
+
+# output tolerance (max-abs) by input dtype
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def device_inputs(w, layer=0, q=None, K=None, V=None):
+    q = torch_io.q_device(w, layer) if q is None else q
+    K = torch_io.kv_device(w, layer, "k") if K is None else K
+    V = torch_io.kv_device(w, layer, "v") if V is None else V
+    return q, K, V
+
+
+def run_library(w, q, K, V, components=True):
+    """All four entry points on the device; results copied to host numpy."""
+    st = rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta)
+    res = {"sizes": st.sizes}
+    if components:
+        sel, nsel, sc = st.score_select(span_scores=True)
+        k_win, v_win, q_rot, W = st.gather_rope(sel, nsel)
+        out = st.window_attend(q_rot, k_win, v_win, W)
+        res.update(sel=sel, nsel=nsel, sc=sc, k_win=k_win, v_win=v_win, q_rot=q_rot, W=W,
+                   out=out)
+    Hkv, nb = w.Hkv, st.sizes.n_blocks
+    sel2 = torch.full((nb, Hkv, max(w.topk, 1)), -7, dtype=torch.int32, device=q.device)
+    nsel2 = torch.empty((nb, Hkv), dtype=torch.int32, device=q.device)
+    res["out_step"] = st.decode_step(sel=sel2 if w.topk > 0 else None, nsel=nsel2)
+    res["sel_step"], res["nsel_step"] = sel2[:, :, :w.topk], nsel2
+    torch.cuda.synchronize()
+    host = {}
+    for k, v in res.items():
+        if isinstance(v, torch.Tensor):
+            if v.dtype == torch.bfloat16:
+                v = v.view(torch.int16).cpu().numpy().view(np.uint16)
+                v = synth.bf16_bits_to_f32(v)
+            else:
+                v = v.cpu().numpy()
+        host[k] = v
+    return host
+
+
+def oracle_head(w, layer, h, q64=None, K_h=None, V_h=None):
+    """Oracle steps for KV head h alone (heads are independent)."""
+    g = w.g
+    if q64 is None:
+        q64 = synth.to_f32(w.q(layer), w.dtype).astype(np.float64)
+    qh = q64[:, h * g:(h + 1) * g]
+    if K_h is None:
+        K_h = synth.to_f32(w.kv(layer, "k", h, h + 1), w.dtype).astype(np.float64)
+    if V_h is None:
+        V_h = synth.to_f32(w.kv(layer, "v", h, h + 1), w.dtype).astype(np.float64)
+    sel, sc = O.score_select(qh, K_h, w.G, w.S, w.topk, w.L, w.block_q, return_scores=True)
+    Kw, Vw, qr, W, qpos = O.gather_rope(qh, K_h, V_h, sel, w.G, w.S, w.L, w.block_q,
+                                        w.rope_theta)
+    out = O.window_attend(qr, Kw, Vw, qpos, w.block_q)
+    return dict(sel=[s[0] for s in sel], sc=sc[:, 0], Kw=[k[0] for k in Kw],
+                Vw=[v[0] for v in Vw], q_rot=qr, W=W[:, 0], out=out)
+
+
+def compare_head(w, gpu, ora, h, check_windows=True):
+    """Assert parity of KV head h; returns the max-abs output error."""
+    g, nb = w.g, len(ora["sel"])
+    for b in range(nb):
+        exp = ora["sel"][b]
+        ns = int(gpu["nsel"][b, h])
+        got = gpu["sel"][b, h, :ns].tolist() if w.topk > 0 else []
+        assert ns == len(exp), (b, h, ns, len(exp))
+        assert got == exp, (b, h, sorted(set(got) ^ set(exp))[:10])
+        if w.topk > ns:
+            assert np.all(gpu["sel"][b, h, ns:] == -1)
+        got_step = gpu["sel_step"][b, h, :ns].tolist() if w.topk > 0 else []
+        assert got_step == exp and int(gpu["nsel_step"][b, h]) == ns
+    if ora["sc"].size:
+        ref = ora["sc"]
+        scale = max(1.0, float(np.abs(ref).max()))
+        err = np.abs(gpu["sc"][:, h, :] - ref).max()
+        assert err <= 1e-12 * scale, ("span scores", h, err)
+    assert np.array_equal(gpu["W"][:, h], ora["W"]), (gpu["W"][:, h], ora["W"])
+    if check_windows:
+        for b in range(nb):
+            Wb = int(ora["W"][b])
+            kref = ora["Kw"][b]
+            kgot = gpu["k_win"][b, h, :Wb].astype(np.float64)
+            slack = 1e-13 * float(np.abs(kref).max()) if kref.size else 0.0
+            assert np.all(np.abs(kgot - kref) <= 1.2e-7 * np.abs(kref) + slack), ("k_win", b, h)
+            assert np.array_equal(gpu["v_win"][b, h, :Wb].astype(np.float64), ora["Vw"][b]), \
+                ("v_win", b, h)
+        qref = ora["q_rot"]
+        qgot = gpu["q_rot"][:, h * g:(h + 1) * g].astype(np.float64)
+        slack = 1e-13 * float(np.abs(qref).max())
+        assert np.all(np.abs(qgot - qref) <= 1.2e-7 * np.abs(qref) + slack), ("q_rot", h)
+    oref = ora["out"]
+    ogot = gpu["out_step"][:, h * g:(h + 1) * g].astype(np.float64)
+    err = float(np.abs(ogot - oref).max())
+    assert err <= TOL[w.dtype], ("out", h, err)
+    if "out" in gpu:
+        assert np.array_equal(gpu["out"][:, h * g:(h + 1) * g], gpu["out_step"][:, h * g:(h + 1) * g])
+    return err

@@ -1,0 +1,161 @@
+"""C-ABI contract on the host: the library loads, exports every declared entry
+point, reports sizes, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_kv_cache_amd as rea
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # an aligned non-null address; nothing is launched
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "rea.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rea_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = rea.lib()
+    syms = declared_symbols()
+    assert set(syms) >= {"rea_score_select", "rea_gather_rope", "rea_window_attend",
+                         "rea_decode_step", "rea_query_sizes"}
+    for s in syms:
+        assert hasattr(L, s), s
+    assert sorted(rea.ENTRY_POINTS) == syms
+    assert L.rea_abi_version() == 1
+    for i, name in enumerate(rea.STATUS):
+        assert L.rea_status_string(i).decode() == name
+
+
+def good(dtype=rea.REA_BF16, n_q=1, Hq=32, Hkv=8, d=128, T=131072):
+    p = rea.problem(FAKE, FAKE, FAKE, dtype=dtype, n_q=n_q, Hq=Hq, Hkv=Hkv, d=d, T=T,
+                    stride_head=T * d, stride_tok=d)
+    a = rea.params(32, 32, 120, 4096, 1)
+    return p, a
+
+
+def sizes_status(p, a):
+    s = rea.Sizes()
+    return rea.lib().rea_query_sizes(ctypes.byref(p), ctypes.byref(a), ctypes.byref(s)), s
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_sizes_match_workloads(cfg):
+    w = synth.config(cfg)
+    p = rea.problem(FAKE, FAKE, FAKE, dtype=rea.REA_BF16 if w.dtype == "bf16" else rea.REA_F32,
+                    n_q=w.n_q, Hq=w.Hq, Hkv=w.Hkv, d=w.d, T=w.T, stride_head=w.T * w.d,
+                    stride_tok=w.d)
+    a = rea.params(w.G, w.S, w.topk, w.L, w.block_q)
+    st, s = sizes_status(p, a)
+    assert st == 0, rea.lib().rea_last_error()
+    assert s.n_spans == w.n_spans
+    assert s.k_sel == min(w.topk, w.n_spans)
+    assert s.W_cap == w.W_cap
+    assert s.n_blocks == w.n_q // w.block_q
+    assert s.ws_decode_step >= s.ws_score_select > 0
+
+
+def mutate(**kw):
+    p, a = good()
+    for k, v in kw.items():
+        if hasattr(p, k):
+            setattr(p, k, v)
+        else:
+            setattr(a, k, v)
+    return p, a
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(struct_size=12), rea.STATUS.index("REA_EINVAL")),
+    (dict(q=None), rea.STATUS.index("REA_EINVAL")),
+    (dict(k=None), rea.STATUS.index("REA_EINVAL")),
+    (dict(S=0), rea.STATUS.index("REA_EINVAL")),
+    (dict(topk=-1), rea.STATUS.index("REA_EINVAL")),
+    (dict(G=-1), rea.STATUS.index("REA_EINVAL")),
+    (dict(L=-5), rea.STATUS.index("REA_EINVAL")),
+    (dict(block_q=0), rea.STATUS.index("REA_EINVAL")),
+    (dict(reserved=3), rea.STATUS.index("REA_EINVAL")),
+    (dict(rope_theta=0.0), rea.STATUS.index("REA_EINVAL")),
+    (dict(rope_theta=float("inf")), rea.STATUS.index("REA_EINVAL")),
+    (dict(softmax_scale=float("nan")), rea.STATUS.index("REA_EINVAL")),
+    (dict(dtype=7), rea.STATUS.index("REA_EDTYPE")),
+    (dict(n_q_heads=30), rea.STATUS.index("REA_ESHAPE")),
+    (dict(n_kv_heads=0), rea.STATUS.index("REA_ESHAPE")),
+    (dict(n_q=0), rea.STATUS.index("REA_ESHAPE")),
+    (dict(n_q=4, block_q=3), rea.STATUS.index("REA_ESHAPE")),
+    (dict(T=0), rea.STATUS.index("REA_ESHAPE")),
+    (dict(T=1 << 31), rea.STATUS.index("REA_ESHAPE")),
+    (dict(kv_stride_tok=64), rea.STATUS.index("REA_ESHAPE")),
+    (dict(kv_stride_head=128), rea.STATUS.index("REA_ESHAPE")),
+    (dict(n_q=4097, block_q=1), rea.STATUS.index("REA_ESHAPE")),   # queries beyond the local region
+    (dict(head_dim=96), rea.STATUS.index("REA_EUNSUPPORTED")),
+    (dict(k=FAKE + 8), rea.STATUS.index("REA_EALIGN")),
+    (dict(kv_stride_tok=132), rea.STATUS.index("REA_EALIGN")),
+    (dict(n_q=128, block_q=128), rea.STATUS.index("REA_EUNSUPPORTED")),
+])
+def test_invalid_arguments(kw, expect):
+    p, a = mutate(**kw)
+    if "head_dim" in kw:
+        p.kv_stride_tok, p.kv_stride_head = kw["head_dim"], p.T * kw["head_dim"]
+    if kw.get("kv_stride_tok") == 132:      # misaligned rows, no overlap
+        p.kv_stride_head = p.T * 132
+    st, _ = sizes_status(p, a)
+    assert st == expect, (rea.STATUS[st], rea.lib().rea_last_error())
+    assert rea.lib().rea_last_error().decode() != ""
+    # the entry points run the same validation before any HIP call
+    L = rea.lib()
+    st2 = L.rea_score_select(ctypes.byref(p), ctypes.byref(a), FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert st2 == expect
+    st3 = L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE, 1 << 40,
+                            None, None)
+    assert st3 == expect
+
+
+def test_no_middle_allows_many_queries():
+    # T <= G + L: every query may be anywhere (plain causal attention)
+    p, a = good(n_q=64, T=1000)
+    a.block_q = 64
+    st, s = sizes_status(p, a)
+    assert st == 0 and s.n_spans == 0 and s.W_cap == 1000 and s.k_sel == 0
+
+
+def test_entry_point_argument_errors():
+    L = rea.lib()
+    p, a = good()
+    _, s = sizes_status(p, a)
+    E = rea.STATUS.index
+    # workspace too small / misaligned
+    assert L.rea_score_select(ctypes.byref(p), ctypes.byref(a), FAKE, FAKE, None, FAKE,
+                              s.ws_score_select - 1, None) == E("REA_EWORKSPACE")
+    assert L.rea_score_select(ctypes.byref(p), ctypes.byref(a), FAKE, FAKE, None, FAKE + 16,
+                              s.ws_score_select, None) == E("REA_EALIGN")
+    assert L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE,
+                             s.ws_decode_step - 1, None, None) == E("REA_EWORKSPACE")
+    # null outputs
+    assert L.rea_score_select(ctypes.byref(p), ctypes.byref(a), None, FAKE, None, FAKE,
+                              s.ws_score_select, None) == E("REA_EINVAL")
+    assert L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), None, None, None, FAKE,
+                             s.ws_decode_step, None, None) == E("REA_EINVAL")
+    # window capacity too small
+    assert L.rea_gather_rope(ctypes.byref(p), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, int(s.W_cap) - 1, None) == E("REA_ESHAPE")
+    assert L.rea_window_attend(ctypes.byref(p), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE,
+                               int(s.W_cap), FAKE, FAKE, s.ws_window_attend - 1,
+                               None) == E("REA_EWORKSPACE")
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = rea.lib()
+    p, a = good()
+    _, s = sizes_status(p, a)
+    st = L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE,
+                           s.ws_decode_step, None, None)
+    assert st == rea.STATUS.index("REA_ENODEVICE"), L.rea_last_error()

@@ -1,0 +1,107 @@
+"""GPU parity: the library (through its C ABI) against the fp64 oracle on the
+same seeded inputs.  Selection must match exactly, window lengths and value
+rows bit-exactly, rotated rows to fp32 rounding, outputs within the stated
+max-abs tolerance (2e-2 for bf16 inputs, 1e-5 for fp32)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import torch_io
+from tests.parity import (TOL, compare_head, device_inputs, log, oracle_head,
+                          run_library)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def S(**kw):
+    return synth.small(**kw)
+
+
+SMALL = {
+    "bf16_g2_d64_partial": S(),
+    "f32_g1_d128_partial": S(dtype="f32", Hq=2, Hkv=2, d=128, T=1010, S=32, topk=7, L=100),
+    "bf16_k0": S(topk=0, T=500),
+    "bf16_all_spans": S(T=300, S=16, topk=50),
+    "bf16_no_middle": S(T=50, G=4, L=64),
+    "bf16_prefill_blocks": S(Hq=8, Hkv=2, d=128, T=600, n_q=8, block_q=4, S=16, topk=6,
+                             L=64, needles=0),
+    "f32_prefill_blocks": S(dtype="f32", Hq=4, Hkv=1, d=64, T=900, n_q=16, block_q=16, S=32,
+                            topk=3, L=40, needles=0),
+    "bf16_G0": S(G=0, T=800),
+    "bf16_token_level_S1": S(S=1, topk=40, T=400),
+    "bf16_S20": S(S=20, topk=9, T=1500, kv_scaled=True),
+    "bf16_S64_g8": S(Hq=8, Hkv=1, d=128, S=64, topk=6, T=3000, L=200, needles=2),
+    "f32_L1": S(dtype="f32", L=1, T=400, topk=4),
+    "bf16_many_heads": S(Hq=32, Hkv=8, d=128, T=2048, S=32, topk=12, L=256, needles=2,
+                         kv_scaled=True),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small(name):
+    w = SMALL[name]
+    log(f"[small] {name}: T={w.T} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} k={w.topk} "
+        f"n_q={w.n_q} bq={w.block_q} {w.dtype}")
+    q, K, V = device_inputs(w)
+    gpu = run_library(w, q, K, V)
+    errs = [compare_head(w, gpu, oracle_head(w, 0, h), h) for h in range(w.Hkv)]
+    log(f"  max-abs out err {max(errs):.3e}")
+
+
+def test_exact_ties_lower_index_wins():
+    """Integer-valued inputs: many spans tie exactly; fp64 sums are exact on
+    both sides, so the lower-index rule must be reproduced bit-exactly."""
+    rng = np.random.default_rng(1234)
+    w = S(Hq=4, Hkv=2, d=64, T=1200, S=16, topk=11, L=64, needles=0)
+    qn = rng.integers(-1, 2, size=(1, w.Hq, w.d)).astype(np.float32)
+    Kn = rng.integers(-2, 3, size=(w.Hkv, w.T, w.d)).astype(np.float32)
+    Kn[:, 200:260] = Kn[:, 300:360]           # duplicated spans -> equal scores
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    q, K, V = to_bf(qn), to_bf(Kn), to_bf(Vn)
+    gpu = run_library(w, q, K, V)
+    q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
+    n_ties = 0
+    for h in range(w.Hkv):
+        ora = oracle_head(w, 0, h, q64, K64[h:h + 1], V64[h:h + 1])
+        sc = ora["sc"][0]
+        kth = np.sort(sc)[::-1][w.topk - 1]
+        n_ties += int((sc == kth).sum())
+        compare_head(w, gpu, ora, h)
+    assert n_ties > 2 * w.Hkv       # the case really exercises the tie rule
+
+
+def test_deterministic():
+    w = SMALL["bf16_many_heads"]
+    q, K, V = device_inputs(w)
+    a = run_library(w, q, K, V, components=False)
+    b = run_library(w, q, K, V, components=False)
+    assert np.array_equal(a["out_step"], b["out_step"])
+    assert np.array_equal(a["sel_step"], b["sel_step"])
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_config_one_layer(cfg):
+    w = synth.config(cfg)
+    log(f"[config {cfg}] {w.name}")
+    q, K, V = device_inputs(w)
+    gpu = run_library(w, q, K, V)
+    q64 = synth.to_f32(w.q(0), w.dtype).astype(np.float64)
+    errs = []
+    for h in range(w.Hkv):
+        ora = oracle_head(w, 0, h, q64)
+        errs.append(compare_head(w, gpu, ora, h))
+        needles = [j for (hh, j) in w.needle_spans(0) if hh == h]
+        assert set(needles) <= set(ora["sel"][0])
+    log(f"  max-abs out err {max(errs):.3e} (tolerance {TOL[w.dtype]})")

@@ -299,7 +299,7 @@ def _mut_span_max_of_sum(s, spans, mid_lo):
 _orig_token_scores = O.token_scores
 _orig_select = O.select_topk
 _orig_rope = O.rope
-_orig_attend = O.attend_one
+_orig_attend = O.attend_rows
 _orig_regions = O.regions
 _orig_span_list = O.span_list
 
@@ -344,12 +344,12 @@ def _mut_rope_adjacent_pairs(x, pos, theta):
     return _orig_rope(x[..., perm], pos, theta)[..., inv_perm]
 
 
-def _mut_no_scale(qv, Kr, V, qpos, scale):
-    return _orig_attend(qv, Kr, V, qpos, 1.0)
+def _mut_no_scale(Q, Kr, V, qpos, scale):
+    return _orig_attend(Q, Kr, V, qpos, 1.0)
 
 
-def _mut_exclude_self(qv, Kr, V, qpos, scale):
-    return _orig_attend(qv, Kr, V, max(qpos - 1, 0), scale)
+def _mut_exclude_self(Q, Kr, V, qpos, scale):
+    return _orig_attend(Q, Kr, V, np.maximum(np.asarray(qpos) - 1, 0), scale)
 
 
 def _mut_local_short(T, G, L):
@@ -372,8 +372,8 @@ MUTATIONS = {
     "spans_in_score_order": ("select_topk", _mut_unsorted),
     "rope_sign_flip": ("rope", _mut_rope_sign),
     "rope_adjacent_pairing": ("rope", _mut_rope_adjacent_pairs),
-    "no_softmax_scale": ("attend_one", _mut_no_scale),
-    "query_excludes_own_key": ("attend_one", _mut_exclude_self),
+    "no_softmax_scale": ("attend_rows", _mut_no_scale),
+    "query_excludes_own_key": ("attend_rows", _mut_exclude_self),
     "local_region_short_by_one": ("regions", _mut_local_short),
     "partial_span_dropped": ("span_list", _mut_drop_partial),
 }

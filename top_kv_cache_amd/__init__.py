@@ -1,0 +1,240 @@
+"""Python binding of librea.so (the ReAttention hot path on MI355X).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory (tensors) and the stream
+(``torch.cuda.current_stream()``).  The library must be built
+(``python -m top_kv_cache_amd._build``); importing the package never falls back
+to any other implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librea.so")
+
+REA_BF16, REA_F32 = 0, 1
+STATUS = ["REA_OK", "REA_EINVAL", "REA_ESHAPE", "REA_EDTYPE", "REA_EALIGN",
+          "REA_EWORKSPACE", "REA_ENODEVICE", "REA_ELAUNCH", "REA_EUNSUPPORTED"]
+ENTRY_POINTS = ["rea_abi_version", "rea_status_string", "rea_last_error", "rea_query_sizes",
+                "rea_score_select", "rea_gather_rope", "rea_window_attend", "rea_decode_step"]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", ctypes.c_int32),
+                ("n_q", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("T", ctypes.c_int64), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("kv_stride_head", ctypes.c_int64),
+                ("kv_stride_tok", ctypes.c_int64)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("G", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("L", ctypes.c_int32), ("block_q", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("n_blocks", ctypes.c_int64), ("n_spans", ctypes.c_int64),
+                ("k_sel", ctypes.c_int64), ("W_cap", ctypes.c_int64),
+                ("ws_score_select", ctypes.c_size_t), ("ws_window_attend", ctypes.c_size_t),
+                ("ws_decode_step", ctypes.c_size_t)]
+
+
+class Timing(ctypes.Structure):
+    _fields_ = [("score_begin", ctypes.c_void_p), ("score_end", ctypes.c_void_p)]
+
+
+class ReaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        name = STATUS[status] if 0 <= status < len(STATUS) else str(status)
+        super().__init__(f"{name}: {detail}")
+
+
+_lib = None
+
+
+def lib():
+    """Load librea.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          f"`python -m top_kv_cache_amd._build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, A = ctypes.POINTER(Problem), ctypes.POINTER(Params)
+    vp, i32p = ctypes.c_void_p, ctypes.c_void_p
+    L.rea_abi_version.restype = ctypes.c_int
+    L.rea_status_string.restype = ctypes.c_char_p
+    L.rea_status_string.argtypes = [ctypes.c_int]
+    L.rea_last_error.restype = ctypes.c_char_p
+    L.rea_query_sizes.restype = ctypes.c_int
+    L.rea_query_sizes.argtypes = [P, A, ctypes.POINTER(Sizes)]
+    L.rea_score_select.restype = ctypes.c_int
+    L.rea_score_select.argtypes = [P, A, i32p, i32p, vp, vp, ctypes.c_size_t, vp]
+    L.rea_gather_rope.restype = ctypes.c_int
+    L.rea_gather_rope.argtypes = [P, A, i32p, i32p, vp, vp, vp, i32p, ctypes.c_int32, vp]
+    L.rea_window_attend.restype = ctypes.c_int
+    L.rea_window_attend.argtypes = [P, A, vp, vp, vp, i32p, ctypes.c_int32, vp, vp,
+                                    ctypes.c_size_t, vp]
+    L.rea_decode_step.restype = ctypes.c_int
+    L.rea_decode_step.argtypes = [P, A, vp, i32p, i32p, vp, ctypes.c_size_t, vp,
+                                  ctypes.POINTER(Timing)]
+    if L.rea_abi_version() != 1:
+        raise ImportError("librea.so ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise ReaError(status, lib().rea_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# struct builders (plain values; pointers as ints)
+# ---------------------------------------------------------------------------
+def problem(q_ptr, k_ptr, v_ptr, *, dtype, n_q, Hq, Hkv, d, T, stride_head, stride_tok) -> Problem:
+    return Problem(ctypes.sizeof(Problem), dtype, n_q, Hq, Hkv, d, T, q_ptr, k_ptr, v_ptr,
+                   stride_head, stride_tok)
+
+
+def params(G, S, topk, L, block_q=1, rope_theta=500000.0, softmax_scale=0.0) -> Params:
+    return Params(ctypes.sizeof(Params), G, S, topk, L, block_q, rope_theta, softmax_scale, 0)
+
+
+def query_sizes(p: Problem, a: Params) -> Sizes:
+    s = Sizes()
+    _check(lib().rea_query_sizes(ctypes.byref(p), ctypes.byref(a), ctypes.byref(s)))
+    return s
+
+
+# ---------------------------------------------------------------------------
+# torch front end
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def problem_from_tensors(q, k, v, T=None) -> Problem:
+    """q [n_q][Hq][d] contiguous; k, v [Hkv][T_cap][d] with unit channel stride."""
+    torch = _torch()
+    if q.dtype == torch.bfloat16:
+        dt = REA_BF16
+    elif q.dtype == torch.float32:
+        dt = REA_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if k.stride() != v.stride() or k.shape != v.shape or k.stride(2) != 1:
+        raise ValueError("k and v must share shape and strides, channel stride 1")
+    n_q, Hq, d = q.shape
+    Hkv, Tcap, _ = k.shape
+    return problem(q.data_ptr(), k.data_ptr(), v.data_ptr(), dtype=dt, n_q=n_q, Hq=Hq, Hkv=Hkv,
+                   d=d, T=Tcap if T is None else T, stride_head=k.stride(0),
+                   stride_tok=k.stride(1))
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ws(nbytes, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned(buf):
+    off = (-buf.data_ptr()) % 256
+    return buf[off:]
+
+
+class Step:
+    """One layer's call configuration: problem + hyperparameters + sizes."""
+
+    def __init__(self, q, k, v, G, S, topk, L, block_q=1, T=None, rope_theta=500000.0,
+                 softmax_scale=0.0):
+        self.q, self.k, self.v = q, k, v
+        self.prob = problem_from_tensors(q, k, v, T)
+        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale)
+        self.sizes = query_sizes(self.prob, self.par)
+        self.device = q.device
+
+    @property
+    def shape(self):
+        p = self.prob
+        return p.n_q, p.n_q_heads, p.n_kv_heads, p.head_dim
+
+    def score_select(self, span_scores=False, stream=None):
+        torch = _torch()
+        n_q, Hq, Hkv, d = self.shape
+        nb, topk = self.sizes.n_blocks, self.par.topk
+        sel = torch.empty((nb, Hkv, max(topk, 1)), dtype=torch.int32, device=self.device)
+        nsel = torch.empty((nb, Hkv), dtype=torch.int32, device=self.device)
+        sc = (torch.empty((nb, Hkv, max(self.sizes.n_spans, 1)), dtype=torch.float64,
+                          device=self.device) if span_scores else None)
+        ws = _aligned(_ws(self.sizes.ws_score_select, self.device))
+        _check(lib().rea_score_select(ctypes.byref(self.prob), ctypes.byref(self.par),
+                                      _ptr(sel), _ptr(nsel), _ptr(sc), _ptr(ws),
+                                      ws.numel(), _stream(stream)))
+        sel = sel[:, :, :topk]
+        return (sel, nsel, sc[:, :, :self.sizes.n_spans]) if span_scores else (sel, nsel)
+
+    def gather_rope(self, sel, nsel, W_cap=None, stream=None):
+        torch = _torch()
+        n_q, Hq, Hkv, d = self.shape
+        nb = self.sizes.n_blocks
+        W_cap = int(self.sizes.W_cap if W_cap is None else W_cap)
+        k_win = torch.empty((nb, Hkv, max(W_cap, 1), d), dtype=torch.float32, device=self.device)
+        v_win = torch.empty((nb, Hkv, max(W_cap, 1), d), dtype=self.q.dtype, device=self.device)
+        q_rot = torch.empty((n_q, Hq, d), dtype=torch.float32, device=self.device)
+        W = torch.empty((nb, Hkv), dtype=torch.int32, device=self.device)
+        sel_arg = sel.contiguous() if self.par.topk > 0 else None
+        _check(lib().rea_gather_rope(ctypes.byref(self.prob), ctypes.byref(self.par),
+                                     _ptr(sel_arg), _ptr(nsel.contiguous()), _ptr(k_win),
+                                     _ptr(v_win), _ptr(q_rot), _ptr(W), W_cap, _stream(stream)))
+        return k_win, v_win, q_rot, W
+
+    def window_attend(self, q_rot, k_win, v_win, W, stream=None):
+        torch = _torch()
+        n_q, Hq, Hkv, d = self.shape
+        out = torch.empty((n_q, Hq, d), dtype=torch.float32, device=self.device)
+        W_cap = k_win.shape[2]
+        # the size query covers W_cap == sizes.W_cap; scale up for larger buffers
+        ratio = max(1, -(-W_cap // max(self.sizes.W_cap, 1)))
+        ws = _aligned(_ws(self.sizes.ws_window_attend * ratio, self.device))
+        _check(lib().rea_window_attend(ctypes.byref(self.prob), ctypes.byref(self.par), _ptr(q_rot),
+                                       _ptr(k_win), _ptr(v_win), _ptr(W), W_cap, _ptr(out),
+                                       _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+    def workspace(self):
+        return _aligned(_ws(self.sizes.ws_decode_step, self.device))
+
+    def decode_step(self, out=None, sel=None, nsel=None, ws=None, stream=None, timing=None):
+        torch = _torch()
+        n_q, Hq, Hkv, d = self.shape
+        if out is None:
+            out = torch.empty((n_q, Hq, d), dtype=torch.float32, device=self.device)
+        if ws is None:
+            ws = self.workspace()
+        _check(lib().rea_decode_step(ctypes.byref(self.prob), ctypes.byref(self.par), _ptr(out),
+                                     _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel(),
+                                     _stream(stream),
+                                     ctypes.byref(timing) if timing is not None else None))
+        return out

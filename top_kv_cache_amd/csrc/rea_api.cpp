@@ -1,0 +1,337 @@
+// rea_api.cpp - the C ABI declared in include/rea.h: argument validation,
+// size queries, workspace carving and the launch sequences.
+//
+// Validation is pure host code and runs before any HIP call, so every error
+// status is observable on a machine without a GPU.  Nothing here allocates
+// device memory or synchronises: all buffers come from the caller and all
+// kernels are enqueued on the caller's stream.
+#include "rea.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "rea_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rea_status fail(rea_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validate problem + params and derive the geometry.  No HIP call.
+rea_status make_geom(const rea_problem *p, const rea_params *a, rea::Geom *g) {
+    if (!p || !a) return fail(REA_EINVAL, "problem or params is NULL");
+    if (p->struct_size != sizeof(rea_problem))
+        return fail(REA_EINVAL, "rea_problem.struct_size %u != %zu", p->struct_size,
+                    sizeof(rea_problem));
+    if (a->struct_size != sizeof(rea_params))
+        return fail(REA_EINVAL, "rea_params.struct_size %u != %zu", a->struct_size,
+                    sizeof(rea_params));
+    if (p->dtype != REA_BF16 && p->dtype != REA_F32)
+        return fail(REA_EDTYPE, "dtype %d is neither REA_BF16 nor REA_F32", p->dtype);
+    if (!p->q || !p->k || !p->v) return fail(REA_EINVAL, "q, k or v is NULL");
+    if (p->n_q < 1) return fail(REA_ESHAPE, "n_q %d < 1", p->n_q);
+    if (p->n_kv_heads < 1) return fail(REA_ESHAPE, "n_kv_heads %d < 1", p->n_kv_heads);
+    if (p->n_q_heads < 1 || p->n_q_heads % p->n_kv_heads != 0)
+        return fail(REA_ESHAPE, "n_q_heads %d is not a positive multiple of n_kv_heads %d",
+                    p->n_q_heads, p->n_kv_heads);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(REA_EUNSUPPORTED, "head_dim %d: this build implements 64 and 128",
+                    p->head_dim);
+    if (p->T < p->n_q || p->T >= ((int64_t)1 << 31))
+        return fail(REA_ESHAPE, "T %lld must satisfy n_q <= T < 2^31", (long long)p->T);
+    if (a->G < 0 || a->L < 0) return fail(REA_EINVAL, "G %d and L %d must be >= 0", a->G, a->L);
+    if (a->S < 1) return fail(REA_EINVAL, "span size S %d < 1", a->S);
+    if (a->topk < 0) return fail(REA_EINVAL, "topk %d < 0", a->topk);
+    if (a->block_q < 1) return fail(REA_EINVAL, "block_q %d < 1", a->block_q);
+    if (a->reserved != 0) return fail(REA_EINVAL, "rea_params.reserved must be 0");
+    if (!(a->rope_theta > 0.0) || !isfinite(a->rope_theta))
+        return fail(REA_EINVAL, "rope_theta must be finite and > 0");
+    if (!isfinite(a->softmax_scale)) return fail(REA_EINVAL, "softmax_scale is not finite");
+    if (p->n_q % a->block_q != 0)
+        return fail(REA_ESHAPE, "n_q %d is not a multiple of block_q %d", p->n_q, a->block_q);
+    if (p->kv_stride_tok < p->head_dim)
+        return fail(REA_ESHAPE, "kv_stride_tok %lld < head_dim %d", (long long)p->kv_stride_tok,
+                    p->head_dim);
+    if (p->kv_stride_head < p->T * p->kv_stride_tok)
+        return fail(REA_ESHAPE, "kv_stride_head %lld < T * kv_stride_tok",
+                    (long long)p->kv_stride_head);
+
+    const int esize = p->dtype == REA_BF16 ? 2 : 4;
+    if (!aligned(p->q, 16) || !aligned(p->k, 16) || !aligned(p->v, 16))
+        return fail(REA_EALIGN, "q, k and v must be 16-byte aligned");
+    if ((p->kv_stride_tok * esize) % 16 != 0 || (p->kv_stride_head * esize) % 16 != 0)
+        return fail(REA_EALIGN, "kv strides must be multiples of 16 bytes");
+
+    g->dtype = p->dtype;
+    g->esize = esize;
+    g->n_q = p->n_q;
+    g->Hq = p->n_q_heads;
+    g->Hkv = p->n_kv_heads;
+    g->g = p->n_q_heads / p->n_kv_heads;
+    g->d = p->head_dim;
+    g->T = p->T;
+    g->Gp = a->G < p->T ? a->G : p->T;
+    g->Lp = a->L < p->T - g->Gp ? a->L : p->T - g->Gp;
+    g->mid_lo = g->Gp;
+    g->mid_hi = p->T - g->Lp;
+    const int64_t n_mid = g->mid_hi - g->mid_lo;
+    g->n_spans = (n_mid + a->S - 1) / a->S;
+    g->S = a->S;
+    g->topk = a->topk;
+    g->block_q = a->block_q;
+    g->n_blk = p->n_q / a->block_q;
+    g->k_sel = (int)(a->topk < g->n_spans ? a->topk : g->n_spans);
+    g->last_len = g->n_spans > 0 ? (int)(n_mid - (g->n_spans - 1) * a->S) : 0;
+    int64_t wc = g->Gp + (int64_t)g->k_sel * a->S + g->Lp;
+    g->W_cap = wc < p->T ? wc : p->T;
+    g->sh = p->kv_stride_head;
+    g->st = p->kv_stride_tok;
+    g->scale = a->softmax_scale > 0.f ? a->softmax_scale : (float)(1.0 / sqrt((double)g->d));
+    g->theta = a->rope_theta;
+
+    if (n_mid > 0 && p->n_q > g->Lp)
+        return fail(REA_ESHAPE,
+                    "the %d queries must lie in the local region (L' = %lld) unless T <= G + L",
+                    p->n_q, (long long)g->Lp);
+    if ((int64_t)g->n_blk * g->Hkv * (g->n_spans > 0 ? g->n_spans : 1) >= ((int64_t)1 << 40))
+        return fail(REA_EUNSUPPORTED, "too many spans");
+    if (g->block_q > 1 && (size_t)g->block_q * g->d * sizeof(double) > 65536)
+        return fail(REA_EUNSUPPORTED, "block_q %d too large for head_dim %d (needs <= %d)",
+                    g->block_q, g->d, (int)(65536 / (g->d * sizeof(double))));
+    return REA_OK;
+}
+
+struct Carve {
+    char *base;
+    size_t off;
+    template <typename T> T *take(size_t bytes) {
+        T *p = base ? (T *)(base + off) : nullptr;
+        off += align256(bytes);
+        return p;
+    }
+};
+
+size_t score_scores_bytes(const rea::Geom &g) {
+    return (size_t)g.n_blk * g.Hkv * (size_t)g.n_spans * sizeof(double);
+}
+
+size_t decode_ws_bytes(const rea::Geom &g) {
+    Carve c{nullptr, 0};
+    c.take<double>(score_scores_bytes(g));
+    c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
+    c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+    c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+    c.take<float>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * sizeof(float));
+    c.take<char>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * g.esize);
+    c.take<float>((size_t)g.n_q * g.Hq * g.d * sizeof(float));
+    c.take<char>(rea::attend_ws_bytes(g, g.W_cap));
+    return c.off;
+}
+
+rea_status device_ready(int *num_cu) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(REA_ENODEVICE, "no HIP device available");
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(REA_ENODEVICE, "cannot query device %d", dev);
+    }
+    *num_cu = n;
+    return REA_OK;
+}
+
+rea_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(REA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return REA_OK;
+}
+
+rea_status check_ws(void *ws, size_t have, size_t need) {
+    if (need > 0 && !ws) return fail(REA_EWORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (have < need) return fail(REA_EWORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+    if (ws && !aligned(ws, 256)) return fail(REA_EALIGN, "workspace must be 256-byte aligned");
+    return REA_OK;
+}
+
+rea_status check_sel(const rea::Geom &g, const int32_t *sel, const int32_t *n_sel) {
+    if (!n_sel) return fail(REA_EINVAL, "n_sel is NULL");
+    if (g.topk > 0 && !sel) return fail(REA_EINVAL, "sel is NULL while topk > 0");
+    if (!aligned(n_sel, 4) || (sel && !aligned(sel, 4)))
+        return fail(REA_EALIGN, "sel / n_sel must be 4-byte aligned");
+    return REA_OK;
+}
+
+rea_status check_window(const rea::Geom &g, const void *k_win, const void *v_win,
+                        int32_t W_cap) {
+    if (!k_win || !v_win) return fail(REA_EINVAL, "k_win or v_win is NULL");
+    if (!aligned(k_win, 16) || !aligned(v_win, 16))
+        return fail(REA_EALIGN, "k_win and v_win must be 16-byte aligned");
+    if (W_cap < g.W_cap)
+        return fail(REA_ESHAPE, "W_cap %d < %lld (the largest possible window)", W_cap,
+                    (long long)g.W_cap);
+    return REA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rea_abi_version(void) { return REA_ABI_VERSION; }
+
+const char *rea_status_string(int status) {
+    switch (status) {
+    case REA_OK: return "REA_OK";
+    case REA_EINVAL: return "REA_EINVAL";
+    case REA_ESHAPE: return "REA_ESHAPE";
+    case REA_EDTYPE: return "REA_EDTYPE";
+    case REA_EALIGN: return "REA_EALIGN";
+    case REA_EWORKSPACE: return "REA_EWORKSPACE";
+    case REA_ENODEVICE: return "REA_ENODEVICE";
+    case REA_ELAUNCH: return "REA_ELAUNCH";
+    case REA_EUNSUPPORTED: return "REA_EUNSUPPORTED";
+    default: return "REA_UNKNOWN";
+    }
+}
+
+const char *rea_last_error(void) { return g_err; }
+
+rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes *out) {
+    g_err[0] = 0;
+    if (!out) return fail(REA_EINVAL, "out is NULL");
+    rea::Geom g;
+    rea_status st = make_geom(p, a, &g);
+    if (st != REA_OK) return st;
+    out->n_blocks = g.n_blk;
+    out->n_spans = g.n_spans;
+    out->k_sel = g.k_sel;
+    out->W_cap = g.W_cap;
+    out->ws_score_select = align256(score_scores_bytes(g));
+    out->ws_window_attend = rea::attend_ws_bytes(g, g.W_cap);
+    out->ws_decode_step = decode_ws_bytes(g);
+    return REA_OK;
+}
+
+rea_status rea_score_select(const rea_problem *p, const rea_params *a, int32_t *sel,
+                            int32_t *n_sel, double *span_scores, void *ws, size_t ws_bytes,
+                            void *stream) {
+    g_err[0] = 0;
+    rea::Geom g;
+    rea_status st = make_geom(p, a, &g);
+    if (st != REA_OK) return st;
+    if ((st = check_sel(g, sel, n_sel)) != REA_OK) return st;
+    if (span_scores && !aligned(span_scores, 8))
+        return fail(REA_EALIGN, "span_scores must be 8-byte aligned");
+    const size_t need = span_scores ? 0 : align256(score_scores_bytes(g));
+    if ((st = check_ws(ws, ws_bytes, need)) != REA_OK) return st;
+    int num_cu = 0;
+    if ((st = device_ready(&num_cu)) != REA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    double *scores = span_scores ? span_scores : (double *)ws;
+    if ((st = launched(rea::launch_score(g, p->q, p->k, scores, num_cu, s), "score")) != REA_OK)
+        return st;
+    return launched(rea::launch_topk(g, scores, sel, n_sel, s), "topk");
+}
+
+rea_status rea_gather_rope(const rea_problem *p, const rea_params *a, const int32_t *sel,
+                           const int32_t *n_sel, float *k_win, void *v_win, float *q_rot,
+                           int32_t *W, int32_t W_cap, void *stream) {
+    g_err[0] = 0;
+    rea::Geom g;
+    rea_status st = make_geom(p, a, &g);
+    if (st != REA_OK) return st;
+    if ((st = check_sel(g, sel, n_sel)) != REA_OK) return st;
+    if ((st = check_window(g, k_win, v_win, W_cap)) != REA_OK) return st;
+    if (!q_rot || !W) return fail(REA_EINVAL, "q_rot or W is NULL");
+    if (!aligned(q_rot, 16) || !aligned(W, 4)) return fail(REA_EALIGN, "q_rot / W misaligned");
+    int num_cu = 0;
+    if ((st = device_ready(&num_cu)) != REA_OK) return st;
+    return launched(rea::launch_gather_rope(g, p->k, p->v, p->q, sel, n_sel, k_win, v_win,
+                                            q_rot, W, W_cap, (hipStream_t)stream),
+                    "gather_rope");
+}
+
+rea_status rea_window_attend(const rea_problem *p, const rea_params *a, const float *q_rot,
+                             const float *k_win, const void *v_win, const int32_t *W,
+                             int32_t W_cap, float *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+    g_err[0] = 0;
+    rea::Geom g;
+    rea_status st = make_geom(p, a, &g);
+    if (st != REA_OK) return st;
+    if ((st = check_window(g, k_win, v_win, W_cap)) != REA_OK) return st;
+    if (!q_rot || !W || !out) return fail(REA_EINVAL, "q_rot, W or out is NULL");
+    if (!aligned(q_rot, 16) || !aligned(W, 4) || !aligned(out, 16))
+        return fail(REA_EALIGN, "q_rot / W / out misaligned");
+    if ((st = check_ws(ws, ws_bytes, rea::attend_ws_bytes(g, W_cap))) != REA_OK) return st;
+    int num_cu = 0;
+    if ((st = device_ready(&num_cu)) != REA_OK) return st;
+    return launched(rea::launch_attend(g, q_rot, k_win, v_win, W, W_cap, out, ws,
+                                       (hipStream_t)stream),
+                    "window_attend");
+}
+
+rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out,
+                           int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes,
+                           void *stream, const rea_timing *timing) {
+    g_err[0] = 0;
+    rea::Geom g;
+    rea_status st = make_geom(p, a, &g);
+    if (st != REA_OK) return st;
+    if (!out) return fail(REA_EINVAL, "out is NULL");
+    if (!aligned(out, 16)) return fail(REA_EALIGN, "out must be 16-byte aligned");
+    if ((sel && !aligned(sel, 4)) || (n_sel && !aligned(n_sel, 4)))
+        return fail(REA_EALIGN, "sel / n_sel must be 4-byte aligned");
+    if ((st = check_ws(ws, ws_bytes, decode_ws_bytes(g))) != REA_OK) return st;
+    int num_cu = 0;
+    if ((st = device_ready(&num_cu)) != REA_OK) return st;
+
+    Carve c{(char *)ws, 0};
+    double *scores = c.take<double>(score_scores_bytes(g));
+    int32_t *ws_sel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
+    int32_t *ws_nsel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+    int32_t *Wlen = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+    float *k_win = c.take<float>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * sizeof(float));
+    void *v_win = c.take<char>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * g.esize);
+    float *q_rot = c.take<float>((size_t)g.n_q * g.Hq * g.d * sizeof(float));
+    void *att_ws = c.take<char>(rea::attend_ws_bytes(g, g.W_cap));
+    int32_t *use_sel = sel ? sel : ws_sel;
+    int32_t *use_nsel = n_sel ? n_sel : ws_nsel;
+    if (g.topk == 0) use_sel = sel;   // may be NULL: nothing is selected
+
+    hipStream_t s = (hipStream_t)stream;
+    if (timing && timing->score_begin) {
+        if (hipEventRecord((hipEvent_t)timing->score_begin, s) != hipSuccess)
+            return launched(hipGetLastError(), "event record");
+    }
+    if ((st = launched(rea::launch_score(g, p->q, p->k, scores, num_cu, s), "score")) != REA_OK)
+        return st;
+    if (timing && timing->score_end) {
+        if (hipEventRecord((hipEvent_t)timing->score_end, s) != hipSuccess)
+            return launched(hipGetLastError(), "event record");
+    }
+    if ((st = launched(rea::launch_topk(g, scores, use_sel, use_nsel, s), "topk")) != REA_OK)
+        return st;
+    if ((st = launched(rea::launch_gather_rope(g, p->k, p->v, p->q, use_sel, use_nsel, k_win,
+                                               v_win, q_rot, Wlen, g.W_cap, s),
+                       "gather_rope")) != REA_OK)
+        return st;
+    return launched(rea::launch_attend(g, q_rot, k_win, v_win, Wlen, g.W_cap, out, att_ws, s),
+                    "window_attend");
+}
+
+}  // extern "C"

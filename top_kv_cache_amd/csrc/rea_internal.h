@@ -1,0 +1,52 @@
+// rea_internal.h - declarations shared by the host API (rea_api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rea {
+
+// Validated geometry of one call (all values derived on the host).
+struct Geom {
+    int dtype;          // 0 bf16, 1 f32
+    int esize;          // bytes per stored element
+    int n_q, Hq, Hkv, g, d;
+    int64_t T;
+    int64_t Gp, Lp;     // G' = min(G,T), L' = min(L, T-G')
+    int64_t mid_lo, mid_hi;
+    int64_t n_spans;    // ceil((mid_hi - mid_lo) / S)
+    int S, topk, block_q, n_blk;
+    int k_sel;          // min(topk, n_spans)
+    int last_len;       // length of span n_spans-1 (S unless the middle is ragged)
+    int64_t W_cap;      // min(T, G' + k_sel*S + L')
+    int64_t sh, st;     // K/V strides (elements) per head / per token
+    float scale;        // softmax scale
+    double theta;       // RoPE base
+};
+
+constexpr int kMaxHalfDim = 64;   // head_dim <= 128
+
+// ---- launchers (each returns hipGetLastError() of its launches) ----------
+
+// Step 1a: span scores [n_blk][Hkv][n_spans] (double).
+hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
+                        int num_cu, hipStream_t s);
+
+// Step 1b: top-k per (block, KV head).
+hipError_t launch_topk(const Geom &g, const double *span_scores, int32_t *sel, int32_t *n_sel,
+                       hipStream_t s);
+
+// Steps 2-3: window rows (K rotated fp32, V copied) + lengths, then the queries.
+hipError_t launch_gather_rope(const Geom &g, const void *k, const void *v, const void *q,
+                              const int32_t *sel, const int32_t *n_sel, float *k_win,
+                              void *v_win, float *q_rot, int32_t *W, int64_t W_cap,
+                              hipStream_t s);
+
+// Step 4: split-window attention + combine.
+size_t attend_ws_bytes(const Geom &g, int64_t W_cap);
+hipError_t launch_attend(const Geom &g, const float *q_rot, const float *k_win,
+                         const void *v_win, const int32_t *W, int64_t W_cap, float *out,
+                         void *ws, hipStream_t s);
+
+}  // namespace rea
