@@ -1,0 +1,213 @@
+"""Benchmark: ReAttention decode step on one MI355X.
+
+Default workload: LLaMA3-8B-shaped decode at a 1,048,576-token context with all
+32 layers' K/V resident in HBM (bf16, 32 q heads / 8 KV heads, d 128; G 32,
+S 32, top-k 120, L 4096).  One step = rea_decode_step for each of the 32
+layers (score + select + gather/RoPE + window attention), inputs resident
+before the timed region.
+
+Prints one JSON line:  value = middle-cache keys scored per second over the
+whole step; ms_per_step = decode-step latency; roofline = the scoring kernel's
+achieved HBM bandwidth from HIP events recorded around each of its launches on
+the launch stream; cpu_baseline = the CPU oracle on one layer of the same
+workload.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "middle-cache keys scored/s (achieved HBM GB/s) + decode-step latency @1M ctx"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_decode_llama8b_1m_traffic.json")
+SCORE_SRC = os.path.join(ROOT, "top_kv_cache_amd", "csrc", "score.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events on the launch stream)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.L.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(e)
+
+
+def traffic_for(score_bytes):
+    """Measured HBM traffic per scoring launch from the committed rocprofv3 PMC
+    summary, if it was taken on the current scoring kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+        if t.get("score_src_sha256") != src:
+            return None
+        return t["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(w):
+    """The oracle, as it stands, on one layer (all KV heads) of the workload."""
+    import numpy as np
+    import oracle.rea_oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    q64 = synth.to_f32(w.q(0), w.dtype).astype(np.float64)
+    g = w.g
+    total = 0.0
+    for h in range(w.Hkv):
+        K = synth.to_f32(w.kv(0, "k", h, h + 1), w.dtype).astype(np.float64)
+        V = synth.to_f32(w.kv(0, "v", h, h + 1), w.dtype).astype(np.float64)
+        t0 = time.perf_counter()
+        O.step(q64[:, h * g:(h + 1) * g], K, V, w.G, w.S, w.topk, w.L, w.block_q, w.rope_theta)
+        total += time.perf_counter() - t0
+        del K, V
+    lo, hi = w.mid
+    keys = (hi - lo) * w.Hkv
+    return {"value": keys / total, "unit": "keys/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"layer 0 of {w.n_layers}, all {w.Hkv} KV heads: one layer's full decode "
+                      f"step (score, select, gather+RoPE, attend) in fp64 numpy, "
+                      f"{total:.1f} s; input generation not timed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload number (default: 1M x 32 layers)")
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (exploration only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              f"(the path is measured on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import top_kv_cache_amd as rea
+    from synth import torch_io
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rea.lib()                                   # fails loudly if the library is missing
+    w = synth.config(args.config)
+    n_layers = args.layers or w.n_layers
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: {n_layers} layers, T={w.T}, Hq={w.Hq}, Hkv={w.Hkv}, "
+        f"d={w.d}, G={w.G} S={w.S} k={w.topk} L={w.L}")
+
+    t_gen = time.perf_counter()
+    steps_l, outs = [], []
+    for layer in range(n_layers):
+        q = torch_io.q_device(w, layer, dev)
+        K = torch_io.kv_device(w, layer, "k", device=dev)
+        V = torch_io.kv_device(w, layer, "v", device=dev)
+        steps_l.append(rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta))
+        outs.append(torch.empty((w.n_q, w.Hq, w.d), dtype=torch.float32, device=dev))
+        if layer % 4 == 3 or layer == n_layers - 1:
+            log(f"[bench] generated + uploaded layer {layer + 1}/{n_layers} "
+                f"({time.perf_counter() - t_gen:.0f} s)")
+    ws = steps_l[0].workspace()
+    stream = torch.cuda.current_stream()
+    hip = Hip()
+
+    def one_step(timing=None):
+        for li, st in enumerate(steps_l):
+            st.decode_step(out=outs[li], ws=ws, stream=stream,
+                           timing=timing[li] if timing is not None else None)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, HIP events around every scoring launch
+    ev = [[(hip.event(), hip.event()) for _ in steps_l] for _ in range(args.steps)]
+    timings = [[rea.Timing(b.value, e.value) for (b, e) in row] for row in ev]
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(e0, stream.cuda_stream)
+    for s in range(args.steps):
+        one_step(timings[s])
+    hip.record(e1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = hip.elapsed_ms(e0, e1)
+    k1 = [hip.elapsed_ms(b, e) for row in ev for (b, e) in row]
+    for row in ev:
+        for (b, e) in row:
+            hip.destroy(b)
+            hip.destroy(e)
+
+    lo, hi = w.mid
+    keys_per_layer = (hi - lo) * w.Hkv
+    ms_per_step = total_ms / args.steps
+    value = keys_per_layer * n_layers / (ms_per_step / 1e3)
+    k1_ms = sum(k1) / len(k1)
+    score_bytes = (keys_per_layer * w.d * (2 if w.dtype == "bf16" else 4)
+                   + w.n_spans * w.Hkv * 8 + w.Hq * w.d * (2 if w.dtype == "bf16" else 4))
+    achieved = score_bytes / (k1_ms / 1e3) / 1e9
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
+        f"scoring kernel {k1_ms * 1e3:.1f} us/launch = {achieved:.0f} GB/s "
+        f"({achieved / HBM_PEAK_GBS * 100:.1f}% of {HBM_PEAK_GBS:.0f}), "
+        f"{value / 1e9:.2f} G keys/s")
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": w.name, "layers": n_layers, "context": w.T, "batch": 1,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "storage": w.dtype,
+                   "G": w.G, "S": w.S, "topk": w.topk, "L": w.L,
+                   "needles_per_kv_head": w.needles, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(score_bytes),
+                     "kernel": "k_score_decode", "algorithmic_bytes_per_launch": score_bytes,
+                     "avg_launch_us": k1_ms * 1e3},
+        "cpu_baseline": None,
+    }
+    del steps_l, outs, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one layer ...")
+        res["cpu_baseline"] = cpu_baseline(w)
+        log(f"[bench] oracle: {res['cpu_baseline']['value'] / 1e6:.2f} M keys/s")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -62,8 +62,8 @@ def test_exact_ties_lower_index_wins():
     both sides, so the lower-index rule must be reproduced bit-exactly."""
     rng = np.random.default_rng(1234)
     w = S(Hq=4, Hkv=2, d=64, T=1200, S=16, topk=11, L=64, needles=0)
-    qn = rng.integers(-1, 2, size=(1, w.Hq, w.d)).astype(np.float32)
-    Kn = rng.integers(-2, 3, size=(w.Hkv, w.T, w.d)).astype(np.float32)
+    qn = rng.integers(0, 2, size=(1, w.Hq, w.d)).astype(np.float32)
+    Kn = rng.integers(0, 2, size=(w.Hkv, w.T, w.d)).astype(np.float32)
     Kn[:, 200:260] = Kn[:, 300:360]           # duplicated spans -> equal scores
     Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
     to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
@@ -72,14 +72,16 @@ def test_exact_ties_lower_index_wins():
     q, K, V = to_bf(qn), to_bf(Kn), to_bf(Vn)
     gpu = run_library(w, q, K, V)
     q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
-    n_ties = 0
+    split_groups = 0
     for h in range(w.Hkv):
         ora = oracle_head(w, 0, h, q64, K64[h:h + 1], V64[h:h + 1])
         sc = ora["sc"][0]
         kth = np.sort(sc)[::-1][w.topk - 1]
-        n_ties += int((sc == kth).sum())
+        above, tied = int((sc > kth).sum()), int((sc == kth).sum())
+        log(f"  head {h}: {above} above the k-th score, {tied} tied at it")
+        split_groups += above < w.topk < above + tied
         compare_head(w, gpu, ora, h)
-    assert n_ties > 2 * w.Hkv       # the case really exercises the tie rule
+    assert split_groups >= 1       # the k-th boundary cuts through a tie group
 
 
 def test_deterministic():
