@@ -6,18 +6,24 @@
 // first, equal scores -> lower span index first.  The selection is emitted in
 // ascending span order, which is the order the spans take in the window.
 //
-// Algorithm (one 1024-thread workgroup per (block, KV head); scores are read
-// from L2, never sorted):
-//   1. find the cutoff element e* = the k-th best under (score desc, index
-//      asc).  Candidates start as all spans; each level takes min/max of the
-//      candidates, histograms them into 4096 equal-width bins, keeps the bin
-//      that holds the k-th best and counts the candidates above it.  Once at
-//      most 2048 candidates remain they are ranked exactly in LDS; if they are
-//      all equal, e* is the right one of them by index order.
-//   2. span j is selected iff score_j > score* or (score_j == score* and
-//      j <= j*); a block-wide ordered compaction writes the indices ascending.
-// Binning uses floor((x - min) * (4096 / (max - min))) in fp64, which is
-// monotone in x, so no element can land in a bin out of order.
+// One 512-thread workgroup per (block, KV head).  Fast path (n <= 65536
+// spans), three coalesced passes over the span scores in L2:
+//   1. maxima of groups of 32 consecutive spans -> LDS.  The k-th largest
+//      group maximum tau is a lower bound of the k-th largest score (the k
+//      best groups hold k distinct scores >= tau), so every selected span has
+//      score >= tau.
+//   2. spans with score >= tau are appended to LDS (at most 8192 fit).
+//   3. the cutoff e* (the k-th best under score desc, index asc) is found in
+//      LDS by histogram levels over the candidates; span j is selected iff
+//      score_j > score* or (score_j == score* and j <= j*); a bitmap over the
+//      spans and one block scan write the indices in ascending order.
+// Histogram level: 2048 equal-width bins between the candidates' min and max,
+// bin = floor((x - min) * (2048 / (max - min))) in fp64 -- monotone in x, so
+// bins are ordered; only the bin holding the k-th best survives.  Once all
+// survivors share one score the order is by index, so the level key becomes
+// the negated index.  At most 256 survivors are ranked pairwise.
+// Larger inputs, or more than 8192 spans at or above the bound, take a generic
+// path that makes the same decisions with global-memory passes.
 #include "rea_internal.h"
 
 #include <math.h>
@@ -25,72 +31,367 @@
 namespace rea {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 4096;
-constexpr int kCap = 2048;
-constexpr int kMaxLevels = 12;
+constexpr int kGroup = 32;
+constexpr int kMaxGroups = 2048;
+constexpr int64_t kFastN = (int64_t)kGroup * kMaxGroups;   // 65536
+constexpr int kCandCap = 8192;
+constexpr int kPerThread = kCandCap / kThreads;             // 16
+constexpr int kBins = 2048;
+constexpr int kRankMax = 256;
+constexpr int kBatch = 8;
 
-struct TopkShared {
+struct FastShared {
+    double val[kCandCap];
+    int32_t idx[kCandCap];
+    double gval[kMaxGroups];
+    int32_t gidx[kMaxGroups];
     uint32_t hist[kBins];
-    double cand_v[kCap];
-    int32_t cand_j[kCap];
-    double lev_mn[kMaxLevels];
-    double lev_inv[kMaxLevels];
-    int32_t lev_bin[kMaxLevels];
+    uint32_t bitmap[kFastN / 32];
+};
+
+// generic path state
+constexpr int kGBins = 4096;
+constexpr int kGCap = 2048;
+constexpr int kGMaxLevels = 12;
+struct GenericShared {
+    uint32_t hist[kGBins];
+    double cand_v[kGCap];
+    int32_t cand_j[kGCap];
+    double lev_mn[kGMaxLevels];
+    double lev_inv[kGMaxLevels];
+    int32_t lev_bin[kGMaxLevels];
+};
+
+struct Common {
     double red_d[2][kWaves];
     uint32_t red_u[kWaves];
     uint32_t scan[kWaves + 1];
-    uint32_t n_cand;
+    uint32_t count;
+    uint32_t above;
+    int32_t bstar;
+    int32_t found;
     int32_t cut_j;
     double cut_v;
-    int32_t found;
 };
 
-__device__ __forceinline__ int bin_of(double x, double mn, double inv) {
+__device__ __forceinline__ int bin_of(double x, double mn, double inv, int nbins) {
     const double f = floor((x - mn) * inv);
-    if (!(f > 0.0)) return 0;                      // also x == mn with inv == inf
-    if (f >= (double)(kBins - 1)) return kBins - 1;
+    if (!(f > 0.0)) return 0;                       // also x == mn with inv == inf
+    if (f >= (double)(nbins - 1)) return nbins - 1;
     return (int)f;
 }
 
-__device__ __forceinline__ bool is_candidate(const TopkShared &sh, int nlev, double x) {
-    for (int l = 0; l < nlev; ++l) {
-        if (x < sh.lev_mn[l]) return false;
-        if (bin_of(x, sh.lev_mn[l], sh.lev_inv[l]) != sh.lev_bin[l]) return false;
+// Workgroup min / max / sum; every thread gets the results.
+__device__ __forceinline__ void block_minmax_count(Common &cm, double &mn, double &mx, uint32_t &cnt) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fmin(mn, __shfl_xor(mn, o));
+        mx = fmax(mx, __shfl_xor(mx, o));
+        cnt += __shfl_xor(cnt, o);
     }
-    return true;
+    if (lane == 0) {
+        cm.red_d[0][wave] = mn;
+        cm.red_d[1][wave] = mx;
+        cm.red_u[wave] = cnt;
+    }
+    __syncthreads();
+    mn = INFINITY;
+    mx = -INFINITY;
+    cnt = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        mn = fmin(mn, cm.red_d[0][w]);
+        mx = fmax(mx, cm.red_d[1][w]);
+        cnt += cm.red_u[w];
+    }
+    __syncthreads();
 }
 
-// Exclusive prefix of `flag` over the workgroup in thread order; returns the
-// prefix and writes the total to *total.  All threads must call it.
-__device__ uint32_t block_excl_scan(TopkShared &sh, bool flag, uint32_t *total) {
+// Exclusive prefix sum of v over the workgroup in thread order.
+__device__ __forceinline__ uint32_t block_excl_sum(Common &cm, uint32_t v, uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const unsigned long long m = __ballot(flag);
-    const uint32_t in_wave = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) sh.red_u[wave] = (uint32_t)__popcll(m);
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) cm.red_u[wave] = x;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t acc = 0;
         for (int w = 0; w < kWaves; ++w) {
-            sh.scan[w] = acc;
-            acc += sh.red_u[w];
+            cm.scan[w] = acc;
+            acc += cm.red_u[w];
         }
-        sh.scan[kWaves] = acc;
+        cm.scan[kWaves] = acc;
     }
     __syncthreads();
-    const uint32_t r = sh.scan[wave] + in_wave;
-    *total = sh.scan[kWaves];
+    const uint32_t r = cm.scan[wave] + x - v;
+    *total = cm.scan[kWaves];
     __syncthreads();
     return r;
 }
+
+// Wave 0 finds the bin holding the need-th best (bins counted from the top);
+// sets cm.bstar and cm.above (candidates in higher bins).
+__device__ __forceinline__ void find_bin(Common &cm, const uint32_t *hist, int nbins, int64_t need) {
+    const int lane = threadIdx.x & 63;
+    if ((threadIdx.x >> 6) == 0) {
+        const int bpl = nbins / 64;
+        uint32_t own = 0;
+        for (int i = 0; i < bpl; ++i) own += hist[lane * bpl + i];
+        uint32_t suf = own;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_down(suf, o);
+            if (lane + o < 64) suf += y;
+        }
+        const uint32_t after = suf - own;
+        if ((int64_t)after < need && need <= (int64_t)suf) {
+            uint32_t above = after;
+            int b = lane * bpl + bpl - 1;
+            for (; b > lane * bpl; --b) {
+                if ((int64_t)(above + hist[b]) >= need) break;
+                above += hist[b];
+            }
+            cm.bstar = b;
+            cm.above = above;
+        }
+    }
+    __syncthreads();
+}
+
+// The need-th best of `count` (<= kCandCap) LDS entries (val, idx) under
+// (val desc, idx asc); result in cm.cut_v / cm.cut_j.  Reorders and shrinks
+// the arrays.
+__device__ __forceinline__ void find_kth(Common &cm, uint32_t *hist, double *val, int32_t *idx,
+                         uint32_t count, int64_t need) {
+    const int tid = threadIdx.x;
+    bool by_index = false;
+    for (;;) {
+        if (count <= (uint32_t)kRankMax) {
+            for (uint32_t c = tid; c < count; c += kThreads) {
+                const double x = val[c];
+                const int32_t jc = idx[c];
+                int64_t rank = 0;
+                for (uint32_t o = 0; o < count; ++o) {
+                    const double y = val[o];
+                    rank += (y > x) || (y == x && idx[o] < jc);
+                }
+                if (rank == need - 1) {
+                    cm.cut_v = x;
+                    cm.cut_j = jc;
+                }
+            }
+            __syncthreads();
+            return;
+        }
+        double mn = INFINITY, mx = -INFINITY;
+        uint32_t dummy = 0;
+        for (uint32_t c = tid; c < count; c += kThreads) {
+            const double k = by_index ? -(double)idx[c] : val[c];
+            mn = fmin(mn, k);
+            mx = fmax(mx, k);
+        }
+        block_minmax_count(cm, mn, mx, dummy);
+        if (mn == mx) {          // every survivor has this score: order by index
+            by_index = true;
+            continue;
+        }
+        const double inv = (double)kBins / (mx - mn);
+        for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
+        __syncthreads();
+        for (uint32_t c = tid; c < count; c += kThreads) {
+            const double k = by_index ? -(double)idx[c] : val[c];
+            atomicAdd(&hist[bin_of(k, mn, inv, kBins)], 1u);
+        }
+        __syncthreads();
+        find_bin(cm, hist, kBins, need);
+        const int bstar = cm.bstar;
+        need -= cm.above;
+        // keep the survivors (bin == bstar)
+        double rv[kPerThread];
+        int32_t ri[kPerThread];
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+            const uint32_t c = tid + (uint32_t)e * kThreads;
+            rv[e] = c < count ? val[c] : 0.0;
+            ri[e] = c < count ? idx[c] : -1;
+        }
+        if (tid == 0) cm.count = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+            const uint32_t c = tid + (uint32_t)e * kThreads;
+            if (c < count) {
+                const double k = by_index ? -(double)ri[e] : rv[e];
+                if (bin_of(k, mn, inv, kBins) == bstar) {
+                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    val[slot] = rv[e];
+                    idx[slot] = ri[e];
+                }
+            }
+        }
+        __syncthreads();
+        count = cm.count;
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// generic path: the same decisions with global-memory passes (any n)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool g_candidate(const GenericShared &gs, int nlev, double x) {
+    for (int l = 0; l < nlev; ++l) {
+        if (x < gs.lev_mn[l]) return false;
+        if (bin_of(x, gs.lev_mn[l], gs.lev_inv[l], kGBins) != gs.lev_bin[l]) return false;
+    }
+    return true;
+}
+
+__device__ __forceinline__ void generic_cutoff(Common &cm, GenericShared &gs, const double *sc, int64_t n,
+                               int64_t need) {
+    const int tid = threadIdx.x;
+    int nlev = 0;
+    for (;;) {
+        double mn = INFINITY, mx = -INFINITY;
+        uint32_t cnt = 0;
+        for (int64_t j = tid; j < n; j += kThreads) {
+            const double x = sc[j];
+            if (g_candidate(gs, nlev, x)) {
+                mn = fmin(mn, x);
+                mx = fmax(mx, x);
+                ++cnt;
+            }
+        }
+        block_minmax_count(cm, mn, mx, cnt);
+        if (cnt <= (uint32_t)kGCap) {
+            if (tid == 0) cm.count = 0;
+            __syncthreads();
+            for (int64_t j = tid; j < n; j += kThreads) {
+                const double x = sc[j];
+                if (g_candidate(gs, nlev, x)) {
+                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    gs.cand_v[slot] = x;
+                    gs.cand_j[slot] = (int32_t)j;
+                }
+            }
+            __syncthreads();
+            const uint32_t m = cm.count;
+            for (uint32_t c = tid; c < m; c += kThreads) {
+                const double x = gs.cand_v[c];
+                const int32_t jc = gs.cand_j[c];
+                int64_t rank = 0;
+                for (uint32_t o = 0; o < m; ++o) {
+                    const double y = gs.cand_v[o];
+                    rank += (y > x) || (y == x && gs.cand_j[o] < jc);
+                }
+                if (rank == need - 1) {
+                    cm.cut_v = x;
+                    cm.cut_j = jc;
+                }
+            }
+            __syncthreads();
+            return;
+        }
+        if (mn == mx || nlev == kGMaxLevels) {
+            // equal scores (or an extreme dynamic range): walk the candidates in
+            // index order; equal scores are ordered by index, others are ranked
+            // against all candidates
+            if (tid == 0) cm.found = 0;
+            __syncthreads();
+            uint32_t before = 0;
+            for (int64_t base = 0; base < n; base += kThreads) {
+                const int64_t j = base + tid;
+                bool f = false;
+                double x = 0.0;
+                if (j < n) {
+                    x = sc[j];
+                    f = g_candidate(gs, nlev, x);
+                }
+                if (mn != mx && f) {
+                    int64_t rank = 0;
+                    for (int64_t o = 0; o < n; ++o) {
+                        const double y = sc[o];
+                        rank += g_candidate(gs, nlev, y) && (y > x || (y == x && o < j));
+                    }
+                    if (rank == need - 1) {
+                        cm.cut_v = x;
+                        cm.cut_j = (int32_t)j;
+                        cm.found = 1;
+                    }
+                }
+                uint32_t tot;
+                const uint32_t pre = block_excl_sum(cm, f ? 1u : 0u, &tot);
+                if (mn == mx && f && before + pre == (uint32_t)(need - 1)) {
+                    cm.cut_v = x;
+                    cm.cut_j = (int32_t)j;
+                    cm.found = 1;
+                }
+                before += tot;
+                __syncthreads();
+                if (cm.found) break;
+            }
+            __syncthreads();
+            return;
+        }
+        const double inv = (double)kGBins / (mx - mn);
+        for (int i = tid; i < kGBins; i += kThreads) gs.hist[i] = 0u;
+        __syncthreads();
+        for (int64_t j = tid; j < n; j += kThreads) {
+            const double x = sc[j];
+            if (g_candidate(gs, nlev, x)) atomicAdd(&gs.hist[bin_of(x, mn, inv, kGBins)], 1u);
+        }
+        __syncthreads();
+        find_bin(cm, gs.hist, kGBins, need);
+        if (tid == 0) {
+            gs.lev_mn[nlev] = mn;
+            gs.lev_inv[nlev] = inv;
+            gs.lev_bin[nlev] = cm.bstar;
+        }
+        need -= cm.above;
+        ++nlev;
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ void generic_emit(Common &cm, const double *sc, int64_t n, int32_t *sel, int topk) {
+    const double cv = cm.cut_v;
+    const int64_t cj = cm.cut_j;
+    uint32_t written = 0;
+    for (int64_t base = 0; base < n; base += kThreads) {
+        const int64_t j = base + threadIdx.x;
+        bool f = false;
+        if (j < n) {
+            const double x = sc[j];
+            f = x > cv || (x == cv && j <= cj);
+        }
+        uint32_t tot;
+        const uint32_t pre = block_excl_sum(cm, f ? 1u : 0u, &tot);
+        if (f && written + pre < (uint32_t)topk) sel[written + pre] = (int32_t)j;
+        written += tot;
+    }
+}
+
+// Loads batch e0..e0+kBatch-1 of rows (element j = row*kThreads + tid).
+#define LOAD_ROWS(x, e0)                                                    \
+    _Pragma("unroll") for (int i_ = 0; i_ < kBatch; ++i_) {                  \
+        const int64_t j_ = ((e0) + i_) * kThreads + tid;                     \
+        x[i_] = j_ < n ? sc[j_] : -INFINITY;                                 \
+    }
 
 __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ scores_all,
                                                    int64_t n, int kk, int topk,
                                                    int32_t *__restrict__ sel_all,
                                                    int32_t *__restrict__ nsel_all) {
-    __shared__ TopkShared sh;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ Common cm;
+    __shared__ union {
+        FastShared f;
+        GenericShared g;
+    } u;
+    const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
     const double *sc = scores_all + bh * n;
     int32_t *sel = sel_all ? sel_all + bh * topk : nullptr;
@@ -102,158 +403,109 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
         return;
     }
 
-    int nlev = 0;
-    int64_t need = kk;              // rank (1-based) of e* among current candidates
-    for (;;) {
-        // min / max / count over the candidates
-        double mn = INFINITY, mx = -INFINITY;
-        uint32_t cnt = 0;
-        for (int64_t j = tid; j < n; j += kThreads) {
-            const double x = sc[j];
-            if (is_candidate(sh, nlev, x)) {
-                mn = fmin(mn, x);
-                mx = fmax(mx, x);
-                ++cnt;
+    if (n <= kFastN) {
+        FastShared &f = u.f;
+        const int64_t m = (n + kGroup - 1) / kGroup;
+        const int64_t rows = (n + kThreads - 1) / kThreads;
+        // 1. group maxima: lanes 0-31 / 32-63 of a wave hold one group per row
+        for (int64_t e0 = 0; e0 < rows; e0 += kBatch) {
+            double x[kBatch];
+            LOAD_ROWS(x, e0)
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                double gm = x[i];
+                for (int o = 16; o > 0; o >>= 1) gm = fmax(gm, __shfl_xor(gm, o));
+                const int64_t grp = ((e0 + i) * kThreads + tid) / kGroup;
+                if ((tid & (kGroup - 1)) == 0 && grp < m) {
+                    f.gval[grp] = gm;
+                    f.gidx[grp] = (int32_t)grp;
+                }
             }
-        }
-        for (int o = 32; o > 0; o >>= 1) {
-            mn = fmin(mn, __shfl_xor(mn, o));
-            mx = fmax(mx, __shfl_xor(mx, o));
-            cnt += __shfl_xor(cnt, o);
-        }
-        if (lane == 0) {
-            sh.red_d[0][wave] = mn;
-            sh.red_d[1][wave] = mx;
-            sh.red_u[wave] = cnt;
         }
         __syncthreads();
-        mn = INFINITY;
-        mx = -INFINITY;
-        cnt = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            mn = fmin(mn, sh.red_d[0][w]);
-            mx = fmax(mx, sh.red_d[1][w]);
-            cnt += sh.red_u[w];
+        // 2. tau = kk-th largest group maximum (all spans compete if kk > m)
+        double tau = -INFINITY;
+        if (kk <= m) {
+            find_kth(cm, f.hist, f.gval, f.gidx, (uint32_t)m, kk);
+            tau = cm.cut_v;
+        }
+        // 3. candidates: score >= tau
+        if (tid == 0) cm.count = 0;
+        __syncthreads();
+        for (int64_t e0 = 0; e0 < rows; e0 += kBatch) {
+            double x[kBatch];
+            LOAD_ROWS(x, e0)
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int64_t j = (e0 + i) * kThreads + tid;
+                if (j < n && x[i] >= tau) {
+                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    if (slot < (uint32_t)kCandCap) {
+                        f.val[slot] = x[i];
+                        f.idx[slot] = (int32_t)j;
+                    }
+                }
+            }
         }
         __syncthreads();
-
-        if (cnt <= (uint32_t)kCap) {
-            // gather the candidates and rank them exactly in LDS
-            if (tid == 0) sh.n_cand = 0;
+        const uint32_t count = cm.count;
+        __syncthreads();
+        if (count <= (uint32_t)kCandCap) {
+            find_kth(cm, f.hist, f.val, f.idx, count, kk);
+            // 4. bitmap of the selected spans, then ordered compaction
+            const double cv = cm.cut_v;
+            const int64_t cj = cm.cut_j;
+            const int nwords = (int)((n + 31) / 32);
+            for (int i = tid; i < nwords; i += kThreads) f.bitmap[i] = 0u;
             __syncthreads();
-            for (int64_t j = tid; j < n; j += kThreads) {
-                const double x = sc[j];
-                if (is_candidate(sh, nlev, x)) {
-                    const uint32_t slot = atomicAdd(&sh.n_cand, 1u);
-                    sh.cand_v[slot] = x;
-                    sh.cand_j[slot] = (int32_t)j;
-                }
-            }
-            __syncthreads();
-            const int m = (int)sh.n_cand;
-            for (int c = tid; c < m; c += kThreads) {
-                const double v = sh.cand_v[c];
-                const int32_t jc = sh.cand_j[c];
-                int rank = 0;
-                for (int o = 0; o < m; ++o) {
-                    const double vo = sh.cand_v[o];
-                    rank += (vo > v) || (vo == v && sh.cand_j[o] < jc);
-                }
-                if (rank == need - 1) {
-                    sh.cut_v = v;
-                    sh.cut_j = jc;
-                }
-            }
-            __syncthreads();
-            break;
-        }
-        if (mn == mx) {
-            // all candidates are equal: e* is the need-th of them in index order
-            if (tid == 0) sh.found = 0;
-            __syncthreads();
-            uint32_t before = 0;
-            for (int64_t base = 0; base < n; base += kThreads) {
-                const int64_t j = base + tid;
-                const bool f = j < n && is_candidate(sh, nlev, sc[j]);
-                uint32_t tot;
-                const uint32_t pre = block_excl_scan(sh, f, &tot);
-                if (f && before + pre == (uint32_t)(need - 1)) {
-                    sh.cut_j = (int32_t)j;
-                    sh.cut_v = sc[j];
-                    sh.found = 1;
-                }
-                before += tot;
-                __syncthreads();
-                if (sh.found) break;
-            }
-            break;
-        }
-        if (nlev == kMaxLevels) {
-            // levels exhausted (only for scores spread over an extreme dynamic
-            // range): rank every candidate against all others, O(n^2)
-            for (int64_t j = tid; j < n; j += kThreads) {
-                const double x = sc[j];
-                if (!is_candidate(sh, nlev, x)) continue;
-                int64_t rank = 0;
-                for (int64_t o = 0; o < n; ++o) {
-                    const double y = sc[o];
-                    if (is_candidate(sh, nlev, y) && (y > x || (y == x && o < j))) ++rank;
-                }
-                if (rank == need - 1) {
-                    sh.cut_v = x;
-                    sh.cut_j = (int32_t)j;
+            for (int64_t e0 = 0; e0 < rows; e0 += kBatch) {
+                double x[kBatch];
+                LOAD_ROWS(x, e0)
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int64_t j = (e0 + i) * kThreads + tid;
+                    if (j < n && (x[i] > cv || (x[i] == cv && j <= cj)))
+                        atomicOr(&f.bitmap[j >> 5], 1u << (j & 31));
                 }
             }
             __syncthreads();
-            break;
-        }
-
-        // one histogram level
-        const double inv = (double)kBins / (mx - mn);
-        for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
-        __syncthreads();
-        for (int64_t j = tid; j < n; j += kThreads) {
-            const double x = sc[j];
-            if (is_candidate(sh, nlev, x)) atomicAdd(&sh.hist[bin_of(x, mn, inv)], 1u);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int64_t above = 0;
-            int b = kBins - 1;
-            for (; b > 0; --b) {
-                if (above + sh.hist[b] >= need) break;
-                above += sh.hist[b];
+            constexpr int WPT = (int)(kFastN / 32 / kThreads);     // 4 words per thread
+            uint32_t words[WPT];
+            uint32_t mine = 0;
+#pragma unroll
+            for (int i = 0; i < WPT; ++i) {
+                const int wi = tid * WPT + i;
+                words[i] = wi < nwords ? f.bitmap[wi] : 0u;
+                mine += __popc(words[i]);
             }
-            sh.lev_mn[nlev] = mn;
-            sh.lev_inv[nlev] = inv;
-            sh.lev_bin[nlev] = b;
-            sh.red_u[0] = (uint32_t)above;
+            uint32_t tot;
+            uint32_t pos = block_excl_sum(cm, mine, &tot);
+            if (sel) {
+#pragma unroll
+                for (int i = 0; i < WPT; ++i) {
+                    uint32_t w = words[i];
+                    while (w) {
+                        const int bit = __ffs(w) - 1;
+                        w &= w - 1;
+                        if (pos < (uint32_t)topk) sel[pos] = (tid * WPT + i) * 32 + bit;
+                        ++pos;
+                    }
+                }
+                for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
+            }
+            return;
         }
-        __syncthreads();
-        need -= sh.red_u[0];
-        ++nlev;
-        __syncthreads();
+        // too many spans at or above the bound: generic path below
     }
 
-    // ordered compaction of the selected spans
-    const double cv = sh.cut_v;
-    const int64_t cj = sh.cut_j;
-    uint32_t written = 0;
-    for (int64_t base = 0; base < n; base += kThreads) {
-        const int64_t j = base + tid;
-        bool f = false;
-        if (j < n) {
-            const double x = sc[j];
-            f = x > cv || (x == cv && j <= cj);
-        }
-        uint32_t tot;
-        const uint32_t pre = block_excl_scan(sh, f, &tot);
-        if (f && sel && written + pre < (uint32_t)topk) sel[written + pre] = (int32_t)j;
-        written += tot;
-    }
-    if (sel)
+    generic_cutoff(cm, u.g, sc, n, kk);
+    if (sel) {
+        generic_emit(cm, sc, n, sel, topk);
         for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
+    }
 }
+
+#undef LOAD_ROWS
 
 }  // namespace
 
