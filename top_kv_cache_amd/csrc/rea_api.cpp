@@ -128,9 +128,19 @@ size_t score_scores_bytes(const rea::Geom &g) {
     return (size_t)g.n_blk * g.Hkv * (size_t)g.n_spans * sizeof(double);
 }
 
+size_t group_max_bytes(const rea::Geom &g) {
+    return (size_t)g.n_blk * g.Hkv * (size_t)rea::score_groups(g) * sizeof(double);
+}
+
+// score_select workspace: [span scores unless the caller keeps them][group maxima]
+size_t score_ws_bytes(const rea::Geom &g, bool caller_scores) {
+    return (caller_scores ? 0 : align256(score_scores_bytes(g))) + align256(group_max_bytes(g));
+}
+
 size_t decode_ws_bytes(const rea::Geom &g) {
     Carve c{nullptr, 0};
     c.take<double>(score_scores_bytes(g));
+    c.take<double>(group_max_bytes(g));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
@@ -220,7 +230,7 @@ rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes 
     out->n_spans = g.n_spans;
     out->k_sel = g.k_sel;
     out->W_cap = g.W_cap;
-    out->ws_score_select = align256(score_scores_bytes(g));
+    out->ws_score_select = score_ws_bytes(g, false);
     out->ws_window_attend = rea::attend_ws_bytes(g, g.W_cap);
     out->ws_decode_step = decode_ws_bytes(g);
     return REA_OK;
@@ -236,15 +246,18 @@ rea_status rea_score_select(const rea_problem *p, const rea_params *a, int32_t *
     if ((st = check_sel(g, sel, n_sel)) != REA_OK) return st;
     if (span_scores && !aligned(span_scores, 8))
         return fail(REA_EALIGN, "span_scores must be 8-byte aligned");
-    const size_t need = span_scores ? 0 : align256(score_scores_bytes(g));
-    if ((st = check_ws(ws, ws_bytes, need)) != REA_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, score_ws_bytes(g, span_scores != nullptr))) != REA_OK)
+        return st;
     int num_cu = 0;
     if ((st = device_ready(&num_cu)) != REA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    double *scores = span_scores ? span_scores : (double *)ws;
-    if ((st = launched(rea::launch_score(g, p->q, p->k, scores, num_cu, s), "score")) != REA_OK)
+    Carve c{(char *)ws, 0};
+    double *scores = span_scores ? span_scores : c.take<double>(score_scores_bytes(g));
+    double *gmax = c.take<double>(group_max_bytes(g));
+    if ((st = launched(rea::launch_score(g, p->q, p->k, scores, gmax, num_cu, s), "score")) !=
+        REA_OK)
         return st;
-    return launched(rea::launch_topk(g, scores, sel, n_sel, s), "topk");
+    return launched(rea::launch_topk(g, scores, gmax, sel, n_sel, s), "topk");
 }
 
 rea_status rea_gather_rope(const rea_problem *p, const rea_params *a, const int32_t *sel,
@@ -302,6 +315,7 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
 
     Carve c{(char *)ws, 0};
     double *scores = c.take<double>(score_scores_bytes(g));
+    double *gmax = c.take<double>(group_max_bytes(g));
     int32_t *ws_sel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     int32_t *ws_nsel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     int32_t *Wlen = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
@@ -318,13 +332,15 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
         if (hipEventRecord((hipEvent_t)timing->score_begin, s) != hipSuccess)
             return launched(hipGetLastError(), "event record");
     }
-    if ((st = launched(rea::launch_score(g, p->q, p->k, scores, num_cu, s), "score")) != REA_OK)
+    if ((st = launched(rea::launch_score(g, p->q, p->k, scores, gmax, num_cu, s), "score")) !=
+        REA_OK)
         return st;
     if (timing && timing->score_end) {
         if (hipEventRecord((hipEvent_t)timing->score_end, s) != hipSuccess)
             return launched(hipGetLastError(), "event record");
     }
-    if ((st = launched(rea::launch_topk(g, scores, use_sel, use_nsel, s), "topk")) != REA_OK)
+    if ((st = launched(rea::launch_topk(g, scores, gmax, use_sel, use_nsel, s), "topk")) !=
+        REA_OK)
         return st;
     if ((st = launched(rea::launch_gather_rope(g, p->k, p->v, p->q, use_sel, use_nsel, k_win,
                                                v_win, q_rot, Wlen, g.W_cap, s),

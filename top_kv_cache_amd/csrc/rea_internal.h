@@ -29,13 +29,15 @@ constexpr int kMaxHalfDim = 64;   // head_dim <= 128
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
 
-// Step 1a: span scores [n_blk][Hkv][n_spans] (double).
+// Step 1a: span scores [n_blk][Hkv][n_spans] (double) and the maximum of every
+// group of 32 consecutive spans [n_blk][Hkv][score_groups(g)].
+int64_t score_groups(const Geom &g);
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
-                        int num_cu, hipStream_t s);
+                        double *group_max, int num_cu, hipStream_t s);
 
-// Step 1b: top-k per (block, KV head).
-hipError_t launch_topk(const Geom &g, const double *span_scores, int32_t *sel, int32_t *n_sel,
-                       hipStream_t s);
+// Step 1b: top-k per (block, KV head) from the span scores and group maxima.
+hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
+                       int32_t *sel, int32_t *n_sel, hipStream_t s);
 
 // Steps 2-3: window rows (K rotated fp32, V copied) + lengths, then the queries.
 hipError_t launch_gather_rope(const Geom &g, const void *k, const void *v, const void *q,

@@ -7,20 +7,25 @@
 // query/un-positioned-key dot product; OpenReview discussion, "Decoding Phase"
 // pseudocode: score = query @ key[G:-L]^T).  A span's score is the maximum of
 // its token scores; a block of queries sums its queries' maxima.  Token scores
-// are never written out: only span scores leave the kernel.
+// are never written out: only span scores leave the kernel, together with the
+// maximum of every group of 32 consecutive spans (used by the top-k step).
 //
 // Arithmetic: the group-summed query is formed in fp64 (exact for bf16 and,
-// in practice, fp32 inputs), every product bf16/fp32 x fp64 is exact in fp64,
-// and sums are fp64, so span scores agree with the exact ones to ~1e-16
-// relative and the top-k decision downstream matches an exact evaluation
-// except for gaps below that.
+// in practice, fp32 inputs), every product with a bf16/fp32 key element is
+// exact in fp64, and sums are fp64, so span scores agree with the exact ones
+// to ~1e-16 relative (for ordinary bf16 data the sums are exact).
 //
-// Memory: decoding streams the whole middle K once (2.14 GB per layer at 1M
-// tokens, d=128, 8 KV heads).  Four lanes share one key row; each lane issues
-// 16-byte loads so that one wave instruction reads 16 rows x 64 contiguous
-// bytes.  Two rounds (32 tokens = 8 KB per wave for d=128 bf16) are loaded
-// before any arithmetic to keep enough bytes in flight.  The grid gives every
-// (block, KV head) P workgroups, each streaming a contiguous run of spans.
+// Memory (decode): the whole middle K is streamed once (2.14 GB per layer at
+// 1M tokens, d=128, 8 KV heads).  A key row is read by the lanes of one DPP
+// row (16 lanes x 16 B for d=128 bf16), so one load instruction reads whole
+// rows, contiguous; loads are non-temporal (the cache is touched once); up to
+// 32 rows per wave are loaded before any arithmetic.  Partial dot products
+// are summed across a row's lanes with DPP quad-permute and mirror moves
+// (symmetric pairings, so every lane ends with identical bits).  Each
+// workgroup owns a contiguous run of 32-span groups of one (block, KV head);
+// its four waves take adjacent spans, so the workgroup reads 32 KB
+// contiguous per step.  About two workgroups per compute unit run: more
+// concurrent streams lowered measured bandwidth.
 #include "rea_internal.h"
 
 #include <math.h>
@@ -30,26 +35,29 @@ namespace {
 
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kWaves = kThreads / 64;
+constexpr int kGroup = 32;      // spans per group maximum
 
 struct ScoreArgs {
     const void *q;
     const unsigned char *k;
-    double *out;
+    double *out;                // [n_blk][Hkv][n_spans]
+    double *gmax;               // [n_blk][Hkv][n_groups]
     int64_t sh_bytes, st_bytes;
-    int64_t mid_lo, mid_hi, n_spans;
+    int64_t mid_lo, mid_hi, n_spans, n_groups;
     int S, Hq, Hkv, g, block_q, P;
 };
 
-template <typename TIn> struct Elem;
-template <> struct Elem<uint16_t> { static constexpr int EPV = 8; };   // bf16 per 16 B
-template <> struct Elem<float> { static constexpr int EPV = 4; };
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_nt(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ double load_f64(const uint16_t *p, int64_t i) {
     return (double)__uint_as_float(((uint32_t)p[i]) << 16);
 }
-__device__ __forceinline__ double load_f64(const float *p, int64_t i) {
-    return (double)p[i];
-}
+__device__ __forceinline__ double load_f64(const float *p, int64_t i) { return (double)p[i]; }
 
 __device__ __forceinline__ void unpack(const uint4 &x, double (&o)[8]) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -66,74 +74,112 @@ __device__ __forceinline__ void unpack(const uint4 &x, double (&o)[4]) {
     o[3] = (double)__uint_as_float(x.w);
 }
 
-__device__ __forceinline__ double wave_max(double v) {
-    v = fmax(v, __shfl_xor(v, 4));
-    v = fmax(v, __shfl_xor(v, 8));
-    v = fmax(v, __shfl_xor(v, 16));
-    v = fmax(v, __shfl_xor(v, 32));
+// v + (v from the lane chosen by DPP control CTRL), on the two halves of a double
+template <int CTRL> __device__ __forceinline__ double dpp_add(double v) {
+    const int2 x = *reinterpret_cast<const int2 *>(&v);
+    int2 y;
+    y.x = __builtin_amdgcn_mov_dpp(x.x, CTRL, 0xF, 0xF, false);
+    y.y = __builtin_amdgcn_mov_dpp(x.y, CTRL, 0xF, 0xF, false);
+    return v + *reinterpret_cast<const double *>(&y);
+}
+
+// Sum over the LPR consecutive lanes that share a key row.  Every step pairs
+// lanes symmetrically: quad-permute xor 1, xor 2, half-row mirror, row mirror.
+template <int LPR> __device__ __forceinline__ double row_sum(double v) {
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+    if (LPR >= 8) v = dpp_add<0x141>(v);
+    if (LPR >= 16) v = dpp_add<0x140>(v);
+    if (LPR >= 32) v += __shfl_xor(v, 16);
     return v;
 }
 
+// Max over the rows of a wave (lanes LPR apart).
+template <int LPR> __device__ __forceinline__ double rows_max(double v) {
+    for (int o = LPR; o < 64; o <<= 1) v = fmax(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Group bookkeeping shared by both kernels: the workgroup's group range and
+// the per-group maximum across its waves (double-buffered by group parity).
+struct GroupRange {
+    int64_t g0, g1;
+};
+__device__ __forceinline__ GroupRange group_range(const ScoreArgs &a, int p) {
+    return {(int64_t)p * a.n_groups / a.P, (int64_t)(p + 1) * a.n_groups / a.P};
+}
+
+__device__ __forceinline__ void publish_group_max(const ScoreArgs &a, double (&slot)[2][kWaves],
+                                                  int64_t bh, int64_t grp, double wave_best) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) slot[grp & 1][wave] = wave_best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double m = slot[grp & 1][0];
+        for (int w = 1; w < kWaves; ++w) m = fmax(m, slot[grp & 1][w]);
+        a.gmax[bh * a.n_groups + grp] = m;
+    }
+}
+
 // Decode: one query per block; the group-summed query lives in registers.
+// R = load instructions per batch (each instruction covers RPI rows).
 template <typename TIn, int D, int R>
 __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
-    constexpr int EPV = Elem<TIn>::EPV;
-    constexpr int NV = D / (4 * EPV);            // 16-byte vectors per lane per token
+    constexpr int ESZ = sizeof(TIn);
+    constexpr int LPR = D * ESZ / 16;          // lanes per key row
+    constexpr int RPI = 64 / LPR;              // rows per load instruction
+    constexpr int EPL = 16 / ESZ;              // elements per lane
+    __shared__ double slot[2][kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int quad = lane >> 2, c4 = lane & 3;
+    const int rs = lane / LPR, ch = lane % LPR;
     const int bh = blockIdx.x / a.P, p = blockIdx.x % a.P;
     const int b = bh / a.Hkv, h = bh % a.Hkv;
-    const int64_t j0 = (int64_t)p * a.n_spans / a.P;
-    const int64_t j1 = (int64_t)(p + 1) * a.n_spans / a.P;
 
-    double qr[NV][EPV];
+    double qr[EPL];
     {
         const TIn *qb = (const TIn *)a.q + (int64_t)b * a.Hq * D + (int64_t)h * a.g * D;
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const int c = v * 4 * EPV + c4 * EPV + e;
-                double s = 0.0;
-                for (int gg = 0; gg < a.g; ++gg) s += load_f64(qb, (int64_t)gg * D + c);
-                qr[v][e] = s;
-            }
+        for (int e = 0; e < EPL; ++e) {
+            double s = 0.0;
+            for (int gg = 0; gg < a.g; ++gg) s += load_f64(qb, (int64_t)gg * D + ch * EPL + e);
+            qr[e] = s;
+        }
     }
 
-    const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes;
-    for (int64_t j = j0 + wave; j < j1; j += kWaves) {
-        const int64_t t_beg = a.mid_lo + j * a.S;
-        const int64_t t_end = min(t_beg + (int64_t)a.S, a.mid_hi);
-        double best = -INFINITY;
-        for (int64_t r0 = t_beg; r0 < t_end; r0 += 16 * R) {
-            uint4 buf[R][NV];
-            bool ok[R];
+    const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes + ch * 16;
+    const GroupRange gr = group_range(a, p);
+    for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
+        const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
+        double gbest = -INFINITY;
+        for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
+            const int64_t tb = a.mid_lo + j * a.S;
+            const int64_t te = min(tb + (int64_t)a.S, a.mid_hi);
+            double best = -INFINITY;
+            for (int64_t r0 = tb; r0 < te; r0 += (int64_t)R * RPI) {
+                uint4 buf[R];
+                bool ok[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int64_t t = r0 + r * 16 + quad;
-                ok[r] = t < t_end;
-                const uint4 *src = (const uint4 *)(kh + t * a.st_bytes) + c4;
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-                    buf[r][v] = ok[r] ? src[v * 4] : make_uint4(0u, 0u, 0u, 0u);
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                double acc = 0.0;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    double x[EPV];
-                    unpack(buf[r][v], x);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) acc = fma(qr[v][e], x[e], acc);
+                for (int r = 0; r < R; ++r) {
+                    const int64_t t = r0 + r * RPI + rs;
+                    ok[r] = t < te;
+                    buf[r] = ok[r] ? load_nt(kh + t * a.st_bytes) : make_uint4(0u, 0u, 0u, 0u);
                 }
-                acc += __shfl_xor(acc, 1);
-                acc += __shfl_xor(acc, 2);
-                if (ok[r]) best = fmax(best, acc);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    double x[EPL];
+                    unpack(buf[r], x);
+                    double acc = 0.0;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc = fma(qr[e], x[e], acc);
+                    acc = row_sum<LPR>(acc);
+                    if (ok[r]) best = fmax(best, acc);
+                }
             }
+            best = rows_max<LPR>(best) + 0.0;       // -0 -> +0
+            if (lane == 0) a.out[(int64_t)bh * a.n_spans + j] = best;
+            gbest = fmax(gbest, best);
         }
-        best = wave_max(best);
-        if (lane == 0) a.out[(int64_t)bh * a.n_spans + j] = best + 0.0;   // -0 -> +0
+        publish_group_max(a, slot, bh, grp, gbest);
     }
 }
 
@@ -141,15 +187,16 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
 // queries of the block sit in LDS; span score = sum over queries of the max.
 template <typename TIn, int D>
 __global__ __launch_bounds__(kThreads) void k_score_block(ScoreArgs a) {
-    constexpr int EPV = Elem<TIn>::EPV;
-    constexpr int NV = D / (4 * EPV);
+    constexpr int ESZ = sizeof(TIn);
+    constexpr int LPR = D * ESZ / 16;
+    constexpr int RPI = 64 / LPR;
+    constexpr int EPL = 16 / ESZ;
     extern __shared__ double qe[];                // [block_q][D]
+    __shared__ double slot[2][kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int quad = lane >> 2, c4 = lane & 3;
+    const int rs = lane / LPR, ch = lane % LPR;
     const int bh = blockIdx.x / a.P, p = blockIdx.x % a.P;
     const int b = bh / a.Hkv, h = bh % a.Hkv;
-    const int64_t j0 = (int64_t)p * a.n_spans / a.P;
-    const int64_t j1 = (int64_t)(p + 1) * a.n_spans / a.P;
 
     const TIn *qb = (const TIn *)a.q;
     for (int idx = threadIdx.x; idx < a.block_q * D; idx += kThreads) {
@@ -161,45 +208,59 @@ __global__ __launch_bounds__(kThreads) void k_score_block(ScoreArgs a) {
     }
     __syncthreads();
 
-    const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes;
-    for (int64_t j = j0 + wave; j < j1; j += kWaves) {
-        const int64_t t_beg = a.mid_lo + j * a.S;
-        const int64_t t_end = min(t_beg + (int64_t)a.S, a.mid_hi);
-        double total = 0.0;
-        for (int i = 0; i < a.block_q; ++i) {
-            const double *qi = qe + (int64_t)i * D;
-            double best = -INFINITY;
-            for (int64_t r0 = t_beg; r0 < t_end; r0 += 16) {
-                const int64_t t = r0 + quad;
-                const bool ok = t < t_end;
-                const uint4 *src = (const uint4 *)(kh + t * a.st_bytes) + c4;
-                double acc = 0.0;
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const uint4 raw = ok ? src[v * 4] : make_uint4(0u, 0u, 0u, 0u);
-                    double x[EPV];
+    const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes + ch * 16;
+    const GroupRange gr = group_range(a, p);
+    for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
+        const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
+        double gbest = -INFINITY;
+        for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
+            const int64_t tb = a.mid_lo + j * a.S;
+            const int64_t te = min(tb + (int64_t)a.S, a.mid_hi);
+            double total = 0.0;
+            for (int i = 0; i < a.block_q; ++i) {
+                const double *qi = qe + (int64_t)i * D + ch * EPL;
+                double best = -INFINITY;
+                for (int64_t r0 = tb; r0 < te; r0 += RPI) {
+                    const int64_t t = r0 + rs;
+                    const bool ok = t < te;
+                    const uint4 raw = ok ? *(const uint4 *)(kh + t * a.st_bytes)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+                    double x[EPL];
                     unpack(raw, x);
+                    double acc = 0.0;
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e)
-                        acc = fma(qi[v * 4 * EPV + c4 * EPV + e], x[e], acc);
+                    for (int e = 0; e < EPL; ++e) acc = fma(qi[e], x[e], acc);
+                    acc = row_sum<LPR>(acc);
+                    if (ok) best = fmax(best, acc);
                 }
-                acc += __shfl_xor(acc, 1);
-                acc += __shfl_xor(acc, 2);
-                if (ok) best = fmax(best, acc);
+                total += rows_max<LPR>(best);
             }
-            total += wave_max(best);
+            total += 0.0;
+            if (lane == 0) a.out[(int64_t)bh * a.n_spans + j] = total;
+            gbest = fmax(gbest, total);
         }
-        if (lane == 0) a.out[(int64_t)bh * a.n_spans + j] = total + 0.0;
+        publish_group_max(a, slot, bh, grp, gbest);
     }
+}
+
+template <typename TIn, int D, int R>
+void launch_decode(const ScoreArgs &a, int nblocks, hipStream_t s) {
+    hipLaunchKernelGGL((k_score_decode<TIn, D, R>), dim3(nblocks), dim3(kThreads), 0, s, a);
 }
 
 template <typename TIn, int D>
 hipError_t launch_typed(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
     if (g.block_q == 1) {
-        if (g.S <= 16)
-            hipLaunchKernelGGL((k_score_decode<TIn, D, 1>), dim3(nblocks), dim3(kThreads), 0, s, a);
+        constexpr int RPI = 64 / (D * (int)sizeof(TIn) / 16);
+        const int per_span = (g.S + RPI - 1) / RPI;       // load instructions per span
+        if (per_span >= 8)
+            launch_decode<TIn, D, 8>(a, nblocks, s);
+        else if (per_span >= 4)
+            launch_decode<TIn, D, 4>(a, nblocks, s);
+        else if (per_span >= 2)
+            launch_decode<TIn, D, 2>(a, nblocks, s);
         else
-            hipLaunchKernelGGL((k_score_decode<TIn, D, 2>), dim3(nblocks), dim3(kThreads), 0, s, a);
+            launch_decode<TIn, D, 1>(a, nblocks, s);
     } else {
         const size_t lds = (size_t)g.block_q * D * sizeof(double);
         hipLaunchKernelGGL((k_score_block<TIn, D>), dim3(nblocks), dim3(kThreads), lds, s, a);
@@ -209,28 +270,31 @@ hipError_t launch_typed(const Geom &g, const ScoreArgs &a, int nblocks, hipStrea
 
 }  // namespace
 
+int64_t score_groups(const Geom &g) { return (g.n_spans + kGroup - 1) / kGroup; }
+
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
-                        int num_cu, hipStream_t s) {
+                        double *group_max, int num_cu, hipStream_t s) {
     if (g.n_spans == 0) return hipSuccess;
     ScoreArgs a;
     a.q = q;
     a.k = (const unsigned char *)k;
     a.out = span_scores;
+    a.gmax = group_max;
     a.sh_bytes = g.sh * g.esize;
     a.st_bytes = g.st * g.esize;
     a.mid_lo = g.mid_lo;
     a.mid_hi = g.mid_hi;
     a.n_spans = g.n_spans;
+    a.n_groups = score_groups(g);
     a.S = g.S;
     a.Hq = g.Hq;
     a.Hkv = g.Hkv;
     a.g = g.g;
     a.block_q = g.block_q;
     const int64_t units = (int64_t)g.n_blk * g.Hkv;
-    const int64_t target = (int64_t)(num_cu > 0 ? num_cu : 256) * 4;
+    const int64_t target = (int64_t)(num_cu > 0 ? num_cu : 256) * 2;
     int64_t P = (target + units - 1) / units;
-    const int64_t maxP = (g.n_spans + kWaves - 1) / kWaves;
-    if (P > maxP) P = maxP;
+    if (P > a.n_groups) P = a.n_groups;
     if (P < 1) P = 1;
     a.P = (int)P;
     const int nblocks = (int)(units * P);

@@ -6,24 +6,26 @@
 // first, equal scores -> lower span index first.  The selection is emitted in
 // ascending span order, which is the order the spans take in the window.
 //
-// One 512-thread workgroup per (block, KV head).  Fast path (n <= 65536
-// spans), three coalesced passes over the span scores in L2:
-//   1. maxima of groups of 32 consecutive spans -> LDS.  The k-th largest
-//      group maximum tau is a lower bound of the k-th largest score (the k
-//      best groups hold k distinct scores >= tau), so every selected span has
-//      score >= tau.
-//   2. spans with score >= tau are appended to LDS (at most 8192 fit).
+// One 512-thread workgroup per (block, KV head).  The scoring kernel also
+// wrote the maximum of every group of 32 consecutive spans.  Fast path (at
+// most 2048 groups):
+//   1. tau = the k-th largest group maximum.  It is a lower bound of the k-th
+//      largest score (the k best groups hold k distinct scores >= tau), so
+//      every selected span lies in a group whose maximum is >= tau; at most
+//      256 such groups are accepted (more only with massive ties).
+//   2. the spans of those groups with score >= tau are loaded into LDS;
 //   3. the cutoff e* (the k-th best under score desc, index asc) is found in
-//      LDS by histogram levels over the candidates; span j is selected iff
-//      score_j > score* or (score_j == score* and j <= j*); a bitmap over the
-//      spans and one block scan write the indices in ascending order.
+//      LDS by histogram levels; span j is selected iff score_j > score* or
+//      (score_j == score* and j <= j*).  Each candidate group becomes one
+//      32-bit word of a bitmap over the spans, and one block scan over the
+//      words writes the indices in ascending order.
 // Histogram level: 2048 equal-width bins between the candidates' min and max,
 // bin = floor((x - min) * (2048 / (max - min))) in fp64 -- monotone in x, so
 // bins are ordered; only the bin holding the k-th best survives.  Once all
 // survivors share one score the order is by index, so the level key becomes
 // the negated index.  At most 256 survivors are ranked pairwise.
-// Larger inputs, or more than 8192 spans at or above the bound, take a generic
-// path that makes the same decisions with global-memory passes.
+// Otherwise a generic path makes the same decisions with passes over all
+// scores in global memory.
 #include "rea_internal.h"
 
 #include <math.h>
@@ -35,12 +37,11 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kGroup = 32;
 constexpr int kMaxGroups = 2048;
-constexpr int64_t kFastN = (int64_t)kGroup * kMaxGroups;   // 65536
 constexpr int kCandCap = 8192;
 constexpr int kPerThread = kCandCap / kThreads;             // 16
 constexpr int kBins = 2048;
 constexpr int kRankMax = 256;
-constexpr int kBatch = 8;
+constexpr int kMaxCandGroups = kCandCap / kGroup;        // 256
 
 struct FastShared {
     double val[kCandCap];
@@ -48,7 +49,8 @@ struct FastShared {
     double gval[kMaxGroups];
     int32_t gidx[kMaxGroups];
     uint32_t hist[kBins];
-    uint32_t bitmap[kFastN / 32];
+    uint32_t bitmap[kMaxGroups];
+    int32_t cgrp[kMaxCandGroups];
 };
 
 // generic path state
@@ -375,15 +377,9 @@ __device__ __forceinline__ void generic_emit(Common &cm, const double *sc, int64
     }
 }
 
-// Loads batch e0..e0+kBatch-1 of rows (element j = row*kThreads + tid).
-#define LOAD_ROWS(x, e0)                                                    \
-    _Pragma("unroll") for (int i_ = 0; i_ < kBatch; ++i_) {                  \
-        const int64_t j_ = ((e0) + i_) * kThreads + tid;                     \
-        x[i_] = j_ < n ? sc[j_] : -INFINITY;                                 \
-    }
-
 __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ scores_all,
-                                                   int64_t n, int kk, int topk,
+                                                   const double *__restrict__ gmax_all,
+                                                   int64_t n, int64_t m, int kk, int topk,
                                                    int32_t *__restrict__ sel_all,
                                                    int32_t *__restrict__ nsel_all) {
     __shared__ Common cm;
@@ -391,9 +387,10 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
         FastShared f;
         GenericShared g;
     } u;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t bh = blockIdx.x;
     const double *sc = scores_all + bh * n;
+    const double *gm = gmax_all + bh * m;
     int32_t *sel = sel_all ? sel_all + bh * topk : nullptr;
     if (tid == 0) nsel_all[bh] = kk;
 
@@ -403,79 +400,75 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
         return;
     }
 
-    if (n <= kFastN) {
+    if (m <= kMaxGroups) {
         FastShared &f = u.f;
-        const int64_t m = (n + kGroup - 1) / kGroup;
-        const int64_t rows = (n + kThreads - 1) / kThreads;
-        // 1. group maxima: lanes 0-31 / 32-63 of a wave hold one group per row
-        for (int64_t e0 = 0; e0 < rows; e0 += kBatch) {
-            double x[kBatch];
-            LOAD_ROWS(x, e0)
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                double gm = x[i];
-                for (int o = 16; o > 0; o >>= 1) gm = fmax(gm, __shfl_xor(gm, o));
-                const int64_t grp = ((e0 + i) * kThreads + tid) / kGroup;
-                if ((tid & (kGroup - 1)) == 0 && grp < m) {
-                    f.gval[grp] = gm;
-                    f.gidx[grp] = (int32_t)grp;
-                }
-            }
-        }
-        __syncthreads();
-        // 2. tau = kk-th largest group maximum (all spans compete if kk > m)
+        // 1. tau = kk-th largest group maximum (every span competes if kk > m)
         double tau = -INFINITY;
         if (kk <= m) {
+            for (int i = tid; i < m; i += kThreads) {
+                f.gval[i] = gm[i];
+                f.gidx[i] = i;
+            }
+            __syncthreads();
             find_kth(cm, f.hist, f.gval, f.gidx, (uint32_t)m, kk);
             tau = cm.cut_v;
         }
-        // 3. candidates: score >= tau
+        // candidate groups: maximum >= tau
         if (tid == 0) cm.count = 0;
         __syncthreads();
-        for (int64_t e0 = 0; e0 < rows; e0 += kBatch) {
-            double x[kBatch];
-            LOAD_ROWS(x, e0)
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int64_t j = (e0 + i) * kThreads + tid;
-                if (j < n && x[i] >= tau) {
-                    const uint32_t slot = atomicAdd(&cm.count, 1u);
-                    if (slot < (uint32_t)kCandCap) {
-                        f.val[slot] = x[i];
+        for (int i = tid; i < m; i += kThreads) {
+            if (gm[i] >= tau) {
+                const uint32_t slot = atomicAdd(&cm.count, 1u);
+                if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
+            }
+        }
+        __syncthreads();
+        const uint32_t ncg = cm.count;
+        __syncthreads();
+        if (ncg <= (uint32_t)kMaxCandGroups) {
+            // 2. their spans with score >= tau; half a wave per group
+            const int half = tid >> 5, hl = tid & 31;
+            if (tid == 0) cm.count = 0;
+            __syncthreads();
+            for (uint32_t c = half; c < ncg; c += kThreads / 32) {
+                const int64_t j = (int64_t)f.cgrp[c] * kGroup + hl;
+                if (j < n) {
+                    const double x = sc[j];
+                    if (x >= tau) {
+                        const uint32_t slot = atomicAdd(&cm.count, 1u);
+                        f.val[slot] = x;
                         f.idx[slot] = (int32_t)j;
                     }
                 }
             }
-        }
-        __syncthreads();
-        const uint32_t count = cm.count;
-        __syncthreads();
-        if (count <= (uint32_t)kCandCap) {
+            __syncthreads();
+            const uint32_t count = cm.count;
+            __syncthreads();
+            // 3. cutoff, bitmap words of the candidate groups, ordered output
             find_kth(cm, f.hist, f.val, f.idx, count, kk);
-            // 4. bitmap of the selected spans, then ordered compaction
             const double cv = cm.cut_v;
             const int64_t cj = cm.cut_j;
-            const int nwords = (int)((n + 31) / 32);
-            for (int i = tid; i < nwords; i += kThreads) f.bitmap[i] = 0u;
+            for (int i = tid; i < m; i += kThreads) f.bitmap[i] = 0u;
             __syncthreads();
-            for (int64_t e0 = 0; e0 < rows; e0 += kBatch) {
-                double x[kBatch];
-                LOAD_ROWS(x, e0)
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i) {
-                    const int64_t j = (e0 + i) * kThreads + tid;
-                    if (j < n && (x[i] > cv || (x[i] == cv && j <= cj)))
-                        atomicOr(&f.bitmap[j >> 5], 1u << (j & 31));
+            for (uint32_t c = half; c < ncg; c += kThreads / 32) {
+                const int g = f.cgrp[c];
+                const int64_t j = (int64_t)g * kGroup + hl;
+                bool pick = false;
+                if (j < n) {
+                    const double x = sc[j];
+                    pick = x > cv || (x == cv && j <= cj);
                 }
+                const unsigned long long bal = __ballot(pick);
+                if (hl == 0) f.bitmap[g] = (uint32_t)(bal >> (lane & 32));
             }
             __syncthreads();
-            constexpr int WPT = (int)(kFastN / 32 / kThreads);     // 4 words per thread
+            constexpr int WPT = kMaxGroups / kThreads;      // 4 words per thread
             uint32_t words[WPT];
             uint32_t mine = 0;
 #pragma unroll
             for (int i = 0; i < WPT; ++i) {
                 const int wi = tid * WPT + i;
-                words[i] = wi < nwords ? f.bitmap[wi] : 0u;
+                words[i] = wi < m ? f.bitmap[wi] : 0u;
                 mine += __popc(words[i]);
             }
             uint32_t tot;
@@ -487,15 +480,16 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
                     while (w) {
                         const int bit = __ffs(w) - 1;
                         w &= w - 1;
-                        if (pos < (uint32_t)topk) sel[pos] = (tid * WPT + i) * 32 + bit;
+                        if (pos < (uint32_t)topk) sel[pos] = (tid * WPT + i) * kGroup + bit;
                         ++pos;
                     }
                 }
                 for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
             }
+            (void)wave;
             return;
         }
-        // too many spans at or above the bound: generic path below
+        // too many groups at or above the bound: generic path below
     }
 
     generic_cutoff(cm, u.g, sc, n, kk);
@@ -505,15 +499,13 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
     }
 }
 
-#undef LOAD_ROWS
-
 }  // namespace
 
-hipError_t launch_topk(const Geom &g, const double *span_scores, int32_t *sel, int32_t *n_sel,
-                       hipStream_t s) {
+hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
+                       int32_t *sel, int32_t *n_sel, hipStream_t s) {
     const int nbh = g.n_blk * g.Hkv;
-    hipLaunchKernelGGL(k_topk, dim3(nbh), dim3(kThreads), 0, s, span_scores, g.n_spans,
-                       g.k_sel, g.topk, sel, n_sel);
+    hipLaunchKernelGGL(k_topk, dim3(nbh), dim3(kThreads), 0, s, span_scores, group_max,
+                       g.n_spans, score_groups(g), g.k_sel, g.topk, sel, n_sel);
     return hipGetLastError();
 }
 
