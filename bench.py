@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "middle-cache keys scored/s (achieved HBM GB/s) + decode-step latency @1M ctx"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_decode_llama8b_1m_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_decode_llama8b_1m_traffic.txt")
 SCORE_SRC = os.path.join(ROOT, "top_kv_cache_amd", "csrc", "score.hip")
 
 
@@ -72,8 +72,9 @@ def traffic_for(score_bytes):
         return None
 
 
-def cpu_baseline(w):
-    """The oracle, as it stands, on one layer (all KV heads) of the workload."""
+def cpu_baseline(w, min_seconds=10.0):
+    """The oracle, as it stands, on whole layers of the workload (all KV heads),
+    layer after layer until at least `min_seconds` of oracle time."""
     import numpy as np
     import oracle.rea_oracle as O
     import synth
@@ -82,22 +83,27 @@ def cpu_baseline(w):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    q64 = synth.to_f32(w.q(0), w.dtype).astype(np.float64)
     g = w.g
-    total = 0.0
-    for h in range(w.Hkv):
-        K = synth.to_f32(w.kv(0, "k", h, h + 1), w.dtype).astype(np.float64)
-        V = synth.to_f32(w.kv(0, "v", h, h + 1), w.dtype).astype(np.float64)
-        t0 = time.perf_counter()
-        O.step(q64[:, h * g:(h + 1) * g], K, V, w.G, w.S, w.topk, w.L, w.block_q, w.rope_theta)
-        total += time.perf_counter() - t0
-        del K, V
+    total, layers = 0.0, 0
+    for layer in range(w.n_layers):
+        q64 = synth.to_f32(w.q(layer), w.dtype).astype(np.float64)
+        for h in range(w.Hkv):
+            K = synth.to_f32(w.kv(layer, "k", h, h + 1), w.dtype).astype(np.float64)
+            V = synth.to_f32(w.kv(layer, "v", h, h + 1), w.dtype).astype(np.float64)
+            t0 = time.perf_counter()
+            O.step(q64[:, h * g:(h + 1) * g], K, V, w.G, w.S, w.topk, w.L, w.block_q,
+                   w.rope_theta)
+            total += time.perf_counter() - t0
+            del K, V
+        layers += 1
+        if total >= min_seconds:
+            break
     lo, hi = w.mid
-    keys = (hi - lo) * w.Hkv
+    keys = (hi - lo) * w.Hkv * layers
     return {"value": keys / total, "unit": "keys/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"layer 0 of {w.n_layers}, all {w.Hkv} KV heads: one layer's full decode "
-                      f"step (score, select, gather+RoPE, attend) in fp64 numpy, "
-                      f"{total:.1f} s; input generation not timed"}
+            "sample": f"layers 0..{layers - 1} of {w.n_layers}, all {w.Hkv} KV heads each: the "
+                      f"full decode step (score, select, gather+RoPE, attend) in fp64 numpy, "
+                      f"{total:.1f} s of oracle time; input generation not timed"}
 
 
 def main():
@@ -108,6 +114,8 @@ def main():
     ap.add_argument("--config", type=int, default=3, help="workload number (default: 1M x 32 layers)")
     ap.add_argument("--layers", type=int, default=0, help="override layer count (exploration only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="also run one plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -148,6 +156,16 @@ def main():
         for li, st in enumerate(steps_l):
             st.decode_step(out=outs[li], ws=ws, stream=stream,
                            timing=timing[li] if timing is not None else None)
+
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n * 4} bytes done")
+        del src, dst
 
     for _ in range(args.warmup):
         one_step()
