@@ -69,6 +69,13 @@ def oracle_head(w, layer, h, q64=None, K_h=None, V_h=None):
                 Vw=[v[0] for v in Vw], q_rot=qr, W=W[:, 0], out=out)
 
 
+def mfma_path(w):
+    """Blocks of 64 bf16 queries with d 128 are scored on MFMA: their span scores
+    are approximations within a proven bound (selection stays exact)."""
+    return (w.dtype == "bf16" and w.d == 128 and w.block_q == 64 and w.S % 32 == 0
+            and 0 < w.n_spans <= 4096)
+
+
 def compare_head(w, gpu, ora, h, check_windows=True):
     """Assert parity of KV head h; returns the max-abs output error."""
     g, nb = w.g, len(ora["sel"])
@@ -86,7 +93,8 @@ def compare_head(w, gpu, ora, h, check_windows=True):
         ref = ora["sc"]
         scale = max(1.0, float(np.abs(ref).max()))
         err = np.abs(gpu["sc"][:, h, :] - ref).max()
-        assert err <= 1e-12 * scale, ("span scores", h, err)
+        rel = 1e-4 if mfma_path(w) else 1e-12
+        assert err <= rel * scale, ("span scores", h, err)
     assert np.array_equal(gpu["W"][:, h], ora["W"]), (gpu["W"][:, h], ora["W"])
     if check_windows:
         for b in range(nb):

@@ -43,6 +43,13 @@ SMALL = {
     "f32_L1": S(dtype="f32", L=1, T=400, topk=4),
     "bf16_many_heads": S(Hq=32, Hkv=8, d=128, T=2048, S=32, topk=12, L=256, needles=2,
                          kv_scaled=True),
+    # blocks of 64 bf16 queries, d 128: scored on MFMA, certified top-k
+    "bf16_mfma_blocks": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,
+                          L=128, needles=0),
+    "bf16_mfma_S64_partial": S(Hq=8, Hkv=2, d=128, T=5000, n_q=64, block_q=64, S=64, topk=9,
+                               L=100, needles=0, kv_scaled=True),
+    "bf16_mfma_5_blocks_g1": S(Hq=2, Hkv=2, d=128, T=2500, n_q=320, block_q=64, S=32, topk=7,
+                               L=400, needles=0),
 }
 
 
@@ -82,6 +89,34 @@ def test_exact_ties_lower_index_wins():
         split_groups += above < w.topk < above + tied
         compare_head(w, gpu, ora, h)
     assert split_groups >= 1       # the k-th boundary cuts through a tie group
+
+
+def test_exact_ties_mfma_blocks():
+    """Integer inputs through the MFMA block path: tied spans share identical
+    approximate scores and must be resolved by index after exact re-scoring."""
+    rng = np.random.default_rng(4321)
+    w = S(Hq=8, Hkv=2, d=128, T=3000, n_q=64, block_q=64, S=32, topk=10, L=128, needles=0)
+    qn = rng.integers(0, 2, size=(w.n_q, w.Hq, w.d)).astype(np.float32)
+    Kn = rng.integers(0, 2, size=(w.Hkv, w.T, w.d)).astype(np.float32)
+    # 14 identical spans that outscore the rest: the top-10 boundary cuts the tie
+    pattern = rng.integers(1, 3, size=(w.S, w.d)).astype(np.float32)
+    for j in rng.choice(80, size=14, replace=False):
+        Kn[:, w.G + j * w.S:w.G + (j + 1) * w.S] = pattern
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    gpu = run_library(w, to_bf(qn), to_bf(Kn), to_bf(Vn))
+    q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
+    ties = 0
+    for h in range(w.Hkv):
+        ora = oracle_head(w, 0, h, q64, K64[h:h + 1], V64[h:h + 1])
+        sc = ora["sc"][0]
+        kth = np.sort(sc)[::-1][w.topk - 1]
+        above, tied = int((sc > kth).sum()), int((sc == kth).sum())
+        ties += above < w.topk < above + tied
+        compare_head(w, gpu, ora, h)
+    assert ties == w.Hkv
 
 
 def test_deterministic():

@@ -132,15 +132,43 @@ size_t group_max_bytes(const rea::Geom &g) {
     return (size_t)g.n_blk * g.Hkv * (size_t)rea::score_groups(g) * sizeof(double);
 }
 
-// score_select workspace: [span scores unless the caller keeps them][group maxima]
+// score_select workspace: [span scores unless the caller keeps them][group
+// maxima, or the MFMA path's query rows / bounds]
+size_t select_aux_bytes(const rea::Geom &g) {
+    return rea::mfma_block_path(g) ? align256(rea::mfma_ws_bytes(g)) : align256(group_max_bytes(g));
+}
+
 size_t score_ws_bytes(const rea::Geom &g, bool caller_scores) {
-    return (caller_scores ? 0 : align256(score_scores_bytes(g))) + align256(group_max_bytes(g));
+    return (caller_scores ? 0 : align256(score_scores_bytes(g))) + select_aux_bytes(g);
+}
+
+// Steps 1a+1b on whichever path fits the problem.
+hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, double *scores,
+                         void *aux, int32_t *sel, int32_t *n_sel, int num_cu, hipStream_t s,
+                         const rea_timing *timing) {
+    if (timing && timing->score_begin) {
+        hipError_t e = hipEventRecord((hipEvent_t)timing->score_begin, s);
+        if (e != hipSuccess) return e;
+    }
+    if (rea::mfma_block_path(g)) {
+        hipError_t e = rea::launch_score_select_mfma(g, q, k, scores, sel, n_sel, aux, num_cu, s);
+        if (e == hipSuccess && timing && timing->score_end)
+            e = hipEventRecord((hipEvent_t)timing->score_end, s);
+        return e;
+    }
+    hipError_t e = rea::launch_score(g, q, k, scores, (double *)aux, num_cu, s);
+    if (e != hipSuccess) return e;
+    if (timing && timing->score_end) {
+        e = hipEventRecord((hipEvent_t)timing->score_end, s);
+        if (e != hipSuccess) return e;
+    }
+    return rea::launch_topk(g, scores, (const double *)aux, sel, n_sel, s);
 }
 
 size_t decode_ws_bytes(const rea::Geom &g) {
     Carve c{nullptr, 0};
     c.take<double>(score_scores_bytes(g));
-    c.take<double>(group_max_bytes(g));
+    c.take<char>(select_aux_bytes(g));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
@@ -253,11 +281,9 @@ rea_status rea_score_select(const rea_problem *p, const rea_params *a, int32_t *
     hipStream_t s = (hipStream_t)stream;
     Carve c{(char *)ws, 0};
     double *scores = span_scores ? span_scores : c.take<double>(score_scores_bytes(g));
-    double *gmax = c.take<double>(group_max_bytes(g));
-    if ((st = launched(rea::launch_score(g, p->q, p->k, scores, gmax, num_cu, s), "score")) !=
-        REA_OK)
-        return st;
-    return launched(rea::launch_topk(g, scores, gmax, sel, n_sel, s), "topk");
+    void *aux = c.take<char>(select_aux_bytes(g));
+    return launched(launch_select(g, p->q, p->k, scores, aux, sel, n_sel, num_cu, s, nullptr),
+                    "score_select");
 }
 
 rea_status rea_gather_rope(const rea_problem *p, const rea_params *a, const int32_t *sel,
@@ -315,7 +341,7 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
 
     Carve c{(char *)ws, 0};
     double *scores = c.take<double>(score_scores_bytes(g));
-    double *gmax = c.take<double>(group_max_bytes(g));
+    void *aux = c.take<char>(select_aux_bytes(g));
     int32_t *ws_sel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     int32_t *ws_nsel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     int32_t *Wlen = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
@@ -328,19 +354,9 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
     if (g.topk == 0) use_sel = sel;   // may be NULL: nothing is selected
 
     hipStream_t s = (hipStream_t)stream;
-    if (timing && timing->score_begin) {
-        if (hipEventRecord((hipEvent_t)timing->score_begin, s) != hipSuccess)
-            return launched(hipGetLastError(), "event record");
-    }
-    if ((st = launched(rea::launch_score(g, p->q, p->k, scores, gmax, num_cu, s), "score")) !=
-        REA_OK)
-        return st;
-    if (timing && timing->score_end) {
-        if (hipEventRecord((hipEvent_t)timing->score_end, s) != hipSuccess)
-            return launched(hipGetLastError(), "event record");
-    }
-    if ((st = launched(rea::launch_topk(g, scores, gmax, use_sel, use_nsel, s), "topk")) !=
-        REA_OK)
+    if ((st = launched(launch_select(g, p->q, p->k, scores, aux, use_sel, use_nsel, num_cu, s,
+                                     timing),
+                       "score_select")) != REA_OK)
         return st;
     if ((st = launched(rea::launch_gather_rope(g, p->k, p->v, p->q, use_sel, use_nsel, k_win,
                                                v_win, q_rot, Wlen, g.W_cap, s),

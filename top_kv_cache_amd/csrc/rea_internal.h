@@ -39,6 +39,15 @@ hipError_t launch_score(const Geom &g, const void *q, const void *k, double *spa
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
                        int32_t *sel, int32_t *n_sel, hipStream_t s);
 
+// Step 1 for blocks of 64 queries on MFMA (bf16, d 128, S a multiple of 32,
+// at most 4096 spans): approximate span scores with a proven error bound, then
+// an exact top-k that re-scores the uncertain spans in fp64.
+bool mfma_block_path(const Geom &g);
+size_t mfma_ws_bytes(const Geom &g);
+hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
+                                    double *span_scores, int32_t *sel, int32_t *n_sel,
+                                    void *ws, int num_cu, hipStream_t s);
+
 // Steps 2-3: window rows (K rotated fp32, V copied) + lengths, then the queries.
 hipError_t launch_gather_rope(const Geom &g, const void *k, const void *v, const void *q,
                               const int32_t *sel, const int32_t *n_sel, float *k_win,
