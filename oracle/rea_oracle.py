@@ -125,8 +125,8 @@ def span_scores_from_tokens(s: np.ndarray, spans, mid_lo: int) -> np.ndarray:
     return sig + 0.0
 
 
-def exact_span_score(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int, span) -> Fraction:
-    """Exact rational value of sigma for one span (inputs are dyadic floats)."""
+def _exact_span_score_fractions(q_blk, K_h, h, g, span) -> Fraction:
+    """Exact rational span score by direct Fraction arithmetic (slow)."""
     a, b = span
     total = Fraction(0)
     nb, _, d = q_blk.shape
@@ -142,6 +142,41 @@ def exact_span_score(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int, span) -
                 best = acc
         total += best
     return total
+
+
+def _lsb_exponent(x: np.ndarray):
+    """Largest e such that every element of x is a multiple of 2**e (None if all 0)."""
+    nz = x[x != 0]
+    if nz.size == 0:
+        return None
+    m, e = np.frexp(nz)                              # nz = m * 2**e, 0.5 <= |m| < 1
+    M = np.abs(np.ldexp(m, 53).astype(np.int64))     # exact integer significand
+    low = (M & -M).astype(np.float64)                # lowest set bit, a power of two
+    return int(np.min(e - 53 + np.log2(low).astype(np.int64)))
+
+
+def exact_span_score(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int, span) -> Fraction:
+    """Exact rational value of sigma for one span (inputs are dyadic floats).
+
+    Every product is a multiple of u = 2**(lsb(q) + lsb(K)); if every partial sum
+    of the token scores and of the block sum is bounded by 2**52 * u, all fp64
+    operations on these values are exact and the fp64 evaluation is the exact
+    value.  Otherwise the score is evaluated with Fractions.
+    """
+    a, b = span
+    nb, _, d = q_blk.shape
+    Q = q_blk[:, h * g:(h + 1) * g, :].reshape(nb * g, d)
+    Ks = K_h[a:b]
+    lq, lk = _lsb_exponent(Q), _lsb_exponent(Ks)
+    if lq is None or lk is None:
+        return Fraction(0)
+    unit = 2.0 ** (lq + lk)
+    bound = (np.abs(Q) @ np.abs(Ks).T).reshape(nb, g, -1).sum(axis=1) * (1.0 + 1e-9)
+    limit = 2.0 ** 52 * unit
+    if bound.max() < limit and bound.max(axis=1).sum() * (1.0 + 1e-9) < limit:
+        s = (Q @ Ks.T).reshape(nb, g, -1).sum(axis=1)
+        return Fraction(float(s.max(axis=1).sum()))
+    return _exact_span_score_fractions(q_blk, K_h, h, g, span)
 
 
 # --------------------------------------------------------------------------

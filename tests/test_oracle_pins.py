@@ -284,6 +284,24 @@ def test_exact_guard_resolves_near_tie():
     assert O.select_topk(sig, 2, lambda j: [1, 3, 2][j]) == [1, 2]
 
 
+def test_exact_score_fast_path_matches_fractions():
+    """The fp64-is-exact shortcut of the tie guard equals Fraction arithmetic,
+    and falls back to it when the exponent spread is too wide."""
+    rng = np.random.default_rng(12)
+    for kind in ("bf16", "int", "f32"):
+        q, K, V = rand_problem(rng, 3, 4, 2, 8, 40, kind)
+        for h in range(2):
+            for span in [(3, 9), (10, 11), (20, 40)]:
+                fast = O.exact_span_score(q, K[h], h, 2, span)
+                slow = O._exact_span_score_fractions(q, K[h], h, 2, span)
+                assert fast == slow, (kind, h, span)
+    # spread of 2^80 between terms: fp64 cannot hold the sum, Fractions must be used
+    q = np.array([[[1.0, 1.0]]])
+    K = np.array([[2.0 ** 40, 2.0 ** -40]])
+    assert O.exact_span_score(q, K, 0, 1, (0, 1)) == Fraction(2 ** 40) + Fraction(1, 2 ** 40)
+    assert O._lsb_exponent(np.array([0.75, 3.0, 0.0])) == -2
+
+
 # --------------------------------------------------------------------------
 # mutation tests: a planted mistake must fail at least one pin
 # --------------------------------------------------------------------------

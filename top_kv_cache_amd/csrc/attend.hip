@@ -265,6 +265,7 @@ size_t attend_ws_bytes(const Geom &g, int64_t W_cap) {
 hipError_t launch_attend(const Geom &g, const float *q_rot, const float *k_win,
                          const void *v_win, const int32_t *W, int64_t W_cap, float *out,
                          void *ws, hipStream_t s) {
+    if (mfma_attend_path(g)) return launch_attend_mfma(g, q_rot, k_win, v_win, W, W_cap, out, s);
     AttendArgs a;
     a.q_rot = q_rot;
     a.k_win = k_win;

@@ -54,7 +54,13 @@ hipError_t launch_gather_rope(const Geom &g, const void *k, const void *v, const
                               void *v_win, float *q_rot, int32_t *W, int64_t W_cap,
                               hipStream_t s);
 
-// Step 4: split-window attention + combine.
+// Step 4 for query blocks of at least 32 rows (bf16, d 128) on MFMA.
+bool mfma_attend_path(const Geom &g);
+hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_win,
+                              const void *v_win, const int32_t *W, int64_t W_cap, float *out,
+                              hipStream_t s);
+
+// Step 4: split-window attention + combine (MFMA for large query blocks).
 size_t attend_ws_bytes(const Geom &g, int64_t W_cap);
 hipError_t launch_attend(const Geom &g, const float *q_rot, const float *k_win,
                          const void *v_win, const int32_t *W, int64_t W_cap, float *out,
