@@ -111,8 +111,23 @@ __global__ __launch_bounds__(kD) void k_qprep(PrepArgs a) {
 
 // ---------------------------------------------------------------------------
 // k_score_mfma: grid (n_qg * Hkv * NR) with the query group slowest, so the
-// workgroups sharing a key range of one head sit on one XCD; 256 threads.
+// workgroups sharing a key range of one head sit on one XCD; 256 threads,
+// two workgroups per CU so that one hides the other's LDS and reduction
+// latency.
+//
+// Key tiles stream through a 6-deep LDS ring filled by global_load_lds
+// (16 bytes per lane straight into LDS, no staging registers), so five tiles
+// are in flight while one is multiplied.  Within a tile, 16-byte chunk c of
+// token row m is stored at slot c ^ (m % 16), which makes the MFMA operand
+// reads bank-conflict free.  Span results are buffered in LDS and written
+// after the loop, so only the ring's loads count in vmcnt.  The key norms a
+// span's error bound needs are computed by one wave of the whole grid per
+// span, spread evenly over the query groups.
 // ---------------------------------------------------------------------------
+constexpr int kNBuf = 6;
+constexpr int kTileBytes = kTile * kD * 2;          // 8 KB
+constexpr int kMaxSpansWG = 512;
+
 struct MfmaArgs {
     const unsigned char *k;     // K cache (bf16)
     const uint16_t *qhl;        // [Hkv][n_q][256]
@@ -125,16 +140,115 @@ struct MfmaArgs {
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *(const uint4 *)p; }
 
-__global__ __launch_bounds__(256) void k_score_mfma(MfmaArgs a) {
-    __shared__ __align__(16) uint16_t kt[2][kTile][kRowPad];
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// Eight 16-byte LDS reads issued together and completed (lgkmcnt(0)) inside
+// one asm block.  Written as asm so that the compiler does not make them wait
+// for every DMA still in flight to other ring slots; the ring slot read here
+// is complete by the explicit vmcnt wait and barrier that precede the call.
+__device__ __forceinline__ void lds_read8(const uint32_t (&ad)[8], uint4 (&o)[8]) {
+    u32x4v r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+          "v"(ad[7])
+        : "memory");
+    o[0] = make_uint4(r0.x, r0.y, r0.z, r0.w);
+    o[1] = make_uint4(r1.x, r1.y, r1.z, r1.w);
+    o[2] = make_uint4(r2.x, r2.y, r2.z, r2.w);
+    o[3] = make_uint4(r3.x, r3.y, r3.z, r3.w);
+    o[4] = make_uint4(r4.x, r4.y, r4.z, r4.w);
+    o[5] = make_uint4(r5.x, r5.y, r5.z, r5.w);
+    o[6] = make_uint4(r6.x, r6.y, r6.z, r6.w);
+    o[7] = make_uint4(r7.x, r7.y, r7.z, r7.w);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(const void __attribute__((address_space(3))) *)p;
+}
+
+// s_waitcnt vmcnt(n) for even n <= 14 (expcnt and lgkmcnt not waited for)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0xF78); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0xF7A); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0xF7C); break;
+    default: __builtin_amdgcn_s_waitcnt(0xF7E); break;
+    }
+}
+
+// The value of lane l ^ 32 (v_permlane32_swap: either result half may hold
+// the partner, so the caller combines both with a symmetric operation).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ double pair_sum(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    const double a = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0]));
+    const double b = __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+    return a + b;     // own + partner in either order: the same value
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Every lane of each 16-lane row ends with the row's sum (max): partners are
+// lane^1, lane^2, then the mirror within 8 and within 16 lanes, each a
+// symmetric pairing, so both partners compute the same value.
+__device__ __forceinline__ double row_sum16(double v) {
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    return v;
+}
+__device__ __forceinline__ double row_max16(double v) {
+    v = fmax(v, dpp_f64<0xB1>(v));
+    v = fmax(v, dpp_f64<0x4E>(v));
+    v = fmax(v, dpp_f64<0x141>(v));
+    v = fmax(v, dpp_f64<0x140>(v));
+    return v;
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__global__ __launch_bounds__(256, 2) void k_score_mfma(MfmaArgs a) {
+    __shared__ __align__(16) unsigned char ring[kNBuf * kTileBytes];
+    __shared__ double res[kWavesM][kMaxSpansWG];
+    __shared__ double kres[kMaxSpansWG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int units = a.Hkv * a.NR;
+    const int n_qg = gridDim.x / units;
     const int qg = blockIdx.x / units;
     const int rest = blockIdx.x % units;
     const int h = rest / a.NR, r = rest % a.NR;
     const int b = qg * kWavesM + wave;              // this wave's block
     const bool active = b < a.n_blk;
-    const int64_t j0 = (int64_t)r * a.n_spans / a.NR, j1 = (int64_t)(r + 1) * a.n_spans / a.NR;
+    const int j0 = (int)((int64_t)r * a.n_spans / a.NR), j1 = (int)((int64_t)(r + 1) * a.n_spans / a.NR);
     const int tiles_per_span = a.S / kTile;
 
     // B fragments: [hi|lo] of the wave's 64 queries, two 32-query tiles x 16 k-steps
@@ -149,54 +263,60 @@ __global__ __launch_bounds__(256) void k_score_mfma(MfmaArgs a) {
             for (int ks = 0; ks < 16; ++ks) qf[t][ks] = ld16(row + ks * 16 + kb * 8);
         }
     }
+    __builtin_amdgcn_s_waitcnt(0xF70);              // fragments in registers before the ring starts
 
     const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes;
-    // staging: thread -> (token rows tid/16 and tid/16 + 16, 16-byte chunk tid%16);
-    // the next tile's rows are loaded into registers before this tile's MFMAs
-    // and written to the other LDS buffer after them
-    const int srow = tid >> 4, schk = tid & 15;
-    uint4 nxt[2];
-    auto load_rows = [&](int64_t t0) {
+    const int n_tiles = (j1 - j0) * tiles_per_span;
+    // each wave moves 2 x 1 KB (8 token rows) of every tile; (ij, isub) is the
+    // span and sub-tile of the next tile to issue
+    int ij = j0, isub = 0, it_issue = 0;
+    auto issue_next = [&]() {
+        if (it_issue >= n_tiles) return;
+        const int64_t t0 = a.mid_lo + (int64_t)ij * a.S + isub * kTile;
+        unsigned char *dst = ring + (it_issue % kNBuf) * kTileBytes;
 #pragma unroll
-        for (int hr = 0; hr < 2; ++hr) {
-            const int64_t t = t0 + srow + hr * 16;
-            nxt[hr] = t < a.mid_hi ? ld16(kh + t * a.st_bytes + schk * 16) : make_uint4(0u, 0u, 0u, 0u);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int row = (wave * 2 + jj) * 4 + (lane >> 4);
+            const int chunk = (lane & 15) ^ (row & 15);
+            int64_t t = t0 + row;
+            if (t >= a.mid_hi) t = a.mid_hi - 1;       // rows past the middle are masked later
+            __builtin_amdgcn_global_load_lds((const void *)(kh + t * a.st_bytes + chunk * 16),
+                                             (void __attribute__((address_space(3))) *)(dst + (wave * 2 + jj) * 1024),
+                                             16, 0, 0);
+        }
+        ++it_issue;
+        if (++isub == tiles_per_span) {
+            isub = 0;
+            ++ij;
         }
     };
-    auto store_rows = [&](int bufi) {
-#pragma unroll
-        for (int hr = 0; hr < 2; ++hr) *(uint4 *)&kt[bufi][srow + hr * 16][schk * 8] = nxt[hr];
-    };
-    auto tile_t0 = [&](int64_t it) {
-        return a.mid_lo + (j0 + it / tiles_per_span) * a.S + (int64_t)(it % tiles_per_span) * kTile;
-    };
+    for (int i = 0; i < kNBuf - 1; ++i) issue_next();
 
-    const int64_t n_tiles = (j1 - j0) * tiles_per_span;
-    int buf = 0;
-    if (n_tiles > 0) {
-        load_rows(tile_t0(0));
-        store_rows(0);
-    }
-    __syncthreads();
-    float run[2] = {-INFINITY, -INFINITY};   // running max over the span's tiles
-    double kn_run = 0.0;                     // running max of squared key norms
-    for (int64_t it = 0; it < n_tiles; ++it) {
-        const int64_t j = j0 + it / tiles_per_span;
-        const int sub = (int)(it % tiles_per_span);
-        const int64_t t0 = tile_t0(it);
-        const bool more = it + 1 < n_tiles;
-        if (more) load_rows(tile_t0(it + 1));
-        if (sub == 0) {
-            run[0] = -INFINITY;
-            run[1] = -INFINITY;
-            kn_run = 0.0;
-        }
-        // A fragments: token row m = lane%32, channels ks*16 + (lane/32)*8 .. +8
+    float run[2] = {-INFINITY, -INFINITY};   // lane-local running max over the span's tiles
+    double kn_run = 0.0;                     // running max of squared key norms (owner wave)
+    int j = j0, sub = 0;
+    for (int it = 0; it < n_tiles; ++it) {
+        int later = n_tiles - 1 - it;                 // tiles issued after this one
+        if (later > kNBuf - 2) later = kNBuf - 2;
+        wait_vmcnt(2 * later);
+        // A plain barrier, not __syncthreads(): its release fence would wait for
+        // every DMA in flight.  This wave's copies into the slot are complete by
+        // the vmcnt wait above, the other waves' by the barrier; every wave
+        // finished reading (lgkmcnt(0)) the slot refilled below before it got here.
+        __builtin_amdgcn_s_barrier();
+        issue_next();
+        const unsigned char *tb = ring + (it % kNBuf) * kTileBytes;
+        const int64_t t0 = a.mid_lo + (int64_t)j * a.S + sub * kTile;
+        const bool owner = (j & 3) == wave && ((j >> 2) % n_qg) == qg;
+        // A fragments: token row m = lane%32, channel chunk ks*2 + lane/32
         uint4 af[8];
         {
             const int m = lane & 31, kb = lane >> 5;
+            const uint32_t base = lds_addr(tb) + m * 256;
+            uint32_t ad[8];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) af[ks] = *(const uint4 *)&kt[buf][m][ks * 16 + kb * 8];
+            for (int ks = 0; ks < 8; ++ks) ad[ks] = base + (((ks * 2 + kb) ^ (m & 15)) * 16);
+            lds_read8(ad, af);
         }
         f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
@@ -208,46 +328,69 @@ __global__ __launch_bounds__(256) void k_score_mfma(MfmaArgs a) {
                                                            acc1, 0, 0, 0);
         }
         // tokens past the middle (a short last span) do not count
-        const int64_t valid = a.mid_hi - t0;           // tokens of this tile inside the middle
-        float m0 = -INFINITY, m1 = -INFINITY;
+        const int64_t valid = a.mid_hi - t0;
+        if (valid >= kTile) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-            if (row < valid) {
-                m0 = fmaxf(m0, acc0[rr]);
-                m1 = fmaxf(m1, acc1[rr]);
+            for (int rr = 0; rr < 16; ++rr) {
+                run[0] = fmaxf(run[0], acc0[rr]);
+                run[1] = fmaxf(run[1], acc1[rr]);
             }
-        }
-        m0 = fmaxf(m0, __shfl_xor(m0, 32));
-        m1 = fmaxf(m1, __shfl_xor(m1, 32));
-        run[0] = fmaxf(run[0], m0);
-        run[1] = fmaxf(run[1], m1);
-        if (qg == 0 && wave == 0 && lane < kTile) {
-            // squared norm of key row `lane` of this tile, fp64
-            if (lane < valid) {
-                double s = 0.0;
-                for (int c = 0; c < kD; ++c) {
-                    const double x = bf16_to_f64(kt[buf][lane][c]);
-                    s = fma(x, x, s);
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+                if (row < valid) {
+                    run[0] = fmaxf(run[0], acc0[rr]);
+                    run[1] = fmaxf(run[1], acc1[rr]);
                 }
-                kn_run = fmax(kn_run, s);
             }
         }
-        if (sub == tiles_per_span - 1) {
-            // span done: sum over the block's 64 queries (lanes 0..31 hold queries
-            // n and 32+n after the cross-half max)
-            double v = (double)run[0] + (double)run[1];
-            for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o);
-            if (active && lane == 0) a.out[((int64_t)b * a.Hkv + h) * a.n_spans + j] = v + 0.0;
-            if (qg == 0 && wave == 0) {
-                double kn = kn_run;
-                for (int o = 16; o > 0; o >>= 1) kn = fmax(kn, __shfl_xor(kn, o));
-                if (lane == 0) a.kbar[(int64_t)h * a.n_spans + j] = sqrt(kn) * (1.0 + 1e-12);
+        if (owner) {
+            // squared norm of key row lane%32: this lane's half of the channels
+            // (its A fragments) plus the partner lane's half
+            double sq = 0.0;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const uint32_t w4[4] = {af[ks].x, af[ks].y, af[ks].z, af[ks].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const double x0 = (double)__uint_as_float(w4[e] << 16);
+                    const double x1 = (double)__uint_as_float(w4[e] & 0xffff0000u);
+                    sq = fma(x0, x0, sq);
+                    sq = fma(x1, x1, sq);
+                }
             }
+            sq = pair_sum(sq);
+            if ((lane & 31) < valid) kn_run = fmax(kn_run, sq);
         }
-        if (more) store_rows(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
+        if (++sub == tiles_per_span) {
+            // span done: per-query maximum (lanes l and l^32 hold the two row
+            // halves), then the sum over the block's 64 queries
+            const float m0 = pair_max(run[0]), m1 = pair_max(run[1]);
+            const double v = row_sum16((double)m0 + (double)m1);
+            const double tot = readlane_f64(v, 0) + readlane_f64(v, 16);
+            if (lane == 0) res[wave][j - j0] = tot + 0.0;
+            if (owner) {
+                const double kn = row_max16(kn_run);
+                const double km = fmax(readlane_f64(kn, 0), readlane_f64(kn, 16));
+                if (lane == 0) kres[j - j0] = sqrt(km) * (1.0 + 1e-12);
+            }
+            run[0] = -INFINITY;
+            run[1] = -INFINITY;
+            kn_run = 0.0;
+            sub = 0;
+            ++j;
+        }
+    }
+    __syncthreads();
+    const int nsp = j1 - j0;
+    for (int x = tid; x < nsp; x += 256) {
+#pragma unroll
+        for (int w = 0; w < kWavesM; ++w) {
+            const int bw = qg * kWavesM + w;
+            if (bw < a.n_blk) a.out[((int64_t)bw * a.Hkv + h) * a.n_spans + j0 + x] = res[w][x];
+        }
+        if ((((j0 + x) >> 2) % n_qg) == qg) a.kbar[(int64_t)h * a.n_spans + j0 + x] = kres[x];
     }
 }
 
@@ -602,6 +745,8 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     const int n_qg = (g.n_blk + kWavesM - 1) / kWavesM;
     const int64_t units = (int64_t)n_qg * g.Hkv;
     int64_t NR = ((int64_t)(num_cu > 0 ? num_cu : 256) * 2 + units - 1) / units;
+    const int64_t NRmin = (g.n_spans + kMaxSpansWG - 1) / kMaxSpansWG;
+    if (NR < NRmin) NR = NRmin;
     if (NR > g.n_spans) NR = g.n_spans;
     if (NR < 1) NR = 1;
     ma.NR = (int)NR;
