@@ -8,9 +8,9 @@ before the timed region.
 
 Prints one JSON line:  value = middle-cache keys scored per second over the
 whole step; ms_per_step = decode-step latency; roofline = the scoring kernel's
-achieved HBM bandwidth from HIP events recorded around each of its launches on
-the launch stream; cpu_baseline = the CPU oracle on one layer of the same
-workload.
+achieved HBM bandwidth (decode) or bf16 MFMA rate (query blocks, --config 4)
+from HIP events recorded around each of its launches on the launch stream;
+cpu_baseline = the CPU oracle on whole layers of the same workload.
 """
 import argparse
 import ctypes
@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "middle-cache keys scored/s (achieved HBM GB/s) + decode-step latency @1M ctx"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_decode_llama8b_1m_traffic.txt")
 SCORE_SRC = os.path.join(ROOT, "top_kv_cache_amd", "csrc", "score.hip")
 
@@ -195,12 +196,30 @@ def main():
     ms_per_step = total_ms / args.steps
     value = keys_per_layer * n_layers / (ms_per_step / 1e3)
     k1_ms = sum(k1) / len(k1)
-    score_bytes = (keys_per_layer * w.d * (2 if w.dtype == "bf16" else 4)
-                   + w.n_spans * w.Hkv * 8 + w.Hq * w.d * (2 if w.dtype == "bf16" else 4))
-    achieved = score_bytes / (k1_ms / 1e3) / 1e9
+    if w.block_q == 1:
+        # decode: the scoring kernel streams the middle keys once
+        score_bytes = (keys_per_layer * w.d * (2 if w.dtype == "bf16" else 4)
+                       + w.n_spans * w.Hkv * 8 + w.Hq * w.d * (2 if w.dtype == "bf16" else 4))
+        achieved = score_bytes / (k1_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(score_bytes),
+                    "kernel": "k_score_decode", "algorithmic_bytes_per_launch": score_bytes,
+                    "avg_launch_us": k1_ms * 1e3}
+        log(f"[bench] scoring kernel {k1_ms * 1e3:.1f} us/launch = {achieved:.0f} GB/s "
+            f"({achieved / HBM_PEAK_GBS * 100:.1f}% of {HBM_PEAK_GBS:.0f})")
+    else:
+        # query blocks: a bf16 GEMM of every query's group-summed vector against
+        # every middle key (the kernel runs it twice, for the hi and lo halves)
+        flops = 2.0 * w.n_q * keys_per_layer * w.d
+        achieved = flops / (k1_ms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                    "kernel": "k_score_mfma", "algorithmic_flops_per_launch": flops,
+                    "mfma_flops_issued_per_launch": 2 * flops, "avg_launch_us": k1_ms * 1e3}
+        log(f"[bench] scoring kernel {k1_ms * 1e3:.1f} us/launch = {achieved:.0f} TFLOP/s "
+            f"algorithmic, {2 * achieved:.0f} TFLOP/s issued on MFMA "
+            f"({2 * achieved / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of {MFMA_BF16_PEAK_TFLOPS:.0f})")
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
-        f"scoring kernel {k1_ms * 1e3:.1f} us/launch = {achieved:.0f} GB/s "
-        f"({achieved / HBM_PEAK_GBS * 100:.1f}% of {HBM_PEAK_GBS:.0f}), "
         f"{value / 1e9:.2f} G keys/s")
 
     res = {
@@ -212,10 +231,7 @@ def main():
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "storage": w.dtype,
                    "G": w.G, "S": w.S, "topk": w.topk, "L": w.L,
                    "needles_per_kv_head": w.needles, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(score_bytes),
-                     "kernel": "k_score_decode", "algorithmic_bytes_per_launch": score_bytes,
-                     "avg_launch_us": k1_ms * 1e3},
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     del steps_l, outs, ws

@@ -76,6 +76,12 @@ def mfma_path(w):
             and 0 < w.n_spans <= 4096)
 
 
+def fused_path(w):
+    """Up to 8 query rows per (block, KV head): rea_decode_step runs steps 2-4
+    fused, reading the window straight from the cache."""
+    return w.block_q * w.g <= 8
+
+
 def compare_head(w, gpu, ora, h, check_windows=True):
     """Assert parity of KV head h; returns the max-abs output error."""
     g, nb = w.g, len(ora["sel"])
@@ -114,5 +120,12 @@ def compare_head(w, gpu, ora, h, check_windows=True):
     err = float(np.abs(ogot - oref).max())
     assert err <= TOL[w.dtype], ("out", h, err)
     if "out" in gpu:
-        assert np.array_equal(gpu["out"][:, h * g:(h + 1) * g], gpu["out_step"][:, h * g:(h + 1) * g])
+        got = gpu["out"][:, h * g:(h + 1) * g]
+        if fused_path(w):
+            # rea_decode_step attends straight from the cache: same tolerance,
+            # different rounding than window_attend over the written window
+            err_sep = float(np.abs(got.astype(np.float64) - oref).max())
+            assert err_sep <= TOL[w.dtype], ("out (window_attend)", h, err_sep)
+        else:
+            assert np.array_equal(got, gpu["out_step"][:, h * g:(h + 1) * g])
     return err

@@ -1,0 +1,539 @@
+// decode_attend.hip - steps 2-4 fused for small query groups (decode).
+//
+// Same result as gather + RoPE (window.hip) followed by window attention
+// (attend.hip), without writing the window: every window row is read straight
+// from the cache, rotated to its window position in registers and attended.
+// The window is global [0, G') ++ selected spans in ascending order ++ local
+// [T-L', T) (OpenReview discussion, "Decoding Phase" pseudocode); row w turns
+// by angle w * theta^(-2c/d) (rotate-half RoPE, research-map summary,
+// "Approach": positions are assigned after the concatenation); query i of a
+// block is rotated to W - n_q + i and sees rows w <= that position.
+//
+//   k_fused_split    one workgroup per (128-row split of the window, KV head,
+//                    block), 4 waves x 32 rows.  One round trip fetches the
+//                    selection slots the split can touch and the raw queries;
+//                    then every row's K and V load is issued at once, and the
+//                    queries are rotated while those are in flight (barriers
+//                    order LDS only).  A 16-lane DPP row of a wave is a stream
+//                    of 8 consecutive window rows; a lane holds D/32 channel
+//                    pairs (c, c + D/2) of its stream's rows.  The rotation
+//                    angle of row w+1 follows from row w's by one fp64 complex
+//                    multiplication with (cos, sin) of the channel's
+//                    frequency; the rotated key is rounded to fp32.  Per
+//                    stream the 8 logits of each query row give an exact max,
+//                    weights and P.V; streams and waves are merged with the
+//                    usual (m, l, acc) rule and one partial per split is
+//                    written.
+//   k_fused_combine  one workgroup per (KV head, block) merges the splits:
+//                    out = sum_s e^(m_s-M) acc_s / sum_s e^(m_s-M) l_s.
+#include "rea_internal.h"
+
+#include <math.h>
+
+namespace rea {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSL = 8;                          // rows per stream
+constexpr int kRowsPerSplit = 4 * 4 * kSL;      // waves x streams x rows
+constexpr int kSelStage = kRowsPerSplit + 2;    // selection slots a split can touch (S = 1)
+constexpr int kCombBatch = 16;                  // partials loaded together by the merge
+
+struct FusedArgs {
+    const unsigned char *k, *v;
+    const void *q;
+    const int32_t *sel, *n_sel;
+    float *part_acc;        // [n_blk][Hkv][n_split][QR][D]
+    float *part_ml;         // [n_blk][Hkv][n_split][QR][2]: m, l
+    float *out;             // [n_q][Hq][D]
+    int64_t sh, st;         // elements
+    int64_t T, Gp, Lp, mid_lo, n_spans;
+    int S, last_len, topk, Hkv, Hq, g, n_q, block_q, QR, n_split;
+    float scale;
+    double frev_hi[kMaxHalfDim], frev_lo[kMaxHalfDim];   // theta_c / 2pi as hi + lo
+    double step_c[kMaxHalfDim], step_s[kMaxHalfDim];     // cos, sin of theta_c
+};
+
+// (cos, sin) of the angle w * theta_c, from the fractional number of turns
+// t = frac(w * theta_c / 2pi): the product is split exactly (fma) so t is
+// good to ~1e-16 for any w < 2^31; then the quadrant is taken out and Taylor
+// polynomials in fp32 on |x| <= pi/4 give cos and sin to fp32 rounding
+// (truncation below 3e-9).
+__device__ __forceinline__ void rope_cs(int64_t w, double fhi, double flo, float &c, float &s) {
+    const double wd = (double)w;
+    const double p = wd * fhi;
+    const double e = fma(wd, fhi, -p);
+    const double t = (p - rint(p)) + (e + wd * flo);
+    const double qd = rint(t * 4.0);
+    const int q = (int)qd & 3;
+    const float x = (float)(t - qd * 0.25) * 6.28318530717958647692f;
+    const float x2 = x * x;
+    float sp = fmaf(x2, 2.75573192e-6f, -1.98412698e-4f);      // 1/9!, -1/7!
+    sp = fmaf(x2, sp, 8.33333333e-3f);                          // 1/5!
+    sp = fmaf(x2, sp, -1.66666667e-1f);                         // -1/3!
+    const float sx = fmaf(x * x2, sp, x);
+    float cp = fmaf(x2, -2.75573192e-7f, 2.48015873e-5f);       // -1/10!, 1/8!
+    cp = fmaf(x2, cp, -1.38888889e-3f);                         // -1/6!
+    cp = fmaf(x2, cp, 4.16666667e-2f);                          // 1/4!
+    cp = fmaf(x2, cp, -0.5f);
+    const float cx = fmaf(x2, cp, 1.f);
+    c = q == 0 ? cx : q == 1 ? -sx : q == 2 ? -cx : sx;
+    s = q == 0 ? sx : q == 1 ? cx : q == 2 ? -sx : -cx;
+}
+
+// PPL consecutive stored elements (the lane's share of one half of a row).
+template <typename TIn, int PPL> struct Part;
+template <> struct Part<uint16_t, 4> {
+    uint2 a;
+    __device__ void load(const uint16_t *p) { a = *(const uint2 *)p; }
+    __device__ void get(float (&x)[4]) const {
+        x[0] = __uint_as_float(a.x << 16);
+        x[1] = __uint_as_float(a.x & 0xffff0000u);
+        x[2] = __uint_as_float(a.y << 16);
+        x[3] = __uint_as_float(a.y & 0xffff0000u);
+    }
+};
+template <> struct Part<uint16_t, 2> {
+    uint32_t a;
+    __device__ void load(const uint16_t *p) { a = *(const uint32_t *)p; }
+    __device__ void get(float (&x)[2]) const {
+        x[0] = __uint_as_float(a << 16);
+        x[1] = __uint_as_float(a & 0xffff0000u);
+    }
+};
+template <> struct Part<float, 4> {
+    float4 a;
+    __device__ void load(const float *p) { a = *(const float4 *)p; }
+    __device__ void get(float (&x)[4]) const {
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    }
+};
+template <> struct Part<float, 2> {
+    float2 a;
+    __device__ void load(const float *p) { a = *(const float2 *)p; }
+    __device__ void get(float (&x)[2]) const {
+        x[0] = a.x; x[1] = a.y;
+    }
+};
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum
+// (partners lane^1, lane^2, mirror within 8, mirror within 16).
+__device__ __forceinline__ float row_sum16f(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
+// Merge (m, l, acc) of another stream into this one.
+template <int N>
+__device__ __forceinline__ void merge(float &m, float &l, float (&acc)[N], float mo, float lo,
+                                      const float (&acco)[N]) {
+    const float mn = fmaxf(m, mo);
+    const float f = (m == -INFINITY) ? 0.f : expf(m - mn);
+    const float fo = (mo == -INFINITY) ? 0.f : expf(mo - mn);
+    l = l * f + lo * fo;
+#pragma unroll
+    for (int e = 0; e < N; ++e) acc[e] = acc[e] * f + acco[e] * fo;
+    m = mn;
+}
+
+// Barrier that orders LDS only: global loads issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <typename TIn, int D, int QRM>
+__global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
+    constexpr int HALF = D / 2;
+    constexpr int PPL = HALF / 16;              // channel pairs per lane
+    constexpr int NA = 2 * PPL;                 // accumulated channels per lane and query row
+    constexpr int QPT = (QRM * HALF + kThreads - 1) / kThreads;   // query pairs per thread
+    __shared__ float qs[QRM][D];
+    __shared__ int32_t ssel[kSelStage];
+    __shared__ double tab[HALF][4];             // theta_c/2pi (hi, lo), cos and sin of theta_c
+    __shared__ float wm[4][QRM], wl[4][QRM];
+    __shared__ float wacc[4][QRM][D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = (int64_t)b * a.Hkv + h;
+    const int64_t w0 = (int64_t)sp * kRowsPerSplit;
+
+    // One round trip: the selection count, the selection slots this split's
+    // rows can touch, and the raw query elements (all loads before any store).
+    const int ns = a.n_sel[bh];
+    const int64_t slot0 = w0 > a.Gp ? (w0 - a.Gp) / a.S : 0;
+    int32_t sv = 0;
+    if (a.topk > 0 && tid < kSelStage && slot0 + tid < a.topk) sv = a.sel[bh * a.topk + slot0 + tid];
+    float qx1[QPT], qx2[QPT];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int idx = tid + j * kThreads, r = idx / HALF, c = idx % HALF;
+        qx1[j] = qx2[j] = 0.f;
+        if (r < a.QR) {
+            const int64_t i = (int64_t)b * a.block_q + r / a.g;
+            const TIn *qp = (const TIn *)a.q + (i * a.Hq + h * a.g + r % a.g) * D;
+            if (sizeof(TIn) == 2) {
+                qx1[j] = __uint_as_float((uint32_t)((const uint16_t *)qp)[c] << 16);
+                qx2[j] = __uint_as_float((uint32_t)((const uint16_t *)qp)[c + HALF] << 16);
+            } else {
+                qx1[j] = ((const float *)qp)[c];
+                qx2[j] = ((const float *)qp)[c + HALF];
+            }
+        }
+    }
+    double fh = 0.0, fl = 0.0, scs = 0.0, ssn = 0.0;
+    if (tid < HALF) {
+        fh = a.frev_hi[tid];
+        fl = a.frev_lo[tid];
+        scs = a.step_c[tid];
+        ssn = a.step_s[tid];
+    }
+    if (tid < kSelStage) ssel[tid] = sv;
+    if (tid < HALF) {
+        tab[tid][0] = fh;
+        tab[tid][1] = fl;
+        tab[tid][2] = scs;
+        tab[tid][3] = ssn;
+    }
+    // window length: only span n_spans-1 can be short, and a sorted selection
+    // holds it last
+    int64_t sel_len = (int64_t)ns * a.S;
+    if (a.last_len != a.S && ns > 0 && a.sel[bh * a.topk + ns - 1] == a.n_spans - 1)
+        sel_len -= a.S - a.last_len;
+    const int64_t Wbh = a.Gp + sel_len + a.Lp;
+    __syncthreads();
+
+    // this stream's rows: source token and K, V.  Rows past the window load
+    // token 0 (finite data whose logits are masked and weights are 0), so every
+    // load is unconditional and all of them are in flight together.
+    // (oq, orr) = (slot, offset) of window row max(w, G') within the selected spans.
+    const int rho = lane >> 4, c0 = (lane & 15) * PPL;
+    const int64_t wf = w0 + wave * (4 * kSL) + rho * kSL;
+    Part<TIn, PPL> k1[kSL], k2[kSL], v1[kSL], v2[kSL];
+    {
+        const TIn *kb = (const TIn *)a.k + (int64_t)h * a.sh;
+        const TIn *vb = (const TIn *)a.v + (int64_t)h * a.sh;
+        const int64_t o0 = wf - a.Gp;
+        const uint32_t oc = (uint32_t)(o0 > 0 ? o0 : 0);
+        int oq = (int)(oc / (uint32_t)a.S), orr = (int)(oc - (uint32_t)oq * (uint32_t)a.S);
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) {
+            const int64_t w = wf + i, o = o0 + i;
+            int64_t src = 0;
+            if (w < Wbh) {
+                if (o < 0)
+                    src = w;
+                else if (o < sel_len)
+                    src = a.mid_lo + (int64_t)ssel[oq - slot0] * a.S + orr;
+                else
+                    src = a.T - a.Lp + (o - sel_len);
+            }
+            const int64_t row = src * a.st;
+            k1[i].load(kb + row + c0);
+            k2[i].load(kb + row + c0 + HALF);
+            v1[i].load(vb + row + c0);
+            v2[i].load(vb + row + c0 + HALF);
+            if (o >= 0 && ++orr == a.S) {
+                orr = 0;
+                ++oq;
+            }
+        }
+    }
+
+    // while they load: the query rows r = (query r / g, head h*g + r % g)
+    // rotated to their positions and rounded to fp32
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int idx = tid + j * kThreads, r = idx / HALF, c = idx % HALF;
+        if (r < QRM) {
+            float y1 = 0.f, y2 = 0.f;
+            if (r < a.QR) {
+                const int64_t i = (int64_t)b * a.block_q + r / a.g;
+                float co, sn;
+                rope_cs(Wbh - a.n_q + i, tab[c][0], tab[c][1], co, sn);
+                y1 = qx1[j] * co - qx2[j] * sn;
+                y2 = qx2[j] * co + qx1[j] * sn;
+            }
+            qs[r][c] = y1;
+            qs[r][c + HALF] = y2;
+        }
+    }
+    lds_barrier();
+
+    float q1[QRM][PPL], q2[QRM][PPL];
+#pragma unroll
+    for (int r = 0; r < QRM; ++r)
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+            q1[r][p] = qs[r][c0 + p];
+            q2[r][p] = qs[r][c0 + p + HALF];
+        }
+    // rotation of the stream's first row, and the per-row step (fp64, so the
+    // 7 steps add no error of note)
+    double cs[PPL], sn[PPL], cst[PPL], snt[PPL];
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+        float c1, s1;
+        rope_cs(wf, tab[c0 + p][0], tab[c0 + p][1], c1, s1);
+        cs[p] = c1;
+        sn[p] = s1;
+        cst[p] = tab[c0 + p][2];
+        snt[p] = tab[c0 + p][3];
+    }
+
+    // logits of the stream's rows
+    float lg[kSL][QRM];
+#pragma unroll
+    for (int i = 0; i < kSL; ++i) {
+        const int64_t w = wf + i;
+        float x1[PPL], x2[PPL];
+        k1[i].get(x1);
+        k2[i].get(x2);
+        float y1[PPL], y2[PPL];
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+            const float c = (float)cs[p], s = (float)sn[p];
+            y1[p] = x1[p] * c - x2[p] * s;
+            y2[p] = x2[p] * c + x1[p] * s;
+            const double cn = cs[p] * cst[p] - sn[p] * snt[p];
+            sn[p] = sn[p] * cst[p] + cs[p] * snt[p];
+            cs[p] = cn;
+        }
+#pragma unroll
+        for (int r = 0; r < QRM; ++r) {
+            float d = 0.f;
+#pragma unroll
+            for (int p = 0; p < PPL; ++p) {
+                d = fmaf(q1[r][p], y1[p], d);
+                d = fmaf(q2[r][p], y2[p], d);
+            }
+            d = row_sum16f(d) * a.scale;
+            const int64_t pos = Wbh - a.n_q + ((int64_t)b * a.block_q + r / a.g);
+            lg[i][r] = (w < Wbh && w <= pos && r < a.QR) ? d : -INFINITY;
+        }
+    }
+
+    // exact softmax statistics of the stream, then P.V
+    float m[QRM], l[QRM], acc[QRM][NA];
+#pragma unroll
+    for (int r = 0; r < QRM; ++r) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) mx = fmaxf(mx, lg[i][r]);
+        m[r] = mx;
+        l[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < NA; ++e) acc[r][e] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kSL; ++i) {
+        float x1[PPL], x2[PPL];
+        v1[i].get(x1);
+        v2[i].get(x2);
+#pragma unroll
+        for (int r = 0; r < QRM; ++r) {
+            const float p = (lg[i][r] == -INFINITY) ? 0.f : expf(lg[i][r] - m[r]);
+            l[r] += p;
+#pragma unroll
+            for (int e = 0; e < PPL; ++e) {
+                acc[r][e] = fmaf(p, x1[e], acc[r][e]);
+                acc[r][PPL + e] = fmaf(p, x2[e], acc[r][PPL + e]);
+            }
+        }
+    }
+
+    // merge the wave's four streams (lanes l, l^16, l^32, l^48 hold the same channels)
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+#pragma unroll
+        for (int r = 0; r < QRM; ++r) {
+            float acco[NA];
+#pragma unroll
+            for (int e = 0; e < NA; ++e) acco[e] = __shfl_xor(acc[r][e], o);
+            const float mo = __shfl_xor(m[r], o), lo = __shfl_xor(l[r], o);
+            merge<NA>(m[r], l[r], acc[r], mo, lo, acco);
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int r = 0; r < QRM; ++r) {
+#pragma unroll
+            for (int p = 0; p < PPL; ++p) {
+                wacc[wave][r][c0 + p] = acc[r][p];
+                wacc[wave][r][c0 + p + HALF] = acc[r][PPL + p];
+            }
+            if (lane == 0) {
+                wm[wave][r] = m[r];
+                wl[wave][r] = l[r];
+            }
+        }
+    }
+    __syncthreads();
+    // merge the four waves and write the split's partial
+    const int64_t pbase = bh * a.n_split * a.QR;
+    for (int idx = tid; idx < a.QR * D; idx += kThreads) {
+        const int r = idx / D, c = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][r]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = (wm[w][r] == -INFINITY) ? 0.f : expf(wm[w][r] - M);
+            L += wl[w][r] * f;
+            A += wacc[w][r][c] * f;
+        }
+        const int64_t slot = pbase + (int64_t)sp * a.QR + r;
+        a.part_acc[slot * D + c] = A;
+        if (c == 0) *(float2 *)(a.part_ml + slot * 2) = make_float2(M, L);
+    }
+
+}
+
+// grid (Hkv, n_blk): merges the splits of one (block, KV head).  Thread =
+// (query row r, channel quad, split phase j); each thread folds its splits
+// into a running (m, l, acc), loading kCombBatch partials at a time, and the
+// phases are folded in LDS.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_fused_combine(FusedArgs a) {
+    constexpr int NQ = D / 4;
+    __shared__ float cm[kThreads], cl[kThreads];
+    __shared__ float4 ca[kThreads];
+    const int tid = threadIdx.x;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int64_t bh = (int64_t)b * a.Hkv + h;
+    const int64_t pbase = bh * a.n_split * a.QR;
+    const int items = a.QR * NQ;
+    const int tpi = kThreads / items;
+    const int item = tid % items, j = tid / items;
+    const int r = item / NQ, cq = item % NQ;
+    float M = -INFINITY, L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j < tpi) {
+        for (int s0 = j; s0 < a.n_split; s0 += kCombBatch * tpi) {
+            float2 ml[kCombBatch];
+            float4 x[kCombBatch];
+#pragma unroll
+            for (int u = 0; u < kCombBatch; ++u) {
+                const int s = s0 + u * tpi;
+                const int64_t slot = pbase + (int64_t)(s < a.n_split ? s : 0) * a.QR + r;
+                ml[u] = *(const float2 *)(a.part_ml + slot * 2);
+                x[u] = *(const float4 *)(a.part_acc + slot * D + cq * 4);
+                if (s >= a.n_split) ml[u].x = -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < kCombBatch; ++u) {
+                const float mn = fmaxf(M, ml[u].x);
+                if (mn == -INFINITY) continue;
+                const float f = expf(M - mn), fo = expf(ml[u].x - mn);
+                L = L * f + ml[u].y * fo;
+                A.x = A.x * f + x[u].x * fo;
+                A.y = A.y * f + x[u].y * fo;
+                A.z = A.z * f + x[u].z * fo;
+                A.w = A.w * f + x[u].w * fo;
+                M = mn;
+            }
+        }
+    }
+    cm[tid] = M;
+    cl[tid] = L;
+    ca[tid] = A;
+    __syncthreads();
+    if (tid < items) {
+        for (int jj = 1; jj < tpi; ++jj) {
+            const int o = jj * items + tid;
+            const float mn = fmaxf(M, cm[o]);
+            if (mn == -INFINITY) continue;
+            const float f = expf(M - mn), fo = expf(cm[o] - mn);
+            L = L * f + cl[o] * fo;
+            A.x = A.x * f + ca[o].x * fo;
+            A.y = A.y * f + ca[o].y * fo;
+            A.z = A.z * f + ca[o].z * fo;
+            A.w = A.w * f + ca[o].w * fo;
+            M = mn;
+        }
+        const float inv = 1.f / L;
+        const int64_t i = (int64_t)b * a.block_q + r / a.g;
+        const int hq = h * a.g + r % a.g;
+        *(float4 *)(a.out + (i * a.Hq + hq) * D + cq * 4) =
+            make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+    }
+}
+
+template <typename TIn, int D, int QRM>
+hipError_t launch_typed(const Geom &g, const FusedArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((k_fused_split<TIn, D, QRM>), dim3(a.n_split, g.Hkv, g.n_blk),
+                       dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_fused_combine<D>), dim3(g.Hkv, g.n_blk), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename TIn, int D>
+hipError_t launch_qr(const Geom &g, const FusedArgs &a, hipStream_t s) {
+    return a.QR <= 4 ? launch_typed<TIn, D, 4>(g, a, s) : launch_typed<TIn, D, 8>(g, a, s);
+}
+
+int fused_n_split(int64_t W_cap) { return (int)((W_cap + kRowsPerSplit - 1) / kRowsPerSplit); }
+
+}  // namespace
+
+bool fused_decode_path(const Geom &g) { return g.block_q * g.g <= 8 && !mfma_block_path(g); }
+
+size_t fused_ws_bytes(const Geom &g) {
+    const size_t rows = (size_t)g.n_blk * g.Hkv * fused_n_split(g.W_cap) * (size_t)(g.block_q * g.g);
+    return ((rows * g.d * sizeof(float) + 255) & ~(size_t)255) +
+           ((rows * 2 * sizeof(float) + 255) & ~(size_t)255);
+}
+
+hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, const void *q,
+                               const int32_t *sel, const int32_t *n_sel, float *out, void *ws,
+                               hipStream_t s) {
+    FusedArgs a;
+    a.k = (const unsigned char *)k;
+    a.v = (const unsigned char *)v;
+    a.q = q;
+    a.sel = sel;
+    a.n_sel = n_sel;
+    a.out = out;
+    a.sh = g.sh;
+    a.st = g.st;
+    a.T = g.T;
+    a.Gp = g.Gp;
+    a.Lp = g.Lp;
+    a.mid_lo = g.mid_lo;
+    a.n_spans = g.n_spans;
+    a.S = g.S;
+    a.last_len = g.last_len;
+    a.topk = g.topk;
+    a.Hkv = g.Hkv;
+    a.Hq = g.Hq;
+    a.g = g.g;
+    a.n_q = g.n_q;
+    a.block_q = g.block_q;
+    a.QR = g.block_q * g.g;
+    a.n_split = fused_n_split(g.W_cap);
+    a.scale = g.scale;
+    for (int c = 0; c < kMaxHalfDim; ++c) {
+        const double f = c < g.d / 2 ? pow(g.theta, -2.0 * (double)c / (double)g.d) : 0.0;
+        const long double turns = (long double)f / (2.0L * 3.14159265358979323846264338327950288L);
+        a.frev_hi[c] = (double)turns;
+        a.frev_lo[c] = (double)(turns - (long double)a.frev_hi[c]);
+        a.step_c[c] = cos(f);
+        a.step_s[c] = sin(f);
+    }
+    const size_t rows = (size_t)g.n_blk * g.Hkv * a.n_split * (size_t)a.QR;
+    a.part_acc = (float *)ws;
+    a.part_ml = (float *)((char *)ws + ((rows * g.d * sizeof(float) + 255) & ~(size_t)255));
+    if (g.dtype == 0)
+        return g.d == 128 ? launch_qr<uint16_t, 128>(g, a, s) : launch_qr<uint16_t, 64>(g, a, s);
+    return g.d == 128 ? launch_qr<float, 128>(g, a, s) : launch_qr<float, 64>(g, a, s);
+}
+
+}  // namespace rea

@@ -146,15 +146,13 @@ size_t score_ws_bytes(const rea::Geom &g, bool caller_scores) {
 hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, double *scores,
                          void *aux, int32_t *sel, int32_t *n_sel, int num_cu, hipStream_t s,
                          const rea_timing *timing) {
+    if (rea::mfma_block_path(g))
+        return rea::launch_score_select_mfma(g, q, k, scores, sel, n_sel, aux, num_cu, s,
+                                             timing ? (hipEvent_t)timing->score_begin : nullptr,
+                                             timing ? (hipEvent_t)timing->score_end : nullptr);
     if (timing && timing->score_begin) {
         hipError_t e = hipEventRecord((hipEvent_t)timing->score_begin, s);
         if (e != hipSuccess) return e;
-    }
-    if (rea::mfma_block_path(g)) {
-        hipError_t e = rea::launch_score_select_mfma(g, q, k, scores, sel, n_sel, aux, num_cu, s);
-        if (e == hipSuccess && timing && timing->score_end)
-            e = hipEventRecord((hipEvent_t)timing->score_end, s);
-        return e;
     }
     hipError_t e = rea::launch_score(g, q, k, scores, (double *)aux, num_cu, s);
     if (e != hipSuccess) return e;
@@ -171,6 +169,10 @@ size_t decode_ws_bytes(const rea::Geom &g) {
     c.take<char>(select_aux_bytes(g));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+    if (rea::fused_decode_path(g)) {
+        c.take<char>(rea::fused_ws_bytes(g));
+        return c.off;
+    }
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     c.take<float>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * sizeof(float));
     c.take<char>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * g.esize);
@@ -344,20 +346,25 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
     void *aux = c.take<char>(select_aux_bytes(g));
     int32_t *ws_sel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     int32_t *ws_nsel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
-    int32_t *Wlen = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
-    float *k_win = c.take<float>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * sizeof(float));
-    void *v_win = c.take<char>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * g.esize);
-    float *q_rot = c.take<float>((size_t)g.n_q * g.Hq * g.d * sizeof(float));
-    void *att_ws = c.take<char>(rea::attend_ws_bytes(g, g.W_cap));
     int32_t *use_sel = sel ? sel : ws_sel;
     int32_t *use_nsel = n_sel ? n_sel : ws_nsel;
     if (g.topk == 0) use_sel = sel;   // may be NULL: nothing is selected
-
     hipStream_t s = (hipStream_t)stream;
     if ((st = launched(launch_select(g, p->q, p->k, scores, aux, use_sel, use_nsel, num_cu, s,
                                      timing),
                        "score_select")) != REA_OK)
         return st;
+    if (rea::fused_decode_path(g)) {
+        void *fws = c.take<char>(rea::fused_ws_bytes(g));
+        return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out,
+                                                 fws, s),
+                        "fused gather + window attention");
+    }
+    int32_t *Wlen = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+    float *k_win = c.take<float>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * sizeof(float));
+    void *v_win = c.take<char>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * g.esize);
+    float *q_rot = c.take<float>((size_t)g.n_q * g.Hq * g.d * sizeof(float));
+    void *att_ws = c.take<char>(rea::attend_ws_bytes(g, g.W_cap));
     if ((st = launched(rea::launch_gather_rope(g, p->k, p->v, p->q, use_sel, use_nsel, k_win,
                                                v_win, q_rot, Wlen, g.W_cap, s),
                        "gather_rope")) != REA_OK)

@@ -46,13 +46,22 @@ bool mfma_block_path(const Geom &g);
 size_t mfma_ws_bytes(const Geom &g);
 hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
                                     double *span_scores, int32_t *sel, int32_t *n_sel,
-                                    void *ws, int num_cu, hipStream_t s);
+                                    void *ws, int num_cu, hipStream_t s,
+                                    hipEvent_t ev_begin, hipEvent_t ev_end);
 
 // Steps 2-3: window rows (K rotated fp32, V copied) + lengths, then the queries.
 hipError_t launch_gather_rope(const Geom &g, const void *k, const void *v, const void *q,
                               const int32_t *sel, const int32_t *n_sel, float *k_win,
                               void *v_win, float *q_rot, int32_t *W, int64_t W_cap,
                               hipStream_t s);
+
+// Steps 2-4 fused for at most 8 query rows per (block, KV head): the window
+// is read from the cache and attended without being written.
+bool fused_decode_path(const Geom &g);
+size_t fused_ws_bytes(const Geom &g);
+hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, const void *q,
+                               const int32_t *sel, const int32_t *n_sel, float *out, void *ws,
+                               hipStream_t s);
 
 // Step 4 for query blocks of at least 32 rows (bf16, d 128) on MFMA.
 bool mfma_attend_path(const Geom &g);

@@ -712,7 +712,8 @@ size_t mfma_ws_bytes(const Geom &g) {
 
 hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
                                     double *span_scores, int32_t *sel, int32_t *n_sel,
-                                    void *ws, int num_cu, hipStream_t s) {
+                                    void *ws, int num_cu, hipStream_t s,
+                                    hipEvent_t ev_begin, hipEvent_t ev_end) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     char *p = (char *)ws;
     uint16_t *qhl = (uint16_t *)p;
@@ -750,9 +751,11 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     if (NR > g.n_spans) NR = g.n_spans;
     if (NR < 1) NR = 1;
     ma.NR = (int)NR;
+    if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_score_mfma, dim3((unsigned)(units * NR)), dim3(256), 0, s, ma);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
 
     CertArgs ca;
     ca.shat = span_scores;
