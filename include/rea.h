@@ -152,7 +152,12 @@ rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes 
  *              padded with -1 after n_sel entries.  May be NULL if topk == 0.
  * n_sel        [n_blocks][n_kv_heads] int32 = k_sel.
  * span_scores  NULL, or [n_blocks][n_kv_heads][n_spans] double: sum over the
- *              block's queries of the span's maximum token score.
+ *              block's queries of the span's maximum token score.  Exact for
+ *              bf16/fp32 inputs except on the MFMA path (bf16, head_dim 128,
+ *              block_q 64, S a multiple of 32, at most 4096 spans), where they
+ *              are bf16-MFMA approximations within a proven per-span bound;
+ *              the selection is exact on every path (uncertain spans are
+ *              re-scored in fp64 before the top-k is decided).
  * ws           device workspace of at least sizes.ws_score_select bytes
  *              (256-byte aligned); contents are scratch.
  */

@@ -17,18 +17,23 @@
 //                    order LDS only).  A 16-lane DPP row of a wave is a stream
 //                    of 8 consecutive window rows; a lane holds D/32 channel
 //                    pairs (c, c + D/2) of its stream's rows.  The rotation
-//                    angle of row w+1 follows from row w's by one fp64 complex
-//                    multiplication with (cos, sin) of the channel's
-//                    frequency; the rotated key is rounded to fp32.  Per
+//                    angle of row w+1 follows from row w's by one complex
+//                    multiplication with (cos, sin) of the channel's frequency
+//                    (fp32 for bf16 inputs, fp64 for fp32 inputs); the rotated
+//                    key is fp32.  Logits are kept in log2 units (the softmax
+//                    scale carries log2 e) so weights are single exp2s.  Per
 //                    stream the 8 logits of each query row give an exact max,
-//                    weights and P.V; streams and waves are merged with the
-//                    usual (m, l, acc) rule and one partial per split is
-//                    written.
+//                    weights and P.V; the workgroup's 16 streams are merged
+//                    through LDS with the usual (m, l, acc) rule and one
+//                    partial per split is written.
 //   k_fused_combine  one workgroup per (KV head, block) merges the splits:
-//                    out = sum_s e^(m_s-M) acc_s / sum_s e^(m_s-M) l_s.
+//                    out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s
+//                    (maxima m_s in log2 units).
 #include "rea_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace rea {
 namespace {
@@ -49,7 +54,7 @@ struct FusedArgs {
     int64_t sh, st;         // elements
     int64_t T, Gp, Lp, mid_lo, n_spans;
     int S, last_len, topk, Hkv, Hq, g, n_q, block_q, QR, n_split;
-    float scale;
+    float scale_log2;       // softmax scale * log2(e): logits in log2 units
     double frev_hi[kMaxHalfDim], frev_lo[kMaxHalfDim];   // theta_c / 2pi as hi + lo
     double step_c[kMaxHalfDim], step_s[kMaxHalfDim];     // cos, sin of theta_c
 };
@@ -126,19 +131,6 @@ __device__ __forceinline__ float row_sum16f(float v) {
     return v;
 }
 
-// Merge (m, l, acc) of another stream into this one.
-template <int N>
-__device__ __forceinline__ void merge(float &m, float &l, float (&acc)[N], float mo, float lo,
-                                      const float (&acco)[N]) {
-    const float mn = fmaxf(m, mo);
-    const float f = (m == -INFINITY) ? 0.f : expf(m - mn);
-    const float fo = (mo == -INFINITY) ? 0.f : expf(mo - mn);
-    l = l * f + lo * fo;
-#pragma unroll
-    for (int e = 0; e < N; ++e) acc[e] = acc[e] * f + acco[e] * fo;
-    m = mn;
-}
-
 // Barrier that orders LDS only: global loads issued before it stay in flight.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -155,8 +147,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     __shared__ float qs[QRM][D];
     __shared__ int32_t ssel[kSelStage];
     __shared__ double tab[HALF][4];             // theta_c/2pi (hi, lo), cos and sin of theta_c
-    __shared__ float wm[4][QRM], wl[4][QRM];
-    __shared__ float wacc[4][QRM][D];
+    __shared__ float sm[16][QRM], sl[16][QRM], sf[16][QRM], smax[QRM];
+    __shared__ float sacc[16][QRM][D];
+    using RT = typename std::conditional<sizeof(TIn) == 2, float, double>::type;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -273,24 +266,24 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
             q1[r][p] = qs[r][c0 + p];
             q2[r][p] = qs[r][c0 + p + HALF];
         }
-    // rotation of the stream's first row, and the per-row step (fp64, so the
-    // 7 steps add no error of note)
-    double cs[PPL], sn[PPL], cst[PPL], snt[PPL];
+    // rotation of the stream's first row, and the per-row step.  bf16 inputs
+    // step in fp32 (7 steps add a few fp32 ulps), fp32 inputs in fp64.
+    RT cs[PPL], sn[PPL], cst[PPL], snt[PPL];
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
         float c1, s1;
         rope_cs(wf, tab[c0 + p][0], tab[c0 + p][1], c1, s1);
         cs[p] = c1;
         sn[p] = s1;
-        cst[p] = tab[c0 + p][2];
-        snt[p] = tab[c0 + p][3];
+        cst[p] = (RT)tab[c0 + p][2];
+        snt[p] = (RT)tab[c0 + p][3];
     }
 
-    // logits of the stream's rows
+    // logits of the stream's rows, in log2 units (the scale carries log2 e)
+    const int wfi = (int)wf, Wi = (int)Wbh;
     float lg[kSL][QRM];
 #pragma unroll
     for (int i = 0; i < kSL; ++i) {
-        const int64_t w = wf + i;
         float x1[PPL], x2[PPL];
         k1[i].get(x1);
         k2[i].get(x2);
@@ -300,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
             const float c = (float)cs[p], s = (float)sn[p];
             y1[p] = x1[p] * c - x2[p] * s;
             y2[p] = x2[p] * c + x1[p] * s;
-            const double cn = cs[p] * cst[p] - sn[p] * snt[p];
+            const RT cn = cs[p] * cst[p] - sn[p] * snt[p];
             sn[p] = sn[p] * cst[p] + cs[p] * snt[p];
             cs[p] = cn;
         }
@@ -312,9 +305,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
                 d = fmaf(q1[r][p], y1[p], d);
                 d = fmaf(q2[r][p], y2[p], d);
             }
-            d = row_sum16f(d) * a.scale;
-            const int64_t pos = Wbh - a.n_q + ((int64_t)b * a.block_q + r / a.g);
-            lg[i][r] = (w < Wbh && w <= pos && r < a.QR) ? d : -INFINITY;
+            d = row_sum16f(d) * a.scale_log2;
+            const int pos = Wi - a.n_q + b * a.block_q + r / a.g;
+            lg[i][r] = (wfi + i < Wi && wfi + i <= pos && r < a.QR) ? d : -INFINITY;
         }
     }
 
@@ -337,7 +330,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
         v2[i].get(x2);
 #pragma unroll
         for (int r = 0; r < QRM; ++r) {
-            const float p = (lg[i][r] == -INFINITY) ? 0.f : expf(lg[i][r] - m[r]);
+            // exp2(-inf) = 0 covers masked rows; m = -inf only when all 8 are masked
+            const float p = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[i][r] - m[r]);
             l[r] += p;
 #pragma unroll
             for (int e = 0; e < PPL; ++e) {
@@ -347,52 +341,45 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
         }
     }
 
-    // merge the wave's four streams (lanes l, l^16, l^32, l^48 hold the same channels)
+    // the workgroup's 16 streams -> LDS, then one merge per (query row, channel)
+    const int st_id = wave * 4 + rho;
 #pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
+    for (int r = 0; r < QRM; ++r) {
 #pragma unroll
-        for (int r = 0; r < QRM; ++r) {
-            float acco[NA];
-#pragma unroll
-            for (int e = 0; e < NA; ++e) acco[e] = __shfl_xor(acc[r][e], o);
-            const float mo = __shfl_xor(m[r], o), lo = __shfl_xor(l[r], o);
-            merge<NA>(m[r], l[r], acc[r], mo, lo, acco);
+        for (int p = 0; p < PPL; ++p) {
+            sacc[st_id][r][c0 + p] = acc[r][p];
+            sacc[st_id][r][c0 + p + HALF] = acc[r][PPL + p];
         }
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int r = 0; r < QRM; ++r) {
-#pragma unroll
-            for (int p = 0; p < PPL; ++p) {
-                wacc[wave][r][c0 + p] = acc[r][p];
-                wacc[wave][r][c0 + p + HALF] = acc[r][PPL + p];
-            }
-            if (lane == 0) {
-                wm[wave][r] = m[r];
-                wl[wave][r] = l[r];
-            }
+        if ((lane & 15) == 0) {
+            sm[st_id][r] = m[r];
+            sl[st_id][r] = l[r];
         }
     }
     __syncthreads();
-    // merge the four waves and write the split's partial
+    if (tid < 16 * QRM) {
+        // weight of stream s for query row r: 2^(m_s - M_r)
+        const int s2 = tid / QRM, r = tid % QRM;
+        float M = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) M = fmaxf(M, sm[t][r]);
+        sf[s2][r] = sm[s2][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[s2][r] - M);
+        if (s2 == 0) smax[r] = M;
+    }
+    __syncthreads();
     const int64_t pbase = bh * a.n_split * a.QR;
     for (int idx = tid; idx < a.QR * D; idx += kThreads) {
         const int r = idx / D, c = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][r]);
         float L = 0.f, A = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float f = (wm[w][r] == -INFINITY) ? 0.f : expf(wm[w][r] - M);
-            L += wl[w][r] * f;
-            A += wacc[w][r][c] * f;
+        for (int t = 0; t < 16; ++t) {
+            const float f = sf[t][r];
+            L = fmaf(sl[t][r], f, L);
+            A = fmaf(sacc[t][r][c], f, A);
         }
         const int64_t slot = pbase + (int64_t)sp * a.QR + r;
         a.part_acc[slot * D + c] = A;
-        if (c == 0) *(float2 *)(a.part_ml + slot * 2) = make_float2(M, L);
+        if (c == 0) *(float2 *)(a.part_ml + slot * 2) = make_float2(smax[r], L);
     }
-
 }
 
 // grid (Hkv, n_blk): merges the splits of one (block, KV head).  Thread =
@@ -430,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_combine(FusedArgs a) {
             for (int u = 0; u < kCombBatch; ++u) {
                 const float mn = fmaxf(M, ml[u].x);
                 if (mn == -INFINITY) continue;
-                const float f = expf(M - mn), fo = expf(ml[u].x - mn);
+                const float f = __builtin_amdgcn_exp2f(M - mn), fo = __builtin_amdgcn_exp2f(ml[u].x - mn);
                 L = L * f + ml[u].y * fo;
                 A.x = A.x * f + x[u].x * fo;
                 A.y = A.y * f + x[u].y * fo;
@@ -449,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_combine(FusedArgs a) {
             const int o = jj * items + tid;
             const float mn = fmaxf(M, cm[o]);
             if (mn == -INFINITY) continue;
-            const float f = expf(M - mn), fo = expf(cm[o] - mn);
+            const float f = __builtin_amdgcn_exp2f(M - mn), fo = __builtin_amdgcn_exp2f(cm[o] - mn);
             L = L * f + cl[o] * fo;
             A.x = A.x * f + ca[o].x * fo;
             A.y = A.y * f + ca[o].y * fo;
@@ -519,7 +506,7 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
     a.block_q = g.block_q;
     a.QR = g.block_q * g.g;
     a.n_split = fused_n_split(g.W_cap);
-    a.scale = g.scale;
+    a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
     for (int c = 0; c < kMaxHalfDim; ++c) {
         const double f = c < g.d / 2 ? pow(g.theta, -2.0 * (double)c / (double)g.d) : 0.0;
         const long double turns = (long double)f / (2.0L * 3.14159265358979323846264338327950288L);

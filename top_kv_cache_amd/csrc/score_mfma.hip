@@ -16,8 +16,8 @@
 //                 queries (K = 256: the key tile is fed twice).  The tile's
 //                 token maxima, the span maximum and the sum over the block's
 //                 queries are taken in the epilogue; one fp64 span score per
-//                 (block, span) is written.  The first query group also writes
-//                 each span's largest key norm.
+//                 (block, span) is written, and each span's largest key norm
+//                 (by one wave of the grid per span).
 //   k_certify     per (block, KV head): exact top-k from the approximate
 //                 scores (see below).
 //
@@ -44,7 +44,6 @@ constexpr int kD = 128;             // head_dim handled here
 constexpr int kQB = 64;             // queries per block
 constexpr int kWavesM = 4;          // blocks (waves) per workgroup
 constexpr int kTile = 32;           // tokens per MFMA tile
-constexpr int kRowPad = 136;        // LDS row stride (bf16) of a staged key tile
 constexpr double kGammaMfma = 255.0 * 1.1920928955078125e-07 * (1.0 + 1e-6);   // 255 * 2^-23
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t b) {
