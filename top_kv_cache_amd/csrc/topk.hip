@@ -23,7 +23,7 @@
 // bin = floor((x - min) * (2048 / (max - min))) in fp64 -- monotone in x, so
 // bins are ordered; only the bin holding the k-th best survives.  Once all
 // survivors share one score the order is by index, so the level key becomes
-// the negated index.  At most 256 survivors are ranked pairwise.
+// the negated index.  At most 64 survivors are ranked pairwise.
 // Otherwise a generic path makes the same decisions with passes over all
 // scores in global memory.
 #include "rea_internal.h"
@@ -40,7 +40,7 @@ constexpr int kMaxGroups = 2048;
 constexpr int kCandCap = 8192;
 constexpr int kPerThread = kCandCap / kThreads;             // 16
 constexpr int kBins = 2048;
-constexpr int kRankMax = 256;
+constexpr int kRankMax = 64;
 constexpr int kMaxCandGroups = kCandCap / kGroup;        // 256
 
 struct FastShared {
@@ -137,29 +137,41 @@ __device__ __forceinline__ uint32_t block_excl_sum(Common &cm, uint32_t v, uint3
 }
 
 // Wave 0 finds the bin holding the need-th best (bins counted from the top);
-// sets cm.bstar and cm.above (candidates in higher bins).
+// sets cm.bstar and cm.above (candidates in higher bins).  Each lane sums a run
+// of nbins/64 bins (read in a lane-rotated order, so the 64 lanes hit distinct
+// banks), a suffix scan over the lanes picks the run, and the wave then scans
+// that run's bins in parallel.
 __device__ __forceinline__ void find_bin(Common &cm, const uint32_t *hist, int nbins, int64_t need) {
     const int lane = threadIdx.x & 63;
     if ((threadIdx.x >> 6) == 0) {
-        const int bpl = nbins / 64;
+        const int bpl = nbins / 64;           // 32 or 64
         uint32_t own = 0;
-        for (int i = 0; i < bpl; ++i) own += hist[lane * bpl + i];
+        for (int i = 0; i < bpl; ++i) own += hist[lane * bpl + ((i + lane) & (bpl - 1))];
         uint32_t suf = own;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const uint32_t y = __shfl_down(suf, o);
             if (lane + o < 64) suf += y;
         }
-        const uint32_t after = suf - own;
-        if ((int64_t)after < need && need <= (int64_t)suf) {
-            uint32_t above = after;
-            int b = lane * bpl + bpl - 1;
-            for (; b > lane * bpl; --b) {
-                if ((int64_t)(above + hist[b]) >= need) break;
-                above += hist[b];
-            }
-            cm.bstar = b;
-            cm.above = above;
+        const uint32_t after = suf - own;       // candidates in runs above this lane's
+        const unsigned long long hit =
+            __ballot((int64_t)after < need && need <= (int64_t)suf);
+        const int L = __ffsll((long long)hit) - 1;
+        const uint32_t aboveL = __shfl(after, L);
+        // bins of run L, top first: lane i < bpl holds bin L*bpl + bpl-1-i
+        const uint32_t c = lane < bpl ? hist[L * bpl + bpl - 1 - lane] : 0u;
+        uint32_t pre = c;                       // inclusive prefix from the top
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(pre, o);
+            if (lane >= o) pre += y;
+        }
+        const unsigned long long at =
+            __ballot(lane < bpl && (int64_t)(aboveL + pre) >= need);
+        const int i = __ffsll((long long)at) - 1;
+        if (lane == i) {
+            cm.bstar = L * bpl + bpl - 1 - i;
+            cm.above = aboveL + pre - c;
         }
     }
     __syncthreads();
@@ -174,14 +186,25 @@ __device__ __forceinline__ void find_kth(Common &cm, uint32_t *hist, double *val
     bool by_index = false;
     for (;;) {
         if (count <= (uint32_t)kRankMax) {
+            // pairwise ranks; 8 entries are read per step so the LDS latency
+            // is paid once per 8 comparisons
             for (uint32_t c = tid; c < count; c += kThreads) {
                 const double x = val[c];
                 const int32_t jc = idx[c];
-                int64_t rank = 0;
-                for (uint32_t o = 0; o < count; ++o) {
-                    const double y = val[o];
-                    rank += (y > x) || (y == x && idx[o] < jc);
+                int rank = 0;
+                uint32_t o = 0;
+                for (; o + 8 <= count; o += 8) {
+                    double y[8];
+                    int32_t yi[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        y[u] = val[o + u];
+                        yi[u] = idx[o + u];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) rank += (y[u] > x) || (y[u] == x && yi[u] < jc);
                 }
+                for (; o < count; ++o) rank += (val[o] > x) || (val[o] == x && idx[o] < jc);
                 if (rank == need - 1) {
                     cm.cut_v = x;
                     cm.cut_j = jc;
@@ -402,12 +425,23 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
 
     if (m <= kMaxGroups) {
         FastShared &f = u.f;
+        constexpr int GPT = kMaxGroups / kThreads;         // group maxima per thread (4)
+        double gr[GPT];
+#pragma unroll
+        for (int e = 0; e < GPT; ++e) {
+            const int i = tid + e * kThreads;
+            gr[e] = gm[i < m ? i : m - 1];
+        }
         // 1. tau = kk-th largest group maximum (every span competes if kk > m)
         double tau = -INFINITY;
         if (kk <= m) {
-            for (int i = tid; i < m; i += kThreads) {
-                f.gval[i] = gm[i];
-                f.gidx[i] = i;
+#pragma unroll
+            for (int e = 0; e < GPT; ++e) {
+                const int i = tid + e * kThreads;
+                if (i < m) {
+                    f.gval[i] = gr[e];
+                    f.gidx[i] = i;
+                }
             }
             __syncthreads();
             find_kth(cm, f.hist, f.gval, f.gidx, (uint32_t)m, kk);
@@ -416,8 +450,10 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
         // candidate groups: maximum >= tau
         if (tid == 0) cm.count = 0;
         __syncthreads();
-        for (int i = tid; i < m; i += kThreads) {
-            if (gm[i] >= tau) {
+#pragma unroll
+        for (int e = 0; e < GPT; ++e) {
+            const int i = tid + e * kThreads;
+            if (i < m && gr[e] >= tau) {
                 const uint32_t slot = atomicAdd(&cm.count, 1u);
                 if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
             }
@@ -426,19 +462,27 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
         const uint32_t ncg = cm.count;
         __syncthreads();
         if (ncg <= (uint32_t)kMaxCandGroups) {
-            // 2. their spans with score >= tau; half a wave per group
+            // 2. their spans with score >= tau; half a wave per group, every
+            //    load issued before any is used (addresses clamped in range)
+            constexpr int CPT = kMaxCandGroups / (kThreads / 32);   // 16
             const int half = tid >> 5, hl = tid & 31;
+            double cx[CPT];
+            int32_t cjx[CPT];            // span index, -1 where (group, lane) is not a span
+#pragma unroll
+            for (int it = 0; it < CPT; ++it) {
+                const uint32_t c = half + it * (kThreads / 32);
+                const int64_t j = (int64_t)f.cgrp[c < ncg ? c : 0] * kGroup + hl;
+                cjx[it] = (c < ncg && j < n) ? (int32_t)j : -1;
+                cx[it] = sc[j < n ? j : n - 1];
+            }
             if (tid == 0) cm.count = 0;
             __syncthreads();
-            for (uint32_t c = half; c < ncg; c += kThreads / 32) {
-                const int64_t j = (int64_t)f.cgrp[c] * kGroup + hl;
-                if (j < n) {
-                    const double x = sc[j];
-                    if (x >= tau) {
-                        const uint32_t slot = atomicAdd(&cm.count, 1u);
-                        f.val[slot] = x;
-                        f.idx[slot] = (int32_t)j;
-                    }
+#pragma unroll
+            for (int it = 0; it < CPT; ++it) {
+                if (cjx[it] >= 0 && cx[it] >= tau) {
+                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    f.val[slot] = cx[it];
+                    f.idx[slot] = cjx[it];
                 }
             }
             __syncthreads();
@@ -450,16 +494,12 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
             const int64_t cj = cm.cut_j;
             for (int i = tid; i < m; i += kThreads) f.bitmap[i] = 0u;
             __syncthreads();
-            for (uint32_t c = half; c < ncg; c += kThreads / 32) {
-                const int g = f.cgrp[c];
-                const int64_t j = (int64_t)g * kGroup + hl;
-                bool pick = false;
-                if (j < n) {
-                    const double x = sc[j];
-                    pick = x > cv || (x == cv && j <= cj);
-                }
+#pragma unroll
+            for (int it = 0; it < CPT; ++it) {
+                const uint32_t c = half + it * (kThreads / 32);
+                const bool pick = cjx[it] >= 0 && (cx[it] > cv || (cx[it] == cv && cjx[it] <= cj));
                 const unsigned long long bal = __ballot(pick);
-                if (hl == 0) f.bitmap[g] = (uint32_t)(bal >> (lane & 32));
+                if (hl == 0 && c < ncg) f.bitmap[f.cgrp[c]] = (uint32_t)(bal >> (lane & 32));
             }
             __syncthreads();
             constexpr int WPT = kMaxGroups / kThreads;      // 4 words per thread
