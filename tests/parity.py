@@ -77,9 +77,11 @@ def mfma_path(w):
 
 
 def fused_path(w):
-    """Up to 8 query rows per (block, KV head): rea_decode_step runs steps 2-4
-    fused, reading the window straight from the cache."""
-    return w.block_q * w.g <= 8
+    """rea_decode_step runs steps 2-4 fused, reading the window straight from
+    the cache: up to 8 query rows per (block, KV head) on the VALU, or bf16
+    d 128 blocks of >= 32 query rows on MFMA."""
+    mfma_cache = w.dtype == "bf16" and w.d == 128 and w.block_q * w.g >= 32 and w.topk <= 4096
+    return w.block_q * w.g <= 8 or mfma_cache
 
 
 def compare_head(w, gpu, ora, h, check_windows=True):

@@ -10,10 +10,23 @@
 //   S^T = K' Q'^T on v_mfma_f32_32x32x16_bf16 with K' and Q' each split into
 //         bf16 hi + lo (three products: hi.hi + hi.lo + lo.hi, ~16-bit inputs),
 //         so a lane holds one query's 16 logits of the tile and the softmax
-//         statistics stay lane-local (one exchange with the partner half-wave);
+//         statistics stay lane-local (one exchange with the partner half-wave).
+//         Q' carries the softmax scale times log2(e): logits are in log2
+//         units and weights are single exp2s; the accumulators are rescaled
+//         only in tiles where some query's running maximum grows;
 //   O^T += V^T P^T with V exact in bf16 and P rounded to bf16; V is staged
 //         transposed so each A fragment is one 16-byte LDS read.
 // The next tile's global loads are issued before this tile's MFMAs.
+//
+// Two sources for the tiles (template parameter):
+//   window  the rotated window written by the gather step (rea_window_attend);
+//   cache   inside rea_decode_step: window row w is read from the bf16 cache
+//           through the selection (global ++ selected spans ++ local), and
+//           rotated to position w while it is staged, with (cos, sin) from a
+//           per-call table of the window positions (k_rope_table, fp64
+//           angles rounded to fp32).  The queries are rotated the same way
+//           from the table, so neither the window nor the rotated queries are
+//           ever written.
 #include "rea_internal.h"
 
 #include <math.h>
@@ -30,16 +43,30 @@ constexpr int kKPad = 136;          // K' tile row stride (bf16)
 constexpr int kVPad = 40;           // V^T tile row stride (bf16)
 constexpr int kRowsWG = 128;        // query rows per workgroup
 
+constexpr int kSelCap = 4096;       // selection entries staged in LDS (cache source)
+
 struct MAttnArgs {
+    // window source
     const float *q_rot;     // [n_q][Hq][D]
     const float *k_win;     // [n_blk][Hkv][W_cap][D]
     const uint16_t *v_win;  // [n_blk][Hkv][W_cap][D] bf16
     const int32_t *W;       // [n_blk][Hkv]
+    // cache source
+    const uint16_t *q;      // [n_q][Hq][D] bf16, un-rotated
+    const uint16_t *k, *v;  // caches, element strides sh (head), st (token)
+    const int32_t *sel, *n_sel;
+    const float2 *rope;     // [W_cap][D/2] (cos, sin) of w * theta_c
+    int64_t sh, st, T, Gp, Lp, mid_lo, n_spans;
+    int S, last_len, topk;
+    // both
     float *out;             // [n_q][Hq][D]
     int64_t W_cap;
     int QR, Hq, Hkv, g, n_q, block_q, n_rg;
-    float scale;
+    float scale_log2;       // softmax scale * log2(e)
 };
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     uint32_t b = __float_as_uint(f);
@@ -47,28 +74,57 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     return b >> 16;
 }
 
-// 8 floats -> hi (bf16) and lo = bf16(x - hi), packed 2 per dword
-__device__ __forceinline__ void split8(const float (&x)[8], uint4 &hi, uint4 &lo) {
-    uint32_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        h[e] = bf16_rne_bits(x[e]);
-        l[e] = bf16_rne_bits(x[e] - __uint_as_float(h[e] << 16));
-    }
-    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+// two floats -> two bf16 (round to nearest even), packed low first
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
 }
 
-__global__ __launch_bounds__(256) void k_attend_mfma(MAttnArgs a) {
+// 8 floats -> hi (bf16) and lo = bf16(x - hi), packed 2 per dword
+__device__ __forceinline__ void split8(const float (&x)[8], uint4 &hi, uint4 &lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
+        l[e] = pack_bf16(x[2 * e] - __uint_as_float(h[e] << 16),
+                         x[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float (&x)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+
+template <bool kCache>
+__global__ __launch_bounds__(256, 2) void k_attend_mfma(MAttnArgs a) {
     __shared__ __align__(16) uint16_t khi[2][kKT][kKPad];
     __shared__ __align__(16) uint16_t klo[2][kKT][kKPad];
     __shared__ __align__(16) uint16_t vt[2][kD][kVPad];
+    __shared__ int32_t ssel[kCache ? kSelCap : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rg = blockIdx.x % a.n_rg;
     const int bh = blockIdx.x / a.n_rg;
     const int b = bh / a.Hkv, h = bh % a.Hkv;
-    const int64_t Wbh = a.W[bh];
     const int n = lane & 31, hb = lane >> 5;
+    int64_t Wbh, sel_len = 0;
+    if (kCache) {
+        // window length from the selection (only span n_spans-1 can be short,
+        // and a sorted selection holds it last); the selection goes to LDS
+        const int ns = a.n_sel[bh];
+        sel_len = (int64_t)ns * a.S;
+        if (a.last_len != a.S && ns > 0 && a.sel[(int64_t)bh * a.topk + ns - 1] == a.n_spans - 1)
+            sel_len -= a.S - a.last_len;
+        for (int t = tid; t < ns; t += 256) ssel[t] = a.sel[(int64_t)bh * a.topk + t];
+        Wbh = a.Gp + sel_len + a.Lp;
+    } else {
+        Wbh = a.W[bh];
+    }
 
     // this lane's query column
     const int r = rg * kRowsWG + wave * 32 + n;
@@ -78,15 +134,38 @@ __global__ __launch_bounds__(256) void k_attend_mfma(MAttnArgs a) {
     const int hq = h * a.g + rq % a.g;
     const int64_t pos = Wbh - a.n_q + qi;
 
-    // B fragments of Q' (hi, lo): channels ks*16 + hb*8 .. +8
+    // B fragments of Q' (hi, lo): channels ks*16 + hb*8 .. +8.  The query is
+    // scaled by softmax_scale * log2(e) first, so logits come out in log2
+    // units and every weight is one exp2.
     uint4 qh[8], ql[8];
-    {
+    const float sc = a.scale_log2;
+    if (kCache) {
+        // rotate the raw query to its position: channel ks*16+hb*8+e (ks < 4)
+        // pairs with the same offset in ks+4, both held by this lane
+        const uint16_t *qrow = a.q + (qi * a.Hq + hq) * kD;
+        const float2 *rp = a.rope + pos * (kD / 2);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float x1[8], x2[8], y1[8], y2[8];
+            bf16x8_to_f32(*(const uint4 *)(qrow + ks * 16 + hb * 8), x1);
+            bf16x8_to_f32(*(const uint4 *)(qrow + ks * 16 + hb * 8 + kD / 2), x2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float2 cs = rp[ks * 16 + hb * 8 + e];
+                y1[e] = (x1[e] * cs.x - x2[e] * cs.y) * sc;
+                y2[e] = (x2[e] * cs.x + x1[e] * cs.y) * sc;
+            }
+            split8(y1, qh[ks], ql[ks]);
+            split8(y2, qh[ks + 4], ql[ks + 4]);
+        }
+    } else {
         const float *qrow = a.q_rot + (qi * a.Hq + hq) * kD;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const float4 u0 = *(const float4 *)(qrow + ks * 16 + hb * 8);
             const float4 u1 = *(const float4 *)(qrow + ks * 16 + hb * 8 + 4);
-            const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            const float x[8] = {u0.x * sc, u0.y * sc, u0.z * sc, u0.w * sc,
+                                u1.x * sc, u1.y * sc, u1.z * sc, u1.w * sc};
             split8(x, qh[ks], ql[ks]);
         }
     }
@@ -98,39 +177,96 @@ __global__ __launch_bounds__(256) void k_attend_mfma(MAttnArgs a) {
     if (kend > Wbh) kend = Wbh;
     const int64_t n_tiles = (kend + kKT - 1) / kKT;
 
-    const float *kb = a.k_win + (int64_t)bh * a.W_cap * kD;
-    const uint16_t *vb = a.v_win + (int64_t)bh * a.W_cap * kD;
-    // staging: thread -> key row tid/8, channels (tid%8)*16 .. +16
-    const int skey = tid >> 3, sch = (tid & 7) * 16;
-    float4 kr[4];
-    uint4 vr[2];
+    // staging.  window: thread -> key row tid/8, channels (tid%8)*16 .. +16.
+    // cache: thread -> key row tid/8, channel pairs (tid%8)*8 .. +8, i.e.
+    // channels c0 .. c0+8 and c0+D/2 .. c0+D/2+8.
+    const int skey = tid >> 3, sch = (tid & 7) * 16, c0 = (tid & 7) * 8;
+    const float *kwb = a.k_win + (int64_t)bh * a.W_cap * kD;
+    const uint16_t *vwb = a.v_win + (int64_t)bh * a.W_cap * kD;
+    const uint16_t *kcb = a.k + (int64_t)h * a.sh;
+    const uint16_t *vcb = a.v + (int64_t)h * a.sh;
+    float4 kr[4];               // window: 16 fp32 keys; cache: 4 x (cos, sin) pairs
+    uint4 vr[2], kc[2];
     auto load_tile = [&](int64_t w0) {
         const int64_t w = w0 + skey;
         const bool ok = w < kend;
+        if (kCache) {
+            // rows past the end read window row 0 (finite data, never used)
+            const int64_t wl = ok ? w : 0;
+            int64_t src;
+            if (wl < a.Gp) {
+                src = wl;
+            } else if (wl < a.Gp + sel_len) {
+                const uint32_t o = (uint32_t)(wl - a.Gp);
+                const uint32_t qs = o / (uint32_t)a.S;
+                src = a.mid_lo + (int64_t)ssel[qs] * a.S + (o - qs * (uint32_t)a.S);
+            } else {
+                src = a.T - a.Lp + (wl - a.Gp - sel_len);
+            }
+            const int64_t row = src * a.st;
+            kc[0] = *(const uint4 *)(kcb + row + c0);
+            kc[1] = *(const uint4 *)(kcb + row + c0 + kD / 2);
+            vr[0] = *(const uint4 *)(vcb + row + c0);
+            vr[1] = *(const uint4 *)(vcb + row + c0 + kD / 2);
+            const float4 *rp = (const float4 *)(a.rope + wl * (kD / 2) + c0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            kr[e] = ok ? *(const float4 *)(kb + w * kD + sch + e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int e = 0; e < 4; ++e) kr[e] = rp[e];
+        } else {
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-            vr[e] = ok ? *(const uint4 *)(vb + w * kD + sch + e * 8) : make_uint4(0u, 0u, 0u, 0u);
+            for (int e = 0; e < 4; ++e)
+                kr[e] = ok ? *(const float4 *)(kwb + w * kD + sch + e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                vr[e] = ok ? *(const uint4 *)(vwb + w * kD + sch + e * 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
     };
     auto store_tile = [&](int buf) {
+        if (kCache) {
+            float x1[8], x2[8], y1[8], y2[8];
+            bf16x8_to_f32(kc[0], x1);
+            bf16x8_to_f32(kc[1], x2);
+            const float cs[8][2] = {{kr[0].x, kr[0].y}, {kr[0].z, kr[0].w}, {kr[1].x, kr[1].y},
+                                    {kr[1].z, kr[1].w}, {kr[2].x, kr[2].y}, {kr[2].z, kr[2].w},
+                                    {kr[3].x, kr[3].y}, {kr[3].z, kr[3].w}};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const float x[8] = {kr[2 * e].x, kr[2 * e].y, kr[2 * e].z, kr[2 * e].w,
-                                kr[2 * e + 1].x, kr[2 * e + 1].y, kr[2 * e + 1].z, kr[2 * e + 1].w};
+            for (int e = 0; e < 8; ++e) {
+                y1[e] = x1[e] * cs[e][0] - x2[e] * cs[e][1];
+                y2[e] = x2[e] * cs[e][0] + x1[e] * cs[e][1];
+            }
             uint4 hi, lo;
-            split8(x, hi, lo);
-            *(uint4 *)&khi[buf][skey][sch + e * 8] = hi;
-            *(uint4 *)&klo[buf][skey][sch + e * 8] = lo;
-        }
+            split8(y1, hi, lo);
+            *(uint4 *)&khi[buf][skey][c0] = hi;
+            *(uint4 *)&klo[buf][skey][c0] = lo;
+            split8(y2, hi, lo);
+            *(uint4 *)&khi[buf][skey][c0 + kD / 2] = hi;
+            *(uint4 *)&klo[buf][skey][c0 + kD / 2] = lo;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const uint32_t w4[4] = {vr[e].x, vr[e].y, vr[e].z, vr[e].w};
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t w4[4] = {vr[e].x, vr[e].y, vr[e].z, vr[e].w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                vt[buf][sch + e * 8 + 2 * k][skey] = (uint16_t)(w4[k] & 0xffffu);
-                vt[buf][sch + e * 8 + 2 * k + 1][skey] = (uint16_t)(w4[k] >> 16);
+                for (int k = 0; k < 4; ++k) {
+                    vt[buf][c0 + e * (kD / 2) + 2 * k][skey] = (uint16_t)(w4[k] & 0xffffu);
+                    vt[buf][c0 + e * (kD / 2) + 2 * k + 1][skey] = (uint16_t)(w4[k] >> 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float x[8] = {kr[2 * e].x, kr[2 * e].y, kr[2 * e].z, kr[2 * e].w,
+                                    kr[2 * e + 1].x, kr[2 * e + 1].y, kr[2 * e + 1].z, kr[2 * e + 1].w};
+                uint4 hi, lo;
+                split8(x, hi, lo);
+                *(uint4 *)&khi[buf][skey][sch + e * 8] = hi;
+                *(uint4 *)&klo[buf][skey][sch + e * 8] = lo;
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t w4[4] = {vr[e].x, vr[e].y, vr[e].z, vr[e].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    vt[buf][sch + e * 8 + 2 * k][skey] = (uint16_t)(w4[k] & 0xffffu);
+                    vt[buf][sch + e * 8 + 2 * k + 1][skey] = (uint16_t)(w4[k] >> 16);
+                }
             }
         }
     };
@@ -143,6 +279,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(MAttnArgs a) {
         for (int rr = 0; rr < 16; ++rr) o[t][rr] = 0.f;
 
     int buf = 0;
+    if (kCache) __syncthreads();        // ssel visible before the first row lookup
     if (n_tiles > 0) {
         load_tile(0);
         store_tile(0);
@@ -165,32 +302,47 @@ __global__ __launch_bounds__(256) void k_attend_mfma(MAttnArgs a) {
             st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl8, st, 0, 0, 0);
             st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh8, st, 0, 0, 0);
         }
-        // mask, online softmax (this lane's query; keys 8(rr/4) + 4hb + rr%4)
+        // mask, online softmax (this lane's query; keys 8(rr/4) + 4hb + rr%4).
+        // Tiles wholly before every query of the wave and inside the window
+        // need no mask.
         float x[16];
-        float mt = -INFINITY;
+        const int w0i = (int)w0, posi = (int)pos, Wi = (int)Wbh;
+        const bool whole = w0i + kKT <= Wi && w0i + kKT - 1 <= posi;
+        if (__builtin_amdgcn_read_exec() == __ballot(whole)) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int64_t w = w0 + 8 * (rr >> 2) + 4 * hb + (rr & 3);
-            x[rr] = (w < Wbh && w <= pos) ? st[rr] * a.scale : -INFINITY;
-            mt = fmaxf(mt, x[rr]);
+            for (int rr = 0; rr < 16; ++rr) x[rr] = st[rr];
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int w = w0i + 8 * (rr >> 2) + 4 * hb + (rr & 3);
+                x[rr] = (w < Wi && w <= posi) ? st[rr] : -INFINITY;
+            }
         }
+        float mt = x[0];
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
+        // rescale the accumulators only when some query's maximum moved
+        if (__ballot(m_new > m_run)) {
+            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) o[t][rr] *= alpha;
+            m_run = m_new;
+        }
         float p[16];
         float lt = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            p[rr] = (x[rr] == -INFINITY) ? 0.f : expf(x[rr] - m_new);
+            // exp2(-inf) = 0; m_run is finite once the query has seen a key
+            p[rr] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[rr] - m_run);
             lt += p[rr];
         }
         lt += __shfl_xor(lt, 32);
-        l_run = l_run * alpha + lt;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) o[t][rr] *= alpha;
+        l_run += lt;
 
         // B fragments of P^T: k-step s covers keys 16s .. 16s+15; this lane
         // (kb = hb) needs keys 16s + 8hb + e; a lane holds keys 8a + 4hb + c.
@@ -242,16 +394,41 @@ __global__ __launch_bounds__(256) void k_attend_mfma(MAttnArgs a) {
     }
 }
 
+// (cos, sin) of w * theta_c for every window position w < W_cap and channel
+// pair c: angles and their sine/cosine in fp64, rounded once to fp32.
+struct RopeArgs {
+    float2 *rope;
+    int64_t n;
+    int half;
+    double inv_freq[kMaxHalfDim];
+};
+
+__global__ __launch_bounds__(256) void k_rope_table(RopeArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.n) return;
+    const int64_t w = i / a.half;
+    const int c = (int)(i % a.half);
+    double sn, cs;
+    sincos((double)w * a.inv_freq[c], &sn, &cs);
+    a.rope[i] = make_float2((float)cs, (float)sn);
+}
+
 }  // namespace
 
 bool mfma_attend_path(const Geom &g) {
     return g.dtype == 0 && g.d == kD && g.block_q * g.g >= 32;
 }
 
+bool mfma_cache_attend_path(const Geom &g) { return mfma_attend_path(g) && g.topk <= kSelCap; }
+
+size_t rope_table_bytes(const Geom &g) {
+    return (size_t)g.W_cap * (g.d / 2) * sizeof(float2);
+}
+
 hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_win,
                               const void *v_win, const int32_t *W, int64_t W_cap, float *out,
                               hipStream_t s) {
-    MAttnArgs a;
+    MAttnArgs a{};
     a.q_rot = q_rot;
     a.k_win = k_win;
     a.v_win = (const uint16_t *)v_win;
@@ -265,8 +442,53 @@ hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_
     a.n_q = g.n_q;
     a.block_q = g.block_q;
     a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
-    a.scale = g.scale;
-    hipLaunchKernelGGL(k_attend_mfma, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(256), 0, s, a);
+    a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
+    hipLaunchKernelGGL(k_attend_mfma<false>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k, const void *v,
+                                    const int32_t *sel, const int32_t *n_sel, float *out,
+                                    void *ws, hipStream_t s) {
+    float2 *rope = (float2 *)ws;
+    RopeArgs ra;
+    ra.rope = rope;
+    ra.n = g.W_cap * (g.d / 2);
+    ra.half = g.d / 2;
+    for (int c = 0; c < kMaxHalfDim; ++c)
+        ra.inv_freq[c] = c < g.d / 2 ? pow(g.theta, -2.0 * (double)c / (double)g.d) : 0.0;
+    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((ra.n + 255) / 256)), dim3(256), 0, s, ra);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    MAttnArgs a{};
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.sel = sel;
+    a.n_sel = n_sel;
+    a.rope = rope;
+    a.sh = g.sh;
+    a.st = g.st;
+    a.T = g.T;
+    a.Gp = g.Gp;
+    a.Lp = g.Lp;
+    a.mid_lo = g.mid_lo;
+    a.n_spans = g.n_spans;
+    a.S = g.S;
+    a.last_len = g.last_len;
+    a.topk = g.topk;
+    a.out = out;
+    a.W_cap = g.W_cap;
+    a.QR = g.block_q * g.g;
+    a.Hq = g.Hq;
+    a.Hkv = g.Hkv;
+    a.g = g.g;
+    a.n_q = g.n_q;
+    a.block_q = g.block_q;
+    a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
+    a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
+    hipLaunchKernelGGL(k_attend_mfma<true>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -173,6 +173,10 @@ size_t decode_ws_bytes(const rea::Geom &g) {
         c.take<char>(rea::fused_ws_bytes(g));
         return c.off;
     }
+    if (rea::mfma_cache_attend_path(g)) {
+        c.take<char>(rea::rope_table_bytes(g));
+        return c.off;
+    }
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     c.take<float>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * sizeof(float));
     c.take<char>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * g.esize);
@@ -359,6 +363,12 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
         return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out,
                                                  fws, s),
                         "fused gather + window attention");
+    }
+    if (rea::mfma_cache_attend_path(g)) {
+        void *rws = c.take<char>(rea::rope_table_bytes(g));
+        return launched(rea::launch_attend_mfma_cache(g, p->q, p->k, p->v, use_sel, use_nsel, out,
+                                                      rws, s),
+                        "window attention from the cache (MFMA)");
     }
     int32_t *Wlen = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     float *k_win = c.take<float>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * sizeof(float));

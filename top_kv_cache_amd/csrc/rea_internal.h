@@ -63,6 +63,15 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
                                const int32_t *sel, const int32_t *n_sel, float *out, void *ws,
                                hipStream_t s);
 
+// Steps 2-4 for query blocks of at least 32 rows inside rea_decode_step: the
+// MFMA attention reads the window rows from the cache through the selection.
+// ws holds rope_table_bytes(g).
+bool mfma_cache_attend_path(const Geom &g);
+size_t rope_table_bytes(const Geom &g);
+hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k, const void *v,
+                                    const int32_t *sel, const int32_t *n_sel, float *out,
+                                    void *ws, hipStream_t s);
+
 // Step 4 for query blocks of at least 32 rows (bf16, d 128) on MFMA.
 bool mfma_attend_path(const Geom &g);
 hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_win,
