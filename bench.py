@@ -79,9 +79,13 @@ def cpu_baseline(w, min_seconds=10.0):
     import numpy as np
     import oracle.rea_oracle as O
     import synth
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in info] or [1])
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in info
+                                 if p.get("user_api") == "blas"})) or blas
     except Exception:
         cores = len(os.sched_getaffinity(0))
     g = w.g
@@ -102,6 +106,7 @@ def cpu_baseline(w, min_seconds=10.0):
     lo, hi = w.mid
     keys = (hi - lo) * w.Hkv * layers
     return {"value": keys / total, "unit": "keys/s", "cores": int(cores), "kind": "oracle",
+            "blas": blas,
             "sample": f"layers 0..{layers - 1} of {w.n_layers}, all {w.Hkv} KV heads each: the "
                       f"full decode step (score, select, gather+RoPE, attend) in fp64 numpy, "
                       f"{total:.1f} s of oracle time; input generation not timed"}
@@ -110,7 +115,7 @@ def cpu_baseline(w, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload number (default: 1M x 32 layers)")
     ap.add_argument("--layers", type=int, default=0, help="override layer count (exploration only)")
@@ -172,24 +177,27 @@ def main():
         one_step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, HIP events around every scoring launch
+    # timed region: K steps, HIP events around every step and every scoring launch
     ev = [[(hip.event(), hip.event()) for _ in steps_l] for _ in range(args.steps)]
     timings = [[rea.Timing(b.value, e.value) for (b, e) in row] for row in ev]
-    e0, e1 = hip.event(), hip.event()
+    step_ev = [hip.event() for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    hip.record(e0, stream.cuda_stream)
+    hip.record(step_ev[0], stream.cuda_stream)
     for s in range(args.steps):
         one_step(timings[s])
-    hip.record(e1, stream.cuda_stream)
+        hip.record(step_ev[s + 1], stream.cuda_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = hip.elapsed_ms(e0, e1)
+    total_ms = hip.elapsed_ms(step_ev[0], step_ev[-1])
+    step_ms = sorted(hip.elapsed_ms(step_ev[s], step_ev[s + 1]) for s in range(args.steps))
     k1 = [hip.elapsed_ms(b, e) for row in ev for (b, e) in row]
     for row in ev:
         for (b, e) in row:
             hip.destroy(b)
             hip.destroy(e)
+    for e in step_ev:
+        hip.destroy(e)
 
     lo, hi = w.mid
     keys_per_layer = (hi - lo) * w.Hkv
@@ -219,12 +227,16 @@ def main():
         log(f"[bench] scoring kernel {k1_ms * 1e3:.1f} us/launch = {achieved:.0f} TFLOP/s "
             f"algorithmic, {2 * achieved:.0f} TFLOP/s issued on MFMA "
             f"({2 * achieved / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of {MFMA_BF16_PEAK_TFLOPS:.0f})")
-    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
-        f"{value / 1e9:.2f} G keys/s")
+    med = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
+    p90 = step_ms[min(len(step_ms) - 1, int(0.9 * len(step_ms)))]
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}; "
+        f"median {med:.3f}, p90 {p90:.3f}), {value / 1e9:.2f} G keys/s")
 
     res = {
         "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "step_ms_median": med, "step_ms_p90": p90,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f64", "data": "synthetic",
         "config": {"workload": w.name, "layers": n_layers, "context": w.T, "batch": 1,

@@ -91,6 +91,41 @@ def test_exact_ties_lower_index_wins():
     assert split_groups >= 1       # the k-th boundary cuts through a tie group
 
 
+@pytest.mark.parametrize("T,S_,k", [(40000, 16, 40), (60000, 8, 300), (200000, 4, 600),
+                                    (150000, 2, 2000)])
+def test_exact_ties_many_candidates(T, S_, k):
+    """Binary inputs over thousands of spans, the k-th boundary cutting a tie
+    group, through each way the top-k step can go: under 192 candidates
+    (pairwise ranks), thousands of candidates (histogram levels down to the
+    by-index level), more than 256 candidate groups and more than 2048 groups
+    (the generic path over global memory)."""
+    rng = np.random.default_rng(T + k)
+    w = S(Hq=2, Hkv=2, d=64, T=T, S=S_, topk=k, L=64, needles=0)
+    qn = rng.integers(0, 2, size=(1, w.Hq, w.d)).astype(np.float32)
+    Kn = rng.integers(0, 2, size=(w.Hkv, w.T, w.d)).astype(np.float32)
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    gpu = run_library(w, to_bf(qn), to_bf(Kn), to_bf(Vn))
+    q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
+    split, crowded = 0, 0
+    for h in range(w.Hkv):
+        ora = oracle_head(w, 0, h, q64, K64[h:h + 1], V64[h:h + 1])
+        sc = ora["sc"][0]
+        kth = np.sort(sc)[::-1][w.topk - 1]
+        above, tied = int((sc > kth).sum()), int((sc == kth).sum())
+        # spans at or above the k-th largest group maximum: a lower bound of
+        # the candidates the top-k step ranks
+        gmax = np.array([sc[i:i + 32].max() for i in range(0, len(sc), 32)])
+        cand = int((sc >= np.sort(gmax)[::-1][min(w.topk, len(gmax)) - 1]).sum())
+        log(f"  head {h}: {len(sc)} spans, {above} above the k-th, {tied} tied, >= {cand} candidates")
+        split += above < w.topk < above + tied
+        crowded += cand > 192
+        compare_head(w, gpu, ora, h)
+    assert split >= 1 and (crowded >= 1 or T == 40000)
+
+
 def test_exact_ties_mfma_blocks():
     """Integer inputs through the MFMA block path: tied spans share identical
     approximate scores and must be resolved by index after exact re-scoring."""

@@ -9,16 +9,23 @@
 // One 512-thread workgroup per (block, KV head).  The scoring kernel also
 // wrote the maximum of every group of 32 consecutive spans.  Fast path (at
 // most 2048 groups):
-//   1. tau = the k-th largest group maximum.  It is a lower bound of the k-th
-//      largest score (the k best groups hold k distinct scores >= tau), so
-//      every selected span lies in a group whose maximum is >= tau; at most
-//      256 such groups are accepted (more only with massive ties).
-//   2. the spans of those groups with score >= tau are loaded into LDS;
-//   3. the cutoff e* (the k-th best under score desc, index asc) is found in
-//      LDS by histogram levels; span j is selected iff score_j > score* or
-//      (score_j == score* and j <= j*).  Each candidate group becomes one
-//      32-bit word of a bitmap over the spans, and one block scan over the
-//      words writes the indices in ascending order.
+//   1. tau, a lower bound of the k-th largest group maximum, from one
+//      histogram level over the group maxima: the smallest maximum in the
+//      bins at or above the bin holding the k-th largest.  It also bounds the
+//      k-th largest score from below (the k best groups hold k distinct
+//      scores), so every selected span scores >= tau and lies in a group
+//      whose maximum is >= tau; at most 256 such groups are accepted (more
+//      only with massive ties).
+//   2. the spans of those groups with score >= tau (all spans scoring >= tau)
+//      are loaded into LDS;
+//   3. with at most 192 of them, each one's rank among them (score desc,
+//      index asc) is its global rank: ranks < k are kept and each kept span is
+//      written at the count of kept indices below its own.  Otherwise the
+//      cutoff e* (the k-th best) is found in LDS by histogram levels; span j
+//      is selected iff score_j > score* or (score_j == score* and j <= j*);
+//      each candidate group becomes one 32-bit word of a bitmap over the
+//      spans, and one block scan over the words writes the indices in
+//      ascending order.
 // Histogram level: 2048 equal-width bins between the candidates' min and max,
 // bin = floor((x - min) * (2048 / (max - min))) in fp64 -- monotone in x, so
 // bins are ordered; only the bin holding the k-th best survives.  Once all
@@ -42,6 +49,7 @@ constexpr int kPerThread = kCandCap / kThreads;             // 16
 constexpr int kBins = 2048;
 constexpr int kRankMax = 64;
 constexpr int kMaxCandGroups = kCandCap / kGroup;        // 256
+constexpr int kPairCap = 192;       // candidates ranked pairwise (else histogram levels)
 
 struct FastShared {
     double val[kCandCap];
@@ -432,20 +440,39 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
             const int i = tid + e * kThreads;
             gr[e] = gm[i < m ? i : m - 1];
         }
-        // 1. tau = kk-th largest group maximum (every span competes if kk > m)
+        // 1. tau <= the kk-th largest group maximum (every span competes if
+        //    kk > m): one histogram level over the group maxima finds the bin
+        //    b* holding the kk-th largest, and tau is the smallest maximum in
+        //    bins >= b* (bins are monotone in the value).
         double tau = -INFINITY;
         if (kk <= m) {
+            for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
+            double mn = INFINITY, mx = -INFINITY;
+            uint32_t dummy = 0;
 #pragma unroll
-            for (int e = 0; e < GPT; ++e) {
-                const int i = tid + e * kThreads;
-                if (i < m) {
-                    f.gval[i] = gr[e];
-                    f.gidx[i] = i;
+            for (int e = 0; e < GPT; ++e)
+                if (tid + e * kThreads < m) {
+                    mn = fmin(mn, gr[e]);
+                    mx = fmax(mx, gr[e]);
                 }
+            block_minmax_count(cm, mn, mx, dummy);
+            if (mn == mx) {
+                tau = mn;
+            } else {
+                const double inv = (double)kBins / (mx - mn);
+#pragma unroll
+                for (int e = 0; e < GPT; ++e)
+                    if (tid + e * kThreads < m) atomicAdd(&f.hist[bin_of(gr[e], mn, inv, kBins)], 1u);
+                __syncthreads();
+                find_bin(cm, f.hist, kBins, kk);
+                const int bstar = cm.bstar;
+                double lo = INFINITY, unused = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < GPT; ++e)
+                    if (tid + e * kThreads < m && bin_of(gr[e], mn, inv, kBins) >= bstar) lo = fmin(lo, gr[e]);
+                block_minmax_count(cm, lo, unused, dummy);
+                tau = lo;
             }
-            __syncthreads();
-            find_kth(cm, f.hist, f.gval, f.gidx, (uint32_t)m, kk);
-            tau = cm.cut_v;
         }
         // candidate groups: maximum >= tau
         if (tid == 0) cm.count = 0;
@@ -488,6 +515,52 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
             __syncthreads();
             const uint32_t count = cm.count;
             __syncthreads();
+            if (count <= (uint32_t)kPairCap) {
+                // 3'. every span scoring >= tau is a candidate, so a candidate's
+                //     rank among them (score desc, index asc) is its rank among
+                //     all spans: rank every candidate pairwise, keep ranks < kk,
+                //     and place each kept span by the kept indices below it.
+                if (tid == 0) cm.count = 0;
+                __syncthreads();
+                for (uint32_t c = tid; c < count; c += kThreads) {
+                    const double x = f.val[c];
+                    const int32_t jc = f.idx[c];
+                    int rank = 0;
+                    uint32_t o = 0;
+                    for (; o + 8 <= count; o += 8) {
+                        double y[8];
+                        int32_t yi[8];
+#pragma unroll
+                        for (int u2 = 0; u2 < 8; ++u2) {
+                            y[u2] = f.val[o + u2];
+                            yi[u2] = f.idx[o + u2];
+                        }
+#pragma unroll
+                        for (int u2 = 0; u2 < 8; ++u2) rank += (y[u2] > x) || (y[u2] == x && yi[u2] < jc);
+                    }
+                    for (; o < count; ++o) rank += (f.val[o] > x) || (f.val[o] == x && f.idx[o] < jc);
+                    if (rank < kk) f.gidx[atomicAdd(&cm.count, 1u)] = jc;
+                }
+                __syncthreads();
+                if (sel) {
+                    for (int t = tid; t < kk; t += kThreads) {
+                        const int32_t jt = f.gidx[t];
+                        int pos = 0;
+                        int o = 0;
+                        for (; o + 8 <= kk; o += 8) {
+                            int32_t yi[8];
+#pragma unroll
+                            for (int u2 = 0; u2 < 8; ++u2) yi[u2] = f.gidx[o + u2];
+#pragma unroll
+                            for (int u2 = 0; u2 < 8; ++u2) pos += yi[u2] < jt;
+                        }
+                        for (; o < kk; ++o) pos += f.gidx[o] < jt;
+                        sel[pos] = jt;
+                    }
+                    for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
+                }
+                return;
+            }
             // 3. cutoff, bitmap words of the candidate groups, ordered output
             find_kth(cm, f.hist, f.val, f.idx, count, kk);
             const double cv = cm.cut_v;
