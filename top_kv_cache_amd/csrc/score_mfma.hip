@@ -421,6 +421,7 @@ struct CertShared {
     int32_t xs[kCCap];              // their indices
     uint32_t hist[kCBins];
     uint32_t bitmap[kCCap / 32];
+    double qblk[32 * kD];           // q_eff of 32 of the block's queries (re-scoring)
     double red_d[2][kCWaves];
     uint32_t red_u[kCWaves];
     uint32_t scan[kCWaves + 1];
@@ -611,41 +612,80 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
     const uint32_t nd = sh.nd, nx = sh.nx;
     const int64_t need = (int64_t)kk - nd;
     if (need > 0) {
-        // exact (fp64) block scores of the uncertain spans: a wave per span,
-        // 16 lanes per key row, the group-summed queries read from L2
-        const int rs = lane >> 4, ch = lane & 15;
-        const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes + ch * 16;
-        const double *qb = a.qeff + ((int64_t)h * a.n_q + (int64_t)b * kQB) * kD + ch * 8;
-        for (uint32_t x = wave; x < nx; x += kCWaves) {
-            const int64_t j = sh.xs[x];
-            const int64_t tb = a.mid_lo + j * a.S, te = min(tb + (int64_t)a.S, a.mid_hi);
-            double total = 0.0;
-            for (int il = 0; il < kQB; ++il) {
-                double qv[8];
+        // exact (fp64) block scores of the uncertain spans, a wave per span.
+        // The block's q_eff is staged in LDS 32 queries at a time; lane =
+        // (token tl of a 32-token chunk, query half sub): it accumulates the
+        // 16 dot products of its token with queries sub*16.. in fp64 (the
+        // products of a bf16 key with q_eff are exact), then the per-query
+        // maxima over the 32 token lanes come from a transpose-reduce and the
+        // 32 maxima are summed; the two query halves are added in order.
+        const int tl = lane & 31, sub = lane >> 5;
+        const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes;
+        for (int qh = 0; qh < 2; ++qh) {
+            const double *qsrc = a.qeff + ((int64_t)h * a.n_q + (int64_t)b * kQB + qh * 32) * kD;
+            for (int i = tid; i < 32 * kD; i += kCThreads) sh.qblk[i] = qsrc[i];
+            __syncthreads();
+            for (uint32_t x = wave; x < nx; x += kCWaves) {
+                const int64_t j = sh.xs[x];
+                const int64_t tb = a.mid_lo + j * a.S, te = min(tb + (int64_t)a.S, a.mid_hi);
+                double best[16];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] = qb[(int64_t)il * kD + e];
-                double best = -INFINITY;
-                for (int64_t t0 = tb; t0 < te; t0 += 4) {
-                    const int64_t t = t0 + rs;
+                for (int i = 0; i < 16; ++i) best[i] = -INFINITY;
+                for (int64_t c0 = tb; c0 < te; c0 += 32) {
+                    const int64_t t = c0 + tl;
                     const bool ok = t < te;
-                    const uint4 raw = ok ? ld16(kh + t * a.st_bytes) : make_uint4(0u, 0u, 0u, 0u);
-                    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-                    double acc = 0.0;
+                    const unsigned char *krow = kh + (ok ? t : tb) * a.st_bytes;
+                    double acc[16];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc = fma(qv[2 * e], (double)__uint_as_float(w4[e] << 16), acc);
-                        acc = fma(qv[2 * e + 1], (double)__uint_as_float(w4[e] & 0xffff0000u), acc);
+                    for (int i = 0; i < 16; ++i) acc[i] = 0.0;
+                    // the key row in two halves of 8 chunks, each half's loads
+                    // issued together before its arithmetic
+                    for (int half = 0; half < 2; ++half) {
+                        uint4 kraw[8];
+#pragma unroll
+                        for (int cc = 0; cc < 8; ++cc) kraw[cc] = ld16(krow + (half * 8 + cc) * 16);
+#pragma unroll
+                        for (int cc = 0; cc < 8; ++cc) {
+                            const uint32_t w4[4] = {kraw[cc].x, kraw[cc].y, kraw[cc].z, kraw[cc].w};
+                            double kd[8];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                kd[2 * e] = (double)__uint_as_float(w4[e] << 16);
+                                kd[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
+                            }
+                            const double *qc = sh.qblk + sub * 16 * kD + (half * 8 + cc) * 8;
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[i] = fma(qc[i * kD + e], kd[e], acc[i]);
+                            }
+                        }
                     }
-                    for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
-                    if (ok) best = fmax(best, acc);
+                    if (ok)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) best[i] = fmax(best[i], acc[i]);
                 }
-                best = fmax(best, __shfl_xor(best, 16));
-                best = fmax(best, __shfl_xor(best, 32));
-                total += best;
+                // transpose-max over the 32 token lanes: after the steps over
+                // lane^16, ^8, ^4, ^2 lane l keeps query slot (l/2)%16 (bits of
+                // l taken from the top), and lane^1 holds the same value
+#pragma unroll
+                for (int o = 16, nv = 16; o >= 2; o >>= 1, nv >>= 1) {
+                    const bool upper = (tl & o) != 0;
+#pragma unroll
+                    for (int i = 0; i < nv / 2; ++i) {
+                        const double keep = upper ? best[i + nv / 2] : best[i];
+                        const double send = upper ? best[i] : best[i + nv / 2];
+                        best[i] = fmax(keep, __shfl_xor(send, o));
+                    }
+                }
+                best[0] = fmax(best[0], __shfl_xor(best[0], 1));
+                // sum of the 32 maxima (even lanes hold one query each)
+                double v = (lane & 1) ? 0.0 : best[0];
+                for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+                if (lane == 0) sh.xv[x] = (qh == 0 ? v : sh.xv[x] + v) + 0.0;
             }
-            if (lane == 0) sh.xv[x] = total + 0.0;
+            __syncthreads();
         }
-        __syncthreads();
         for (uint32_t x = tid; x < nx; x += kCThreads) {
             sh.val[x] = sh.xv[x];
             sh.idx[x] = sh.xs[x];
