@@ -5,8 +5,10 @@
 // flash_attention(query, key_recall, value_recall)), flash-style: key tiles of
 // 32 window rows are staged in LDS and the softmax is carried online.
 //
-// One workgroup = 4 waves = 128 query rows of one (block, KV head); a wave
-// owns 32 query rows r (query i = r / g, head h*g + r % g).  Per key tile:
+// One workgroup = 8 waves = 256 query rows of one (block, KV head) (a block
+// of 64 queries with g = 4 in one workgroup, so its key tiles are staged
+// once); a wave owns 32 query rows r (query i = r / g, head h*g + r % g).
+// Per key tile:
 //   S^T = K' Q'^T on v_mfma_f32_32x32x16_bf16 with K' and Q' each split into
 //         bf16 hi + lo (three products: hi.hi + hi.lo + lo.hi, ~16-bit inputs),
 //         so a lane holds one query's 16 logits of the tile and the softmax
@@ -41,7 +43,8 @@ constexpr int kD = 128;
 constexpr int kKT = 32;             // keys per tile
 constexpr int kKPad = 136;          // K' tile row stride (bf16)
 constexpr int kVPad = 40;           // V^T tile row stride (bf16)
-constexpr int kRowsWG = 128;        // query rows per workgroup
+constexpr int kAThreads = 512;      // 8 waves
+constexpr int kRowsWG = kAThreads / 2;   // query rows per workgroup (32 per wave)
 
 constexpr int kSelCap = 4096;       // selection entries staged in LDS (cache source)
 
@@ -102,7 +105,7 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float (&x)[8]) {
 }
 
 template <bool kCache>
-__global__ __launch_bounds__(256, 2) void k_attend_mfma(MAttnArgs a) {
+__global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
     __shared__ __align__(16) uint16_t khi[2][kKT][kKPad];
     __shared__ __align__(16) uint16_t klo[2][kKT][kKPad];
     __shared__ __align__(16) uint16_t vt[2][kD][kVPad];
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_mfma(MAttnArgs a) {
         sel_len = (int64_t)ns * a.S;
         if (a.last_len != a.S && ns > 0 && a.sel[(int64_t)bh * a.topk + ns - 1] == a.n_spans - 1)
             sel_len -= a.S - a.last_len;
-        for (int t = tid; t < ns; t += 256) ssel[t] = a.sel[(int64_t)bh * a.topk + t];
+        for (int t = tid; t < ns; t += kAThreads) ssel[t] = a.sel[(int64_t)bh * a.topk + t];
         Wbh = a.Gp + sel_len + a.Lp;
     } else {
         Wbh = a.W[bh];
@@ -177,98 +180,99 @@ __global__ __launch_bounds__(256, 2) void k_attend_mfma(MAttnArgs a) {
     if (kend > Wbh) kend = Wbh;
     const int64_t n_tiles = (kend + kKT - 1) / kKT;
 
-    // staging.  window: thread -> key row tid/8, channels (tid%8)*16 .. +16.
-    // cache: thread -> key row tid/8, channel pairs (tid%8)*8 .. +8, i.e.
-    // channels c0 .. c0+8 and c0+D/2 .. c0+D/2+8.
-    const int skey = tid >> 3, sch = (tid & 7) * 16, c0 = (tid & 7) * 8;
+    // staging (512 threads, 32 rows).  K, window: thread -> key row tid/16,
+    // channels (tid%16)*8 .. +8.  K, cache: thread -> key row tid/16, channel
+    // pairs (tid%16)*4 .. +4, i.e. channels c0 .. c0+4 and c0+D/2 .. c0+D/2+4.
+    // V: thread -> key row tid%32, channels (tid/32)*8 .. +8, so lanes l and
+    // l^1 hold adjacent keys and V^T is written one 32-bit word (two keys) at
+    // a time.
+    const int skey = tid >> 4, sch = (tid & 15) * 8, c0 = (tid & 15) * 4;
+    const int vkey = tid & 31, vch = (tid >> 5) * 8;
     const float *kwb = a.k_win + (int64_t)bh * a.W_cap * kD;
     const uint16_t *vwb = a.v_win + (int64_t)bh * a.W_cap * kD;
     const uint16_t *kcb = a.k + (int64_t)h * a.sh;
     const uint16_t *vcb = a.v + (int64_t)h * a.sh;
-    float4 kr[4];               // window: 16 fp32 keys; cache: 4 x (cos, sin) pairs
-    uint4 vr[2], kc[2];
+    float4 kr[2];               // window: 8 fp32 keys; cache: 4 x (cos, sin)
+    uint4 vr;
+    uint2 kc[2];
+    // cache row of window row wl (rows past the end read window row 0: finite
+    // data that is masked or multiplied by a zero weight)
+    auto src_row = [&](int64_t wl) -> int64_t {
+        int64_t src;
+        if (wl < a.Gp) {
+            src = wl;
+        } else if (wl < a.Gp + sel_len) {
+            const uint32_t o = (uint32_t)(wl - a.Gp);
+            const uint32_t qs = o / (uint32_t)a.S;
+            src = a.mid_lo + (int64_t)ssel[qs] * a.S + (o - qs * (uint32_t)a.S);
+        } else {
+            src = a.T - a.Lp + (wl - a.Gp - sel_len);
+        }
+        return src * a.st;
+    };
     auto load_tile = [&](int64_t w0) {
-        const int64_t w = w0 + skey;
-        const bool ok = w < kend;
+        const int64_t w = w0 + skey, wv = w0 + vkey;
+        const bool ok = w < kend, okv = wv < kend;
         if (kCache) {
-            // rows past the end read window row 0 (finite data, never used)
             const int64_t wl = ok ? w : 0;
-            int64_t src;
-            if (wl < a.Gp) {
-                src = wl;
-            } else if (wl < a.Gp + sel_len) {
-                const uint32_t o = (uint32_t)(wl - a.Gp);
-                const uint32_t qs = o / (uint32_t)a.S;
-                src = a.mid_lo + (int64_t)ssel[qs] * a.S + (o - qs * (uint32_t)a.S);
-            } else {
-                src = a.T - a.Lp + (wl - a.Gp - sel_len);
-            }
-            const int64_t row = src * a.st;
-            kc[0] = *(const uint4 *)(kcb + row + c0);
-            kc[1] = *(const uint4 *)(kcb + row + c0 + kD / 2);
-            vr[0] = *(const uint4 *)(vcb + row + c0);
-            vr[1] = *(const uint4 *)(vcb + row + c0 + kD / 2);
+            const int64_t row = src_row(wl), rowv = src_row(okv ? wv : 0);
+            kc[0] = *(const uint2 *)(kcb + row + c0);
+            kc[1] = *(const uint2 *)(kcb + row + c0 + kD / 2);
+            vr = *(const uint4 *)(vcb + rowv + vch);
             const float4 *rp = (const float4 *)(a.rope + wl * (kD / 2) + c0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kr[e] = rp[e];
+            kr[0] = rp[0];
+            kr[1] = rp[1];
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                kr[e] = ok ? *(const float4 *)(kwb + w * kD + sch + e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
             for (int e = 0; e < 2; ++e)
-                vr[e] = ok ? *(const uint4 *)(vwb + w * kD + sch + e * 8) : make_uint4(0u, 0u, 0u, 0u);
+                kr[e] = ok ? *(const float4 *)(kwb + w * kD + sch + e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            vr = okv ? *(const uint4 *)(vwb + wv * kD + vch) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    // V^T from this lane's 16 channels of key vkey and lane^1's (key vkey^1):
+    // the even lane writes the even channels, the odd lane the odd ones, each
+    // word holding (key 2m, key 2m+1)
+    auto store_vt = [&](int buf) {
+        const bool odd = (vkey & 1) != 0;
+        const uint32_t w8[4] = {vr.x, vr.y, vr.z, vr.w};
+        uint32_t *vrow = (uint32_t *)&vt[buf][0][0];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t send = odd ? (w8[m] & 0xffffu) : (w8[m] >> 16);
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+            const uint32_t word = odd ? (recv | (w8[m] & 0xffff0000u)) : ((w8[m] & 0xffffu) | (recv << 16));
+            const int ch = vch + 2 * m + (odd ? 1 : 0);
+            vrow[(ch * kVPad + (vkey & ~1)) / 2] = word;
         }
     };
     auto store_tile = [&](int buf) {
         if (kCache) {
-            float x1[8], x2[8], y1[8], y2[8];
-            bf16x8_to_f32(kc[0], x1);
-            bf16x8_to_f32(kc[1], x2);
-            const float cs[8][2] = {{kr[0].x, kr[0].y}, {kr[0].z, kr[0].w}, {kr[1].x, kr[1].y},
-                                    {kr[1].z, kr[1].w}, {kr[2].x, kr[2].y}, {kr[2].z, kr[2].w},
-                                    {kr[3].x, kr[3].y}, {kr[3].z, kr[3].w}};
+            const float x1[4] = {__uint_as_float(kc[0].x << 16), __uint_as_float(kc[0].x & 0xffff0000u),
+                                 __uint_as_float(kc[0].y << 16), __uint_as_float(kc[0].y & 0xffff0000u)};
+            const float x2[4] = {__uint_as_float(kc[1].x << 16), __uint_as_float(kc[1].x & 0xffff0000u),
+                                 __uint_as_float(kc[1].y << 16), __uint_as_float(kc[1].y & 0xffff0000u)};
+            const float cs[4][2] = {{kr[0].x, kr[0].y}, {kr[0].z, kr[0].w}, {kr[1].x, kr[1].y},
+                                    {kr[1].z, kr[1].w}};
+            float y[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                y1[e] = x1[e] * cs[e][0] - x2[e] * cs[e][1];
-                y2[e] = x2[e] * cs[e][0] + x1[e] * cs[e][1];
+            for (int e = 0; e < 4; ++e) {
+                y[e] = x1[e] * cs[e][0] - x2[e] * cs[e][1];
+                y[4 + e] = x2[e] * cs[e][0] + x1[e] * cs[e][1];
             }
             uint4 hi, lo;
-            split8(y1, hi, lo);
-            *(uint4 *)&khi[buf][skey][c0] = hi;
-            *(uint4 *)&klo[buf][skey][c0] = lo;
-            split8(y2, hi, lo);
-            *(uint4 *)&khi[buf][skey][c0 + kD / 2] = hi;
-            *(uint4 *)&klo[buf][skey][c0 + kD / 2] = lo;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t w4[4] = {vr[e].x, vr[e].y, vr[e].z, vr[e].w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    vt[buf][c0 + e * (kD / 2) + 2 * k][skey] = (uint16_t)(w4[k] & 0xffffu);
-                    vt[buf][c0 + e * (kD / 2) + 2 * k + 1][skey] = (uint16_t)(w4[k] >> 16);
-                }
-            }
+            split8(y, hi, lo);
+            *(uint2 *)&khi[buf][skey][c0] = make_uint2(hi.x, hi.y);
+            *(uint2 *)&klo[buf][skey][c0] = make_uint2(lo.x, lo.y);
+            *(uint2 *)&khi[buf][skey][c0 + kD / 2] = make_uint2(hi.z, hi.w);
+            *(uint2 *)&klo[buf][skey][c0 + kD / 2] = make_uint2(lo.z, lo.w);
         } else {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float x[8] = {kr[2 * e].x, kr[2 * e].y, kr[2 * e].z, kr[2 * e].w,
-                                    kr[2 * e + 1].x, kr[2 * e + 1].y, kr[2 * e + 1].z, kr[2 * e + 1].w};
-                uint4 hi, lo;
-                split8(x, hi, lo);
-                *(uint4 *)&khi[buf][skey][sch + e * 8] = hi;
-                *(uint4 *)&klo[buf][skey][sch + e * 8] = lo;
-            }
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t w4[4] = {vr[e].x, vr[e].y, vr[e].z, vr[e].w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    vt[buf][sch + e * 8 + 2 * k][skey] = (uint16_t)(w4[k] & 0xffffu);
-                    vt[buf][sch + e * 8 + 2 * k + 1][skey] = (uint16_t)(w4[k] >> 16);
-                }
-            }
+            const float x[8] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w, kr[1].x, kr[1].y, kr[1].z, kr[1].w};
+            uint4 hi, lo;
+            split8(x, hi, lo);
+            *(uint4 *)&khi[buf][skey][sch] = hi;
+            *(uint4 *)&klo[buf][skey][sch] = lo;
         }
+        store_vt(buf);
     };
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -443,7 +447,7 @@ hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_
     a.block_q = g.block_q;
     a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
     a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
-    hipLaunchKernelGGL(k_attend_mfma<false>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attend_mfma<false>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(kAThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -488,7 +492,7 @@ hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k,
     a.block_q = g.block_q;
     a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
     a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
-    hipLaunchKernelGGL(k_attend_mfma<true>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attend_mfma<true>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(kAThreads), 0, s, a);
     return hipGetLastError();
 }
 
