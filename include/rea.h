@@ -208,6 +208,42 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
                            void *ws, size_t ws_bytes, void *stream,
                            const rea_timing *timing);
 
+/*
+ * Chunked prefill of a whole prompt (OpenReview discussion, "Prefilling
+ * Phase" pseudocode: the first chunk of G + L tokens is attended in full, and
+ * every later chunk is appended to the cache and attended through its own
+ * top-k; the NIAH reply's settings use chunks of 512).  Every prompt token is a
+ * query: p->n_q == p->T, q = [T][n_q_heads][head_dim], and the K/V cache holds
+ * the whole prompt.  Chunk c covers queries [start, start + n_q) and is run as
+ * one rea_decode_step with the cache cut to its first start + n_q tokens, so
+ * each chunk sees exactly the tokens before and inside it.
+ *
+ * Plan (rea_prefill_plan): F = min(T, G + L) rounded down to a multiple of
+ * block_q; if F > 0 the first chunk is [0, F) (no middle cache yet: plain
+ * causal attention); then chunks of `chunk` tokens, the last one possibly
+ * shorter.  A chunk whose length n is not a multiple of block_q is cut into
+ * equal blocks of the largest divisor of n not above block_q.
+ * Preconditions (REA_EINVAL): n_q == T, 1 <= chunk <= L, chunk a multiple of
+ * block_q; every chunk must pass rea_decode_step's own checks.
+ */
+typedef struct rea_chunk {
+    int64_t start;      /* first query (prompt token) of the chunk */
+    int32_t n_q;        /* queries in the chunk */
+    int32_t block_q;    /* queries per selection block within the chunk */
+} rea_chunk;
+
+/* Host-only: writes up to `cap` chunks to `chunks` (may be NULL when cap is 0),
+ * the total count to *n_chunks, and the workspace rea_prefill needs to
+ * *ws_bytes (the largest of its chunk steps').  Makes no HIP call. */
+rea_status rea_prefill_plan(const rea_problem *p, const rea_params *a, int32_t chunk,
+                            rea_chunk *chunks, int32_t cap, int32_t *n_chunks,
+                            size_t *ws_bytes);
+
+/* Runs the plan on `stream` without host synchronisation; out is
+ * [T][n_q_heads][head_dim] float32.  ws as given by rea_prefill_plan. */
+rea_status rea_prefill(const rea_problem *p, const rea_params *a, int32_t chunk, float *out,
+                       void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

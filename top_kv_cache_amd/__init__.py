@@ -18,7 +18,8 @@ REA_BF16, REA_F32 = 0, 1
 STATUS = ["REA_OK", "REA_EINVAL", "REA_ESHAPE", "REA_EDTYPE", "REA_EALIGN",
           "REA_EWORKSPACE", "REA_ENODEVICE", "REA_ELAUNCH", "REA_EUNSUPPORTED"]
 ENTRY_POINTS = ["rea_abi_version", "rea_status_string", "rea_last_error", "rea_query_sizes",
-                "rea_score_select", "rea_gather_rope", "rea_window_attend", "rea_decode_step"]
+                "rea_score_select", "rea_gather_rope", "rea_window_attend", "rea_decode_step",
+                "rea_prefill_plan", "rea_prefill"]
 
 
 class Problem(ctypes.Structure):
@@ -46,6 +47,10 @@ class Sizes(ctypes.Structure):
 
 class Timing(ctypes.Structure):
     _fields_ = [("score_begin", ctypes.c_void_p), ("score_end", ctypes.c_void_p)]
+
+
+class Chunk(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_int64), ("n_q", ctypes.c_int32), ("block_q", ctypes.c_int32)]
 
 
 class ReaError(RuntimeError):
@@ -85,6 +90,11 @@ def lib():
     L.rea_decode_step.restype = ctypes.c_int
     L.rea_decode_step.argtypes = [P, A, vp, i32p, i32p, vp, ctypes.c_size_t, vp,
                                   ctypes.POINTER(Timing)]
+    L.rea_prefill_plan.restype = ctypes.c_int
+    L.rea_prefill_plan.argtypes = [P, A, ctypes.c_int32, ctypes.POINTER(Chunk), ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
+    L.rea_prefill.restype = ctypes.c_int
+    L.rea_prefill.argtypes = [P, A, ctypes.c_int32, vp, vp, ctypes.c_size_t, vp]
     if L.rea_abi_version() != 1:
         raise ImportError("librea.so ABI version mismatch")
     _lib = L
@@ -106,6 +116,18 @@ def problem(q_ptr, k_ptr, v_ptr, *, dtype, n_q, Hq, Hkv, d, T, stride_head, stri
 
 def params(G, S, topk, L, block_q=1, rope_theta=500000.0, softmax_scale=0.0) -> Params:
     return Params(ctypes.sizeof(Params), G, S, topk, L, block_q, rope_theta, softmax_scale, 0)
+
+
+def prefill_plan(p: Problem, a: Params, chunk: int):
+    """(list of (start, n_q, block_q), workspace bytes) of a chunked prefill.
+    Host-only (no GPU needed)."""
+    n, ws = ctypes.c_int32(), ctypes.c_size_t()
+    _check(lib().rea_prefill_plan(ctypes.byref(p), ctypes.byref(a), chunk, None, 0,
+                                  ctypes.byref(n), ctypes.byref(ws)))
+    arr = (Chunk * max(n.value, 1))()
+    _check(lib().rea_prefill_plan(ctypes.byref(p), ctypes.byref(a), chunk, arr, n.value,
+                                  ctypes.byref(n), ctypes.byref(ws)))
+    return [(c.start, c.n_q, c.block_q) for c in arr[:n.value]], ws.value
 
 
 def query_sizes(p: Problem, a: Params) -> Sizes:
@@ -237,4 +259,32 @@ class Step:
                                      _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel(),
                                      _stream(stream),
                                      ctypes.byref(timing) if timing is not None else None))
+        return out
+
+
+class Prefill:
+    """Chunked prefill of a whole prompt: q [T][Hq][d] (every prompt token is a
+    query) against the cache k, v of the same T tokens."""
+
+    def __init__(self, q, k, v, G, S, topk, L, block_q, chunk, rope_theta=500000.0,
+                 softmax_scale=0.0):
+        self.q, self.k, self.v = q, k, v
+        self.prob = problem_from_tensors(q, k, v)
+        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale)
+        self.chunk = chunk
+        self.plan, self.ws_bytes = prefill_plan(self.prob, self.par, chunk)
+        self.device = q.device
+
+    def workspace(self):
+        return _aligned(_ws(self.ws_bytes, self.device))
+
+    def run(self, out=None, ws=None, stream=None):
+        torch = _torch()
+        T, Hq, d = self.prob.n_q, self.prob.n_q_heads, self.prob.head_dim
+        if out is None:
+            out = torch.empty((T, Hq, d), dtype=torch.float32, device=self.device)
+        if ws is None:
+            ws = self.workspace()
+        _check(lib().rea_prefill(ctypes.byref(self.prob), ctypes.byref(self.par), self.chunk,
+                                 _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
         return out

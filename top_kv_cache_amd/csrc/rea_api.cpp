@@ -384,3 +384,106 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
 }
 
 }  // extern "C"
+
+// ---- chunked prefill ------------------------------------------------------
+
+namespace {
+
+int32_t block_for(int32_t n, int32_t bq) {
+    if (n % bq == 0) return bq;
+    for (int32_t b = bq < n ? bq : n; b > 1; --b)
+        if (n % b == 0) return b;
+    return 1;
+}
+
+// The chunk plan; calls emit(start, n_q, block_q) for each chunk in order.
+template <typename F>
+rea_status prefill_plan(const rea_problem *p, const rea_params *a, int32_t chunk, F emit) {
+    if (!p || !a) return fail(REA_EINVAL, "problem or params is NULL");
+    if (p->n_q != p->T)
+        return fail(REA_EINVAL, "prefill needs every prompt token as a query (n_q %d != T %lld)",
+                    p->n_q, (long long)p->T);
+    if (a->block_q < 1) return fail(REA_EINVAL, "block_q %d < 1", a->block_q);
+    if (chunk < 1 || chunk > a->L || chunk % a->block_q != 0)
+        return fail(REA_EINVAL, "chunk %d must lie in [1, L = %d] and be a multiple of block_q %d",
+                    chunk, a->L, a->block_q);
+    const int64_t T = p->T;
+    int64_t first = (int64_t)a->G + a->L < T ? (int64_t)a->G + a->L : T;
+    first -= first % a->block_q;
+    int64_t pos = 0;
+    if (first > 0) {
+        rea_status st = emit(0, (int32_t)first, a->block_q);
+        if (st != REA_OK) return st;
+        pos = first;
+    }
+    while (pos < T) {
+        const int32_t n = (int32_t)(T - pos < chunk ? T - pos : chunk);
+        rea_status st = emit(pos, n, block_for(n, a->block_q));
+        if (st != REA_OK) return st;
+        pos += n;
+    }
+    return REA_OK;
+}
+
+// The problem and params of one chunk: the cache cut after the chunk.
+void chunk_view(const rea_problem *p, const rea_params *a, int64_t start, int32_t n, int32_t bq,
+                rea_problem *pc, rea_params *ac) {
+    *pc = *p;
+    pc->T = start + n;
+    pc->n_q = n;
+    pc->q = (const char *)p->q + (size_t)start * p->n_q_heads * p->head_dim *
+                                     (p->dtype == REA_BF16 ? 2 : 4);
+    *ac = *a;
+    ac->block_q = bq;
+}
+
+}  // namespace
+
+extern "C" {
+
+rea_status rea_prefill_plan(const rea_problem *p, const rea_params *a, int32_t chunk,
+                            rea_chunk *chunks, int32_t cap, int32_t *n_chunks,
+                            size_t *ws_bytes) {
+    g_err[0] = 0;
+    if (!n_chunks || !ws_bytes) return fail(REA_EINVAL, "n_chunks or ws_bytes is NULL");
+    if (cap > 0 && !chunks) return fail(REA_EINVAL, "chunks is NULL while cap > 0");
+    int32_t count = 0;
+    size_t need = 0;
+    rea_status st = prefill_plan(p, a, chunk, [&](int64_t start, int32_t n, int32_t bq) {
+        rea_problem pc;
+        rea_params ac;
+        chunk_view(p, a, start, n, bq, &pc, &ac);
+        rea::Geom g;
+        rea_status s2 = make_geom(&pc, &ac, &g);
+        if (s2 != REA_OK) return s2;
+        const size_t w = decode_ws_bytes(g);
+        if (w > need) need = w;
+        if (count < cap) chunks[count] = rea_chunk{start, n, bq};
+        ++count;
+        return REA_OK;
+    });
+    if (st != REA_OK) return st;
+    *n_chunks = count;
+    *ws_bytes = need;
+    return REA_OK;
+}
+
+rea_status rea_prefill(const rea_problem *p, const rea_params *a, int32_t chunk, float *out,
+                       void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    if (!out) return fail(REA_EINVAL, "out is NULL");
+    int32_t count = 0;
+    size_t need = 0;
+    rea_status st = rea_prefill_plan(p, a, chunk, nullptr, 0, &count, &need);
+    if (st != REA_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, need)) != REA_OK) return st;
+    return prefill_plan(p, a, chunk, [&](int64_t start, int32_t n, int32_t bq) {
+        rea_problem pc;
+        rea_params ac;
+        chunk_view(p, a, start, n, bq, &pc, &ac);
+        float *oc = out + (size_t)start * p->n_q_heads * p->head_dim;
+        return rea_decode_step(&pc, &ac, oc, nullptr, nullptr, ws, ws_bytes, stream, nullptr);
+    });
+}
+
+}  // extern "C"
