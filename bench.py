@@ -112,6 +112,50 @@ def cpu_baseline(w, min_seconds=10.0):
                       f"{total:.1f} s of oracle time; input generation not timed"}
 
 
+def prefill_main(args):
+    """Chunked prefill of one 8B-shaped layer over a prompt of args.prefill_prompt
+    tokens (first G+L tokens in full, then 512-token chunks in blocks of 64):
+    one JSON line with prompt tokens per second (a TTFT-style figure for one
+    layer; not the headline)."""
+    import torch
+    import synth
+    import top_kv_cache_amd as rea
+    from synth import torch_io
+
+    T = args.prefill_prompt
+    w = synth.small(name=f"llama8b-bf16-prefill-prompt-{T}", seed=240715180, dtype="bf16",
+                    Hq=32, Hkv=8, d=128, T=T, n_q=T, block_q=1, G=32, S=32, topk=120, L=4096,
+                    needles=0, kv_scaled=True)
+    dev = torch.device("cuda:0")
+    q = torch_io.q_device(w, 0, dev)
+    K = torch_io.kv_device(w, 0, "k", device=dev)
+    V = torch_io.kv_device(w, 0, "v", device=dev)
+    pf = rea.Prefill(q, K, V, w.G, w.S, w.topk, w.L, 64, args.chunk, rope_theta=w.rope_theta)
+    ws, out = pf.workspace(), torch.empty((T, w.Hq, w.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pf.run(out=out, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        pf.run(out=out, ws=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] prefill of {T} tokens in {len(pf.plan)} chunks: {ms:.3f} ms "
+        f"({T / ms * 1e3 / 1e6:.2f} M prompt tokens/s, one layer)")
+    print(json.dumps({
+        "metric": "chunked-prefill prompt tokens/s (one layer)", "value": T / (ms / 1e3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": w.name, "layers": 1, "prompt": T, "chunk": args.chunk,
+                   "block_q": 64, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "G": w.G, "S": w.S, "topk": w.topk, "L": w.L, "chunks": len(pf.plan)},
+        "roofline": None, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,11 +166,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run one plain device copy of this size (HBM counter calibration)")
+    ap.add_argument("--prefill-prompt", type=int, default=0,
+                    help="instead: time a chunked prefill over a prompt of this many tokens")
+    ap.add_argument("--chunk", type=int, default=512, help="prefill chunk (with --prefill-prompt)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               f"(the path is measured on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.prefill_prompt > 0:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        prefill_main(args)
+        return
 
     import torch
     import synth
