@@ -46,7 +46,9 @@ Sources (the page title and the part of it each step follows):
 
 Readings taken where the pages are silent (each is listed in the design doc):
   * GQA: one selection per KV head, scoring with the sum of the group's
-    query-head logits (step 3).
+    query-head logits (step 3).  Variant (per_q_head=True): one selection per
+    query head with its own logits, its window gathered from its group's KV
+    head.  Token-level selection is the special case S = 1.
   * span reduce: max over the span's tokens (step 4); a block of queries sums
     its queries' span maxima.
   * ties: lower span index first (step 5).
@@ -93,17 +95,33 @@ def span_list(mid_lo: int, mid_hi: int, S: int):
 # --------------------------------------------------------------------------
 # 3-4. scores
 # --------------------------------------------------------------------------
-def token_scores(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int,
+def selection_units(Hq: int, Hkv: int, per_q_head: bool = False):
+    """(KV head, query heads) of every independent selection.
+
+    Default: one selection per KV head, scored with the summed logits of the
+    query heads of its GQA group.  per_q_head: one selection per query head,
+    scored with that head's own logits against its group's KV head (the
+    discussion's remark that selection is made for each attention head).
+    """
+    g = Hq // Hkv
+    if per_q_head:
+        return [(hq // g, [hq]) for hq in range(Hq)]
+    return [(h, list(range(h * g, (h + 1) * g))) for h in range(Hkv)]
+
+
+def token_scores(q_blk: np.ndarray, K_h: np.ndarray, qheads,
                  mid_lo: int, mid_hi: int) -> np.ndarray:
-    """s[i, t - mid_lo] = sum_g q[i, h*g+gg] . K_h[t]  for t in the middle.
+    """s[i, t - mid_lo] = sum over query heads hq in qheads of q[i, hq] . K_h[t],
+    for t in the middle.
 
     q_blk: [nb][Hq][d] fp64, K_h: [T][d] fp64.  Un-rotated, unscaled.
     """
     nb, _, d = q_blk.shape
-    Qh = q_blk[:, h * g:(h + 1) * g, :].reshape(nb * g, d)       # [nb*g][d]
+    m = len(qheads)
+    Qh = q_blk[:, qheads, :].reshape(nb * m, d)                   # [nb*m][d]
     Km = K_h[mid_lo:mid_hi]                                       # [N][d]
-    per_head = Qh @ Km.T                                          # [nb*g][N]
-    return per_head.reshape(nb, g, -1).sum(axis=1)                # [nb][N]
+    per_head = Qh @ Km.T                                          # [nb*m][N]
+    return per_head.reshape(nb, m, -1).sum(axis=1)                # [nb][N]
 
 
 def span_scores_from_tokens(s: np.ndarray, spans, mid_lo: int) -> np.ndarray:
@@ -125,7 +143,7 @@ def span_scores_from_tokens(s: np.ndarray, spans, mid_lo: int) -> np.ndarray:
     return sig + 0.0
 
 
-def _exact_span_score_fractions(q_blk, K_h, h, g, span) -> Fraction:
+def _exact_span_score_fractions(q_blk, K_h, qheads, span) -> Fraction:
     """Exact rational span score by direct Fraction arithmetic (slow)."""
     a, b = span
     total = Fraction(0)
@@ -134,8 +152,8 @@ def _exact_span_score_fractions(q_blk, K_h, h, g, span) -> Fraction:
         best = None
         for t in range(a, b):
             acc = Fraction(0)
-            for gg in range(g):
-                qv = q_blk[i, h * g + gg]
+            for hq in qheads:
+                qv = q_blk[i, hq]
                 for c in range(d):
                     acc += Fraction(float(qv[c])) * Fraction(float(K_h[t, c]))
             if best is None or acc > best:
@@ -155,7 +173,7 @@ def _lsb_exponent(x: np.ndarray):
     return int(np.min(e - 53 + np.log2(low).astype(np.int64)))
 
 
-def exact_span_score(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int, span) -> Fraction:
+def exact_span_score(q_blk: np.ndarray, K_h: np.ndarray, qheads, span) -> Fraction:
     """Exact rational value of sigma for one span (inputs are dyadic floats).
 
     Every product is a multiple of u = 2**(lsb(q) + lsb(K)); if every partial sum
@@ -165,18 +183,19 @@ def exact_span_score(q_blk: np.ndarray, K_h: np.ndarray, h: int, g: int, span) -
     """
     a, b = span
     nb, _, d = q_blk.shape
-    Q = q_blk[:, h * g:(h + 1) * g, :].reshape(nb * g, d)
+    m = len(qheads)
+    Q = q_blk[:, qheads, :].reshape(nb * m, d)
     Ks = K_h[a:b]
     lq, lk = _lsb_exponent(Q), _lsb_exponent(Ks)
     if lq is None or lk is None:
         return Fraction(0)
     unit = 2.0 ** (lq + lk)
-    bound = (np.abs(Q) @ np.abs(Ks).T).reshape(nb, g, -1).sum(axis=1) * (1.0 + 1e-9)
+    bound = (np.abs(Q) @ np.abs(Ks).T).reshape(nb, m, -1).sum(axis=1) * (1.0 + 1e-9)
     limit = 2.0 ** 52 * unit
     if bound.max() < limit and bound.max(axis=1).sum() * (1.0 + 1e-9) < limit:
-        s = (Q @ Ks.T).reshape(nb, g, -1).sum(axis=1)
+        s = (Q @ Ks.T).reshape(nb, m, -1).sum(axis=1)
         return Fraction(float(s.max(axis=1).sum()))
-    return _exact_span_score_fractions(q_blk, K_h, h, g, span)
+    return _exact_span_score_fractions(q_blk, K_h, qheads, span)
 
 
 # --------------------------------------------------------------------------
@@ -253,94 +272,101 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def score_select(q, K, G, S, k, L, block_q=1, return_scores=False):
+def score_select(q, K, G, S, k, L, block_q=1, return_scores=False, per_q_head=False):
     """Steps 1-5.  q [n_q][Hq][d], K [Hkv][T][d] (any float dtype, upcast to fp64).
 
-    Returns sel: list over blocks of list over KV heads of ascending span
-    indices (and the fp64 span scores [n_blk][Hkv][n_spans] if asked).
+    Returns sel: list over blocks of list over selection units (KV heads, or
+    query heads when per_q_head) of ascending span indices (and the fp64 span
+    scores [n_blk][n_units][n_spans] if asked).
     """
     q = _f64(q)
     K = _f64(K)
     n_q, Hq, d = q.shape
     Hkv, T, _ = K.shape
-    g = Hq // Hkv
+    units = selection_units(Hq, Hkv, per_q_head)
     Gp, Lp, lo, hi = regions(T, G, L)
     spans = span_list(lo, hi, S)
     n_blk = n_q // block_q
     sel = []
-    scores = np.zeros((n_blk, Hkv, len(spans)), dtype=np.float64)
+    scores = np.zeros((n_blk, len(units), len(spans)), dtype=np.float64)
     for b in range(n_blk):
         qb = q[b * block_q:(b + 1) * block_q]
         row = []
-        for h in range(Hkv):
+        for u, (h, qheads) in enumerate(units):
             if spans:
-                s = token_scores(qb, K[h], h, g, lo, hi)
+                s = token_scores(qb, K[h], qheads, lo, hi)
                 sig = span_scores_from_tokens(s, spans, lo)
             else:
                 sig = np.zeros(0)
-            scores[b, h] = sig
+            scores[b, u] = sig
             row.append(select_topk(
-                sig, k, lambda j, qb=qb, h=h: exact_span_score(qb, K[h], h, g, spans[j])))
+                sig, k,
+                lambda j, qb=qb, h=h, qh=qheads: exact_span_score(qb, K[h], qh, spans[j])))
         sel.append(row)
     return (sel, scores) if return_scores else sel
 
 
-def gather_rope(q, K, V, sel, G, S, L, block_q=1, theta=500000.0):
+def gather_rope(q, K, V, sel, G, S, L, block_q=1, theta=500000.0, per_q_head=False):
     """Steps 6-7.  Returns (K_win, V_win, q_rot, W, qpos) with
-    K_win/V_win lists [n_blk][Hkv] of [W][d] fp64 arrays (K rotated, V plain),
-    q_rot [n_q][Hq][d] fp64, W [n_blk][Hkv], qpos [n_q][Hkv] window positions."""
+    K_win/V_win lists [n_blk][n_units] of [W][d] fp64 arrays (K rotated, V
+    plain), q_rot [n_q][Hq][d] fp64, W [n_blk][n_units], qpos [n_q][n_units]
+    window positions; the units are the KV heads, or the query heads when
+    per_q_head (each window is gathered from the unit's KV head)."""
     q = _f64(q)
     K = _f64(K)
     V = _f64(V)
     n_q, Hq, d = q.shape
     Hkv, T, _ = K.shape
-    g = Hq // Hkv
+    units = selection_units(Hq, Hkv, per_q_head)
     Gp, Lp, lo, hi = regions(T, G, L)
     spans = span_list(lo, hi, S)
     n_blk = n_q // block_q
     K_win, V_win = [], []
-    W = np.zeros((n_blk, Hkv), dtype=np.int64)
-    qpos = np.zeros((n_q, Hkv), dtype=np.int64)
+    W = np.zeros((n_blk, len(units)), dtype=np.int64)
+    qpos = np.zeros((n_q, len(units)), dtype=np.int64)
     q_rot = np.zeros_like(q)
     for b in range(n_blk):
         kr, vr = [], []
-        for h in range(Hkv):
-            src = window_src(T, Gp, Lp, spans, sel[b][h])
+        for u, (h, qheads) in enumerate(units):
+            src = window_src(T, Gp, Lp, spans, sel[b][u])
             Wbh = len(src)
-            W[b, h] = Wbh
+            W[b, u] = Wbh
             kr.append(rope(K[h][src], np.arange(Wbh), theta))
             vr.append(V[h][src])
             for i in range(b * block_q, (b + 1) * block_q):
                 p_abs = T - n_q + i
                 pos = Wbh - (T - p_abs)       # row holding the query's own key
-                qpos[i, h] = pos
-                q_rot[i, h * g:(h + 1) * g] = rope(q[i, h * g:(h + 1) * g], np.full(g, pos), theta)
+                qpos[i, u] = pos
+                q_rot[i, qheads] = rope(q[i, qheads], np.full(len(qheads), pos), theta)
         K_win.append(kr)
         V_win.append(vr)
     return K_win, V_win, q_rot, W, qpos
 
 
 def window_attend(q_rot, K_win, V_win, qpos, block_q=1, scale=None):
-    """Step 8.  Returns out [n_q][Hq][d] fp64."""
+    """Step 8.  Returns out [n_q][Hq][d] fp64.  Unit u of K_win (a KV head, or a
+    query head) serves the Hq / n_units consecutive query heads from u * that."""
     n_q, Hq, d = q_rot.shape
-    Hkv = len(K_win[0])
-    g = Hq // Hkv
+    n_units = len(K_win[0])
+    m = Hq // n_units
     sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
     out = np.zeros((n_q, Hq, d), dtype=np.float64)
     for b in range(n_q // block_q):
         i0, i1 = b * block_q, (b + 1) * block_q
-        for h in range(Hkv):
-            Q = q_rot[i0:i1, h * g:(h + 1) * g].reshape(-1, d)     # rows (i, gg)
-            pos = np.repeat(qpos[i0:i1, h], g)
-            out[i0:i1, h * g:(h + 1) * g] = attend_rows(
-                Q, K_win[b][h], V_win[b][h], pos, sc).reshape(i1 - i0, g, d)
+        for u in range(n_units):
+            Q = q_rot[i0:i1, u * m:(u + 1) * m].reshape(-1, d)     # rows (i, head)
+            pos = np.repeat(qpos[i0:i1, u], m)
+            out[i0:i1, u * m:(u + 1) * m] = attend_rows(
+                Q, K_win[b][u], V_win[b][u], pos, sc).reshape(i1 - i0, m, d)
     return out
 
 
-def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, return_all=False):
+def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, return_all=False,
+         per_q_head=False):
     """Steps 1-8 (the fused decode/prefill step).  Returns (out, sel)."""
-    sel = score_select(q, K, G, S, k, L, block_q)
-    K_win, V_win, q_rot, W, qpos = gather_rope(q, K, V, sel, G, S, L, block_q, theta)
+    sel = score_select(q, K, G, S, k, L, block_q, per_q_head=per_q_head)
+    K_win, V_win, q_rot, W, qpos = gather_rope(q, K, V, sel, G, S, L, block_q, theta,
+                                               per_q_head=per_q_head)
     out = window_attend(q_rot, K_win, V_win, qpos, block_q, scale)
     if return_all:
         return dict(out=out, sel=sel, K_win=K_win, V_win=V_win, q_rot=q_rot, W=W, qpos=qpos)

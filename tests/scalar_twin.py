@@ -20,10 +20,13 @@ def _rot(x, pos, theta):
     return y
 
 
-def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None):
+def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, per_q_head=False):
     """q [n_q][Hq][d], K/V [Hkv][T][d] as nested lists of floats.
 
-    Returns (out [n_q][Hq][d] floats, sel [n_blk][Hkv] lists, W [n_blk][Hkv]).
+    Returns (out [n_q][Hq][d] floats, sel [n_blk][units] lists, W [n_blk][units]),
+    where the units are the KV heads (each scored with its group's summed
+    logits) or, with per_q_head, the query heads (each with its own logits
+    against its group's KV head).
     """
     n_q, Hq, d = len(q), len(q[0]), len(q[0][0])
     Hkv, T = len(K), len(K[0])
@@ -39,9 +42,17 @@ def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None):
     sc = 1.0 / math.sqrt(d) if scale is None else scale
     out = [[[0.0] * d for _ in range(Hq)] for _ in range(n_q)]
     sel_all, W_all = [], []
+    if per_q_head:
+        units = []
+        for hq in range(Hq):
+            units.append((hq // g, [hq]))
+    else:
+        units = []
+        for h in range(Hkv):
+            units.append((h, [h * g + gg for gg in range(g)]))
     for b in range(n_q // block_q):
         sel_b, W_b = [], []
-        for h in range(Hkv):
+        for (h, heads) in units:
             sig = []
             for (a, e) in spans:
                 tot = Fraction(0)
@@ -49,9 +60,9 @@ def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None):
                     best = None
                     for t in range(a, e):
                         acc = Fraction(0)
-                        for gg in range(g):
+                        for hq in heads:
                             for c in range(d):
-                                acc += Fraction(q[i][h * g + gg][c]) * Fraction(K[h][t][c])
+                                acc += Fraction(q[i][hq][c]) * Fraction(K[h][t][c])
                         if best is None or acc > best:
                             best = acc
                     tot += best
@@ -74,8 +85,7 @@ def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None):
             krot = [_rot(K[h][src[w]], w, theta) for w in range(Wh)]
             for i in range(b * block_q, (b + 1) * block_q):
                 pos = Wh - n_q + i
-                for gg in range(g):
-                    hq = h * g + gg
+                for hq in heads:
                     qr = _rot(q[i][hq], pos, theta)
                     logits = []
                     for w in range(pos + 1):

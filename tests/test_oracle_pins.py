@@ -87,19 +87,23 @@ def check_golden():
         K = np.array(case["K"], dtype=np.float64)
         V = K.copy()
         G, S, L, bq = case["G"], case["S"], case["L"], case["block_q"]
+        pqh = case.get("per_q_head", False)
         Hkv, T, _ = K.shape
+        g = q.shape[1] // Hkv
         for ex in case["expect"]:
-            sel, sc = O.score_select(q, K, G, S, ex["k"], L, bq, return_scores=True)
+            sel, sc = O.score_select(q, K, G, S, ex["k"], L, bq, return_scores=True,
+                                     per_q_head=pqh)
             assert sel == ex["sel"], (case["name"], ex["k"], sel)
             exp_sc = np.array(case["span_scores"], dtype=np.float64)
             assert sc.shape == exp_sc.shape and np.array_equal(sc, exp_sc), (case["name"], sc)
-            Kw, Vw, qr, W, qpos = O.gather_rope(q, K, V, sel, G, S, L, bq)
+            Kw, Vw, qr, W, qpos = O.gather_rope(q, K, V, sel, G, S, L, bq, per_q_head=pqh)
             assert W.tolist() == ex["W"], (case["name"], W)
             assert qpos.tolist() == ex["qpos"], (case["name"], qpos)
             for b in range(len(sel)):
-                for h in range(Hkv):
-                    src = np.array(ex["src"][b][h])
-                    assert np.array_equal(Vw[b][h], V[h][src]), (case["name"], "V window")
+                for u in range(len(sel[b])):
+                    h = u // g if pqh else u
+                    src = np.array(ex["src"][b][u])
+                    assert np.array_equal(Vw[b][u], V[h][src]), (case["name"], "V window")
 
 
 def check_full_attention(seed=1):
@@ -167,13 +171,42 @@ def check_scalar_twin(seed=4):
         (2, 1, 3, 1, 4, 19, 0, 2, 3, 3, "int"),
         (1, 1, 2, 2, 4, 11, 4, 2, 1, 8, "bf16"),     # T <= G+L
     ]
-    for (n_q, bq, Hq, Hkv, d, T, G, S, k, L, kind) in shapes:
+    per_head_shapes = [
+        (1, 1, 4, 2, 4, 29, 2, 3, 3, 4, "bf16"),
+        (2, 2, 3, 1, 4, 23, 1, 2, 2, 5, "int"),
+        (1, 1, 2, 1, 4, 21, 2, 1, 5, 3, "f32"),      # token level (S = 1)
+    ]
+    cases = [(sh, False) for sh in shapes] + [(sh, True) for sh in per_head_shapes]
+    for (n_q, bq, Hq, Hkv, d, T, G, S, k, L, kind), pqh in cases:
         q, K, V = rand_problem(rng, n_q, Hq, Hkv, d, T, kind)
-        out_tw, sel_tw, W_tw = scalar_twin.step(q.tolist(), K.tolist(), V.tolist(), G, S, k, L, bq)
-        res = O.step(q, K, V, G, S, k, L, bq, return_all=True)
+        out_tw, sel_tw, W_tw = scalar_twin.step(q.tolist(), K.tolist(), V.tolist(), G, S, k, L, bq,
+                                                per_q_head=pqh)
+        res = O.step(q, K, V, G, S, k, L, bq, return_all=True, per_q_head=pqh)
         assert res["sel"] == sel_tw, (res["sel"], sel_tw)
         assert res["W"].tolist() == W_tw
         np.testing.assert_allclose(res["out"], np.array(out_tw), rtol=1e-9, atol=1e-12)
+
+
+def check_per_q_head_is_repeated_kv(seed=7):
+    """Selecting per query head equals selecting per KV head on a cache whose
+    KV heads are repeated once per query head (group size 1): same span
+    scores, selections, windows and outputs."""
+    rng = np.random.default_rng(seed)
+    for (n_q, bq, Hq, Hkv, d, T, G, S, k, L, kind) in [
+            (1, 1, 4, 2, 8, 70, 3, 4, 5, 6, "bf16"),
+            (4, 2, 6, 2, 8, 61, 2, 3, 4, 9, "int"),
+            (1, 1, 3, 1, 4, 40, 1, 1, 9, 4, "f32")]:
+        q, K, V = rand_problem(rng, n_q, Hq, Hkv, d, T, kind)
+        g = Hq // Hkv
+        Kr, Vr = np.repeat(K, g, axis=0), np.repeat(V, g, axis=0)
+        a = O.step(q, K, V, G, S, k, L, bq, return_all=True, per_q_head=True)
+        b = O.step(q, Kr, Vr, G, S, k, L, bq, return_all=True)
+        assert a["sel"] == b["sel"]
+        assert np.array_equal(a["W"], b["W"]) and np.array_equal(a["qpos"], b["qpos"])
+        np.testing.assert_array_equal(a["out"], b["out"])
+        _, sa = O.score_select(q, K, G, S, k, L, bq, return_scores=True, per_q_head=True)
+        _, sb = O.score_select(q, Kr, G, S, k, L, bq, return_scores=True)
+        np.testing.assert_array_equal(sa, sb)
 
 
 def check_needle(seed=5):
@@ -219,7 +252,7 @@ def check_rope():
 
 
 PINS = [check_golden, check_full_attention, check_k0, check_bruteforce,
-        check_scalar_twin, check_needle, check_rope]
+        check_scalar_twin, check_needle, check_rope, check_per_q_head_is_repeated_kv]
 
 
 # --------------------------------------------------------------------------
@@ -292,13 +325,16 @@ def test_exact_score_fast_path_matches_fractions():
         q, K, V = rand_problem(rng, 3, 4, 2, 8, 40, kind)
         for h in range(2):
             for span in [(3, 9), (10, 11), (20, 40)]:
-                fast = O.exact_span_score(q, K[h], h, 2, span)
-                slow = O._exact_span_score_fractions(q, K[h], h, 2, span)
+                fast = O.exact_span_score(q, K[h], [2 * h, 2 * h + 1], span)
+                slow = O._exact_span_score_fractions(q, K[h], [2 * h, 2 * h + 1], span)
+                assert fast == slow, (kind, h, span)
+                fast = O.exact_span_score(q, K[h], [2 * h + 1], span)
+                slow = O._exact_span_score_fractions(q, K[h], [2 * h + 1], span)
                 assert fast == slow, (kind, h, span)
     # spread of 2^80 between terms: fp64 cannot hold the sum, Fractions must be used
     q = np.array([[[1.0, 1.0]]])
     K = np.array([[2.0 ** 40, 2.0 ** -40]])
-    assert O.exact_span_score(q, K, 0, 1, (0, 1)) == Fraction(2 ** 40) + Fraction(1, 2 ** 40)
+    assert O.exact_span_score(q, K, [0], (0, 1)) == Fraction(2 ** 40) + Fraction(1, 2 ** 40)
     assert O._lsb_exponent(np.array([0.75, 3.0, 0.0])) == -2
 
 
@@ -322,14 +358,30 @@ _orig_regions = O.regions
 _orig_span_list = O.span_list
 
 
-def _mut_first_head(q_blk, K_h, h, g, lo, hi):
-    return q_blk[:, h * g, :] @ K_h[lo:hi].T
+_orig_units = O.selection_units
 
 
-def _mut_wrong_head(q_blk, K_h, h, g, lo, hi):
-    Hq = q_blk.shape[1]
-    h2 = (h + 1) % (Hq // g)
-    return _orig_token_scores(q_blk, K_h, h2, g, lo, hi)
+def _mut_first_head(q_blk, K_h, qheads, lo, hi):
+    return q_blk[:, qheads[0], :] @ K_h[lo:hi].T
+
+
+def _mut_wrong_head(q_blk, K_h, qheads, lo, hi):
+    Hq, m = q_blk.shape[1], len(qheads)
+    return _orig_token_scores(q_blk, K_h, [(hq + m) % Hq for hq in qheads], lo, hi)
+
+
+def _mut_per_head_kv_modulo(Hq, Hkv, per_q_head=False):
+    if per_q_head:
+        return [(hq % Hkv, [hq]) for hq in range(Hq)]
+    return _orig_units(Hq, Hkv, per_q_head)
+
+
+def _mut_per_head_sums_group(Hq, Hkv, per_q_head=False):
+    units = _orig_units(Hq, Hkv, False)
+    if per_q_head:
+        g = Hq // Hkv
+        return [units[hq // g] for hq in range(Hq)]
+    return units
 
 
 def _mut_tie_high(sigma, k, exact_fn=None):
@@ -386,6 +438,8 @@ MUTATIONS = {
     "block_max_of_sums": ("span_scores_from_tokens", _mut_span_max_of_sum),
     "gqa_first_head_only": ("token_scores", _mut_first_head),
     "gqa_wrong_group": ("token_scores", _mut_wrong_head),
+    "per_q_head_kv_by_modulo": ("selection_units", _mut_per_head_kv_modulo),
+    "per_q_head_scores_whole_group": ("selection_units", _mut_per_head_sums_group),
     "ties_to_higher_index": ("select_topk", _mut_tie_high),
     "spans_in_score_order": ("select_topk", _mut_unsorted),
     "rope_sign_flip": ("rope", _mut_rope_sign),
