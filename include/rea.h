@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define REA_ABI_VERSION 1
+#define REA_ABI_VERSION 2
 
 typedef enum rea_status {
     REA_OK = 0,
@@ -99,7 +99,18 @@ typedef struct rea_problem {
  * L [OpenReview discussion, hyperparameter list of the NIAH reply: global 32,
  * seg_size 32, num_seg 127, local 4096 on LLaMA3-8B-8K], and the number of
  * consecutive queries that share one selection (1 when decoding; a prefill
- * chunk is cut into blocks of block_q queries).
+ * chunk is cut into blocks of block_q queries).  S = 1 is token-level
+ * selection, the granularity of the discussion's pseudocode (topk over the
+ * middle keys' scores).
+ *
+ * Selection heads (select_per_q_head): 0 selects once per KV head, scoring
+ * with the summed logits of the query heads of its group; 1 selects once per
+ * query head with its own logits against its group's KV head (the
+ * discussion's reply on eviction: selection is redone for each attention
+ * head).  H_sel = n_kv_heads or n_q_heads accordingly; every [..][H_sel][..]
+ * array below is indexed by selection head, and selection head u serves query
+ * heads [u * Hq / H_sel, (u + 1) * Hq / H_sel) and reads KV head
+ * u * n_kv_heads / H_sel.
  *
  * Regions: G' = min(G, T), L' = min(L, T - G'), middle = [G', T - L').
  * Precondition: n_q <= L', or the middle is empty (T <= G + L).
@@ -113,18 +124,19 @@ typedef struct rea_params {
     int32_t block_q;           /* >= 1, divides n_q */
     double rope_theta;         /* > 0 */
     float softmax_scale;       /* <= 0 selects 1/sqrt(head_dim) */
-    int32_t reserved;          /* must be 0 */
+    int32_t select_per_q_head; /* 0 (one selection per KV head) or 1 (per query head) */
 } rea_params;
 
 /* Derived sizes and the workspace each entry point needs. */
 typedef struct rea_sizes {
     int64_t n_blocks;          /* n_q / block_q */
     int64_t n_spans;           /* ceil((T - L' - G') / S) */
-    int64_t k_sel;             /* min(topk, n_spans): spans selected per (block, KV head) */
+    int64_t k_sel;             /* min(topk, n_spans): spans selected per (block, H_sel head) */
     int64_t W_cap;             /* min(T, G' + k_sel*S + L'): the largest possible window */
     size_t ws_score_select;    /* bytes of workspace rea_score_select needs */
     size_t ws_window_attend;   /* bytes of workspace rea_window_attend needs */
     size_t ws_decode_step;     /* bytes of workspace rea_decode_step needs */
+    int64_t n_sel_heads;       /* H_sel: n_kv_heads, or n_q_heads with select_per_q_head */
 } rea_sizes;
 
 /* Optional timing hooks: hipEvent_t handles (as void*) that rea_decode_step
@@ -146,12 +158,12 @@ rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes 
 /*
  * Step 1: position-agnostic span scoring and top-k selection.
  *
- * sel          [n_blocks][n_kv_heads][topk] int32: for block b and KV head h
+ * sel          [n_blocks][H_sel][topk] int32: for block b and selection head h
  *              the selected span indices (span j covers middle tokens
  *              [G' + j*S, min(G' + (j+1)*S, T - L'))), strictly ascending,
  *              padded with -1 after n_sel entries.  May be NULL if topk == 0.
- * n_sel        [n_blocks][n_kv_heads] int32 = k_sel.
- * span_scores  NULL, or [n_blocks][n_kv_heads][n_spans] double: sum over the
+ * n_sel        [n_blocks][H_sel] int32 = k_sel.
+ * span_scores  NULL, or [n_blocks][H_sel][n_spans] double: sum over the
  *              block's queries of the span's maximum token score.  Exact for
  *              bf16/fp32 inputs except on the MFMA path (bf16, head_dim 128,
  *              block_q 64, S a multiple of 32, at most 4096 spans), where they
@@ -169,13 +181,13 @@ rea_status rea_score_select(const rea_problem *p, const rea_params *a,
  * Steps 2-3: gather the window and apply RoPE at window positions.
  *
  * sel, n_sel   as produced by rea_score_select (device).
- * k_win        [n_blocks][n_kv_heads][W_cap][head_dim] float32: row w of the
+ * k_win        [n_blocks][H_sel][W_cap][head_dim] float32: row w of the
  *              window key, rotated to position w (rows >= W untouched).
- * v_win        [n_blocks][n_kv_heads][W_cap][head_dim], problem dtype: the
+ * v_win        [n_blocks][H_sel][W_cap][head_dim], problem dtype: the
  *              window value rows, bit-exact copies of the cache rows.
  * q_rot        [n_q][n_q_heads][head_dim] float32: each query rotated to the
  *              window position of its own key, W - n_q + (query index in q).
- * W            [n_blocks][n_kv_heads] int32 window lengths.
+ * W            [n_blocks][H_sel] int32 window lengths.
  * W_cap        row capacity of k_win/v_win; must be >= sizes.W_cap.
  */
 rea_status rea_gather_rope(const rea_problem *p, const rea_params *a,

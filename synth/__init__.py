@@ -232,12 +232,23 @@ class Workload:
     kv_scaled: bool = False   # per-channel scale U(0.5, 2) on K and V
     needle_noise: float = 0.1
     rope_theta: float = 500000.0
+    per_q_head: bool = False  # one selection per query head instead of per KV head
     extra: dict = field(default_factory=dict)
 
     # -- derived sizes ---------------------------------------------------
     @property
     def g(self) -> int:
         return self.Hq // self.Hkv
+
+    @property
+    def H_sel(self) -> int:
+        """Selection heads: the KV heads, or the query heads when each selects."""
+        return self.Hq if self.per_q_head else self.Hkv
+
+    @property
+    def g_sel(self) -> int:
+        """Query heads served by one selection head."""
+        return 1 if self.per_q_head else self.g
 
     @property
     def mid(self):
@@ -369,7 +380,8 @@ def config(i: int) -> Workload:
 
 
 def small(name="small", seed=7, dtype="bf16", Hq=4, Hkv=2, d=64, T=700, n_q=1, block_q=1,
-          G=4, S=16, topk=5, L=64, needles=1, kv_scaled=False, layers=1) -> Workload:
+          G=4, S=16, topk=5, L=64, needles=1, kv_scaled=False, layers=1,
+          per_q_head=False) -> Workload:
     """A shrunken workload with the same recipe, for quick tests."""
     return Workload(name, seed, dtype, layers, Hq, Hkv, d, T, n_q, block_q, G, S, topk, L,
-                    needles=needles, kv_scaled=kv_scaled)
+                    needles=needles, kv_scaled=kv_scaled, per_q_head=per_q_head)

@@ -25,7 +25,8 @@ def device_inputs(w, layer=0, q=None, K=None, V=None):
 
 def run_library(w, q, K, V, components=True):
     """All four entry points on the device; results copied to host numpy."""
-    st = rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta)
+    st = rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta,
+                  per_q_head=w.per_q_head)
     res = {"sizes": st.sizes}
     if components:
         sel, nsel, sc = st.score_select(span_scores=True)
@@ -33,9 +34,10 @@ def run_library(w, q, K, V, components=True):
         out = st.window_attend(q_rot, k_win, v_win, W)
         res.update(sel=sel, nsel=nsel, sc=sc, k_win=k_win, v_win=v_win, q_rot=q_rot, W=W,
                    out=out)
-    Hkv, nb = w.Hkv, st.sizes.n_blocks
-    sel2 = torch.full((nb, Hkv, max(w.topk, 1)), -7, dtype=torch.int32, device=q.device)
-    nsel2 = torch.empty((nb, Hkv), dtype=torch.int32, device=q.device)
+    Hs, nb = st.sizes.n_sel_heads, st.sizes.n_blocks
+    assert Hs == w.H_sel
+    sel2 = torch.full((nb, Hs, max(w.topk, 1)), -7, dtype=torch.int32, device=q.device)
+    nsel2 = torch.empty((nb, Hs), dtype=torch.int32, device=q.device)
     res["out_step"] = st.decode_step(sel=sel2 if w.topk > 0 else None, nsel=nsel2)
     res["sel_step"], res["nsel_step"] = sel2[:, :, :w.topk], nsel2
     torch.cuda.synchronize()
@@ -52,21 +54,27 @@ def run_library(w, q, K, V, components=True):
 
 
 def oracle_head(w, layer, h, q64=None, K_h=None, V_h=None):
-    """Oracle steps for KV head h alone (heads are independent)."""
+    """Oracle steps for selection head h alone (KV heads are independent): KV
+    head h with its query group, or, when each query head selects, query head h
+    within its KV head's group (the oracle runs the whole group, per head)."""
     g = w.g
+    hp = h // g if w.per_q_head else h          # KV head
     if q64 is None:
         q64 = synth.to_f32(w.q(layer), w.dtype).astype(np.float64)
-    qh = q64[:, h * g:(h + 1) * g]
+    qh = q64[:, hp * g:(hp + 1) * g]
     if K_h is None:
-        K_h = synth.to_f32(w.kv(layer, "k", h, h + 1), w.dtype).astype(np.float64)
+        K_h = synth.to_f32(w.kv(layer, "k", hp, hp + 1), w.dtype).astype(np.float64)
     if V_h is None:
-        V_h = synth.to_f32(w.kv(layer, "v", h, h + 1), w.dtype).astype(np.float64)
-    sel, sc = O.score_select(qh, K_h, w.G, w.S, w.topk, w.L, w.block_q, return_scores=True)
+        V_h = synth.to_f32(w.kv(layer, "v", hp, hp + 1), w.dtype).astype(np.float64)
+    sel, sc = O.score_select(qh, K_h, w.G, w.S, w.topk, w.L, w.block_q, return_scores=True,
+                             per_q_head=w.per_q_head)
     Kw, Vw, qr, W, qpos = O.gather_rope(qh, K_h, V_h, sel, w.G, w.S, w.L, w.block_q,
-                                        w.rope_theta)
+                                        w.rope_theta, per_q_head=w.per_q_head)
     out = O.window_attend(qr, Kw, Vw, qpos, w.block_q)
-    return dict(sel=[s[0] for s in sel], sc=sc[:, 0], Kw=[k[0] for k in Kw],
-                Vw=[v[0] for v in Vw], q_rot=qr, W=W[:, 0], out=out)
+    u = h - hp * g if w.per_q_head else 0       # unit within the group's result
+    cols = slice(u, u + 1) if w.per_q_head else slice(0, g)
+    return dict(sel=[s[u] for s in sel], sc=sc[:, u], Kw=[k[u] for k in Kw],
+                Vw=[v[u] for v in Vw], q_rot=qr[:, cols], W=W[:, u], out=out[:, cols])
 
 
 def mfma_path(w):
@@ -80,13 +88,14 @@ def fused_path(w):
     """rea_decode_step runs steps 2-4 fused, reading the window straight from
     the cache: up to 8 query rows per (block, KV head) on the VALU, or bf16
     d 128 blocks of >= 32 query rows on MFMA."""
-    mfma_cache = w.dtype == "bf16" and w.d == 128 and w.block_q * w.g >= 32 and w.topk <= 4096
-    return w.block_q * w.g <= 8 or mfma_cache
+    rows = w.block_q * w.g_sel
+    mfma_cache = w.dtype == "bf16" and w.d == 128 and rows >= 32 and w.topk <= 4096
+    return rows <= 8 or mfma_cache
 
 
 def compare_head(w, gpu, ora, h, check_windows=True):
-    """Assert parity of KV head h; returns the max-abs output error."""
-    g, nb = w.g, len(ora["sel"])
+    """Assert parity of selection head h; returns the max-abs output error."""
+    g, nb = w.g_sel, len(ora["sel"])
     for b in range(nb):
         exp = ora["sel"][b]
         ns = int(gpu["nsel"][b, h])

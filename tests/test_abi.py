@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert sorted(rea.ENTRY_POINTS) == syms
-    assert L.rea_abi_version() == 1
+    assert L.rea_abi_version() == 2
     for i, name in enumerate(rea.STATUS):
         assert L.rea_status_string(i).decode() == name
 
@@ -79,7 +79,7 @@ def mutate(**kw):
     (dict(G=-1), rea.STATUS.index("REA_EINVAL")),
     (dict(L=-5), rea.STATUS.index("REA_EINVAL")),
     (dict(block_q=0), rea.STATUS.index("REA_EINVAL")),
-    (dict(reserved=3), rea.STATUS.index("REA_EINVAL")),
+    (dict(select_per_q_head=3), rea.STATUS.index("REA_EINVAL")),
     (dict(rope_theta=0.0), rea.STATUS.index("REA_EINVAL")),
     (dict(rope_theta=float("inf")), rea.STATUS.index("REA_EINVAL")),
     (dict(softmax_scale=float("nan")), rea.STATUS.index("REA_EINVAL")),
@@ -159,3 +159,18 @@ def test_valid_call_without_gpu_reports_no_device():
     st = L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE,
                            s.ws_decode_step, None, None)
     assert st == rea.STATUS.index("REA_ENODEVICE"), L.rea_last_error()
+
+
+def test_sizes_per_query_head_selection():
+    p, a = good()
+    st, s = sizes_status(p, a)
+    assert st == 0 and s.n_sel_heads == 8
+    a.select_per_q_head = 1
+    st, s2 = sizes_status(p, a)
+    assert st == 0, rea.lib().rea_last_error()
+    assert s2.n_sel_heads == 32 and s2.n_spans == s.n_spans and s2.W_cap == s.W_cap
+    assert s2.ws_decode_step > s.ws_decode_step      # four times the span scores
+    # token level: spans of one token
+    a.S, a.topk = 1, 3840
+    st, s3 = sizes_status(p, a)
+    assert st == 0 and s3.n_spans == 131072 - 32 - 4096 and s3.W_cap == 32 + 3840 + 4096

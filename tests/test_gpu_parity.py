@@ -2,6 +2,8 @@
 same seeded inputs.  Selection must match exactly, window lengths and value
 rows bit-exactly, rotated rows to fp32 rounding, outputs within the stated
 max-abs tolerance (2e-2 for bf16 inputs, 1e-5 for fp32)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -50,6 +52,19 @@ SMALL = {
                                L=100, needles=0, kv_scaled=True),
     "bf16_mfma_5_blocks_g1": S(Hq=2, Hkv=2, d=128, T=2500, n_q=320, block_q=64, S=32, topk=7,
                                L=400, needles=0),
+    # one selection per query head
+    "pqh_bf16_g4_d128": S(Hq=8, Hkv=2, d=128, T=2048, S=32, topk=12, L=256, needles=2,
+                          kv_scaled=True, per_q_head=True),
+    "pqh_f32_g2_partial": S(dtype="f32", per_q_head=True),
+    "pqh_bf16_g3_S16": S(Hq=6, Hkv=2, d=128, T=1500, S=16, topk=9, L=100, per_q_head=True),
+    "pqh_bf16_g8_d64": S(Hq=8, Hkv=1, d=64, T=1800, S=32, topk=10, L=128, per_q_head=True),
+    "pqh_bf16_g5_generic": S(Hq=10, Hkv=2, d=64, T=900, S=16, topk=6, L=64, per_q_head=True),
+    "pqh_bf16_token_level": S(S=1, topk=40, T=400, per_q_head=True),
+    "pqh_bf16_prefill_blocks": S(Hq=8, Hkv=2, d=128, T=600, n_q=8, block_q=4, S=16, topk=6,
+                                 L=64, needles=0, per_q_head=True),
+    "pqh_bf16_mfma_blocks": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,
+                              L=128, needles=0, per_q_head=True),
+    "f32_token_level_S1_g1": S(dtype="f32", Hq=2, Hkv=2, d=128, S=1, topk=100, T=1200, L=50),
 }
 
 
@@ -60,7 +75,7 @@ def test_small(name):
         f"n_q={w.n_q} bq={w.block_q} {w.dtype}")
     q, K, V = device_inputs(w)
     gpu = run_library(w, q, K, V)
-    errs = [compare_head(w, gpu, oracle_head(w, 0, h), h) for h in range(w.Hkv)]
+    errs = [compare_head(w, gpu, oracle_head(w, 0, h), h) for h in range(w.H_sel)]
     log(f"  max-abs out err {max(errs):.3e}")
 
 
@@ -176,4 +191,29 @@ def test_config_one_layer(cfg):
         errs.append(compare_head(w, gpu, ora, h))
         needles = [j for (hh, j) in w.needle_spans(0) if hh == h]
         assert set(needles) <= set(ora["sel"][0])
+    log(f"  max-abs out err {max(errs):.3e} (tolerance {TOL[w.dtype]})")
+
+
+VARIANTS = {
+    # the 8B decode at 131072 tokens with one selection per query head
+    "per_q_head": dict(per_q_head=True),
+    # token-level selection: spans of one token, the same 3840-token budget
+    "token_level": dict(S=1, topk=3840),
+}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_config2_variant(variant):
+    w = dataclasses.replace(synth.config(2), **VARIANTS[variant])
+    w.name = f"{w.name}-{variant}"
+    log(f"[variant] {w.name}: S={w.S} k={w.topk} per_q_head={w.per_q_head}")
+    q, K, V = device_inputs(w)
+    gpu = run_library(w, q, K, V)
+    del K, V
+    torch.cuda.empty_cache()
+    q64 = synth.to_f32(w.q(0), w.dtype).astype(np.float64)
+    errs = []
+    for h in range(w.H_sel):
+        ora = oracle_head(w, 0, h, q64)
+        errs.append(compare_head(w, gpu, ora, h))
     log(f"  max-abs out err {max(errs):.3e} (tolerance {TOL[w.dtype]})")

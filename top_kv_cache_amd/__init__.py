@@ -35,14 +35,14 @@ class Params(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("G", ctypes.c_int32), ("S", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("L", ctypes.c_int32), ("block_q", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("select_per_q_head", ctypes.c_int32)]
 
 
 class Sizes(ctypes.Structure):
     _fields_ = [("n_blocks", ctypes.c_int64), ("n_spans", ctypes.c_int64),
                 ("k_sel", ctypes.c_int64), ("W_cap", ctypes.c_int64),
                 ("ws_score_select", ctypes.c_size_t), ("ws_window_attend", ctypes.c_size_t),
-                ("ws_decode_step", ctypes.c_size_t)]
+                ("ws_decode_step", ctypes.c_size_t), ("n_sel_heads", ctypes.c_int64)]
 
 
 class Timing(ctypes.Structure):
@@ -95,7 +95,7 @@ def lib():
                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
     L.rea_prefill.restype = ctypes.c_int
     L.rea_prefill.argtypes = [P, A, ctypes.c_int32, vp, vp, ctypes.c_size_t, vp]
-    if L.rea_abi_version() != 1:
+    if L.rea_abi_version() != 2:
         raise ImportError("librea.so ABI version mismatch")
     _lib = L
     return L
@@ -114,8 +114,10 @@ def problem(q_ptr, k_ptr, v_ptr, *, dtype, n_q, Hq, Hkv, d, T, stride_head, stri
                    stride_head, stride_tok)
 
 
-def params(G, S, topk, L, block_q=1, rope_theta=500000.0, softmax_scale=0.0) -> Params:
-    return Params(ctypes.sizeof(Params), G, S, topk, L, block_q, rope_theta, softmax_scale, 0)
+def params(G, S, topk, L, block_q=1, rope_theta=500000.0, softmax_scale=0.0,
+           per_q_head=False) -> Params:
+    return Params(ctypes.sizeof(Params), G, S, topk, L, block_q, rope_theta, softmax_scale,
+                  1 if per_q_head else 0)
 
 
 def prefill_plan(p: Problem, a: Params, chunk: int):
@@ -190,17 +192,19 @@ class Step:
     """One layer's call configuration: problem + hyperparameters + sizes."""
 
     def __init__(self, q, k, v, G, S, topk, L, block_q=1, T=None, rope_theta=500000.0,
-                 softmax_scale=0.0):
+                 softmax_scale=0.0, per_q_head=False):
         self.q, self.k, self.v = q, k, v
         self.prob = problem_from_tensors(q, k, v, T)
-        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale)
+        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale, per_q_head)
         self.sizes = query_sizes(self.prob, self.par)
         self.device = q.device
 
     @property
     def shape(self):
+        """(n_q, Hq, selection heads, d): the selection heads are the KV heads,
+        or the query heads when each query head selects."""
         p = self.prob
-        return p.n_q, p.n_q_heads, p.n_kv_heads, p.head_dim
+        return p.n_q, p.n_q_heads, self.sizes.n_sel_heads, p.head_dim
 
     def score_select(self, span_scores=False, stream=None):
         torch = _torch()
@@ -267,10 +271,10 @@ class Prefill:
     query) against the cache k, v of the same T tokens."""
 
     def __init__(self, q, k, v, G, S, topk, L, block_q, chunk, rope_theta=500000.0,
-                 softmax_scale=0.0):
+                 softmax_scale=0.0, per_q_head=False):
         self.q, self.k, self.v = q, k, v
         self.prob = problem_from_tensors(q, k, v)
-        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale)
+        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale, per_q_head)
         self.chunk = chunk
         self.plan, self.ws_bytes = prefill_plan(self.prob, self.par, chunk)
         self.device = q.device

@@ -64,7 +64,7 @@ struct MAttnArgs {
     // both
     float *out;             // [n_q][Hq][D]
     int64_t W_cap;
-    int QR, Hq, Hkv, g, n_q, block_q, n_rg;
+    int QR, Hq, Hkv, g, n_q, block_q, n_rg, rep;
     float scale_log2;       // softmax scale * log2(e)
 };
 
@@ -190,8 +190,8 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
     const int vkey = tid & 31, vch = (tid >> 5) * 8;
     const float *kwb = a.k_win + (int64_t)bh * a.W_cap * kD;
     const uint16_t *vwb = a.v_win + (int64_t)bh * a.W_cap * kD;
-    const uint16_t *kcb = a.k + (int64_t)h * a.sh;
-    const uint16_t *vcb = a.v + (int64_t)h * a.sh;
+    const uint16_t *kcb = a.k + (int64_t)(h / a.rep) * a.sh;
+    const uint16_t *vcb = a.v + (int64_t)(h / a.rep) * a.sh;
     float4 kr[2];               // window: 8 fp32 keys; cache: 4 x (cos, sin)
     uint4 vr;
     uint2 kc[2];
@@ -443,6 +443,7 @@ hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_
     a.Hq = g.Hq;
     a.Hkv = g.Hkv;
     a.g = g.g;
+    a.rep = g.rep;
     a.n_q = g.n_q;
     a.block_q = g.block_q;
     a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
@@ -488,6 +489,7 @@ hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k,
     a.Hq = g.Hq;
     a.Hkv = g.Hkv;
     a.g = g.g;
+    a.rep = g.rep;
     a.n_q = g.n_q;
     a.block_q = g.block_q;
     a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;

@@ -53,7 +53,7 @@ struct FusedArgs {
     float *out;             // [n_q][Hq][D]
     int64_t sh, st;         // elements
     int64_t T, Gp, Lp, mid_lo, n_spans;
-    int S, last_len, topk, Hkv, Hq, g, n_q, block_q, QR, n_split;
+    int S, last_len, topk, Hkv, Hq, g, n_q, block_q, QR, n_split, rep;
     float scale_log2;       // softmax scale * log2(e): logits in log2 units
     double frev_hi[kMaxHalfDim], frev_lo[kMaxHalfDim];   // theta_c / 2pi as hi + lo
     double step_c[kMaxHalfDim], step_s[kMaxHalfDim];     // cos, sin of theta_c
@@ -209,8 +209,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     const int64_t wf = w0 + wave * (4 * kSL) + rho * kSL;
     Part<TIn, PPL> k1[kSL], k2[kSL], v1[kSL], v2[kSL];
     {
-        const TIn *kb = (const TIn *)a.k + (int64_t)h * a.sh;
-        const TIn *vb = (const TIn *)a.v + (int64_t)h * a.sh;
+        const TIn *kb = (const TIn *)a.k + (int64_t)(h / a.rep) * a.sh;
+        const TIn *vb = (const TIn *)a.v + (int64_t)(h / a.rep) * a.sh;
         const int64_t o0 = wf - a.Gp;
         const uint32_t oc = (uint32_t)(o0 > 0 ? o0 : 0);
         int oq = (int)(oc / (uint32_t)a.S), orr = (int)(oc - (uint32_t)oq * (uint32_t)a.S);
@@ -502,6 +502,7 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
     a.Hkv = g.Hkv;
     a.Hq = g.Hq;
     a.g = g.g;
+    a.rep = g.rep;
     a.n_q = g.n_q;
     a.block_q = g.block_q;
     a.QR = g.block_q * g.g;

@@ -56,7 +56,8 @@ rea_status make_geom(const rea_problem *p, const rea_params *a, rea::Geom *g) {
     if (a->S < 1) return fail(REA_EINVAL, "span size S %d < 1", a->S);
     if (a->topk < 0) return fail(REA_EINVAL, "topk %d < 0", a->topk);
     if (a->block_q < 1) return fail(REA_EINVAL, "block_q %d < 1", a->block_q);
-    if (a->reserved != 0) return fail(REA_EINVAL, "rea_params.reserved must be 0");
+    if (a->select_per_q_head != 0 && a->select_per_q_head != 1)
+        return fail(REA_EINVAL, "select_per_q_head %d is neither 0 nor 1", a->select_per_q_head);
     if (!(a->rope_theta > 0.0) || !isfinite(a->rope_theta))
         return fail(REA_EINVAL, "rope_theta must be finite and > 0");
     if (!isfinite(a->softmax_scale)) return fail(REA_EINVAL, "softmax_scale is not finite");
@@ -79,8 +80,15 @@ rea_status make_geom(const rea_problem *p, const rea_params *a, rea::Geom *g) {
     g->esize = esize;
     g->n_q = p->n_q;
     g->Hq = p->n_q_heads;
-    g->Hkv = p->n_kv_heads;
-    g->g = p->n_q_heads / p->n_kv_heads;
+    if (a->select_per_q_head) {     // every query head is its own selection head
+        g->Hkv = p->n_q_heads;
+        g->g = 1;
+        g->rep = p->n_q_heads / p->n_kv_heads;
+    } else {
+        g->Hkv = p->n_kv_heads;
+        g->g = p->n_q_heads / p->n_kv_heads;
+        g->rep = 1;
+    }
     g->d = p->head_dim;
     g->T = p->T;
     g->Gp = a->G < p->T ? a->G : p->T;
@@ -267,6 +275,7 @@ rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes 
     out->ws_score_select = score_ws_bytes(g, false);
     out->ws_window_attend = rea::attend_ws_bytes(g, g.W_cap);
     out->ws_decode_step = decode_ws_bytes(g);
+    out->n_sel_heads = g.Hkv;
     return REA_OK;
 }
 

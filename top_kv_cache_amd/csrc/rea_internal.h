@@ -11,7 +11,10 @@ namespace rea {
 struct Geom {
     int dtype;          // 0 bf16, 1 f32
     int esize;          // bytes per stored element
-    int n_q, Hq, Hkv, g, d;
+    int n_q, Hq, d;
+    int Hkv;            // selection heads: the KV heads, or the query heads when each selects
+    int g;              // query heads per selection head (1 when each query head selects)
+    int rep;            // selection heads per cache head: selection head h reads KV head h / rep
     int64_t T;
     int64_t Gp, Lp;     // G' = min(G,T), L' = min(L, T-G')
     int64_t mid_lo, mid_hi;

@@ -44,7 +44,7 @@ struct ScoreArgs {
     double *gmax;               // [n_blk][Hkv][n_groups]
     int64_t sh_bytes, st_bytes;
     int64_t mid_lo, mid_hi, n_spans, n_groups;
-    int S, Hq, Hkv, g, block_q, P;
+    int S, Hq, Hkv, g, block_q, P, rep;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
         }
     }
 
-    const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes + ch * 16;
+    const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes + ch * 16;
     const GroupRange gr = group_range(a, p);
     for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
         const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
@@ -183,6 +183,90 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
     }
 }
 
+// Decode with one selection per query head: the NH query heads of a group
+// share their KV head, so each key row is loaded once and scored against all
+// NH queries (NH dot products per row).  The workgroup covers KV head hp; its
+// selection heads are hp*NH .. hp*NH+NH-1 (rep == NH, g == 1).
+template <typename TIn, int D, int R, int NH>
+__global__ __launch_bounds__(kThreads) void k_score_decode_heads(ScoreArgs a) {
+    constexpr int ESZ = sizeof(TIn);
+    constexpr int LPR = D * ESZ / 16;
+    constexpr int RPI = 64 / LPR;
+    constexpr int EPL = 16 / ESZ;
+    __shared__ double slot[2][NH][kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rs = lane / LPR, ch = lane % LPR;
+    const int Hp = a.Hkv / NH;                   // KV heads
+    const int bp = blockIdx.x / a.P, p = blockIdx.x % a.P;
+    const int b = bp / Hp, hp = bp % Hp;
+    const int64_t bh0 = (int64_t)b * a.Hkv + (int64_t)hp * NH;   // first selection head
+
+    double qr[NH][EPL];
+    {
+        const TIn *qb = (const TIn *)a.q + (int64_t)b * a.Hq * D + (int64_t)hp * NH * D;
+#pragma unroll
+        for (int m = 0; m < NH; ++m)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qr[m][e] = load_f64(qb, (int64_t)m * D + ch * EPL + e);
+    }
+
+    const unsigned char *kh = a.k + (int64_t)hp * a.sh_bytes + ch * 16;
+    const GroupRange gr = group_range(a, p);
+    for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
+        const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
+        double gbest[NH];
+#pragma unroll
+        for (int m = 0; m < NH; ++m) gbest[m] = -INFINITY;
+        for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
+            const int64_t tb = a.mid_lo + j * a.S;
+            const int64_t te = min(tb + (int64_t)a.S, a.mid_hi);
+            double best[NH];
+#pragma unroll
+            for (int m = 0; m < NH; ++m) best[m] = -INFINITY;
+            for (int64_t r0 = tb; r0 < te; r0 += (int64_t)R * RPI) {
+                uint4 buf[R];
+                bool ok[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t t = r0 + r * RPI + rs;
+                    ok[r] = t < te;
+                    buf[r] = ok[r] ? load_nt(kh + t * a.st_bytes) : make_uint4(0u, 0u, 0u, 0u);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    double x[EPL];
+                    unpack(buf[r], x);
+#pragma unroll
+                    for (int m = 0; m < NH; ++m) {
+                        double acc = 0.0;
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc = fma(qr[m][e], x[e], acc);
+                        acc = row_sum<LPR>(acc);
+                        if (ok[r]) best[m] = fmax(best[m], acc);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NH; ++m) {
+                const double v = rows_max<LPR>(best[m]) + 0.0;       // -0 -> +0
+                if (lane == 0) a.out[(bh0 + m) * a.n_spans + j] = v;
+                gbest[m] = fmax(gbest[m], v);
+            }
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int m = 0; m < NH; ++m) slot[grp & 1][m][wave] = gbest[m];
+        }
+        __syncthreads();
+        if (threadIdx.x < NH) {
+            const int m = threadIdx.x;
+            double v = slot[grp & 1][m][0];
+            for (int w = 1; w < kWaves; ++w) v = fmax(v, slot[grp & 1][m][w]);
+            a.gmax[(bh0 + m) * a.n_groups + grp] = v;
+        }
+    }
+}
+
 // Blocks of several queries (chunked prefill on the VALU): the group-summed
 // queries of the block sit in LDS; span score = sum over queries of the max.
 template <typename TIn, int D>
@@ -208,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_score_block(ScoreArgs a) {
     }
     __syncthreads();
 
-    const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes + ch * 16;
+    const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes + ch * 16;
     const GroupRange gr = group_range(a, p);
     for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
         const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
@@ -248,9 +332,36 @@ void launch_decode(const ScoreArgs &a, int nblocks, hipStream_t s) {
     hipLaunchKernelGGL((k_score_decode<TIn, D, R>), dim3(nblocks), dim3(kThreads), 0, s, a);
 }
 
+template <typename TIn, int D, int NH>
+void launch_heads(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
+    constexpr int RPI = 64 / (D * (int)sizeof(TIn) / 16);
+    const int per_span = (g.S + RPI - 1) / RPI;
+    if (per_span >= 4)
+        hipLaunchKernelGGL((k_score_decode_heads<TIn, D, 4, NH>), dim3(nblocks), dim3(kThreads),
+                           0, s, a);
+    else if (per_span >= 2)
+        hipLaunchKernelGGL((k_score_decode_heads<TIn, D, 2, NH>), dim3(nblocks), dim3(kThreads),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((k_score_decode_heads<TIn, D, 1, NH>), dim3(nblocks), dim3(kThreads),
+                           0, s, a);
+}
+
+// Query heads per KV head that one multi-head decode workgroup scores
+// together (0: score each selection head on its own, reading its KV head).
+int multi_heads(const Geom &g) {
+    if (g.block_q != 1 || g.rep < 2) return 0;
+    return (g.rep == 2 || g.rep == 3 || g.rep == 4 || g.rep == 8) ? g.rep : 0;
+}
+
 template <typename TIn, int D>
 hipError_t launch_typed(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
-    if (g.block_q == 1) {
+    if (const int nh = multi_heads(g)) {
+        if (nh == 2) launch_heads<TIn, D, 2>(g, a, nblocks, s);
+        else if (nh == 3) launch_heads<TIn, D, 3>(g, a, nblocks, s);
+        else if (nh == 4) launch_heads<TIn, D, 4>(g, a, nblocks, s);
+        else launch_heads<TIn, D, 8>(g, a, nblocks, s);
+    } else if (g.block_q == 1) {
         constexpr int RPI = 64 / (D * (int)sizeof(TIn) / 16);
         const int per_span = (g.S + RPI - 1) / RPI;       // load instructions per span
         if (per_span >= 8)
@@ -291,7 +402,11 @@ hipError_t launch_score(const Geom &g, const void *q, const void *k, double *spa
     a.Hkv = g.Hkv;
     a.g = g.g;
     a.block_q = g.block_q;
-    const int64_t units = (int64_t)g.n_blk * g.Hkv;
+    a.rep = g.rep;
+    // one workgroup column per (block, KV head); a multi-head decode covers the
+    // rep selection heads of a KV head together
+    const int nh = multi_heads(g);
+    const int64_t units = (int64_t)g.n_blk * (nh ? g.Hkv / nh : g.Hkv);
     const int64_t target = (int64_t)(num_cu > 0 ? num_cu : 256) * 2;
     int64_t P = (target + units - 1) / units;
     if (P > a.n_groups) P = a.n_groups;

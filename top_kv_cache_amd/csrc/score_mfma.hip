@@ -134,7 +134,7 @@ struct MfmaArgs {
     double *kbar;               // [Hkv][n_spans]
     int64_t sh_bytes, st_bytes;
     int64_t mid_lo, mid_hi, n_spans;
-    int S, Hkv, n_q, n_blk, NR;
+    int S, Hkv, n_q, n_blk, NR, rep;
 };
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *(const uint4 *)p; }
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void k_score_mfma(MfmaArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0xF70);              // fragments in registers before the ring starts
 
-    const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes;
+    const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
     const int n_tiles = (j1 - j0) * tiles_per_span;
     // each wave moves 2 x 1 KB (8 token rows) of every tile; (ij, isub) is the
     // span and sub-tile of the next tile to issue
@@ -411,7 +411,7 @@ struct CertArgs {
     const unsigned char *k;
     int32_t *sel, *nsel;
     int64_t sh_bytes, st_bytes, mid_lo, mid_hi, n_spans;
-    int S, Hkv, n_q, kk, topk;
+    int S, Hkv, n_q, kk, topk, rep;
 };
 
 struct CertShared {
@@ -620,7 +620,7 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
         // maxima over the 32 token lanes come from a transpose-reduce and the
         // 32 maxima are summed; the two query halves are added in order.
         const int tl = lane & 31, sub = lane >> 5;
-        const unsigned char *kh = a.k + (int64_t)h * a.sh_bytes;
+        const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
         for (int qh = 0; qh < 2; ++qh) {
             const double *qsrc = a.qeff + ((int64_t)h * a.n_q + (int64_t)b * kQB + qh * 32) * kD;
             for (int i = tid; i < 32 * kD; i += kCThreads) sh.qblk[i] = qsrc[i];
@@ -780,6 +780,7 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     ma.n_spans = g.n_spans;
     ma.S = g.S;
     ma.Hkv = g.Hkv;
+    ma.rep = g.rep;
     ma.n_q = g.n_q;
     ma.n_blk = g.n_blk;
     const int n_qg = (g.n_blk + kWavesM - 1) / kWavesM;
@@ -811,6 +812,7 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     ca.n_spans = g.n_spans;
     ca.S = g.S;
     ca.Hkv = g.Hkv;
+    ca.rep = g.rep;
     ca.n_q = g.n_q;
     ca.kk = g.k_sel;
     ca.topk = g.topk;

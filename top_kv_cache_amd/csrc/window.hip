@@ -41,7 +41,7 @@ struct GatherArgs {
     int32_t *W;
     int64_t sh, st;         // elements
     int64_t T, Gp, Lp, mid_lo, n_spans, W_cap;
-    int S, last_len, topk, Hkv, Hq, g, n_q, block_q;
+    int S, last_len, topk, Hkv, Hq, g, n_q, block_q, rep;
     double inv_freq[kMaxHalfDim];
 };
 
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_rope(GatherArgs a) {
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
             if (ok[hb]) {
-                const int64_t row = (int64_t)(h0 + hb) * a.sh + src[hb] * a.st;
+                const int64_t row = (int64_t)((h0 + hb) / a.rep) * a.sh + src[hb] * a.st;
                 k1[hb].load(kb + row + c0);
                 k2[hb].load(kb + row + c0 + HALF);
                 v1[hb].load(vb + row + c0);
@@ -246,6 +246,7 @@ hipError_t launch_gather_rope(const Geom &g, const void *k, const void *v, const
     a.g = g.g;
     a.n_q = g.n_q;
     a.block_q = g.block_q;
+    a.rep = g.rep;
     for (int c = 0; c < kMaxHalfDim; ++c)
         a.inv_freq[c] = c < g.d / 2 ? pow(g.theta, -2.0 * (double)c / (double)g.d) : 0.0;
     if (g.dtype == 0)
