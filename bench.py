@@ -14,6 +14,7 @@ cpu_baseline = the CPU oracle on whole layers of the same workload.
 """
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -28,6 +29,13 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_decode_llama8b_1m_traffic.txt")
 SCORE_SRC = os.path.join(ROOT, "top_kv_cache_amd", "csrc", "score.hip")
+
+
+# selection variants of a workload (--variant)
+VARIANTS = {
+    "per_q_head": dict(per_q_head=True),       # one selection per query head
+    "token_level": dict(S=1, topk=3840),       # spans of one token, the same token budget
+}
 
 
 def log(*a):
@@ -97,7 +105,7 @@ def cpu_baseline(w, min_seconds=10.0):
             V = synth.to_f32(w.kv(layer, "v", h, h + 1), w.dtype).astype(np.float64)
             t0 = time.perf_counter()
             O.step(q64[:, h * g:(h + 1) * g], K, V, w.G, w.S, w.topk, w.L, w.block_q,
-                   w.rope_theta)
+                   w.rope_theta, per_q_head=w.per_q_head)
             total += time.perf_counter() - t0
             del K, V
         layers += 1
@@ -169,6 +177,9 @@ def main():
     ap.add_argument("--prefill-prompt", type=int, default=0,
                     help="instead: time a chunked prefill over a prompt of this many tokens")
     ap.add_argument("--chunk", type=int, default=512, help="prefill chunk (with --prefill-prompt)")
+    ap.add_argument("--variant", choices=sorted(VARIANTS), default=None,
+                    help="selection variant of the workload (default: one selection per KV "
+                         "head over spans of S tokens)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -192,6 +203,9 @@ def main():
         sys.exit(1)
     rea.lib()                                   # fails loudly if the library is missing
     w = synth.config(args.config)
+    if args.variant:
+        w = dataclasses.replace(w, **VARIANTS[args.variant])
+        w.name = f"{w.name}-{args.variant.replace('_', '-')}"
     n_layers = args.layers or w.n_layers
     dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: {n_layers} layers, T={w.T}, Hq={w.Hq}, Hkv={w.Hkv}, "
@@ -203,7 +217,8 @@ def main():
         q = torch_io.q_device(w, layer, dev)
         K = torch_io.kv_device(w, layer, "k", device=dev)
         V = torch_io.kv_device(w, layer, "v", device=dev)
-        steps_l.append(rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta))
+        steps_l.append(rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta,
+                                per_q_head=w.per_q_head))
         outs.append(torch.empty((w.n_q, w.Hq, w.d), dtype=torch.float32, device=dev))
         if layer % 4 == 3 or layer == n_layers - 1:
             log(f"[bench] generated + uploaded layer {layer + 1}/{n_layers} "
@@ -261,11 +276,12 @@ def main():
     if w.block_q == 1:
         # decode: the scoring kernel streams the middle keys once
         score_bytes = (keys_per_layer * w.d * (2 if w.dtype == "bf16" else 4)
-                       + w.n_spans * w.Hkv * 8 + w.Hq * w.d * (2 if w.dtype == "bf16" else 4))
+                       + w.n_spans * w.H_sel * 8 + w.Hq * w.d * (2 if w.dtype == "bf16" else 4))
         achieved = score_bytes / (k1_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(score_bytes),
-                    "kernel": "k_score_decode", "algorithmic_bytes_per_launch": score_bytes,
+                    "kernel": "k_score_decode_heads" if w.per_q_head else "k_score_decode",
+                    "algorithmic_bytes_per_launch": score_bytes,
                     "avg_launch_us": k1_ms * 1e3}
         log(f"[bench] scoring kernel {k1_ms * 1e3:.1f} us/launch = {achieved:.0f} GB/s "
             f"({achieved / HBM_PEAK_GBS * 100:.1f}% of {HBM_PEAK_GBS:.0f})")
@@ -296,6 +312,7 @@ def main():
         "config": {"workload": w.name, "layers": n_layers, "context": w.T, "batch": 1,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "storage": w.dtype,
                    "G": w.G, "S": w.S, "topk": w.topk, "L": w.L,
+                   "selection": "per query head" if w.per_q_head else "per KV head",
                    "needles_per_kv_head": w.needles, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": None,

@@ -267,6 +267,85 @@ __global__ __launch_bounds__(kThreads) void k_score_decode_heads(ScoreArgs a) {
     }
 }
 
+// Token-level decode (S = 1: every middle token is its own span).  A wave
+// takes one group of 32 consecutive tokens per step (all its rows loaded
+// before any arithmetic) and writes their 32 scores with one store per
+// selection head; the group maximum needs no exchange between waves.  NH > 1
+// scores the NH query heads of a KV head from one read of each row (one
+// selection per query head); NH == 1 scores selection head u with the summed
+// queries of its group.
+template <typename TIn, int D, int NH>
+__global__ __launch_bounds__(kThreads) void k_score_tokens(ScoreArgs a) {
+    constexpr int ESZ = sizeof(TIn);
+    constexpr int LPR = D * ESZ / 16;
+    constexpr int RPI = 64 / LPR;
+    constexpr int EPL = 16 / ESZ;
+    constexpr int R = kGroup / RPI;              // load instructions per group
+    static_assert(R <= LPR, "one lane per row slot writes the group's scores");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rs = lane / LPR, ch = lane % LPR;
+    const int Hu = a.Hkv / NH;
+    const int bu = blockIdx.x / a.P, p = blockIdx.x % a.P;
+    const int b = bu / Hu, u = bu % Hu;
+    const int64_t bh0 = (int64_t)b * a.Hkv + (int64_t)u * NH;   // first selection head
+
+    double qr[NH][EPL];
+    {
+        const TIn *qb = (const TIn *)a.q + (int64_t)b * a.Hq * D;
+#pragma unroll
+        for (int m = 0; m < NH; ++m)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                double s = 0.0;
+                for (int gg = 0; gg < a.g; ++gg)
+                    s += load_f64(qb, ((int64_t)(u * NH + m) * a.g + gg) * D + ch * EPL + e);
+                qr[m][e] = s;
+            }
+    }
+
+    const unsigned char *kh = a.k + (int64_t)((u * NH) / a.rep) * a.sh_bytes + ch * 16;
+    const GroupRange gr = group_range(a, p);
+    for (int64_t grp = gr.g0 + wave; grp < gr.g1; grp += kWaves) {
+        const int64_t t0 = a.mid_lo + grp * kGroup;
+        uint4 buf[R];
+        bool ok[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t t = t0 + r * RPI + rs;
+            ok[r] = t < a.mid_hi;
+            buf[r] = ok[r] ? load_nt(kh + t * a.st_bytes) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        double v[NH][R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            double x[EPL];
+            unpack(buf[r], x);
+#pragma unroll
+            for (int m = 0; m < NH; ++m) {
+                double acc = 0.0;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc = fma(qr[m][e], x[e], acc);
+                v[m][r] = row_sum<LPR>(acc) + 0.0;          // -0 -> +0
+            }
+        }
+        // lane (rs, ch < R) stores the score of token t0 + ch*RPI + rs
+        const int64_t tw = t0 + ch * RPI + rs;
+        const bool wr = ch < R && tw < a.mid_hi;
+#pragma unroll
+        for (int m = 0; m < NH; ++m) {
+            double mine = v[m][0], best = ok[0] ? v[m][0] : -INFINITY;
+#pragma unroll
+            for (int r = 1; r < R; ++r) {
+                if (ch == r) mine = v[m][r];
+                if (ok[r]) best = fmax(best, v[m][r]);
+            }
+            if (wr) a.out[(bh0 + m) * a.n_spans + (tw - a.mid_lo)] = mine;
+            best = rows_max<LPR>(best);
+            if (lane == 0) a.gmax[(bh0 + m) * a.n_groups + grp] = best;
+        }
+    }
+}
+
 // Blocks of several queries (chunked prefill on the VALU): the group-summed
 // queries of the block sit in LDS; span score = sum over queries of the max.
 template <typename TIn, int D>
@@ -351,12 +430,24 @@ void launch_heads(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s)
 // together (0: score each selection head on its own, reading its KV head).
 int multi_heads(const Geom &g) {
     if (g.block_q != 1 || g.rep < 2) return 0;
+    if (g.S == 1) return g.rep <= 4 ? g.rep : 0;     // token level: at most 4 heads' scores held
     return (g.rep == 2 || g.rep == 3 || g.rep == 4 || g.rep == 8) ? g.rep : 0;
+}
+
+template <typename TIn, int D, int NH>
+void launch_tokens(const ScoreArgs &a, int nblocks, hipStream_t s) {
+    hipLaunchKernelGGL((k_score_tokens<TIn, D, NH>), dim3(nblocks), dim3(kThreads), 0, s, a);
 }
 
 template <typename TIn, int D>
 hipError_t launch_typed(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
-    if (const int nh = multi_heads(g)) {
+    if (g.block_q == 1 && g.S == 1) {
+        const int nh = multi_heads(g);
+        if (nh == 2) launch_tokens<TIn, D, 2>(a, nblocks, s);
+        else if (nh == 3) launch_tokens<TIn, D, 3>(a, nblocks, s);
+        else if (nh == 4) launch_tokens<TIn, D, 4>(a, nblocks, s);
+        else launch_tokens<TIn, D, 1>(a, nblocks, s);
+    } else if (const int nh = multi_heads(g)) {
         if (nh == 2) launch_heads<TIn, D, 2>(g, a, nblocks, s);
         else if (nh == 3) launch_heads<TIn, D, 3>(g, a, nblocks, s);
         else if (nh == 4) launch_heads<TIn, D, 4>(g, a, nblocks, s);

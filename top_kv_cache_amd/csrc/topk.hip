@@ -74,6 +74,18 @@ struct GenericShared {
     int32_t lev_bin[kGMaxLevels];
 };
 
+// large path state (many groups, or many candidate groups)
+constexpr int kLGroups = 8192;      // candidate groups held, ascending
+static_assert(8 * kWaves == 64, "one wave scans the slice counts");
+struct LargeShared {
+    double val[kCandCap];
+    int32_t idx[kCandCap];
+    uint32_t hist[kBins];
+    int32_t cgrp[kLGroups];
+    uint32_t wcnt[8 * kWaves];
+    uint32_t wpre[8 * kWaves + 1];
+};
+
 struct Common {
     double red_d[2][kWaves];
     uint32_t red_u[kWaves];
@@ -274,6 +286,189 @@ __device__ __forceinline__ void find_kth(Common &cm, uint32_t *hist, double *val
 }
 
 // ---------------------------------------------------------------------------
+// large path: the fast path's decisions with the group maxima streamed from
+// global memory (any number of groups), for at most kLGroups candidate groups
+// and kCandCap candidate spans.  Returns false (uniformly, before writing any
+// output) when either bound is exceeded.
+// ---------------------------------------------------------------------------
+// Streams the group maxima in batches of 8 per thread (one batch covers
+// 8 * kThreads consecutive groups, e-major), calling f(i, x) for each.
+template <typename F>
+__device__ __forceinline__ void for_each_gmax(const double *gm, int64_t m, F f) {
+    const int tid = threadIdx.x;
+    for (int64_t b0 = 0; b0 < m; b0 += 8 * kThreads) {
+        double x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t i = b0 + e * kThreads + tid;
+            x[e] = gm[i < m ? i : m - 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t i = b0 + e * kThreads + tid;
+            if (i < m) f(i, x[e]);
+        }
+    }
+}
+
+__device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const double *sc,
+                                           const double *gm, int64_t n, int64_t m, int kk,
+                                           int topk, int32_t *sel) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // 1. tau: the smallest group maximum in the histogram bins at or above the
+    //    one holding the kk-th largest maximum (a lower bound of the kk-th
+    //    largest span score)
+    double mn = INFINITY, mx = -INFINITY;
+    uint32_t dummy = 0;
+    for_each_gmax(gm, m, [&](int64_t, double x) {
+        mn = fmin(mn, x);
+        mx = fmax(mx, x);
+    });
+    block_minmax_count(cm, mn, mx, dummy);
+    double tau = mn;
+    if (mn != mx) {
+        const double inv = (double)kBins / (mx - mn);
+        for (int i = tid; i < kBins; i += kThreads) L.hist[i] = 0u;
+        __syncthreads();
+        for_each_gmax(gm, m, [&](int64_t, double x) {
+            atomicAdd(&L.hist[bin_of(x, mn, inv, kBins)], 1u);
+        });
+        __syncthreads();
+        find_bin(cm, L.hist, kBins, kk);
+        const int bstar = cm.bstar;
+        double lo = INFINITY, unused = -INFINITY;
+        for_each_gmax(gm, m, [&](int64_t, double x) {
+            if (bin_of(x, mn, inv, kBins) >= bstar) lo = fmin(lo, x);
+        });
+        block_minmax_count(cm, lo, unused, dummy);
+        tau = lo;
+    }
+    // 2. candidate groups (maximum >= tau) in ascending order: per batch of
+    //    8 * kThreads groups, the count of every (e, wave) slice orders the writes
+    uint32_t ncg = 0;
+    for (int64_t b0 = 0; b0 < m; b0 += 8 * kThreads) {
+        double x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t i = b0 + e * kThreads + tid;
+            x[e] = gm[i < m ? i : m - 1];
+        }
+        unsigned long long bal[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t i = b0 + e * kThreads + tid;
+            bal[e] = __ballot(i < m && x[e] >= tau);
+            if (lane == 0) L.wcnt[e * kWaves + wave] = (uint32_t)__popcll(bal[e]);
+        }
+        __syncthreads();
+        if (wave == 0) {                 // exclusive prefix over the 64 slices
+            const uint32_t v = L.wcnt[lane];
+            uint32_t incl = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            L.wpre[lane] = incl - v;
+            if (lane == 63) L.wpre[64] = incl;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t off = ncg + L.wpre[e * kWaves + wave];
+            const unsigned long long bb = bal[e];
+            if ((bb >> lane) & 1ull) {
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(bb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u));
+                const uint32_t slot = off + below;
+                if (slot < (uint32_t)kLGroups) L.cgrp[slot] = (int32_t)(b0 + e * kThreads + tid);
+            }
+        }
+        ncg += L.wpre[64];
+    }
+    if (ncg > (uint32_t)kLGroups) return false;
+    if (tid == 0) cm.count = 0;
+    __syncthreads();
+    // 3. their spans scoring >= tau (half a wave per group, U groups in flight)
+    constexpr int U = 8;
+    const int half = tid >> 5, hl = tid & 31;
+    constexpr int GPI = kThreads / 32;                 // groups per pass (16)
+    for (uint32_t c0 = 0; c0 < ncg; c0 += GPI * U) {
+        double x[U];
+        int64_t j[U];
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+            const uint32_t c = c0 + e * GPI + half;
+            j[e] = c < ncg ? (int64_t)L.cgrp[c] * kGroup + hl : n;
+            x[e] = sc[j[e] < n ? j[e] : n - 1];
+        }
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+            if (j[e] < n && x[e] >= tau) {
+                const uint32_t slot = atomicAdd(&cm.count, 1u);
+                if (slot < (uint32_t)kCandCap) {
+                    L.val[slot] = x[e];
+                    L.idx[slot] = (int32_t)j[e];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t count = cm.count;
+    __syncthreads();
+    if (count > (uint32_t)kCandCap) return false;
+    // 4. the kk-th best candidate = the cutoff
+    find_kth(cm, L.hist, L.val, L.idx, count, kk);
+    const double cv = cm.cut_v;
+    const int64_t cj = cm.cut_j;
+    // 5. one selection word per candidate group (over the candidate values,
+    //    which are no longer needed), then one ordered scan writes the indices
+    uint32_t *words = reinterpret_cast<uint32_t *>(L.val);
+    for (uint32_t c0 = 0; c0 < ncg; c0 += GPI * U) {
+        double x[U];
+        int64_t j[U];
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+            const uint32_t c = c0 + e * GPI + half;
+            j[e] = c < ncg ? (int64_t)L.cgrp[c] * kGroup + hl : n;
+            x[e] = sc[j[e] < n ? j[e] : n - 1];
+        }
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+            const uint32_t c = c0 + e * GPI + half;
+            const bool pick = j[e] < n && (x[e] > cv || (x[e] == cv && j[e] <= cj));
+            const unsigned long long bal = __ballot(pick);
+            if (hl == 0 && c < ncg) words[c] = (uint32_t)(bal >> (lane & 32));
+        }
+    }
+    __syncthreads();
+    constexpr int WPT = kLGroups / kThreads;           // 16 words per thread
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+        const uint32_t c = (uint32_t)(tid * WPT + i);
+        mine += c < ncg ? (uint32_t)__popc(words[c]) : 0u;
+    }
+    uint32_t tot;
+    uint32_t pos = block_excl_sum(cm, mine, &tot);
+    if (sel) {
+        for (int i = 0; i < WPT; ++i) {
+            const uint32_t c = (uint32_t)(tid * WPT + i);
+            if (c >= ncg) break;
+            uint32_t w = words[c];
+            while (w) {
+                const int bit = __ffs(w) - 1;
+                w &= w - 1;
+                if (pos < (uint32_t)topk) sel[pos] = L.cgrp[c] * kGroup + bit;
+                ++pos;
+            }
+        }
+        for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
 // generic path: the same decisions with global-memory passes (any n)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool g_candidate(const GenericShared &gs, int nlev, double x) {
@@ -416,6 +611,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
     __shared__ Common cm;
     __shared__ union {
         FastShared f;
+        LargeShared l;
         GenericShared g;
     } u;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -602,8 +798,11 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
             (void)wave;
             return;
         }
-        // too many groups at or above the bound: generic path below
+        // too many groups at or above the bound: the large path below
+        __syncthreads();
     }
+
+    if (kk <= m && large_path(cm, u.l, sc, gm, n, m, kk, topk, sel)) return;
 
     generic_cutoff(cm, u.g, sc, n, kk);
     if (sel) {
