@@ -60,6 +60,10 @@ SMALL = {
     "pqh_bf16_g8_d64": S(Hq=8, Hkv=1, d=64, T=1800, S=32, topk=10, L=128, per_q_head=True),
     "pqh_bf16_g5_generic": S(Hq=10, Hkv=2, d=64, T=900, S=16, topk=6, L=64, per_q_head=True),
     "pqh_bf16_token_level": S(S=1, topk=40, T=400, per_q_head=True),
+    "pqh_bf16_g2_d128_S20": S(Hq=4, Hkv=2, d=128, T=1500, S=20, topk=9, L=100,
+                              kv_scaled=True, per_q_head=True),
+    "pqh_f32_g4_d64_S8": S(dtype="f32", Hq=8, Hkv=2, d=64, T=1300, S=8, topk=17, L=90,
+                           per_q_head=True),
     "pqh_bf16_prefill_blocks": S(Hq=8, Hkv=2, d=128, T=600, n_q=8, block_q=4, S=16, topk=6,
                                  L=64, needles=0, per_q_head=True),
     "pqh_bf16_mfma_blocks": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,

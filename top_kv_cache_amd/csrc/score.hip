@@ -267,6 +267,330 @@ __global__ __launch_bounds__(kThreads) void k_score_decode_heads(ScoreArgs a) {
     }
 }
 
+// DPP move of a double (both halves), for sums of two different registers.
+template <int CTRL> __device__ __forceinline__ double dpp_mov(double v) {
+    const int2 x = *reinterpret_cast<const int2 *>(&v);
+    int2 y;
+    y.x = __builtin_amdgcn_mov_dpp(x.x, CTRL, 0xF, 0xF, false);
+    y.y = __builtin_amdgcn_mov_dpp(x.y, CTRL, 0xF, 0xF, false);
+    return *reinterpret_cast<const double *>(&y);
+}
+
+// Head whose full row sum lane c (0..7 within its row) ends with after the
+// reduce-scatter of k_score_decode_heads8.
+template <int NH> __device__ __forceinline__ int heads8_final(int c) {
+    return NH == 4 ? 2 * ((c >> 2) & 1) + (c & 1) : ((c >> 2) & 1);
+}
+
+// Per-query-head decode for 256-byte key rows (bf16 d 128, fp32 d 64) and
+// NH = 2 or 4 query heads per KV head: 8 lanes per row (two 16-byte loads
+// each), and the NH partial dot products of a row are reduced with a
+// reduce-scatter instead of NH separate reductions.  Step 1 pairs lanes c and
+// c^7 (half-row mirror), step 2 c and c^1, step 3 c and c^2.  Each lane holds
+// its partial sums in an order fixed for it, so that every step adds the
+// partner's second half to its own first half with no selects: for NH = 4 the
+// order is F(c), F(c^1), F(c^7), F(c^6), with F(c) = 2*bit2 + bit0 the head
+// the lane ends with (lanes c and c^2 end with the same head); for NH = 2 it is
+// F(c), F(c^7) with F(c) = bit2.  Per row that is 12 DPP moves and 6 adds
+// instead of 4 x 4 x 3 operations.
+template <typename TIn, int D, int R, int NH>
+__global__ __launch_bounds__(kThreads) void k_score_decode_heads8(ScoreArgs a) {
+    constexpr int ESZ = sizeof(TIn);
+    static_assert(D * ESZ == 256, "256-byte key rows");
+    static_assert(NH == 2 || NH == 4, "two or four heads");
+    constexpr int RPI = 8;                       // rows per pair of load instructions
+    constexpr int EPL = 16 / ESZ;                // elements per 16-byte chunk
+    __shared__ double slot[2][NH][kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rs = lane >> 3, c = lane & 7;
+    const int Hp = a.Hkv / NH;
+    const int bp = blockIdx.x / a.P, p = blockIdx.x % a.P;
+    const int b = bp / Hp, hp = bp % Hp;
+    const int64_t bh0 = (int64_t)b * a.Hkv + (int64_t)hp * NH;
+
+    int order[NH];
+    if (NH == 4) {
+        order[0] = heads8_final<NH>(c);
+        order[1] = heads8_final<NH>(c ^ 1);
+        order[2] = heads8_final<NH>(c ^ 7);
+        order[3] = heads8_final<NH>(c ^ 6);
+    } else {
+        order[0] = heads8_final<NH>(c);
+        order[1] = heads8_final<NH>(c ^ 7);
+    }
+    double qr[NH][2 * EPL];
+    {
+        const TIn *qb = (const TIn *)a.q + (int64_t)b * a.Hq * D + (int64_t)hp * NH * D;
+#pragma unroll
+        for (int o = 0; o < NH; ++o)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                qr[o][e] = load_f64(qb, (int64_t)order[o] * D + c * EPL + e);
+                qr[o][EPL + e] = load_f64(qb, (int64_t)order[o] * D + D / 2 + c * EPL + e);
+            }
+    }
+    const int mine = heads8_final<NH>(c);
+    const bool writer = rs == 0 && ((c & 2) == 0) && (NH == 4 || (c & 1) == 0);
+
+    const unsigned char *kh = a.k + (int64_t)hp * a.sh_bytes + c * 16;
+    const GroupRange gr = group_range(a, p);
+    for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
+        const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
+        double gbest = -INFINITY;
+        for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
+            const int64_t tb = a.mid_lo + j * a.S;
+            const int64_t te = min(tb + (int64_t)a.S, a.mid_hi);
+            double best = -INFINITY;
+            for (int64_t r0 = tb; r0 < te; r0 += (int64_t)R * RPI) {
+                uint4 lo[R], hi[R];
+                bool ok[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t t = r0 + r * RPI + rs;
+                    ok[r] = t < te;
+                    const unsigned char *row = kh + (ok[r] ? t : tb) * a.st_bytes;
+                    lo[r] = load_nt(row);
+                    hi[r] = load_nt(row + 128);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    double acc[NH];
+#pragma unroll
+                    for (int o = 0; o < NH; ++o) acc[o] = 0.0;
+                    double x[EPL];
+                    unpack(lo[r], x);
+#pragma unroll
+                    for (int o = 0; o < NH; ++o)
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[o] = fma(qr[o][e], x[e], acc[o]);
+                    unpack(hi[r], x);
+#pragma unroll
+                    for (int o = 0; o < NH; ++o)
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[o] = fma(qr[o][EPL + e], x[e], acc[o]);
+                    double v;
+                    if (NH == 4) {
+                        const double s0 = acc[0] + dpp_mov<0x141>(acc[2]);
+                        const double s1 = acc[1] + dpp_mov<0x141>(acc[3]);
+                        v = s0 + dpp_mov<0xB1>(s1);
+                    } else {
+                        v = acc[0] + dpp_mov<0x141>(acc[1]);
+                        v = v + dpp_mov<0xB1>(v);
+                    }
+                    v = v + dpp_mov<0x4E>(v);
+                    if (ok[r]) best = fmax(best, v);
+                }
+            }
+            best = rows_max<8>(best) + 0.0;              // -0 -> +0
+            if (writer) a.out[(bh0 + mine) * a.n_spans + j] = best;
+            gbest = fmax(gbest, best);
+        }
+        if (writer) slot[grp & 1][mine][wave] = gbest;
+        __syncthreads();
+        if (threadIdx.x < NH) {
+            const int m = threadIdx.x;
+            double v = slot[grp & 1][m][0];
+            for (int w = 1; w < kWaves; ++w) v = fmax(v, slot[grp & 1][m][w]);
+            a.gmax[(bh0 + m) * a.n_groups + grp] = v;
+        }
+    }
+}
+
+// s_waitcnt vmcnt(n) for even n <= 14 (expcnt and lgkmcnt not waited for)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0xF78); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0xF7A); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0xF7C); break;
+    default: __builtin_amdgcn_s_waitcnt(0xF7E); break;
+    }
+}
+
+typedef unsigned int lds_u32x4 __attribute__((ext_vector_type(4)));
+
+// Two 16-byte LDS reads completed (lgkmcnt(0)) inside one asm block, so that
+// the compiler does not make them wait for the DMA still in flight to other
+// ring slots (the slot read here is complete by an explicit vmcnt wait).
+__device__ __forceinline__ void lds_read2(uint32_t a0, uint32_t a1, uint4 &o0, uint4 &o1) {
+    lds_u32x4 r0, r1;
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1)
+        : "v"(a0), "v"(a1)
+        : "memory");
+    o0 = make_uint4(r0.x, r0.y, r0.z, r0.w);
+    o1 = make_uint4(r1.x, r1.y, r1.z, r1.w);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(const void __attribute__((address_space(3))) *)p;
+}
+
+// k_score_decode_heads8 with the key rows staged through LDS by DMA
+// (global_load_lds), so that many rows are in flight without holding them in
+// registers.  Every wave runs its own pipeline over whole groups of 32 spans
+// (no barriers): a stage is 8 rows, moved by two 1 KB copies, the first
+// halves of the 8 rows then their second halves, so that lane (row r, chunk c)
+// reads LDS at 16 * lane in each half (conflict-free).  kHNB stages per wave
+// are in flight.
+constexpr int kHNB = 8;
+static_assert((kHNB & (kHNB - 1)) == 0, "ring slots: a power of two");
+
+template <typename TIn, int D, int NH>
+__global__ __launch_bounds__(kThreads, 2) void k_score_heads_lds(ScoreArgs a) {
+    constexpr int ESZ = sizeof(TIn);
+    static_assert(D * ESZ == 256, "256-byte key rows");
+    static_assert(NH == 2 || NH == 4, "two or four heads");
+    constexpr int EPL = 16 / ESZ;
+    __shared__ __align__(16) unsigned char ring[kWaves][kHNB][2048];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int rs = lane >> 3, c = lane & 7;
+    const int Hp = a.Hkv / NH;
+    const int bp = blockIdx.x / a.P, p = blockIdx.x % a.P;
+    const int b = bp / Hp, hp = bp % Hp;
+    const int64_t bh0 = (int64_t)b * a.Hkv + (int64_t)hp * NH;
+
+    int order[NH];
+    if (NH == 4) {
+        order[0] = heads8_final<NH>(c);
+        order[1] = heads8_final<NH>(c ^ 1);
+        order[2] = heads8_final<NH>(c ^ 7);
+        order[3] = heads8_final<NH>(c ^ 6);
+    } else {
+        order[0] = heads8_final<NH>(c);
+        order[1] = heads8_final<NH>(c ^ 7);
+    }
+    double qr[NH][2 * EPL];
+    {
+        const TIn *qb = (const TIn *)a.q + (int64_t)b * a.Hq * D + (int64_t)hp * NH * D;
+#pragma unroll
+        for (int o = 0; o < NH; ++o)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                qr[o][e] = load_f64(qb, (int64_t)order[o] * D + c * EPL + e);
+                qr[o][EPL + e] = load_f64(qb, (int64_t)order[o] * D + D / 2 + c * EPL + e);
+            }
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);              // queries in registers before the ring starts
+    const int mine = heads8_final<NH>(c);
+    const bool writer = rs == 0 && ((c & 2) == 0) && (NH == 4 || (c & 1) == 0);
+
+    // this wave's groups: g0 + wave, g0 + wave + 4, ...; stages: (span, sub)
+    const GroupRange gr = group_range(a, p);
+    const int64_t first = gr.g0 + wave;
+    const int64_t n_grp = first < gr.g1 ? (gr.g1 - first + kWaves - 1) / kWaves : 0;
+    if (n_grp == 0) return;
+    const int64_t last_grp = first + (n_grp - 1) * kWaves;
+    const int64_t n_spans_w = (n_grp - 1) * kGroup + min((int64_t)kGroup, a.n_spans - last_grp * kGroup);
+    const int sps = (a.S + 7) / 8;                   // stages per span
+    const int64_t n_st = n_spans_w * sps;
+
+    const unsigned char *kh = a.k + (int64_t)hp * a.sh_bytes;
+    const uint32_t ring_w = lds_addr(&ring[wave][0][0]);
+    // Stage cursors (issue side and consume side) advance incrementally: sub
+    // stage within the span, span within the group, group (stride kWaves).
+    struct Cursor {
+        int sub, sig;
+        int64_t grp, j, tb, te;
+    };
+    auto start = [&](Cursor &u) {
+        u.sub = 0;
+        u.sig = 0;
+        u.grp = first;
+        u.j = first * kGroup;
+        u.tb = a.mid_lo + u.j * a.S;
+        u.te = min(u.tb + (int64_t)a.S, a.mid_hi);
+    };
+    auto advance = [&](Cursor &u) {
+        if (++u.sub < sps) return;
+        u.sub = 0;
+        if (++u.sig == kGroup) {
+            u.sig = 0;
+            u.grp += kWaves;
+            u.j = u.grp * kGroup;
+        } else {
+            ++u.j;
+        }
+        u.tb = a.mid_lo + u.j * a.S;
+        u.te = min(u.tb + (int64_t)a.S, a.mid_hi);
+    };
+    Cursor iss, con;
+    start(iss);
+    start(con);
+    int64_t is = 0;                                  // stages issued
+    auto issue_next = [&]() {
+        if (is >= n_st) return;
+        int64_t t = iss.tb + iss.sub * 8 + (lane >> 3);
+        if (t >= iss.te) t = iss.tb;                 // masked when consumed
+        const unsigned char *src = kh + t * a.st_bytes + (lane & 7) * 16;
+        unsigned char *dst = &ring[wave][is & (kHNB - 1)][0];
+        __builtin_amdgcn_global_load_lds((const void *)src,
+                                         (void __attribute__((address_space(3))) *)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(src + 128),
+                                         (void __attribute__((address_space(3))) *)(dst + 1024),
+                                         16, 0, 0);
+        ++is;
+        advance(iss);
+    };
+    for (int i = 0; i < kHNB - 1; ++i) issue_next();
+
+    double best = -INFINITY, gbest = -INFINITY;
+    for (int64_t it = 0; it < n_st; ++it) {
+        int64_t later = n_st - 1 - it;               // stages issued after this one
+        if (later > kHNB - 2) later = kHNB - 2;
+        wait_vmcnt(2 * (int)later);
+        issue_next();                                // refills the slot read last step
+        const bool ok = con.tb + con.sub * 8 + rs < con.te;
+
+        uint4 lo, hi;
+        const uint32_t sa = ring_w + (uint32_t)((it & (kHNB - 1)) * 2048) + lane * 16;
+        lds_read2(sa, sa + 1024, lo, hi);
+        double acc[NH];
+#pragma unroll
+        for (int o = 0; o < NH; ++o) acc[o] = 0.0;
+        double x[EPL];
+        unpack(lo, x);
+#pragma unroll
+        for (int o = 0; o < NH; ++o)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[o] = fma(qr[o][e], x[e], acc[o]);
+        unpack(hi, x);
+#pragma unroll
+        for (int o = 0; o < NH; ++o)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[o] = fma(qr[o][EPL + e], x[e], acc[o]);
+        double v;
+        if (NH == 4) {
+            const double s0 = acc[0] + dpp_mov<0x141>(acc[2]);
+            const double s1 = acc[1] + dpp_mov<0x141>(acc[3]);
+            v = s0 + dpp_mov<0xB1>(s1);
+        } else {
+            v = acc[0] + dpp_mov<0x141>(acc[1]);
+            v = v + dpp_mov<0xB1>(v);
+        }
+        v = v + dpp_mov<0x4E>(v);
+        if (ok) best = fmax(best, v);
+        if (con.sub == sps - 1) {                    // span complete
+            best = rows_max<8>(best) + 0.0;          // -0 -> +0
+            if (writer) a.out[(bh0 + mine) * a.n_spans + con.j] = best;
+            gbest = fmax(gbest, best);
+            best = -INFINITY;
+            if (con.sig == kGroup - 1 || con.j == a.n_spans - 1) {   // group complete
+                if (writer) a.gmax[(bh0 + mine) * a.n_groups + con.grp] = gbest;
+                gbest = -INFINITY;
+            }
+        }
+        advance(con);
+    }
+}
+
 // Token-level decode (S = 1: every middle token is its own span).  A wave
 // takes one group of 32 consecutive tokens per step (all its rows loaded
 // before any arithmetic) and writes their 32 scores with one store per
@@ -412,7 +736,25 @@ void launch_decode(const ScoreArgs &a, int nblocks, hipStream_t s) {
 }
 
 template <typename TIn, int D, int NH>
+void launch_heads8(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
+    const int per_span = (g.S + 7) / 8;          // load pairs per span
+    if (per_span >= 4)
+        hipLaunchKernelGGL((k_score_decode_heads8<TIn, D, 4, NH>), dim3(nblocks), dim3(kThreads),
+                           0, s, a);
+    else if (per_span >= 2)
+        hipLaunchKernelGGL((k_score_decode_heads8<TIn, D, 2, NH>), dim3(nblocks), dim3(kThreads),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((k_score_decode_heads8<TIn, D, 1, NH>), dim3(nblocks), dim3(kThreads),
+                           0, s, a);
+}
+
+template <typename TIn, int D, int NH>
 void launch_heads(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
+    if constexpr (D * sizeof(TIn) == 256 && (NH == 2 || NH == 4)) {
+        hipLaunchKernelGGL((k_score_heads_lds<TIn, D, NH>), dim3(nblocks), dim3(kThreads), 0, s, a);
+        return;
+    }
     constexpr int RPI = 64 / (D * (int)sizeof(TIn) / 16);
     const int per_span = (g.S + RPI - 1) / RPI;
     if (per_span >= 4)
