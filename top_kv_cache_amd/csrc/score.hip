@@ -26,6 +26,10 @@
 // its four waves take adjacent spans, so the workgroup reads 32 KB
 // contiguous per step.  About two workgroups per compute unit run: more
 // concurrent streams lowered measured bandwidth.
+//
+// Variants: one selection per query head (every query head of a KV head's
+// group scored from one read of each key row), token-level selection (S = 1,
+// one 32-token group per wave), and blocks of several queries on the VALU.
 #include "rea_internal.h"
 
 #include <math.h>
@@ -277,123 +281,9 @@ template <int CTRL> __device__ __forceinline__ double dpp_mov(double v) {
 }
 
 // Head whose full row sum lane c (0..7 within its row) ends with after the
-// reduce-scatter of k_score_decode_heads8.
+// reduce-scatter of k_score_heads_lds.
 template <int NH> __device__ __forceinline__ int heads8_final(int c) {
     return NH == 4 ? 2 * ((c >> 2) & 1) + (c & 1) : ((c >> 2) & 1);
-}
-
-// Per-query-head decode for 256-byte key rows (bf16 d 128, fp32 d 64) and
-// NH = 2 or 4 query heads per KV head: 8 lanes per row (two 16-byte loads
-// each), and the NH partial dot products of a row are reduced with a
-// reduce-scatter instead of NH separate reductions.  Step 1 pairs lanes c and
-// c^7 (half-row mirror), step 2 c and c^1, step 3 c and c^2.  Each lane holds
-// its partial sums in an order fixed for it, so that every step adds the
-// partner's second half to its own first half with no selects: for NH = 4 the
-// order is F(c), F(c^1), F(c^7), F(c^6), with F(c) = 2*bit2 + bit0 the head
-// the lane ends with (lanes c and c^2 end with the same head); for NH = 2 it is
-// F(c), F(c^7) with F(c) = bit2.  Per row that is 12 DPP moves and 6 adds
-// instead of 4 x 4 x 3 operations.
-template <typename TIn, int D, int R, int NH>
-__global__ __launch_bounds__(kThreads) void k_score_decode_heads8(ScoreArgs a) {
-    constexpr int ESZ = sizeof(TIn);
-    static_assert(D * ESZ == 256, "256-byte key rows");
-    static_assert(NH == 2 || NH == 4, "two or four heads");
-    constexpr int RPI = 8;                       // rows per pair of load instructions
-    constexpr int EPL = 16 / ESZ;                // elements per 16-byte chunk
-    __shared__ double slot[2][NH][kWaves];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rs = lane >> 3, c = lane & 7;
-    const int Hp = a.Hkv / NH;
-    const int bp = blockIdx.x / a.P, p = blockIdx.x % a.P;
-    const int b = bp / Hp, hp = bp % Hp;
-    const int64_t bh0 = (int64_t)b * a.Hkv + (int64_t)hp * NH;
-
-    int order[NH];
-    if (NH == 4) {
-        order[0] = heads8_final<NH>(c);
-        order[1] = heads8_final<NH>(c ^ 1);
-        order[2] = heads8_final<NH>(c ^ 7);
-        order[3] = heads8_final<NH>(c ^ 6);
-    } else {
-        order[0] = heads8_final<NH>(c);
-        order[1] = heads8_final<NH>(c ^ 7);
-    }
-    double qr[NH][2 * EPL];
-    {
-        const TIn *qb = (const TIn *)a.q + (int64_t)b * a.Hq * D + (int64_t)hp * NH * D;
-#pragma unroll
-        for (int o = 0; o < NH; ++o)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                qr[o][e] = load_f64(qb, (int64_t)order[o] * D + c * EPL + e);
-                qr[o][EPL + e] = load_f64(qb, (int64_t)order[o] * D + D / 2 + c * EPL + e);
-            }
-    }
-    const int mine = heads8_final<NH>(c);
-    const bool writer = rs == 0 && ((c & 2) == 0) && (NH == 4 || (c & 1) == 0);
-
-    const unsigned char *kh = a.k + (int64_t)hp * a.sh_bytes + c * 16;
-    const GroupRange gr = group_range(a, p);
-    for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
-        const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
-        double gbest = -INFINITY;
-        for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
-            const int64_t tb = a.mid_lo + j * a.S;
-            const int64_t te = min(tb + (int64_t)a.S, a.mid_hi);
-            double best = -INFINITY;
-            for (int64_t r0 = tb; r0 < te; r0 += (int64_t)R * RPI) {
-                uint4 lo[R], hi[R];
-                bool ok[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int64_t t = r0 + r * RPI + rs;
-                    ok[r] = t < te;
-                    const unsigned char *row = kh + (ok[r] ? t : tb) * a.st_bytes;
-                    lo[r] = load_nt(row);
-                    hi[r] = load_nt(row + 128);
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    double acc[NH];
-#pragma unroll
-                    for (int o = 0; o < NH; ++o) acc[o] = 0.0;
-                    double x[EPL];
-                    unpack(lo[r], x);
-#pragma unroll
-                    for (int o = 0; o < NH; ++o)
-#pragma unroll
-                        for (int e = 0; e < EPL; ++e) acc[o] = fma(qr[o][e], x[e], acc[o]);
-                    unpack(hi[r], x);
-#pragma unroll
-                    for (int o = 0; o < NH; ++o)
-#pragma unroll
-                        for (int e = 0; e < EPL; ++e) acc[o] = fma(qr[o][EPL + e], x[e], acc[o]);
-                    double v;
-                    if (NH == 4) {
-                        const double s0 = acc[0] + dpp_mov<0x141>(acc[2]);
-                        const double s1 = acc[1] + dpp_mov<0x141>(acc[3]);
-                        v = s0 + dpp_mov<0xB1>(s1);
-                    } else {
-                        v = acc[0] + dpp_mov<0x141>(acc[1]);
-                        v = v + dpp_mov<0xB1>(v);
-                    }
-                    v = v + dpp_mov<0x4E>(v);
-                    if (ok[r]) best = fmax(best, v);
-                }
-            }
-            best = rows_max<8>(best) + 0.0;              // -0 -> +0
-            if (writer) a.out[(bh0 + mine) * a.n_spans + j] = best;
-            gbest = fmax(gbest, best);
-        }
-        if (writer) slot[grp & 1][mine][wave] = gbest;
-        __syncthreads();
-        if (threadIdx.x < NH) {
-            const int m = threadIdx.x;
-            double v = slot[grp & 1][m][0];
-            for (int w = 1; w < kWaves; ++w) v = fmax(v, slot[grp & 1][m][w]);
-            a.gmax[(bh0 + m) * a.n_groups + grp] = v;
-        }
-    }
 }
 
 // s_waitcnt vmcnt(n) for even n <= 14 (expcnt and lgkmcnt not waited for)
@@ -432,13 +322,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(size_t)(const void __attribute__((address_space(3))) *)p;
 }
 
-// k_score_decode_heads8 with the key rows staged through LDS by DMA
-// (global_load_lds), so that many rows are in flight without holding them in
-// registers.  Every wave runs its own pipeline over whole groups of 32 spans
-// (no barriers): a stage is 8 rows, moved by two 1 KB copies, the first
-// halves of the 8 rows then their second halves, so that lane (row r, chunk c)
-// reads LDS at 16 * lane in each half (conflict-free).  kHNB stages per wave
-// are in flight.
+// Per-query-head decode for 256-byte key rows (bf16 d 128, fp32 d 64) and
+// NH = 2 or 4 query heads per KV head.
+//
+// Arithmetic: 8 lanes per row, 32 bytes each, and the NH partial dot
+// products of a row are reduced with a reduce-scatter instead of NH separate
+// reductions.  Step 1 pairs lanes c and c^7 (half-row mirror), step 2 c and
+// c^1, step 3 c and c^2.  Each lane holds its partial sums in an order fixed
+// for it, so that every step adds the partner's second half to its own first
+// half with no selects: for NH = 4 the order is F(c), F(c^1), F(c^7), F(c^6),
+// with F(c) = 2*bit2 + bit0 the head the lane ends with (lanes c and c^2 end
+// with the same head); for NH = 2 it is F(c), F(c^7) with F(c) = bit2.  Per
+// row that is 6 DPP moves of doubles and 3 adds instead of NH x 3 of each.
+//
+// Memory: the key rows are staged through LDS by DMA (global_load_lds), so
+// that many rows are in flight without holding them in registers.  Every wave
+// runs its own pipeline over whole groups of 32 spans (no barriers): a stage
+// is 8 rows, moved by two 1 KB copies, the first halves of the 8 rows then
+// their second halves, so that lane (row r, chunk c) reads LDS at 16 * lane in
+// each half (conflict-free).  kHNB stages per wave are in flight.
 constexpr int kHNB = 8;
 static_assert((kHNB & (kHNB - 1)) == 0, "ring slots: a power of two");
 
@@ -733,20 +635,6 @@ __global__ __launch_bounds__(kThreads) void k_score_block(ScoreArgs a) {
 template <typename TIn, int D, int R>
 void launch_decode(const ScoreArgs &a, int nblocks, hipStream_t s) {
     hipLaunchKernelGGL((k_score_decode<TIn, D, R>), dim3(nblocks), dim3(kThreads), 0, s, a);
-}
-
-template <typename TIn, int D, int NH>
-void launch_heads8(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
-    const int per_span = (g.S + 7) / 8;          // load pairs per span
-    if (per_span >= 4)
-        hipLaunchKernelGGL((k_score_decode_heads8<TIn, D, 4, NH>), dim3(nblocks), dim3(kThreads),
-                           0, s, a);
-    else if (per_span >= 2)
-        hipLaunchKernelGGL((k_score_decode_heads8<TIn, D, 2, NH>), dim3(nblocks), dim3(kThreads),
-                           0, s, a);
-    else
-        hipLaunchKernelGGL((k_score_decode_heads8<TIn, D, 1, NH>), dim3(nblocks), dim3(kThreads),
-                           0, s, a);
 }
 
 template <typename TIn, int D, int NH>
