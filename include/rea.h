@@ -256,6 +256,37 @@ rea_status rea_prefill_plan(const rea_problem *p, const rea_params *a, int32_t c
 rea_status rea_prefill(const rea_problem *p, const rea_params *a, int32_t chunk, float *out,
                        void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Batched decode: one decode step (one query token each) for `batch`
+ * sequences that share the layer shape and the hyperparameters, in one
+ * launch sequence (OpenReview discussion, the authors' decoding-throughput
+ * replies: LLaMA3-8B decoding at 32K and 64K contexts with batch sizes larger
+ * than full attention fits).
+ *
+ * p            one sequence's shape with n_q = 1 and T = the cache capacity
+ *              (the largest length); p->q is [batch][n_q_heads][head_dim]
+ *              (all the batch's queries); p->k, p->v are sequence 0's cache,
+ *              and sequence b's cache starts b * kv_stride_seq elements later
+ *              (same head and token strides).
+ * a            block_q must be 1 and L >= 1; at most 8 query heads per
+ *              selection head.
+ * lengths      DEVICE array [batch] int64: sequence b has lengths[b] valid
+ *              tokens, its query being token lengths[b] - 1; every region,
+ *              span and window is derived from its own length.  Values are
+ *              clamped to [1, p->T] on the device (never read on the host).
+ * out          [batch][n_q_heads][head_dim] float32.
+ * sel, n_sel   optional [batch][H_sel][topk] / [batch][H_sel] (NULL to skip).
+ * ws           rea_decode_batch_workspace() bytes, 256-byte aligned.
+ * Errors: as rea_decode_step, plus REA_EUNSUPPORTED for n_q or block_q != 1
+ * and REA_ESHAPE for kv_stride_seq < n_kv_heads * kv_stride_head.
+ */
+rea_status rea_decode_batch_workspace(const rea_problem *p, const rea_params *a, int32_t batch,
+                                      size_t *ws_bytes);
+rea_status rea_decode_batch(const rea_problem *p, const rea_params *a, int32_t batch,
+                            const int64_t *lengths, int64_t kv_stride_seq, float *out,
+                            int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -174,3 +174,43 @@ def test_sizes_per_query_head_selection():
     a.S, a.topk = 1, 3840
     st, s3 = sizes_status(p, a)
     assert st == 0 and s3.n_spans == 131072 - 32 - 4096 and s3.W_cap == 32 + 3840 + 4096
+
+
+def test_batched_decode_workspace_and_errors():
+    L = rea.lib()
+    E = rea.STATUS.index
+    p, a = good()
+    ws = ctypes.c_size_t()
+    assert L.rea_decode_batch_workspace(ctypes.byref(p), ctypes.byref(a), 4, ctypes.byref(ws)) == 0
+    ws4 = ws.value
+    assert L.rea_decode_batch_workspace(ctypes.byref(p), ctypes.byref(a), 1, ctypes.byref(ws)) == 0
+    ws1 = ws.value
+    _, s = sizes_status(p, a)
+    assert ws1 == s.ws_decode_step and ws4 > 3 * ws1
+    assert L.rea_decode_batch_workspace(ctypes.byref(p), ctypes.byref(a), 0,
+                                        ctypes.byref(ws)) == E("REA_EINVAL")
+    stride = p.n_kv_heads * p.kv_stride_head
+
+    def call(pp=p, aa=a, batch=4, lens=FAKE, kvs=stride, out=FAKE, wsb=ws4):
+        return L.rea_decode_batch(ctypes.byref(pp), ctypes.byref(aa), batch, lens, kvs, out,
+                                  None, None, FAKE, wsb, None)
+
+    assert call(lens=None) == E("REA_EINVAL")
+    assert call(lens=FAKE + 4) == E("REA_EALIGN")
+    assert call(kvs=stride - 8) == E("REA_ESHAPE")
+    assert call(kvs=stride + 4) == E("REA_EALIGN")
+    assert call(out=None) == E("REA_EINVAL")
+    assert call(wsb=ws4 - 1) == E("REA_EWORKSPACE")
+    p2, a2 = good(n_q=2)
+    a2.block_q = 2
+    assert call(pp=p2, aa=a2) == E("REA_EUNSUPPORTED")
+    p3, a3 = good(Hq=64, Hkv=4)          # 16 query heads per KV head
+    assert call(pp=p3, aa=a3, kvs=p3.n_kv_heads * p3.kv_stride_head) == E("REA_EUNSUPPORTED")
+    a4 = rea.params(32, 32, 120, 0, 1)
+    assert call(aa=a4) == E("REA_ESHAPE")   # L = 0: the query token would not be local
+    p5, a5 = good(T=32)                     # T <= G + L passes the one-sequence check
+    a5.L = 0
+    assert call(pp=p5, aa=a5, kvs=p5.n_kv_heads * p5.kv_stride_head) == E("REA_EINVAL")
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == E("REA_ENODEVICE")

@@ -19,7 +19,8 @@ STATUS = ["REA_OK", "REA_EINVAL", "REA_ESHAPE", "REA_EDTYPE", "REA_EALIGN",
           "REA_EWORKSPACE", "REA_ENODEVICE", "REA_ELAUNCH", "REA_EUNSUPPORTED"]
 ENTRY_POINTS = ["rea_abi_version", "rea_status_string", "rea_last_error", "rea_query_sizes",
                 "rea_score_select", "rea_gather_rope", "rea_window_attend", "rea_decode_step",
-                "rea_prefill_plan", "rea_prefill"]
+                "rea_prefill_plan", "rea_prefill", "rea_decode_batch_workspace",
+                "rea_decode_batch"]
 
 
 class Problem(ctypes.Structure):
@@ -95,6 +96,11 @@ def lib():
                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
     L.rea_prefill.restype = ctypes.c_int
     L.rea_prefill.argtypes = [P, A, ctypes.c_int32, vp, vp, ctypes.c_size_t, vp]
+    L.rea_decode_batch_workspace.restype = ctypes.c_int
+    L.rea_decode_batch_workspace.argtypes = [P, A, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    L.rea_decode_batch.restype = ctypes.c_int
+    L.rea_decode_batch.argtypes = [P, A, ctypes.c_int32, vp, ctypes.c_int64, vp, i32p, i32p, vp,
+                                   ctypes.c_size_t, vp]
     if L.rea_abi_version() != 2:
         raise ImportError("librea.so ABI version mismatch")
     _lib = L
@@ -291,4 +297,48 @@ class Prefill:
             ws = self.workspace()
         _check(lib().rea_prefill(ctypes.byref(self.prob), ctypes.byref(self.par), self.chunk,
                                  _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+
+class DecodeBatch:
+    """One decode step for a batch of sequences: q [B][Hq][d], caches k, v
+    [B][Hkv][T_cap][d] (or any tensors whose sequence b starts at a fixed
+    stride), lengths a device int64 tensor [B] of valid tokens per sequence."""
+
+    def __init__(self, q, k, v, lengths, G, S, topk, L, rope_theta=500000.0,
+                 softmax_scale=0.0, per_q_head=False):
+        torch = _torch()
+        if k.dim() != 4 or v.shape != k.shape or k.stride() != v.stride() or k.stride(3) != 1:
+            raise ValueError("k and v must be [B][Hkv][T_cap][d] views with channel stride 1")
+        if q.dim() != 3 or not q.is_contiguous() or q.shape[0] != k.shape[0]:
+            raise ValueError("q must be a contiguous [B][Hq][d] tensor")
+        if lengths.dtype != torch.int64 or lengths.numel() != q.shape[0] or not lengths.is_contiguous():
+            raise ValueError("lengths must be a contiguous int64 tensor [B]")
+        self.q, self.k, self.v, self.lengths = q, k, v, lengths
+        self.batch = q.shape[0]
+        # one sequence's problem: q viewed as [1][Hq][d] of sequence 0
+        self.prob = problem_from_tensors(q[:1], k[0], v[0])
+        self.kv_stride_seq = k.stride(0)
+        self.par = params(G, S, topk, L, 1, rope_theta, softmax_scale, per_q_head)
+        self.sizes = query_sizes(self.prob, self.par)
+        ws = ctypes.c_size_t()
+        _check(lib().rea_decode_batch_workspace(ctypes.byref(self.prob), ctypes.byref(self.par),
+                                                self.batch, ctypes.byref(ws)))
+        self.ws_bytes = ws.value
+        self.device = q.device
+
+    def workspace(self):
+        return _aligned(_ws(self.ws_bytes, self.device))
+
+    def run(self, out=None, sel=None, nsel=None, ws=None, stream=None):
+        torch = _torch()
+        B, Hq, d = self.q.shape
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=self.device)
+        if ws is None:
+            ws = self.workspace()
+        _check(lib().rea_decode_batch(ctypes.byref(self.prob), ctypes.byref(self.par), self.batch,
+                                      _ptr(self.lengths), self.kv_stride_seq, _ptr(out),
+                                      _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel(),
+                                      _stream(stream)))
         return out

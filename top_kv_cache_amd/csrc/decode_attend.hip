@@ -54,6 +54,10 @@ struct FusedArgs {
     int64_t sh, st;         // elements
     int64_t T, Gp, Lp, mid_lo, n_spans;
     int S, last_len, topk, Hkv, Hq, g, n_q, block_q, QR, n_split, rep;
+    // batched decode (see Geom): per-sequence lengths and cache offsets
+    const int64_t *lens;
+    int hps, G, L;
+    int64_t seq_stride;
     float scale_log2;       // softmax scale * log2(e): logits in log2 units
     double frev_hi[kMaxHalfDim], frev_lo[kMaxHalfDim];   // theta_c / 2pi as hi + lo
     double step_c[kMaxHalfDim], step_s[kMaxHalfDim];     // cos, sin of theta_c
@@ -155,11 +159,13 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * a.Hkv + h;
     const int64_t w0 = (int64_t)sp * kRowsPerSplit;
+    const SeqOf so = seq_of(a.lens, h, a.hps, a.rep, a.seq_stride, a.sh, a.T);
+    const SeqGeom sg = seq_geom(so.T, a.G, a.L, a.S);
 
     // One round trip: the selection count, the selection slots this split's
     // rows can touch, and the raw query elements (all loads before any store).
     const int ns = a.n_sel[bh];
-    const int64_t slot0 = w0 > a.Gp ? (w0 - a.Gp) / a.S : 0;
+    const int64_t slot0 = w0 > sg.Gp ? (w0 - sg.Gp) / a.S : 0;
     int32_t sv = 0;
     if (a.topk > 0 && tid < kSelStage && slot0 + tid < a.topk) sv = a.sel[bh * a.topk + slot0 + tid];
     float qx1[QPT], qx2[QPT];
@@ -196,9 +202,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     // window length: only span n_spans-1 can be short, and a sorted selection
     // holds it last
     int64_t sel_len = (int64_t)ns * a.S;
-    if (a.last_len != a.S && ns > 0 && a.sel[bh * a.topk + ns - 1] == a.n_spans - 1)
-        sel_len -= a.S - a.last_len;
-    const int64_t Wbh = a.Gp + sel_len + a.Lp;
+    if (sg.last_len != a.S && ns > 0 && a.sel[bh * a.topk + ns - 1] == sg.n_spans - 1)
+        sel_len -= a.S - sg.last_len;
+    const int64_t Wbh = sg.Gp + sel_len + sg.Lp;
     __syncthreads();
 
     // this stream's rows: source token and K, V.  Rows past the window load
@@ -209,9 +215,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     const int64_t wf = w0 + wave * (4 * kSL) + rho * kSL;
     Part<TIn, PPL> k1[kSL], k2[kSL], v1[kSL], v2[kSL];
     {
-        const TIn *kb = (const TIn *)a.k + (int64_t)(h / a.rep) * a.sh;
-        const TIn *vb = (const TIn *)a.v + (int64_t)(h / a.rep) * a.sh;
-        const int64_t o0 = wf - a.Gp;
+        const TIn *kb = (const TIn *)a.k + so.kv_off;
+        const TIn *vb = (const TIn *)a.v + so.kv_off;
+        const int64_t o0 = wf - sg.Gp;
         const uint32_t oc = (uint32_t)(o0 > 0 ? o0 : 0);
         int oq = (int)(oc / (uint32_t)a.S), orr = (int)(oc - (uint32_t)oq * (uint32_t)a.S);
 #pragma unroll
@@ -222,9 +228,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
                 if (o < 0)
                     src = w;
                 else if (o < sel_len)
-                    src = a.mid_lo + (int64_t)ssel[oq - slot0] * a.S + orr;
+                    src = sg.mid_lo + (int64_t)ssel[oq - slot0] * a.S + orr;
                 else
-                    src = a.T - a.Lp + (o - sel_len);
+                    src = sg.T - sg.Lp + (o - sel_len);
             }
             const int64_t row = src * a.st;
             k1[i].load(kb + row + c0);
@@ -503,6 +509,11 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
     a.Hq = g.Hq;
     a.g = g.g;
     a.rep = g.rep;
+    a.lens = g.lens;
+    a.hps = g.hps;
+    a.G = g.G;
+    a.L = g.L;
+    a.seq_stride = g.seq_stride;
     a.n_q = g.n_q;
     a.block_q = g.block_q;
     a.QR = g.block_q * g.g;

@@ -109,6 +109,11 @@ rea_status make_geom(const rea_problem *p, const rea_params *a, rea::Geom *g) {
     g->st = p->kv_stride_tok;
     g->scale = a->softmax_scale > 0.f ? a->softmax_scale : (float)(1.0 / sqrt((double)g->d));
     g->theta = a->rope_theta;
+    g->lens = nullptr;
+    g->hps = g->Hkv;
+    g->seq_stride = 0;
+    g->G = a->G;
+    g->L = a->L;
 
     if (n_mid > 0 && p->n_q > g->Lp)
         return fail(REA_ESHAPE,
@@ -493,6 +498,96 @@ rea_status rea_prefill(const rea_problem *p, const rea_params *a, int32_t chunk,
         float *oc = out + (size_t)start * p->n_q_heads * p->head_dim;
         return rea_decode_step(&pc, &ac, oc, nullptr, nullptr, ws, ws_bytes, stream, nullptr);
     });
+}
+
+}  // extern "C"
+
+// ---- batched decode ---------------------------------------------------------
+
+namespace {
+
+// Validates one sequence's problem and the batch, then folds the batch into
+// the selection heads: sequence b owns selection heads [b * H_sel, (b+1) * H_sel)
+// and query heads [b * Hq, (b+1) * Hq); its cache starts b * kv_stride_seq
+// elements after p->k / p->v.  Kernels re-derive every sequence's regions from
+// its own length.
+rea_status make_batch_geom(const rea_problem *p, const rea_params *a, int32_t batch,
+                           rea::Geom *g) {
+    rea_status st = make_geom(p, a, g);
+    if (st != REA_OK) return st;
+    if (batch < 1) return fail(REA_EINVAL, "batch %d < 1", batch);
+    if (p->n_q != 1 || a->block_q != 1)
+        return fail(REA_EUNSUPPORTED, "batched decode takes one query per sequence (n_q %d, "
+                    "block_q %d)", p->n_q, a->block_q);
+    if (a->L < 1)
+        return fail(REA_EINVAL, "batched decode needs L >= 1 (the query token is local)");
+    if (!rea::fused_decode_path(*g))
+        return fail(REA_EUNSUPPORTED, "batched decode needs at most 8 query heads per selection "
+                    "head (have %d)", g->g);
+    if ((int64_t)batch * g->Hkv >= ((int64_t)1 << 24) || (int64_t)batch * g->Hq >= ((int64_t)1 << 24))
+        return fail(REA_EUNSUPPORTED, "batch %d too large", batch);
+    g->hps = g->Hkv;
+    g->Hkv *= batch;
+    g->Hq *= batch;
+    return REA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rea_status rea_decode_batch_workspace(const rea_problem *p, const rea_params *a, int32_t batch,
+                                      size_t *ws_bytes) {
+    g_err[0] = 0;
+    if (!ws_bytes) return fail(REA_EINVAL, "ws_bytes is NULL");
+    rea::Geom g;
+    rea_status st = make_batch_geom(p, a, batch, &g);
+    if (st != REA_OK) return st;
+    *ws_bytes = decode_ws_bytes(g);
+    return REA_OK;
+}
+
+rea_status rea_decode_batch(const rea_problem *p, const rea_params *a, int32_t batch,
+                            const int64_t *lengths, int64_t kv_stride_seq, float *out,
+                            int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes,
+                            void *stream) {
+    g_err[0] = 0;
+    rea::Geom g;
+    rea_status st = make_batch_geom(p, a, batch, &g);
+    if (st != REA_OK) return st;
+    if (!lengths) return fail(REA_EINVAL, "lengths is NULL");
+    if (!aligned(lengths, 8)) return fail(REA_EALIGN, "lengths must be 8-byte aligned");
+    if (kv_stride_seq < (int64_t)p->n_kv_heads * p->kv_stride_head)
+        return fail(REA_ESHAPE, "kv_stride_seq %lld < n_kv_heads * kv_stride_head",
+                    (long long)kv_stride_seq);
+    if ((kv_stride_seq * g.esize) % 16 != 0)
+        return fail(REA_EALIGN, "kv_stride_seq must be a multiple of 16 bytes");
+    g.lens = lengths;
+    g.seq_stride = kv_stride_seq;
+    if (!out) return fail(REA_EINVAL, "out is NULL");
+    if (!aligned(out, 16)) return fail(REA_EALIGN, "out must be 16-byte aligned");
+    if ((sel && !aligned(sel, 4)) || (n_sel && !aligned(n_sel, 4)))
+        return fail(REA_EALIGN, "sel / n_sel must be 4-byte aligned");
+    if ((st = check_ws(ws, ws_bytes, decode_ws_bytes(g))) != REA_OK) return st;
+    int num_cu = 0;
+    if ((st = device_ready(&num_cu)) != REA_OK) return st;
+
+    Carve c{(char *)ws, 0};
+    double *scores = c.take<double>(score_scores_bytes(g));
+    void *aux = c.take<char>(select_aux_bytes(g));
+    int32_t *ws_sel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
+    int32_t *ws_nsel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+    int32_t *use_sel = sel ? sel : ws_sel;
+    int32_t *use_nsel = n_sel ? n_sel : ws_nsel;
+    if (g.topk == 0) use_sel = sel;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = launched(launch_select(g, p->q, p->k, scores, aux, use_sel, use_nsel, num_cu, s,
+                                     nullptr),
+                       "batched score_select")) != REA_OK)
+        return st;
+    void *fws = c.take<char>(rea::fused_ws_bytes(g));
+    return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out, fws, s),
+                    "batched gather + window attention");
 }
 
 }  // extern "C"

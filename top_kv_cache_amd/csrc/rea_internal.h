@@ -26,7 +26,55 @@ struct Geom {
     int64_t sh, st;     // K/V strides (elements) per head / per token
     float scale;        // softmax scale
     double theta;       // RoPE base
+    // batched decode: selection heads [b * hps, (b + 1) * hps) belong to
+    // sequence b, whose cache starts seq_stride elements after sequence b-1's
+    // and whose length is lens[b] (device memory; nullptr: one sequence of T)
+    const int64_t *lens;
+    int hps;            // selection heads per sequence (Hkv when not batched)
+    int64_t seq_stride;
+    int G, L;           // the hyperparameters (regions are re-derived per sequence)
 };
+
+// Regions of one sequence of T tokens (the host derives the same for a
+// single sequence): G' = min(G, T), L' = min(L, T - G'), middle [G', T - L')
+// cut into spans of S from its start, in groups of 32 spans.
+struct SeqGeom {
+    int64_t T, Gp, Lp, mid_lo, mid_hi, n_spans, n_groups;
+    int last_len;
+};
+__host__ __device__ inline SeqGeom seq_geom(int64_t T, int64_t G, int64_t L, int64_t S) {
+    SeqGeom r;
+    r.T = T;
+    r.Gp = G < T ? G : T;
+    r.Lp = L < T - r.Gp ? L : T - r.Gp;
+    r.mid_lo = r.Gp;
+    r.mid_hi = T - r.Lp;
+    const int64_t n_mid = r.mid_hi - r.mid_lo;
+    r.n_spans = (n_mid + S - 1) / S;
+    r.n_groups = (r.n_spans + 31) / 32;
+    r.last_len = r.n_spans > 0 ? (int)(n_mid - (r.n_spans - 1) * S) : 0;
+    return r;
+}
+
+// The sequence of selection head h: its length (lens[b] clamped to [1, Tcap],
+// or Tcap) and the element offset of its KV head in the cache.
+struct SeqOf {
+    int64_t T;
+    int64_t kv_off;
+};
+__device__ __forceinline__ SeqOf seq_of(const int64_t *lens, int h, int hps, int rep,
+                                        int64_t seq_stride, int64_t sh, int64_t Tcap) {
+    const int b = h / hps;
+    SeqOf r;
+    int64_t T = Tcap;
+    if (lens) {
+        T = lens[b];
+        T = T < 1 ? 1 : (T > Tcap ? Tcap : T);
+    }
+    r.T = T;
+    r.kv_off = (int64_t)b * seq_stride + (int64_t)((h - b * hps) / rep) * sh;
+    return r;
+}
 
 constexpr int kMaxHalfDim = 64;   // head_dim <= 128
 

@@ -47,8 +47,12 @@ struct ScoreArgs {
     double *out;                // [n_blk][Hkv][n_spans]
     double *gmax;               // [n_blk][Hkv][n_groups]
     int64_t sh_bytes, st_bytes;
-    int64_t mid_lo, mid_hi, n_spans, n_groups;
+    int64_t mid_lo, mid_hi, n_spans, n_groups;   // n_spans, n_groups: also the row strides
     int S, Hq, Hkv, g, block_q, P, rep;
+    // batched decode (see Geom): per-sequence lengths and cache offsets
+    const int64_t *lens;
+    int hps, G, L;
+    int64_t T, seq_stride_bytes;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -109,8 +113,20 @@ template <int LPR> __device__ __forceinline__ double rows_max(double v) {
 struct GroupRange {
     int64_t g0, g1;
 };
-__device__ __forceinline__ GroupRange group_range(const ScoreArgs &a, int p) {
-    return {(int64_t)p * a.n_groups / a.P, (int64_t)(p + 1) * a.n_groups / a.P};
+__device__ __forceinline__ GroupRange group_range(const ScoreArgs &a, int p, int64_t n_groups) {
+    const int64_t g1 = (int64_t)(p + 1) * a.n_groups / a.P;
+    return {(int64_t)p * a.n_groups / a.P, g1 < n_groups ? g1 : n_groups};
+}
+
+// The regions of the sequence that selection head hs belongs to, and the
+// byte offset of its KV head in the cache.
+struct Unit {
+    SeqGeom sg;
+    int64_t kv_off;
+};
+__device__ __forceinline__ Unit unit_of(const ScoreArgs &a, int hs) {
+    const SeqOf so = seq_of(a.lens, hs, a.hps, a.rep, a.seq_stride_bytes, a.sh_bytes, a.T);
+    return {seq_geom(so.T, a.G, a.L, a.S), so.kv_off};
 }
 
 __device__ __forceinline__ void publish_group_max(const ScoreArgs &a, double (&slot)[2][kWaves],
@@ -150,14 +166,15 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
         }
     }
 
-    const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes + ch * 16;
-    const GroupRange gr = group_range(a, p);
+    const Unit un = unit_of(a, h);
+    const unsigned char *kh = a.k + un.kv_off + ch * 16;
+    const GroupRange gr = group_range(a, p, un.sg.n_groups);
     for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
-        const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
+        const int64_t jend = min((grp + 1) * kGroup, un.sg.n_spans);
         double gbest = -INFINITY;
         for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
-            const int64_t tb = a.mid_lo + j * a.S;
-            const int64_t te = min(tb + (int64_t)a.S, a.mid_hi);
+            const int64_t tb = un.sg.mid_lo + j * a.S;
+            const int64_t te = min(tb + (int64_t)a.S, un.sg.mid_hi);
             double best = -INFINITY;
             for (int64_t r0 = tb; r0 < te; r0 += (int64_t)R * RPI) {
                 uint4 buf[R];
@@ -214,16 +231,17 @@ __global__ __launch_bounds__(kThreads) void k_score_decode_heads(ScoreArgs a) {
             for (int e = 0; e < EPL; ++e) qr[m][e] = load_f64(qb, (int64_t)m * D + ch * EPL + e);
     }
 
-    const unsigned char *kh = a.k + (int64_t)hp * a.sh_bytes + ch * 16;
-    const GroupRange gr = group_range(a, p);
+    const Unit un = unit_of(a, hp * NH);
+    const unsigned char *kh = a.k + un.kv_off + ch * 16;
+    const GroupRange gr = group_range(a, p, un.sg.n_groups);
     for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
-        const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
+        const int64_t jend = min((grp + 1) * kGroup, un.sg.n_spans);
         double gbest[NH];
 #pragma unroll
         for (int m = 0; m < NH; ++m) gbest[m] = -INFINITY;
         for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
-            const int64_t tb = a.mid_lo + j * a.S;
-            const int64_t te = min(tb + (int64_t)a.S, a.mid_hi);
+            const int64_t tb = un.sg.mid_lo + j * a.S;
+            const int64_t te = min(tb + (int64_t)a.S, un.sg.mid_hi);
             double best[NH];
 #pragma unroll
             for (int m = 0; m < NH; ++m) best[m] = -INFINITY;
@@ -385,16 +403,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_score_heads_lds(ScoreArgs a) {
     const bool writer = rs == 0 && ((c & 2) == 0) && (NH == 4 || (c & 1) == 0);
 
     // this wave's groups: g0 + wave, g0 + wave + 4, ...; stages: (span, sub)
-    const GroupRange gr = group_range(a, p);
+    const Unit un = unit_of(a, hp * NH);
+    const GroupRange gr = group_range(a, p, un.sg.n_groups);
     const int64_t first = gr.g0 + wave;
     const int64_t n_grp = first < gr.g1 ? (gr.g1 - first + kWaves - 1) / kWaves : 0;
     if (n_grp == 0) return;
     const int64_t last_grp = first + (n_grp - 1) * kWaves;
-    const int64_t n_spans_w = (n_grp - 1) * kGroup + min((int64_t)kGroup, a.n_spans - last_grp * kGroup);
+    const int64_t n_spans_w = (n_grp - 1) * kGroup + min((int64_t)kGroup, un.sg.n_spans - last_grp * kGroup);
     const int sps = (a.S + 7) / 8;                   // stages per span
     const int64_t n_st = n_spans_w * sps;
 
-    const unsigned char *kh = a.k + (int64_t)hp * a.sh_bytes;
+    const unsigned char *kh = a.k + un.kv_off;
     const uint32_t ring_w = lds_addr(&ring[wave][0][0]);
     // Stage cursors (issue side and consume side) advance incrementally: sub
     // stage within the span, span within the group, group (stride kWaves).
@@ -407,8 +426,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_score_heads_lds(ScoreArgs a) {
         u.sig = 0;
         u.grp = first;
         u.j = first * kGroup;
-        u.tb = a.mid_lo + u.j * a.S;
-        u.te = min(u.tb + (int64_t)a.S, a.mid_hi);
+        u.tb = un.sg.mid_lo + u.j * a.S;
+        u.te = min(u.tb + (int64_t)a.S, un.sg.mid_hi);
     };
     auto advance = [&](Cursor &u) {
         if (++u.sub < sps) return;
@@ -420,8 +439,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_score_heads_lds(ScoreArgs a) {
         } else {
             ++u.j;
         }
-        u.tb = a.mid_lo + u.j * a.S;
-        u.te = min(u.tb + (int64_t)a.S, a.mid_hi);
+        u.tb = un.sg.mid_lo + u.j * a.S;
+        u.te = min(u.tb + (int64_t)a.S, un.sg.mid_hi);
     };
     Cursor iss, con;
     start(iss);
@@ -484,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_score_heads_lds(ScoreArgs a) {
             if (writer) a.out[(bh0 + mine) * a.n_spans + con.j] = best;
             gbest = fmax(gbest, best);
             best = -INFINITY;
-            if (con.sig == kGroup - 1 || con.j == a.n_spans - 1) {   // group complete
+            if (con.sig == kGroup - 1 || con.j == un.sg.n_spans - 1) {   // group complete
                 if (writer) a.gmax[(bh0 + mine) * a.n_groups + con.grp] = gbest;
                 gbest = -INFINITY;
             }
@@ -529,16 +548,17 @@ __global__ __launch_bounds__(kThreads) void k_score_tokens(ScoreArgs a) {
             }
     }
 
-    const unsigned char *kh = a.k + (int64_t)((u * NH) / a.rep) * a.sh_bytes + ch * 16;
-    const GroupRange gr = group_range(a, p);
+    const Unit un = unit_of(a, u * NH);
+    const unsigned char *kh = a.k + un.kv_off + ch * 16;
+    const GroupRange gr = group_range(a, p, un.sg.n_groups);
     for (int64_t grp = gr.g0 + wave; grp < gr.g1; grp += kWaves) {
-        const int64_t t0 = a.mid_lo + grp * kGroup;
+        const int64_t t0 = un.sg.mid_lo + grp * kGroup;
         uint4 buf[R];
         bool ok[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int64_t t = t0 + r * RPI + rs;
-            ok[r] = t < a.mid_hi;
+            ok[r] = t < un.sg.mid_hi;
             buf[r] = ok[r] ? load_nt(kh + t * a.st_bytes) : make_uint4(0u, 0u, 0u, 0u);
         }
         double v[NH][R];
@@ -556,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void k_score_tokens(ScoreArgs a) {
         }
         // lane (rs, ch < R) stores the score of token t0 + ch*RPI + rs
         const int64_t tw = t0 + ch * RPI + rs;
-        const bool wr = ch < R && tw < a.mid_hi;
+        const bool wr = ch < R && tw < un.sg.mid_hi;
 #pragma unroll
         for (int m = 0; m < NH; ++m) {
             double mine = v[m][0], best = ok[0] ? v[m][0] : -INFINITY;
@@ -565,7 +585,7 @@ __global__ __launch_bounds__(kThreads) void k_score_tokens(ScoreArgs a) {
                 if (ch == r) mine = v[m][r];
                 if (ok[r]) best = fmax(best, v[m][r]);
             }
-            if (wr) a.out[(bh0 + m) * a.n_spans + (tw - a.mid_lo)] = mine;
+            if (wr) a.out[(bh0 + m) * a.n_spans + (tw - un.sg.mid_lo)] = mine;
             best = rows_max<LPR>(best);
             if (lane == 0) a.gmax[(bh0 + m) * a.n_groups + grp] = best;
         }
@@ -597,14 +617,15 @@ __global__ __launch_bounds__(kThreads) void k_score_block(ScoreArgs a) {
     }
     __syncthreads();
 
-    const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes + ch * 16;
-    const GroupRange gr = group_range(a, p);
+    const Unit un = unit_of(a, h);
+    const unsigned char *kh = a.k + un.kv_off + ch * 16;
+    const GroupRange gr = group_range(a, p, un.sg.n_groups);
     for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
-        const int64_t jend = min((grp + 1) * kGroup, a.n_spans);
+        const int64_t jend = min((grp + 1) * kGroup, un.sg.n_spans);
         double gbest = -INFINITY;
         for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
-            const int64_t tb = a.mid_lo + j * a.S;
-            const int64_t te = min(tb + (int64_t)a.S, a.mid_hi);
+            const int64_t tb = un.sg.mid_lo + j * a.S;
+            const int64_t te = min(tb + (int64_t)a.S, un.sg.mid_hi);
             double total = 0.0;
             for (int i = 0; i < a.block_q; ++i) {
                 const double *qi = qe + (int64_t)i * D + ch * EPL;
@@ -724,6 +745,12 @@ hipError_t launch_score(const Geom &g, const void *q, const void *k, double *spa
     a.g = g.g;
     a.block_q = g.block_q;
     a.rep = g.rep;
+    a.lens = g.lens;
+    a.hps = g.hps;
+    a.G = g.G;
+    a.L = g.L;
+    a.T = g.T;
+    a.seq_stride_bytes = g.seq_stride * g.esize;
     // one workgroup column per (block, KV head); a multi-head decode covers the
     // rep selection heads of a KV head together
     const int nh = multi_heads(g);

@@ -603,11 +603,20 @@ __device__ __forceinline__ void generic_emit(Common &cm, const double *sc, int64
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ scores_all,
-                                                   const double *__restrict__ gmax_all,
-                                                   int64_t n, int64_t m, int kk, int topk,
-                                                   int32_t *__restrict__ sel_all,
-                                                   int32_t *__restrict__ nsel_all) {
+struct TopkArgs {
+    const double *scores;       // [n_blk * Hkv][n_stride]
+    const double *gmax;         // [n_blk * Hkv][m_stride]
+    int32_t *sel, *nsel;
+    int64_t n_stride, m_stride;
+    int topk, Hkv, S;
+    // the (block, selection head)'s sequence: length lens[h / hps] (batched
+    // decode) or T; its span count and group count follow from G, L and S
+    const int64_t *lens;
+    int hps;
+    int64_t T, G, L;
+};
+
+__global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
     __shared__ Common cm;
     __shared__ union {
         FastShared f;
@@ -616,10 +625,20 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
     } u;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t bh = blockIdx.x;
-    const double *sc = scores_all + bh * n;
-    const double *gm = gmax_all + bh * m;
-    int32_t *sel = sel_all ? sel_all + bh * topk : nullptr;
-    if (tid == 0) nsel_all[bh] = kk;
+    const int h = (int)(bh % ta.Hkv);
+    int64_t T = ta.T;
+    if (ta.lens) {
+        T = ta.lens[h / ta.hps];
+        T = T < 1 ? 1 : (T > ta.T ? ta.T : T);
+    }
+    const SeqGeom sg = seq_geom(T, ta.G, ta.L, ta.S);
+    const int64_t n = sg.n_spans, m = sg.n_groups;
+    const int topk = ta.topk;
+    const int kk = (int)(topk < n ? topk : n);
+    const double *sc = ta.scores + bh * ta.n_stride;
+    const double *gm = ta.gmax + bh * ta.m_stride;
+    int32_t *sel = ta.sel ? ta.sel + bh * topk : nullptr;
+    if (tid == 0) ta.nsel[bh] = kk;
 
     if (kk == 0 || kk >= n) {       // nothing or everything
         if (sel)
@@ -816,8 +835,22 @@ __global__ __launch_bounds__(kThreads) void k_topk(const double *__restrict__ sc
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
                        int32_t *sel, int32_t *n_sel, hipStream_t s) {
     const int nbh = g.n_blk * g.Hkv;
-    hipLaunchKernelGGL(k_topk, dim3(nbh), dim3(kThreads), 0, s, span_scores, group_max,
-                       g.n_spans, score_groups(g), g.k_sel, g.topk, sel, n_sel);
+    TopkArgs ta;
+    ta.scores = span_scores;
+    ta.gmax = group_max;
+    ta.sel = sel;
+    ta.nsel = n_sel;
+    ta.n_stride = g.n_spans;
+    ta.m_stride = score_groups(g);
+    ta.topk = g.topk;
+    ta.Hkv = g.Hkv;
+    ta.S = g.S;
+    ta.lens = g.lens;
+    ta.hps = g.hps;
+    ta.T = g.T;
+    ta.G = g.G;
+    ta.L = g.L;
+    hipLaunchKernelGGL(k_topk, dim3(nbh), dim3(kThreads), 0, s, ta);
     return hipGetLastError();
 }
 
