@@ -164,6 +164,90 @@ def prefill_main(args):
         "roofline": None, "cpu_baseline": None}), flush=True)
 
 
+def batch_main(args):
+    """Batched decode: args.batch sequences of the 8B shape, all 32 layers
+    resident, one rea_decode_batch per layer; lengths all equal to
+    args.context, or (--ragged) spread evenly over [context/2, context].
+    One JSON line with decoded tokens per second, and the same batch run as
+    one rea_decode_step per sequence and layer for comparison."""
+    import torch
+    import synth
+    import top_kv_cache_amd as rea
+    from synth import torch_io
+
+    B, T = args.batch, args.context
+    base = synth.small(name=f"llama8b-bf16-decode-batch{B}-{T // 1024}k" + ("-ragged" if args.ragged else ""),
+                       seed=240715190, dtype="bf16", Hq=32, Hkv=8, d=128, T=T, n_q=1, block_q=1,
+                       G=32, S=32, topk=120, L=4096, needles=4, kv_scaled=True, layers=32)
+    n_layers = args.layers or 32
+    dev = torch.device("cuda:0")
+    lens = [T - (i * (T // 2)) // max(B - 1, 1) for i in range(B)] if args.ragged else [T] * B
+    lengths = torch.tensor(lens, dtype=torch.int64, device=dev)
+    t_gen = time.perf_counter()
+    runs, outs, steps = [], [], []
+    for layer in range(n_layers):
+        q = torch.empty((B, base.Hq, base.d), dtype=torch.bfloat16, device=dev)
+        K = torch.empty((B, base.Hkv, T, base.d), dtype=torch.bfloat16, device=dev)
+        V = torch.empty_like(K)
+        for b in range(B):
+            wb = dataclasses.replace(base, seed=base.seed + 1000 * b)
+            q[b] = torch_io.q_device(wb, layer, dev)[0]
+            torch_io.kv_device(wb, layer, "k", out=K[b], device=dev)
+            torch_io.kv_device(wb, layer, "v", out=V[b], device=dev)
+        runs.append(rea.DecodeBatch(q, K, V, lengths, base.G, base.S, base.topk, base.L,
+                                    rope_theta=base.rope_theta))
+        steps.append([rea.Step(q[b:b + 1], K[b], V[b], base.G, base.S, base.topk, base.L, 1,
+                               T=lens[b], rope_theta=base.rope_theta) for b in range(B)])
+        outs.append(torch.empty((B, base.Hq, base.d), dtype=torch.float32, device=dev))
+        if layer % 8 == 7 or layer == n_layers - 1:
+            log(f"[bench] generated + uploaded layer {layer + 1}/{n_layers} "
+                f"({time.perf_counter() - t_gen:.0f} s)")
+    ws = runs[0].workspace()
+    ws1 = steps[0][0].workspace()
+    stream = torch.cuda.current_stream()
+
+    def batched():
+        for li in range(n_layers):
+            runs[li].run(out=outs[li], ws=ws, stream=stream)
+
+    def looped():
+        for li in range(n_layers):
+            for b in range(B):
+                steps[li][b].decode_step(out=outs[li][b:b + 1], ws=ws1, stream=stream)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = timed(batched)
+    ms_loop = timed(looped)
+    keys = sum(max(0, t - base.G - base.L) for t in lens) * base.Hkv * n_layers
+    gbs = keys * base.d * 2 / (ms / 1e3) / 1e9
+    log(f"[bench] batch of {B} at {T} tokens ({'ragged' if args.ragged else 'equal'} lengths), "
+        f"{n_layers} layers: {ms:.3f} ms/step = {B / ms * 1e3:.0f} tokens/s "
+        f"(middle keys at {gbs:.0f} GB/s over the whole step); one sequence at a time: "
+        f"{ms_loop:.3f} ms/step ({ms_loop / ms:.2f}x slower)")
+    print(json.dumps({
+        "metric": "batched decode tokens/s (all layers)", "value": B / (ms / 1e3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": base.name, "layers": n_layers, "batch": B, "context": T,
+                   "lengths": "ragged" if args.ragged else "equal", "q_heads": base.Hq,
+                   "kv_heads": base.Hkv, "head_dim": base.d, "G": base.G, "S": base.S,
+                   "topk": base.topk, "L": base.L},
+        "middle_key_GBps_whole_step": gbs, "ms_per_step_one_sequence_at_a_time": ms_loop,
+        "roofline": None, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +261,11 @@ def main():
     ap.add_argument("--prefill-prompt", type=int, default=0,
                     help="instead: time a chunked prefill over a prompt of this many tokens")
     ap.add_argument("--chunk", type=int, default=512, help="prefill chunk (with --prefill-prompt)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="instead: batched decode of this many sequences (8B shape, 32 layers)")
+    ap.add_argument("--context", type=int, default=32768, help="sequence length (with --batch)")
+    ap.add_argument("--ragged", action="store_true",
+                    help="with --batch: lengths spread over [context/2, context]")
     ap.add_argument("--variant", choices=sorted(VARIANTS), default=None,
                     help="selection variant of the workload (default: one selection per KV "
                          "head over spans of S tokens)")
@@ -185,6 +274,13 @@ def main():
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               f"(the path is measured on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.batch > 0:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        batch_main(args)
+        return
     if args.prefill_prompt > 0:
         import torch
         if not torch.cuda.is_available():
