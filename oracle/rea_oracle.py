@@ -49,6 +49,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
     query-head logits (step 3).  Variant (per_q_head=True): one selection per
     query head with its own logits, its window gathered from its group's KV
     head.  Token-level selection is the special case S = 1.
+  * token segments (token_segments=True): the discussion's InfLLM reply says
+    ReAttention selects from the K cache directly rather than from blocks cut
+    in advance; read as: the k best tokens, each widened to S tokens centred
+    on it, clipped to the middle, overlaps merged.
   * span reduce: max over the span's tokens (step 4); a block of queries sums
     its queries' span maxima.
   * ties: lower span index first (step 5).
@@ -227,6 +231,19 @@ def select_topk(sigma: np.ndarray, k: int, exact_fn=None):
     return sorted(chosen)
 
 
+def widen_merge(sel_tokens, n_mid: int, S: int):
+    """Token-segment selection: every selected token u (middle-relative) is
+    widened to the S tokens [u - (S-1)//2, u - (S-1)//2 + S), clipped to the
+    middle [0, n_mid); the result is the union, ascending."""
+    left = (S - 1) // 2
+    cover = set()
+    for u in sel_tokens:
+        for x in range(u - left, u - left + S):
+            if 0 <= x < n_mid:
+                cover.add(x)
+    return sorted(cover)
+
+
 # --------------------------------------------------------------------------
 # 6-7. window and RoPE
 # --------------------------------------------------------------------------
@@ -272,12 +289,18 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def score_select(q, K, G, S, k, L, block_q=1, return_scores=False, per_q_head=False):
+def score_select(q, K, G, S, k, L, block_q=1, return_scores=False, per_q_head=False,
+                 token_segments=False):
     """Steps 1-5.  q [n_q][Hq][d], K [Hkv][T][d] (any float dtype, upcast to fp64).
 
     Returns sel: list over blocks of list over selection units (KV heads, or
     query heads when per_q_head) of ascending span indices (and the fp64 span
     scores [n_blk][n_units][n_spans] if asked).
+
+    token_segments: the k best single tokens are selected instead (their
+    scores are the token scores, summed over the block's queries), each is
+    widened to a segment of S tokens (widen_merge), and sel holds the union's
+    middle-relative token indices; the scores returned are the token scores.
     """
     q = _f64(q)
     K = _f64(K)
@@ -285,7 +308,7 @@ def score_select(q, K, G, S, k, L, block_q=1, return_scores=False, per_q_head=Fa
     Hkv, T, _ = K.shape
     units = selection_units(Hq, Hkv, per_q_head)
     Gp, Lp, lo, hi = regions(T, G, L)
-    spans = span_list(lo, hi, S)
+    spans = span_list(lo, hi, 1 if token_segments else S)
     n_blk = n_q // block_q
     sel = []
     scores = np.zeros((n_blk, len(units), len(spans)), dtype=np.float64)
@@ -299,19 +322,22 @@ def score_select(q, K, G, S, k, L, block_q=1, return_scores=False, per_q_head=Fa
             else:
                 sig = np.zeros(0)
             scores[b, u] = sig
-            row.append(select_topk(
+            chosen = select_topk(
                 sig, k,
-                lambda j, qb=qb, h=h, qh=qheads: exact_span_score(qb, K[h], qh, spans[j])))
+                lambda j, qb=qb, h=h, qh=qheads: exact_span_score(qb, K[h], qh, spans[j]))
+            row.append(widen_merge(chosen, hi - lo, S) if token_segments else chosen)
         sel.append(row)
     return (sel, scores) if return_scores else sel
 
 
-def gather_rope(q, K, V, sel, G, S, L, block_q=1, theta=500000.0, per_q_head=False):
+def gather_rope(q, K, V, sel, G, S, L, block_q=1, theta=500000.0, per_q_head=False,
+                token_segments=False):
     """Steps 6-7.  Returns (K_win, V_win, q_rot, W, qpos) with
     K_win/V_win lists [n_blk][n_units] of [W][d] fp64 arrays (K rotated, V
     plain), q_rot [n_q][Hq][d] fp64, W [n_blk][n_units], qpos [n_q][n_units]
     window positions; the units are the KV heads, or the query heads when
-    per_q_head (each window is gathered from the unit's KV head)."""
+    per_q_head (each window is gathered from the unit's KV head).  With
+    token_segments, sel holds middle-relative token indices."""
     q = _f64(q)
     K = _f64(K)
     V = _f64(V)
@@ -319,7 +345,7 @@ def gather_rope(q, K, V, sel, G, S, L, block_q=1, theta=500000.0, per_q_head=Fal
     Hkv, T, _ = K.shape
     units = selection_units(Hq, Hkv, per_q_head)
     Gp, Lp, lo, hi = regions(T, G, L)
-    spans = span_list(lo, hi, S)
+    spans = span_list(lo, hi, 1 if token_segments else S)
     n_blk = n_q // block_q
     K_win, V_win = [], []
     W = np.zeros((n_blk, len(units)), dtype=np.int64)
@@ -362,11 +388,13 @@ def window_attend(q_rot, K_win, V_win, qpos, block_q=1, scale=None):
 
 
 def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, return_all=False,
-         per_q_head=False):
+         per_q_head=False, token_segments=False):
     """Steps 1-8 (the fused decode/prefill step).  Returns (out, sel)."""
-    sel = score_select(q, K, G, S, k, L, block_q, per_q_head=per_q_head)
+    sel = score_select(q, K, G, S, k, L, block_q, per_q_head=per_q_head,
+                       token_segments=token_segments)
     K_win, V_win, q_rot, W, qpos = gather_rope(q, K, V, sel, G, S, L, block_q, theta,
-                                               per_q_head=per_q_head)
+                                               per_q_head=per_q_head,
+                                               token_segments=token_segments)
     out = window_attend(q_rot, K_win, V_win, qpos, block_q, scale)
     if return_all:
         return dict(out=out, sel=sel, K_win=K_win, V_win=V_win, q_rot=q_rot, W=W, qpos=qpos)

@@ -20,13 +20,16 @@ def _rot(x, pos, theta):
     return y
 
 
-def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, per_q_head=False):
+def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, per_q_head=False,
+         token_segments=False):
     """q [n_q][Hq][d], K/V [Hkv][T][d] as nested lists of floats.
 
     Returns (out [n_q][Hq][d] floats, sel [n_blk][units] lists, W [n_blk][units]),
     where the units are the KV heads (each scored with its group's summed
     logits) or, with per_q_head, the query heads (each with its own logits
-    against its group's KV head).
+    against its group's KV head).  token_segments: the k best single tokens,
+    each widened to S tokens around it (from u - (S-1)//2), clipped to the
+    middle and joined; sel then lists middle-relative tokens.
     """
     n_q, Hq, d = len(q), len(q[0]), len(q[0][0])
     Hkv, T = len(K), len(K[0])
@@ -34,11 +37,12 @@ def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, per_q_head=
     Gp = min(G, T)
     Lp = min(L, T - Gp)
     lo, hi = Gp, T - Lp
+    width = 1 if token_segments else S
     spans = []
     a = lo
     while a < hi:
-        spans.append((a, min(a + S, hi)))
-        a += S
+        spans.append((a, min(a + width, hi)))
+        a += width
     sc = 1.0 / math.sqrt(d) if scale is None else scale
     out = [[[0.0] * d for _ in range(Hq)] for _ in range(n_q)]
     sel_all, W_all = [], []
@@ -77,6 +81,18 @@ def step(q, K, V, G, S, k, L, block_q=1, theta=500000.0, scale=None, per_q_head=
                 chosen.append(bj)
                 remaining.remove(bj)
             chosen.sort()
+            if token_segments:
+                # walk the tokens in order, extending the current run of the
+                # union or starting a new one
+                runs = []
+                for u in chosen:
+                    a0 = max(u - (S - 1) // 2, 0)
+                    a1 = min(u - (S - 1) // 2 + S, hi - lo)
+                    if runs and a0 <= runs[-1][1]:
+                        runs[-1][1] = max(runs[-1][1], a1)
+                    else:
+                        runs.append([a0, a1])
+                chosen = [x for (r0, r1) in runs for x in range(r0, r1)]
             src = list(range(Gp))
             for j in chosen:
                 src += list(range(spans[j][0], spans[j][1]))

@@ -88,15 +88,17 @@ def check_golden():
         V = K.copy()
         G, S, L, bq = case["G"], case["S"], case["L"], case["block_q"]
         pqh = case.get("per_q_head", False)
+        tseg = case.get("token_segments", False)
         Hkv, T, _ = K.shape
         g = q.shape[1] // Hkv
         for ex in case["expect"]:
             sel, sc = O.score_select(q, K, G, S, ex["k"], L, bq, return_scores=True,
-                                     per_q_head=pqh)
+                                     per_q_head=pqh, token_segments=tseg)
             assert sel == ex["sel"], (case["name"], ex["k"], sel)
             exp_sc = np.array(case["span_scores"], dtype=np.float64)
             assert sc.shape == exp_sc.shape and np.array_equal(sc, exp_sc), (case["name"], sc)
-            Kw, Vw, qr, W, qpos = O.gather_rope(q, K, V, sel, G, S, L, bq, per_q_head=pqh)
+            Kw, Vw, qr, W, qpos = O.gather_rope(q, K, V, sel, G, S, L, bq, per_q_head=pqh,
+                                                token_segments=tseg)
             assert W.tolist() == ex["W"], (case["name"], W)
             assert qpos.tolist() == ex["qpos"], (case["name"], qpos)
             for b in range(len(sel)):
@@ -176,12 +178,19 @@ def check_scalar_twin(seed=4):
         (2, 2, 3, 1, 4, 23, 1, 2, 2, 5, "int"),
         (1, 1, 2, 1, 4, 21, 2, 1, 5, 3, "f32"),      # token level (S = 1)
     ]
-    cases = [(sh, False) for sh in shapes] + [(sh, True) for sh in per_head_shapes]
-    for (n_q, bq, Hq, Hkv, d, T, G, S, k, L, kind), pqh in cases:
+    segment_shapes = [
+        (1, 1, 4, 2, 4, 37, 2, 3, 3, 4, "bf16"),
+        (2, 2, 2, 1, 4, 31, 1, 4, 2, 5, "int"),      # ties, blocks, even width
+        (1, 1, 2, 1, 4, 26, 2, 5, 4, 3, "f32"),      # overlapping and clipped segments
+    ]
+    cases = ([(sh, False, False) for sh in shapes] + [(sh, True, False) for sh in per_head_shapes]
+             + [(sh, False, True) for sh in segment_shapes])
+    for (n_q, bq, Hq, Hkv, d, T, G, S, k, L, kind), pqh, tseg in cases:
         q, K, V = rand_problem(rng, n_q, Hq, Hkv, d, T, kind)
         out_tw, sel_tw, W_tw = scalar_twin.step(q.tolist(), K.tolist(), V.tolist(), G, S, k, L, bq,
-                                                per_q_head=pqh)
-        res = O.step(q, K, V, G, S, k, L, bq, return_all=True, per_q_head=pqh)
+                                                per_q_head=pqh, token_segments=tseg)
+        res = O.step(q, K, V, G, S, k, L, bq, return_all=True, per_q_head=pqh,
+                     token_segments=tseg)
         assert res["sel"] == sel_tw, (res["sel"], sel_tw)
         assert res["W"].tolist() == W_tw
         np.testing.assert_allclose(res["out"], np.array(out_tw), rtol=1e-9, atol=1e-12)
@@ -251,8 +260,37 @@ def check_rope():
     np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-9)
 
 
+def check_token_segments(seed=8):
+    """Token segments of width 1 are token-level span selection; every
+    selected token's segment lies in the union, which holds at most k*S
+    tokens; selecting every token gives full attention."""
+    rng = np.random.default_rng(seed)
+    for (n_q, bq, Hq, Hkv, d, T, G, S, k, L) in [(1, 1, 4, 2, 8, 90, 3, 5, 6, 7),
+                                                (4, 2, 2, 1, 8, 70, 2, 4, 5, 6)]:
+        q, K, V = rand_problem(rng, n_q, Hq, Hkv, d, T)
+        a = O.step(q, K, V, G, 1, k, L, bq, return_all=True, token_segments=True)
+        b = O.step(q, K, V, G, 1, k, L, bq, return_all=True)
+        assert a["sel"] == b["sel"]
+        np.testing.assert_array_equal(a["out"], b["out"])
+        sel_tok = O.score_select(q, K, G, 1, k, L, bq)
+        seg = O.score_select(q, K, G, S, k, L, bq, token_segments=True)
+        n_mid = T - G - L
+        for blk in range(len(seg)):
+            for h in range(Hkv):
+                u = set(seg[blk][h])
+                assert len(u) <= k * S and seg[blk][h] == sorted(u)
+                for t in sel_tok[blk][h]:
+                    lo = t - (S - 1) // 2
+                    assert all(x in u for x in range(max(lo, 0), min(lo + S, n_mid)))
+        out, _ = O.step(q, K, V, G, S, T, L, bq, token_segments=True)
+        pos = np.arange(T)
+        np.testing.assert_allclose(out, sdpa_ref(q, K, V, pos, pos[T - n_q:]), rtol=1e-10,
+                                   atol=1e-12)
+
+
 PINS = [check_golden, check_full_attention, check_k0, check_bruteforce,
-        check_scalar_twin, check_needle, check_rope, check_per_q_head_is_repeated_kv]
+        check_scalar_twin, check_needle, check_rope, check_per_q_head_is_repeated_kv,
+        check_token_segments]
 
 
 # --------------------------------------------------------------------------
@@ -359,6 +397,15 @@ _orig_span_list = O.span_list
 
 
 _orig_units = O.selection_units
+_orig_widen = O.widen_merge
+
+
+def _mut_widen_left_heavy(sel_tokens, n_mid, S):
+    return _orig_widen([u + ((S - 1) // 2) - S // 2 for u in sel_tokens], n_mid, S)
+
+
+def _mut_widen_no_clip(sel_tokens, n_mid, S):
+    return _orig_widen(sel_tokens, n_mid + S, S)
 
 
 def _mut_first_head(q_blk, K_h, qheads, lo, hi):
@@ -440,6 +487,8 @@ MUTATIONS = {
     "gqa_wrong_group": ("token_scores", _mut_wrong_head),
     "per_q_head_kv_by_modulo": ("selection_units", _mut_per_head_kv_modulo),
     "per_q_head_scores_whole_group": ("selection_units", _mut_per_head_sums_group),
+    "segment_extra_token_on_the_left": ("widen_merge", _mut_widen_left_heavy),
+    "segment_not_clipped_to_middle": ("widen_merge", _mut_widen_no_clip),
     "ties_to_higher_index": ("select_topk", _mut_tie_high),
     "spans_in_score_order": ("select_topk", _mut_unsorted),
     "rope_sign_flip": ("rope", _mut_rope_sign),
