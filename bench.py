@@ -35,6 +35,7 @@ SCORE_SRC = os.path.join(ROOT, "top_kv_cache_amd", "csrc", "score.hip")
 VARIANTS = {
     "per_q_head": dict(per_q_head=True),       # one selection per query head
     "token_level": dict(S=1, topk=3840),       # spans of one token, the same token budget
+    "token_segments": dict(token_segments=True),   # 120 best tokens, each widened to 32
 }
 
 
@@ -105,7 +106,7 @@ def cpu_baseline(w, min_seconds=10.0):
             V = synth.to_f32(w.kv(layer, "v", h, h + 1), w.dtype).astype(np.float64)
             t0 = time.perf_counter()
             O.step(q64[:, h * g:(h + 1) * g], K, V, w.G, w.S, w.topk, w.L, w.block_q,
-                   w.rope_theta, per_q_head=w.per_q_head)
+                   w.rope_theta, per_q_head=w.per_q_head, token_segments=w.token_segments)
             total += time.perf_counter() - t0
             del K, V
         layers += 1
@@ -314,7 +315,7 @@ def main():
         K = torch_io.kv_device(w, layer, "k", device=dev)
         V = torch_io.kv_device(w, layer, "v", device=dev)
         steps_l.append(rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta,
-                                per_q_head=w.per_q_head))
+                                per_q_head=w.per_q_head, token_segments=w.token_segments))
         outs.append(torch.empty((w.n_q, w.Hq, w.d), dtype=torch.float32, device=dev))
         if layer % 4 == 3 or layer == n_layers - 1:
             log(f"[bench] generated + uploaded layer {layer + 1}/{n_layers} "
@@ -371,12 +372,14 @@ def main():
     k1_ms = sum(k1) / len(k1)
     if w.block_q == 1:
         # decode: the scoring kernel streams the middle keys once
+        n_scores = (hi - lo) if w.token_segments else w.n_spans
         score_bytes = (keys_per_layer * w.d * (2 if w.dtype == "bf16" else 4)
-                       + w.n_spans * w.H_sel * 8 + w.Hq * w.d * (2 if w.dtype == "bf16" else 4))
+                       + n_scores * w.H_sel * 8 + w.Hq * w.d * (2 if w.dtype == "bf16" else 4))
         achieved = score_bytes / (k1_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(score_bytes),
-                    "kernel": "k_score_decode_heads" if w.per_q_head else "k_score_decode",
+                    "kernel": ("k_score_tokens" if (w.S == 1 or w.token_segments) else
+                               "k_score_heads_lds" if w.per_q_head else "k_score_decode"),
                     "algorithmic_bytes_per_launch": score_bytes,
                     "avg_launch_us": k1_ms * 1e3}
         log(f"[bench] scoring kernel {k1_ms * 1e3:.1f} us/launch = {achieved:.0f} GB/s "
@@ -408,7 +411,8 @@ def main():
         "config": {"workload": w.name, "layers": n_layers, "context": w.T, "batch": 1,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "storage": w.dtype,
                    "G": w.G, "S": w.S, "topk": w.topk, "L": w.L,
-                   "selection": "per query head" if w.per_q_head else "per KV head",
+                   "selection": ("per query head" if w.per_q_head else "per KV head") +
+                                (", token segments" if w.token_segments else ""),
                    "needles_per_kv_head": w.needles, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": None,

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define REA_ABI_VERSION 2
+#define REA_ABI_VERSION 3
 
 typedef enum rea_status {
     REA_OK = 0,
@@ -61,6 +61,11 @@ typedef enum rea_status {
     REA_ELAUNCH = 7,       /* a kernel launch failed (hipGetLastError) */
     REA_EUNSUPPORTED = 8   /* valid arguments outside what this build implements */
 } rea_status;
+
+enum {
+    REA_SELECT_PER_Q_HEAD = 1,
+    REA_SELECT_TOKEN_SEGMENTS = 2
+};
 
 typedef enum rea_dtype {
     REA_BF16 = 0,          /* bfloat16 storage of q, K, V */
@@ -103,11 +108,23 @@ typedef struct rea_problem {
  * selection, the granularity of the discussion's pseudocode (topk over the
  * middle keys' scores).
  *
- * Selection heads (select_per_q_head): 0 selects once per KV head, scoring
- * with the summed logits of the query heads of its group; 1 selects once per
- * query head with its own logits against its group's KV head (the
- * discussion's reply on eviction: selection is redone for each attention
- * head).  H_sel = n_kv_heads or n_q_heads accordingly; every [..][H_sel][..]
+ * Selection flags (select_flags, a bit set):
+ *   REA_SELECT_PER_Q_HEAD      select once per query head with its own
+ *                              logits against its group's KV head (the
+ *                              discussion's reply on eviction: selection is
+ *                              redone for each attention head); without it,
+ *                              once per KV head with the summed logits of the
+ *                              query heads of its group.
+ *   REA_SELECT_TOKEN_SEGMENTS  select the topk best single tokens instead of
+ *                              spans, widen each to the S tokens
+ *                              [u - (S-1)/2, u - (S-1)/2 + S) around it,
+ *                              clipped to the middle, and take the union (the
+ *                              discussion's InfLLM reply: the K cache is
+ *                              selected directly, not cut into blocks in
+ *                              advance).  Then a selection lists up to
+ *                              topk * S middle-relative TOKENS (spans of one
+ *                              token), sizes.n_spans counts tokens and span
+ *                              scores are token scores.  H_sel = n_kv_heads or n_q_heads accordingly; every [..][H_sel][..]
  * array below is indexed by selection head, and selection head u serves query
  * heads [u * Hq / H_sel, (u + 1) * Hq / H_sel) and reads KV head
  * u * n_kv_heads / H_sel.
@@ -124,14 +141,15 @@ typedef struct rea_params {
     int32_t block_q;           /* >= 1, divides n_q */
     double rope_theta;         /* > 0 */
     float softmax_scale;       /* <= 0 selects 1/sqrt(head_dim) */
-    int32_t select_per_q_head; /* 0 (one selection per KV head) or 1 (per query head) */
+    int32_t select_flags;      /* REA_SELECT_* bits, 0 for the default selection */
 } rea_params;
 
 /* Derived sizes and the workspace each entry point needs. */
 typedef struct rea_sizes {
     int64_t n_blocks;          /* n_q / block_q */
     int64_t n_spans;           /* ceil((T - L' - G') / S) */
-    int64_t k_sel;             /* min(topk, n_spans): spans selected per (block, H_sel head) */
+    int64_t k_sel;             /* min(topk, n_spans): spans selected per (block, H_sel head);
+                                  token segments: min(topk * S, middle tokens), an upper bound */
     int64_t W_cap;             /* min(T, G' + k_sel*S + L'): the largest possible window */
     size_t ws_score_select;    /* bytes of workspace rea_score_select needs */
     size_t ws_window_attend;   /* bytes of workspace rea_window_attend needs */
@@ -162,7 +180,10 @@ rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes 
  *              the selected span indices (span j covers middle tokens
  *              [G' + j*S, min(G' + (j+1)*S, T - L'))), strictly ascending,
  *              padded with -1 after n_sel entries.  May be NULL if topk == 0.
- * n_sel        [n_blocks][H_sel] int32 = k_sel.
+ *              Token segments: [n_blocks][H_sel][topk * S], the union's
+ *              middle-relative token indices (token u is cache row G' + u).
+ * n_sel        [n_blocks][H_sel] int32 = k_sel (token segments: the union's
+ *              size, at most k_sel).
  * span_scores  NULL, or [n_blocks][H_sel][n_spans] double: sum over the
  *              block's queries of the span's maximum token score.  Exact for
  *              bf16/fp32 inputs except on the MFMA path (bf16, head_dim 128,

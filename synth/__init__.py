@@ -233,6 +233,7 @@ class Workload:
     needle_noise: float = 0.1
     rope_theta: float = 500000.0
     per_q_head: bool = False  # one selection per query head instead of per KV head
+    token_segments: bool = False  # the topk best tokens, each widened to S tokens
     extra: dict = field(default_factory=dict)
 
     # -- derived sizes ---------------------------------------------------
@@ -244,6 +245,11 @@ class Workload:
     def H_sel(self) -> int:
         """Selection heads: the KV heads, or the query heads when each selects."""
         return self.Hq if self.per_q_head else self.Hkv
+
+    @property
+    def sel_cap(self) -> int:
+        """Entries of one selection: topk spans, or up to topk * S tokens."""
+        return self.topk * self.S if self.token_segments else self.topk
 
     @property
     def g_sel(self) -> int:
@@ -381,7 +387,8 @@ def config(i: int) -> Workload:
 
 def small(name="small", seed=7, dtype="bf16", Hq=4, Hkv=2, d=64, T=700, n_q=1, block_q=1,
           G=4, S=16, topk=5, L=64, needles=1, kv_scaled=False, layers=1,
-          per_q_head=False) -> Workload:
+          per_q_head=False, token_segments=False) -> Workload:
     """A shrunken workload with the same recipe, for quick tests."""
     return Workload(name, seed, dtype, layers, Hq, Hkv, d, T, n_q, block_q, G, S, topk, L,
-                    needles=needles, kv_scaled=kv_scaled, per_q_head=per_q_head)
+                    needles=needles, kv_scaled=kv_scaled, per_q_head=per_q_head,
+                    token_segments=token_segments)

@@ -26,7 +26,7 @@ def device_inputs(w, layer=0, q=None, K=None, V=None):
 def run_library(w, q, K, V, components=True):
     """All four entry points on the device; results copied to host numpy."""
     st = rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta,
-                  per_q_head=w.per_q_head)
+                  per_q_head=w.per_q_head, token_segments=w.token_segments)
     res = {"sizes": st.sizes}
     if components:
         sel, nsel, sc = st.score_select(span_scores=True)
@@ -36,10 +36,11 @@ def run_library(w, q, K, V, components=True):
                    out=out)
     Hs, nb = st.sizes.n_sel_heads, st.sizes.n_blocks
     assert Hs == w.H_sel
-    sel2 = torch.full((nb, Hs, max(w.topk, 1)), -7, dtype=torch.int32, device=q.device)
+    cap = w.sel_cap
+    sel2 = torch.full((nb, Hs, max(cap, 1)), -7, dtype=torch.int32, device=q.device)
     nsel2 = torch.empty((nb, Hs), dtype=torch.int32, device=q.device)
-    res["out_step"] = st.decode_step(sel=sel2 if w.topk > 0 else None, nsel=nsel2)
-    res["sel_step"], res["nsel_step"] = sel2[:, :, :w.topk], nsel2
+    res["out_step"] = st.decode_step(sel=sel2 if cap > 0 else None, nsel=nsel2)
+    res["sel_step"], res["nsel_step"] = sel2[:, :, :cap], nsel2
     torch.cuda.synchronize()
     host = {}
     for k, v in res.items():
@@ -67,9 +68,10 @@ def oracle_head(w, layer, h, q64=None, K_h=None, V_h=None):
     if V_h is None:
         V_h = synth.to_f32(w.kv(layer, "v", hp, hp + 1), w.dtype).astype(np.float64)
     sel, sc = O.score_select(qh, K_h, w.G, w.S, w.topk, w.L, w.block_q, return_scores=True,
-                             per_q_head=w.per_q_head)
+                             per_q_head=w.per_q_head, token_segments=w.token_segments)
     Kw, Vw, qr, W, qpos = O.gather_rope(qh, K_h, V_h, sel, w.G, w.S, w.L, w.block_q,
-                                        w.rope_theta, per_q_head=w.per_q_head)
+                                        w.rope_theta, per_q_head=w.per_q_head,
+                                        token_segments=w.token_segments)
     out = O.window_attend(qr, Kw, Vw, qpos, w.block_q)
     u = h - hp * g if w.per_q_head else 0       # unit within the group's result
     cols = slice(u, u + 1) if w.per_q_head else slice(0, g)
@@ -81,7 +83,7 @@ def mfma_path(w):
     """Blocks of 64 bf16 queries with d 128 are scored on MFMA: their span scores
     are approximations within a proven bound (selection stays exact)."""
     return (w.dtype == "bf16" and w.d == 128 and w.block_q == 64 and w.S % 32 == 0
-            and 0 < w.n_spans <= 4096)
+            and 0 < w.n_spans <= 4096 and not w.token_segments)
 
 
 def fused_path(w):
@@ -89,7 +91,7 @@ def fused_path(w):
     the cache: up to 8 query rows per (block, KV head) on the VALU, or bf16
     d 128 blocks of >= 32 query rows on MFMA."""
     rows = w.block_q * w.g_sel
-    mfma_cache = w.dtype == "bf16" and w.d == 128 and rows >= 32 and w.topk <= 4096
+    mfma_cache = w.dtype == "bf16" and w.d == 128 and rows >= 32 and w.sel_cap <= 4096
     return rows <= 8 or mfma_cache
 
 
@@ -102,7 +104,7 @@ def compare_head(w, gpu, ora, h, check_windows=True):
         got = gpu["sel"][b, h, :ns].tolist() if w.topk > 0 else []
         assert ns == len(exp), (b, h, ns, len(exp))
         assert got == exp, (b, h, sorted(set(got) ^ set(exp))[:10])
-        if w.topk > ns:
+        if w.sel_cap > ns:
             assert np.all(gpu["sel"][b, h, ns:] == -1)
         got_step = gpu["sel_step"][b, h, :ns].tolist() if w.topk > 0 else []
         assert got_step == exp and int(gpu["nsel_step"][b, h]) == ns

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert sorted(rea.ENTRY_POINTS) == syms
-    assert L.rea_abi_version() == 2
+    assert L.rea_abi_version() == 3
     for i, name in enumerate(rea.STATUS):
         assert L.rea_status_string(i).decode() == name
 
@@ -79,7 +79,7 @@ def mutate(**kw):
     (dict(G=-1), rea.STATUS.index("REA_EINVAL")),
     (dict(L=-5), rea.STATUS.index("REA_EINVAL")),
     (dict(block_q=0), rea.STATUS.index("REA_EINVAL")),
-    (dict(select_per_q_head=3), rea.STATUS.index("REA_EINVAL")),
+    (dict(select_flags=4), rea.STATUS.index("REA_EINVAL")),
     (dict(rope_theta=0.0), rea.STATUS.index("REA_EINVAL")),
     (dict(rope_theta=float("inf")), rea.STATUS.index("REA_EINVAL")),
     (dict(softmax_scale=float("nan")), rea.STATUS.index("REA_EINVAL")),
@@ -165,7 +165,7 @@ def test_sizes_per_query_head_selection():
     p, a = good()
     st, s = sizes_status(p, a)
     assert st == 0 and s.n_sel_heads == 8
-    a.select_per_q_head = 1
+    a.select_flags = rea.REA_SELECT_PER_Q_HEAD
     st, s2 = sizes_status(p, a)
     assert st == 0, rea.lib().rea_last_error()
     assert s2.n_sel_heads == 32 and s2.n_spans == s.n_spans and s2.W_cap == s.W_cap
@@ -214,3 +214,15 @@ def test_batched_decode_workspace_and_errors():
     import torch
     if not torch.cuda.is_available():
         assert call() == E("REA_ENODEVICE")
+
+
+def test_sizes_token_segments():
+    p, a = good()
+    a.select_flags = rea.REA_SELECT_TOKEN_SEGMENTS
+    st, s = sizes_status(p, a)
+    assert st == 0, rea.lib().rea_last_error()
+    n_mid = 131072 - 32 - 4096
+    assert s.n_spans == n_mid and s.k_sel == 120 * 32 and s.W_cap == 32 + 120 * 32 + 4096
+    a.select_flags = rea.REA_SELECT_TOKEN_SEGMENTS | rea.REA_SELECT_PER_Q_HEAD
+    st, s2 = sizes_status(p, a)
+    assert st == 0 and s2.n_sel_heads == 32 and s2.ws_decode_step > s.ws_decode_step

@@ -35,6 +35,8 @@ CASES = {
                                  L=32), [1500, 300, 37, 1100]),
     "bf16_d64_g3_partial_spans": (dict(Hq=6, Hkv=2, d=64, T=2000, S=20, topk=9, G=2, L=50),
                                   [2000, 1999, 1013, 77, 52]),
+    "bf16_d128_token_segments": (dict(Hq=8, Hkv=2, d=128, T=2500, S=16, topk=10, G=4, L=64,
+                                      token_segments=True), [2500, 2, 900, 1777]),
     "llama8b_32k": (dict(Hq=32, Hkv=8, d=128, T=32768, S=32, topk=120, G=32, L=4096,
                          needles=4, kv_scaled=True), [32768, 30000, 24577, 8300]),
 }
@@ -52,9 +54,11 @@ def test_batch_matches_oracle_per_sequence(name):
     kw, lens = CASES[name]
     kw = dict(kw)
     pqh = kw.pop("per_q_head", False)
+    tseg = kw.pop("token_segments", False)
     B = len(lens)
     needles = kw.pop("needles", 1)
-    base = synth.small(name=name, seed=300, needles=needles, per_q_head=pqh, **kw)
+    base = synth.small(name=name, seed=300, needles=needles, per_q_head=pqh,
+                       token_segments=tseg, **kw)
     seqs = [dataclasses.replace(base, seed=300 + b, name=f"{name}-{b}") for b in range(B)]
     dev = torch.device("cuda:0")
     dt = torch_io.torch_dtype(base)
@@ -69,9 +73,9 @@ def test_batch_matches_oracle_per_sequence(name):
         V[b, :, lens[b]:] = 1000.0
     lengths = torch.tensor(lens, dtype=torch.int64, device=dev)
     db = rea.DecodeBatch(q, K, V, lengths, base.G, base.S, base.topk, base.L,
-                         rope_theta=base.rope_theta, per_q_head=pqh)
+                         rope_theta=base.rope_theta, per_q_head=pqh, token_segments=tseg)
     Hs = db.sizes.n_sel_heads
-    sel = torch.full((B, Hs, max(base.topk, 1)), -7, dtype=torch.int32, device=dev)
+    sel = torch.full((B, Hs, max(base.sel_cap, 1)), -7, dtype=torch.int32, device=dev)
     nsel = torch.empty((B, Hs), dtype=torch.int32, device=dev)
     log(f"[batch] {name}: B={B} lengths={lens} H_sel={Hs} ws={db.ws_bytes}")
     out = db.run(sel=sel, nsel=nsel)
@@ -85,7 +89,7 @@ def test_batch_matches_oracle_per_sequence(name):
         Kb = _bits_to_f64(K[b, :, :Tb], base.dtype)
         Vb = _bits_to_f64(V[b, :, :Tb], base.dtype)
         ref, rsel = O.step(qb, Kb, Vb, base.G, base.S, base.topk, base.L, 1, base.rope_theta,
-                           per_q_head=pqh)
+                           per_q_head=pqh, token_segments=tseg)
         for u in range(Hs):
             ns = int(nsel_h[b, u])
             assert ns == len(rsel[0][u]), (b, u, ns, len(rsel[0][u]))

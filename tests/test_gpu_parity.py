@@ -69,6 +69,14 @@ SMALL = {
     "pqh_bf16_mfma_blocks": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,
                               L=128, needles=0, per_q_head=True),
     "f32_token_level_S1_g1": S(dtype="f32", Hq=2, Hkv=2, d=128, S=1, topk=100, T=1200, L=50),
+    # token segments: the best tokens, each widened to S tokens
+    "seg_bf16_d64": S(S=8, topk=6, T=700, token_segments=True),
+    "seg_bf16_d128_pqh": S(Hq=8, Hkv=2, d=128, T=2048, S=32, topk=12, L=256, needles=2,
+                           per_q_head=True, token_segments=True),
+    "seg_f32_blocks_S5": S(dtype="f32", Hq=4, Hkv=1, d=64, T=900, n_q=16, block_q=16, S=5,
+                           topk=7, L=40, needles=0, token_segments=True),
+    "seg_bf16_blocks_mfma_attention": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32,
+                                        topk=12, L=128, needles=0, token_segments=True),
 }
 
 
@@ -203,6 +211,8 @@ VARIANTS = {
     "per_q_head": dict(per_q_head=True),
     # token-level selection: spans of one token, the same 3840-token budget
     "token_level": dict(S=1, topk=3840),
+    # the 120 best tokens, each widened to 32 tokens
+    "token_segments": dict(token_segments=True),
 }
 
 
@@ -210,7 +220,8 @@ VARIANTS = {
 def test_config2_variant(variant):
     w = dataclasses.replace(synth.config(2), **VARIANTS[variant])
     w.name = f"{w.name}-{variant}"
-    log(f"[variant] {w.name}: S={w.S} k={w.topk} per_q_head={w.per_q_head}")
+    log(f"[variant] {w.name}: S={w.S} k={w.topk} per_q_head={w.per_q_head} "
+        f"token_segments={w.token_segments}")
     q, K, V = device_inputs(w)
     gpu = run_library(w, q, K, V)
     del K, V

@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librea.so")
 
 REA_BF16, REA_F32 = 0, 1
+REA_SELECT_PER_Q_HEAD, REA_SELECT_TOKEN_SEGMENTS = 1, 2
 STATUS = ["REA_OK", "REA_EINVAL", "REA_ESHAPE", "REA_EDTYPE", "REA_EALIGN",
           "REA_EWORKSPACE", "REA_ENODEVICE", "REA_ELAUNCH", "REA_EUNSUPPORTED"]
 ENTRY_POINTS = ["rea_abi_version", "rea_status_string", "rea_last_error", "rea_query_sizes",
@@ -36,7 +37,7 @@ class Params(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("G", ctypes.c_int32), ("S", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("L", ctypes.c_int32), ("block_q", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("select_per_q_head", ctypes.c_int32)]
+                ("select_flags", ctypes.c_int32)]
 
 
 class Sizes(ctypes.Structure):
@@ -101,7 +102,7 @@ def lib():
     L.rea_decode_batch.restype = ctypes.c_int
     L.rea_decode_batch.argtypes = [P, A, ctypes.c_int32, vp, ctypes.c_int64, vp, i32p, i32p, vp,
                                    ctypes.c_size_t, vp]
-    if L.rea_abi_version() != 2:
+    if L.rea_abi_version() != 3:
         raise ImportError("librea.so ABI version mismatch")
     _lib = L
     return L
@@ -121,9 +122,10 @@ def problem(q_ptr, k_ptr, v_ptr, *, dtype, n_q, Hq, Hkv, d, T, stride_head, stri
 
 
 def params(G, S, topk, L, block_q=1, rope_theta=500000.0, softmax_scale=0.0,
-           per_q_head=False) -> Params:
-    return Params(ctypes.sizeof(Params), G, S, topk, L, block_q, rope_theta, softmax_scale,
-                  1 if per_q_head else 0)
+           per_q_head=False, token_segments=False) -> Params:
+    flags = (REA_SELECT_PER_Q_HEAD if per_q_head else 0) | \
+        (REA_SELECT_TOKEN_SEGMENTS if token_segments else 0)
+    return Params(ctypes.sizeof(Params), G, S, topk, L, block_q, rope_theta, softmax_scale, flags)
 
 
 def prefill_plan(p: Problem, a: Params, chunk: int):
@@ -198,11 +200,14 @@ class Step:
     """One layer's call configuration: problem + hyperparameters + sizes."""
 
     def __init__(self, q, k, v, G, S, topk, L, block_q=1, T=None, rope_theta=500000.0,
-                 softmax_scale=0.0, per_q_head=False):
+                 softmax_scale=0.0, per_q_head=False, token_segments=False):
         self.q, self.k, self.v = q, k, v
         self.prob = problem_from_tensors(q, k, v, T)
-        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale, per_q_head)
+        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale, per_q_head,
+                          token_segments)
         self.sizes = query_sizes(self.prob, self.par)
+        # entries per selection: topk spans, or up to topk * S tokens with token segments
+        self.sel_cap = topk * S if token_segments else topk
         self.device = q.device
 
     @property
@@ -215,7 +220,7 @@ class Step:
     def score_select(self, span_scores=False, stream=None):
         torch = _torch()
         n_q, Hq, Hkv, d = self.shape
-        nb, topk = self.sizes.n_blocks, self.par.topk
+        nb, topk = self.sizes.n_blocks, self.sel_cap
         sel = torch.empty((nb, Hkv, max(topk, 1)), dtype=torch.int32, device=self.device)
         nsel = torch.empty((nb, Hkv), dtype=torch.int32, device=self.device)
         sc = (torch.empty((nb, Hkv, max(self.sizes.n_spans, 1)), dtype=torch.float64,
@@ -277,10 +282,11 @@ class Prefill:
     query) against the cache k, v of the same T tokens."""
 
     def __init__(self, q, k, v, G, S, topk, L, block_q, chunk, rope_theta=500000.0,
-                 softmax_scale=0.0, per_q_head=False):
+                 softmax_scale=0.0, per_q_head=False, token_segments=False):
         self.q, self.k, self.v = q, k, v
         self.prob = problem_from_tensors(q, k, v)
-        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale, per_q_head)
+        self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale, per_q_head,
+                          token_segments)
         self.chunk = chunk
         self.plan, self.ws_bytes = prefill_plan(self.prob, self.par, chunk)
         self.device = q.device
@@ -306,7 +312,7 @@ class DecodeBatch:
     stride), lengths a device int64 tensor [B] of valid tokens per sequence."""
 
     def __init__(self, q, k, v, lengths, G, S, topk, L, rope_theta=500000.0,
-                 softmax_scale=0.0, per_q_head=False):
+                 softmax_scale=0.0, per_q_head=False, token_segments=False):
         torch = _torch()
         if k.dim() != 4 or v.shape != k.shape or k.stride() != v.stride() or k.stride(3) != 1:
             raise ValueError("k and v must be [B][Hkv][T_cap][d] views with channel stride 1")
@@ -319,7 +325,7 @@ class DecodeBatch:
         # one sequence's problem: q viewed as [1][Hq][d] of sequence 0
         self.prob = problem_from_tensors(q[:1], k[0], v[0])
         self.kv_stride_seq = k.stride(0)
-        self.par = params(G, S, topk, L, 1, rope_theta, softmax_scale, per_q_head)
+        self.par = params(G, S, topk, L, 1, rope_theta, softmax_scale, per_q_head, token_segments)
         self.sizes = query_sizes(self.prob, self.par)
         ws = ctypes.c_size_t()
         _check(lib().rea_decode_batch_workspace(ctypes.byref(self.prob), ctypes.byref(self.par),

@@ -56,8 +56,11 @@ rea_status make_geom(const rea_problem *p, const rea_params *a, rea::Geom *g) {
     if (a->S < 1) return fail(REA_EINVAL, "span size S %d < 1", a->S);
     if (a->topk < 0) return fail(REA_EINVAL, "topk %d < 0", a->topk);
     if (a->block_q < 1) return fail(REA_EINVAL, "block_q %d < 1", a->block_q);
-    if (a->select_per_q_head != 0 && a->select_per_q_head != 1)
-        return fail(REA_EINVAL, "select_per_q_head %d is neither 0 nor 1", a->select_per_q_head);
+    if (a->select_flags & ~(REA_SELECT_PER_Q_HEAD | REA_SELECT_TOKEN_SEGMENTS))
+        return fail(REA_EINVAL, "select_flags 0x%x has unknown bits", a->select_flags);
+    const bool segs = (a->select_flags & REA_SELECT_TOKEN_SEGMENTS) != 0;
+    if (segs && (int64_t)a->topk * a->S >= ((int64_t)1 << 30))
+        return fail(REA_EUNSUPPORTED, "topk * S too large for token segments");
     if (!(a->rope_theta > 0.0) || !isfinite(a->rope_theta))
         return fail(REA_EINVAL, "rope_theta must be finite and > 0");
     if (!isfinite(a->softmax_scale)) return fail(REA_EINVAL, "softmax_scale is not finite");
@@ -80,7 +83,7 @@ rea_status make_geom(const rea_problem *p, const rea_params *a, rea::Geom *g) {
     g->esize = esize;
     g->n_q = p->n_q;
     g->Hq = p->n_q_heads;
-    if (a->select_per_q_head) {     // every query head is its own selection head
+    if (a->select_flags & REA_SELECT_PER_Q_HEAD) {   // every query head selects
         g->Hkv = p->n_q_heads;
         g->g = 1;
         g->rep = p->n_q_heads / p->n_kv_heads;
@@ -96,14 +99,18 @@ rea_status make_geom(const rea_problem *p, const rea_params *a, rea::Geom *g) {
     g->mid_lo = g->Gp;
     g->mid_hi = p->T - g->Lp;
     const int64_t n_mid = g->mid_hi - g->mid_lo;
-    g->n_spans = (n_mid + a->S - 1) / a->S;
-    g->S = a->S;
-    g->topk = a->topk;
+    // token segments: kernels see one-token spans, a selection holds up to
+    // topk * S tokens
+    g->seg = segs ? a->S : 0;
+    g->k_tok = a->topk;
+    g->S = segs ? 1 : a->S;
+    g->topk = segs ? a->topk * a->S : a->topk;
+    g->n_spans = (n_mid + g->S - 1) / g->S;
     g->block_q = a->block_q;
     g->n_blk = p->n_q / a->block_q;
-    g->k_sel = (int)(a->topk < g->n_spans ? a->topk : g->n_spans);
-    g->last_len = g->n_spans > 0 ? (int)(n_mid - (g->n_spans - 1) * a->S) : 0;
-    int64_t wc = g->Gp + (int64_t)g->k_sel * a->S + g->Lp;
+    g->k_sel = (int)(g->topk < g->n_spans ? g->topk : g->n_spans);
+    g->last_len = g->n_spans > 0 ? (int)(n_mid - (g->n_spans - 1) * g->S) : 0;
+    int64_t wc = g->Gp + (int64_t)g->k_sel * g->S + g->Lp;
     g->W_cap = wc < p->T ? wc : p->T;
     g->sh = p->kv_stride_head;
     g->st = p->kv_stride_tok;
@@ -151,14 +158,22 @@ size_t select_aux_bytes(const rea::Geom &g) {
     return rea::mfma_block_path(g) ? align256(rea::mfma_ws_bytes(g)) : align256(group_max_bytes(g));
 }
 
+// token segments: the best tokens before widening, [n_blk][Hkv][k_tok] + counts
+size_t seg_tok_bytes(const rea::Geom &g) {
+    if (!g.seg) return 0;
+    return align256((size_t)g.n_blk * g.Hkv * g.k_tok * sizeof(int32_t)) +
+           align256((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+}
+
 size_t score_ws_bytes(const rea::Geom &g, bool caller_scores) {
-    return (caller_scores ? 0 : align256(score_scores_bytes(g))) + select_aux_bytes(g);
+    return (caller_scores ? 0 : align256(score_scores_bytes(g))) + select_aux_bytes(g) +
+           seg_tok_bytes(g);
 }
 
 // Steps 1a+1b on whichever path fits the problem.
 hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, double *scores,
-                         void *aux, int32_t *sel, int32_t *n_sel, int num_cu, hipStream_t s,
-                         const rea_timing *timing) {
+                         void *aux, void *seg_ws, int32_t *sel, int32_t *n_sel, int num_cu,
+                         hipStream_t s, const rea_timing *timing) {
     if (rea::mfma_block_path(g))
         return rea::launch_score_select_mfma(g, q, k, scores, sel, n_sel, aux, num_cu, s,
                                              timing ? (hipEvent_t)timing->score_begin : nullptr,
@@ -173,13 +188,24 @@ hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, doubl
         e = hipEventRecord((hipEvent_t)timing->score_end, s);
         if (e != hipSuccess) return e;
     }
-    return rea::launch_topk(g, scores, (const double *)aux, sel, n_sel, s);
+    if (!g.seg) return rea::launch_topk(g, scores, (const double *)aux, sel, n_sel, s);
+    // token segments: the k_tok best tokens, then their widened union
+    rea::Geom gt = g;
+    gt.topk = g.k_tok;
+    gt.k_sel = g.k_tok < g.n_spans ? g.k_tok : (int)g.n_spans;
+    Carve c{(char *)seg_ws, 0};
+    int32_t *sel_tok = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.k_tok * sizeof(int32_t));
+    int32_t *nsel_tok = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
+    e = rea::launch_topk(gt, scores, (const double *)aux, sel_tok, nsel_tok, s);
+    if (e != hipSuccess) return e;
+    return rea::launch_widen(g, sel_tok, nsel_tok, sel, n_sel, s);
 }
 
 size_t decode_ws_bytes(const rea::Geom &g) {
     Carve c{nullptr, 0};
     c.take<double>(score_scores_bytes(g));
     c.take<char>(select_aux_bytes(g));
+    c.take<char>(seg_tok_bytes(g));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     if (rea::fused_decode_path(g)) {
@@ -302,7 +328,9 @@ rea_status rea_score_select(const rea_problem *p, const rea_params *a, int32_t *
     Carve c{(char *)ws, 0};
     double *scores = span_scores ? span_scores : c.take<double>(score_scores_bytes(g));
     void *aux = c.take<char>(select_aux_bytes(g));
-    return launched(launch_select(g, p->q, p->k, scores, aux, sel, n_sel, num_cu, s, nullptr),
+    void *seg_ws = c.take<char>(seg_tok_bytes(g));
+    return launched(launch_select(g, p->q, p->k, scores, aux, seg_ws, sel, n_sel, num_cu, s,
+                                  nullptr),
                     "score_select");
 }
 
@@ -362,13 +390,14 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
     Carve c{(char *)ws, 0};
     double *scores = c.take<double>(score_scores_bytes(g));
     void *aux = c.take<char>(select_aux_bytes(g));
+    void *seg_ws = c.take<char>(seg_tok_bytes(g));
     int32_t *ws_sel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     int32_t *ws_nsel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     int32_t *use_sel = sel ? sel : ws_sel;
     int32_t *use_nsel = n_sel ? n_sel : ws_nsel;
     if (g.topk == 0) use_sel = sel;   // may be NULL: nothing is selected
     hipStream_t s = (hipStream_t)stream;
-    if ((st = launched(launch_select(g, p->q, p->k, scores, aux, use_sel, use_nsel, num_cu, s,
+    if ((st = launched(launch_select(g, p->q, p->k, scores, aux, seg_ws, use_sel, use_nsel, num_cu, s,
                                      timing),
                        "score_select")) != REA_OK)
         return st;
@@ -575,13 +604,14 @@ rea_status rea_decode_batch(const rea_problem *p, const rea_params *a, int32_t b
     Carve c{(char *)ws, 0};
     double *scores = c.take<double>(score_scores_bytes(g));
     void *aux = c.take<char>(select_aux_bytes(g));
+    void *seg_ws = c.take<char>(seg_tok_bytes(g));
     int32_t *ws_sel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     int32_t *ws_nsel = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     int32_t *use_sel = sel ? sel : ws_sel;
     int32_t *use_nsel = n_sel ? n_sel : ws_nsel;
     if (g.topk == 0) use_sel = sel;
     hipStream_t s = (hipStream_t)stream;
-    if ((st = launched(launch_select(g, p->q, p->k, scores, aux, use_sel, use_nsel, num_cu, s,
+    if ((st = launched(launch_select(g, p->q, p->k, scores, aux, seg_ws, use_sel, use_nsel, num_cu, s,
                                      nullptr),
                        "batched score_select")) != REA_OK)
         return st;

@@ -21,6 +21,10 @@ struct Geom {
     int64_t n_spans;    // ceil((mid_hi - mid_lo) / S)
     int S, topk, block_q, n_blk;
     int k_sel;          // min(topk, n_spans)
+    // token segments: the kernels see spans of one token (S = 1); k_tok best
+    // tokens are picked and each is widened to seg tokens; topk (= k_tok *
+    // seg) is then the capacity of a selection.  seg = 0: span selection.
+    int seg, k_tok;
     int last_len;       // length of span n_spans-1 (S unless the middle is ragged)
     int64_t W_cap;      // min(T, G' + k_sel*S + L')
     int64_t sh, st;     // K/V strides (elements) per head / per token
@@ -85,6 +89,12 @@ constexpr int kMaxHalfDim = 64;   // head_dim <= 128
 int64_t score_groups(const Geom &g);
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
                         double *group_max, int num_cu, hipStream_t s);
+
+// Token segments: widen each selected token (sel_tok [n_blk*Hkv][k_tok],
+// middle-relative, ascending) to g.seg tokens and write the union, ascending,
+// to sel [n_blk*Hkv][g.topk] and its size to n_sel.
+hipError_t launch_widen(const Geom &g, const int32_t *sel_tok, const int32_t *nsel_tok,
+                        int32_t *sel, int32_t *n_sel, hipStream_t s);
 
 // Step 1b: top-k per (block, KV head) from the span scores and group maxima.
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,

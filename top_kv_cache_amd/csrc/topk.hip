@@ -830,7 +830,103 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
     }
 }
 
+// Token segments: one workgroup per (block, selection head).  Selected token
+// u_i (ascending, middle-relative) covers [a_i, b_i) = [u_i - (seg-1)/2,
+// u_i - (seg-1)/2 + seg) clipped to the middle; both ends are non-decreasing
+// in i, so token i adds [max(a_i, b_{i-1}), b_i) to the union, and an
+// exclusive scan of those lengths places every token of the union in order.
+constexpr int kWThreads = 256;
+
+struct WidenArgs {
+    const int32_t *sel_tok, *nsel_tok;
+    int32_t *sel, *n_sel;
+    int k_tok, cap, seg, Hkv;
+    const int64_t *lens;
+    int hps;
+    int64_t T, G, L;
+};
+
+__global__ __launch_bounds__(kWThreads) void k_widen(WidenArgs a) {
+    __shared__ uint32_t red[kWThreads / 64 + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % a.Hkv);
+    int64_t T = a.T;
+    if (a.lens) {
+        T = a.lens[h / a.hps];
+        T = T < 1 ? 1 : (T > a.T ? a.T : T);
+    }
+    const SeqGeom sg = seq_geom(T, a.G, a.L, 1);
+    const int64_t n_mid = sg.n_spans;
+    const int kk = a.nsel_tok[bh];
+    const int32_t *tok = a.sel_tok + bh * a.k_tok;
+    int32_t *out = a.sel ? a.sel + bh * a.cap : nullptr;
+    const int left = (a.seg - 1) / 2;
+    uint32_t written = 0;
+    for (int base = 0; base < kk; base += kWThreads) {
+        const int i = base + tid;
+        int64_t lo = 0, hi = 0;
+        if (i < kk) {
+            const int64_t u = tok[i];
+            int64_t a0 = u - left, b0 = u - left + a.seg;
+            a0 = a0 < 0 ? 0 : a0;
+            b0 = b0 > n_mid ? n_mid : b0;
+            int64_t prev_b = -1;
+            if (i > 0) {
+                prev_b = (int64_t)tok[i - 1] - left + a.seg;
+                prev_b = prev_b > n_mid ? n_mid : prev_b;
+            }
+            lo = a0 > prev_b ? a0 : prev_b;
+            hi = b0;
+        }
+        const uint32_t len = hi > lo ? (uint32_t)(hi - lo) : 0u;
+        // exclusive scan of len in thread order
+        uint32_t x = len;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) red[wave] = x;
+        __syncthreads();
+        uint32_t off = 0, tot = 0;
+        for (int w = 0; w < kWThreads / 64; ++w) {
+            off += w < wave ? red[w] : 0u;
+            tot += red[w];
+        }
+        const uint32_t pos = written + off + x - len;
+        if (out)
+            for (uint32_t e = 0; e < len; ++e)
+                if (pos + e < (uint32_t)a.cap) out[pos + e] = (int32_t)(lo + e);
+        written += tot;
+        __syncthreads();
+    }
+    if (out)
+        for (int64_t i = (int64_t)written + tid; i < a.cap; i += kWThreads) out[i] = -1;
+    if (tid == 0) a.n_sel[bh] = (int32_t)(written < (uint32_t)a.cap ? written : (uint32_t)a.cap);
+}
+
 }  // namespace
+
+hipError_t launch_widen(const Geom &g, const int32_t *sel_tok, const int32_t *nsel_tok,
+                        int32_t *sel, int32_t *n_sel, hipStream_t s) {
+    WidenArgs a;
+    a.sel_tok = sel_tok;
+    a.nsel_tok = nsel_tok;
+    a.sel = sel;
+    a.n_sel = n_sel;
+    a.k_tok = g.k_tok;
+    a.cap = g.topk;
+    a.seg = g.seg;
+    a.Hkv = g.Hkv;
+    a.lens = g.lens;
+    a.hps = g.hps;
+    a.T = g.T;
+    a.G = g.G;
+    a.L = g.L;
+    hipLaunchKernelGGL(k_widen, dim3(g.n_blk * g.Hkv), dim3(kWThreads), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
                        int32_t *sel, int32_t *n_sel, hipStream_t s) {
