@@ -66,6 +66,11 @@ struct MAttnArgs {
     int64_t W_cap;
     int QR, Hq, Hkv, g, n_q, block_q, n_rg, rep;
     float scale_log2;       // softmax scale * log2(e)
+    // key-tile splits (cache source, small grids): split sp of a workgroup's
+    // tiles writes unnormalised partials, merged by k_attend_merge
+    int n_split;
+    float *part_o;          // [units][n_split][kRowsWG][D]
+    float2 *part_ml;        // [units][n_split][kRowsWG]: running max, sum
 };
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -111,8 +116,10 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
     __shared__ __align__(16) uint16_t vt[2][kD][kVPad];
     __shared__ int32_t ssel[kCache ? kSelCap : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rg = blockIdx.x % a.n_rg;
-    const int bh = blockIdx.x / a.n_rg;
+    const int sp = blockIdx.x % a.n_split;
+    const int unit = blockIdx.x / a.n_split;
+    const int rg = unit % a.n_rg;
+    const int bh = unit / a.n_rg;
     const int b = bh / a.Hkv, h = bh % a.Hkv;
     const int n = lane & 31, hb = lane >> 5;
     int64_t Wbh, sel_len = 0;
@@ -178,7 +185,10 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
     if (rmax > a.QR - 1) rmax = a.QR - 1;
     int64_t kend = Wbh - a.n_q + (int64_t)b * a.block_q + rmax / a.g + 1;
     if (kend > Wbh) kend = Wbh;
-    const int64_t n_tiles = (kend + kKT - 1) / kKT;
+    const int64_t n_tiles_all = (kend + kKT - 1) / kKT;
+    // this split's tiles
+    const int64_t it0 = n_tiles_all * sp / a.n_split;
+    const int64_t it1 = n_tiles_all * (sp + 1) / a.n_split;
 
     // staging (512 threads, 32 rows).  K, window: thread -> key row tid/16,
     // channels (tid%16)*8 .. +8.  K, cache: thread -> key row tid/16, channel
@@ -284,14 +294,14 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
 
     int buf = 0;
     if (kCache) __syncthreads();        // ssel visible before the first row lookup
-    if (n_tiles > 0) {
-        load_tile(0);
+    if (it1 > it0) {
+        load_tile(it0 * kKT);
         store_tile(0);
     }
     __syncthreads();
-    for (int64_t it = 0; it < n_tiles; ++it) {
+    for (int64_t it = it0; it < it1; ++it) {
         const int64_t w0 = it * kKT;
-        const bool more = it + 1 < n_tiles;
+        const bool more = it + 1 < it1;
         if (more) load_tile(w0 + kKT);
 
         // S^T tile: rows = keys (A = K'), cols = queries (B = Q'^T)
@@ -384,6 +394,21 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
         buf ^= 1;
     }
 
+    if (a.n_split > 1) {
+        // unnormalised partial of this split (rows past QR are never merged)
+        const int64_t prow = ((int64_t)unit * a.n_split + sp) * kRowsWG + wave * 32 + n;
+        float *po = a.part_o + prow * kD;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int aa = 0; aa < 4; ++aa) {
+                const int c = t * 32 + 8 * aa + 4 * hb;
+                *(float4 *)(po + c) = make_float4(o[t][4 * aa], o[t][4 * aa + 1], o[t][4 * aa + 2],
+                                                  o[t][4 * aa + 3]);
+            }
+        if (hb == 0) a.part_ml[prow] = make_float2(m_run, l_run);
+        return;
+    }
     if (valid_q) {
         const float inv = 1.f / l_run;
         float *orow = a.out + (qi * a.Hq + hq) * kD;
@@ -396,6 +421,43 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
                                                     o[t][4 * aa + 2] * inv, o[t][4 * aa + 3] * inv);
             }
     }
+}
+
+// Merge of the key-tile splits: one thread per (query row, 4 channels), 8 rows
+// per workgroup; weights 2^(m_s - M) as in the online softmax.
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void k_attend_merge(MAttnArgs a) {
+    const int tid = threadIdx.x;
+    const int per_unit = kRowsWG / 8;
+    const int unit = blockIdx.x / per_unit;
+    const int r = (blockIdx.x % per_unit) * 8 + tid / 32;   // row within the workgroup's 256
+    const int cq = tid % 32;
+    const int rg = unit % a.n_rg, bh = unit / a.n_rg;
+    const int b = bh / a.Hkv, h = bh % a.Hkv;
+    const int rr = rg * kRowsWG + r;
+    if (rr >= a.QR) return;
+    float M = -INFINITY, L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < a.n_split; ++s) {
+        const int64_t prow = ((int64_t)unit * a.n_split + s) * kRowsWG + r;
+        const float2 ml = a.part_ml[prow];
+        const float4 x = *(const float4 *)(a.part_o + prow * kD + cq * 4);
+        const float mn = fmaxf(M, ml.x);
+        if (mn == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f(M - mn), fo = __builtin_amdgcn_exp2f(ml.x - mn);
+        L = L * f + ml.y * fo;
+        A.x = A.x * f + x.x * fo;
+        A.y = A.y * f + x.y * fo;
+        A.z = A.z * f + x.z * fo;
+        A.w = A.w * f + x.w * fo;
+        M = mn;
+    }
+    const float inv = 1.f / L;
+    const int64_t qi = (int64_t)b * a.block_q + rr / a.g;
+    const int hq = h * a.g + rr % a.g;
+    *(float4 *)(a.out + (qi * a.Hq + hq) * kD + cq * 4) =
+        make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
 }
 
 // (cos, sin) of w * theta_c for every window position w < W_cap and channel
@@ -425,8 +487,40 @@ bool mfma_attend_path(const Geom &g) {
 
 bool mfma_cache_attend_path(const Geom &g) { return mfma_attend_path(g) && g.topk <= kSelCap; }
 
+namespace {
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t attend_units(const Geom &g) {
+    const int QR = g.block_q * g.g;
+    return (int64_t)g.n_blk * g.Hkv * ((QR + kRowsWG - 1) / kRowsWG);
+}
+
+// Key-tile splits of the cache-source attention: enough workgroups for every
+// CU (one 512-thread workgroup per CU), at least 8 key tiles per split.
+int attend_splits(const Geom &g) {
+    const int64_t units = attend_units(g);
+    if (units >= 256) return 1;
+    int64_t ns = (256 + units - 1) / units;
+    const int64_t tiles = (g.W_cap + kKT - 1) / kKT;
+    const int64_t by_tiles = tiles / 8 > 1 ? tiles / 8 : 1;
+    if (ns > by_tiles) ns = by_tiles;
+    if (ns > 16) ns = 16;
+    return (int)ns;
+}
+
+size_t rope_bytes(const Geom &g) { return (size_t)g.W_cap * (g.d / 2) * sizeof(float2); }
+
+}  // namespace
+
 size_t rope_table_bytes(const Geom &g) {
-    return (size_t)g.W_cap * (g.d / 2) * sizeof(float2);
+    size_t b = al256(rope_bytes(g));
+    const int ns = attend_splits(g);
+    if (ns > 1) {
+        const size_t rows = (size_t)attend_units(g) * ns * kRowsWG;
+        b += al256(rows * kD * sizeof(float)) + al256(rows * sizeof(float2));
+    }
+    return b;
 }
 
 hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_win,
@@ -448,6 +542,7 @@ hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_
     a.block_q = g.block_q;
     a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
     a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
+    a.n_split = 1;
     hipLaunchKernelGGL(k_attend_mfma<false>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(kAThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -494,7 +589,20 @@ hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k,
     a.block_q = g.block_q;
     a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
     a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
-    hipLaunchKernelGGL(k_attend_mfma<true>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(kAThreads), 0, s, a);
+    a.n_split = attend_splits(g);
+    const int64_t units = (int64_t)g.n_blk * g.Hkv * a.n_rg;
+    if (a.n_split > 1) {
+        char *p = (char *)ws + al256(rope_bytes(g));
+        const size_t rows = (size_t)units * a.n_split * kRowsWG;
+        a.part_o = (float *)p;
+        a.part_ml = (float2 *)(p + al256(rows * kD * sizeof(float)));
+    }
+    hipLaunchKernelGGL(k_attend_mfma<true>, dim3((unsigned)(units * a.n_split)), dim3(kAThreads),
+                       0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.n_split == 1) return e;
+    hipLaunchKernelGGL(k_attend_merge, dim3((unsigned)(units * (kRowsWG / 8))),
+                       dim3(kMergeThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -126,7 +126,8 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
 
 // Steps 2-4 for query blocks of at least 32 rows inside rea_decode_step: the
 // MFMA attention reads the window rows from the cache through the selection.
-// ws holds rope_table_bytes(g).
+// ws holds rope_table_bytes(g): the RoPE table and, for grids too small to fill the
+// GPU, the partials of the key-tile splits.
 bool mfma_cache_attend_path(const Geom &g);
 size_t rope_table_bytes(const Geom &g);
 hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k, const void *v,

@@ -58,7 +58,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// k_qprep: grid (n_blk, Hkv), 128 threads (one per channel)
+// k_qprep: grid (n_blk, Hkv), 256 threads: each wave takes every 4th query of
+// the block, a lane two channels (c and c + 64); the block's bound E_b is the
+// sum of the per-query bounds, added in query order by one thread.
 // ---------------------------------------------------------------------------
 struct PrepArgs {
     const uint16_t *q;      // [n_q][Hq][D]
@@ -68,44 +70,67 @@ struct PrepArgs {
     int Hq, Hkv, g, n_q;
 };
 
-__global__ __launch_bounds__(kD) void k_qprep(PrepArgs a) {
-    __shared__ double red[kD / 64][2];
-    __shared__ double esum;
-    const int b = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
-    const int lane = c & 63, wave = c >> 6;
-    if (c == 0) esum = 0.0;
-    __syncthreads();
-    for (int il = 0; il < kQB; ++il) {
+constexpr int kPrepThreads = 256;
+
+__global__ __launch_bounds__(kPrepThreads) void k_qprep(PrepArgs a) {
+    __shared__ double e_q[kQB];
+    const int b = blockIdx.x, h = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int kWavesP = kPrepThreads / 64;
+    constexpr int QPW = kQB / kWavesP;                 // queries per wave (16)
+    // group sums: per query head of the group, every load of the wave's
+    // queries is issued before any is added
+    double s[QPW][2];
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) s[u][0] = s[u][1] = 0.0;
+    for (int gg = 0; gg < a.g; ++gg) {
+        uint16_t raw[QPW][2];
+#pragma unroll
+        for (int u = 0; u < QPW; ++u) {
+            const int64_t i = (int64_t)b * kQB + wave + u * kWavesP;
+            const uint16_t *qr = a.q + (i * a.Hq + h * a.g + gg) * kD + lane;
+            raw[u][0] = qr[0];
+            raw[u][1] = qr[64];
+        }
+#pragma unroll
+        for (int u = 0; u < QPW; ++u) {
+            s[u][0] += bf16_to_f64(raw[u][0]);
+            s[u][1] += bf16_to_f64(raw[u][1]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+        const int il = wave + u * kWavesP;
         const int64_t i = (int64_t)b * kQB + il;
-        double s = 0.0;
-        for (int gg = 0; gg < a.g; ++gg) s += bf16_to_f64(a.q[(i * a.Hq + h * a.g + gg) * kD + c]);
-        const uint16_t hi = f32_to_bf16((float)s);
-        const double hid = bf16_to_f64(hi);
-        const uint16_t lo = f32_to_bf16((float)(s - hid));
-        const double lod = bf16_to_f64(lo);
-        const double r = s - hid - lod;
         const int64_t row = (int64_t)h * a.n_q + i;
-        a.qhl[row * 256 + c] = hi;
-        a.qhl[row * 256 + kD + c] = lo;
-        a.qeff[row * kD + c] = s;
-        double n1 = (fabs(hid) + fabs(lod)) * (fabs(hid) + fabs(lod));
-        double n2 = r * r;
+        double n1 = 0.0, n2 = 0.0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int c = lane + half * 64;
+            const double sv = s[u][half];
+            const uint16_t hi = f32_to_bf16((float)sv);
+            const double hid = bf16_to_f64(hi);
+            const uint16_t lo = f32_to_bf16((float)(sv - hid));
+            const double lod = bf16_to_f64(lo);
+            const double r = sv - hid - lod;
+            a.qhl[row * 256 + c] = hi;
+            a.qhl[row * 256 + kD + c] = lo;
+            a.qeff[row * kD + c] = sv;
+            n1 += (fabs(hid) + fabs(lod)) * (fabs(hid) + fabs(lod));
+            n2 += r * r;
+        }
         for (int o = 32; o > 0; o >>= 1) {
             n1 += __shfl_xor(n1, o);
             n2 += __shfl_xor(n2, o);
         }
-        if (lane == 0) {
-            red[wave][0] = n1;
-            red[wave][1] = n2;
-        }
-        __syncthreads();
-        if (c == 0) {
-            const double s1 = red[0][0] + red[1][0], s2 = red[0][1] + red[1][1];
-            esum += (kGammaMfma * sqrt(s1) + sqrt(s2)) * (1.0 + 1e-12);
-        }
-        __syncthreads();
+        if (lane == 0) e_q[il] = (kGammaMfma * sqrt(n1) + sqrt(n2)) * (1.0 + 1e-12);
     }
-    if (c == 0) a.E[(int64_t)b * a.Hkv + h] = esum * (1.0 + 1e-9);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double esum = 0.0;
+        for (int il = 0; il < kQB; ++il) esum += e_q[il];
+        a.E[(int64_t)b * a.Hkv + h] = esum * (1.0 + 1e-9);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -464,11 +489,25 @@ __device__ __forceinline__ void c_find_kth(CertShared &sh, uint32_t count, int64
     bool by_index = false;
     for (;;) {
         if (count <= (uint32_t)kCRank) {
+            // pairwise ranks, 8 entries read per step so the LDS latency is
+            // paid once per 8 comparisons
             for (uint32_t c = tid; c < count; c += kCThreads) {
                 const double x = sh.val[c];
                 const int32_t jc = sh.idx[c];
                 int64_t rank = 0;
-                for (uint32_t o = 0; o < count; ++o) {
+                uint32_t o = 0;
+                for (; o + 8 <= count; o += 8) {
+                    double y[8];
+                    int32_t yi[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        y[u] = sh.val[o + u];
+                        yi[u] = sh.idx[o + u];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) rank += (y[u] > x) || (y[u] == x && yi[u] < jc);
+                }
+                for (; o < count; ++o) {
                     const double y = sh.val[o];
                     rank += (y > x) || (y == x && sh.idx[o] < jc);
                 }
@@ -573,19 +612,40 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
             for (int64_t i = tid; i < a.topk; i += kCThreads) sel[i] = i < kk ? (int32_t)i : -1;
         return;
     }
+    // the approximate scores and their error bounds, every load in flight
+    // together (n <= kCCap: kCPer per thread), kept in registers for the
+    // three passes below
+    double sv[kCPer], ev[kCPer];
+    {
+        double kv[kCPer];
+#pragma unroll
+        for (int e = 0; e < kCPer; ++e) {
+            const int64_t j = tid + (int64_t)e * kCThreads;
+            sv[e] = shat[j < n ? j : 0];
+            kv[e] = kbar[j < n ? j : 0];
+        }
+#pragma unroll
+        for (int e = 0; e < kCPer; ++e) ev[e] = cert_eps(Eb, kv[e], sv[e]);
+    }
     // tau_L = kk-th largest lower end, tau_U = (kk+1)-th largest upper end
-    for (int64_t j = tid; j < n; j += kCThreads) {
-        const double s = shat[j];
-        sh.val[j] = s - cert_eps(Eb, kbar[j], s);
-        sh.idx[j] = (int32_t)j;
+#pragma unroll
+    for (int e = 0; e < kCPer; ++e) {
+        const int64_t j = tid + (int64_t)e * kCThreads;
+        if (j < n) {
+            sh.val[j] = sv[e] - ev[e];
+            sh.idx[j] = (int32_t)j;
+        }
     }
     __syncthreads();
     c_find_kth(sh, (uint32_t)n, kk);
     const double tauL = sh.cut_v;
-    for (int64_t j = tid; j < n; j += kCThreads) {
-        const double s = shat[j];
-        sh.val[j] = s + cert_eps(Eb, kbar[j], s);
-        sh.idx[j] = (int32_t)j;
+#pragma unroll
+    for (int e = 0; e < kCPer; ++e) {
+        const int64_t j = tid + (int64_t)e * kCThreads;
+        if (j < n) {
+            sh.val[j] = sv[e] + ev[e];
+            sh.idx[j] = (int32_t)j;
+        }
     }
     __syncthreads();
     c_find_kth(sh, (uint32_t)n, kk + 1);
@@ -598,8 +658,11 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
         sh.nx = 0;
     }
     __syncthreads();
-    for (int64_t j = tid; j < n; j += kCThreads) {
-        const double s = shat[j], e = cert_eps(Eb, kbar[j], s);
+#pragma unroll
+    for (int ei = 0; ei < kCPer; ++ei) {
+        const int64_t j = tid + (int64_t)ei * kCThreads;
+        if (j >= n) continue;
+        const double s = sv[ei], e = ev[ei];
         if (s - e > tauU) {
             atomicOr(&sh.bitmap[j >> 5], 1u << (j & 31));
             atomicAdd(&sh.nd, 1u);
@@ -623,7 +686,14 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
         const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
         for (int qh = 0; qh < 2; ++qh) {
             const double *qsrc = a.qeff + ((int64_t)h * a.n_q + (int64_t)b * kQB + qh * 32) * kD;
-            for (int i = tid; i < 32 * kD; i += kCThreads) sh.qblk[i] = qsrc[i];
+            {
+                constexpr int QPT = 32 * kD / kCThreads;      // 8 per thread
+                double qv[QPT];
+#pragma unroll
+                for (int u = 0; u < QPT; ++u) qv[u] = qsrc[tid + u * kCThreads];
+#pragma unroll
+                for (int u = 0; u < QPT; ++u) sh.qblk[tid + u * kCThreads] = qv[u];
+            }
             __syncthreads();
             for (uint32_t x = wave; x < nx; x += kCWaves) {
                 const int64_t j = sh.xs[x];
@@ -764,7 +834,7 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     double *kbar = (double *)p;
 
     PrepArgs pa{(const uint16_t *)q, qhl, qeff, E, g.Hq, g.Hkv, g.g, g.n_q};
-    hipLaunchKernelGGL(k_qprep, dim3(g.n_blk, g.Hkv), dim3(kD), 0, s, pa);
+    hipLaunchKernelGGL(k_qprep, dim3(g.n_blk, g.Hkv), dim3(kPrepThreads), 0, s, pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
