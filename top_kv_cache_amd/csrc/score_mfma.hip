@@ -196,6 +196,34 @@ __device__ __forceinline__ void lds_read8(const uint32_t (&ad)[8], uint4 (&o)[8]
     o[7] = make_uint4(r7.x, r7.y, r7.z, r7.w);
 }
 
+// Eight 16-byte LDS reads at base + {0, 16, 32, 48} and base + 1024 + {0, 16,
+// 32, 48} (8 channels of two fp64 rows 128 doubles apart), completed inside
+// one asm block like lds_read8.
+__device__ __forceinline__ void lds_read8_rows2(uint32_t base, uint4 (&o)[8]) {
+    u32x4v r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:16\n\t"
+        "ds_read_b128 %2, %8 offset:32\n\t"
+        "ds_read_b128 %3, %8 offset:48\n\t"
+        "ds_read_b128 %4, %8 offset:1024\n\t"
+        "ds_read_b128 %5, %8 offset:1040\n\t"
+        "ds_read_b128 %6, %8 offset:1056\n\t"
+        "ds_read_b128 %7, %8 offset:1072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(base)
+        : "memory");
+    o[0] = make_uint4(r0.x, r0.y, r0.z, r0.w);
+    o[1] = make_uint4(r1.x, r1.y, r1.z, r1.w);
+    o[2] = make_uint4(r2.x, r2.y, r2.z, r2.w);
+    o[3] = make_uint4(r3.x, r3.y, r3.z, r3.w);
+    o[4] = make_uint4(r4.x, r4.y, r4.z, r4.w);
+    o[5] = make_uint4(r5.x, r5.y, r5.z, r5.w);
+    o[6] = make_uint4(r6.x, r6.y, r6.z, r6.w);
+    o[7] = make_uint4(r7.x, r7.y, r7.z, r7.w);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(size_t)(const void __attribute__((address_space(3))) *)p;
 }
@@ -675,14 +703,20 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
     const uint32_t nd = sh.nd, nx = sh.nx;
     const int64_t need = (int64_t)kk - nd;
     if (need > 0) {
-        // exact (fp64) block scores of the uncertain spans, a wave per span.
-        // The block's q_eff is staged in LDS 32 queries at a time; lane =
-        // (token tl of a 32-token chunk, query half sub): it accumulates the
-        // 16 dot products of its token with queries sub*16.. in fp64 (the
-        // products of a bf16 key with q_eff are exact), then the per-query
-        // maxima over the 32 token lanes come from a transpose-reduce and the
-        // 32 maxima are summed; the two query halves are added in order.
+        // exact (fp64) block scores of the uncertain spans.  The block's
+        // q_eff is staged in LDS 32 queries at a time; a work item is (span,
+        // part): lane = (token tl of a 32-token chunk, query half sub) and it
+        // accumulates the 8 dot products of its token with queries
+        // sub*16 + part*8 .. +8 in fp64 (the products of a bf16 key with q_eff
+        // are exact), the per-query maxima over the 32 token lanes come from a
+        // transpose-reduce, and the 16 maxima are summed.  When the spans are
+        // too few to occupy every wave (nx <= 4) the two parts of a span run on
+        // different waves, their sums kept apart in val (free during
+        // re-scoring) and added in a fixed order; otherwise one wave takes
+        // both parts of its span in turn.
         const int tl = lane & 31, sub = lane >> 5;
+        const bool split = nx <= (uint32_t)(kCWaves / 2);
+        const uint32_t n_items = split ? 2 * nx : nx;
         const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
         for (int qh = 0; qh < 2; ++qh) {
             const double *qsrc = a.qeff + ((int64_t)h * a.n_q + (int64_t)b * kQB + qh * 32) * kD;
@@ -695,66 +729,98 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
                 for (int u = 0; u < QPT; ++u) sh.qblk[tid + u * kCThreads] = qv[u];
             }
             __syncthreads();
-            for (uint32_t x = wave; x < nx; x += kCWaves) {
+            for (uint32_t it = wave; it < n_items; it += kCWaves) {
+                const uint32_t x = split ? it >> 1 : it;
+                const int p0 = split ? (int)(it & 1) : 0, p1 = split ? p0 + 1 : 2;
                 const int64_t j = sh.xs[x];
                 const int64_t tb = a.mid_lo + j * a.S, te = min(tb + (int64_t)a.S, a.mid_hi);
-                double best[16];
+                double total = 0.0;
+                for (int part = p0; part < p1; ++part) {
+                    double best[8];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) best[i] = -INFINITY;
-                for (int64_t c0 = tb; c0 < te; c0 += 32) {
-                    const int64_t t = c0 + tl;
-                    const bool ok = t < te;
-                    const unsigned char *krow = kh + (ok ? t : tb) * a.st_bytes;
-                    double acc[16];
+                    for (int i = 0; i < 8; ++i) best[i] = -INFINITY;
+                    for (int64_t c0 = tb; c0 < te; c0 += 32) {
+                        const int64_t t = c0 + tl;
+                        const bool ok = t < te;
+                        const unsigned char *krow = kh + (ok ? t : tb) * a.st_bytes;
+                        double acc[8];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[i] = 0.0;
-                    // the key row in two halves of 8 chunks, each half's loads
-                    // issued together before its arithmetic
-                    for (int half = 0; half < 2; ++half) {
-                        uint4 kraw[8];
+                        for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+                        // the key row in two halves of 8 chunks, each half's
+                        // loads issued together before its arithmetic
+                        for (int half = 0; half < 2; ++half) {
+                            uint4 kraw[8];
 #pragma unroll
-                        for (int cc = 0; cc < 8; ++cc) kraw[cc] = ld16(krow + (half * 8 + cc) * 16);
+                            for (int cc = 0; cc < 8; ++cc) kraw[cc] = ld16(krow + (half * 8 + cc) * 16);
 #pragma unroll
-                        for (int cc = 0; cc < 8; ++cc) {
-                            const uint32_t w4[4] = {kraw[cc].x, kraw[cc].y, kraw[cc].z, kraw[cc].w};
-                            double kd[8];
+                            for (int cc = 0; cc < 8; ++cc) {
+                                const uint32_t w4[4] = {kraw[cc].x, kraw[cc].y, kraw[cc].z, kraw[cc].w};
+                                double kd[8];
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                kd[2 * e] = (double)__uint_as_float(w4[e] << 16);
-                                kd[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
-                            }
-                            const double *qc = sh.qblk + sub * 16 * kD + (half * 8 + cc) * 8;
+                                for (int e = 0; e < 4; ++e) {
+                                    kd[2 * e] = (double)__uint_as_float(w4[e] << 16);
+                                    kd[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
+                                }
+                                // the 8 channels of 2 queries per LDS batch
+                                // (eight 16-byte reads completed together; the
+                                // lanes of a half-wave read the same addresses)
+                                const uint32_t qc = lds_addr(sh.qblk + (sub * 16 + part * 8) * kD +
+                                                             (half * 8 + cc) * 8);
+                                static_assert(kD * 8 == 1024, "query rows 1024 bytes apart");
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) {
+                                for (int i0 = 0; i0 < 8; i0 += 2) {
+                                    uint4 qv[8];
+                                    lds_read8_rows2(qc + (uint32_t)(i0 * kD * 8), qv);
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) acc[i] = fma(qc[i * kD + e], kd[e], acc[i]);
+                                    for (int u = 0; u < 8; ++u) {
+                                        const double q0 = __hiloint2double((int)qv[u].y, (int)qv[u].x);
+                                        const double q1 = __hiloint2double((int)qv[u].w, (int)qv[u].z);
+                                        const int i = i0 + (u >> 2), e = 2 * (u & 3);
+                                        acc[i] = fma(q0, kd[e], acc[i]);
+                                        acc[i] = fma(q1, kd[e + 1], acc[i]);
+                                    }
+                                }
                             }
                         }
+                        if (ok)
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) best[i] = fmax(best[i], acc[i]);
                     }
-                    if (ok)
+                    // transpose-max over the 32 token lanes: after the steps
+                    // over lane^16, ^8, ^4 lane l keeps query slot (l/4)%8,
+                    // then the maxima over lane^2 and lane^1 complete it
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) best[i] = fmax(best[i], acc[i]);
-                }
-                // transpose-max over the 32 token lanes: after the steps over
-                // lane^16, ^8, ^4, ^2 lane l keeps query slot (l/2)%16 (bits of
-                // l taken from the top), and lane^1 holds the same value
+                    for (int o = 16, nv = 8; o >= 4; o >>= 1, nv >>= 1) {
+                        const bool upper = (tl & o) != 0;
 #pragma unroll
-                for (int o = 16, nv = 16; o >= 2; o >>= 1, nv >>= 1) {
-                    const bool upper = (tl & o) != 0;
-#pragma unroll
-                    for (int i = 0; i < nv / 2; ++i) {
-                        const double keep = upper ? best[i + nv / 2] : best[i];
-                        const double send = upper ? best[i] : best[i + nv / 2];
-                        best[i] = fmax(keep, __shfl_xor(send, o));
+                        for (int i = 0; i < nv / 2; ++i) {
+                            const double keep = upper ? best[i + nv / 2] : best[i];
+                            const double send = upper ? best[i] : best[i + nv / 2];
+                            best[i] = fmax(keep, __shfl_xor(send, o));
+                        }
                     }
+                    best[0] = fmax(best[0], __shfl_xor(best[0], 2));
+                    best[0] = fmax(best[0], __shfl_xor(best[0], 1));
+                    // sum of the 16 maxima (lanes with tl % 4 == 0 hold one each)
+                    double v = (tl & 3) ? 0.0 : best[0];
+                    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+                    total = part == p0 ? v : total + v;
                 }
-                best[0] = fmax(best[0], __shfl_xor(best[0], 1));
-                // sum of the 32 maxima (even lanes hold one query each)
-                double v = (lane & 1) ? 0.0 : best[0];
-                for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-                if (lane == 0) sh.xv[x] = (qh == 0 ? v : sh.xv[x] + v) + 0.0;
+                if (lane == 0) {
+                    if (split)
+                        sh.val[it] = total;
+                    else
+                        sh.xv[x] = (qh == 0 ? total : sh.xv[x] + total) + 0.0;
+                }
             }
             __syncthreads();
+            if (split) {
+                for (uint32_t x = tid; x < nx; x += kCThreads) {
+                    const double v = sh.val[2 * x] + sh.val[2 * x + 1];
+                    sh.xv[x] = (qh == 0 ? v : sh.xv[x] + v) + 0.0;
+                }
+                __syncthreads();
+            }
         }
         for (uint32_t x = tid; x < nx; x += kCThreads) {
             sh.val[x] = sh.xv[x];
