@@ -76,12 +76,6 @@ struct MAttnArgs {
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-    uint32_t b = __float_as_uint(f);
-    b += 0x7FFFu + ((b >> 16) & 1u);
-    return b >> 16;
-}
-
 // two floats -> two bf16 (round to nearest even), packed low first
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
@@ -360,25 +354,19 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
 
         // B fragments of P^T: k-step s covers keys 16s .. 16s+15; this lane
         // (kb = hb) needs keys 16s + 8hb + e; a lane holds keys 8a + 4hb + c.
+        // P is rounded to bf16 first (packed pairs), then v_permlane32_swap of
+        // (keys 8(2s) + 4hb .., keys 8(2s+1) + 4hb ..) leaves keys 16s + e in
+        // the first register and 16s + 8 + e in the second on both halves.
         uint4 pb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            float send[4], recv[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) send[c] = hb == 0 ? p[4 * (2 * s + 1) + c] : p[4 * (2 * s) + c];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) recv[c] = __shfl_xor(send[c], 32);
-            float v8[8];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                v8[c] = hb == 0 ? p[4 * (2 * s) + c] : recv[c];
-                v8[4 + c] = hb == 0 ? recv[c] : p[4 * (2 * s + 1) + c];
-            }
-            uint32_t bb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bb[e] = bf16_rne_bits(v8[e]);
-            pb[s] = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
-                               bb[6] | (bb[7] << 16));
+            const uint32_t e0 = pack_bf16(p[8 * s], p[8 * s + 1]);
+            const uint32_t e1 = pack_bf16(p[8 * s + 2], p[8 * s + 3]);
+            const uint32_t o0 = pack_bf16(p[8 * s + 4], p[8 * s + 5]);
+            const uint32_t o1 = pack_bf16(p[8 * s + 6], p[8 * s + 7]);
+            const auto x0 = __builtin_amdgcn_permlane32_swap(e0, o0, false, false);
+            const auto x1 = __builtin_amdgcn_permlane32_swap(e1, o1, false, false);
+            pb[s] = make_uint4(x0[0], x1[0], x0[1], x1[1]);
         }
         // O^T (channels x queries) += V^T (channels x keys) P^T (keys x queries)
 #pragma unroll
