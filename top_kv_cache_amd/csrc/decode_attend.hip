@@ -470,6 +470,8 @@ hipError_t launch_typed(const Geom &g, const FusedArgs &a, hipStream_t s) {
 
 template <typename TIn, int D>
 hipError_t launch_qr(const Geom &g, const FusedArgs &a, hipStream_t s) {
+    if (a.QR == 1) return launch_typed<TIn, D, 1>(g, a, s);
+    if (a.QR == 2) return launch_typed<TIn, D, 2>(g, a, s);
     return a.QR <= 4 ? launch_typed<TIn, D, 4>(g, a, s) : launch_typed<TIn, D, 8>(g, a, s);
 }
 
