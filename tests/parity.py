@@ -88,10 +88,11 @@ def mfma_path(w):
 
 def fused_path(w):
     """rea_decode_step runs steps 2-4 fused, reading the window straight from
-    the cache: up to 8 query rows per (block, KV head) on the VALU, or bf16
-    d 128 blocks of >= 32 query rows on MFMA."""
+    the cache: up to 8 query rows per (block, selection head) on the VALU;
+    bf16 d 128 beyond that on MFMA (2-wave workgroups up to 64 rows, 8-wave
+    ones with at most 4096 selection entries beyond)."""
     rows = w.block_q * w.g_sel
-    mfma_cache = w.dtype == "bf16" and w.d == 128 and rows >= 32 and w.sel_cap <= 4096
+    mfma_cache = w.dtype == "bf16" and w.d == 128 and rows > 8 and (rows <= 64 or w.sel_cap <= 4096)
     return rows <= 8 or mfma_cache
 
 

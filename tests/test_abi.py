@@ -204,7 +204,8 @@ def test_batched_decode_workspace_and_errors():
     p2, a2 = good(n_q=2)
     a2.block_q = 2
     assert call(pp=p2, aa=a2) == E("REA_EUNSUPPORTED")
-    p3, a3 = good(Hq=64, Hkv=4)          # 16 query heads per KV head
+    # 16 query heads per KV head: fp32 has only the VALU attention (at most 8)
+    p3, a3 = good(dtype=rea.REA_F32, Hq=64, Hkv=4)
     assert call(pp=p3, aa=a3, kvs=p3.n_kv_heads * p3.kv_stride_head) == E("REA_EUNSUPPORTED")
     a4 = rea.params(32, 32, 120, 0, 1)
     assert call(aa=a4) == E("REA_ESHAPE")   # L = 0: the query token would not be local

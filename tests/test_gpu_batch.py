@@ -37,6 +37,8 @@ CASES = {
                                   [2000, 1999, 1013, 77, 52]),
     "bf16_d128_token_segments": (dict(Hq=8, Hkv=2, d=128, T=2500, S=16, topk=10, G=4, L=64,
                                       token_segments=True), [2500, 2, 900, 1777]),
+    "bf16_g16_mfma_attention": (dict(Hq=32, Hkv=2, d=128, T=2200, S=32, topk=10, G=4, L=128),
+                                [2200, 700, 1500]),
     "llama8b_32k": (dict(Hq=32, Hkv=8, d=128, T=32768, S=32, topk=120, G=32, L=4096,
                          needles=4, kv_scaled=True), [32768, 30000, 24577, 8300]),
 }

@@ -69,6 +69,11 @@ SMALL = {
     "pqh_bf16_mfma_blocks": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,
                               L=128, needles=0, per_q_head=True),
     "f32_token_level_S1_g1": S(dtype="f32", Hq=2, Hkv=2, d=128, S=1, topk=100, T=1200, L=50),
+    # 9..64 query rows per (block, selection head): 2-wave MFMA attention
+    "bf16_blocks_of_16_rows_S24": S(Hq=8, Hkv=2, d=128, T=1900, n_q=8, block_q=4, S=24, topk=9,
+                                    L=96, needles=0, kv_scaled=True),
+    "pqh_bf16_blocks_64_rows": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,
+                                 L=128, needles=0, per_q_head=True),
     # token segments: the best tokens, each widened to S tokens
     "seg_bf16_d64": S(S=8, topk=6, T=700, token_segments=True),
     "seg_bf16_d128_pqh": S(Hq=8, Hkv=2, d=128, T=2048, S=32, topk=12, L=256, needles=2,

@@ -43,10 +43,15 @@ constexpr int kD = 128;
 constexpr int kKT = 32;             // keys per tile
 constexpr int kKPad = 136;          // K' tile row stride (bf16)
 constexpr int kVPad = 40;           // V^T tile row stride (bf16)
-constexpr int kAThreads = 512;      // 8 waves
-constexpr int kRowsWG = kAThreads / 2;   // query rows per workgroup (32 per wave)
+constexpr int kAThreads = 512;      // 8 waves (blocks of many query rows)
+constexpr int kRowsWG = kAThreads / 2;   // query rows per 8-wave workgroup (32 per wave)
 
-constexpr int kSelCap = 4096;       // selection entries staged in LDS (cache source)
+constexpr int kSelCap = 4096;       // selection entries staged in LDS (cache source, 8 waves)
+// 2-wave workgroups (at most 64 query rows: decode steps, small blocks) take
+// at most kSmallTiles key tiles per split and stage only the selection
+// entries those rows use
+constexpr int kSmallTiles = 8;
+constexpr int kSmallSel = kSmallTiles * 32 + 8;
 
 struct MAttnArgs {
     // window source
@@ -66,11 +71,15 @@ struct MAttnArgs {
     int64_t W_cap;
     int QR, Hq, Hkv, g, n_q, block_q, n_rg, rep;
     float scale_log2;       // softmax scale * log2(e)
-    // key-tile splits (cache source, small grids): split sp of a workgroup's
-    // tiles writes unnormalised partials, merged by k_attend_merge
-    int n_split;
-    float *part_o;          // [units][n_split][kRowsWG][D]
-    float2 *part_ml;        // [units][n_split][kRowsWG]: running max, sum
+    // key-tile splits (cache source): split sp of a workgroup's tiles writes
+    // unnormalised partials of its valid rows, merged by k_attend_merge
+    int n_split, rw;        // rw: query rows per workgroup (32 per wave)
+    float *part_o;          // [units][n_split][rw][D]
+    float2 *part_ml;        // [units][n_split][rw]: running max, sum
+    // batched decode (see Geom): per-sequence lengths and cache offsets
+    const int64_t *lens;
+    int hps, G, L;
+    int64_t seq_stride;
 };
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -103,12 +112,19 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float (&x)[8]) {
     }
 }
 
-template <bool kCache>
-__global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
-    __shared__ __align__(16) uint16_t khi[2][kKT][kKPad];
-    __shared__ __align__(16) uint16_t klo[2][kKT][kKPad];
-    __shared__ __align__(16) uint16_t vt[2][kD][kVPad];
-    __shared__ int32_t ssel[kCache ? kSelCap : 1];
+template <bool kCache, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnArgs a) {
+    static_assert(NW == 8 || (NW == 2 && kCache), "8 waves, or 2 waves on the cache source");
+    constexpr int NT = 64 * NW;                 // threads
+    constexpr int RW = 32 * NW;                 // query rows per workgroup
+    constexpr int NB = NW == 8 ? 2 : 1;         // LDS tile buffers
+    constexpr int TPR = NT / kKT;               // staging threads per key row (16 or 4)
+    constexpr int PG = 16 / TPR;                // groups of 4 channel pairs (K) / 8 channels (V) per thread
+    constexpr int kSel = NW == 8 ? kSelCap : kSmallSel;
+    __shared__ __align__(16) uint16_t khi[NB][kKT][kKPad];
+    __shared__ __align__(16) uint16_t klo[NB][kKT][kKPad];
+    __shared__ __align__(16) uint16_t vt[NB][kD][kVPad];
+    __shared__ int32_t ssel[kCache ? kSel : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sp = blockIdx.x % a.n_split;
     const int unit = blockIdx.x / a.n_split;
@@ -116,27 +132,61 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
     const int bh = unit / a.n_rg;
     const int b = bh / a.Hkv, h = bh % a.Hkv;
     const int n = lane & 31, hb = lane >> 5;
+    // the (block, head)'s sequence: its own regions when decoding a batch
+    SeqGeom sg{};
+    int64_t kv_off = 0;
+    if (kCache) {
+        const SeqOf so = seq_of(a.lens, h, a.hps, a.rep, a.seq_stride, a.sh, a.T);
+        sg = seq_geom(so.T, a.G, a.L, a.S);
+        kv_off = so.kv_off;
+    }
     int64_t Wbh, sel_len = 0;
+    int ns = 0;
     if (kCache) {
         // window length from the selection (only span n_spans-1 can be short,
-        // and a sorted selection holds it last); the selection goes to LDS
-        const int ns = a.n_sel[bh];
+        // and a sorted selection holds it last)
+        ns = a.n_sel[bh];
         sel_len = (int64_t)ns * a.S;
-        if (a.last_len != a.S && ns > 0 && a.sel[(int64_t)bh * a.topk + ns - 1] == a.n_spans - 1)
-            sel_len -= a.S - a.last_len;
-        for (int t = tid; t < ns; t += kAThreads) ssel[t] = a.sel[(int64_t)bh * a.topk + t];
-        Wbh = a.Gp + sel_len + a.Lp;
+        if (sg.last_len != a.S && ns > 0 && a.sel[(int64_t)bh * a.topk + ns - 1] == sg.n_spans - 1)
+            sel_len -= a.S - sg.last_len;
+        Wbh = sg.Gp + sel_len + sg.Lp;
     } else {
         Wbh = a.W[bh];
     }
 
     // this lane's query column
-    const int r = rg * kRowsWG + wave * 32 + n;
+    const int r = rg * RW + wave * 32 + n;
     const bool valid_q = r < a.QR;
     const int rq = valid_q ? r : 0;
     const int64_t qi = (int64_t)b * a.block_q + rq / a.g;
     const int hq = h * a.g + rq % a.g;
     const int64_t pos = Wbh - a.n_q + qi;
+
+    // keys this workgroup needs: up to the largest position among its rows,
+    // and this split's share of their tiles
+    int64_t rmax = (int64_t)(rg + 1) * RW - 1;
+    if (rmax > a.QR - 1) rmax = a.QR - 1;
+    int64_t kend = Wbh - a.n_q + (int64_t)b * a.block_q + rmax / a.g + 1;
+    if (kend > Wbh) kend = Wbh;
+    const int64_t n_tiles_all = (kend + kKT - 1) / kKT;
+    const int64_t it0 = n_tiles_all * sp / a.n_split;
+    const int64_t it1 = n_tiles_all * (sp + 1) / a.n_split;
+
+    // the selection entries the split's rows use go to LDS (all of them with
+    // 8 waves; with 2 waves a split spans at most kSmallTiles tiles)
+    int64_t slot0 = 0;
+    if (kCache) {
+        int64_t slot1 = ns;
+        if (NW != 8) {
+            const int64_t wl = it0 * kKT - sg.Gp, wh = it1 * kKT - 1 - sg.Gp;
+            slot0 = wl > 0 ? wl / a.S : 0;
+            slot1 = wh >= 0 ? wh / a.S + 1 : 0;
+            if (slot1 > ns) slot1 = ns;
+            if (slot1 < slot0) slot1 = slot0;
+        }
+        for (int64_t t = tid; t < slot1 - slot0; t += NT)
+            ssel[t] = a.sel[(int64_t)bh * a.topk + slot0 + t];
+    }
 
     // B fragments of Q' (hi, lo): channels ks*16 + hb*8 .. +8.  The query is
     // scaled by softmax_scale * log2(e) first, so logits come out in log2
@@ -174,43 +224,33 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
         }
     }
 
-    // keys this workgroup needs: up to the largest position among its rows
-    int64_t rmax = (int64_t)(rg + 1) * kRowsWG - 1;
-    if (rmax > a.QR - 1) rmax = a.QR - 1;
-    int64_t kend = Wbh - a.n_q + (int64_t)b * a.block_q + rmax / a.g + 1;
-    if (kend > Wbh) kend = Wbh;
-    const int64_t n_tiles_all = (kend + kKT - 1) / kKT;
-    // this split's tiles
-    const int64_t it0 = n_tiles_all * sp / a.n_split;
-    const int64_t it1 = n_tiles_all * (sp + 1) / a.n_split;
-
-    // staging (512 threads, 32 rows).  K, window: thread -> key row tid/16,
-    // channels (tid%16)*8 .. +8.  K, cache: thread -> key row tid/16, channel
-    // pairs (tid%16)*4 .. +4, i.e. channels c0 .. c0+4 and c0+D/2 .. c0+D/2+4.
-    // V: thread -> key row tid%32, channels (tid/32)*8 .. +8, so lanes l and
-    // l^1 hold adjacent keys and V^T is written one 32-bit word (two keys) at
-    // a time.
-    const int skey = tid >> 4, sch = (tid & 15) * 8, c0 = (tid & 15) * 4;
-    const int vkey = tid & 31, vch = (tid >> 5) * 8;
+    // staging (NT threads, 32 rows).  K, window (8 waves): thread -> key row
+    // tid/16, channels (tid%16)*8 .. +8.  K, cache: thread -> key row tid/TPR,
+    // PG groups of 4 channel pairs from (tid%TPR)*4*PG, i.e. channels c0 ..
+    // c0+4 and c0+D/2 .. c0+D/2+4 per group.  V: thread -> key row tid%32, PG
+    // groups of 8 channels from (tid/32)*8*PG, so lanes l and l^1 hold
+    // adjacent keys and V^T is written one 32-bit word (two keys) at a time.
+    const int skey = tid / TPR, sch = (tid & 15) * 8, c0 = (tid % TPR) * 4 * PG;
+    const int vkey = tid & 31, vch = (tid >> 5) * 8 * PG;
     const float *kwb = a.k_win + (int64_t)bh * a.W_cap * kD;
     const uint16_t *vwb = a.v_win + (int64_t)bh * a.W_cap * kD;
-    const uint16_t *kcb = a.k + (int64_t)(h / a.rep) * a.sh;
-    const uint16_t *vcb = a.v + (int64_t)(h / a.rep) * a.sh;
-    float4 kr[2];               // window: 8 fp32 keys; cache: 4 x (cos, sin)
-    uint4 vr;
-    uint2 kc[2];
+    const uint16_t *kcb = a.k + kv_off;
+    const uint16_t *vcb = a.v + kv_off;
+    float4 kr[PG][2];           // window: 8 fp32 keys; cache: 4 x (cos, sin) per group
+    uint4 vr[PG];
+    uint2 kc[PG][2];
     // cache row of window row wl (rows past the end read window row 0: finite
     // data that is masked or multiplied by a zero weight)
     auto src_row = [&](int64_t wl) -> int64_t {
         int64_t src;
-        if (wl < a.Gp) {
+        if (wl < sg.Gp) {
             src = wl;
-        } else if (wl < a.Gp + sel_len) {
-            const uint32_t o = (uint32_t)(wl - a.Gp);
+        } else if (wl < sg.Gp + sel_len) {
+            const uint32_t o = (uint32_t)(wl - sg.Gp);
             const uint32_t qs = o / (uint32_t)a.S;
-            src = a.mid_lo + (int64_t)ssel[qs] * a.S + (o - qs * (uint32_t)a.S);
+            src = sg.mid_lo + (int64_t)ssel[qs - slot0] * a.S + (o - qs * (uint32_t)a.S);
         } else {
-            src = a.T - a.Lp + (wl - a.Gp - sel_len);
+            src = sg.T - sg.Lp + (wl - sg.Gp - sel_len);
         }
         return src * a.st;
     };
@@ -218,65 +258,77 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
         const int64_t w = w0 + skey, wv = w0 + vkey;
         const bool ok = w < kend, okv = wv < kend;
         if (kCache) {
-            const int64_t wl = ok ? w : 0;
-            const int64_t row = src_row(wl), rowv = src_row(okv ? wv : 0);
-            kc[0] = *(const uint2 *)(kcb + row + c0);
-            kc[1] = *(const uint2 *)(kcb + row + c0 + kD / 2);
-            vr = *(const uint4 *)(vcb + rowv + vch);
-            const float4 *rp = (const float4 *)(a.rope + wl * (kD / 2) + c0);
-            kr[0] = rp[0];
-            kr[1] = rp[1];
+            const int64_t wl = ok ? w : it0 * kKT;
+            const int64_t row = src_row(wl), rowv = src_row(okv ? wv : it0 * kKT);
+#pragma unroll
+            for (int gq = 0; gq < PG; ++gq) {
+                const int c = c0 + gq * 4;
+                kc[gq][0] = *(const uint2 *)(kcb + row + c);
+                kc[gq][1] = *(const uint2 *)(kcb + row + c + kD / 2);
+                vr[gq] = *(const uint4 *)(vcb + rowv + vch + gq * 8);
+                const float4 *rp = (const float4 *)(a.rope + wl * (kD / 2) + c);
+                kr[gq][0] = rp[0];
+                kr[gq][1] = rp[1];
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-                kr[e] = ok ? *(const float4 *)(kwb + w * kD + sch + e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            vr = okv ? *(const uint4 *)(vwb + wv * kD + vch) : make_uint4(0u, 0u, 0u, 0u);
+                kr[0][e] = ok ? *(const float4 *)(kwb + w * kD + sch + e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            vr[0] = okv ? *(const uint4 *)(vwb + wv * kD + vch) : make_uint4(0u, 0u, 0u, 0u);
         }
     };
-    // V^T from this lane's 16 channels of key vkey and lane^1's (key vkey^1):
-    // the even lane writes the even channels, the odd lane the odd ones, each
-    // word holding (key 2m, key 2m+1)
-    auto store_vt = [&](int buf) {
+    // V^T from this lane's 8-channel groups of key vkey and lane^1's (key
+    // vkey^1): the even lane writes the even channels, the odd lane the odd
+    // ones, each word holding (key 2m, key 2m+1)
+    auto store_vt = [&](int bf) {
         const bool odd = (vkey & 1) != 0;
-        const uint32_t w8[4] = {vr.x, vr.y, vr.z, vr.w};
-        uint32_t *vrow = (uint32_t *)&vt[buf][0][0];
+        uint32_t *vrow = (uint32_t *)&vt[bf][0][0];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const uint32_t send = odd ? (w8[m] & 0xffffu) : (w8[m] >> 16);
-            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-            const uint32_t word = odd ? (recv | (w8[m] & 0xffff0000u)) : ((w8[m] & 0xffffu) | (recv << 16));
-            const int ch = vch + 2 * m + (odd ? 1 : 0);
-            vrow[(ch * kVPad + (vkey & ~1)) / 2] = word;
+        for (int gq = 0; gq < PG; ++gq) {
+            const uint32_t w8[4] = {vr[gq].x, vr[gq].y, vr[gq].z, vr[gq].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t send = odd ? (w8[m] & 0xffffu) : (w8[m] >> 16);
+                const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+                const uint32_t word = odd ? (recv | (w8[m] & 0xffff0000u)) : ((w8[m] & 0xffffu) | (recv << 16));
+                const int ch = vch + gq * 8 + 2 * m + (odd ? 1 : 0);
+                vrow[(ch * kVPad + (vkey & ~1)) / 2] = word;
+            }
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int bf) {
         if (kCache) {
-            const float x1[4] = {__uint_as_float(kc[0].x << 16), __uint_as_float(kc[0].x & 0xffff0000u),
-                                 __uint_as_float(kc[0].y << 16), __uint_as_float(kc[0].y & 0xffff0000u)};
-            const float x2[4] = {__uint_as_float(kc[1].x << 16), __uint_as_float(kc[1].x & 0xffff0000u),
-                                 __uint_as_float(kc[1].y << 16), __uint_as_float(kc[1].y & 0xffff0000u)};
-            const float cs[4][2] = {{kr[0].x, kr[0].y}, {kr[0].z, kr[0].w}, {kr[1].x, kr[1].y},
-                                    {kr[1].z, kr[1].w}};
-            float y[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                y[e] = x1[e] * cs[e][0] - x2[e] * cs[e][1];
-                y[4 + e] = x2[e] * cs[e][0] + x1[e] * cs[e][1];
+            for (int gq = 0; gq < PG; ++gq) {
+                const int c = c0 + gq * 4;
+                const float x1[4] = {__uint_as_float(kc[gq][0].x << 16), __uint_as_float(kc[gq][0].x & 0xffff0000u),
+                                     __uint_as_float(kc[gq][0].y << 16), __uint_as_float(kc[gq][0].y & 0xffff0000u)};
+                const float x2[4] = {__uint_as_float(kc[gq][1].x << 16), __uint_as_float(kc[gq][1].x & 0xffff0000u),
+                                     __uint_as_float(kc[gq][1].y << 16), __uint_as_float(kc[gq][1].y & 0xffff0000u)};
+                const float cs[4][2] = {{kr[gq][0].x, kr[gq][0].y}, {kr[gq][0].z, kr[gq][0].w},
+                                        {kr[gq][1].x, kr[gq][1].y}, {kr[gq][1].z, kr[gq][1].w}};
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y[e] = x1[e] * cs[e][0] - x2[e] * cs[e][1];
+                    y[4 + e] = x2[e] * cs[e][0] + x1[e] * cs[e][1];
+                }
+                uint4 hi, lo;
+                split8(y, hi, lo);
+                *(uint2 *)&khi[bf][skey][c] = make_uint2(hi.x, hi.y);
+                *(uint2 *)&klo[bf][skey][c] = make_uint2(lo.x, lo.y);
+                *(uint2 *)&khi[bf][skey][c + kD / 2] = make_uint2(hi.z, hi.w);
+                *(uint2 *)&klo[bf][skey][c + kD / 2] = make_uint2(lo.z, lo.w);
             }
-            uint4 hi, lo;
-            split8(y, hi, lo);
-            *(uint2 *)&khi[buf][skey][c0] = make_uint2(hi.x, hi.y);
-            *(uint2 *)&klo[buf][skey][c0] = make_uint2(lo.x, lo.y);
-            *(uint2 *)&khi[buf][skey][c0 + kD / 2] = make_uint2(hi.z, hi.w);
-            *(uint2 *)&klo[buf][skey][c0 + kD / 2] = make_uint2(lo.z, lo.w);
         } else {
-            const float x[8] = {kr[0].x, kr[0].y, kr[0].z, kr[0].w, kr[1].x, kr[1].y, kr[1].z, kr[1].w};
+            const float x[8] = {kr[0][0].x, kr[0][0].y, kr[0][0].z, kr[0][0].w,
+                                kr[0][1].x, kr[0][1].y, kr[0][1].z, kr[0][1].w};
             uint4 hi, lo;
             split8(x, hi, lo);
-            *(uint4 *)&khi[buf][skey][sch] = hi;
-            *(uint4 *)&klo[buf][skey][sch] = lo;
+            *(uint4 *)&khi[bf][skey][sch] = hi;
+            *(uint4 *)&klo[bf][skey][sch] = lo;
         }
-        store_vt(buf);
+        store_vt(bf);
     };
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -377,24 +429,33 @@ __global__ __launch_bounds__(kAThreads, 1) void k_attend_mfma(MAttnArgs a) {
                 o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, pb[s]),
                                                                o[t], 0, 0, 0);
             }
-        if (more) store_tile(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
+        if (NB == 2) {
+            if (more) store_tile(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        } else {
+            // one buffer: every wave has read it before it is refilled
+            __syncthreads();
+            if (more) store_tile(0);
+            __syncthreads();
+        }
     }
 
     if (a.n_split > 1) {
-        // unnormalised partial of this split (rows past QR are never merged)
-        const int64_t prow = ((int64_t)unit * a.n_split + sp) * kRowsWG + wave * 32 + n;
-        float *po = a.part_o + prow * kD;
+        // unnormalised partial of this split, valid rows only
+        if (valid_q) {
+            const int64_t prow = ((int64_t)unit * a.n_split + sp) * RW + wave * 32 + n;
+            float *po = a.part_o + prow * kD;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int aa = 0; aa < 4; ++aa) {
-                const int c = t * 32 + 8 * aa + 4 * hb;
-                *(float4 *)(po + c) = make_float4(o[t][4 * aa], o[t][4 * aa + 1], o[t][4 * aa + 2],
-                                                  o[t][4 * aa + 3]);
-            }
-        if (hb == 0) a.part_ml[prow] = make_float2(m_run, l_run);
+                for (int aa = 0; aa < 4; ++aa) {
+                    const int c = t * 32 + 8 * aa + 4 * hb;
+                    *(float4 *)(po + c) = make_float4(o[t][4 * aa], o[t][4 * aa + 1], o[t][4 * aa + 2],
+                                                      o[t][4 * aa + 3]);
+                }
+            if (hb == 0) a.part_ml[prow] = make_float2(m_run, l_run);
+        }
         return;
     }
     if (valid_q) {
@@ -417,29 +478,41 @@ constexpr int kMergeThreads = 256;
 
 __global__ __launch_bounds__(kMergeThreads) void k_attend_merge(MAttnArgs a) {
     const int tid = threadIdx.x;
-    const int per_unit = kRowsWG / 8;
+    const int rows = a.QR < a.rw ? a.QR : a.rw;             // rows a unit can hold
+    const int per_unit = (rows + 7) / 8;
     const int unit = blockIdx.x / per_unit;
-    const int r = (blockIdx.x % per_unit) * 8 + tid / 32;   // row within the workgroup's 256
+    const int r = (blockIdx.x % per_unit) * 8 + tid / 32;   // row within the workgroup's rw
     const int cq = tid % 32;
     const int rg = unit % a.n_rg, bh = unit / a.n_rg;
     const int b = bh / a.Hkv, h = bh % a.Hkv;
-    const int rr = rg * kRowsWG + r;
-    if (rr >= a.QR) return;
+    const int rr = rg * a.rw + r;
+    if (r >= a.rw || rr >= a.QR) return;
     float M = -INFINITY, L = 0.f;
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < a.n_split; ++s) {
-        const int64_t prow = ((int64_t)unit * a.n_split + s) * kRowsWG + r;
-        const float2 ml = a.part_ml[prow];
-        const float4 x = *(const float4 *)(a.part_o + prow * kD + cq * 4);
-        const float mn = fmaxf(M, ml.x);
-        if (mn == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(M - mn), fo = __builtin_amdgcn_exp2f(ml.x - mn);
-        L = L * f + ml.y * fo;
-        A.x = A.x * f + x.x * fo;
-        A.y = A.y * f + x.y * fo;
-        A.z = A.z * f + x.z * fo;
-        A.w = A.w * f + x.w * fo;
-        M = mn;
+    constexpr int kBatch = 8;                   // partials loaded together
+    for (int s0 = 0; s0 < a.n_split; s0 += kBatch) {
+        float2 ml[kBatch];
+        float4 x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int s = s0 + u < a.n_split ? s0 + u : s0;
+            const int64_t prow = ((int64_t)unit * a.n_split + s) * a.rw + r;
+            ml[u] = a.part_ml[prow];
+            x[u] = *(const float4 *)(a.part_o + prow * kD + cq * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (s0 + u >= a.n_split) break;
+            const float mn = fmaxf(M, ml[u].x);
+            if (mn == -INFINITY) continue;
+            const float f = __builtin_amdgcn_exp2f(M - mn), fo = __builtin_amdgcn_exp2f(ml[u].x - mn);
+            L = L * f + ml[u].y * fo;
+            A.x = A.x * f + x[u].x * fo;
+            A.y = A.y * f + x[u].y * fo;
+            A.z = A.z * f + x[u].z * fo;
+            A.w = A.w * f + x[u].w * fo;
+            M = mn;
+        }
     }
     const float inv = 1.f / L;
     const int64_t qi = (int64_t)b * a.block_q + rr / a.g;
@@ -473,39 +546,61 @@ bool mfma_attend_path(const Geom &g) {
     return g.dtype == 0 && g.d == kD && g.block_q * g.g >= 32;
 }
 
-bool mfma_cache_attend_path(const Geom &g) { return mfma_attend_path(g) && g.topk <= kSelCap; }
-
 namespace {
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Cache-source attention: 2-wave workgroups for at most 64 query rows per
+// (block, head), else 8-wave workgroups of 256 rows.
+int cache_waves(const Geom &g) { return g.block_q * g.g <= 64 ? 2 : 8; }
+
 int64_t attend_units(const Geom &g) {
-    const int QR = g.block_q * g.g;
-    return (int64_t)g.n_blk * g.Hkv * ((QR + kRowsWG - 1) / kRowsWG);
+    const int QR = g.block_q * g.g, rw = 32 * cache_waves(g);
+    return (int64_t)g.n_blk * g.Hkv * ((QR + rw - 1) / rw);
 }
 
-// Key-tile splits of the cache-source attention: enough workgroups for every
-// CU (one 512-thread workgroup per CU), at least 8 key tiles per split.
+// Key-tile splits.  8 waves: enough workgroups for every CU (one 512-thread
+// workgroup per CU), at least 8 key tiles per split.  2 waves: at most
+// kSmallTiles tiles per split, and about 1024 workgroups when the window
+// allows (at least 2 tiles per split).
 int attend_splits(const Geom &g) {
     const int64_t units = attend_units(g);
-    if (units >= 256) return 1;
-    int64_t ns = (256 + units - 1) / units;
     const int64_t tiles = (g.W_cap + kKT - 1) / kKT;
-    const int64_t by_tiles = tiles / 8 > 1 ? tiles / 8 : 1;
-    if (ns > by_tiles) ns = by_tiles;
-    if (ns > 16) ns = 16;
-    return (int)ns;
+    if (cache_waves(g) == 8) {
+        if (units >= 256) return 1;
+        int64_t ns = (256 + units - 1) / units;
+        const int64_t by_tiles = tiles / 8 > 1 ? tiles / 8 : 1;
+        if (ns > by_tiles) ns = by_tiles;
+        if (ns > 16) ns = 16;
+        return (int)ns;
+    }
+    const int64_t least = (tiles + kSmallTiles - 1) / kSmallTiles;
+    int64_t want = (1024 + units - 1) / units;
+    const int64_t most = (tiles + 1) / 2;
+    if (want > most) want = most;
+    const int64_t ns = want > least ? want : least;
+    return (int)(ns > 0 ? ns : 1);
 }
 
 size_t rope_bytes(const Geom &g) { return (size_t)g.W_cap * (g.d / 2) * sizeof(float2); }
 
 }  // namespace
 
+// Decode-sized groups (at most 8 query rows) stay on the fused VALU kernel,
+// which measured faster there; 9 to 64 rows take 2-wave workgroups, more take
+// 8-wave ones (which stage the whole selection: at most kSelCap entries).
+bool mfma_cache_attend_path(const Geom &g) {
+    if (g.dtype != 0 || g.d != kD) return false;
+    const int QR = g.block_q * g.g;
+    if (QR <= 8) return false;
+    return QR <= 64 || g.topk <= kSelCap;
+}
+
 size_t rope_table_bytes(const Geom &g) {
     size_t b = al256(rope_bytes(g));
     const int ns = attend_splits(g);
     if (ns > 1) {
-        const size_t rows = (size_t)attend_units(g) * ns * kRowsWG;
+        const size_t rows = (size_t)attend_units(g) * ns * 32 * cache_waves(g);
         b += al256(rows * kD * sizeof(float)) + al256(rows * sizeof(float2));
     }
     return b;
@@ -531,7 +626,8 @@ hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_
     a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
     a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
     a.n_split = 1;
-    hipLaunchKernelGGL(k_attend_mfma<false>, dim3(g.n_blk * g.Hkv * a.n_rg), dim3(kAThreads), 0, s, a);
+    a.rw = kRowsWG;
+    hipLaunchKernelGGL((k_attend_mfma<false, 8>), dim3(g.n_blk * g.Hkv * a.n_rg), dim3(kAThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -575,21 +671,33 @@ hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k,
     a.rep = g.rep;
     a.n_q = g.n_q;
     a.block_q = g.block_q;
-    a.n_rg = (a.QR + kRowsWG - 1) / kRowsWG;
+    const int nw = cache_waves(g);
+    a.rw = 32 * nw;
+    a.n_rg = (a.QR + a.rw - 1) / a.rw;
     a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
+    a.lens = g.lens;
+    a.hps = g.hps;
+    a.G = g.G;
+    a.L = g.L;
+    a.seq_stride = g.seq_stride;
     a.n_split = attend_splits(g);
     const int64_t units = (int64_t)g.n_blk * g.Hkv * a.n_rg;
     if (a.n_split > 1) {
         char *p = (char *)ws + al256(rope_bytes(g));
-        const size_t rows = (size_t)units * a.n_split * kRowsWG;
+        const size_t rows = (size_t)units * a.n_split * a.rw;
         a.part_o = (float *)p;
         a.part_ml = (float2 *)(p + al256(rows * kD * sizeof(float)));
     }
-    hipLaunchKernelGGL(k_attend_mfma<true>, dim3((unsigned)(units * a.n_split)), dim3(kAThreads),
-                       0, s, a);
+    if (nw == 2)
+        hipLaunchKernelGGL((k_attend_mfma<true, 2>), dim3((unsigned)(units * a.n_split)), dim3(128),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((k_attend_mfma<true, 8>), dim3((unsigned)(units * a.n_split)),
+                           dim3(kAThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
-    hipLaunchKernelGGL(k_attend_merge, dim3((unsigned)(units * (kRowsWG / 8))),
+    const int rows = a.QR < a.rw ? a.QR : a.rw;
+    hipLaunchKernelGGL(k_attend_merge, dim3((unsigned)(units * ((rows + 7) / 8))),
                        dim3(kMergeThreads), 0, s, a);
     return hipGetLastError();
 }

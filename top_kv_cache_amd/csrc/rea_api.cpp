@@ -208,12 +208,12 @@ size_t decode_ws_bytes(const rea::Geom &g) {
     c.take<char>(seg_tok_bytes(g));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.topk * sizeof(int32_t));
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
-    if (rea::fused_decode_path(g)) {
-        c.take<char>(rea::fused_ws_bytes(g));
-        return c.off;
-    }
     if (rea::mfma_cache_attend_path(g)) {
         c.take<char>(rea::rope_table_bytes(g));
+        return c.off;
+    }
+    if (rea::fused_decode_path(g)) {
+        c.take<char>(rea::fused_ws_bytes(g));
         return c.off;
     }
     c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
@@ -401,17 +401,17 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
                                      timing),
                        "score_select")) != REA_OK)
         return st;
-    if (rea::fused_decode_path(g)) {
-        void *fws = c.take<char>(rea::fused_ws_bytes(g));
-        return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out,
-                                                 fws, s),
-                        "fused gather + window attention");
-    }
     if (rea::mfma_cache_attend_path(g)) {
         void *rws = c.take<char>(rea::rope_table_bytes(g));
         return launched(rea::launch_attend_mfma_cache(g, p->q, p->k, p->v, use_sel, use_nsel, out,
                                                       rws, s),
                         "window attention from the cache (MFMA)");
+    }
+    if (rea::fused_decode_path(g)) {
+        void *fws = c.take<char>(rea::fused_ws_bytes(g));
+        return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out,
+                                                 fws, s),
+                        "fused gather + window attention");
     }
     int32_t *Wlen = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
     float *k_win = c.take<float>((size_t)g.n_blk * g.Hkv * g.W_cap * g.d * sizeof(float));
@@ -550,9 +550,10 @@ rea_status make_batch_geom(const rea_problem *p, const rea_params *a, int32_t ba
                     "block_q %d)", p->n_q, a->block_q);
     if (a->L < 1)
         return fail(REA_EINVAL, "batched decode needs L >= 1 (the query token is local)");
-    if (!rea::fused_decode_path(*g))
-        return fail(REA_EUNSUPPORTED, "batched decode needs at most 8 query heads per selection "
-                    "head (have %d)", g->g);
+    const bool mfma = rea::mfma_cache_attend_path(*g) && g->g <= 64;
+    if (!mfma && !rea::fused_decode_path(*g))
+        return fail(REA_EUNSUPPORTED, "batched decode needs at most %d query heads per selection "
+                    "head (have %d)", g->dtype == 0 && g->d == 128 ? 64 : 8, g->g);
     if ((int64_t)batch * g->Hkv >= ((int64_t)1 << 24) || (int64_t)batch * g->Hq >= ((int64_t)1 << 24))
         return fail(REA_EUNSUPPORTED, "batch %d too large", batch);
     g->hps = g->Hkv;
@@ -615,6 +616,12 @@ rea_status rea_decode_batch(const rea_problem *p, const rea_params *a, int32_t b
                                      nullptr),
                        "batched score_select")) != REA_OK)
         return st;
+    if (rea::mfma_cache_attend_path(g)) {
+        void *rws = c.take<char>(rea::rope_table_bytes(g));
+        return launched(rea::launch_attend_mfma_cache(g, p->q, p->k, p->v, use_sel, use_nsel, out,
+                                                      rws, s),
+                        "batched window attention from the cache (MFMA)");
+    }
     void *fws = c.take<char>(rea::fused_ws_bytes(g));
     return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out, fws, s),
                     "batched gather + window attention");
