@@ -15,10 +15,13 @@
 //         statistics stay lane-local (one exchange with the partner half-wave).
 //         Q' carries the softmax scale times log2(e): logits are in log2
 //         units and weights are single exp2s; the accumulators are rescaled
-//         only in tiles where some query's running maximum grows;
+//         only in tiles where some query's maximum outgrows the reference
+//         maximum the weights are taken against by more than 2^8;
 //   O^T += V^T P^T with V exact in bf16 and P rounded to bf16; V is staged
 //         transposed so each A fragment is one 16-byte LDS read.
-// The next tile's global loads are issued before this tile's MFMAs.
+// 8-wave workgroups run the tiles as a three-stage software pipeline (tile
+// it+2 staged, logits of tile it+1 on the MFMA pipe while tile it's softmax
+// runs on the VALU, then tile it's O update); 2-wave ones use one buffer.
 //
 // Two sources for the tiles (template parameter):
 //   window  the rotated window written by the gather step (rea_window_attend);
@@ -46,6 +49,7 @@ constexpr int kVPad = 40;           // V^T tile row stride (bf16)
 constexpr int kAThreads = 512;      // 8 waves (blocks of many query rows)
 constexpr int kRowsWG = kAThreads / 2;   // query rows per 8-wave workgroup (32 per wave)
 
+constexpr float kLazy = 8.f;         // log2 of the largest unnormalised weight
 constexpr int kSelCap = 4096;       // selection entries staged in LDS (cache source, 8 waves)
 // 2-wave workgroups (at most 64 query rows: decode steps, small blocks) take
 // at most kSmallTiles key tiles per split and stage only the selection
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
     static_assert(NW == 8 || (NW == 2 && kCache), "8 waves, or 2 waves on the cache source");
     constexpr int NT = 64 * NW;                 // threads
     constexpr int RW = 32 * NW;                 // query rows per workgroup
-    constexpr int NB = NW == 8 ? 2 : 1;         // LDS tile buffers
+    constexpr int NB = NW == 8 ? 3 : 1;         // LDS tile buffers
     constexpr int TPR = NT / kKT;               // staging threads per key row (16 or 4)
     constexpr int PG = 16 / TPR;                // groups of 4 channel pairs (K) / 8 channels (V) per thread
     constexpr int kSel = NW == 8 ? kSelCap : kSmallSel;
@@ -126,8 +130,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
     __shared__ __align__(16) uint16_t vt[NB][kD][kVPad];
     __shared__ int32_t ssel[kCache ? kSel : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sp = blockIdx.x % a.n_split;
-    const int unit = blockIdx.x / a.n_split;
+    // Later blocks of a chunk see more keys (causal): the grid runs them
+    // first, so that the shorter ones fill in behind them.
+    const int bid = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int sp = bid % a.n_split;
+    const int unit = bid / a.n_split;
     const int rg = unit % a.n_rg;
     const int bh = unit / a.n_rg;
     const int b = bh / a.Hkv, h = bh % a.Hkv;
@@ -236,9 +243,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
     const uint16_t *vwb = a.v_win + (int64_t)bh * a.W_cap * kD;
     const uint16_t *kcb = a.k + kv_off;
     const uint16_t *vcb = a.v + kv_off;
-    float4 kr[PG][2];           // window: 8 fp32 keys; cache: 4 x (cos, sin) per group
-    uint4 vr[PG];
-    uint2 kc[PG][2];
+    // one tile's staging registers
+    struct Stage {
+        float4 kr[PG][2];       // window: 8 fp32 keys; cache: 4 x (cos, sin) per group
+        uint4 vr[PG];
+        uint2 kc[PG][2];
+    };
     // cache row of window row wl (rows past the end read window row 0: finite
     // data that is masked or multiplied by a zero weight)
     auto src_row = [&](int64_t wl) -> int64_t {
@@ -254,38 +264,41 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
         }
         return src * a.st;
     };
-    auto load_tile = [&](int64_t w0) {
+    auto load_tile = [&](Stage &stg, int64_t w0) {
         const int64_t w = w0 + skey, wv = w0 + vkey;
         const bool ok = w < kend, okv = wv < kend;
         if (kCache) {
+            // lane l < 32 looks up key l of the tile (its V row); the K row
+            // of key skey comes from lane skey
             const int64_t wl = ok ? w : it0 * kKT;
-            const int64_t row = src_row(wl), rowv = src_row(okv ? wv : it0 * kKT);
+            const int64_t rowv = src_row(okv ? wv : it0 * kKT);
+            const int64_t row = __shfl(rowv, skey);
 #pragma unroll
             for (int gq = 0; gq < PG; ++gq) {
                 const int c = c0 + gq * 4;
-                kc[gq][0] = *(const uint2 *)(kcb + row + c);
-                kc[gq][1] = *(const uint2 *)(kcb + row + c + kD / 2);
-                vr[gq] = *(const uint4 *)(vcb + rowv + vch + gq * 8);
+                stg.kc[gq][0] = *(const uint2 *)(kcb + row + c);
+                stg.kc[gq][1] = *(const uint2 *)(kcb + row + c + kD / 2);
+                stg.vr[gq] = *(const uint4 *)(vcb + rowv + vch + gq * 8);
                 const float4 *rp = (const float4 *)(a.rope + wl * (kD / 2) + c);
-                kr[gq][0] = rp[0];
-                kr[gq][1] = rp[1];
+                stg.kr[gq][0] = rp[0];
+                stg.kr[gq][1] = rp[1];
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-                kr[0][e] = ok ? *(const float4 *)(kwb + w * kD + sch + e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            vr[0] = okv ? *(const uint4 *)(vwb + wv * kD + vch) : make_uint4(0u, 0u, 0u, 0u);
+                stg.kr[0][e] = ok ? *(const float4 *)(kwb + w * kD + sch + e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            stg.vr[0] = okv ? *(const uint4 *)(vwb + wv * kD + vch) : make_uint4(0u, 0u, 0u, 0u);
         }
     };
     // V^T from this lane's 8-channel groups of key vkey and lane^1's (key
     // vkey^1): the even lane writes the even channels, the odd lane the odd
     // ones, each word holding (key 2m, key 2m+1)
-    auto store_vt = [&](int bf) {
+    auto store_vt = [&](const Stage &stg, int bf) {
         const bool odd = (vkey & 1) != 0;
         uint32_t *vrow = (uint32_t *)&vt[bf][0][0];
 #pragma unroll
         for (int gq = 0; gq < PG; ++gq) {
-            const uint32_t w8[4] = {vr[gq].x, vr[gq].y, vr[gq].z, vr[gq].w};
+            const uint32_t w8[4] = {stg.vr[gq].x, stg.vr[gq].y, stg.vr[gq].z, stg.vr[gq].w};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const uint32_t send = odd ? (w8[m] & 0xffffu) : (w8[m] >> 16);
@@ -296,17 +309,17 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
             }
         }
     };
-    auto store_tile = [&](int bf) {
+    auto store_tile = [&](const Stage &stg, int bf) {
         if (kCache) {
 #pragma unroll
             for (int gq = 0; gq < PG; ++gq) {
                 const int c = c0 + gq * 4;
-                const float x1[4] = {__uint_as_float(kc[gq][0].x << 16), __uint_as_float(kc[gq][0].x & 0xffff0000u),
-                                     __uint_as_float(kc[gq][0].y << 16), __uint_as_float(kc[gq][0].y & 0xffff0000u)};
-                const float x2[4] = {__uint_as_float(kc[gq][1].x << 16), __uint_as_float(kc[gq][1].x & 0xffff0000u),
-                                     __uint_as_float(kc[gq][1].y << 16), __uint_as_float(kc[gq][1].y & 0xffff0000u)};
-                const float cs[4][2] = {{kr[gq][0].x, kr[gq][0].y}, {kr[gq][0].z, kr[gq][0].w},
-                                        {kr[gq][1].x, kr[gq][1].y}, {kr[gq][1].z, kr[gq][1].w}};
+                const float x1[4] = {__uint_as_float(stg.kc[gq][0].x << 16), __uint_as_float(stg.kc[gq][0].x & 0xffff0000u),
+                                     __uint_as_float(stg.kc[gq][0].y << 16), __uint_as_float(stg.kc[gq][0].y & 0xffff0000u)};
+                const float x2[4] = {__uint_as_float(stg.kc[gq][1].x << 16), __uint_as_float(stg.kc[gq][1].x & 0xffff0000u),
+                                     __uint_as_float(stg.kc[gq][1].y << 16), __uint_as_float(stg.kc[gq][1].y & 0xffff0000u)};
+                const float cs[4][2] = {{stg.kr[gq][0].x, stg.kr[gq][0].y}, {stg.kr[gq][0].z, stg.kr[gq][0].w},
+                                        {stg.kr[gq][1].x, stg.kr[gq][1].y}, {stg.kr[gq][1].z, stg.kr[gq][1].w}};
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -321,14 +334,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
                 *(uint2 *)&klo[bf][skey][c + kD / 2] = make_uint2(lo.z, lo.w);
             }
         } else {
-            const float x[8] = {kr[0][0].x, kr[0][0].y, kr[0][0].z, kr[0][0].w,
-                                kr[0][1].x, kr[0][1].y, kr[0][1].z, kr[0][1].w};
+            const float x[8] = {stg.kr[0][0].x, stg.kr[0][0].y, stg.kr[0][0].z, stg.kr[0][0].w,
+                                stg.kr[0][1].x, stg.kr[0][1].y, stg.kr[0][1].z, stg.kr[0][1].w};
             uint4 hi, lo;
             split8(x, hi, lo);
             *(uint4 *)&khi[bf][skey][sch] = hi;
             *(uint4 *)&klo[bf][skey][sch] = lo;
         }
-        store_vt(bf);
+        store_vt(stg, bf);
     };
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -338,34 +351,28 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) o[t][rr] = 0.f;
 
-    int buf = 0;
-    if (kCache) __syncthreads();        // ssel visible before the first row lookup
-    if (it1 > it0) {
-        load_tile(it0 * kKT);
-        store_tile(0);
-    }
-    __syncthreads();
-    for (int64_t it = it0; it < it1; ++it) {
-        const int64_t w0 = it * kKT;
-        const bool more = it + 1 < it1;
-        if (more) load_tile(w0 + kKT);
-
-        // S^T tile: rows = keys (A = K'), cols = queries (B = Q'^T)
-        f32x16 st = {};
+    // S^T tile from buffer bf: rows = keys (A = K'), cols = queries (B = Q'^T)
+    // (two accumulation chains, even and odd k-steps, so that consecutive
+    // MFMAs do not wait on each other's result)
+    auto logits = [&](int bf) {
+        f32x16 sa = {}, sb = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 ah = __builtin_bit_cast(bf16x8, *(const uint4 *)&khi[buf][n][ks * 16 + hb * 8]);
-            const bf16x8 al = __builtin_bit_cast(bf16x8, *(const uint4 *)&klo[buf][n][ks * 16 + hb * 8]);
+            const bf16x8 ah = __builtin_bit_cast(bf16x8, *(const uint4 *)&khi[bf][n][ks * 16 + hb * 8]);
+            const bf16x8 al = __builtin_bit_cast(bf16x8, *(const uint4 *)&klo[bf][n][ks * 16 + hb * 8]);
             const bf16x8 bh8 = __builtin_bit_cast(bf16x8, qh[ks]);
             const bf16x8 bl8 = __builtin_bit_cast(bf16x8, ql[ks]);
-            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh8, st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl8, st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh8, st, 0, 0, 0);
+            f32x16 &acc = (ks & 1) ? sb : sa;
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh8, acc, 0, 0, 0);
         }
-        // mask, online softmax (this lane's query; keys 8(rr/4) + 4hb + rr%4).
-        // Tiles wholly before every query of the wave and inside the window
-        // need no mask.
-        float x[16];
+        return sa + sb;
+    };
+    // mask (this lane's query; keys w0 + 8(rr/4) + 4hb + rr%4) and the
+    // running maximum.  Tiles wholly before every query of the wave and
+    // inside the window need no mask.
+    auto mask_max = [&](const f32x16 &st, int64_t w0, float (&x)[16]) {
         const int w0i = (int)w0, posi = (int)pos, Wi = (int)Wbh;
         const bool whole = w0i + kKT <= Wi && w0i + kKT - 1 <= posi;
         if (__builtin_amdgcn_read_exec() == __ballot(whole)) {
@@ -382,9 +389,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
 #pragma unroll
         for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
         mt = fmaxf(mt, __shfl_xor(mt, 32));
+        // lazy rescale: weights are taken against m_run until some query's
+        // maximum exceeds it by more than 2^kLazy (weights stay below 2^kLazy,
+        // far from fp32 and bf16 overflow)
         const float m_new = fmaxf(m_run, mt);
-        // rescale the accumulators only when some query's maximum moved
-        if (__ballot(m_new > m_run)) {
+        if (__ballot(m_new > m_run + kLazy)) {
             const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
@@ -393,23 +402,26 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
                 for (int rr = 0; rr < 16; ++rr) o[t][rr] *= alpha;
             m_run = m_new;
         }
+    };
+    // weights, their sum, and the B fragments of P^T: k-step s covers keys 16s ..
+    // 16s+15; this lane (kb = hb) needs keys 16s + 8hb + e; a lane holds keys
+    // 8a + 4hb + c.  P is rounded to bf16 first (packed pairs), then
+    // v_permlane32_swap of (keys 8(2s) + 4hb .., keys 8(2s+1) + 4hb ..) leaves
+    // keys 16s + e in the first register and 16s + 8 + e in the second on
+    // both halves.
+    auto weights = [&](const float (&x)[16], uint4 (&pb)[2]) {
+        // a query that has seen no key yet has m_run = -inf and every x = -inf:
+        // its weights are exp2(-inf - 0) = 0
+        const float mu = m_run == -INFINITY ? 0.f : m_run;
         float p[16];
         float lt = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            // exp2(-inf) = 0; m_run is finite once the query has seen a key
-            p[rr] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[rr] - m_run);
+            p[rr] = __builtin_amdgcn_exp2f(x[rr] - mu);
             lt += p[rr];
         }
         lt += __shfl_xor(lt, 32);
         l_run += lt;
-
-        // B fragments of P^T: k-step s covers keys 16s .. 16s+15; this lane
-        // (kb = hb) needs keys 16s + 8hb + e; a lane holds keys 8a + 4hb + c.
-        // P is rounded to bf16 first (packed pairs), then v_permlane32_swap of
-        // (keys 8(2s) + 4hb .., keys 8(2s+1) + 4hb ..) leaves keys 16s + e in
-        // the first register and 16s + 8 + e in the second on both halves.
-        uint4 pb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const uint32_t e0 = pack_bf16(p[8 * s], p[8 * s + 1]);
@@ -420,23 +432,88 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnA
             const auto x1 = __builtin_amdgcn_permlane32_swap(e1, o1, false, false);
             pb[s] = make_uint4(x0[0], x1[0], x0[1], x1[1]);
         }
-        // O^T (channels x queries) += V^T (channels x keys) P^T (keys x queries)
+    };
+    // O^T (channels x queries) += V^T (channels x keys) P^T (keys x queries)
+    auto accumulate = [&](int bf, const uint4 (&pb)[2]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, *(const uint4 *)&vt[buf][t * 32 + n][s * 16 + hb * 8]);
+                const bf16x8 av = __builtin_bit_cast(bf16x8, *(const uint4 *)&vt[bf][t * 32 + n][s * 16 + hb * 8]);
                 o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, pb[s]),
                                                                o[t], 0, 0, 0);
             }
-        if (NB == 2) {
-            if (more) store_tile(buf ^ 1);
+    };
+
+    if (kCache) __syncthreads();        // ssel visible before the first row lookup
+    if (NB == 3) {
+        // Software pipeline over three tile buffers: while tile it's softmax
+        // runs on the VALU, the logits of tile it+1 are on the MFMA pipe, and
+        // tile it+2 is staged into the buffer tile it-1 used.  Staging and the
+        // logits past the split's last tile run on clamped rows whose results
+        // are never used, so the loop body has no branch around them.  One
+        // barrier per tile: buffer (it+2)%3 was last read by tile it-1's
+        // O update, before the previous barrier.
+        //
+        // Waves w and w+4 share a SIMD; they take the phases of an iteration
+        // in opposite order (ping-pong) so that one wave's MFMA work overlaps
+        // the other's VALU work: waves 0-3 multiply first and stage last,
+        // waves 4-7 stage first (from registers loaded one iteration earlier)
+        // and multiply last.
+        const bool lead = wave < 4;
+        Stage sa;
+        if (it1 > it0) {
+            load_tile(sa, it0 * kKT);
+            store_tile(sa, 0);
+            load_tile(sa, (it0 + 1) * kKT);
+            store_tile(sa, 1);
+        }
+        if (!lead) load_tile(sa, (it0 + 2) * kKT);
+        __syncthreads();
+        f32x16 st = logits(0);
+        int bcur = 0;
+        for (int64_t it = it0; it < it1; ++it) {
+            const int bnext = bcur == 2 ? 0 : bcur + 1;
+            const int bfill = bnext == 2 ? 0 : bnext + 1;
+            float x[16];
+            uint4 pb[2];
+            if (lead) {
+                load_tile(sa, (it + 2) * kKT);
+                mask_max(st, it * kKT, x);
+                st = logits(bnext);
+                weights(x, pb);
+                accumulate(bcur, pb);
+                store_tile(sa, bfill);
+            } else {
+                store_tile(sa, bfill);
+                load_tile(sa, (it + 3) * kKT);
+                mask_max(st, it * kKT, x);
+                weights(x, pb);
+                st = logits(bnext);
+                accumulate(bcur, pb);
+            }
             __syncthreads();
-            buf ^= 1;
-        } else {
-            // one buffer: every wave has read it before it is refilled
+            bcur = bnext;
+        }
+    } else {
+        // one buffer: every wave has read it before it is refilled
+        Stage sa;
+        if (it1 > it0) {
+            load_tile(sa, it0 * kKT);
+            store_tile(sa, 0);
+        }
+        __syncthreads();
+        for (int64_t it = it0; it < it1; ++it) {
+            const bool more = it + 1 < it1;
+            if (more) load_tile(sa, (it + 1) * kKT);
+            const f32x16 st = logits(0);
+            float x[16];
+            mask_max(st, it * kKT, x);
+            uint4 pb[2];
+            weights(x, pb);
+            accumulate(0, pb);
             __syncthreads();
-            if (more) store_tile(0);
+            if (more) store_tile(sa, 0);
             __syncthreads();
         }
     }
