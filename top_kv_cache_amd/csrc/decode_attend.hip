@@ -26,7 +26,7 @@
 //                    weights and P.V; the workgroup's 16 streams are merged
 //                    through LDS with the usual (m, l, acc) rule and one
 //                    partial per split is written.
-//   k_fused_combine  one workgroup per (KV head, block) merges the splits:
+//   k_fused_combine  workgroups per (KV head, block) merge the splits:
 //                    out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s
 //                    (maxima m_s in log2 units).
 #include "rea_internal.h"
@@ -42,7 +42,7 @@ constexpr int kThreads = 256;
 constexpr int kSL = 8;                          // rows per stream
 constexpr int kRowsPerSplit = 4 * 4 * kSL;      // waves x streams x rows
 constexpr int kSelStage = kRowsPerSplit + 2;    // selection slots a split can touch (S = 1)
-constexpr int kCombBatch = 16;                  // partials loaded together by the merge
+constexpr int kCombBatch = 8;                   // partials loaded together by the merge
 
 struct FusedArgs {
     const unsigned char *k, *v;
@@ -54,6 +54,7 @@ struct FusedArgs {
     int64_t sh, st;         // elements
     int64_t T, Gp, Lp, mid_lo, n_spans;
     int S, last_len, topk, Hkv, Hq, g, n_q, block_q, QR, n_split, rep;
+    int comb_tpi;           // merge phases per item (power of two)
     // batched decode (see Geom): per-sequence lengths and cache offsets
     const int64_t *lens;
     int hps, G, L;
@@ -388,10 +389,11 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     }
 }
 
-// grid (Hkv, n_blk): merges the splits of one (block, KV head).  Thread =
-// (query row r, channel quad, split phase j); each thread folds its splits
-// into a running (m, l, acc), loading kCombBatch partials at a time, and the
-// phases are folded in LDS.
+// grid (Hkv, n_blk, item slices): merges the splits of one (block, KV head).
+// Thread = (query row r, channel quad, split phase j); comb_tpi phases, so
+// each thread folds at most kCombBatch splits (one round of loads) into a
+// running (m, l, acc), and the phases are folded in LDS.  A workgroup takes
+// kThreads / comb_tpi of the QR x D/4 items.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_fused_combine(FusedArgs a) {
     constexpr int NQ = D / 4;
@@ -402,12 +404,14 @@ __global__ __launch_bounds__(kThreads) void k_fused_combine(FusedArgs a) {
     const int64_t bh = (int64_t)b * a.Hkv + h;
     const int64_t pbase = bh * a.n_split * a.QR;
     const int items = a.QR * NQ;
-    const int tpi = kThreads / items;
-    const int item = tid % items, j = tid / items;
-    const int r = item / NQ, cq = item % NQ;
+    const int tpi = a.comb_tpi, ipw = kThreads / tpi;
+    const int il = tid % ipw, j = tid / ipw;
+    const int item = blockIdx.z * ipw + il;
+    const bool live = item < items;
+    const int r = live ? item / NQ : 0, cq = item % NQ;
     float M = -INFINITY, L = 0.f;
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (j < tpi) {
+    if (live) {
         for (int s0 = j; s0 < a.n_split; s0 += kCombBatch * tpi) {
             float2 ml[kCombBatch];
             float4 x[kCombBatch];
@@ -437,9 +441,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_combine(FusedArgs a) {
     cl[tid] = L;
     ca[tid] = A;
     __syncthreads();
-    if (tid < items) {
+    if (j == 0 && live) {
         for (int jj = 1; jj < tpi; ++jj) {
-            const int o = jj * items + tid;
+            const int o = jj * ipw + il;
             const float mn = fmaxf(M, cm[o]);
             if (mn == -INFINITY) continue;
             const float f = __builtin_amdgcn_exp2f(M - mn), fo = __builtin_amdgcn_exp2f(cm[o] - mn);
@@ -464,7 +468,9 @@ hipError_t launch_typed(const Geom &g, const FusedArgs &a, hipStream_t s) {
                        dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_fused_combine<D>), dim3(g.Hkv, g.n_blk), dim3(kThreads), 0, s, a);
+    const int ipw = kThreads / a.comb_tpi;
+    const int slices = (a.QR * (D / 4) + ipw - 1) / ipw;
+    hipLaunchKernelGGL((k_fused_combine<D>), dim3(g.Hkv, g.n_blk, slices), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -520,6 +526,12 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
     a.block_q = g.block_q;
     a.QR = g.block_q * g.g;
     a.n_split = fused_n_split(g.W_cap);
+    // merge phases: the fewest (a power of two) that leave each thread at
+    // most kCombBatch splits, and at least enough to fill the workgroup
+    int tpi = 1;
+    while (tpi < 64 && tpi * kCombBatch < a.n_split) tpi *= 2;
+    while (kThreads / tpi > a.QR * (g.d / 4) && tpi < kThreads) tpi *= 2;
+    a.comb_tpi = tpi;
     a.scale_log2 = (float)((double)g.scale * 1.4426950408889634074);
     for (int c = 0; c < kMaxHalfDim; ++c) {
         const double f = c < g.d / 2 ? pow(g.theta, -2.0 * (double)c / (double)g.d) : 0.0;
