@@ -735,14 +735,17 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
                 //     rank among them (score desc, index asc) is its rank among
                 //     all spans: rank every candidate pairwise, keep ranks < kk,
                 //     and place each kept span by the kept indices below it.
+                //     Both counts are split into slices of the compared range,
+                //     one thread per (entry, slice), summed through LDS.
                 if (tid == 0) cm.count = 0;
-                __syncthreads();
-                for (uint32_t c = tid; c < count; c += kThreads) {
+                const uint32_t ns = count ? kThreads / count : 1;         // >= 2
+                if (tid < ns * count) {
+                    const uint32_t c = tid % count, sl = tid / count;
+                    const uint32_t o0 = sl * count / ns, o1 = (sl + 1) * count / ns;
                     const double x = f.val[c];
                     const int32_t jc = f.idx[c];
-                    int rank = 0;
-                    uint32_t o = 0;
-                    for (; o + 8 <= count; o += 8) {
+                    uint32_t rank = 0, o = o0;
+                    for (; o + 8 <= o1; o += 8) {
                         double y[8];
                         int32_t yi[8];
 #pragma unroll
@@ -753,24 +756,38 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
 #pragma unroll
                         for (int u2 = 0; u2 < 8; ++u2) rank += (y[u2] > x) || (y[u2] == x && yi[u2] < jc);
                     }
-                    for (; o < count; ++o) rank += (f.val[o] > x) || (f.val[o] == x && f.idx[o] < jc);
-                    if (rank < kk) f.gidx[atomicAdd(&cm.count, 1u)] = jc;
+                    for (; o < o1; ++o) rank += (f.val[o] > x) || (f.val[o] == x && f.idx[o] < jc);
+                    f.hist[tid] = rank;
+                }
+                __syncthreads();
+                for (uint32_t c = tid; c < count; c += kThreads) {
+                    uint32_t rank = 0;
+                    for (uint32_t sl = 0; sl < ns; ++sl) rank += f.hist[sl * count + c];
+                    if (rank < (uint32_t)kk) f.gidx[atomicAdd(&cm.count, 1u)] = f.idx[c];
                 }
                 __syncthreads();
                 if (sel) {
-                    for (int t = tid; t < kk; t += kThreads) {
+                    const uint32_t nk = (uint32_t)kk, ns2 = kThreads / nk;  // >= 2
+                    if (tid < ns2 * nk) {
+                        const uint32_t t = tid % nk, sl = tid / nk;
+                        const uint32_t o0 = sl * nk / ns2, o1 = (sl + 1) * nk / ns2;
                         const int32_t jt = f.gidx[t];
-                        int pos = 0;
-                        int o = 0;
-                        for (; o + 8 <= kk; o += 8) {
+                        uint32_t pos = 0, o = o0;
+                        for (; o + 8 <= o1; o += 8) {
                             int32_t yi[8];
 #pragma unroll
                             for (int u2 = 0; u2 < 8; ++u2) yi[u2] = f.gidx[o + u2];
 #pragma unroll
                             for (int u2 = 0; u2 < 8; ++u2) pos += yi[u2] < jt;
                         }
-                        for (; o < kk; ++o) pos += f.gidx[o] < jt;
-                        sel[pos] = jt;
+                        for (; o < o1; ++o) pos += f.gidx[o] < jt;
+                        f.hist[tid] = pos;
+                    }
+                    __syncthreads();
+                    for (uint32_t t = tid; t < nk; t += kThreads) {
+                        uint32_t pos = 0;
+                        for (uint32_t sl = 0; sl < ns2; ++sl) pos += f.hist[sl * nk + t];
+                        sel[pos] = f.gidx[t];
                     }
                     for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
                 }
