@@ -116,8 +116,11 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 &u, float (&x)[8]) {
     }
 }
 
+// The occupancy hint of one wave per SIMD lets the 2-wave variant (4 staging
+// groups per thread) keep everything in registers, accumulators in AGPRs,
+// instead of spilling 132 bytes per lane to scratch (15-20% faster).
 template <bool kCache, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void k_attend_mfma(MAttnArgs a) {
+__global__ __launch_bounds__(64 * NW, 1) void k_attend_mfma(MAttnArgs a) {
     static_assert(NW == 8 || (NW == 2 && kCache), "8 waves, or 2 waves on the cache source");
     constexpr int NT = 64 * NW;                 // threads
     constexpr int RW = 32 * NW;                 // query rows per workgroup
