@@ -455,6 +455,7 @@ constexpr int kCCap = 4096;         // spans handled on chip
 constexpr int kCBins = 2048;
 constexpr int kCRank = 256;
 constexpr int kCPer = kCCap / kCThreads;
+constexpr int kCSplit = 256;        // uncertain spans re-scored as two items each
 
 struct CertArgs {
     const double *shat;     // [n_blk][Hkv][n_spans]
@@ -709,13 +710,14 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
         // accumulates the 8 dot products of its token with queries
         // sub*16 + part*8 .. +8 in fp64 (the products of a bf16 key with q_eff
         // are exact), the per-query maxima over the 32 token lanes come from a
-        // transpose-reduce, and the 16 maxima are summed.  When the spans are
-        // too few to occupy every wave (nx <= 4) the two parts of a span run on
-        // different waves, their sums kept apart in val (free during
-        // re-scoring) and added in a fixed order; otherwise one wave takes
-        // both parts of its span in turn.
+        // transpose-reduce, and the 16 maxima are summed.  Up to kCSplit
+        // uncertain spans, the two parts of a span are separate items (the
+        // 2 nx equal items then spread evenly over the SIMDs; whole spans
+        // would leave some SIMDs a span more than others), their sums kept
+        // apart in val (free during re-scoring) and added in a fixed order;
+        // beyond that one wave takes both parts of its span in turn.
         const int tl = lane & 31, sub = lane >> 5;
-        const bool split = nx <= (uint32_t)(kCWaves / 2);
+        const bool split = nx <= (uint32_t)kCSplit;
         const uint32_t n_items = split ? 2 * nx : nx;
         const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
         for (int qh = 0; qh < 2; ++qh) {
