@@ -59,7 +59,7 @@ typedef enum rea_status {
     REA_EWORKSPACE = 5,    /* workspace smaller than rea_query_sizes() asks for */
     REA_ENODEVICE = 6,     /* no usable HIP device */
     REA_ELAUNCH = 7,       /* a kernel launch failed (hipGetLastError) */
-    REA_EUNSUPPORTED = 8   /* valid arguments outside what this build implements */
+    REA_EUNSUPPORTED = 8   /* valid arguments outside what the library implements */
 } rea_status;
 
 enum {

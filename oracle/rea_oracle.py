@@ -44,7 +44,7 @@ Sources (the page title and the part of it each step follows):
       - the reply on token eviction: nothing is evicted and selection is
         redone per head, layer and step.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * GQA: one selection per KV head, scoring with the sum of the group's
     query-head logits (step 3).  Variant (per_q_head=True): one selection per
     query head with its own logits, its window gathered from its group's KV

@@ -48,7 +48,7 @@ rea_status make_geom(const rea_problem *p, const rea_params *a, rea::Geom *g) {
         return fail(REA_ESHAPE, "n_q_heads %d is not a positive multiple of n_kv_heads %d",
                     p->n_q_heads, p->n_kv_heads);
     if (p->head_dim != 64 && p->head_dim != 128)
-        return fail(REA_EUNSUPPORTED, "head_dim %d: this build implements 64 and 128",
+        return fail(REA_EUNSUPPORTED, "head_dim %d: the library implements 64 and 128",
                     p->head_dim);
     if (p->T < p->n_q || p->T >= ((int64_t)1 << 31))
         return fail(REA_ESHAPE, "T %lld must satisfy n_q <= T < 2^31", (long long)p->T);
