@@ -74,6 +74,10 @@ SMALL = {
                                     L=96, needles=0, kv_scaled=True),
     "pqh_bf16_blocks_64_rows": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,
                                  L=128, needles=0, per_q_head=True),
+    # token level over more than 32768 groups of 32 tokens: the top-k's large
+    # path streams the group maxima instead of holding them in registers
+    "bf16_token_level_33k_groups": S(Hq=2, Hkv=1, d=64, T=1_060_000, S=1, topk=300, L=64,
+                                     needles=2),
     # token segments: the best tokens, each widened to S tokens
     "seg_bf16_d64": S(S=8, topk=6, T=700, token_segments=True),
     "seg_bf16_d128_pqh": S(Hq=8, Hkv=2, d=128, T=2048, S=32, topk=12, L=256, needles=2,

@@ -106,6 +106,31 @@ __device__ __forceinline__ int bin_of(double x, double mn, double inv, int nbins
 }
 
 // Workgroup min / max / sum; every thread gets the results.
+// LDS slots for the flagged items of U per-lane flags, appended at *counter:
+// one atomic per wave (the wave's flags are counted with ballots), not one per
+// item, so thousands of appends do not serialise on one LDS address.  Every
+// lane of the wave must take part.
+template <int U>
+__device__ __forceinline__ void wave_append(uint32_t *counter, const bool (&flag)[U],
+                                            uint32_t (&slot)[U]) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long bal[U];
+    uint32_t pre[U], tot = 0;
+#pragma unroll
+    for (int e = 0; e < U; ++e) {
+        bal[e] = __ballot(flag[e]);
+        pre[e] = tot;
+        tot += (uint32_t)__popcll(bal[e]);
+    }
+    uint32_t base = 0;
+    if (lane == 0 && tot) base = atomicAdd(counter, tot);
+    base = (uint32_t)__shfl((int)base, 0);
+#pragma unroll
+    for (int e = 0; e < U; ++e)
+        slot[e] = base + pre[e] +
+                  __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[e], 0u));
+}
+
 __device__ __forceinline__ void block_minmax_count(Common &cm, double &mn, double &mx, uint32_t &cnt) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int o = 32; o > 0; o >>= 1) {
@@ -267,18 +292,21 @@ __device__ __forceinline__ void find_kth(Common &cm, uint32_t *hist, double *val
         }
         if (tid == 0) cm.count = 0;
         __syncthreads();
+        bool keep[kPerThread];
+        uint32_t slot[kPerThread];
 #pragma unroll
         for (int e = 0; e < kPerThread; ++e) {
             const uint32_t c = tid + (uint32_t)e * kThreads;
-            if (c < count) {
-                const double k = by_index ? -(double)ri[e] : rv[e];
-                if (bin_of(k, mn, inv, kBins) == bstar) {
-                    const uint32_t slot = atomicAdd(&cm.count, 1u);
-                    val[slot] = rv[e];
-                    idx[slot] = ri[e];
-                }
-            }
+            const double k = by_index ? -(double)ri[e] : rv[e];
+            keep[e] = c < count && bin_of(k, mn, inv, kBins) == bstar;
         }
+        wave_append(&cm.count, keep, slot);
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e)
+            if (keep[e]) {
+                val[slot[e]] = rv[e];
+                idx[slot[e]] = ri[e];
+            }
         __syncthreads();
         count = cm.count;
         __syncthreads();
@@ -295,32 +323,96 @@ __device__ __forceinline__ void find_kth(Common &cm, uint32_t *hist, double *val
 // 8 * kThreads consecutive groups, e-major), calling f(i, x) for each.
 template <typename F>
 __device__ __forceinline__ void for_each_gmax(const double *gm, int64_t m, F f) {
+    constexpr int B = 16;                       // loads in flight per thread
     const int tid = threadIdx.x;
-    for (int64_t b0 = 0; b0 < m; b0 += 8 * kThreads) {
-        double x[8];
+    for (int64_t b0 = 0; b0 < m; b0 += B * kThreads) {
+        double x[B];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < B; ++e) {
             const int64_t i = b0 + e * kThreads + tid;
             x[e] = gm[i < m ? i : m - 1];
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < B; ++e) {
             const int64_t i = b0 + e * kThreads + tid;
             if (i < m) f(i, x[e]);
         }
     }
 }
 
-__device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const double *sc,
-                                           const double *gm, int64_t n, int64_t m, int kk,
-                                           int topk, int32_t *sel) {
+// The group maxima as steps 1-2 of the large path read them: streamed from
+// global memory (16 loads in flight per thread) each time, or, when there are
+// at most kGReg * kThreads of them, loaded once into registers as fp32 values
+// rounded up (reg[k] = gm[k * kThreads + tid] rounded toward +inf).  Rounding
+// up is monotone, so with the rounded values step 1 finds a tau_r <= the
+// rounded kk-th largest maximum, and the fp32 value just below tau_r is <= the
+// exact kk-th largest maximum: a valid bound.  Step 2 then keeps every group
+// whose rounded maximum reaches it, a superset of the groups whose exact
+// maximum does.
+constexpr int kGReg = 64;
+template <bool kRegs> struct GmaxSource {
+    const double *gm;
+    int64_t m;
+    float reg[kRegs ? kGReg : 1];
+    __device__ void load() {
+        if constexpr (kRegs) {
+            constexpr int C = 16;                   // loads in flight per thread
+#pragma unroll
+            for (int k0 = 0; k0 < kGReg; k0 += C) {
+                double x[C];
+#pragma unroll
+                for (int k = 0; k < C; ++k) {
+                    const int64_t i = (int64_t)(k0 + k) * kThreads + threadIdx.x;
+                    x[k] = gm[i < m ? i : m - 1];
+                }
+#pragma unroll
+                for (int k = 0; k < C; ++k) reg[k0 + k] = __double2float_ru(x[k]);
+            }
+        }
+    }
+    template <typename F> __device__ void each(F f) const {
+        if constexpr (kRegs) {
+#pragma unroll
+            for (int k = 0; k < kGReg; ++k) {
+                const int64_t i = (int64_t)k * kThreads + threadIdx.x;
+                // (an empty asm pins the widening to this pass; hoisted out of
+                // the passes, 64 doubles would not fit in registers)
+                float v = reg[k];
+                __asm__ volatile("" : "+v"(v));
+                if (i < m) f(i, (double)v);
+            }
+        } else {
+            for_each_gmax(gm, m, f);
+        }
+    }
+    // batch bb of 8 * kThreads groups: x[e] = gm[bb * 8 * kThreads + e * kThreads + tid]
+    __device__ void batch(int64_t b0, int bb, double (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (kRegs) {
+                float v = reg[bb * 8 + e];
+                __asm__ volatile("" : "+v"(v));
+                x[e] = (double)v;
+            } else {
+                const int64_t i = b0 + e * kThreads + threadIdx.x;
+                x[e] = gm[i < m ? i : m - 1];
+            }
+        }
+    }
+};
+
+template <bool kRegs>
+__device__ __forceinline__ uint32_t large_tau_groups(Common &cm, LargeShared &L, const double *gm,
+                                                     int64_t m, int kk, double &tau_out) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    GmaxSource<kRegs> src{gm, m, {}};
+    src.load();
     // 1. tau: the smallest group maximum in the histogram bins at or above the
     //    one holding the kk-th largest maximum (a lower bound of the kk-th
     //    largest span score)
     double mn = INFINITY, mx = -INFINITY;
     uint32_t dummy = 0;
-    for_each_gmax(gm, m, [&](int64_t, double x) {
+    src.each([&](int64_t, double x) {
         mn = fmin(mn, x);
         mx = fmax(mx, x);
     });
@@ -330,29 +422,29 @@ __device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const dou
         const double inv = (double)kBins / (mx - mn);
         for (int i = tid; i < kBins; i += kThreads) L.hist[i] = 0u;
         __syncthreads();
-        for_each_gmax(gm, m, [&](int64_t, double x) {
-            atomicAdd(&L.hist[bin_of(x, mn, inv, kBins)], 1u);
-        });
+        src.each([&](int64_t, double x) { atomicAdd(&L.hist[bin_of(x, mn, inv, kBins)], 1u); });
         __syncthreads();
         find_bin(cm, L.hist, kBins, kk);
         const int bstar = cm.bstar;
         double lo = INFINITY, unused = -INFINITY;
-        for_each_gmax(gm, m, [&](int64_t, double x) {
+        src.each([&](int64_t, double x) {
             if (bin_of(x, mn, inv, kBins) >= bstar) lo = fmin(lo, x);
         });
         block_minmax_count(cm, lo, unused, dummy);
         tau = lo;
     }
+    if constexpr (kRegs) tau = (double)nextafterf((float)tau, -INFINITY);
+    tau_out = tau;
     // 2. candidate groups (maximum >= tau) in ascending order: per batch of
     //    8 * kThreads groups, the count of every (e, wave) slice orders the writes
     uint32_t ncg = 0;
-    for (int64_t b0 = 0; b0 < m; b0 += 8 * kThreads) {
+    constexpr int kMaxBatches = kRegs ? kGReg / 8 : 1 << 30;
+#pragma unroll kRegs ? kGReg / 8 : 1
+    for (int bb = 0; bb < kMaxBatches; ++bb) {
+        const int64_t b0 = (int64_t)bb * 8 * kThreads;
+        if (b0 >= m) break;
         double x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t i = b0 + e * kThreads + tid;
-            x[e] = gm[i < m ? i : m - 1];
-        }
+        src.batch(b0, bb, x);
         unsigned long long bal[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -376,40 +468,65 @@ __device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const dou
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t off = ncg + L.wpre[e * kWaves + wave];
-            const unsigned long long bb = bal[e];
-            if ((bb >> lane) & 1ull) {
+            const unsigned long long bb2 = bal[e];
+            if ((bb2 >> lane) & 1ull) {
                 const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-                    (uint32_t)(bb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u));
+                    (uint32_t)(bb2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bb2, 0u));
                 const uint32_t slot = off + below;
                 if (slot < (uint32_t)kLGroups) L.cgrp[slot] = (int32_t)(b0 + e * kThreads + tid);
             }
         }
         ncg += L.wpre[64];
+        __syncthreads();                 // wcnt / wpre are rewritten by the next batch
     }
+    return ncg;
+}
+
+__device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const double *sc,
+                                           const double *gm, int64_t n, int64_t m, int kk,
+                                           int topk, int32_t *sel) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    double tau;
+    const uint32_t ncg = m <= (int64_t)kGReg * kThreads ? large_tau_groups<true>(cm, L, gm, m, kk, tau)
+                                                        : large_tau_groups<false>(cm, L, gm, m, kk, tau);
     if (ncg > (uint32_t)kLGroups) return false;
     if (tid == 0) cm.count = 0;
     __syncthreads();
-    // 3. their spans scoring >= tau (half a wave per group, U groups in flight)
-    constexpr int U = 8;
+    // 3. their spans scoring >= tau (half a wave per group, U groups in
+    //    flight).  A candidate is recorded by its position p = c * 32 + lane
+    //    in the ascending candidate groups, which orders like its span index.
+    constexpr int U = 32;
     const int half = tid >> 5, hl = tid & 31;
     constexpr int GPI = kThreads / 32;                 // groups per pass (16)
     for (uint32_t c0 = 0; c0 < ncg; c0 += GPI * U) {
         double x[U];
-        int64_t j[U];
+        bool ok[U];
+        // (the group index is read unconditionally, clamped, so the LDS reads
+        // are issued together and the loads follow without a wait per read)
+        int32_t gi[U];
 #pragma unroll
         for (int e = 0; e < U; ++e) {
             const uint32_t c = c0 + e * GPI + half;
-            j[e] = c < ncg ? (int64_t)L.cgrp[c] * kGroup + hl : n;
-            x[e] = sc[j[e] < n ? j[e] : n - 1];
+            gi[e] = L.cgrp[c < ncg ? c : ncg - 1];
         }
 #pragma unroll
         for (int e = 0; e < U; ++e) {
-            if (j[e] < n && x[e] >= tau) {
-                const uint32_t slot = atomicAdd(&cm.count, 1u);
-                if (slot < (uint32_t)kCandCap) {
-                    L.val[slot] = x[e];
-                    L.idx[slot] = (int32_t)j[e];
-                }
+            // (span indices are below 2^31: 32-bit offsets from one base)
+            const uint32_t c = c0 + e * GPI + half;
+            const uint32_t j = (uint32_t)gi[e] * kGroup + hl;
+            ok[e] = c < ncg && j < (uint64_t)n;
+            x[e] = sc[j < (uint64_t)n ? j : (uint32_t)(n - 1)];
+        }
+        bool keep[U];
+        uint32_t slot[U];
+#pragma unroll
+        for (int e = 0; e < U; ++e) keep[e] = ok[e] && x[e] >= tau;
+        wave_append(&cm.count, keep, slot);
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+            if (keep[e] && slot[e] < (uint32_t)kCandCap) {
+                L.val[slot[e]] = x[e];
+                L.idx[slot[e]] = (int32_t)((c0 + e * GPI + half) * kGroup + hl);
             }
         }
     }
@@ -417,29 +534,33 @@ __device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const dou
     const uint32_t count = cm.count;
     __syncthreads();
     if (count > (uint32_t)kCandCap) return false;
+    // the candidates stay in registers for step 5 (the cutoff search below
+    // reorders the LDS copy)
+    double rv[kPerThread];
+    int32_t rp[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+        const uint32_t c = tid + (uint32_t)e * kThreads;
+        rv[e] = c < count ? L.val[c] : 0.0;
+        rp[e] = c < count ? L.idx[c] : -1;
+    }
+    __syncthreads();
     // 4. the kk-th best candidate = the cutoff
     find_kth(cm, L.hist, L.val, L.idx, count, kk);
     const double cv = cm.cut_v;
     const int64_t cj = cm.cut_j;
     // 5. one selection word per candidate group (over the candidate values,
-    //    which are no longer needed), then one ordered scan writes the indices
+    //    which are no longer needed), set from the candidates in registers
+    //    (every selected span is a candidate), then one ordered scan writes
+    //    the indices
     uint32_t *words = reinterpret_cast<uint32_t *>(L.val);
-    for (uint32_t c0 = 0; c0 < ncg; c0 += GPI * U) {
-        double x[U];
-        int64_t j[U];
+    for (uint32_t c = tid; c < ncg; c += kThreads) words[c] = 0u;
+    __syncthreads();
 #pragma unroll
-        for (int e = 0; e < U; ++e) {
-            const uint32_t c = c0 + e * GPI + half;
-            j[e] = c < ncg ? (int64_t)L.cgrp[c] * kGroup + hl : n;
-            x[e] = sc[j[e] < n ? j[e] : n - 1];
-        }
-#pragma unroll
-        for (int e = 0; e < U; ++e) {
-            const uint32_t c = c0 + e * GPI + half;
-            const bool pick = j[e] < n && (x[e] > cv || (x[e] == cv && j[e] <= cj));
-            const unsigned long long bal = __ballot(pick);
-            if (hl == 0 && c < ncg) words[c] = (uint32_t)(bal >> (lane & 32));
-        }
+    for (int e = 0; e < kPerThread; ++e) {
+        const int32_t pp = rp[e];
+        if (pp >= 0 && (rv[e] > cv || (rv[e] == cv && pp <= cj)))
+            atomicOr(&words[pp >> 5], 1u << (pp & 31));
     }
     __syncthreads();
     constexpr int WPT = kLGroups / kThreads;           // 16 words per thread
@@ -692,13 +813,15 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         // candidate groups: maximum >= tau
         if (tid == 0) cm.count = 0;
         __syncthreads();
+        {
+            bool keep[GPT];
+            uint32_t slot[GPT];
 #pragma unroll
-        for (int e = 0; e < GPT; ++e) {
-            const int i = tid + e * kThreads;
-            if (i < m && gr[e] >= tau) {
-                const uint32_t slot = atomicAdd(&cm.count, 1u);
-                if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
-            }
+            for (int e = 0; e < GPT; ++e) keep[e] = tid + e * kThreads < m && gr[e] >= tau;
+            wave_append(&cm.count, keep, slot);
+#pragma unroll
+            for (int e = 0; e < GPT; ++e)
+                if (keep[e] && slot[e] < (uint32_t)kMaxCandGroups) f.cgrp[slot[e]] = tid + e * kThreads;
         }
         __syncthreads();
         const uint32_t ncg = cm.count;
@@ -719,13 +842,18 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             }
             if (tid == 0) cm.count = 0;
             __syncthreads();
+            {
+                bool keep[CPT];
+                uint32_t slot[CPT];
 #pragma unroll
-            for (int it = 0; it < CPT; ++it) {
-                if (cjx[it] >= 0 && cx[it] >= tau) {
-                    const uint32_t slot = atomicAdd(&cm.count, 1u);
-                    f.val[slot] = cx[it];
-                    f.idx[slot] = cjx[it];
-                }
+                for (int it = 0; it < CPT; ++it) keep[it] = cjx[it] >= 0 && cx[it] >= tau;
+                wave_append(&cm.count, keep, slot);
+#pragma unroll
+                for (int it = 0; it < CPT; ++it)
+                    if (keep[it]) {
+                        f.val[slot[it]] = cx[it];
+                        f.idx[slot[it]] = cjx[it];
+                    }
             }
             __syncthreads();
             const uint32_t count = cm.count;
