@@ -813,15 +813,14 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         // candidate groups: maximum >= tau
         if (tid == 0) cm.count = 0;
         __syncthreads();
-        {
-            bool keep[GPT];
-            uint32_t slot[GPT];
+        // (about k appends: one LDS atomic each is cheaper than the ballots)
 #pragma unroll
-            for (int e = 0; e < GPT; ++e) keep[e] = tid + e * kThreads < m && gr[e] >= tau;
-            wave_append(&cm.count, keep, slot);
-#pragma unroll
-            for (int e = 0; e < GPT; ++e)
-                if (keep[e] && slot[e] < (uint32_t)kMaxCandGroups) f.cgrp[slot[e]] = tid + e * kThreads;
+        for (int e = 0; e < GPT; ++e) {
+            const int i = tid + e * kThreads;
+            if (i < m && gr[e] >= tau) {
+                const uint32_t slot = atomicAdd(&cm.count, 1u);
+                if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
+            }
         }
         __syncthreads();
         const uint32_t ncg = cm.count;
@@ -842,18 +841,13 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             }
             if (tid == 0) cm.count = 0;
             __syncthreads();
-            {
-                bool keep[CPT];
-                uint32_t slot[CPT];
 #pragma unroll
-                for (int it = 0; it < CPT; ++it) keep[it] = cjx[it] >= 0 && cx[it] >= tau;
-                wave_append(&cm.count, keep, slot);
-#pragma unroll
-                for (int it = 0; it < CPT; ++it)
-                    if (keep[it]) {
-                        f.val[slot[it]] = cx[it];
-                        f.idx[slot[it]] = cjx[it];
-                    }
+            for (int it = 0; it < CPT; ++it) {
+                if (cjx[it] >= 0 && cx[it] >= tau) {
+                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    f.val[slot] = cx[it];
+                    f.idx[slot] = cjx[it];
+                }
             }
             __syncthreads();
             const uint32_t count = cm.count;
