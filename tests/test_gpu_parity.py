@@ -162,6 +162,33 @@ def test_exact_ties_many_candidates(T, S_, k):
     assert split >= 1 and (crowded >= 1 or T == 40000)
 
 
+def test_token_order_below_fp32_resolution():
+    """fp32 inputs whose token scores differ only below fp32 resolution
+    (score = level + 2^-30 * noise): the top-k's large path bounds the k-th
+    score with group maxima rounded up to fp32, which tie in large numbers;
+    the selection must still be the exact fp64 one."""
+    rng = np.random.default_rng(2024)
+    w = S(dtype="f32", Hq=1, Hkv=1, d=64, T=70000, S=1, topk=3000, L=64, needles=0)
+    qn = np.zeros((1, w.Hq, w.d), np.float32)
+    qn[0, 0, 0], qn[0, 0, 1] = 1.0, 2.0 ** -30
+    Kn = np.zeros((w.Hkv, w.T, w.d), np.float32)
+    Kn[0, :, 0] = rng.integers(0, 40, size=w.T)
+    Kn[0, :, 1] = rng.uniform(-1.0, 1.0, size=w.T)
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    gpu = run_library(w, dev(qn), dev(Kn), dev(Vn))
+    ora = oracle_head(w, 0, 0, qn.astype(np.float64), Kn.astype(np.float64), Vn.astype(np.float64))
+    sc = ora["sc"][0]
+    kth = np.sort(sc)[::-1][w.topk - 1]
+    level = np.rint(kth)
+    at_level = int((np.abs(sc - level) < 0.5).sum())
+    # the boundary falls inside one integer level, decided by the 2^-30 terms
+    assert int((sc > level + 0.5).sum()) < w.topk < int((sc > level - 0.5).sum())
+    assert np.float32(level + 2.0 ** -31) == np.float32(level)
+    log(f"  k-th score {kth!r}: {at_level} tokens share its integer level")
+    compare_head(w, gpu, ora, 0)
+
+
 def test_exact_ties_mfma_blocks():
     """Integer inputs through the MFMA block path: tied spans share identical
     approximate scores and must be resolved by index after exact re-scoring."""
