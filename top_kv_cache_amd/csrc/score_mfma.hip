@@ -196,32 +196,36 @@ __device__ __forceinline__ void lds_read8(const uint32_t (&ad)[8], uint4 (&o)[8]
     o[7] = make_uint4(r7.x, r7.y, r7.z, r7.w);
 }
 
-// Eight 16-byte LDS reads at base + {0, 16, 32, 48} and base + 1024 + {0, 16,
-// 32, 48} (8 channels of two fp64 rows 128 doubles apart), completed inside
-// one asm block like lds_read8.
-__device__ __forceinline__ void lds_read8_rows2(uint32_t base, uint4 (&o)[8]) {
-    u32x4v r0, r1, r2, r3, r4, r5, r6, r7;
+// Sixteen 16-byte LDS reads: 8 channels of four fp64 rows 128 doubles apart
+// (base + r * 1024 + {0, 16, 32, 48}), completed inside one asm block like
+// lds_read8.
+__device__ __forceinline__ void lds_read16_rows4(uint32_t base, uint4 (&o)[16]) {
+    u32x4v r[16];
     asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:16\n\t"
-        "ds_read_b128 %2, %8 offset:32\n\t"
-        "ds_read_b128 %3, %8 offset:48\n\t"
-        "ds_read_b128 %4, %8 offset:1024\n\t"
-        "ds_read_b128 %5, %8 offset:1040\n\t"
-        "ds_read_b128 %6, %8 offset:1056\n\t"
-        "ds_read_b128 %7, %8 offset:1072\n\t"
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %16 offset:16\n\t"
+        "ds_read_b128 %2, %16 offset:32\n\t"
+        "ds_read_b128 %3, %16 offset:48\n\t"
+        "ds_read_b128 %4, %16 offset:1024\n\t"
+        "ds_read_b128 %5, %16 offset:1040\n\t"
+        "ds_read_b128 %6, %16 offset:1056\n\t"
+        "ds_read_b128 %7, %16 offset:1072\n\t"
+        "ds_read_b128 %8, %16 offset:2048\n\t"
+        "ds_read_b128 %9, %16 offset:2064\n\t"
+        "ds_read_b128 %10, %16 offset:2080\n\t"
+        "ds_read_b128 %11, %16 offset:2096\n\t"
+        "ds_read_b128 %12, %16 offset:3072\n\t"
+        "ds_read_b128 %13, %16 offset:3088\n\t"
+        "ds_read_b128 %14, %16 offset:3104\n\t"
+        "ds_read_b128 %15, %16 offset:3120\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]),
+          "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
         : "v"(base)
         : "memory");
-    o[0] = make_uint4(r0.x, r0.y, r0.z, r0.w);
-    o[1] = make_uint4(r1.x, r1.y, r1.z, r1.w);
-    o[2] = make_uint4(r2.x, r2.y, r2.z, r2.w);
-    o[3] = make_uint4(r3.x, r3.y, r3.z, r3.w);
-    o[4] = make_uint4(r4.x, r4.y, r4.z, r4.w);
-    o[5] = make_uint4(r5.x, r5.y, r5.z, r5.w);
-    o[6] = make_uint4(r6.x, r6.y, r6.z, r6.w);
-    o[7] = make_uint4(r7.x, r7.y, r7.z, r7.w);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = make_uint4(r[i].x, r[i].y, r[i].z, r[i].w);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -763,18 +767,19 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
                                     kd[2 * e] = (double)__uint_as_float(w4[e] << 16);
                                     kd[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
                                 }
-                                // the 8 channels of 2 queries per LDS batch
-                                // (eight 16-byte reads completed together; the
-                                // lanes of a half-wave read the same addresses)
+                                // the 8 channels of 4 queries per LDS batch
+                                // (sixteen 16-byte reads completed together;
+                                // the lanes of a half-wave read the same
+                                // addresses)
                                 const uint32_t qc = lds_addr(sh.qblk + (sub * 16 + part * 8) * kD +
                                                              (half * 8 + cc) * 8);
                                 static_assert(kD * 8 == 1024, "query rows 1024 bytes apart");
 #pragma unroll
-                                for (int i0 = 0; i0 < 8; i0 += 2) {
-                                    uint4 qv[8];
-                                    lds_read8_rows2(qc + (uint32_t)(i0 * kD * 8), qv);
+                                for (int i0 = 0; i0 < 8; i0 += 4) {
+                                    uint4 qv[16];
+                                    lds_read16_rows4(qc + (uint32_t)(i0 * kD * 8), qv);
 #pragma unroll
-                                    for (int u = 0; u < 8; ++u) {
+                                    for (int u = 0; u < 16; ++u) {
                                         const double q0 = __hiloint2double((int)qv[u].y, (int)qv[u].x);
                                         const double q1 = __hiloint2double((int)qv[u].w, (int)qv[u].z);
                                         const int i = i0 + (u >> 2), e = 2 * (u & 3);
