@@ -21,7 +21,9 @@
 //         transposed so each A fragment is one 16-byte LDS read.
 // 8-wave workgroups run the tiles as a three-stage software pipeline (tile
 // it+2 staged, logits of tile it+1 on the MFMA pipe while tile it's softmax
-// runs on the VALU, then tile it's O update); 2-wave ones use one buffer.
+// runs on the VALU, then tile it's O update), and the two waves that share a
+// SIMD take those phases in opposite order.  2-wave workgroups (at most 64
+// query rows, cache source) use one tile buffer.
 //
 // Two sources for the tiles (template parameter):
 //   window  the rotated window written by the gather step (rea_window_attend);
