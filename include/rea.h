@@ -290,7 +290,8 @@ rea_status rea_prefill(const rea_problem *p, const rea_params *a, int32_t chunk,
  *              and sequence b's cache starts b * kv_stride_seq elements later
  *              (same head and token strides).
  * a            block_q must be 1 and L >= 1; at most 8 query heads per
- *              selection head.
+ *              selection head (64 for bf16 with head_dim 128), else
+ *              REA_EUNSUPPORTED.
  * lengths      DEVICE array [batch] int64: sequence b has lengths[b] valid
  *              tokens, its query being token lengths[b] - 1; every region,
  *              span and window is derived from its own length.  Values are
