@@ -58,82 +58,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// k_qprep: grid (n_blk, Hkv), 256 threads: each wave takes every 4th query of
-// the block, a lane two channels (c and c + 64); the block's bound E_b is the
-// sum of the per-query bounds, added in query order by one thread.
-// ---------------------------------------------------------------------------
-struct PrepArgs {
-    const uint16_t *q;      // [n_q][Hq][D]
-    uint16_t *qhl;          // [Hkv][n_q][256]
-    double *qeff;           // [Hkv][n_q][D]
-    double *E;              // [n_blk][Hkv]
-    int Hq, Hkv, g, n_q;
-};
-
-constexpr int kPrepThreads = 256;
-
-__global__ __launch_bounds__(kPrepThreads) void k_qprep(PrepArgs a) {
-    __shared__ double e_q[kQB];
-    const int b = blockIdx.x, h = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    constexpr int kWavesP = kPrepThreads / 64;
-    constexpr int QPW = kQB / kWavesP;                 // queries per wave (16)
-    // group sums: per query head of the group, every load of the wave's
-    // queries is issued before any is added
-    double s[QPW][2];
-#pragma unroll
-    for (int u = 0; u < QPW; ++u) s[u][0] = s[u][1] = 0.0;
-    for (int gg = 0; gg < a.g; ++gg) {
-        uint16_t raw[QPW][2];
-#pragma unroll
-        for (int u = 0; u < QPW; ++u) {
-            const int64_t i = (int64_t)b * kQB + wave + u * kWavesP;
-            const uint16_t *qr = a.q + (i * a.Hq + h * a.g + gg) * kD + lane;
-            raw[u][0] = qr[0];
-            raw[u][1] = qr[64];
-        }
-#pragma unroll
-        for (int u = 0; u < QPW; ++u) {
-            s[u][0] += bf16_to_f64(raw[u][0]);
-            s[u][1] += bf16_to_f64(raw[u][1]);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < QPW; ++u) {
-        const int il = wave + u * kWavesP;
-        const int64_t i = (int64_t)b * kQB + il;
-        const int64_t row = (int64_t)h * a.n_q + i;
-        double n1 = 0.0, n2 = 0.0;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int c = lane + half * 64;
-            const double sv = s[u][half];
-            const uint16_t hi = f32_to_bf16((float)sv);
-            const double hid = bf16_to_f64(hi);
-            const uint16_t lo = f32_to_bf16((float)(sv - hid));
-            const double lod = bf16_to_f64(lo);
-            const double r = sv - hid - lod;
-            a.qhl[row * 256 + c] = hi;
-            a.qhl[row * 256 + kD + c] = lo;
-            a.qeff[row * kD + c] = sv;
-            n1 += (fabs(hid) + fabs(lod)) * (fabs(hid) + fabs(lod));
-            n2 += r * r;
-        }
-        for (int o = 32; o > 0; o >>= 1) {
-            n1 += __shfl_xor(n1, o);
-            n2 += __shfl_xor(n2, o);
-        }
-        if (lane == 0) e_q[il] = (kGammaMfma * sqrt(n1) + sqrt(n2)) * (1.0 + 1e-12);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double esum = 0.0;
-        for (int il = 0; il < kQB; ++il) esum += e_q[il];
-        a.E[(int64_t)b * a.Hkv + h] = esum * (1.0 + 1e-9);
-    }
-}
-
-// ---------------------------------------------------------------------------
 // k_score_mfma: grid (n_qg * Hkv * NR) with the query group slowest, so the
 // workgroups sharing a key range of one head sit on one XCD; 256 threads,
 // two workgroups per CU so that one hides the other's LDS and reduction
@@ -290,6 +214,95 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// ---------------------------------------------------------------------------
+// k_qprep: grid (n_blk, Hkv), 256 threads: each wave takes every 4th query of
+// the block, a lane two adjacent channels (2l, 2l + 1: one 32-bit load per
+// query and query head, the loads of up to four query heads issued together);
+// the per-query norms are summed over the wave with DPP and read lanes, and
+// the block's bound E_b is the sum of the per-query bounds, added in query
+// order by one thread.
+// ---------------------------------------------------------------------------
+struct PrepArgs {
+    const uint16_t *q;      // [n_q][Hq][D]
+    uint16_t *qhl;          // [Hkv][n_q][256]
+    double *qeff;           // [Hkv][n_q][D]
+    double *E;              // [n_blk][Hkv]
+    int Hq, Hkv, g, n_q;
+};
+
+constexpr int kPrepThreads = 256;
+
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = row_sum16(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+__global__ __launch_bounds__(kPrepThreads) void k_qprep(PrepArgs a) {
+    __shared__ double e_q[kQB];
+    const int b = blockIdx.x, h = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int kWavesP = kPrepThreads / 64;
+    constexpr int QPW = kQB / kWavesP;                 // queries per wave (16)
+    constexpr int GB = 4;                              // query heads loaded together
+    // group sums in fp64, query heads added in order
+    double s[QPW][2];
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) s[u][0] = s[u][1] = 0.0;
+    for (int g0 = 0; g0 < a.g; g0 += GB) {
+        uint32_t raw[GB][QPW];
+#pragma unroll
+        for (int gg = 0; gg < GB; ++gg) {
+            const int hq = h * a.g + (g0 + gg < a.g ? g0 + gg : a.g - 1);
+#pragma unroll
+            for (int u = 0; u < QPW; ++u) {
+                const int64_t i = (int64_t)b * kQB + wave + u * kWavesP;
+                raw[gg][u] = *(const uint32_t *)(a.q + (i * a.Hq + hq) * kD + 2 * lane);
+            }
+        }
+#pragma unroll
+        for (int gg = 0; gg < GB; ++gg)
+            if (g0 + gg < a.g)
+#pragma unroll
+                for (int u = 0; u < QPW; ++u) {
+                    s[u][0] += (double)__uint_as_float(raw[gg][u] << 16);
+                    s[u][1] += (double)__uint_as_float(raw[gg][u] & 0xffff0000u);
+                }
+    }
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+        const int il = wave + u * kWavesP;
+        const int64_t row = (int64_t)h * a.n_q + (int64_t)b * kQB + il;
+        double n1 = 0.0, n2 = 0.0;
+        uint32_t hi2 = 0, lo2 = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const double sv = s[u][e];
+            const uint16_t hi = f32_to_bf16((float)sv);
+            const double hid = bf16_to_f64(hi);
+            const uint16_t lo = f32_to_bf16((float)(sv - hid));
+            const double lod = bf16_to_f64(lo);
+            const double r = sv - hid - lod;
+            hi2 |= (uint32_t)hi << (16 * e);
+            lo2 |= (uint32_t)lo << (16 * e);
+            n1 += (fabs(hid) + fabs(lod)) * (fabs(hid) + fabs(lod));
+            n2 += r * r;
+        }
+        *(uint32_t *)(a.qhl + row * 256 + 2 * lane) = hi2;
+        *(uint32_t *)(a.qhl + row * 256 + kD + 2 * lane) = lo2;
+        *(double2 *)(a.qeff + row * kD + 2 * lane) = make_double2(s[u][0], s[u][1]);
+        n1 = wave_sum_f64(n1);
+        n2 = wave_sum_f64(n2);
+        if (lane == 0) e_q[il] = (kGammaMfma * sqrt(n1) + sqrt(n2)) * (1.0 + 1e-12);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double esum = 0.0;
+        for (int il = 0; il < kQB; ++il) esum += e_q[il];
+        a.E[(int64_t)b * a.Hkv + h] = esum * (1.0 + 1e-9);
+    }
 }
 
 __global__ __launch_bounds__(256, 2) void k_score_mfma(MfmaArgs a) {
