@@ -715,17 +715,20 @@ hipError_t launch_attend_mfma(const Geom &g, const float *q_rot, const float *k_
 
 hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k, const void *v,
                                     const int32_t *sel, const int32_t *n_sel, float *out,
-                                    void *ws, hipStream_t s) {
+                                    void *ws, hipStream_t s, bool table_ready) {
     float2 *rope = (float2 *)ws;
-    RopeArgs ra;
-    ra.rope = rope;
-    ra.n = g.W_cap * (g.d / 2);
-    ra.half = g.d / 2;
-    for (int c = 0; c < kMaxHalfDim; ++c)
-        ra.inv_freq[c] = c < g.d / 2 ? pow(g.theta, -2.0 * (double)c / (double)g.d) : 0.0;
-    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((ra.n + 255) / 256)), dim3(256), 0, s, ra);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!table_ready) {
+        RopeArgs ra;
+        ra.rope = rope;
+        ra.n = g.W_cap * (g.d / 2);
+        ra.half = g.d / 2;
+        for (int c = 0; c < kMaxHalfDim; ++c)
+            ra.inv_freq[c] = c < g.d / 2 ? pow(g.theta, -2.0 * (double)c / (double)g.d) : 0.0;
+        hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((ra.n + 255) / 256)), dim3(256), 0, s, ra);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 
     MAttnArgs a{};
     a.q = (const uint16_t *)q;

@@ -372,10 +372,17 @@ rea_status rea_window_attend(const rea_problem *p, const rea_params *a, const fl
                     "window_attend");
 }
 
-rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out,
-                           int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes,
-                           void *stream, const rea_timing *timing) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// rea_decode_step's body.  rope_rows (may be NULL): in, the number of RoPE
+// table rows already valid at the start of ws (from an earlier step on the
+// same workspace, theta and head_dim); out, the rows valid after this step
+// (0 when the step's path does not keep the table there).
+rea_status decode_step(const rea_problem *p, const rea_params *a, float *out, int32_t *sel,
+                       int32_t *n_sel, void *ws, size_t ws_bytes, void *stream,
+                       const rea_timing *timing, int64_t *rope_rows) {
     rea::Geom g;
     rea_status st = make_geom(p, a, &g);
     if (st != REA_OK) return st;
@@ -388,6 +395,11 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
     if ((st = device_ready(&num_cu)) != REA_OK) return st;
 
     Carve c{(char *)ws, 0};
+    // the MFMA attention's RoPE table goes first: the same place in every step
+    const bool mfma_cache = rea::mfma_cache_attend_path(g);
+    void *rws = mfma_cache ? c.take<char>(rea::rope_table_bytes(g)) : nullptr;
+    const bool table_ready = mfma_cache && rope_rows && *rope_rows >= g.W_cap;
+    if (rope_rows) *rope_rows = mfma_cache ? (table_ready ? *rope_rows : g.W_cap) : 0;
     double *scores = c.take<double>(score_scores_bytes(g));
     void *aux = c.take<char>(select_aux_bytes(g));
     void *seg_ws = c.take<char>(seg_tok_bytes(g));
@@ -401,12 +413,10 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
                                      timing),
                        "score_select")) != REA_OK)
         return st;
-    if (rea::mfma_cache_attend_path(g)) {
-        void *rws = c.take<char>(rea::rope_table_bytes(g));
+    if (mfma_cache)
         return launched(rea::launch_attend_mfma_cache(g, p->q, p->k, p->v, use_sel, use_nsel, out,
-                                                      rws, s),
+                                                      rws, s, table_ready),
                         "window attention from the cache (MFMA)");
-    }
     if (rea::fused_decode_path(g)) {
         void *fws = c.take<char>(rea::fused_ws_bytes(g));
         return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out,
@@ -424,6 +434,17 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
         return st;
     return launched(rea::launch_attend(g, q_rot, k_win, v_win, Wlen, g.W_cap, out, att_ws, s),
                     "window_attend");
+}
+
+}  // namespace
+
+extern "C" {
+
+rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out,
+                           int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes,
+                           void *stream, const rea_timing *timing) {
+    g_err[0] = 0;
+    return decode_step(p, a, out, sel, n_sel, ws, ws_bytes, stream, timing, nullptr);
 }
 
 }  // extern "C"
@@ -520,12 +541,16 @@ rea_status rea_prefill(const rea_problem *p, const rea_params *a, int32_t chunk,
     rea_status st = rea_prefill_plan(p, a, chunk, nullptr, 0, &count, &need);
     if (st != REA_OK) return st;
     if ((st = check_ws(ws, ws_bytes, need)) != REA_OK) return st;
+    // the chunks share the workspace, so the RoPE table of the window
+    // positions is built once (again only when the window capacity grows)
+    int64_t rope_rows = 0;
     return prefill_plan(p, a, chunk, [&](int64_t start, int32_t n, int32_t bq) {
         rea_problem pc;
         rea_params ac;
         chunk_view(p, a, start, n, bq, &pc, &ac);
         float *oc = out + (size_t)start * p->n_q_heads * p->head_dim;
-        return rea_decode_step(&pc, &ac, oc, nullptr, nullptr, ws, ws_bytes, stream, nullptr);
+        return decode_step(&pc, &ac, oc, nullptr, nullptr, ws, ws_bytes, stream, nullptr,
+                           &rope_rows);
     });
 }
 

@@ -124,15 +124,18 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
                                const int32_t *sel, const int32_t *n_sel, float *out, void *ws,
                                hipStream_t s);
 
-// Steps 2-4 for query blocks of at least 32 rows inside rea_decode_step: the
-// MFMA attention reads the window rows from the cache through the selection.
-// ws holds rope_table_bytes(g): the RoPE table and, for grids too small to fill the
-// GPU, the partials of the key-tile splits.
+// Steps 2-4 for more than 8 bf16 query rows per block and KV head inside
+// rea_decode_step: the MFMA attention reads the window rows from the cache
+// through the selection.  ws holds rope_table_bytes(g): the RoPE table of the
+// window positions (first, so that consecutive calls on one workspace find it
+// at the same place) and, for grids too small to fill the GPU, the partials
+// of the key-tile splits.  table_ready: the table already holds rows
+// [0, W_cap) (row w depends on w, d and theta only), so it is not rebuilt.
 bool mfma_cache_attend_path(const Geom &g);
 size_t rope_table_bytes(const Geom &g);
 hipError_t launch_attend_mfma_cache(const Geom &g, const void *q, const void *k, const void *v,
                                     const int32_t *sel, const int32_t *n_sel, float *out,
-                                    void *ws, hipStream_t s);
+                                    void *ws, hipStream_t s, bool table_ready = false);
 
 // Step 4 for query blocks of at least 32 rows (bf16, d 128) on MFMA.
 bool mfma_attend_path(const Geom &g);
