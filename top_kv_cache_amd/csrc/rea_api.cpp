@@ -178,16 +178,10 @@ hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, doubl
         return rea::launch_score_select_mfma(g, q, k, scores, sel, n_sel, aux, num_cu, s,
                                              timing ? (hipEvent_t)timing->score_begin : nullptr,
                                              timing ? (hipEvent_t)timing->score_end : nullptr);
-    if (timing && timing->score_begin) {
-        hipError_t e = hipEventRecord((hipEvent_t)timing->score_begin, s);
-        if (e != hipSuccess) return e;
-    }
-    hipError_t e = rea::launch_score(g, q, k, scores, (double *)aux, num_cu, s);
+    hipError_t e = rea::launch_score(g, q, k, scores, (double *)aux, num_cu, s,
+                                     timing ? (hipEvent_t)timing->score_begin : nullptr,
+                                     timing ? (hipEvent_t)timing->score_end : nullptr);
     if (e != hipSuccess) return e;
-    if (timing && timing->score_end) {
-        e = hipEventRecord((hipEvent_t)timing->score_end, s);
-        if (e != hipSuccess) return e;
-    }
     if (!g.seg) return rea::launch_topk(g, scores, (const double *)aux, sel, n_sel, s);
     // token segments: the k_tok best tokens, then their widened union
     rea::Geom gt = g;

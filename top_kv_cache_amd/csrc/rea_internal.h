@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace rea {
@@ -84,11 +85,24 @@ constexpr int kMaxHalfDim = 64;   // head_dim <= 128
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
 
+// Launches a kernel whose one parameter is an argument struct.  Non-null
+// events take the start and end times of the dispatch itself (hipExtLaunchKernel
+// stamps them from the kernel's own completion signal), so timing a kernel adds
+// no marker packets, and no idle gaps, around it on the stream.
+template <typename A>
+hipError_t launch_struct(void (*kern)(A), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                         const A &a, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr) {
+    void *args[] = {const_cast<A *>(&a)};
+    return hipExtLaunchKernel((const void *)kern, grid, block, args, lds, s, ev_begin, ev_end, 0);
+}
+
 // Step 1a: span scores [n_blk][Hkv][n_spans] (double) and the maximum of every
-// group of 32 consecutive spans [n_blk][Hkv][score_groups(g)].
+// group of 32 consecutive spans [n_blk][Hkv][score_groups(g)].  Non-null
+// events time the scoring kernel's dispatch.
 int64_t score_groups(const Geom &g);
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
-                        double *group_max, int num_cu, hipStream_t s);
+                        double *group_max, int num_cu, hipStream_t s,
+                        hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
 // Token segments: widen each selected token (sel_tok [n_blk*Hkv][k_tok],
 // middle-relative, ascending) to g.seg tokens and write the union, ascending,

@@ -653,28 +653,29 @@ __global__ __launch_bounds__(kThreads) void k_score_block(ScoreArgs a) {
     }
 }
 
+// The events of a timed launch (both null when untimed).
+struct Ev {
+    hipEvent_t b, e;
+};
+
 template <typename TIn, int D, int R>
-void launch_decode(const ScoreArgs &a, int nblocks, hipStream_t s) {
-    hipLaunchKernelGGL((k_score_decode<TIn, D, R>), dim3(nblocks), dim3(kThreads), 0, s, a);
+hipError_t launch_decode(const ScoreArgs &a, int nblocks, hipStream_t s, Ev ev) {
+    return launch_struct(k_score_decode<TIn, D, R>, dim3(nblocks), dim3(kThreads), 0, s, a, ev.b,
+                         ev.e);
 }
 
 template <typename TIn, int D, int NH>
-void launch_heads(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
-    if constexpr (D * sizeof(TIn) == 256 && (NH == 2 || NH == 4)) {
-        hipLaunchKernelGGL((k_score_heads_lds<TIn, D, NH>), dim3(nblocks), dim3(kThreads), 0, s, a);
-        return;
-    }
+hipError_t launch_heads(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s, Ev ev) {
+    const dim3 grid(nblocks), block(kThreads);
+    if constexpr (D * sizeof(TIn) == 256 && (NH == 2 || NH == 4))
+        return launch_struct(k_score_heads_lds<TIn, D, NH>, grid, block, 0, s, a, ev.b, ev.e);
     constexpr int RPI = 64 / (D * (int)sizeof(TIn) / 16);
     const int per_span = (g.S + RPI - 1) / RPI;
     if (per_span >= 4)
-        hipLaunchKernelGGL((k_score_decode_heads<TIn, D, 4, NH>), dim3(nblocks), dim3(kThreads),
-                           0, s, a);
-    else if (per_span >= 2)
-        hipLaunchKernelGGL((k_score_decode_heads<TIn, D, 2, NH>), dim3(nblocks), dim3(kThreads),
-                           0, s, a);
-    else
-        hipLaunchKernelGGL((k_score_decode_heads<TIn, D, 1, NH>), dim3(nblocks), dim3(kThreads),
-                           0, s, a);
+        return launch_struct(k_score_decode_heads<TIn, D, 4, NH>, grid, block, 0, s, a, ev.b, ev.e);
+    if (per_span >= 2)
+        return launch_struct(k_score_decode_heads<TIn, D, 2, NH>, grid, block, 0, s, a, ev.b, ev.e);
+    return launch_struct(k_score_decode_heads<TIn, D, 1, NH>, grid, block, 0, s, a, ev.b, ev.e);
 }
 
 // Query heads per KV head that one multi-head decode workgroup scores
@@ -686,39 +687,37 @@ int multi_heads(const Geom &g) {
 }
 
 template <typename TIn, int D, int NH>
-void launch_tokens(const ScoreArgs &a, int nblocks, hipStream_t s) {
-    hipLaunchKernelGGL((k_score_tokens<TIn, D, NH>), dim3(nblocks), dim3(kThreads), 0, s, a);
+hipError_t launch_tokens(const ScoreArgs &a, int nblocks, hipStream_t s, Ev ev) {
+    return launch_struct(k_score_tokens<TIn, D, NH>, dim3(nblocks), dim3(kThreads), 0, s, a, ev.b,
+                         ev.e);
 }
 
 template <typename TIn, int D>
-hipError_t launch_typed(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s) {
+hipError_t launch_typed(const Geom &g, const ScoreArgs &a, int nblocks, hipStream_t s, Ev ev) {
     if (g.block_q == 1 && g.S == 1) {
         const int nh = multi_heads(g);
-        if (nh == 2) launch_tokens<TIn, D, 2>(a, nblocks, s);
-        else if (nh == 3) launch_tokens<TIn, D, 3>(a, nblocks, s);
-        else if (nh == 4) launch_tokens<TIn, D, 4>(a, nblocks, s);
-        else launch_tokens<TIn, D, 1>(a, nblocks, s);
-    } else if (const int nh = multi_heads(g)) {
-        if (nh == 2) launch_heads<TIn, D, 2>(g, a, nblocks, s);
-        else if (nh == 3) launch_heads<TIn, D, 3>(g, a, nblocks, s);
-        else if (nh == 4) launch_heads<TIn, D, 4>(g, a, nblocks, s);
-        else launch_heads<TIn, D, 8>(g, a, nblocks, s);
-    } else if (g.block_q == 1) {
+        if (nh == 2) return launch_tokens<TIn, D, 2>(a, nblocks, s, ev);
+        if (nh == 3) return launch_tokens<TIn, D, 3>(a, nblocks, s, ev);
+        if (nh == 4) return launch_tokens<TIn, D, 4>(a, nblocks, s, ev);
+        return launch_tokens<TIn, D, 1>(a, nblocks, s, ev);
+    }
+    if (const int nh = multi_heads(g)) {
+        if (nh == 2) return launch_heads<TIn, D, 2>(g, a, nblocks, s, ev);
+        if (nh == 3) return launch_heads<TIn, D, 3>(g, a, nblocks, s, ev);
+        if (nh == 4) return launch_heads<TIn, D, 4>(g, a, nblocks, s, ev);
+        return launch_heads<TIn, D, 8>(g, a, nblocks, s, ev);
+    }
+    if (g.block_q == 1) {
         constexpr int RPI = 64 / (D * (int)sizeof(TIn) / 16);
         const int per_span = (g.S + RPI - 1) / RPI;       // load instructions per span
-        if (per_span >= 8)
-            launch_decode<TIn, D, 8>(a, nblocks, s);
-        else if (per_span >= 4)
-            launch_decode<TIn, D, 4>(a, nblocks, s);
-        else if (per_span >= 2)
-            launch_decode<TIn, D, 2>(a, nblocks, s);
-        else
-            launch_decode<TIn, D, 1>(a, nblocks, s);
-    } else {
-        const size_t lds = (size_t)g.block_q * D * sizeof(double);
-        hipLaunchKernelGGL((k_score_block<TIn, D>), dim3(nblocks), dim3(kThreads), lds, s, a);
+        if (per_span >= 8) return launch_decode<TIn, D, 8>(a, nblocks, s, ev);
+        if (per_span >= 4) return launch_decode<TIn, D, 4>(a, nblocks, s, ev);
+        if (per_span >= 2) return launch_decode<TIn, D, 2>(a, nblocks, s, ev);
+        return launch_decode<TIn, D, 1>(a, nblocks, s, ev);
     }
-    return hipGetLastError();
+    const size_t lds = (size_t)g.block_q * D * sizeof(double);
+    return launch_struct(k_score_block<TIn, D>, dim3(nblocks), dim3(kThreads), lds, s, a, ev.b,
+                         ev.e);
 }
 
 }  // namespace
@@ -726,7 +725,8 @@ hipError_t launch_typed(const Geom &g, const ScoreArgs &a, int nblocks, hipStrea
 int64_t score_groups(const Geom &g) { return (g.n_spans + kGroup - 1) / kGroup; }
 
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
-                        double *group_max, int num_cu, hipStream_t s) {
+                        double *group_max, int num_cu, hipStream_t s, hipEvent_t ev_begin,
+                        hipEvent_t ev_end) {
     if (g.n_spans == 0) return hipSuccess;
     ScoreArgs a;
     a.q = q;
@@ -761,11 +761,12 @@ hipError_t launch_score(const Geom &g, const void *q, const void *k, double *spa
     if (P < 1) P = 1;
     a.P = (int)P;
     const int nblocks = (int)(units * P);
+    const Ev ev{ev_begin, ev_end};
     if (g.dtype == 0)
-        return g.d == 128 ? launch_typed<uint16_t, 128>(g, a, nblocks, s)
-                          : launch_typed<uint16_t, 64>(g, a, nblocks, s);
-    return g.d == 128 ? launch_typed<float, 128>(g, a, nblocks, s)
-                      : launch_typed<float, 64>(g, a, nblocks, s);
+        return g.d == 128 ? launch_typed<uint16_t, 128>(g, a, nblocks, s, ev)
+                          : launch_typed<uint16_t, 64>(g, a, nblocks, s, ev);
+    return g.d == 128 ? launch_typed<float, 128>(g, a, nblocks, s, ev)
+                      : launch_typed<float, 64>(g, a, nblocks, s, ev);
 }
 
 }  // namespace rea

@@ -947,11 +947,9 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     if (NR > g.n_spans) NR = g.n_spans;
     if (NR < 1) NR = 1;
     ma.NR = (int)NR;
-    if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_score_mfma, dim3((unsigned)(units * NR)), dim3(256), 0, s, ma);
-    e = hipGetLastError();
+    e = launch_struct(k_score_mfma, dim3((unsigned)(units * NR)), dim3(256), 0, s, ma, ev_begin,
+                      ev_end);
     if (e != hipSuccess) return e;
-    if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
 
     CertArgs ca;
     ca.shat = span_scores;
