@@ -157,9 +157,10 @@ typedef struct rea_sizes {
     int64_t n_sel_heads;       /* H_sel: n_kv_heads, or n_q_heads with select_per_q_head */
 } rea_sizes;
 
-/* Optional timing hooks: hipEvent_t handles (as void*) that rea_decode_step
- * records on its stream immediately before and after the token-scoring kernel.
- * Either may be NULL. */
+/* Optional timing hooks: hipEvent_t handles (as void*) that take the start and
+ * end times of the token-scoring kernel's dispatch on the call's stream
+ * (hipExtLaunchKernel).  Either may be NULL.  Events created with
+ * hipEventDisableSystemFence perturb the step least. */
 typedef struct rea_timing {
     void *score_begin;
     void *score_end;
