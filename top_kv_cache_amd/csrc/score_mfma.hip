@@ -483,6 +483,12 @@ struct CertArgs {
     int32_t *sel, *nsel;
     int64_t sh_bytes, st_bytes, mid_lo, mid_hi, n_spans;
     int S, Hkv, n_q, kk, topk, rep;
+    // split certification only (R > 1)
+    int R;
+    int32_t *gxs;       // [pairs][kCCap] uncertain spans
+    uint32_t *gbits;    // [pairs][kCCap / 32] certain spans
+    uint32_t *gcnt;     // [pairs][4]: nx, nd, decided without ranking
+    double *gpart;      // [pairs][2][kCCap] per-item sums of the re-scoring
 };
 
 struct CertShared {
@@ -641,11 +647,14 @@ __device__ __forceinline__ double cert_eps(double Eb, double kb, double s) {
     return e * (1.0 + 1e-9) + 1e-12 * (fabs(s) + e) + 1e-300;
 }
 
-__global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
-    __shared__ CertShared sh;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t bh = blockIdx.x;
-    const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+// The steps before re-scoring: interval thresholds, then every span is
+// certainly in (sh.bitmap, nd of them), certainly out, or uncertain (sh.xs,
+// nx of them).  Returns false when the pair needs no ranking at all (kk == 0
+// or kk >= n_spans; sel is then written).
+__device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh, int64_t bh,
+                                              uint32_t &nx_out, uint32_t &nd_out) {
+    const int tid = threadIdx.x;
+    const int h = (int)(bh % a.Hkv);
     const int64_t n = a.n_spans;
     const int kk = a.kk;
     const double *shat = a.shat + bh * n;
@@ -656,7 +665,7 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
     if (kk == 0 || kk >= n) {
         if (sel)
             for (int64_t i = tid; i < a.topk; i += kCThreads) sel[i] = i < kk ? (int32_t)i : -1;
-        return;
+        return false;
     }
     // the approximate scores and their error bounds, every load in flight
     // together (n <= kCCap: kCPer per thread), kept in registers for the
@@ -718,122 +727,139 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
         }
     }
     __syncthreads();
-    const uint32_t nd = sh.nd, nx = sh.nx;
-    const int64_t need = (int64_t)kk - nd;
-    if (need > 0) {
-        // exact (fp64) block scores of the uncertain spans.  The block's
-        // q_eff is staged in LDS 32 queries at a time; a work item is (span,
-        // part): lane = (token tl of a 32-token chunk, query half sub) and it
-        // accumulates the 8 dot products of its token with queries
-        // sub*16 + part*8 .. +8 in fp64 (the products of a bf16 key with q_eff
-        // are exact), the per-query maxima over the 32 token lanes come from a
-        // transpose-reduce, and the 16 maxima are summed.  Up to kCSplit
-        // uncertain spans, the two parts of a span are separate items (the
-        // 2 nx equal items then spread evenly over the SIMDs; whole spans
-        // would leave some SIMDs a span more than others), their sums kept
-        // apart in val (free during re-scoring) and added in a fixed order;
-        // beyond that one wave takes both parts of its span in turn.
-        const int tl = lane & 31, sub = lane >> 5;
-        const bool split = nx <= (uint32_t)kCSplit;
-        const uint32_t n_items = split ? 2 * nx : nx;
-        const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
-        for (int qh = 0; qh < 2; ++qh) {
-            const double *qsrc = a.qeff + ((int64_t)h * a.n_q + (int64_t)b * kQB + qh * 32) * kD;
-            {
-                constexpr int QPT = 32 * kD / kCThreads;      // 8 per thread
-                double qv[QPT];
+    nx_out = sh.nx;
+    nd_out = sh.nd;
+    return true;
+}
+
+// Exact block scores of the nx uncertain spans in sh.xs, over the query
+// halves qh0 .. qh1 - 1.  This workgroup takes the work items first,
+// first + step, ... of each half.  With gpart null (one
+// workgroup per pair) the scores land in sh.xv; else each item's sum goes to
+// gpart[query half * kCCap + item] and cert_gather_xv adds them up in the
+// same order.
+template <bool kToGlobal, int NT, class Sh>
+__device__ __forceinline__ void cert_rescore(const CertArgs &a, Sh &sh, int64_t bh, uint32_t nx,
+                                             int qh0, int qh1, uint32_t first, uint32_t step,
+                                             double *gpart) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int b = (int)(bh / a.Hkv), h = (int)(bh % a.Hkv);
+    // exact (fp64) block scores of the uncertain spans.  The block's
+    // q_eff is staged in LDS 32 queries at a time; a work item is (span,
+    // part): lane = (token tl of a 32-token chunk, query half sub) and it
+    // accumulates the 8 dot products of its token with queries
+    // sub*16 + part*8 .. +8 in fp64 (the products of a bf16 key with q_eff
+    // are exact), the per-query maxima over the 32 token lanes come from a
+    // transpose-reduce, and the 16 maxima are summed.  Up to kCSplit
+    // uncertain spans, the two parts of a span are separate items (the
+    // 2 nx equal items then spread evenly over the SIMDs; whole spans
+    // would leave some SIMDs a span more than others), their sums kept
+    // apart in val (free during re-scoring) and added in a fixed order;
+    // beyond that one wave takes both parts of its span in turn.
+    const int tl = lane & 31, sub = lane >> 5;
+    const bool split = nx <= (uint32_t)kCSplit;
+    const uint32_t n_items = split ? 2 * nx : nx;
+    const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
+    for (int qh = qh0; qh < qh1; ++qh) {
+        const double *qsrc = a.qeff + ((int64_t)h * a.n_q + (int64_t)b * kQB + qh * 32) * kD;
+        {
+            constexpr int QPT = 32 * kD / NT;
+            double qv[QPT];
 #pragma unroll
-                for (int u = 0; u < QPT; ++u) qv[u] = qsrc[tid + u * kCThreads];
+            for (int u = 0; u < QPT; ++u) qv[u] = qsrc[tid + u * NT];
 #pragma unroll
-                for (int u = 0; u < QPT; ++u) sh.qblk[tid + u * kCThreads] = qv[u];
-            }
-            __syncthreads();
-            for (uint32_t it = wave; it < n_items; it += kCWaves) {
-                const uint32_t x = split ? it >> 1 : it;
-                const int p0 = split ? (int)(it & 1) : 0, p1 = split ? p0 + 1 : 2;
-                const int64_t j = sh.xs[x];
-                const int64_t tb = a.mid_lo + j * a.S, te = min(tb + (int64_t)a.S, a.mid_hi);
-                double total = 0.0;
-                for (int part = p0; part < p1; ++part) {
-                    double best[8];
+            for (int u = 0; u < QPT; ++u) sh.qblk[tid + u * NT] = qv[u];
+        }
+        __syncthreads();
+        for (uint32_t it = first; it < n_items; it += step) {
+            const uint32_t x = split ? it >> 1 : it;
+            const int p0 = split ? (int)(it & 1) : 0, p1 = split ? p0 + 1 : 2;
+            const int64_t j = sh.xs[x];
+            const int64_t tb = a.mid_lo + j * a.S, te = min(tb + (int64_t)a.S, a.mid_hi);
+            double total = 0.0;
+            for (int part = p0; part < p1; ++part) {
+                double best[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) best[i] = -INFINITY;
-                    for (int64_t c0 = tb; c0 < te; c0 += 32) {
-                        const int64_t t = c0 + tl;
-                        const bool ok = t < te;
-                        const unsigned char *krow = kh + (ok ? t : tb) * a.st_bytes;
-                        double acc[8];
+                for (int i = 0; i < 8; ++i) best[i] = -INFINITY;
+                for (int64_t c0 = tb; c0 < te; c0 += 32) {
+                    const int64_t t = c0 + tl;
+                    const bool ok = t < te;
+                    const unsigned char *krow = kh + (ok ? t : tb) * a.st_bytes;
+                    double acc[8];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) acc[i] = 0.0;
-                        // the key row in two halves of 8 chunks, each half's
-                        // loads issued together before its arithmetic
-                        for (int half = 0; half < 2; ++half) {
-                            uint4 kraw[8];
+                    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+                    // the key row in two halves of 8 chunks, each half's
+                    // loads issued together before its arithmetic
+                    for (int half = 0; half < 2; ++half) {
+                        uint4 kraw[8];
 #pragma unroll
-                            for (int cc = 0; cc < 8; ++cc) kraw[cc] = ld16(krow + (half * 8 + cc) * 16);
+                        for (int cc = 0; cc < 8; ++cc) kraw[cc] = ld16(krow + (half * 8 + cc) * 16);
 #pragma unroll
-                            for (int cc = 0; cc < 8; ++cc) {
-                                const uint32_t w4[4] = {kraw[cc].x, kraw[cc].y, kraw[cc].z, kraw[cc].w};
-                                double kd[8];
+                        for (int cc = 0; cc < 8; ++cc) {
+                            const uint32_t w4[4] = {kraw[cc].x, kraw[cc].y, kraw[cc].z, kraw[cc].w};
+                            double kd[8];
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    kd[2 * e] = (double)__uint_as_float(w4[e] << 16);
-                                    kd[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
-                                }
-                                // the 8 channels of 4 queries per LDS batch
-                                // (sixteen 16-byte reads completed together;
-                                // the lanes of a half-wave read the same
-                                // addresses)
-                                const uint32_t qc = lds_addr(sh.qblk + (sub * 16 + part * 8) * kD +
-                                                             (half * 8 + cc) * 8);
-                                static_assert(kD * 8 == 1024, "query rows 1024 bytes apart");
+                            for (int e = 0; e < 4; ++e) {
+                                kd[2 * e] = (double)__uint_as_float(w4[e] << 16);
+                                kd[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
+                            }
+                            // the 8 channels of 4 queries per LDS batch
+                            // (sixteen 16-byte reads completed together;
+                            // the lanes of a half-wave read the same
+                            // addresses)
+                            const uint32_t qc = lds_addr(sh.qblk + (sub * 16 + part * 8) * kD +
+                                                         (half * 8 + cc) * 8);
+                            static_assert(kD * 8 == 1024, "query rows 1024 bytes apart");
 #pragma unroll
-                                for (int i0 = 0; i0 < 8; i0 += 4) {
-                                    uint4 qv[16];
-                                    lds_read16_rows4(qc + (uint32_t)(i0 * kD * 8), qv);
+                            for (int i0 = 0; i0 < 8; i0 += 4) {
+                                uint4 qv[16];
+                                lds_read16_rows4(qc + (uint32_t)(i0 * kD * 8), qv);
 #pragma unroll
-                                    for (int u = 0; u < 16; ++u) {
-                                        const double q0 = __hiloint2double((int)qv[u].y, (int)qv[u].x);
-                                        const double q1 = __hiloint2double((int)qv[u].w, (int)qv[u].z);
-                                        const int i = i0 + (u >> 2), e = 2 * (u & 3);
-                                        acc[i] = fma(q0, kd[e], acc[i]);
-                                        acc[i] = fma(q1, kd[e + 1], acc[i]);
-                                    }
+                                for (int u = 0; u < 16; ++u) {
+                                    const double q0 = __hiloint2double((int)qv[u].y, (int)qv[u].x);
+                                    const double q1 = __hiloint2double((int)qv[u].w, (int)qv[u].z);
+                                    const int i = i0 + (u >> 2), e = 2 * (u & 3);
+                                    acc[i] = fma(q0, kd[e], acc[i]);
+                                    acc[i] = fma(q1, kd[e + 1], acc[i]);
                                 }
                             }
                         }
-                        if (ok)
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) best[i] = fmax(best[i], acc[i]);
                     }
-                    // transpose-max over the 32 token lanes: after the steps
-                    // over lane^16, ^8, ^4 lane l keeps query slot (l/4)%8,
-                    // then the maxima over lane^2 and lane^1 complete it
+                    if (ok)
 #pragma unroll
-                    for (int o = 16, nv = 8; o >= 4; o >>= 1, nv >>= 1) {
-                        const bool upper = (tl & o) != 0;
+                        for (int i = 0; i < 8; ++i) best[i] = fmax(best[i], acc[i]);
+                }
+                // transpose-max over the 32 token lanes: after the steps
+                // over lane^16, ^8, ^4 lane l keeps query slot (l/4)%8,
+                // then the maxima over lane^2 and lane^1 complete it
 #pragma unroll
-                        for (int i = 0; i < nv / 2; ++i) {
-                            const double keep = upper ? best[i + nv / 2] : best[i];
-                            const double send = upper ? best[i] : best[i + nv / 2];
-                            best[i] = fmax(keep, __shfl_xor(send, o));
-                        }
+                for (int o = 16, nv = 8; o >= 4; o >>= 1, nv >>= 1) {
+                    const bool upper = (tl & o) != 0;
+#pragma unroll
+                    for (int i = 0; i < nv / 2; ++i) {
+                        const double keep = upper ? best[i + nv / 2] : best[i];
+                        const double send = upper ? best[i] : best[i + nv / 2];
+                        best[i] = fmax(keep, __shfl_xor(send, o));
                     }
-                    best[0] = fmax(best[0], __shfl_xor(best[0], 2));
-                    best[0] = fmax(best[0], __shfl_xor(best[0], 1));
-                    // sum of the 16 maxima (lanes with tl % 4 == 0 hold one each)
-                    double v = (tl & 3) ? 0.0 : best[0];
-                    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-                    total = part == p0 ? v : total + v;
                 }
-                if (lane == 0) {
-                    if (split)
-                        sh.val[it] = total;
-                    else
-                        sh.xv[x] = (qh == 0 ? total : sh.xv[x] + total) + 0.0;
-                }
+                best[0] = fmax(best[0], __shfl_xor(best[0], 2));
+                best[0] = fmax(best[0], __shfl_xor(best[0], 1));
+                // sum of the 16 maxima (lanes with tl % 4 == 0 hold one each)
+                double v = (tl & 3) ? 0.0 : best[0];
+                for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+                total = part == p0 ? v : total + v;
             }
-            __syncthreads();
+            if (lane == 0) {
+                if constexpr (kToGlobal)
+                    gpart[qh * kCCap + it] = total;
+                else if (split)
+                    sh.val[it] = total;
+                else
+                    sh.xv[x] = (qh == 0 ? total : sh.xv[x] + total) + 0.0;
+            }
+        }
+        __syncthreads();
+        if constexpr (!kToGlobal) {
             if (split) {
                 for (uint32_t x = tid; x < nx; x += kCThreads) {
                     const double v = sh.val[2 * x] + sh.val[2 * x + 1];
@@ -842,6 +868,34 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
                 __syncthreads();
             }
         }
+    }
+}
+
+// sh.xv from the per-item sums of the split re-scoring, added as cert_rescore
+// adds them with one workgroup.
+__device__ __forceinline__ void cert_gather_xv(CertShared &sh, const double *gpart, uint32_t nx) {
+    const bool split = nx <= (uint32_t)kCSplit;
+    for (uint32_t x = threadIdx.x; x < nx; x += kCThreads) {
+        double xv = 0.0;
+        for (int qh = 0; qh < 2; ++qh) {
+            const double *p = gpart + qh * kCCap;
+            const double v = split ? p[2 * x] + p[2 * x + 1] : p[x];
+            xv = (qh == 0 ? v : xv + v) + 0.0;
+        }
+        sh.xv[x] = xv;
+    }
+    __syncthreads();
+}
+
+// The need best uncertain spans (sh.xv, sh.xs) join the certain ones in
+// sh.bitmap, and the bitmap is compacted in span order into sel.
+__device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, int64_t bh,
+                                            uint32_t nx, int64_t need) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kk = a.kk;
+    const int nwords = (int)((a.n_spans + 31) / 32);
+    int32_t *sel = a.sel ? a.sel + bh * a.topk : nullptr;
+    if (need > 0) {
         for (uint32_t x = tid; x < nx; x += kCThreads) {
             sh.val[x] = sh.xv[x];
             sh.idx[x] = sh.xs[x];
@@ -890,6 +944,88 @@ __global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
     }
 }
 
+__global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
+    __shared__ CertShared sh;
+    const int64_t bh = blockIdx.x;
+    uint32_t nx, nd;
+    if (!cert_classify(a, sh, bh, nx, nd)) return;
+    const int64_t need = (int64_t)a.kk - nd;
+    if (need > 0)
+        cert_rescore<false, kCThreads>(a, sh, bh, nx, 0, 2, threadIdx.x >> 6, kCWaves, nullptr);
+    cert_finish(a, sh, bh, nx, need);
+}
+
+// Split certification for grids with few (block, KV head) pairs: the
+// classification per pair, the re-scoring spread over a.R workgroups per
+// pair (grid pairs x R, a pair's workgroups adjacent so that they land on
+// different XCDs), then the final ranking per pair.  State passes through
+// gxs / gbits / gcnt / gpart.
+__global__ __launch_bounds__(kCThreads) void k_certify_head(CertArgs a) {
+    __shared__ CertShared sh;
+    const int64_t bh = blockIdx.x;
+    uint32_t *cnt = a.gcnt + bh * 4;
+    uint32_t nx, nd;
+    if (!cert_classify(a, sh, bh, nx, nd)) {
+        if (threadIdx.x == 0) cnt[2] = 1u;
+        return;
+    }
+    for (uint32_t i = threadIdx.x; i < nx; i += kCThreads) a.gxs[bh * kCCap + i] = sh.xs[i];
+    const int nwords = (int)((a.n_spans + 31) / 32);
+    for (int i = threadIdx.x; i < nwords; i += kCThreads) a.gbits[bh * (kCCap / 32) + i] = sh.bitmap[i];
+    if (threadIdx.x == 0) {
+        cnt[0] = nx;
+        cnt[1] = nd;
+        cnt[2] = 0u;
+    }
+}
+
+// What the split re-scoring keeps on chip (a third of CertShared, so that
+// several of its workgroups share a CU).
+struct RescoreShared {
+    int32_t xs[kCCap];
+    double qblk[32 * kD];
+};
+
+constexpr int kRThreads = 256;      // k_rescore: 4 waves, three workgroups per CU
+constexpr int kRWaves = kRThreads / 64;
+
+__global__ __launch_bounds__(kRThreads, 3) void k_rescore(CertArgs a) {
+    __shared__ RescoreShared sh;
+    const int64_t bh = blockIdx.x / a.R;
+    const uint32_t r = blockIdx.x % a.R;
+    const uint32_t *cnt = a.gcnt + bh * 4;
+    if (cnt[2]) return;
+    const uint32_t nx = cnt[0], nd = cnt[1];
+    if ((int64_t)a.kk - nd <= 0) return;
+    // workgroup r takes query half r % 2 and its share of that half's items
+    const int qh = (int)(r & 1);
+    const uint32_t first = (r >> 1) * kRWaves, step = (uint32_t)(a.R / 2) * kRWaves;
+    const uint32_t n_items = nx <= (uint32_t)kCSplit ? 2 * nx : nx;
+    if (first >= n_items) return;
+    for (uint32_t i = threadIdx.x; i < nx; i += kRThreads) sh.xs[i] = a.gxs[bh * kCCap + i];
+    __syncthreads();
+    cert_rescore<true, kRThreads>(a, sh, bh, nx, qh, qh + 1, first + (threadIdx.x >> 6), step,
+                                  a.gpart + bh * 2 * kCCap);
+}
+
+__global__ __launch_bounds__(kCThreads) void k_certify_tail(CertArgs a) {
+    __shared__ CertShared sh;
+    const int64_t bh = blockIdx.x;
+    const uint32_t *cnt = a.gcnt + bh * 4;
+    if (cnt[2]) return;
+    const uint32_t nx = cnt[0], nd = cnt[1];
+    const int64_t need = (int64_t)a.kk - nd;
+    const int nwords = (int)((a.n_spans + 31) / 32);
+    for (int i = threadIdx.x; i < nwords; i += kCThreads) sh.bitmap[i] = a.gbits[bh * (kCCap / 32) + i];
+    if (need > 0) {
+        for (uint32_t i = threadIdx.x; i < nx; i += kCThreads) sh.xs[i] = a.gxs[bh * kCCap + i];
+        __syncthreads();
+        cert_gather_xv(sh, a.gpart + bh * 2 * kCCap, nx);
+    }
+    __syncthreads();
+    cert_finish(a, sh, bh, nx, need);
+}
+
 }  // namespace
 
 bool mfma_block_path(const Geom &g) {
@@ -897,12 +1033,33 @@ bool mfma_block_path(const Geom &g) {
            g.n_spans <= kCCap;
 }
 
+// Workgroups that re-score one (block, KV head) pair's uncertain spans: one
+// (the single certification kernel) when the pairs alone fill half the GPU,
+// else an even number (half per query half) that gives the chunk about 1024
+// four-wave workgroups, at most 16 (32 waves per query half: up to 16
+// uncertain spans re-scored in one round).
+int cert_ways(const Geom &g) {
+    const int64_t pairs = (int64_t)g.n_blk * g.Hkv;
+    if (pairs >= 128) return 1;
+    const int64_t r = 1024 / pairs;
+    return (int)((r < 2 ? 2 : r > 16 ? 16 : r) & ~(int64_t)1);
+}
+
+size_t cert_split_bytes(const Geom &g) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    if (cert_ways(g) == 1) return 0;
+    const size_t pairs = (size_t)g.n_blk * g.Hkv;
+    return al(pairs * kCCap * sizeof(int32_t)) + al(pairs * (kCCap / 32) * sizeof(uint32_t)) +
+           al(pairs * 4 * sizeof(uint32_t)) + al(pairs * 2 * kCCap * sizeof(double));
+}
+
 size_t mfma_ws_bytes(const Geom &g) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return al((size_t)g.Hkv * g.n_q * 256 * sizeof(uint16_t)) +       // [hi|lo]
            al((size_t)g.Hkv * g.n_q * kD * sizeof(double)) +           // q_eff
            al((size_t)g.n_blk * g.Hkv * sizeof(double)) +              // E
-           al((size_t)g.Hkv * g.n_spans * sizeof(double));             // key-norm maxima
+           al((size_t)g.Hkv * g.n_spans * sizeof(double)) +            // key-norm maxima
+           cert_split_bytes(g);                                        // split certification
 }
 
 hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
@@ -918,6 +1075,7 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     double *E = (double *)p;
     p += al((size_t)g.n_blk * g.Hkv * sizeof(double));
     double *kbar = (double *)p;
+    p += al((size_t)g.Hkv * g.n_spans * sizeof(double));
 
     PrepArgs pa{(const uint16_t *)q, qhl, qeff, E, g.Hq, g.Hkv, g.g, g.n_q};
     hipLaunchKernelGGL(k_qprep, dim3(g.n_blk, g.Hkv), dim3(kPrepThreads), 0, s, pa);
@@ -970,8 +1128,26 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     ca.n_q = g.n_q;
     ca.kk = g.k_sel;
     ca.topk = g.topk;
-    hipLaunchKernelGGL(k_certify, dim3(g.n_blk * g.Hkv), dim3(kCThreads), 0, s, ca);
-    return hipGetLastError();
+    ca.R = cert_ways(g);
+    const unsigned pairs = (unsigned)(g.n_blk * g.Hkv);
+    if (ca.R == 1) {
+        ca.gxs = nullptr;
+        ca.gbits = ca.gcnt = nullptr;
+        ca.gpart = nullptr;
+        return launch_struct(k_certify, dim3(pairs), dim3(kCThreads), 0, s, ca);
+    }
+    ca.gxs = (int32_t *)p;
+    p += al((size_t)pairs * kCCap * sizeof(int32_t));
+    ca.gbits = (uint32_t *)p;
+    p += al((size_t)pairs * (kCCap / 32) * sizeof(uint32_t));
+    ca.gcnt = (uint32_t *)p;
+    p += al((size_t)pairs * 4 * sizeof(uint32_t));
+    ca.gpart = (double *)p;
+    if ((e = launch_struct(k_certify_head, dim3(pairs), dim3(kCThreads), 0, s, ca)) != hipSuccess)
+        return e;
+    if ((e = launch_struct(k_rescore, dim3(pairs * ca.R), dim3(kRThreads), 0, s, ca)) != hipSuccess)
+        return e;
+    return launch_struct(k_certify_tail, dim3(pairs), dim3(kCThreads), 0, s, ca);
 }
 
 }  // namespace rea
