@@ -19,7 +19,11 @@
 //                 (block, span) is written, and each span's largest key norm
 //                 (by one wave of the grid per span).
 //   k_certify     per (block, KV head): exact top-k from the approximate
-//                 scores (see below).
+//                 scores (see below).  With under 128 pairs the same steps run
+//                 as k_certify_head (classification per pair), k_rescore (the
+//                 fp64 re-scoring over several workgroups per pair) and
+//                 k_certify_tail (ranking per pair), so that a chunk's few
+//                 pairs do not re-score on a handful of CUs.
 //
 // Error bound.  Every product hi*k, lo*k of two bf16 numbers is exact in fp32;
 // the MFMA sums 256 of them in fp32.  With at most 255 roundings of at most
