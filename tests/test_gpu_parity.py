@@ -52,8 +52,8 @@ SMALL = {
                                L=100, needles=0, kv_scaled=True),
     "bf16_mfma_5_blocks_g1": S(Hq=2, Hkv=2, d=128, T=2500, n_q=320, block_q=64, S=32, topk=7,
                                L=400, needles=0),
-    # 16 blocks x 8 KV heads = 128 pairs: the one-kernel certification (fewer
-    # pairs take the split one)
+    # 16 blocks x 8 KV heads = 128 pairs: the certification's re-scoring on 8
+    # workgroups per pair (the small cases above take 16)
     "bf16_mfma_128_pairs": S(Hq=32, Hkv=8, d=128, T=6000, n_q=1024, block_q=64, S=32, topk=10,
                              L=1024, needles=0, kv_scaled=True),
     # one selection per query head

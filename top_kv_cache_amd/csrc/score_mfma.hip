@@ -18,19 +18,20 @@
 //                 queries are taken in the epilogue; one fp64 span score per
 //                 (block, span) is written, and each span's largest key norm
 //                 (by one wave of the grid per span).
-//   k_certify     per (block, KV head): exact top-k from the approximate
-//                 scores (see below).  With under 128 pairs the same steps run
-//                 as k_certify_head (classification per pair), k_rescore (the
-//                 fp64 re-scoring over several workgroups per pair) and
-//                 k_certify_tail (ranking per pair), so that a chunk's few
-//                 pairs do not re-score on a handful of CUs.
+//   k_certify_head, k_rescore, k_certify_tail
+//                 per (block, KV head): exact top-k from the approximate
+//                 scores (see below): the classification per pair, the fp64
+//                 re-scoring of the uncertain spans over several four-wave
+//                 workgroups per pair (a chunk's few pairs then do not
+//                 re-score on a handful of CUs, and many pairs share CUs three
+//                 at a time), the ranking per pair.
 //
 // Error bound.  Every product hi*k, lo*k of two bf16 numbers is exact in fp32;
 // the MFMA sums 256 of them in fp32.  With at most 255 roundings of at most
 // 2^-23 relative each, |s_hat - s| <= e_i * ||k_t||_2 where
 // e_i = 255*2^-23*(1+1e-6) * ||(|hi|+|lo|)||_2 + ||q_eff - hi - lo||_2.
 // A span maximum moves by at most e_i * max_t ||k_t||, a block sum by
-// E_b * Kbar_j.  k_certify keeps every span whose interval
+// E_b * Kbar_j.  The certification keeps every span whose interval
 // [s_hat - eps, s_hat + eps] lies surely inside the top-k, drops every span
 // surely outside it, re-scores the rest in fp64 (exact for bf16 inputs), and
 // selects among them exactly -- so the selection equals the exact one.
@@ -468,7 +469,8 @@ __global__ __launch_bounds__(256, 2) void k_score_mfma(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_certify: grid (n_blk * Hkv), 512 threads
+// certification: k_certify_head and k_certify_tail grid (n_blk * Hkv), 512
+// threads; k_rescore grid (n_blk * Hkv * R), 256 threads
 // ---------------------------------------------------------------------------
 constexpr int kCThreads = 512;
 constexpr int kCWaves = kCThreads / 64;
@@ -487,7 +489,7 @@ struct CertArgs {
     int32_t *sel, *nsel;
     int64_t sh_bytes, st_bytes, mid_lo, mid_hi, n_spans;
     int S, Hkv, n_q, kk, topk, rep;
-    // split certification only (R > 1)
+    // the three certification kernels' shared state
     int R;
     int32_t *gxs;       // [pairs][kCCap] uncertain spans
     uint32_t *gbits;    // [pairs][kCCap / 32] certain spans
@@ -502,7 +504,6 @@ struct CertShared {
     int32_t xs[kCCap];              // their indices
     uint32_t hist[kCBins];
     uint32_t bitmap[kCCap / 32];
-    double qblk[32 * kD];           // q_eff of 32 of the block's queries (re-scoring)
     double red_d[2][kCWaves];
     uint32_t red_u[kCWaves];
     uint32_t scan[kCWaves + 1];
@@ -738,11 +739,9 @@ __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh,
 
 // Exact block scores of the nx uncertain spans in sh.xs, over the query
 // halves qh0 .. qh1 - 1.  This workgroup takes the work items first,
-// first + step, ... of each half.  With gpart null (one
-// workgroup per pair) the scores land in sh.xv; else each item's sum goes to
-// gpart[query half * kCCap + item] and cert_gather_xv adds them up in the
-// same order.
-template <bool kToGlobal, int NT, class Sh>
+// first + step, ... of each half; each item's sum goes to
+// gpart[query half * kCCap + item], and cert_gather_xv adds them up.
+template <int NT, class Sh>
 __device__ __forceinline__ void cert_rescore(const CertArgs &a, Sh &sh, int64_t bh, uint32_t nx,
                                              int qh0, int qh1, uint32_t first, uint32_t step,
                                              double *gpart) {
@@ -756,10 +755,9 @@ __device__ __forceinline__ void cert_rescore(const CertArgs &a, Sh &sh, int64_t 
     // are exact), the per-query maxima over the 32 token lanes come from a
     // transpose-reduce, and the 16 maxima are summed.  Up to kCSplit
     // uncertain spans, the two parts of a span are separate items (the
-    // 2 nx equal items then spread evenly over the SIMDs; whole spans
-    // would leave some SIMDs a span more than others), their sums kept
-    // apart in val (free during re-scoring) and added in a fixed order;
-    // beyond that one wave takes both parts of its span in turn.
+    // 2 nx equal items then spread evenly over the waves), their sums added
+    // later in a fixed order; beyond that one wave takes both parts of its
+    // span in turn.
     const int tl = lane & 31, sub = lane >> 5;
     const bool split = nx <= (uint32_t)kCSplit;
     const uint32_t n_items = split ? 2 * nx : nx;
@@ -853,30 +851,14 @@ __device__ __forceinline__ void cert_rescore(const CertArgs &a, Sh &sh, int64_t 
                 for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
                 total = part == p0 ? v : total + v;
             }
-            if (lane == 0) {
-                if constexpr (kToGlobal)
-                    gpart[qh * kCCap + it] = total;
-                else if (split)
-                    sh.val[it] = total;
-                else
-                    sh.xv[x] = (qh == 0 ? total : sh.xv[x] + total) + 0.0;
-            }
+            if (lane == 0) gpart[qh * kCCap + it] = total;
         }
         __syncthreads();
-        if constexpr (!kToGlobal) {
-            if (split) {
-                for (uint32_t x = tid; x < nx; x += kCThreads) {
-                    const double v = sh.val[2 * x] + sh.val[2 * x + 1];
-                    sh.xv[x] = (qh == 0 ? v : sh.xv[x] + v) + 0.0;
-                }
-                __syncthreads();
-            }
-        }
     }
 }
 
-// sh.xv from the per-item sums of the split re-scoring, added as cert_rescore
-// adds them with one workgroup.
+// sh.xv from the per-item sums of the re-scoring, in a fixed order: the two
+// parts of a span, then the two query halves.
 __device__ __forceinline__ void cert_gather_xv(CertShared &sh, const double *gpart, uint32_t nx) {
     const bool split = nx <= (uint32_t)kCSplit;
     for (uint32_t x = threadIdx.x; x < nx; x += kCThreads) {
@@ -948,22 +930,10 @@ __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, i
     }
 }
 
-__global__ __launch_bounds__(kCThreads) void k_certify(CertArgs a) {
-    __shared__ CertShared sh;
-    const int64_t bh = blockIdx.x;
-    uint32_t nx, nd;
-    if (!cert_classify(a, sh, bh, nx, nd)) return;
-    const int64_t need = (int64_t)a.kk - nd;
-    if (need > 0)
-        cert_rescore<false, kCThreads>(a, sh, bh, nx, 0, 2, threadIdx.x >> 6, kCWaves, nullptr);
-    cert_finish(a, sh, bh, nx, need);
-}
-
-// Split certification for grids with few (block, KV head) pairs: the
-// classification per pair, the re-scoring spread over a.R workgroups per
-// pair (grid pairs x R, a pair's workgroups adjacent so that they land on
-// different XCDs), then the final ranking per pair.  State passes through
-// gxs / gbits / gcnt / gpart.
+// Certification in three kernels: the classification per pair, the
+// re-scoring spread over a.R workgroups per pair (grid pairs x R, a pair's
+// workgroups adjacent so that they land on different XCDs), then the final
+// ranking per pair.  State passes through gxs / gbits / gcnt / gpart.
 __global__ __launch_bounds__(kCThreads) void k_certify_head(CertArgs a) {
     __shared__ CertShared sh;
     const int64_t bh = blockIdx.x;
@@ -1008,8 +978,8 @@ __global__ __launch_bounds__(kRThreads, 3) void k_rescore(CertArgs a) {
     if (first >= n_items) return;
     for (uint32_t i = threadIdx.x; i < nx; i += kRThreads) sh.xs[i] = a.gxs[bh * kCCap + i];
     __syncthreads();
-    cert_rescore<true, kRThreads>(a, sh, bh, nx, qh, qh + 1, first + (threadIdx.x >> 6), step,
-                                  a.gpart + bh * 2 * kCCap);
+    cert_rescore<kRThreads>(a, sh, bh, nx, qh, qh + 1, first + (threadIdx.x >> 6), step,
+                            a.gpart + bh * 2 * kCCap);
 }
 
 __global__ __launch_bounds__(kCThreads) void k_certify_tail(CertArgs a) {
@@ -1037,21 +1007,18 @@ bool mfma_block_path(const Geom &g) {
            g.n_spans <= kCCap;
 }
 
-// Workgroups that re-score one (block, KV head) pair's uncertain spans: one
-// (the single certification kernel) when the pairs alone fill half the GPU,
-// else an even number (half per query half) that gives the chunk about 1024
-// four-wave workgroups, at most 16 (32 waves per query half: up to 16
+// Workgroups that re-score one (block, KV head) pair's uncertain spans: an
+// even number (half per query half) that gives the grid about 1024 four-wave
+// workgroups, at least 2 and at most 16 (32 waves per query half: up to 16
 // uncertain spans re-scored in one round).
 int cert_ways(const Geom &g) {
     const int64_t pairs = (int64_t)g.n_blk * g.Hkv;
-    if (pairs >= 128) return 1;
     const int64_t r = 1024 / pairs;
     return (int)((r < 2 ? 2 : r > 16 ? 16 : r) & ~(int64_t)1);
 }
 
 size_t cert_split_bytes(const Geom &g) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    if (cert_ways(g) == 1) return 0;
     const size_t pairs = (size_t)g.n_blk * g.Hkv;
     return al(pairs * kCCap * sizeof(int32_t)) + al(pairs * (kCCap / 32) * sizeof(uint32_t)) +
            al(pairs * 4 * sizeof(uint32_t)) + al(pairs * 2 * kCCap * sizeof(double));
@@ -1063,7 +1030,7 @@ size_t mfma_ws_bytes(const Geom &g) {
            al((size_t)g.Hkv * g.n_q * kD * sizeof(double)) +           // q_eff
            al((size_t)g.n_blk * g.Hkv * sizeof(double)) +              // E
            al((size_t)g.Hkv * g.n_spans * sizeof(double)) +            // key-norm maxima
-           cert_split_bytes(g);                                        // split certification
+           cert_split_bytes(g);                                        // certification state
 }
 
 hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
@@ -1134,12 +1101,6 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     ca.topk = g.topk;
     ca.R = cert_ways(g);
     const unsigned pairs = (unsigned)(g.n_blk * g.Hkv);
-    if (ca.R == 1) {
-        ca.gxs = nullptr;
-        ca.gbits = ca.gcnt = nullptr;
-        ca.gpart = nullptr;
-        return launch_struct(k_certify, dim3(pairs), dim3(kCThreads), 0, s, ca);
-    }
     ca.gxs = (int32_t *)p;
     p += al((size_t)pairs * kCCap * sizeof(int32_t));
     ca.gbits = (uint32_t *)p;
