@@ -222,8 +222,8 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 }
 
 // ---------------------------------------------------------------------------
-// k_qprep: grid (n_blk, Hkv), 256 threads: each wave takes every 4th query of
-// the block, a lane two adjacent channels (2l, 2l + 1: one 32-bit load per
+// k_qprep: grid (n_blk, Hkv), 1024 threads: each wave takes every 16th query
+// of the block, a lane two adjacent channels (2l, 2l + 1: one 32-bit load per
 // query and query head, the loads of up to four query heads issued together);
 // the per-query norms are summed over the wave with DPP and read lanes, and
 // the block's bound E_b is the sum of the per-query bounds, added in query
@@ -237,7 +237,7 @@ struct PrepArgs {
     int Hq, Hkv, g, n_q;
 };
 
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 1024;
 
 // Sum over the 64 lanes of a wave (every lane gets it).
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_qprep(PrepArgs a) {
     const int b = blockIdx.x, h = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int kWavesP = kPrepThreads / 64;
-    constexpr int QPW = kQB / kWavesP;                 // queries per wave (16)
+    constexpr int QPW = kQB / kWavesP;                 // queries per wave (4)
     constexpr int GB = 4;                              // query heads loaded together
     // group sums in fp64, query heads added in order
     double s[QPW][2];
