@@ -31,11 +31,34 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_decode_llama8b_1m_traffic.t
 SCORE_SRC = os.path.join(ROOT, "top_kv_cache_amd", "csrc", "score.hip")
 
 
+# What the path computes in.  Decode: span scores in fp64 on the VALU (the
+# scoring pass, 90% of the step), window attention in fp32; prefill blocks of
+# 64: bf16 MFMA products with fp32 sums (certified, uncertain spans re-scored
+# in fp64) and bf16 MFMA attention with fp32 softmax and accumulation.
+DECODE_DTYPE = "f64 scoring, f32 attention"
+PREFILL_DTYPE = "bf16 MFMA scoring and attention (fp32 accumulation, fp64 certification)"
+DECODE_PRECISION = {"storage": "bf16", "scoring": "fp64 (VALU)", "selection": "fp64 scores",
+                    "attention": "fp32 (RoPE, softmax, P.V)", "output": "fp32"}
+PREFILL_PRECISION = {"storage": "bf16",
+                     "scoring": "bf16 MFMA products, fp32 sums, per-span error bound",
+                     "selection": "fp64 re-scoring of the spans the bound leaves uncertain",
+                     "attention": "bf16 MFMA (logits from three bf16 products, P rounded to "
+                                  "bf16), fp32 softmax and accumulation", "output": "fp32"}
+
+
+def precision(w):
+    if w.block_q == 1:
+        d = dict(DECODE_PRECISION, storage=w.dtype)
+        return d
+    return dict(PREFILL_PRECISION, storage=w.dtype)
+
+
 # selection variants of a workload (--variant)
 VARIANTS = {
     "per_q_head": dict(per_q_head=True),       # one selection per query head
     "token_level": dict(S=1, topk=3840),       # spans of one token, the same token budget
     "token_segments": dict(token_segments=True),   # 120 best tokens, each widened to 32
+    "pages_k127": dict(topk=127),               # the pages' 8B tuple: window exactly 8192
 }
 
 
@@ -140,8 +163,8 @@ def prefill_main(args):
 
     T = args.prefill_prompt
     w = synth.small(name=f"llama8b-bf16-prefill-prompt-{T}", seed=240715180, dtype="bf16",
-                    Hq=32, Hkv=8, d=128, T=T, n_q=T, block_q=1, G=32, S=32, topk=120, L=4096,
-                    needles=0, kv_scaled=True)
+                    Hq=32, Hkv=8, d=128, T=T, n_q=T, block_q=1, G=32, S=32, topk=args.topk,
+                    L=4096, needles=0, kv_scaled=True)
     dev = torch.device("cuda:0")
     q = torch_io.q_device(w, 0, dev)
     K = torch_io.kv_device(w, 0, "k", device=dev)
@@ -165,7 +188,7 @@ def prefill_main(args):
         "metric": "chunked-prefill prompt tokens/s (one layer)", "value": T / (ms / 1e3),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f64", "data": "synthetic",
+        "dtype": PREFILL_DTYPE, "precision": PREFILL_PRECISION, "data": "synthetic",
         "config": {"workload": w.name, "layers": 1, "prompt": T, "chunk": args.chunk,
                    "block_q": 64, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
                    "G": w.G, "S": w.S, "topk": w.topk, "L": w.L, "chunks": len(pf.plan)},
@@ -247,7 +270,7 @@ def batch_main(args):
         "metric": "batched decode tokens/s (all layers)", "value": B / (ms / 1e3),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f64", "data": "synthetic",
+        "dtype": DECODE_DTYPE, "precision": DECODE_PRECISION, "data": "synthetic",
         "config": {"workload": base.name, "layers": n_layers, "batch": B, "context": T,
                    "lengths": "ragged" if args.ragged else "equal", "q_heads": base.Hq,
                    "kv_heads": base.Hkv, "head_dim": base.d, "G": base.G, "S": base.S,
@@ -269,6 +292,8 @@ def main():
     ap.add_argument("--prefill-prompt", type=int, default=0,
                     help="instead: time a chunked prefill over a prompt of this many tokens")
     ap.add_argument("--chunk", type=int, default=512, help="prefill chunk (with --prefill-prompt)")
+    ap.add_argument("--topk", type=int, default=120,
+                    help="spans kept per block (with --prefill-prompt; the pages' setting is 127)")
     ap.add_argument("--batch", type=int, default=0,
                     help="instead: batched decode of this many sequences (8B shape, 32 layers)")
     ap.add_argument("--context", type=int, default=32768, help="sequence length (with --batch)")
@@ -414,7 +439,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "step_ms_median": med, "step_ms_p90": p90,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f64", "data": "synthetic",
+        "dtype": DECODE_DTYPE if w.block_q == 1 else PREFILL_DTYPE,
+        "precision": precision(w), "data": "synthetic",
         "config": {"workload": w.name, "layers": n_layers, "context": w.T, "batch": 1,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "storage": w.dtype,
                    "G": w.G, "S": w.S, "topk": w.topk, "L": w.L,

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define REA_ABI_VERSION 3
+#define REA_ABI_VERSION 4
 
 typedef enum rea_status {
     REA_OK = 0,
@@ -157,10 +157,10 @@ typedef struct rea_sizes {
     int64_t n_sel_heads;       /* H_sel: n_kv_heads, or n_q_heads with select_per_q_head */
 } rea_sizes;
 
-/* Optional timing hooks: hipEvent_t handles (as void*) that take the start and
- * end times of the token-scoring kernel's dispatch on the call's stream
- * (hipExtLaunchKernel).  Either may be NULL.  Events created with
- * hipEventDisableSystemFence perturb the step least. */
+/* Measurement hook of rea_decode_step_timed: hipEvent_t handles (as void*)
+ * that take the start and end times of the token-scoring kernel's dispatch on
+ * the call's stream (hipExtLaunchKernel).  Either may be NULL.  Events created
+ * with hipEventDisableSystemFence perturb the step least. */
 typedef struct rea_timing {
     void *score_begin;
     void *score_end;
@@ -175,6 +175,15 @@ const char *rea_last_error(void);
 rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes *out);
 
 /*
+ * Bytes of device workspace that suffice for every entry point below that
+ * takes one (rea_score_select, rea_window_attend with W_cap = sizes.W_cap,
+ * rea_decode_step): the largest of the three rea_sizes fields.  Host-only.
+ * Returns (size_t)-1, a size no allocator grants, when p or a is invalid;
+ * rea_last_error() then says why (rea_query_sizes returns the status).
+ */
+size_t rea_workspace_bytes(const rea_problem *p, const rea_params *a);
+
+/*
  * Step 1: position-agnostic span scoring and top-k selection.
  *
  * sel          [n_blocks][H_sel][topk] int32: for block b and selection head h
@@ -186,14 +195,28 @@ rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes 
  * n_sel        [n_blocks][H_sel] int32 = k_sel (token segments: the union's
  *              size, at most k_sel).
  * span_scores  NULL, or [n_blocks][H_sel][n_spans] double: sum over the
- *              block's queries of the span's maximum token score.  Exact for
- *              bf16/fp32 inputs except on the MFMA path (bf16, head_dim 128,
- *              block_q 64, S a multiple of 32, at most 4096 spans), where they
- *              are bf16-MFMA approximations within a proven per-span bound;
- *              the selection is exact on every path (uncertain spans are
- *              re-scored in fp64 before the top-k is decided).
+ *              block's queries of the span's maximum token score.
  * ws           device workspace of at least sizes.ws_score_select bytes
  *              (256-byte aligned); contents are scratch.
+ *
+ * Precision.  Span scores are computed in fp64: a query group's sum q_eff is
+ * taken in fp64, and every product of q_eff with a key element and every sum
+ * is an fp64 operation.  With bf16 inputs each product is exact (q_eff of a
+ * few bf16 heads has few significant bits) and the sums are exact whenever
+ * they need at most 53 significant bits, which holds unless the products of
+ * one token span more than about 2^30 in magnitude; with fp32 inputs the
+ * products of a group sum (g > 1) and the sums can round.  Where they round, a
+ * token score lies within n * 2^-53 * sum|terms| of the exact value (n the
+ * number of terms), and the selection equals the exact one unless two spans'
+ * exact scores differ by less than that at the k-th boundary; these paths
+ * have no guard for such near-ties.
+ *
+ * Blocks of 64 bf16 queries with head_dim 128 and S a multiple of 32 (the
+ * MFMA path) are scored with bf16 MFMA products and fp32 sums: span_scores are
+ * then approximations, each within a bound eps_j computed for its span, and
+ * every span whose interval could reach across the k-th boundary is re-scored
+ * in fp64 before the top-k is decided, so the selection is the one the fp64
+ * scores above give.
  */
 rea_status rea_score_select(const rea_problem *p, const rea_params *a,
                             int32_t *sel, int32_t *n_sel, double *span_scores,
@@ -233,14 +256,24 @@ rea_status rea_window_attend(const rea_problem *p, const rea_params *a,
  * device).  The decode step of one layer when n_q == block_q == 1; any
  * n_q/block_q accepted by the three calls above is accepted here too.
  * out          [n_q][n_q_heads][head_dim] float32.
- * sel, n_sel   optional copies of the selection (NULL to skip).
+ * sel, n_sel   optional copies of the selection (NULL to skip), laid out as
+ *              rea_score_select's.
  * ws           at least sizes.ws_decode_step bytes.
- * timing       optional events around the scoring kernel (NULL to skip).
  */
 rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out,
                            int32_t *sel, int32_t *n_sel,
-                           void *ws, size_t ws_bytes, void *stream,
-                           const rea_timing *timing);
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * rea_decode_step with a measurement hook: the same launches, the scoring
+ * kernel's dispatch stamped into timing's events (timing may be NULL).  For
+ * benchmarks; the product path is rea_decode_step.
+ */
+rea_status rea_decode_step_timed(const rea_problem *p, const rea_params *a, float *out,
+                                 int32_t *sel, int32_t *n_sel,
+                                 void *ws, size_t ws_bytes, void *stream,
+                                 const rea_timing *timing);
+
 
 /*
  * Chunked prefill of a whole prompt (OpenReview discussion, "Prefilling
@@ -261,22 +294,32 @@ rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out
  * block_q; every chunk must pass rea_decode_step's own checks.
  */
 typedef struct rea_chunk {
-    int64_t start;      /* first query (prompt token) of the chunk */
-    int32_t n_q;        /* queries in the chunk */
-    int32_t block_q;    /* queries per selection block within the chunk */
+    int64_t start;        /* first query (prompt token) of the chunk */
+    int32_t n_q;          /* queries in the chunk */
+    int32_t block_q;      /* queries per selection block within the chunk */
+    int64_t first_block;  /* index of the chunk's first block among all the
+                             plan's blocks (blocks numbered in plan order) */
 } rea_chunk;
 
 /* Host-only: writes up to `cap` chunks to `chunks` (may be NULL when cap is 0),
- * the total count to *n_chunks, and the workspace rea_prefill needs to
+ * the total count to *n_chunks, the number of selection blocks over all
+ * chunks to *n_blocks (may be NULL), and the workspace rea_prefill needs to
  * *ws_bytes (the largest of its chunk steps').  Makes no HIP call. */
 rea_status rea_prefill_plan(const rea_problem *p, const rea_params *a, int32_t chunk,
                             rea_chunk *chunks, int32_t cap, int32_t *n_chunks,
-                            size_t *ws_bytes);
+                            int64_t *n_blocks, size_t *ws_bytes);
 
 /* Runs the plan on `stream` without host synchronisation; out is
- * [T][n_q_heads][head_dim] float32.  ws as given by rea_prefill_plan. */
+ * [T][n_q_heads][head_dim] float32.  ws as given by rea_prefill_plan.
+ * sel, n_sel   NULL, or every block's selection: [n_blocks][H_sel][sel_cap]
+ *              and [n_blocks][H_sel] int32 with n_blocks from the plan and
+ *              sel_cap = topk (topk * S with token segments); the rows of
+ *              chunk c start at block chunks[c].first_block and are laid out
+ *              as rea_score_select's for that chunk's problem (span indices
+ *              relative to the chunk's own middle [G', start + n_q - L')).
+ *              Both or neither. */
 rea_status rea_prefill(const rea_problem *p, const rea_params *a, int32_t chunk, float *out,
-                       void *ws, size_t ws_bytes, void *stream);
+                       int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Batched decode: one decode step (one query token each) for `batch`

@@ -22,12 +22,15 @@ def declared_symbols():
 def test_exports_every_declared_symbol():
     L = rea.lib()
     syms = declared_symbols()
+    # the boundary's calls: score/select, gather+RoPE, window attention, the
+    # fused step and the workspace size
     assert set(syms) >= {"rea_score_select", "rea_gather_rope", "rea_window_attend",
-                         "rea_decode_step", "rea_query_sizes"}
+                         "rea_decode_step", "rea_workspace_bytes", "rea_status_string",
+                         "rea_last_error"}
     for s in syms:
         assert hasattr(L, s), s
     assert sorted(rea.ENTRY_POINTS) == syms
-    assert L.rea_abi_version() == 3
+    assert L.rea_abi_version() == 4
     for i, name in enumerate(rea.STATUS):
         assert L.rea_status_string(i).decode() == name
 
@@ -112,8 +115,12 @@ def test_invalid_arguments(kw, expect):
     st2 = L.rea_score_select(ctypes.byref(p), ctypes.byref(a), FAKE, FAKE, None, FAKE, 1 << 40, None)
     assert st2 == expect
     st3 = L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE, 1 << 40,
-                            None, None)
+                            None)
     assert st3 == expect
+    st4 = L.rea_decode_step_timed(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE,
+                                  1 << 40, None, None)
+    assert st4 == expect
+    assert L.rea_workspace_bytes(ctypes.byref(p), ctypes.byref(a)) == rea.WORKSPACE_INVALID
 
 
 def test_no_middle_allows_many_queries():
@@ -135,12 +142,12 @@ def test_entry_point_argument_errors():
     assert L.rea_score_select(ctypes.byref(p), ctypes.byref(a), FAKE, FAKE, None, FAKE + 16,
                               s.ws_score_select, None) == E("REA_EALIGN")
     assert L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE,
-                             s.ws_decode_step - 1, None, None) == E("REA_EWORKSPACE")
+                             s.ws_decode_step - 1, None) == E("REA_EWORKSPACE")
     # null outputs
     assert L.rea_score_select(ctypes.byref(p), ctypes.byref(a), None, FAKE, None, FAKE,
                               s.ws_score_select, None) == E("REA_EINVAL")
     assert L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), None, None, None, FAKE,
-                             s.ws_decode_step, None, None) == E("REA_EINVAL")
+                             s.ws_decode_step, None) == E("REA_EINVAL")
     # window capacity too small
     assert L.rea_gather_rope(ctypes.byref(p), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE,
                              FAKE, int(s.W_cap) - 1, None) == E("REA_ESHAPE")
@@ -157,7 +164,10 @@ def test_valid_call_without_gpu_reports_no_device():
     p, a = good()
     _, s = sizes_status(p, a)
     st = L.rea_decode_step(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE,
-                           s.ws_decode_step, None, None)
+                           s.ws_decode_step, None)
+    assert st == rea.STATUS.index("REA_ENODEVICE"), L.rea_last_error()
+    st = L.rea_decode_step_timed(ctypes.byref(p), ctypes.byref(a), FAKE, None, None, FAKE,
+                                 s.ws_decode_step, None, None)
     assert st == rea.STATUS.index("REA_ENODEVICE"), L.rea_last_error()
 
 
@@ -227,3 +237,18 @@ def test_sizes_token_segments():
     a.select_flags = rea.REA_SELECT_TOKEN_SEGMENTS | rea.REA_SELECT_PER_Q_HEAD
     st, s2 = sizes_status(p, a)
     assert st == 0 and s2.n_sel_heads == 32 and s2.ws_decode_step > s.ws_decode_step
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workspace_bytes_covers_every_entry_point(cfg):
+    """rea_workspace_bytes is the largest of the three workspaces rea_query_sizes
+    reports, for the default selection and each variant."""
+    w = synth.config(cfg)
+    for extra in (dict(), dict(per_q_head=True), dict(token_segments=True)):
+        p = rea.problem(FAKE, FAKE, FAKE, dtype=rea.REA_BF16 if w.dtype == "bf16" else rea.REA_F32,
+                        n_q=w.n_q, Hq=w.Hq, Hkv=w.Hkv, d=w.d, T=w.T, stride_head=w.T * w.d,
+                        stride_tok=w.d)
+        a = rea.params(w.G, w.S, w.topk, w.L, w.block_q, **extra)
+        s = rea.query_sizes(p, a)
+        n = rea.workspace_bytes(p, a)
+        assert n == max(s.ws_score_select, s.ws_window_attend, s.ws_decode_step) > 0

@@ -3,7 +3,8 @@
   * 3B-shaped decode at 4,194,304 tokens: every KV head checked against the
     oracle (selection exact, span scores, window rows, output).
   * 8B-shaped chunked prefill (4096 queries appended at 131072, blocks of 64):
-    every (block, KV head) selection and every output checked.
+    every (block, KV head) selection and every output checked; and one
+    512-query chunk at 140,000 tokens (more than 4,096 spans per block).
   * 8B-shaped decode at 1,048,576 tokens with all 32 layers resident, run
     exactly as bench.py runs it (one shared workspace, rea_decode_step per
     layer): two layers checked in full against the oracle, every layer checked
@@ -57,6 +58,30 @@ def test_decode_4m_llama3b():
 @pytest.mark.timeout(900)
 def test_prefill_chunk_llama8b():
     _one_layer(4)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_chunk512_past_4096_spans():
+    """A 512-token prefill chunk (8 blocks of 64) at 140,000 tokens with the
+    pages' 8B setting (G 32, S 32, 127 spans, L 4096): 4,246 spans per block
+    and KV head, more than the 4,096 the MFMA block path's certification
+    holds on chip; every (block, KV head) selection and output checked."""
+    w = synth.small(name="llama8b-bf16-prefill-chunk512-at-140k", seed=240715184, Hq=32,
+                    Hkv=8, d=128, T=140000, n_q=512, block_q=64, G=32, S=32, topk=127,
+                    L=4096, needles=8, kv_scaled=True)
+    assert w.n_spans > 4096
+    log(f"[prefill chunk] {w.name}: {w.n_spans} spans per (block, KV head)")
+    q, K, V = device_inputs(w)
+    gpu = run_library(w, q, K, V)
+    del K, V
+    torch.cuda.empty_cache()
+    q64 = synth.to_f32(w.q(0), w.dtype).astype(np.float64)
+    errs = []
+    for h in range(w.Hkv):
+        ora = oracle_head(w, 0, h, q64)
+        errs.append(compare_head(w, gpu, ora, h))
+        log(f"  head {h}: parity ok, out err {errs[-1]:.2e}")
+    log(f"  max-abs out err {max(errs):.3e} (tolerance {TOL[w.dtype]})")
 
 
 @pytest.mark.timeout(1100)

@@ -221,6 +221,89 @@ def test_exact_ties_mfma_blocks():
     assert ties == w.Hkv
 
 
+@pytest.mark.parametrize("n_q,T", [(64, 3000), (128, 3000), (64, 140000)])
+def test_mfma_blocks_order_below_fp32_resolution(n_q, T):
+    """MFMA block scores whose spans differ only below fp32 resolution: 30
+    spans score 64 * (256 + 2^-12 * v_j) with distinct v_j = 1 + m_j / 128
+    (m_j < 32), so their per-token differences (m * 2^-19) lie below the fp32
+    ulp of a token score (2^-15 at 256) and only the fp64 re-scoring of the
+    uncertain spans orders them; the top-10 boundary falls among them.  Each span's
+    approximate score must stay within its bound eps_j, and the selection must
+    be the exact one.  At 140,000 tokens (4,371 spans) the certification ranks
+    only the candidate spans near the boundary."""
+    rng = np.random.default_rng(777 + n_q + T)
+    w = S(Hq=8, Hkv=2, d=128, T=T, n_q=n_q, block_q=64, S=32, topk=10, L=128, needles=0)
+    qn = np.zeros((w.n_q, w.Hq, w.d), np.float32)
+    qn[:, :, 0] = 1.0                              # q_eff[0] = 4 (four heads per KV head)
+    qn[:, :, 1] = 2.0 ** -14                       # q_eff[1] = 2^-12
+    Kn = np.zeros((w.Hkv, w.T, w.d), np.float32)
+    Kn[:, :, 0] = 32.0                             # ordinary spans: about 128 per token
+    Kn[:, :, 2:] = rng.standard_normal((w.Hkv, w.T, w.d - 2)) * 2.0 ** -20
+    lo, hi = w.mid
+    n_full = (hi - lo) // w.S
+    for h in range(w.Hkv):
+        spans = rng.choice(n_full, size=30, replace=False)
+        ms = rng.choice(32, size=30, replace=False)     # neighbours at most 3 apart
+        for j, m in zip(spans, ms):
+            t0 = lo + j * w.S
+            Kn[h, t0:t0 + w.S, 0] = 64.0
+            # the span's maximum sits on one token; the others score lower
+            Kn[h, t0:t0 + w.S, 1] = 1.0
+            Kn[h, t0 + int(rng.integers(w.S)), 1] = 1.0 + m / 128.0
+    Kn = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(Kn))     # noise rounded to bf16
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    assert np.array_equal(bf(Kn), Kn.astype(np.float64)) and np.array_equal(bf(qn), qn)
+    gpu = run_library(w, to_bf(qn), to_bf(Kn), to_bf(Vn))
+    q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
+    for h in range(w.Hkv):
+        ora = oracle_head(w, 0, h, q64, K64[h:h + 1], V64[h:h + 1])
+        sc = ora["sc"]
+        for b in range(w.n_q // w.block_q):
+            top = np.sort(sc[b])[::-1]
+            gap = top[w.topk - 1] - top[w.topk]
+            # the exact gap at the boundary is below one fp32 ulp of a token score
+            assert 0 < gap < 64 * 2.0 ** -15, (h, b, gap)
+            # and the approximate scores cannot order the candidates
+            assert ora["eps"][b].max() > 100 * gap
+        compare_head(w, gpu, ora, h)
+        log(f"  head {h}: worst |s_hat - s| / eps_j = {ora['eps_used']:.3g}")
+
+
+def test_mfma_blocks_massive_ties_past_4096_spans():
+    """Beyond 4096 spans, with every span but a few scoring exactly alike
+    (integer keys repeating one pattern): the candidates near the k-th score
+    would be nearly every span, so the pairs take the exact fallback (fp64
+    scores on the VALU, then the ordinary top-k); the 20 raised spans and the
+    30 lowest indices of the tie must be selected."""
+    rng = np.random.default_rng(5150)
+    w = S(Hq=4, Hkv=2, d=128, T=140000, n_q=64, block_q=64, S=32, topk=50, L=128, needles=0)
+    assert w.n_spans > 4096
+    qn = rng.integers(0, 2, size=(w.n_q, w.Hq, w.d)).astype(np.float32)
+    pattern = rng.integers(0, 3, size=(w.S, w.d)).astype(np.float32)
+    Kn = np.zeros((w.Hkv, w.T, w.d), np.float32)
+    lo, hi = w.mid
+    n_full = (hi - lo) // w.S
+    Kn[:, lo:lo + n_full * w.S] = np.tile(pattern, (n_full, 1))[None]
+    for h in range(w.Hkv):
+        for j in rng.choice(w.n_spans - 1, size=20, replace=False):
+            Kn[h, lo + j * w.S:lo + (j + 1) * w.S] = pattern + 1.0
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    gpu = run_library(w, to_bf(qn), to_bf(Kn), to_bf(Vn))
+    q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
+    for h in range(w.Hkv):
+        ora = oracle_head(w, 0, h, q64, K64[h:h + 1], V64[h:h + 1])
+        sc = ora["sc"][0]
+        kth = np.sort(sc)[::-1][w.topk - 1]
+        assert int((sc > kth).sum()) == 20 and int((sc == kth).sum()) > 4096
+        compare_head(w, gpu, ora, h)
+
+
 def test_deterministic():
     w = SMALL["bf16_many_heads"]
     q, K, V = device_inputs(w)
@@ -253,6 +336,8 @@ VARIANTS = {
     "token_level": dict(S=1, topk=3840),
     # the 120 best tokens, each widened to 32 tokens
     "token_segments": dict(token_segments=True),
+    # the pages' own LLaMA3-8B-8K tuple: 127 spans, window exactly 8192
+    "pages_k127": dict(topk=127),
 }
 
 

@@ -45,6 +45,14 @@ def test_plan_follows_the_stated_rule(T, G, S, k, L, bq, chunk):
     p, a = make(T, G, S, k, L, bq)
     plan, ws = rea.prefill_plan(p, a, chunk)
     assert plan == expected_plan(T, G, L, bq, chunk)
+    # blocks are numbered in plan order for rea_prefill's selection outputs
+    plan4, n_blocks, ws4 = rea.prefill_plan(p, a, chunk, with_blocks=True)
+    assert [c[:3] for c in plan4] == plan and ws4 == ws
+    first = 0
+    for (s0, n, b, fb) in plan4:
+        assert fb == first
+        first += n // b
+    assert n_blocks == first
     # contiguous cover of the prompt, each block size dividing its chunk
     assert plan[0][0] == 0 and sum(n for _, n, _ in plan) == T
     for (s0, n0, _), (s1, _, _) in zip(plan, plan[1:]):
@@ -62,7 +70,7 @@ def test_plan_follows_the_stated_rule(T, G, S, k, L, bq, chunk):
 def status_of(p, a, chunk):
     n, ws = ctypes.c_int32(), ctypes.c_size_t()
     return rea.lib().rea_prefill_plan(ctypes.byref(p), ctypes.byref(a), chunk, None, 0,
-                                      ctypes.byref(n), ctypes.byref(ws))
+                                      ctypes.byref(n), None, ctypes.byref(ws))
 
 
 def test_plan_rejects_bad_arguments():
@@ -75,5 +83,10 @@ def test_plan_rejects_bad_arguments():
                     stride_head=3000 * 128, stride_tok=128)
     assert status_of(q, a, 128) == EINVAL          # not every prompt token is a query
     assert "n_q" in rea.lib().rea_last_error().decode()
-    assert rea.lib().rea_prefill(ctypes.byref(p), ctypes.byref(a), 128, None, None, 0,
-                                 None) == EINVAL   # out is NULL
+    L = rea.lib()
+    assert L.rea_prefill(ctypes.byref(p), ctypes.byref(a), 128, None, None, None, None, 0,
+                         None) == EINVAL           # out is NULL
+    assert L.rea_prefill(ctypes.byref(p), ctypes.byref(a), 128, FAKE, FAKE, None, None, 0,
+                         None) == EINVAL           # sel without n_sel
+    assert L.rea_prefill(ctypes.byref(p), ctypes.byref(a), 128, FAKE, FAKE + 2, FAKE, None, 0,
+                         None) == rea.STATUS.index("REA_EALIGN")

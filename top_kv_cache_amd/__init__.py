@@ -19,9 +19,12 @@ REA_SELECT_PER_Q_HEAD, REA_SELECT_TOKEN_SEGMENTS = 1, 2
 STATUS = ["REA_OK", "REA_EINVAL", "REA_ESHAPE", "REA_EDTYPE", "REA_EALIGN",
           "REA_EWORKSPACE", "REA_ENODEVICE", "REA_ELAUNCH", "REA_EUNSUPPORTED"]
 ENTRY_POINTS = ["rea_abi_version", "rea_status_string", "rea_last_error", "rea_query_sizes",
-                "rea_score_select", "rea_gather_rope", "rea_window_attend", "rea_decode_step",
+                "rea_workspace_bytes", "rea_score_select", "rea_gather_rope",
+                "rea_window_attend", "rea_decode_step", "rea_decode_step_timed",
                 "rea_prefill_plan", "rea_prefill", "rea_decode_batch_workspace",
                 "rea_decode_batch"]
+ABI_VERSION = 4
+WORKSPACE_INVALID = ctypes.c_size_t(-1).value     # rea_workspace_bytes on invalid arguments
 
 
 class Problem(ctypes.Structure):
@@ -52,7 +55,8 @@ class Timing(ctypes.Structure):
 
 
 class Chunk(ctypes.Structure):
-    _fields_ = [("start", ctypes.c_int64), ("n_q", ctypes.c_int32), ("block_q", ctypes.c_int32)]
+    _fields_ = [("start", ctypes.c_int64), ("n_q", ctypes.c_int32), ("block_q", ctypes.c_int32),
+                ("first_block", ctypes.c_int64)]
 
 
 class ReaError(RuntimeError):
@@ -82,6 +86,8 @@ def lib():
     L.rea_last_error.restype = ctypes.c_char_p
     L.rea_query_sizes.restype = ctypes.c_int
     L.rea_query_sizes.argtypes = [P, A, ctypes.POINTER(Sizes)]
+    L.rea_workspace_bytes.restype = ctypes.c_size_t
+    L.rea_workspace_bytes.argtypes = [P, A]
     L.rea_score_select.restype = ctypes.c_int
     L.rea_score_select.argtypes = [P, A, i32p, i32p, vp, vp, ctypes.c_size_t, vp]
     L.rea_gather_rope.restype = ctypes.c_int
@@ -90,20 +96,23 @@ def lib():
     L.rea_window_attend.argtypes = [P, A, vp, vp, vp, i32p, ctypes.c_int32, vp, vp,
                                     ctypes.c_size_t, vp]
     L.rea_decode_step.restype = ctypes.c_int
-    L.rea_decode_step.argtypes = [P, A, vp, i32p, i32p, vp, ctypes.c_size_t, vp,
-                                  ctypes.POINTER(Timing)]
+    L.rea_decode_step.argtypes = [P, A, vp, i32p, i32p, vp, ctypes.c_size_t, vp]
+    L.rea_decode_step_timed.restype = ctypes.c_int
+    L.rea_decode_step_timed.argtypes = [P, A, vp, i32p, i32p, vp, ctypes.c_size_t, vp,
+                                        ctypes.POINTER(Timing)]
     L.rea_prefill_plan.restype = ctypes.c_int
     L.rea_prefill_plan.argtypes = [P, A, ctypes.c_int32, ctypes.POINTER(Chunk), ctypes.c_int32,
-                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
+                                   ctypes.POINTER(ctypes.c_size_t)]
     L.rea_prefill.restype = ctypes.c_int
-    L.rea_prefill.argtypes = [P, A, ctypes.c_int32, vp, vp, ctypes.c_size_t, vp]
+    L.rea_prefill.argtypes = [P, A, ctypes.c_int32, vp, i32p, i32p, vp, ctypes.c_size_t, vp]
     L.rea_decode_batch_workspace.restype = ctypes.c_int
     L.rea_decode_batch_workspace.argtypes = [P, A, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     L.rea_decode_batch.restype = ctypes.c_int
     L.rea_decode_batch.argtypes = [P, A, ctypes.c_int32, vp, ctypes.c_int64, vp, i32p, i32p, vp,
                                    ctypes.c_size_t, vp]
-    if L.rea_abi_version() != 3:
-        raise ImportError("librea.so ABI version mismatch")
+    if L.rea_abi_version() != ABI_VERSION:
+        raise ImportError(f"librea.so ABI version {L.rea_abi_version()} != {ABI_VERSION}: rebuild it")
     _lib = L
     return L
 
@@ -128,16 +137,28 @@ def params(G, S, topk, L, block_q=1, rope_theta=500000.0, softmax_scale=0.0,
     return Params(ctypes.sizeof(Params), G, S, topk, L, block_q, rope_theta, softmax_scale, flags)
 
 
-def prefill_plan(p: Problem, a: Params, chunk: int):
-    """(list of (start, n_q, block_q), workspace bytes) of a chunked prefill.
-    Host-only (no GPU needed)."""
-    n, ws = ctypes.c_int32(), ctypes.c_size_t()
+def prefill_plan(p: Problem, a: Params, chunk: int, with_blocks: bool = False):
+    """(list of (start, n_q, block_q), workspace bytes) of a chunked prefill;
+    with_blocks: (list of (start, n_q, block_q, first_block), total blocks,
+    workspace bytes).  Host-only (no GPU needed)."""
+    n, nb, ws = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_size_t()
     _check(lib().rea_prefill_plan(ctypes.byref(p), ctypes.byref(a), chunk, None, 0,
-                                  ctypes.byref(n), ctypes.byref(ws)))
+                                  ctypes.byref(n), ctypes.byref(nb), ctypes.byref(ws)))
     arr = (Chunk * max(n.value, 1))()
     _check(lib().rea_prefill_plan(ctypes.byref(p), ctypes.byref(a), chunk, arr, n.value,
-                                  ctypes.byref(n), ctypes.byref(ws)))
+                                  ctypes.byref(n), ctypes.byref(nb), ctypes.byref(ws)))
+    if with_blocks:
+        return ([(c.start, c.n_q, c.block_q, c.first_block) for c in arr[:n.value]], nb.value,
+                ws.value)
     return [(c.start, c.n_q, c.block_q) for c in arr[:n.value]], ws.value
+
+
+def workspace_bytes(p: Problem, a: Params) -> int:
+    """rea_workspace_bytes (raises on invalid arguments).  Host-only."""
+    n = lib().rea_workspace_bytes(ctypes.byref(p), ctypes.byref(a))
+    if n == WORKSPACE_INVALID:
+        raise ReaError(1, lib().rea_last_error().decode())
+    return n
 
 
 def query_sizes(p: Problem, a: Params) -> Sizes:
@@ -270,11 +291,17 @@ class Step:
             out = torch.empty((n_q, Hq, d), dtype=torch.float32, device=self.device)
         if ws is None:
             ws = self.workspace()
-        _check(lib().rea_decode_step(ctypes.byref(self.prob), ctypes.byref(self.par), _ptr(out),
-                                     _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel(),
-                                     _stream(stream),
-                                     ctypes.byref(timing) if timing is not None else None))
+        if timing is None:
+            _check(lib().rea_decode_step(ctypes.byref(self.prob), ctypes.byref(self.par),
+                                         _ptr(out), _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel(),
+                                         _stream(stream)))
+        else:
+            _check(lib().rea_decode_step_timed(ctypes.byref(self.prob), ctypes.byref(self.par),
+                                               _ptr(out), _ptr(sel), _ptr(nsel), _ptr(ws),
+                                               ws.numel(), _stream(stream),
+                                               ctypes.byref(timing)))
         return out
+
 
 
 class Prefill:
@@ -288,21 +315,40 @@ class Prefill:
         self.par = params(G, S, topk, L, block_q, rope_theta, softmax_scale, per_q_head,
                           token_segments)
         self.chunk = chunk
-        self.plan, self.ws_bytes = prefill_plan(self.prob, self.par, chunk)
+        plan, self.n_blocks, self.ws_bytes = prefill_plan(self.prob, self.par, chunk,
+                                                          with_blocks=True)
+        self.plan = [c[:3] for c in plan]
+        self.first_block = [c[3] for c in plan]
+        self.n_sel_heads = self.prob.n_q_heads if per_q_head else self.prob.n_kv_heads
+        self.sel_cap = topk * S if token_segments else topk
         self.device = q.device
 
     def workspace(self):
         return _aligned(_ws(self.ws_bytes, self.device))
 
-    def run(self, out=None, ws=None, stream=None):
+    def selection_buffers(self):
+        """(sel [n_blocks][H_sel][sel_cap], n_sel [n_blocks][H_sel]) int32 device
+        tensors for run(); chunk c's blocks start at self.first_block[c]."""
+        torch = _torch()
+        sel = torch.empty((self.n_blocks, self.n_sel_heads, max(self.sel_cap, 1)),
+                          dtype=torch.int32, device=self.device)
+        nsel = torch.empty((self.n_blocks, self.n_sel_heads), dtype=torch.int32,
+                           device=self.device)
+        return sel, nsel
+
+    def run(self, out=None, ws=None, stream=None, sel=None, nsel=None):
         torch = _torch()
         T, Hq, d = self.prob.n_q, self.prob.n_q_heads, self.prob.head_dim
         if out is None:
             out = torch.empty((T, Hq, d), dtype=torch.float32, device=self.device)
         if ws is None:
             ws = self.workspace()
+        if sel is not None and (sel.shape[0] != self.n_blocks or sel.shape[2] != max(self.sel_cap, 1)
+                                or not sel.is_contiguous()):
+            raise ValueError("sel must be a contiguous [n_blocks][H_sel][sel_cap] tensor")
         _check(lib().rea_prefill(ctypes.byref(self.prob), ctypes.byref(self.par), self.chunk,
-                                 _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+                                 _ptr(out), _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel(),
+                                 _stream(stream)))
         return out
 
 

@@ -304,6 +304,15 @@ rea_status rea_query_sizes(const rea_problem *p, const rea_params *a, rea_sizes 
     return REA_OK;
 }
 
+size_t rea_workspace_bytes(const rea_problem *p, const rea_params *a) {
+    rea_sizes s;
+    if (rea_query_sizes(p, a, &s) != REA_OK) return (size_t)-1;
+    size_t need = s.ws_score_select;
+    if (s.ws_window_attend > need) need = s.ws_window_attend;
+    if (s.ws_decode_step > need) need = s.ws_decode_step;
+    return need;
+}
+
 rea_status rea_score_select(const rea_problem *p, const rea_params *a, int32_t *sel,
                             int32_t *n_sel, double *span_scores, void *ws, size_t ws_bytes,
                             void *stream) {
@@ -374,16 +383,25 @@ namespace {
 // table rows already valid at the start of ws (from an earlier step on the
 // same workspace, theta and head_dim); out, the rows valid after this step
 // (0 when the step's path does not keep the table there).
-rea_status decode_step(const rea_problem *p, const rea_params *a, float *out, int32_t *sel,
-                       int32_t *n_sel, void *ws, size_t ws_bytes, void *stream,
-                       const rea_timing *timing, int64_t *rope_rows) {
-    rea::Geom g;
-    rea_status st = make_geom(p, a, &g);
+// Host-side checks of rea_decode_step's arguments other than the workspace;
+// *g gets the geometry.
+rea_status decode_args(const rea_problem *p, const rea_params *a, const float *out,
+                       const int32_t *sel, const int32_t *n_sel, rea::Geom *g) {
+    rea_status st = make_geom(p, a, g);
     if (st != REA_OK) return st;
     if (!out) return fail(REA_EINVAL, "out is NULL");
     if (!aligned(out, 16)) return fail(REA_EALIGN, "out must be 16-byte aligned");
     if ((sel && !aligned(sel, 4)) || (n_sel && !aligned(n_sel, 4)))
         return fail(REA_EALIGN, "sel / n_sel must be 4-byte aligned");
+    return REA_OK;
+}
+
+rea_status decode_step(const rea_problem *p, const rea_params *a, float *out, int32_t *sel,
+                       int32_t *n_sel, void *ws, size_t ws_bytes, void *stream,
+                       const rea_timing *timing, int64_t *rope_rows) {
+    rea::Geom g;
+    rea_status st = decode_args(p, a, out, sel, n_sel, &g);
+    if (st != REA_OK) return st;
     if ((st = check_ws(ws, ws_bytes, decode_ws_bytes(g))) != REA_OK) return st;
     int num_cu = 0;
     if ((st = device_ready(&num_cu)) != REA_OK) return st;
@@ -436,12 +454,20 @@ extern "C" {
 
 rea_status rea_decode_step(const rea_problem *p, const rea_params *a, float *out,
                            int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes,
-                           void *stream, const rea_timing *timing) {
+                           void *stream) {
+    g_err[0] = 0;
+    return decode_step(p, a, out, sel, n_sel, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+rea_status rea_decode_step_timed(const rea_problem *p, const rea_params *a, float *out,
+                                 int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes,
+                                 void *stream, const rea_timing *timing) {
     g_err[0] = 0;
     return decode_step(p, a, out, sel, n_sel, ws, ws_bytes, stream, timing, nullptr);
 }
 
 }  // extern "C"
+
 
 // ---- chunked prefill ------------------------------------------------------
 
@@ -455,6 +481,8 @@ int32_t block_for(int32_t n, int32_t bq) {
 }
 
 // The chunk plan; calls emit(start, n_q, block_q) for each chunk in order.
+// Chunk c's blocks follow chunk c-1's in the numbering of rea_prefill's
+// selection outputs.
 template <typename F>
 rea_status prefill_plan(const rea_problem *p, const rea_params *a, int32_t chunk, F emit) {
     if (!p || !a) return fail(REA_EINVAL, "problem or params is NULL");
@@ -501,11 +529,12 @@ extern "C" {
 
 rea_status rea_prefill_plan(const rea_problem *p, const rea_params *a, int32_t chunk,
                             rea_chunk *chunks, int32_t cap, int32_t *n_chunks,
-                            size_t *ws_bytes) {
+                            int64_t *n_blocks, size_t *ws_bytes) {
     g_err[0] = 0;
     if (!n_chunks || !ws_bytes) return fail(REA_EINVAL, "n_chunks or ws_bytes is NULL");
     if (cap > 0 && !chunks) return fail(REA_EINVAL, "chunks is NULL while cap > 0");
     int32_t count = 0;
+    int64_t blocks = 0;
     size_t need = 0;
     rea_status st = prefill_plan(p, a, chunk, [&](int64_t start, int32_t n, int32_t bq) {
         rea_problem pc;
@@ -516,35 +545,48 @@ rea_status rea_prefill_plan(const rea_problem *p, const rea_params *a, int32_t c
         if (s2 != REA_OK) return s2;
         const size_t w = decode_ws_bytes(g);
         if (w > need) need = w;
-        if (count < cap) chunks[count] = rea_chunk{start, n, bq};
+        if (count < cap) chunks[count] = rea_chunk{start, n, bq, blocks};
         ++count;
+        blocks += n / bq;
         return REA_OK;
     });
     if (st != REA_OK) return st;
     *n_chunks = count;
+    if (n_blocks) *n_blocks = blocks;
     *ws_bytes = need;
     return REA_OK;
 }
 
 rea_status rea_prefill(const rea_problem *p, const rea_params *a, int32_t chunk, float *out,
-                       void *ws, size_t ws_bytes, void *stream) {
+                       int32_t *sel, int32_t *n_sel, void *ws, size_t ws_bytes, void *stream) {
     g_err[0] = 0;
     if (!out) return fail(REA_EINVAL, "out is NULL");
+    if (!sel != !n_sel) return fail(REA_EINVAL, "give both sel and n_sel, or neither");
+    if ((sel && !aligned(sel, 4)) || (n_sel && !aligned(n_sel, 4)))
+        return fail(REA_EALIGN, "sel / n_sel must be 4-byte aligned");
     int32_t count = 0;
     size_t need = 0;
-    rea_status st = rea_prefill_plan(p, a, chunk, nullptr, 0, &count, &need);
+    rea_status st = rea_prefill_plan(p, a, chunk, nullptr, 0, &count, nullptr, &need);
     if (st != REA_OK) return st;
     if ((st = check_ws(ws, ws_bytes, need)) != REA_OK) return st;
+    // rows per block of the selection outputs: the selection heads and the
+    // capacity of one selection, as rea_score_select lays them out (the plan
+    // has validated p and a)
+    const int64_t heads = (a->select_flags & REA_SELECT_PER_Q_HEAD) ? p->n_q_heads : p->n_kv_heads;
+    const int64_t cap_sel =
+        (a->select_flags & REA_SELECT_TOKEN_SEGMENTS) ? (int64_t)a->topk * a->S : a->topk;
     // the chunks share the workspace, so the RoPE table of the window
     // positions is built once (again only when the window capacity grows)
-    int64_t rope_rows = 0;
+    int64_t rope_rows = 0, block = 0;
     return prefill_plan(p, a, chunk, [&](int64_t start, int32_t n, int32_t bq) {
         rea_problem pc;
         rea_params ac;
         chunk_view(p, a, start, n, bq, &pc, &ac);
         float *oc = out + (size_t)start * p->n_q_heads * p->head_dim;
-        return decode_step(&pc, &ac, oc, nullptr, nullptr, ws, ws_bytes, stream, nullptr,
-                           &rope_rows);
+        int32_t *sc = sel ? sel + block * heads * cap_sel : nullptr;
+        int32_t *nc = n_sel ? n_sel + block * heads : nullptr;
+        block += n / bq;
+        return decode_step(&pc, &ac, oc, sc, nc, ws, ws_bytes, stream, nullptr, &rope_rows);
     });
 }
 

@@ -98,11 +98,14 @@ hipError_t launch_struct(void (*kern)(A), dim3 grid, dim3 block, size_t lds, hip
 
 // Step 1a: span scores [n_blk][Hkv][n_spans] (double) and the maximum of every
 // group of 32 consecutive spans [n_blk][Hkv][score_groups(g)].  Non-null
-// events time the scoring kernel's dispatch.
+// events time the scoring kernel's dispatch.  only (blocks of several queries):
+// null, or one flag per (block, KV head) in device memory; then only the
+// flagged pairs are scored.
 int64_t score_groups(const Geom &g);
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
                         double *group_max, int num_cu, hipStream_t s,
-                        hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
+                        hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr,
+                        const uint32_t *only = nullptr);
 
 // Token segments: widen each selected token (sel_tok [n_blk*Hkv][k_tok],
 // middle-relative, ascending) to g.seg tokens and write the union, ascending,
@@ -110,13 +113,15 @@ hipError_t launch_score(const Geom &g, const void *q, const void *k, double *spa
 hipError_t launch_widen(const Geom &g, const int32_t *sel_tok, const int32_t *nsel_tok,
                         int32_t *sel, int32_t *n_sel, hipStream_t s);
 
-// Step 1b: top-k per (block, KV head) from the span scores and group maxima.
+// Step 1b: top-k per (block, KV head) from the span scores and group maxima;
+// only: null, or device flags per (block, KV head) selecting the pairs to run.
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
-                       int32_t *sel, int32_t *n_sel, hipStream_t s);
+                       int32_t *sel, int32_t *n_sel, hipStream_t s,
+                       const uint32_t *only = nullptr);
 
-// Step 1 for blocks of 64 queries on MFMA (bf16, d 128, S a multiple of 32,
-// at most 4096 spans): approximate span scores with a proven error bound, then
-// an exact top-k that re-scores the uncertain spans in fp64.
+// Step 1 for blocks of 64 queries on MFMA (bf16, d 128, S a multiple of 32):
+// approximate span scores with a proven error bound, then an exact top-k that
+// re-scores the uncertain spans in fp64.
 bool mfma_block_path(const Geom &g);
 size_t mfma_ws_bytes(const Geom &g);
 hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,

@@ -53,6 +53,9 @@ struct ScoreArgs {
     const int64_t *lens;
     int hps, G, L;
     int64_t T, seq_stride_bytes;
+    // null, or one flag per (block, KV head): k_score_block scores only the
+    // flagged pairs (the exact fallback of the MFMA block path)
+    const uint32_t *only;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -606,6 +609,7 @@ __global__ __launch_bounds__(kThreads) void k_score_block(ScoreArgs a) {
     const int rs = lane / LPR, ch = lane % LPR;
     const int bh = blockIdx.x / a.P, p = blockIdx.x % a.P;
     const int b = bh / a.Hkv, h = bh % a.Hkv;
+    if (a.only && !a.only[bh]) return;
 
     const TIn *qb = (const TIn *)a.q;
     for (int idx = threadIdx.x; idx < a.block_q * D; idx += kThreads) {
@@ -726,9 +730,10 @@ int64_t score_groups(const Geom &g) { return (g.n_spans + kGroup - 1) / kGroup; 
 
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
                         double *group_max, int num_cu, hipStream_t s, hipEvent_t ev_begin,
-                        hipEvent_t ev_end) {
+                        hipEvent_t ev_end, const uint32_t *only) {
     if (g.n_spans == 0) return hipSuccess;
     ScoreArgs a;
+    a.only = only;
     a.q = q;
     a.k = (const unsigned char *)k;
     a.out = span_scores;

@@ -18,6 +18,11 @@
 //                 queries are taken in the epilogue; one fp64 span score per
 //                 (block, span) is written, and each span's largest key norm
 //                 (by one wave of the grid per span).
+//   k_cert_candidates
+//                 only beyond 4096 spans: per (block, KV head), the spans
+//                 whose approximate score lies within twice the largest error
+//                 bound of the (k+1)-th (a superset of every span the
+//                 certification could keep or re-score); see there.
 //   k_certify_head, k_rescore, k_certify_tail
 //                 per (block, KV head): exact top-k from the approximate
 //                 scores (see below): the classification per pair, the fp64
@@ -491,11 +496,26 @@ struct CertArgs {
     int S, Hkv, n_q, kk, topk, rep;
     // the three certification kernels' shared state
     int R;
-    int32_t *gxs;       // [pairs][kCCap] uncertain spans
-    uint32_t *gbits;    // [pairs][kCCap / 32] certain spans
+    int32_t *gxs;       // [pairs][kCCap] uncertain spans (positions among the ranked ones)
+    uint32_t *gbits;    // [pairs][kCCap / 32] certain spans (bits by position)
     uint32_t *gcnt;     // [pairs][4]: nx, nd, decided without ranking
     double *gpart;      // [pairs][2][kCCap] per-item sums of the re-scoring
+    // more than kCCap spans: the spans ranked per pair are its candidates
+    // (k_cert_candidates); null when every span is ranked (position = index)
+    int32_t *gcand;     // [pairs][kCCap] candidate span indices, ascending
+    uint32_t *gncand;   // [pairs] candidates
+    uint32_t *gover;    // [pairs] 1: too many candidates, the exact fallback selects
 };
+
+// Span index of the pair's ranked span at position c.
+__device__ __forceinline__ int32_t span_at(const CertArgs &a, int64_t bh, int64_t c) {
+    return a.gcand ? a.gcand[bh * kCCap + c] : (int32_t)c;
+}
+
+// Spans the pair ranks: all of them, or its candidates.
+__device__ __forceinline__ int64_t ranked(const CertArgs &a, int64_t bh) {
+    return a.gcand ? (int64_t)a.gncand[bh] : a.n_spans;
+}
 
 struct CertShared {
     double val[kCCap];
@@ -672,17 +692,24 @@ __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh,
             for (int64_t i = tid; i < a.topk; i += kCThreads) sel[i] = i < kk ? (int32_t)i : -1;
         return false;
     }
-    // the approximate scores and their error bounds, every load in flight
-    // together (n <= kCCap: kCPer per thread), kept in registers for the
-    // three passes below
+    // the ranked spans (every span, or the pair's candidates: m <= kCCap),
+    // their approximate scores and error bounds, every load in flight
+    // together (kCPer per thread), kept in registers for the three passes
+    // below; position c holds span jv
+    const int64_t m = ranked(a, bh);
     double sv[kCPer], ev[kCPer];
+    int32_t jv[kCPer];
     {
         double kv[kCPer];
 #pragma unroll
         for (int e = 0; e < kCPer; ++e) {
-            const int64_t j = tid + (int64_t)e * kCThreads;
-            sv[e] = shat[j < n ? j : 0];
-            kv[e] = kbar[j < n ? j : 0];
+            const int64_t c = tid + (int64_t)e * kCThreads;
+            jv[e] = c < m ? span_at(a, bh, c) : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < kCPer; ++e) {
+            sv[e] = shat[jv[e]];
+            kv[e] = kbar[jv[e]];
         }
 #pragma unroll
         for (int e = 0; e < kCPer; ++e) ev[e] = cert_eps(Eb, kv[e], sv[e]);
@@ -690,28 +717,29 @@ __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh,
     // tau_L = kk-th largest lower end, tau_U = (kk+1)-th largest upper end
 #pragma unroll
     for (int e = 0; e < kCPer; ++e) {
-        const int64_t j = tid + (int64_t)e * kCThreads;
-        if (j < n) {
-            sh.val[j] = sv[e] - ev[e];
-            sh.idx[j] = (int32_t)j;
+        const int64_t c = tid + (int64_t)e * kCThreads;
+        if (c < m) {
+            sh.val[c] = sv[e] - ev[e];
+            sh.idx[c] = jv[e];
         }
     }
     __syncthreads();
-    c_find_kth(sh, (uint32_t)n, kk);
+    c_find_kth(sh, (uint32_t)m, kk);
     const double tauL = sh.cut_v;
 #pragma unroll
     for (int e = 0; e < kCPer; ++e) {
-        const int64_t j = tid + (int64_t)e * kCThreads;
-        if (j < n) {
-            sh.val[j] = sv[e] + ev[e];
-            sh.idx[j] = (int32_t)j;
+        const int64_t c = tid + (int64_t)e * kCThreads;
+        if (c < m) {
+            sh.val[c] = sv[e] + ev[e];
+            sh.idx[c] = jv[e];
         }
     }
     __syncthreads();
-    c_find_kth(sh, (uint32_t)n, kk + 1);
+    c_find_kth(sh, (uint32_t)m, kk + 1);
     const double tauU = sh.cut_v;
     // certainly in: lower end above tau_U.  Possibly in: upper end >= tau_L.
-    const int nwords = (int)((n + 31) / 32);
+    // Bits and uncertain entries are by position.
+    const int nwords = (int)((m + 31) / 32);
     for (int i = tid; i < nwords; i += kCThreads) sh.bitmap[i] = 0u;
     if (tid == 0) {
         sh.nd = 0;
@@ -720,15 +748,15 @@ __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh,
     __syncthreads();
 #pragma unroll
     for (int ei = 0; ei < kCPer; ++ei) {
-        const int64_t j = tid + (int64_t)ei * kCThreads;
-        if (j >= n) continue;
+        const int64_t c = tid + (int64_t)ei * kCThreads;
+        if (c >= m) continue;
         const double s = sv[ei], e = ev[ei];
         if (s - e > tauU) {
-            atomicOr(&sh.bitmap[j >> 5], 1u << (j & 31));
+            atomicOr(&sh.bitmap[c >> 5], 1u << (c & 31));
             atomicAdd(&sh.nd, 1u);
         } else if (s + e >= tauL) {
             const uint32_t slot = atomicAdd(&sh.nx, 1u);
-            sh.xs[slot] = (int32_t)j;
+            sh.xs[slot] = (int32_t)c;
         }
     }
     __syncthreads();
@@ -776,7 +804,7 @@ __device__ __forceinline__ void cert_rescore(const CertArgs &a, Sh &sh, int64_t 
         for (uint32_t it = first; it < n_items; it += step) {
             const uint32_t x = split ? it >> 1 : it;
             const int p0 = split ? (int)(it & 1) : 0, p1 = split ? p0 + 1 : 2;
-            const int64_t j = sh.xs[x];
+            const int64_t j = span_at(a, bh, sh.xs[x]);
             const int64_t tb = a.mid_lo + j * a.S, te = min(tb + (int64_t)a.S, a.mid_hi);
             double total = 0.0;
             for (int part = p0; part < p1; ++part) {
@@ -879,12 +907,13 @@ __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, i
                                             uint32_t nx, int64_t need) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kk = a.kk;
-    const int nwords = (int)((a.n_spans + 31) / 32);
+    const int nwords = (int)((ranked(a, bh) + 31) / 32);
     int32_t *sel = a.sel ? a.sel + bh * a.topk : nullptr;
     if (need > 0) {
+        // ranked by exact score, then span index
         for (uint32_t x = tid; x < nx; x += kCThreads) {
             sh.val[x] = sh.xv[x];
-            sh.idx[x] = sh.xs[x];
+            sh.idx[x] = span_at(a, bh, sh.xs[x]);
         }
         __syncthreads();
         c_find_kth(sh, nx, need);
@@ -892,8 +921,9 @@ __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, i
         const int32_t cj = sh.cut_j;
         for (uint32_t x = tid; x < nx; x += kCThreads) {
             const double v = sh.xv[x];
-            const int32_t j = sh.xs[x];
-            if (v > cv || (v == cv && j <= cj)) atomicOr(&sh.bitmap[j >> 5], 1u << (j & 31));
+            const int32_t c = sh.xs[x];
+            const int32_t j = sh.idx[x];
+            if (v > cv || (v == cv && j <= cj)) atomicOr(&sh.bitmap[c >> 5], 1u << (c & 31));
         }
         __syncthreads();
     }
@@ -922,11 +952,162 @@ __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, i
             while (w) {
                 const int bit = __ffs(w) - 1;
                 w &= w - 1;
-                if (pos < (uint32_t)a.topk) sel[pos] = tid * 32 + bit;
+                if (pos < (uint32_t)a.topk) sel[pos] = span_at(a, bh, tid * 32 + bit);
                 ++pos;
             }
             for (int64_t i = (int64_t)kk + tid; i < a.topk; i += kCThreads) sel[i] = -1;
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_cert_candidates: grid (pairs), 1024 threads; only when a pair has more
+// spans than the certification ranks on chip (kCCap).  Let c' be the
+// (kk+1)-th largest approximate score and eps_max the largest error bound of
+// the pair.  Every span scoring below c' - 2 eps_max has an upper end below
+// c' - eps_max, which is below the kk-th largest lower end and below the
+// (kk+1)-th largest upper end (the kk + 1 best approximate scores keep their
+// ends above c' - eps_max and c'): such spans are certainly out, and leaving
+// them out of the ranking changes neither threshold.  So the certification
+// ranks only the spans scoring at least theta = m* - 2 eps_max, with m* the
+// smallest score in the histogram bin holding c' (m* <= c').  They are listed
+// in ascending span order; more than kCCap of them (massive near-ties) flag
+// the pair for the exact fallback (k_score_block on the VALU, then k_topk).
+// Passes over the pair's scores: range, histogram, m*, ordered compaction.
+// ---------------------------------------------------------------------------
+constexpr int kPThreads = 1024;
+constexpr int kPWaves = kPThreads / 64;
+
+__global__ __launch_bounds__(kPThreads) void k_cert_candidates(CertArgs a) {
+    __shared__ uint32_t hist[kCBins];
+    __shared__ double red[3][kPWaves];
+    __shared__ uint32_t wsum[kPWaves];
+    __shared__ int32_t s_bstar;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % a.Hkv);
+    const int64_t n = a.n_spans;
+    const int kk = a.kk;
+    if (kk == 0 || kk >= n) {
+        // nothing to rank (k_certify_head writes the selection)
+        if (tid == 0) {
+            a.gncand[bh] = 0;
+            a.gover[bh] = 0;
+        }
+        return;
+    }
+    const double *shat = a.shat + bh * n;
+    const double *kbar = a.kbar + (int64_t)h * n;
+
+    // range of the scores, largest key norm
+    double mn = INFINITY, mx = -INFINITY, km = 0.0;
+    for (int64_t j = tid; j < n; j += kPThreads) {
+        const double x = shat[j];
+        mn = fmin(mn, x);
+        mx = fmax(mx, x);
+        km = fmax(km, kbar[j]);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fmin(mn, __shfl_xor(mn, o));
+        mx = fmax(mx, __shfl_xor(mx, o));
+        km = fmax(km, __shfl_xor(km, o));
+    }
+    if (lane == 0) {
+        red[0][wave] = mn;
+        red[1][wave] = mx;
+        red[2][wave] = km;
+    }
+    __syncthreads();
+    mn = INFINITY;
+    mx = -INFINITY;
+    km = 0.0;
+    for (int w = 0; w < kPWaves; ++w) {
+        mn = fmin(mn, red[0][w]);
+        mx = fmax(mx, red[1][w]);
+        km = fmax(km, red[2][w]);
+    }
+    if (mn == mx) {
+        // every span scores the same: all of them would be ranked
+        if (tid == 0) {
+            a.gncand[bh] = 0;
+            a.gover[bh] = 1;
+        }
+        return;
+    }
+    // cert_eps grows with the key norm and with |score|
+    const double eps_max = cert_eps(a.E[bh], km, fmax(fabs(mn), fabs(mx)));
+    const double inv = (double)kCBins / (mx - mn);
+
+    // histogram, and the bin b* holding the (kk+1)-th largest score
+    for (int i = tid; i < kCBins; i += kPThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int64_t j = tid; j < n; j += kPThreads) atomicAdd(&hist[c_bin(shat[j], mn, inv)], 1u);
+    __syncthreads();
+    if (wave == 0) {
+        constexpr int bpl = kCBins / 64;
+        const int64_t need = (int64_t)kk + 1;
+        uint32_t own = 0;
+        for (int i = 0; i < bpl; ++i) own += hist[lane * bpl + i];
+        uint32_t suf = own;                       // count in bins >= lane * bpl
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_down(suf, o);
+            if (lane + o < 64) suf += y;
+        }
+        const uint32_t after = suf - own;         // count in bins above this lane's
+        if ((int64_t)after < need && need <= (int64_t)suf) {
+            uint32_t above = after;
+            int bb = lane * bpl + bpl - 1;
+            for (; bb > lane * bpl; --bb) {
+                if ((int64_t)(above + hist[bb]) >= need) break;
+                above += hist[bb];
+            }
+            s_bstar = bb;
+        }
+    }
+    __syncthreads();
+    const int bstar = s_bstar;
+
+    // m*: the smallest score in bin b*
+    double mb = INFINITY;
+    for (int64_t j = tid; j < n; j += kPThreads) {
+        const double x = shat[j];
+        if (c_bin(x, mn, inv) == bstar) mb = fmin(mb, x);
+    }
+    for (int o = 32; o > 0; o >>= 1) mb = fmin(mb, __shfl_xor(mb, o));
+    __syncthreads();
+    if (lane == 0) red[0][wave] = mb;
+    __syncthreads();
+    mb = INFINITY;
+    for (int w = 0; w < kPWaves; ++w) mb = fmin(mb, red[0][w]);
+    // theta = m* - 2 eps_max, lowered past the subtraction's rounding
+    double theta = mb - 2.0 * eps_max;
+    theta -= 4e-16 * fabs(theta) + 1e-300;
+
+    // the spans scoring >= theta, in ascending order
+    int32_t *cand = a.gcand + bh * kCCap;
+    uint32_t total = 0;
+    for (int64_t base = 0; base < n; base += kPThreads) {
+        const int64_t j = base + tid;
+        const bool keep = j < n && shat[j] >= theta;
+        const uint64_t bal = __ballot(keep);
+        const uint32_t before = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t off = 0, tot = 0;
+        for (int w = 0; w < kPWaves; ++w) {
+            const uint32_t c = wsum[w];
+            off += w < wave ? c : 0u;
+            tot += c;
+        }
+        const uint32_t pos = total + off + before;
+        if (keep && pos < (uint32_t)kCCap) cand[pos] = (int32_t)j;
+        total += tot;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const bool over = total > (uint32_t)kCCap;
+        a.gncand[bh] = over ? 0u : total;
+        a.gover[bh] = over ? 1u : 0u;
     }
 }
 
@@ -939,12 +1120,17 @@ __global__ __launch_bounds__(kCThreads) void k_certify_head(CertArgs a) {
     const int64_t bh = blockIdx.x;
     uint32_t *cnt = a.gcnt + bh * 4;
     uint32_t nx, nd;
+    if (a.gover && a.gover[bh]) {
+        // too many candidates: the exact fallback selects this pair
+        if (threadIdx.x == 0) cnt[2] = 1u;
+        return;
+    }
     if (!cert_classify(a, sh, bh, nx, nd)) {
         if (threadIdx.x == 0) cnt[2] = 1u;
         return;
     }
     for (uint32_t i = threadIdx.x; i < nx; i += kCThreads) a.gxs[bh * kCCap + i] = sh.xs[i];
-    const int nwords = (int)((a.n_spans + 31) / 32);
+    const int nwords = (int)((ranked(a, bh) + 31) / 32);
     for (int i = threadIdx.x; i < nwords; i += kCThreads) a.gbits[bh * (kCCap / 32) + i] = sh.bitmap[i];
     if (threadIdx.x == 0) {
         cnt[0] = nx;
@@ -989,7 +1175,7 @@ __global__ __launch_bounds__(kCThreads) void k_certify_tail(CertArgs a) {
     if (cnt[2]) return;
     const uint32_t nx = cnt[0], nd = cnt[1];
     const int64_t need = (int64_t)a.kk - nd;
-    const int nwords = (int)((a.n_spans + 31) / 32);
+    const int nwords = (int)((ranked(a, bh) + 31) / 32);
     for (int i = threadIdx.x; i < nwords; i += kCThreads) sh.bitmap[i] = a.gbits[bh * (kCCap / 32) + i];
     if (need > 0) {
         for (uint32_t i = threadIdx.x; i < nx; i += kCThreads) sh.xs[i] = a.gxs[bh * kCCap + i];
@@ -1003,8 +1189,7 @@ __global__ __launch_bounds__(kCThreads) void k_certify_tail(CertArgs a) {
 }  // namespace
 
 bool mfma_block_path(const Geom &g) {
-    return g.dtype == 0 && g.d == kD && g.block_q == kQB && g.S % kTile == 0 && g.n_spans > 0 &&
-           g.n_spans <= kCCap;
+    return g.dtype == 0 && g.d == kD && g.block_q == kQB && g.S % kTile == 0 && g.n_spans > 0;
 }
 
 // Workgroups that re-score one (block, KV head) pair's uncertain spans: an
@@ -1024,13 +1209,24 @@ size_t cert_split_bytes(const Geom &g) {
            al(pairs * 4 * sizeof(uint32_t)) + al(pairs * 2 * kCCap * sizeof(double));
 }
 
+// More spans than the certification ranks on chip: candidate lists, their
+// counts, the overflow flags and the exact fallback's group maxima.
+size_t cert_many_bytes(const Geom &g) {
+    if (g.n_spans <= kCCap) return 0;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t pairs = (size_t)g.n_blk * g.Hkv;
+    return al(pairs * kCCap * sizeof(int32_t)) + 2 * al(pairs * sizeof(uint32_t)) +
+           al(pairs * (size_t)score_groups(g) * sizeof(double));
+}
+
 size_t mfma_ws_bytes(const Geom &g) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return al((size_t)g.Hkv * g.n_q * 256 * sizeof(uint16_t)) +       // [hi|lo]
            al((size_t)g.Hkv * g.n_q * kD * sizeof(double)) +           // q_eff
            al((size_t)g.n_blk * g.Hkv * sizeof(double)) +              // E
            al((size_t)g.Hkv * g.n_spans * sizeof(double)) +            // key-norm maxima
-           cert_split_bytes(g);                                        // certification state
+           cert_split_bytes(g) +                                       // certification state
+           cert_many_bytes(g);                                         // candidates, fallback
 }
 
 hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
@@ -1108,11 +1304,38 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     ca.gcnt = (uint32_t *)p;
     p += al((size_t)pairs * 4 * sizeof(uint32_t));
     ca.gpart = (double *)p;
+    p += al((size_t)pairs * 2 * kCCap * sizeof(double));
+    const bool many = g.n_spans > kCCap;
+    double *fb_gmax = nullptr;
+    ca.gcand = nullptr;
+    ca.gncand = nullptr;
+    ca.gover = nullptr;
+    if (many) {
+        ca.gcand = (int32_t *)p;
+        p += al((size_t)pairs * kCCap * sizeof(int32_t));
+        ca.gncand = (uint32_t *)p;
+        p += al((size_t)pairs * sizeof(uint32_t));
+        ca.gover = (uint32_t *)p;
+        p += al((size_t)pairs * sizeof(uint32_t));
+        fb_gmax = (double *)p;
+        if ((e = launch_struct(k_cert_candidates, dim3(pairs), dim3(kPThreads), 0, s, ca)) !=
+            hipSuccess)
+            return e;
+    }
     if ((e = launch_struct(k_certify_head, dim3(pairs), dim3(kCThreads), 0, s, ca)) != hipSuccess)
         return e;
     if ((e = launch_struct(k_rescore, dim3(pairs * ca.R), dim3(kRThreads), 0, s, ca)) != hipSuccess)
         return e;
-    return launch_struct(k_certify_tail, dim3(pairs), dim3(kCThreads), 0, s, ca);
+    if ((e = launch_struct(k_certify_tail, dim3(pairs), dim3(kCThreads), 0, s, ca)) != hipSuccess)
+        return e;
+    if (!many) return hipSuccess;
+    // pairs flagged in gover: exact fp64 span scores on the VALU (overwriting
+    // their approximations) and the ordinary top-k; the other pairs' workgroups
+    // return at once
+    if ((e = launch_score(g, q, k, span_scores, fb_gmax, num_cu, s, nullptr, nullptr, ca.gover)) !=
+        hipSuccess)
+        return e;
+    return launch_topk(g, span_scores, fb_gmax, sel, n_sel, s, ca.gover);
 }
 
 }  // namespace rea

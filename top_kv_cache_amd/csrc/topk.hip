@@ -735,6 +735,8 @@ struct TopkArgs {
     const int64_t *lens;
     int hps;
     int64_t T, G, L;
+    // null, or one flag per (block, head): only the flagged pairs are selected
+    const uint32_t *only;
 };
 
 __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
@@ -746,6 +748,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
     } u;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t bh = blockIdx.x;
+    if (ta.only && !ta.only[bh]) return;
     const int h = (int)(bh % ta.Hkv);
     int64_t T = ta.T;
     if (ta.lens) {
@@ -1068,9 +1071,10 @@ hipError_t launch_widen(const Geom &g, const int32_t *sel_tok, const int32_t *ns
 }
 
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
-                       int32_t *sel, int32_t *n_sel, hipStream_t s) {
+                       int32_t *sel, int32_t *n_sel, hipStream_t s, const uint32_t *only) {
     const int nbh = g.n_blk * g.Hkv;
     TopkArgs ta;
+    ta.only = only;
     ta.scores = span_scores;
     ta.gmax = group_max;
     ta.sel = sel;
