@@ -29,7 +29,9 @@
  * Conventions
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *     allocates nothing and keeps no state between calls (apart from a
- *     thread-local error string).  Calls are re-entrant.
+ *     thread-local error string).  Calls are re-entrant.  The one exception
+ *     is rea_decode_step_noalloc, which works in a fixed scratch array that
+ *     the library holds on each device (see there).
  *   - All argument validation happens on the host before any HIP call, so
  *     every error status below is reachable on a machine without a GPU.
  *   - Kernels are enqueued asynchronously on the caller's stream (a
@@ -274,6 +276,26 @@ rea_status rea_decode_step_timed(const rea_problem *p, const rea_params *a, floa
                                  void *ws, size_t ws_bytes, void *stream,
                                  const rea_timing *timing);
 
+/*
+ * rea_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same kernels run on a fixed scratch
+ * array of REA_NOALLOC_SCRATCH_BYTES that the library holds on every device it
+ * is loaded on, until the process ends; the call itself allocates nothing.
+ * The caller still passes q, K/V (in p), out and the optional sel / n_sel.
+ *
+ * Limit: problems whose sizes.ws_decode_step exceeds REA_NOALLOC_SCRATCH_BYTES
+ * are rejected with REA_EWORKSPACE before any HIP call (16 MiB covers decode
+ * steps with one selection per KV or query head up to 4M tokens of context;
+ * token-level selection and large prefill chunks need rea_decode_step).
+ * All calls on one device share its array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * device, on different streams or from different threads, race and must be
+ * serialised by the caller.
+ */
+#define REA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+rea_status rea_decode_step_noalloc(const rea_problem *p, const rea_params *a, float *out,
+                                   int32_t *sel, int32_t *n_sel, void *stream);
 
 /*
  * Chunked prefill of a whole prompt (OpenReview discussion, "Prefilling

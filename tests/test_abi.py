@@ -252,3 +252,30 @@ def test_workspace_bytes_covers_every_entry_point(cfg):
         s = rea.query_sizes(p, a)
         n = rea.workspace_bytes(p, a)
         assert n == max(s.ws_score_select, s.ws_window_attend, s.ws_decode_step) > 0
+
+
+def test_noalloc_validates_on_the_host():
+    """rea_decode_step_noalloc runs rea_decode_step's checks before any HIP
+    call, and rejects steps whose workspace exceeds its fixed scratch array."""
+    L = rea.lib()
+    E = rea.STATUS.index
+    p, a = good()
+    assert rea.query_sizes(p, a).ws_decode_step <= rea.NOALLOC_SCRATCH_BYTES
+    assert L.rea_decode_step_noalloc(ctypes.byref(p), ctypes.byref(a), None, None, None,
+                                     None) == E("REA_EINVAL")
+    assert L.rea_decode_step_noalloc(ctypes.byref(p), ctypes.byref(a), FAKE + 4, None, None,
+                                     None) == E("REA_EALIGN")
+    bad, a2 = mutate(S=0)
+    assert L.rea_decode_step_noalloc(ctypes.byref(bad), ctypes.byref(a2), FAKE, None, None,
+                                     None) == E("REA_EINVAL")
+    big = rea.params(32, 1, 3840, 4096, 1)             # token level at 131072: ~9.6 MB, fits
+    assert rea.query_sizes(p, big).ws_decode_step <= rea.NOALLOC_SCRATCH_BYTES
+    p1m, _ = good(T=1 << 20)                           # token level at 1M: ~70 MB, does not
+    assert rea.query_sizes(p1m, big).ws_decode_step > rea.NOALLOC_SCRATCH_BYTES
+    assert L.rea_decode_step_noalloc(ctypes.byref(p1m), ctypes.byref(big), FAKE, None, None,
+                                     None) == E("REA_EWORKSPACE")
+    assert "scratch" in L.rea_last_error().decode()
+    import torch
+    if not torch.cuda.is_available():
+        assert L.rea_decode_step_noalloc(ctypes.byref(p), ctypes.byref(a), FAKE, None, None,
+                                         None) == E("REA_ENODEVICE")

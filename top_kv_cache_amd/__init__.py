@@ -22,8 +22,9 @@ ENTRY_POINTS = ["rea_abi_version", "rea_status_string", "rea_last_error", "rea_q
                 "rea_workspace_bytes", "rea_score_select", "rea_gather_rope",
                 "rea_window_attend", "rea_decode_step", "rea_decode_step_timed",
                 "rea_prefill_plan", "rea_prefill", "rea_decode_batch_workspace",
-                "rea_decode_batch"]
+                "rea_decode_batch", "rea_decode_step_noalloc"]
 ABI_VERSION = 4
+NOALLOC_SCRATCH_BYTES = 16 << 20          # REA_NOALLOC_SCRATCH_BYTES
 WORKSPACE_INVALID = ctypes.c_size_t(-1).value     # rea_workspace_bytes on invalid arguments
 
 
@@ -100,6 +101,8 @@ def lib():
     L.rea_decode_step_timed.restype = ctypes.c_int
     L.rea_decode_step_timed.argtypes = [P, A, vp, i32p, i32p, vp, ctypes.c_size_t, vp,
                                         ctypes.POINTER(Timing)]
+    L.rea_decode_step_noalloc.restype = ctypes.c_int
+    L.rea_decode_step_noalloc.argtypes = [P, A, vp, i32p, i32p, vp]
     L.rea_prefill_plan.restype = ctypes.c_int
     L.rea_prefill_plan.argtypes = [P, A, ctypes.c_int32, ctypes.POINTER(Chunk), ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
@@ -302,6 +305,17 @@ class Step:
                                                ctypes.byref(timing)))
         return out
 
+
+    def decode_step_noalloc(self, out=None, sel=None, nsel=None, stream=None):
+        """rea_decode_step_noalloc: the decode step on the library's fixed
+        scratch array (no workspace)."""
+        torch = _torch()
+        n_q, Hq, Hkv, d = self.shape
+        if out is None:
+            out = torch.empty((n_q, Hq, d), dtype=torch.float32, device=self.device)
+        _check(lib().rea_decode_step_noalloc(ctypes.byref(self.prob), ctypes.byref(self.par),
+                                             _ptr(out), _ptr(sel), _ptr(nsel), _stream(stream)))
+        return out
 
 
 class Prefill:

@@ -468,6 +468,29 @@ rea_status rea_decode_step_timed(const rea_problem *p, const rea_params *a, floa
 
 }  // extern "C"
 
+// ---- hooks for entry points defined in other translation units --------------
+
+namespace rea {
+
+void api_clear_error() { g_err[0] = 0; }
+
+rea_status api_error(rea_status st, const char *msg) { return fail(st, "%s", msg); }
+
+rea_status decode_check(const rea_problem *p, const rea_params *a, const float *out,
+                        const int32_t *sel, const int32_t *n_sel, size_t *ws_bytes) {
+    Geom g;
+    rea_status st = decode_args(p, a, out, sel, n_sel, &g);
+    if (st != REA_OK) return st;
+    *ws_bytes = decode_ws_bytes(g);
+    return REA_OK;
+}
+
+rea_status decode_step_ws(const rea_problem *p, const rea_params *a, float *out, int32_t *sel,
+                          int32_t *n_sel, void *ws, size_t ws_bytes, void *stream) {
+    return decode_step(p, a, out, sel, n_sel, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+}  // namespace rea
 
 // ---- chunked prefill ------------------------------------------------------
 

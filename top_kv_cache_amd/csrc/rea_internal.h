@@ -6,6 +6,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include "rea.h"
+
 namespace rea {
 
 // Validated geometry of one call (all values derived on the host).
@@ -167,5 +169,18 @@ size_t attend_ws_bytes(const Geom &g, int64_t W_cap);
 hipError_t launch_attend(const Geom &g, const float *q_rot, const float *k_win,
                          const void *v_win, const int32_t *W, int64_t W_cap, float *out,
                          void *ws, hipStream_t s);
+
+// ---- host entry-point hooks (rea_api.cpp) --------------------------------
+
+// Clear / set the calling thread's error detail (rea_last_error).
+void api_clear_error();
+rea_status api_error(rea_status st, const char *msg);
+// rea_decode_step's host checks of everything but the workspace, and the
+// workspace bytes the step needs.  No HIP call.
+rea_status decode_check(const rea_problem *p, const rea_params *a, const float *out,
+                        const int32_t *sel, const int32_t *n_sel, size_t *ws_bytes);
+// rea_decode_step on a given workspace (does not clear the error detail).
+rea_status decode_step_ws(const rea_problem *p, const rea_params *a, float *out, int32_t *sel,
+                          int32_t *n_sel, void *ws, size_t ws_bytes, void *stream);
 
 }  // namespace rea
