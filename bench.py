@@ -279,6 +279,48 @@ def batch_main(args):
         "roofline": None, "cpu_baseline": None}), flush=True)
 
 
+def read_ceiling_main(args):
+    """HBM read ceiling: rea_probe_stream_read (the scoring kernel's load
+    instruction and nothing else) over a 2 GiB buffer, for 1-8 workgroups per
+    CU and 4-16 loads in flight per wave; every shape timed with HIP events
+    on the launch stream over args.steps launches after args.warmup.  One
+    JSON line with the best rate and the table."""
+    import torch
+    import top_kv_cache_amd as rea
+
+    dev = torch.device("cuda:0")
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    cu = rea.lib().rea_probe_cu_count()
+    sink = torch.empty(16 * cu, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    table = []
+    for wpc in (1, 2, 4, 8):
+        for lif in (4, 8, 16):
+            for _ in range(args.warmup):
+                rea.probe_stream_read(buf, wpc, lif, sink, stream)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                rea.probe_stream_read(buf, wpc, lif, sink, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps
+            gbs = nbytes / (us * 1e-6) / 1e9
+            table.append({"wg_per_cu": wpc, "loads_in_flight": lif, "us": us, "GBps": gbs})
+            log(f"[bench] read {nbytes >> 20} MiB, {wpc} workgroups/CU, {lif} loads in flight: "
+                f"{us:.1f} us = {gbs:.0f} GB/s")
+    best = max(table, key=lambda r: r["GBps"])
+    print(json.dumps({
+        "metric": "HBM streaming read ceiling (non-temporal 16-byte loads, 1 KB per wave "
+                  "instruction)", "value": best["GBps"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "dtype": "u32", "data": "synthetic", "peak": HBM_PEAK_GBS,
+        "frac": best["GBps"] / HBM_PEAK_GBS, "bytes": nbytes, "best": best, "table": table,
+        "config": {"workload": "stream-read-2GiB", "cu": cu}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,6 +341,12 @@ def main():
     ap.add_argument("--context", type=int, default=32768, help="sequence length (with --batch)")
     ap.add_argument("--ragged", action="store_true",
                     help="with --batch: lengths spread over [context/2, context]")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="instead: the HBM read ceiling of the scoring kernel's load pattern")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="with --config: context before the queries (T = tokens + queries)")
+    ap.add_argument("--queries", type=int, default=0,
+                    help="with --config: number of queries (a prefill chunk when > 1)")
     ap.add_argument("--variant", choices=sorted(VARIANTS), default=None,
                     help="selection variant of the workload (default: one selection per KV "
                          "head over spans of S tokens)")
@@ -314,12 +362,15 @@ def main():
             sys.exit(1)
         batch_main(args)
         return
-    if args.prefill_prompt > 0:
+    if args.prefill_prompt > 0 or args.read_ceiling:
         import torch
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(1)
-        prefill_main(args)
+        if args.read_ceiling:
+            read_ceiling_main(args)
+        else:
+            prefill_main(args)
         return
 
     import torch
@@ -335,6 +386,13 @@ def main():
     if args.variant:
         w = dataclasses.replace(w, **VARIANTS[args.variant])
         w.name = f"{w.name}-{args.variant.replace('_', '-')}"
+    if args.tokens or args.queries:
+        nq = args.queries or w.n_q
+        base = args.tokens or (w.T - w.n_q)
+        bq = w.block_q if nq % w.block_q == 0 else 1
+        w = dataclasses.replace(w, T=base + nq, n_q=nq, block_q=bq)
+        w.name = (f"{w.name.split('-')[0]}-{w.dtype}-" +
+                  (f"prefill-chunk{nq}-at-{base}" if nq > 1 else f"decode-at-{base}"))
     n_layers = args.layers or w.n_layers
     dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: {n_layers} layers, T={w.T}, Hq={w.Hq}, Hkv={w.Hkv}, "

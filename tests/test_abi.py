@@ -13,10 +13,26 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 0x10000          # an aligned non-null address; nothing is launched
 
 
-def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "rea.h")).read()
+def declared_symbols(header="rea.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(rea_[a-z_]+)\s*\(", text)))
+
+
+def test_every_header_is_checked():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["rea.h", "rea_probe.h"]
+
+
+def test_exports_the_probe():
+    L = rea.lib()
+    syms = declared_symbols("rea_probe.h")
+    assert syms == sorted(rea.PROBE_ENTRY_POINTS)
+    for s in syms:
+        assert hasattr(L, s), s
+    # invalid arguments are refused before any launch
+    assert L.rea_probe_stream_read(None, 1024, 2, 8, FAKE, None) == 1
+    assert L.rea_probe_stream_read(FAKE, 1000, 2, 8, FAKE, None) == 1
+    assert L.rea_probe_stream_read(FAKE, 1024, 2, 5, FAKE, None) == 1
 
 
 def test_exports_every_declared_symbol():

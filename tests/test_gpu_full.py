@@ -84,6 +84,29 @@ def test_prefill_chunk512_past_4096_spans():
     log(f"  max-abs out err {max(errs):.3e} (tolerance {TOL[w.dtype]})")
 
 
+@pytest.mark.timeout(900)
+def test_prefill_block_at_1m_tokens():
+    """One 64-query block of the 8B shape at 1,048,576 tokens: 32,639 spans per
+    KV head scored on MFMA, the certification ranking only its candidate
+    spans; selection, span-score bounds and outputs of KV heads 0 and 7
+    checked against the oracle."""
+    w = synth.small(name="llama8b-bf16-prefill-block-at-1m", seed=240715185, Hq=32, Hkv=8,
+                    d=128, T=1048576, n_q=64, block_q=64, G=32, S=32, topk=120, L=4096,
+                    needles=8, kv_scaled=True)
+    assert w.n_spans == 32639
+    log(f"[prefill block] {w.name}: {w.n_spans} spans per KV head")
+    q, K, V = device_inputs(w)
+    gpu = run_library(w, q, K, V)
+    del K, V
+    torch.cuda.empty_cache()
+    q64 = synth.to_f32(w.q(0), w.dtype).astype(np.float64)
+    for h in (0, w.Hkv - 1):
+        ora = oracle_head(w, 0, h, q64)
+        err = compare_head(w, gpu, ora, h)
+        log(f"  head {h}: selection exact, worst |s_hat - s| / eps_j {ora['eps_used']:.3g}, "
+            f"out err {err:.2e}")
+
+
 @pytest.mark.timeout(1100)
 def test_decode_1m_32_layers_as_benchmarked():
     w = synth.config(3)

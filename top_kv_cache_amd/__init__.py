@@ -23,6 +23,8 @@ ENTRY_POINTS = ["rea_abi_version", "rea_status_string", "rea_last_error", "rea_q
                 "rea_window_attend", "rea_decode_step", "rea_decode_step_timed",
                 "rea_prefill_plan", "rea_prefill", "rea_decode_batch_workspace",
                 "rea_decode_batch", "rea_decode_step_noalloc"]
+# measurement aid (include/rea_probe.h), not part of the method
+PROBE_ENTRY_POINTS = ["rea_probe_stream_read", "rea_probe_cu_count"]
 ABI_VERSION = 4
 NOALLOC_SCRATCH_BYTES = 16 << 20          # REA_NOALLOC_SCRATCH_BYTES
 WORKSPACE_INVALID = ctypes.c_size_t(-1).value     # rea_workspace_bytes on invalid arguments
@@ -114,6 +116,9 @@ def lib():
     L.rea_decode_batch.restype = ctypes.c_int
     L.rea_decode_batch.argtypes = [P, A, ctypes.c_int32, vp, ctypes.c_int64, vp, i32p, i32p, vp,
                                    ctypes.c_size_t, vp]
+    L.rea_probe_stream_read.restype = ctypes.c_int
+    L.rea_probe_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp, vp]
+    L.rea_probe_cu_count.restype = ctypes.c_int
     if L.rea_abi_version() != ABI_VERSION:
         raise ImportError(f"librea.so ABI version {L.rea_abi_version()} != {ABI_VERSION}: rebuild it")
     _lib = L
@@ -408,3 +413,14 @@ class DecodeBatch:
                                       _ptr(sel), _ptr(nsel), _ptr(ws), ws.numel(),
                                       _stream(stream)))
         return out
+
+
+def probe_stream_read(buf, wg_per_cu, loads_in_flight, sink, stream=None):
+    """rea_probe_stream_read (include/rea_probe.h): stream the bytes of the
+    device tensor `buf` once; sink is an int32 device tensor of at least
+    wg_per_cu * CU-count elements."""
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().rea_probe_stream_read(_ptr(buf), nbytes, wg_per_cu, loads_in_flight, _ptr(sink),
+                                     _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"rea_probe_stream_read failed ({st})")

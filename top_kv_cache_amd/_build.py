@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librea.so")
 
 SOURCES = ["rea_api.cpp", "score.hip", "score_mfma.hip", "topk.hip", "window.hip", "attend.hip", "attend_mfma.hip",
-           "decode_attend.hip", "noalloc.hip"]
+           "decode_attend.hip", "noalloc.hip", "probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -9,23 +9,29 @@
 // "Approach": positions are assigned after the concatenation); query i of a
 // block is rotated to W - n_q + i and sees rows w <= that position.
 //
-//   k_fused_split    one workgroup per (128-row split of the window, KV head,
-//                    block), 4 waves x 32 rows.  One round trip fetches the
-//                    selection slots the split can touch and the raw queries;
-//                    then every row's K and V load is issued at once, and the
-//                    queries are rotated while those are in flight (barriers
-//                    order LDS only).  A 16-lane DPP row of a wave is a stream
-//                    of 8 consecutive window rows; a lane holds D/32 channel
-//                    pairs (c, c + D/2) of its stream's rows.  The rotation
-//                    angle of row w+1 follows from row w's by one complex
-//                    multiplication with (cos, sin) of the channel's frequency
-//                    (fp32 for bf16 inputs, fp64 for fp32 inputs); the rotated
-//                    key is fp32.  Logits are kept in log2 units (the softmax
-//                    scale carries log2 e) so weights are single exp2s.  Per
-//                    stream the 8 logits of each query row give an exact max,
-//                    weights and P.V; the workgroup's 16 streams are merged
-//                    through LDS with the usual (m, l, acc) rule and one
-//                    partial per split is written.
+//   k_fused_split    one workgroup per (run of rows_wg window rows, KV head,
+//                    block), 4 waves.  One round trip fetches the selection
+//                    slots the run can touch and the raw queries; the queries
+//                    are rotated while the first rows load.  The run is taken
+//                    in sub-splits of 64 rows: a 16-lane DPP row of a wave is
+//                    a stream of 4 consecutive rows of each sub-split, and the
+//                    loads of the next sub-split are issued before the current
+//                    one is attended, so a workgroup keeps K/V loads in
+//                    flight for its whole run.  A lane holds D/32 channel
+//                    pairs (c, c + D/2) of its stream's rows.  The rotation of
+//                    a stream's first row comes from rope_cs, the next rows'
+//                    by one complex multiplication with (cos, sin) of the
+//                    channel's frequency (fp32 for bf16 inputs, fp64 for fp32
+//                    inputs); the rotated key is fp32.  Logits are kept in
+//                    log2 units (the softmax scale carries log2 e) so weights
+//                    are single exp2s.  Each stream keeps an online (m, l,
+//                    acc) over its rows; the workgroup's 16 streams are merged
+//                    through LDS and one partial per workgroup is written.
+//                    rows_wg is a multiple of 64 chosen on the host: 128 when
+//                    one row run per workgroup already fills the GPU (a
+//                    single decode: 63 workgroups per KV head at 7968 rows),
+//                    longer for batches, so that the workgroups the registers
+//                    allow per CU (two or three) stream their runs.
 //   k_fused_combine  workgroups per (KV head, block) merge the splits:
 //                    out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s
 //                    (maxima m_s in log2 units).
@@ -39,9 +45,10 @@ namespace rea {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSL = 8;                          // rows per stream
-constexpr int kRowsPerSplit = 4 * 4 * kSL;      // waves x streams x rows
-constexpr int kSelStage = kRowsPerSplit + 2;    // selection slots a split can touch (S = 1)
+constexpr int kSL = 4;                          // rows per stream and sub-split
+constexpr int kSub = 4 * 4 * kSL;               // rows per sub-split: waves x streams x rows
+constexpr int kPartRows = 128;                  // the shortest row run (workspace sizing)
+constexpr int kSelCap = 1024;                   // selection slots a workgroup stages
 constexpr int kCombBatch = 8;                   // partials loaded together by the merge
 
 struct FusedArgs {
@@ -54,6 +61,7 @@ struct FusedArgs {
     int64_t sh, st;         // elements
     int64_t T, Gp, Lp, mid_lo, n_spans;
     int S, last_len, topk, Hkv, Hq, g, n_q, block_q, QR, n_split, rep;
+    int rows_wg;            // window rows per workgroup (multiple of kSub); n_split runs
     int comb_tpi;           // merge phases per item (power of two)
     // batched decode (see Geom): per-sequence lengths and cache offsets
     const int64_t *lens;
@@ -143,14 +151,20 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The K and V rows of one stream in one sub-split.
+template <typename TIn, int PPL> struct RowsKV {
+    Part<TIn, PPL> k1[kSL], k2[kSL], v1[kSL], v2[kSL];
+};
+
 template <typename TIn, int D, int QRM>
 __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     constexpr int HALF = D / 2;
     constexpr int PPL = HALF / 16;              // channel pairs per lane
     constexpr int NA = 2 * PPL;                 // accumulated channels per lane and query row
     constexpr int QPT = (QRM * HALF + kThreads - 1) / kThreads;   // query pairs per thread
+    constexpr int SPT = kSelCap / kThreads;     // selection slots per thread
     __shared__ float qs[QRM][D];
-    __shared__ int32_t ssel[kSelStage];
+    __shared__ int32_t ssel[kSelCap];
     __shared__ double tab[HALF][4];             // theta_c/2pi (hi, lo), cos and sin of theta_c
     __shared__ float sm[16][QRM], sl[16][QRM], sf[16][QRM], smax[QRM];
     __shared__ float sacc[16][QRM][D];
@@ -159,16 +173,23 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * a.Hkv + h;
-    const int64_t w0 = (int64_t)sp * kRowsPerSplit;
+    const int64_t w0 = (int64_t)sp * a.rows_wg;
     const SeqOf so = seq_of(a.lens, h, a.hps, a.rep, a.seq_stride, a.sh, a.T);
     const SeqGeom sg = seq_geom(so.T, a.G, a.L, a.S);
 
-    // One round trip: the selection count, the selection slots this split's
-    // rows can touch, and the raw query elements (all loads before any store).
+    // One round trip: the selection count, the selection slots this run's
+    // rows can touch (row w >= G' lies in slot (w - G') / S; the host keeps
+    // rows_wg / S + 2 <= kSelCap), and the raw query elements.
     const int ns = a.n_sel[bh];
     const int64_t slot0 = w0 > sg.Gp ? (w0 - sg.Gp) / a.S : 0;
-    int32_t sv = 0;
-    if (a.topk > 0 && tid < kSelStage && slot0 + tid < a.topk) sv = a.sel[bh * a.topk + slot0 + tid];
+    int64_t nslot = (int64_t)a.rows_wg / a.S + 2;
+    if (nslot > (int64_t)a.topk - slot0) nslot = (int64_t)a.topk - slot0;
+    int32_t sv[SPT];
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int idx = tid + u * kThreads;
+        sv[u] = idx < nslot ? a.sel[bh * a.topk + slot0 + idx] : 0;
+    }
     float qx1[QPT], qx2[QPT];
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
@@ -193,7 +214,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
         scs = a.step_c[tid];
         ssn = a.step_s[tid];
     }
-    if (tid < kSelStage) ssel[tid] = sv;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) ssel[tid + u * kThreads] = sv[u];
     if (tid < HALF) {
         tab[tid][0] = fh;
         tab[tid][1] = fl;
@@ -208,16 +230,18 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     const int64_t Wbh = sg.Gp + sel_len + sg.Lp;
     __syncthreads();
 
-    // this stream's rows: source token and K, V.  Rows past the window load
-    // token 0 (finite data whose logits are masked and weights are 0), so every
-    // load is unconditional and all of them are in flight together.
-    // (oq, orr) = (slot, offset) of window row max(w, G') within the selected spans.
+    // this run's rows [w0, wend) in sub-splits of kSub; rows past the window
+    // are skipped, and within the last sub-split they load token 0 (finite
+    // data whose logits are masked and weights are 0)
+    const int64_t wend = w0 + a.rows_wg < Wbh ? w0 + a.rows_wg : Wbh;
+    const int nsub = wend > w0 ? (int)((wend - w0 + kSub - 1) / kSub) : 0;
     const int rho = lane >> 4, c0 = (lane & 15) * PPL;
-    const int64_t wf = w0 + wave * (4 * kSL) + rho * kSL;
-    Part<TIn, PPL> k1[kSL], k2[kSL], v1[kSL], v2[kSL];
-    {
-        const TIn *kb = (const TIn *)a.k + so.kv_off;
-        const TIn *vb = (const TIn *)a.v + so.kv_off;
+    const int soff = wave * (4 * kSL) + rho * kSL;      // the stream's first row in a sub-split
+    const TIn *kb = (const TIn *)a.k + so.kv_off;
+    const TIn *vb = (const TIn *)a.v + so.kv_off;
+
+    auto issue = [&](int sub, RowsKV<TIn, PPL> &rk) {
+        const int64_t wf = w0 + (int64_t)sub * kSub + soff;
         const int64_t o0 = wf - sg.Gp;
         const uint32_t oc = (uint32_t)(o0 > 0 ? o0 : 0);
         int oq = (int)(oc / (uint32_t)a.S), orr = (int)(oc - (uint32_t)oq * (uint32_t)a.S);
@@ -234,16 +258,19 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
                     src = sg.T - sg.Lp + (o - sel_len);
             }
             const int64_t row = src * a.st;
-            k1[i].load(kb + row + c0);
-            k2[i].load(kb + row + c0 + HALF);
-            v1[i].load(vb + row + c0);
-            v2[i].load(vb + row + c0 + HALF);
+            rk.k1[i].load(kb + row + c0);
+            rk.k2[i].load(kb + row + c0 + HALF);
+            rk.v1[i].load(vb + row + c0);
+            rk.v2[i].load(vb + row + c0 + HALF);
             if (o >= 0 && ++orr == a.S) {
                 orr = 0;
                 ++oq;
             }
         }
-    }
+    };
+
+    RowsKV<TIn, PPL> ra, rb;
+    if (nsub > 0) issue(0, ra);
 
     // while they load: the query rows r = (query r / g, head h*g + r % g)
     // rotated to their positions and rounded to fp32
@@ -273,78 +300,107 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
             q1[r][p] = qs[r][c0 + p];
             q2[r][p] = qs[r][c0 + p + HALF];
         }
-    // rotation of the stream's first row, and the per-row step.  bf16 inputs
-    // step in fp32 (7 steps add a few fp32 ulps), fp32 inputs in fp64.
-    RT cs[PPL], sn[PPL], cst[PPL], snt[PPL];
+    RT cst[PPL], snt[PPL];
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
-        float c1, s1;
-        rope_cs(wf, tab[c0 + p][0], tab[c0 + p][1], c1, s1);
-        cs[p] = c1;
-        sn[p] = s1;
         cst[p] = (RT)tab[c0 + p][2];
         snt[p] = (RT)tab[c0 + p][3];
     }
 
-    // logits of the stream's rows, in log2 units (the scale carries log2 e)
-    const int wfi = (int)wf, Wi = (int)Wbh;
-    float lg[kSL][QRM];
-#pragma unroll
-    for (int i = 0; i < kSL; ++i) {
-        float x1[PPL], x2[PPL];
-        k1[i].get(x1);
-        k2[i].get(x2);
-        float y1[PPL], y2[PPL];
-#pragma unroll
-        for (int p = 0; p < PPL; ++p) {
-            const float c = (float)cs[p], s = (float)sn[p];
-            y1[p] = x1[p] * c - x2[p] * s;
-            y2[p] = x2[p] * c + x1[p] * s;
-            const RT cn = cs[p] * cst[p] - sn[p] * snt[p];
-            sn[p] = sn[p] * cst[p] + cs[p] * snt[p];
-            cs[p] = cn;
-        }
-#pragma unroll
-        for (int r = 0; r < QRM; ++r) {
-            float d = 0.f;
-#pragma unroll
-            for (int p = 0; p < PPL; ++p) {
-                d = fmaf(q1[r][p], y1[p], d);
-                d = fmaf(q2[r][p], y2[p], d);
-            }
-            d = row_sum16f(d) * a.scale_log2;
-            const int pos = Wi - a.n_q + b * a.block_q + r / a.g;
-            lg[i][r] = (wfi + i < Wi && wfi + i <= pos && r < a.QR) ? d : -INFINITY;
-        }
-    }
-
-    // exact softmax statistics of the stream, then P.V
+    // the stream's running softmax state over its rows
     float m[QRM], l[QRM], acc[QRM][NA];
 #pragma unroll
     for (int r = 0; r < QRM; ++r) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < kSL; ++i) mx = fmaxf(mx, lg[i][r]);
-        m[r] = mx;
+        m[r] = -INFINITY;
         l[r] = 0.f;
 #pragma unroll
         for (int e = 0; e < NA; ++e) acc[r][e] = 0.f;
     }
+    const int Wi = (int)Wbh;
+
+    auto consume = [&](int sub, const RowsKV<TIn, PPL> &rk) {
+        const int64_t wf = w0 + (int64_t)sub * kSub + soff;
+        const int wfi = (int)wf;
+        // rotation of the stream's first row, then one step per row (bf16
+        // inputs step in fp32: 3 steps add a few fp32 ulps; fp32 inputs in fp64)
+        RT cs[PPL], sn[PPL];
 #pragma unroll
-    for (int i = 0; i < kSL; ++i) {
-        float x1[PPL], x2[PPL];
-        v1[i].get(x1);
-        v2[i].get(x2);
+        for (int p = 0; p < PPL; ++p) {
+            float c1, s1;
+            rope_cs(wf, tab[c0 + p][0], tab[c0 + p][1], c1, s1);
+            cs[p] = c1;
+            sn[p] = s1;
+        }
+        // logits of the rows, in log2 units (the scale carries log2 e)
+        float lg[kSL][QRM];
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) {
+            float x1[PPL], x2[PPL];
+            rk.k1[i].get(x1);
+            rk.k2[i].get(x2);
+            float y1[PPL], y2[PPL];
+#pragma unroll
+            for (int p = 0; p < PPL; ++p) {
+                const float c = (float)cs[p], s = (float)sn[p];
+                y1[p] = x1[p] * c - x2[p] * s;
+                y2[p] = x2[p] * c + x1[p] * s;
+                const RT cn = cs[p] * cst[p] - sn[p] * snt[p];
+                sn[p] = sn[p] * cst[p] + cs[p] * snt[p];
+                cs[p] = cn;
+            }
+#pragma unroll
+            for (int r = 0; r < QRM; ++r) {
+                float d = 0.f;
+#pragma unroll
+                for (int p = 0; p < PPL; ++p) {
+                    d = fmaf(q1[r][p], y1[p], d);
+                    d = fmaf(q2[r][p], y2[p], d);
+                }
+                d = row_sum16f(d) * a.scale_log2;
+                const int pos = Wi - a.n_q + b * a.block_q + r / a.g;
+                lg[i][r] = (wfi + i < Wi && wfi + i <= pos && r < a.QR) ? d : -INFINITY;
+            }
+        }
+        // online softmax: rescale the state to the new maximum, add the rows
 #pragma unroll
         for (int r = 0; r < QRM; ++r) {
-            // exp2(-inf) = 0 covers masked rows; m = -inf only when all 8 are masked
-            const float p = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[i][r] - m[r]);
-            l[r] += p;
+            float mx = m[r];
 #pragma unroll
-            for (int e = 0; e < PPL; ++e) {
-                acc[r][e] = fmaf(p, x1[e], acc[r][e]);
-                acc[r][PPL + e] = fmaf(p, x2[e], acc[r][PPL + e]);
+            for (int i = 0; i < kSL; ++i) mx = fmaxf(mx, lg[i][r]);
+            if (mx == -INFINITY) continue;          // every row so far masked
+            const float f = __builtin_amdgcn_exp2f(m[r] - mx);   // 0 when m was -inf
+            l[r] *= f;
+#pragma unroll
+            for (int e = 0; e < NA; ++e) acc[r][e] *= f;
+            m[r] = mx;
+        }
+#pragma unroll
+        for (int i = 0; i < kSL; ++i) {
+            float x1[PPL], x2[PPL];
+            rk.v1[i].get(x1);
+            rk.v2[i].get(x2);
+#pragma unroll
+            for (int r = 0; r < QRM; ++r) {
+                // exp2(-inf) = 0 covers masked rows
+                const float p = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[i][r] - m[r]);
+                l[r] += p;
+#pragma unroll
+                for (int e = 0; e < PPL; ++e) {
+                    acc[r][e] = fmaf(p, x1[e], acc[r][e]);
+                    acc[r][PPL + e] = fmaf(p, x2[e], acc[r][PPL + e]);
+                }
             }
+        }
+    };
+
+    // two sub-splits in flight: the next one's loads are issued before the
+    // current one is attended
+    for (int sub = 0; sub < nsub; sub += 2) {
+        if (sub + 1 < nsub) issue(sub + 1, rb);
+        consume(sub, ra);
+        if (sub + 1 < nsub) {
+            if (sub + 2 < nsub) issue(sub + 2, ra);
+            consume(sub + 1, rb);
         }
     }
 
@@ -481,21 +537,38 @@ hipError_t launch_qr(const Geom &g, const FusedArgs &a, hipStream_t s) {
     return a.QR <= 4 ? launch_typed<TIn, D, 4>(g, a, s) : launch_typed<TIn, D, 8>(g, a, s);
 }
 
-int fused_n_split(int64_t W_cap) { return (int)((W_cap + kRowsPerSplit - 1) / kRowsPerSplit); }
+// Partials the workspace holds per (block, KV head): runs of the shortest
+// length.
+int fused_max_parts(int64_t W_cap) { return (int)((W_cap + kPartRows - 1) / kPartRows); }
+
+// Window rows per workgroup: 128, or longer when (block, head) units are many,
+// so that about `per_cu` workgroups per CU stream their runs; at most the
+// rows whose selection slots fit kSelCap.
+int fused_rows_wg(const Geom &g, int num_cu, int per_cu) {
+    const int64_t units = (int64_t)g.n_blk * g.Hkv;
+    const int64_t target = (int64_t)(num_cu > 0 ? num_cu : 256) * per_cu;
+    int64_t rows = (g.W_cap * units + target - 1) / target;
+    rows = (rows + kSub - 1) / kSub * kSub;
+    if (rows < kPartRows) rows = kPartRows;
+    const int64_t cap = (int64_t)(kSelCap - 2) * g.S / kSub * kSub;
+    if (rows > cap) rows = cap;
+    if (rows < kSub) rows = kSub;
+    return (int)rows;
+}
 
 }  // namespace
 
 bool fused_decode_path(const Geom &g) { return g.block_q * g.g <= 8 && !mfma_block_path(g); }
 
 size_t fused_ws_bytes(const Geom &g) {
-    const size_t rows = (size_t)g.n_blk * g.Hkv * fused_n_split(g.W_cap) * (size_t)(g.block_q * g.g);
+    const size_t rows = (size_t)g.n_blk * g.Hkv * fused_max_parts(g.W_cap) * (size_t)(g.block_q * g.g);
     return ((rows * g.d * sizeof(float) + 255) & ~(size_t)255) +
            ((rows * 2 * sizeof(float) + 255) & ~(size_t)255);
 }
 
 hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, const void *q,
                                const int32_t *sel, const int32_t *n_sel, float *out, void *ws,
-                               hipStream_t s) {
+                               int num_cu, hipStream_t s) {
     FusedArgs a;
     a.k = (const unsigned char *)k;
     a.v = (const unsigned char *)v;
@@ -525,7 +598,10 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
     a.n_q = g.n_q;
     a.block_q = g.block_q;
     a.QR = g.block_q * g.g;
-    a.n_split = fused_n_split(g.W_cap);
+    // workgroups per CU that the registers allow: three for one query row
+    // (bf16 d 128: 146 VGPRs), two up to eight rows
+    a.rows_wg = fused_rows_wg(g, num_cu, a.QR == 1 ? 3 : 2);
+    a.n_split = (int)((g.W_cap + a.rows_wg - 1) / a.rows_wg);
     // merge phases: the fewest (a power of two) that leave each thread at
     // most kCombBatch splits, and at least enough to fill the workgroup
     int tpi = 1;
@@ -541,7 +617,7 @@ hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, cons
         a.step_c[c] = cos(f);
         a.step_s[c] = sin(f);
     }
-    const size_t rows = (size_t)g.n_blk * g.Hkv * a.n_split * (size_t)a.QR;
+    const size_t rows = (size_t)g.n_blk * g.Hkv * fused_max_parts(g.W_cap) * (size_t)a.QR;
     a.part_acc = (float *)ws;
     a.part_ml = (float *)((char *)ws + ((rows * g.d * sizeof(float) + 255) & ~(size_t)255));
     if (g.dtype == 0)

@@ -432,7 +432,7 @@ rea_status decode_step(const rea_problem *p, const rea_params *a, float *out, in
     if (rea::fused_decode_path(g)) {
         void *fws = c.take<char>(rea::fused_ws_bytes(g));
         return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out,
-                                                 fws, s),
+                                                 fws, num_cu, s),
                         "fused gather + window attention");
     }
     int32_t *Wlen = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
@@ -707,7 +707,8 @@ rea_status rea_decode_batch(const rea_problem *p, const rea_params *a, int32_t b
                         "batched window attention from the cache (MFMA)");
     }
     void *fws = c.take<char>(rea::fused_ws_bytes(g));
-    return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out, fws, s),
+    return launched(rea::launch_fused_decode(g, p->k, p->v, p->q, use_sel, use_nsel, out, fws,
+                                             num_cu, s),
                     "batched gather + window attention");
 }
 

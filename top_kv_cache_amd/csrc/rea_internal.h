@@ -143,7 +143,7 @@ bool fused_decode_path(const Geom &g);
 size_t fused_ws_bytes(const Geom &g);
 hipError_t launch_fused_decode(const Geom &g, const void *k, const void *v, const void *q,
                                const int32_t *sel, const int32_t *n_sel, float *out, void *ws,
-                               hipStream_t s);
+                               int num_cu, hipStream_t s);
 
 // Steps 2-4 for more than 8 bf16 query rows per block and KV head inside
 // rea_decode_step: the MFMA attention reads the window rows from the cache
