@@ -469,7 +469,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(score_bytes),
                     "kernel": ("k_score_tokens" if (w.S == 1 or w.token_segments) else
-                               "k_score_heads_lds" if w.per_q_head else "k_score_decode"),
+                               "k_score_heads_mfma" if w.per_q_head else "k_score_decode"),
                     "algorithmic_bytes_per_launch": score_bytes,
                     "avg_launch_us": k1_ms * 1e3}
         log(f"[bench] scoring kernel {k1_ms * 1e3:.1f} us/launch = {achieved:.0f} GB/s "

@@ -80,6 +80,9 @@ def oracle_head(w, layer, h, q64=None, K_h=None, V_h=None):
     if mfma_path(w):
         lo, hi = w.mid
         res["eps"] = mfma_span_bounds(qh[:, cols], K_h[0], lo, hi, w.S, w.block_q)
+    elif heads_mfma_path(w):
+        lo, hi = w.mid
+        res["eps"] = heads_span_bounds(qh[0, u], K_h[0], lo, hi, w.S)
     return res
 
 
@@ -88,6 +91,30 @@ def mfma_path(w):
     are approximations within a proven bound (selection stays exact)."""
     return (w.dtype == "bf16" and w.d == 128 and w.block_q == 64 and w.S % 32 == 0
             and w.n_spans > 0 and not w.token_segments)
+
+
+def heads_mfma_path(w):
+    """A decode step with one selection per query head (bf16, d 128, S a
+    multiple of 32, one sequence) scores the query heads of a KV head together
+    on MFMA: approximate span scores within a proven bound, exact selection."""
+    return (w.dtype == "bf16" and w.d == 128 and w.block_q == 1 and w.n_q == 1 and w.per_q_head
+            and 2 <= w.g <= 32 and w.S % 32 == 0 and w.n_spans > 0 and not w.token_segments)
+
+
+GAMMA_HEADS = 128 * 2.0 ** -23
+
+
+def heads_span_bounds(q_head, K_h, mid_lo, mid_hi, S):
+    """Per-span bounds eps[0][j] of the per-query-head MFMA scores, from the
+    bound the scoring path states: q_h is bf16, every product with a bf16 key
+    is exact in fp32, and the fp32 sum of a token's 128 products is within
+    128 * 2^-23 * ||q_h|| * ||k_t|| of the exact score; a span maximum moves by
+    at most that with the span's largest key norm.  q_head [d] fp64."""
+    e = GAMMA_HEADS * float(np.linalg.norm(q_head))
+    kn = np.linalg.norm(K_h[mid_lo:mid_hi], axis=1)
+    n_spans = -(-(mid_hi - mid_lo) // S)
+    kn = np.concatenate([kn, np.zeros(n_spans * S - kn.size)])
+    return e * kn.reshape(n_spans, S).max(axis=1)[None, :]
 
 
 GAMMA_MFMA = 255 * 2.0 ** -23 * (1 + 1e-6)
@@ -145,7 +172,7 @@ def compare_head(w, gpu, ora, h, check_windows=True):
     if ora["sc"].size:
         ref = ora["sc"]
         diff = np.abs(gpu["sc"][:, h, :] - ref)
-        if mfma_path(w):
+        if mfma_path(w) or heads_mfma_path(w):
             # MFMA approximations: every span within its own bound eps_j, the
             # bound the certification of the selection rests on
             eps = ora["eps"]

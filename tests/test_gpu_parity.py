@@ -64,6 +64,12 @@ SMALL = {
     "pqh_bf16_g8_d64": S(Hq=8, Hkv=1, d=64, T=1800, S=32, topk=10, L=128, per_q_head=True),
     "pqh_bf16_g5_generic": S(Hq=10, Hkv=2, d=64, T=900, S=16, topk=6, L=64, per_q_head=True),
     "pqh_bf16_token_level": S(S=1, topk=40, T=400, per_q_head=True),
+    # one selection per query head past 4096 spans: MFMA scoring, candidate
+    # spans, certification with the single-query fp64 re-scoring
+    "pqh_bf16_g4_d128_past_4096_spans": S(Hq=8, Hkv=2, d=128, T=200000, S=32, topk=40, L=256,
+                                          needles=2, kv_scaled=True, per_q_head=True),
+    "pqh_bf16_g2_d128_S64_partial": S(Hq=4, Hkv=2, d=128, T=9000, S=64, topk=11, L=300,
+                                      needles=1, per_q_head=True),
     "pqh_bf16_g2_d128_S20": S(Hq=4, Hkv=2, d=128, T=1500, S=20, topk=9, L=100,
                               kv_scaled=True, per_q_head=True),
     "pqh_f32_g4_d64_S8": S(dtype="f32", Hq=8, Hkv=2, d=64, T=1300, S=8, topk=17, L=90,
@@ -270,6 +276,47 @@ def test_mfma_blocks_order_below_fp32_resolution(n_q, T):
             assert ora["eps"][b].max() > 100 * gap
         compare_head(w, gpu, ora, h)
         log(f"  head {h}: worst |s_hat - s| / eps_j = {ora['eps_used']:.3g}")
+
+
+@pytest.mark.parametrize("T", [3000, 200000])
+def test_per_query_head_order_below_fp32_resolution(T):
+    """One selection per query head (scored on MFMA in fp32): 30 spans score
+    256 + 2^-16 * v_j with distinct v_j = 1 + m_j / 128, so their differences
+    (m * 2^-23) lie below the fp32 ulp of a token score (2^-15 at 256) and only
+    the fp64 re-scoring orders them; the top-10 boundary falls among them for
+    every query head.  At 200,000 tokens the certification ranks only the
+    candidate spans near the boundary."""
+    rng = np.random.default_rng(99 + T)
+    w = S(Hq=8, Hkv=2, d=128, T=T, S=32, topk=10, L=128, needles=0, per_q_head=True)
+    qn = np.zeros((1, w.Hq, w.d), np.float32)
+    qn[0, :, 0] = 1.0
+    qn[0, :, 1] = 2.0 ** -16
+    Kn = np.zeros((w.Hkv, w.T, w.d), np.float32)
+    Kn[:, :, 0] = 128.0
+    Kn[:, :, 2:] = rng.standard_normal((w.Hkv, w.T, w.d - 2)) * 2.0 ** -20
+    lo, hi = w.mid
+    n_full = (hi - lo) // w.S
+    for h in range(w.Hkv):
+        for j, m in zip(rng.choice(n_full, size=30, replace=False),
+                        rng.choice(32, size=30, replace=False)):
+            t0 = lo + j * w.S
+            Kn[h, t0:t0 + w.S, 0] = 256.0
+            Kn[h, t0:t0 + w.S, 1] = 1.0
+            Kn[h, t0 + int(rng.integers(w.S)), 1] = 1.0 + m / 128.0
+    Kn = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(Kn))
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    gpu = run_library(w, to_bf(qn), to_bf(Kn), to_bf(Vn))
+    q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
+    for u in range(w.H_sel):
+        hk = u // w.g
+        ora = oracle_head(w, 0, u, q64, K64[hk:hk + 1], V64[hk:hk + 1])
+        top = np.sort(ora["sc"][0])[::-1]
+        gap = top[w.topk - 1] - top[w.topk]
+        assert 0 < gap < 2.0 ** -15 and ora["eps"][0].max() > 100 * gap, (u, gap)
+        compare_head(w, gpu, ora, u)
 
 
 def test_mfma_blocks_massive_ties_past_4096_spans():

@@ -155,7 +155,9 @@ size_t group_max_bytes(const rea::Geom &g) {
 // score_select workspace: [span scores unless the caller keeps them][group
 // maxima, or the MFMA path's query rows / bounds]
 size_t select_aux_bytes(const rea::Geom &g) {
-    return rea::mfma_block_path(g) ? align256(rea::mfma_ws_bytes(g)) : align256(group_max_bytes(g));
+    if (rea::mfma_block_path(g)) return align256(rea::mfma_ws_bytes(g));
+    if (rea::heads_mfma_path(g)) return align256(rea::heads_ws_bytes(g));
+    return align256(group_max_bytes(g));
 }
 
 // token segments: the best tokens before widening, [n_blk][Hkv][k_tok] + counts
@@ -178,6 +180,10 @@ hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, doubl
         return rea::launch_score_select_mfma(g, q, k, scores, sel, n_sel, aux, num_cu, s,
                                              timing ? (hipEvent_t)timing->score_begin : nullptr,
                                              timing ? (hipEvent_t)timing->score_end : nullptr);
+    if (rea::heads_mfma_path(g))
+        return rea::launch_score_select_heads(g, q, k, scores, sel, n_sel, aux, num_cu, s,
+                                              timing ? (hipEvent_t)timing->score_begin : nullptr,
+                                              timing ? (hipEvent_t)timing->score_end : nullptr);
     hipError_t e = rea::launch_score(g, q, k, scores, (double *)aux, num_cu, s,
                                      timing ? (hipEvent_t)timing->score_begin : nullptr,
                                      timing ? (hipEvent_t)timing->score_end : nullptr);

@@ -131,6 +131,17 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
                                     void *ws, int num_cu, hipStream_t s,
                                     hipEvent_t ev_begin, hipEvent_t ev_end);
 
+// Step 1 of a decode step with one selection per query head (bf16, d 128, S a
+// multiple of 32, one sequence): the query heads of a KV head scored together
+// on MFMA (approximate span scores with a proven bound), then the exact top-k
+// by the certification.
+bool heads_mfma_path(const Geom &g);
+size_t heads_ws_bytes(const Geom &g);
+hipError_t launch_score_select_heads(const Geom &g, const void *q, const void *k,
+                                     double *span_scores, int32_t *sel, int32_t *n_sel,
+                                     void *ws, int num_cu, hipStream_t s,
+                                     hipEvent_t ev_begin, hipEvent_t ev_end);
+
 // Steps 2-3: window rows (K rotated fp32, V copied) + lengths, then the queries.
 hipError_t launch_gather_rope(const Geom &g, const void *k, const void *v, const void *q,
                               const int32_t *sel, const int32_t *n_sel, float *k_win,

@@ -53,8 +53,9 @@ struct ScoreArgs {
     const int64_t *lens;
     int hps, G, L;
     int64_t T, seq_stride_bytes;
-    // null, or one flag per (block, KV head): k_score_block scores only the
-    // flagged pairs (the exact fallback of the MFMA block path)
+    // null, or one flag per (block, selection head): k_score_block and the
+    // per-query-head decode scorers score only the flagged pairs (the exact
+    // fallback of the MFMA paths)
     const uint32_t *only;
 };
 
@@ -224,6 +225,12 @@ __global__ __launch_bounds__(kThreads) void k_score_decode_heads(ScoreArgs a) {
     const int bp = blockIdx.x / a.P, p = blockIdx.x % a.P;
     const int b = bp / Hp, hp = bp % Hp;
     const int64_t bh0 = (int64_t)b * a.Hkv + (int64_t)hp * NH;   // first selection head
+    if (a.only) {
+        bool any = false;
+#pragma unroll
+        for (int m = 0; m < NH; ++m) any |= a.only[bh0 + m] != 0;
+        if (!any) return;
+    }
 
     double qr[NH][EPL];
     {
@@ -379,6 +386,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_score_heads_lds(ScoreArgs a) {
     const int bp = blockIdx.x / a.P, p = blockIdx.x % a.P;
     const int b = bp / Hp, hp = bp % Hp;
     const int64_t bh0 = (int64_t)b * a.Hkv + (int64_t)hp * NH;
+    if (a.only) {
+        bool any = false;
+#pragma unroll
+        for (int m = 0; m < NH; ++m) any |= a.only[bh0 + m] != 0;
+        if (!any) return;
+    }
 
     int order[NH];
     if (NH == 4) {

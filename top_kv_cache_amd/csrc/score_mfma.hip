@@ -16,8 +16,9 @@
 //                 queries (K = 256: the key tile is fed twice).  The tile's
 //                 token maxima, the span maximum and the sum over the block's
 //                 queries are taken in the epilogue; one fp64 span score per
-//                 (block, span) is written, and each span's largest key norm
-//                 (by one wave of the grid per span).
+//                 (block, span) is written, and an upper bound of each span's
+//                 largest key norm (by one wave of the grid per span: squares
+//                 summed in fp32 with v_dot2, rounded up).
 //   k_cert_candidates
 //                 only beyond 4096 spans: per (block, KV head), the spans
 //                 whose approximate score lies within twice the largest error
@@ -48,6 +49,7 @@ namespace rea {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 128;             // head_dim handled here
@@ -193,6 +195,11 @@ __device__ __forceinline__ double pair_sum(double x) {
     const double a = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0]));
     const double b = __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
     return a + b;     // own + partner in either order: the same value
+}
+
+__device__ __forceinline__ float pair_sumf(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);   // own + partner, either order
 }
 
 template <int CTRL>
@@ -426,21 +433,21 @@ __global__ __launch_bounds__(256, 2) void k_score_mfma(MfmaArgs a) {
         }
         if (owner) {
             // squared norm of key row lane%32: this lane's half of the channels
-            // (its A fragments) plus the partner lane's half
-            double sq = 0.0;
+            // (its A fragments) plus the partner lane's half, summed in fp32 by
+            // v_dot2 (bf16 squares are exact in fp32; the at most 130 roundings
+            // of the sums are covered by the factor applied at the span's end)
+            float sq4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
                 const uint32_t w4[4] = {af[ks].x, af[ks].y, af[ks].z, af[ks].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const double x0 = (double)__uint_as_float(w4[e] << 16);
-                    const double x1 = (double)__uint_as_float(w4[e] & 0xffff0000u);
-                    sq = fma(x0, x0, sq);
-                    sq = fma(x1, x1, sq);
+                    const bf16x2 x = __builtin_bit_cast(bf16x2, w4[e]);
+                    sq4[e] = __builtin_amdgcn_fdot2_f32_bf16(x, x, sq4[e], false);
                 }
             }
-            sq = pair_sum(sq);
-            if ((lane & 31) < valid) kn_run = fmax(kn_run, sq);
+            const float sq = pair_sumf((sq4[0] + sq4[1]) + (sq4[2] + sq4[3]));
+            if ((lane & 31) < valid) kn_run = fmax(kn_run, (double)sq);
         }
         if (++sub == tiles_per_span) {
             // span done: per-query maximum (lanes l and l^32 hold the two row
@@ -452,7 +459,10 @@ __global__ __launch_bounds__(256, 2) void k_score_mfma(MfmaArgs a) {
             if (owner) {
                 const double kn = row_max16(kn_run);
                 const double km = fmax(readlane_f64(kn, 0), readlane_f64(kn, 16));
-                if (lane == 0) kres[j - j0] = sqrt(km) * (1.0 + 1e-12);
+                // an upper bound of the largest norm: the fp32 sums low by
+                // at most 130 * 2^-23 relative, squares below 2^-126 flushed
+                if (lane == 0)
+                    kres[j - j0] = sqrt(km * (1.0 + 0x1p-15) + 0x1p-119) * (1.0 + 1e-12);
             }
             run[0] = -INFINITY;
             run[1] = -INFINITY;
@@ -470,6 +480,237 @@ __global__ __launch_bounds__(256, 2) void k_score_mfma(MfmaArgs a) {
             if (bw < a.n_blk) a.out[((int64_t)bw * a.Hkv + h) * a.n_spans + j0 + x] = res[w][x];
         }
         if ((((j0 + x) >> 2) % n_qg) == qg) a.kbar[(int64_t)h * a.n_spans + j0 + x] = kres[x];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_score_heads_mfma: a decode step with one selection per query head (bf16,
+// d 128, S a multiple of 32).  The NH query heads of a KV head are the
+// columns, and 32 consecutive key tokens the rows, of a
+// v_mfma_f32_32x32x16_bf16, so every key row is read once and scored for all
+// NH heads on the matrix cores.  q_h is bf16, so each product is exact in
+// fp32, and the fp32 sum of a token's 128 products is within
+// gamma * ||q_h|| * ||k_t|| of the exact score (at most 128 roundings of at
+// most 2^-23 relative each, whatever the order).  The span scores written are
+// approximations within eps_j = E_h * Kbar_j (E_h = gamma ||q_h||, Kbar_j an
+// upper bound of the span's largest key norm), and the certification below
+// decides the top-k exactly (one query per pair: its fp64 re-scoring runs in
+// k_certify_one).
+//
+// grid (Hp * P), 256 threads, one workgroup per CU: workgroup (hp, p) takes a
+// contiguous run of KV head hp's groups of 32 spans.  Within a group, wave w
+// scores spans w, w + 4, ..., so the four waves stream adjacent spans, each
+// through its own LDS ring of kQNB tiles filled by DMA (global_load_lds;
+// 16-byte chunk c of token row m at slot c ^ (m % 16), as in k_score_mfma).
+// The only barrier is one per group, where the waves' group maxima are
+// combined in LDS.  The DMA loads carry the non-temporal cache policy: the
+// keys are read once, and keeping them out of the caches' normal replacement
+// raises the read rate markedly on this pattern.
+// ---------------------------------------------------------------------------
+constexpr int kQNB = 3;
+constexpr int kGroupH = 32;         // spans per group
+constexpr double kGammaHeads = 128.0 * 1.1920928955078125e-07 * (1.0 + 1e-4);   // 128 * 2^-23
+
+struct HeadsArgs {
+    const unsigned char *k;     // K cache (bf16)
+    const uint16_t *q;          // [Hq][D]: the step's one query
+    double *out;                // [Hsel][n_spans] approximate span scores
+    double *kbar;               // [Hsel][n_spans] key-norm bounds
+    double *E;                  // [Hsel]
+    double *gmx, *gkb;          // [Hsel][groups]: per 32 spans, largest score / norm bound
+    int64_t sh_bytes, st_bytes, mid_lo, mid_hi, n_spans;
+    int S, NH, Hp, P;
+};
+
+__global__ __launch_bounds__(256, 1) void k_score_heads_mfma(HeadsArgs a) {
+    __shared__ __align__(16) unsigned char ring[kWavesM][kQNB][kTileBytes];
+    __shared__ double gsl[2][kWavesM][32], gsk[2][kWavesM][32];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hp = blockIdx.x / a.P, p = blockIdx.x % a.P;
+    const int64_t h0 = (int64_t)hp * a.NH;          // first selection head (query head)
+    const int n = lane & 31, kb = lane >> 5;
+
+    // B fragments: query head n (zero columns beyond NH), channels
+    // ks * 16 + kb * 8 .. + 8
+    uint4 qf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+        qf[ks] = n < a.NH ? ld16(a.q + (h0 + n) * kD + ks * 16 + kb * 8) : make_uint4(0u, 0u, 0u, 0u);
+    if (p == 0 && wave == 0) {
+        // E_h = gamma * ||q_h|| (bf16 squares and their sum exact in fp64), plus
+        // a floor covering fp32 products flushed below 2^-126
+        double sq = 0.0;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const uint32_t w4[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double x0 = (double)__uint_as_float(w4[e] << 16);
+                const double x1 = (double)__uint_as_float(w4[e] & 0xffff0000u);
+                sq = fma(x0, x0, fma(x1, x1, sq));
+            }
+        }
+        sq = pair_sum(sq);
+        if (lane < a.NH) a.E[h0 + lane] = kGammaHeads * sqrt(sq) * (1.0 + 1e-12) + 0x1p-50;
+    }
+
+    // the workgroup's groups [g0, g1) of 32 spans; this wave's span slots
+    // are wave, wave + 4, ... of each group
+    const int64_t ng = (a.n_spans + kGroupH - 1) / kGroupH;
+    const int64_t g0 = (int64_t)p * ng / a.P, g1 = (int64_t)(p + 1) * ng / a.P;
+    const int64_t first = g0;
+    const int64_t n_grp = g1 - g0;
+    const int tps = a.S / kTile;
+    // every wave runs the same number of group steps (8 span slots per group,
+    // slots past the middle's last span masked) so the group barrier matches
+    const int64_t n_tiles = n_grp * (kGroupH / kWavesM) * tps;
+    const unsigned char *kh = a.k + (int64_t)hp * a.sh_bytes;
+    unsigned char *rw = &ring[wave][0][0];
+    // tile cursors (issue side and consume side), advanced incrementally:
+    // sub-tile within the span, span slot within the group (stride 4), group
+    struct Cursor {
+        int sub, sig;
+        int64_t grp, t0;
+    };
+    auto advance = [&](Cursor &u) {
+        if (++u.sub < tps) {
+            u.t0 += kTile;
+            return;
+        }
+        u.sub = 0;
+        u.sig += kWavesM;
+        if (u.sig >= kGroupH) {
+            u.sig = wave;
+            u.grp += 1;
+        }
+        u.t0 = a.mid_lo + (u.grp * kGroupH + u.sig) * a.S;
+    };
+    Cursor iss = {0, wave, first, a.mid_lo + (first * kGroupH + wave) * a.S};
+    Cursor con = iss;
+    int64_t it_issue = 0;
+    int slot_i = 0, slot_c = 0;                  // ring slots of the next issue / consume
+    auto issue_next = [&]() {
+        if (it_issue >= n_tiles) return;
+        const int64_t t0 = iss.t0;
+        unsigned char *dst = rw + slot_i * kTileBytes;
+        slot_i = slot_i + 1 == kQNB ? 0 : slot_i + 1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = i * 4 + (lane >> 4);
+            const int chunk = (lane & 15) ^ (row & 15);
+            int64_t t = t0 + row;
+            if (t >= a.mid_hi) t = a.mid_hi - 1;       // rows past the middle are masked
+            __builtin_amdgcn_global_load_lds((const void *)(kh + t * a.st_bytes + chunk * 16),
+                                             (void __attribute__((address_space(3))) *)(dst + i * 1024),
+                                             16, 0, 2);
+        }
+        ++it_issue;
+        advance(iss);
+    };
+#pragma unroll
+    for (int i = 0; i < kQNB - 1; ++i) issue_next();
+
+    float run = -INFINITY;       // running maximum of this lane's rows (query n)
+    float kn_run = 0.f;          // running maximum of squared key norms (row lane % 32)
+    double gmax = -INFINITY, gkmax = 0.0;   // the group's maxima (lanes n < NH)
+    for (int64_t it = 0; it < n_tiles; ++it) {
+        int64_t later = n_tiles - 1 - it;               // tiles issued after this one
+        if (later > kQNB - 2) later = kQNB - 2;
+        // 8 DMA instructions per tile
+        if (later == 0) __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(0xF78);              // vmcnt(8)
+        const int64_t grp = con.grp;
+        const int sig = con.sig, sub = con.sub;
+        const int64_t j = grp * kGroupH + sig;
+        const int64_t t0 = con.t0;
+        const unsigned char *tb = rw + slot_c * kTileBytes;
+        slot_c = slot_c + 1 == kQNB ? 0 : slot_c + 1;
+        advance(con);
+        // refill the slot read in the previous step (its reads completed there)
+        issue_next();
+        uint4 af[8];
+        {
+            const int m = lane & 31;
+            const uint32_t base = lds_addr(tb) + m * 256;
+            uint32_t ad[8];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) ad[ks] = base + (((ks * 2 + kb) ^ (m & 15)) * 16);
+            lds_read8(ad, af);
+        }
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[ks]),
+                                                          __builtin_bit_cast(bf16x8, qf[ks]),
+                                                          acc, 0, 0, 0);
+        // squared key norm of row lane % 32 (this lane's half of the channels,
+        // then the partner's), fp32 v_dot2 sums
+        float sq4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const uint32_t w4[4] = {af[ks].x, af[ks].y, af[ks].z, af[ks].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2 x = __builtin_bit_cast(bf16x2, w4[e]);
+                sq4[e] = __builtin_amdgcn_fdot2_f32_bf16(x, x, sq4[e], false);
+            }
+        }
+        const float sq = pair_sumf((sq4[0] + sq4[1]) + (sq4[2] + sq4[3]));
+        const int64_t valid = a.mid_hi - t0;
+        if ((lane & 31) < valid) kn_run = fmaxf(kn_run, sq);
+        if (valid >= kTile) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) run = fmaxf(run, acc[rr]);
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 8 * (rr >> 2) + 4 * kb + (rr & 3);
+                if (row < valid) run = fmaxf(run, acc[rr]);
+            }
+        }
+        if (sub == tps - 1) {
+            // span done: query n's maximum (lanes n and n + 32 hold the two
+            // row halves), the largest key norm over the 32 row lanes
+            const double sm = (double)pair_max(run) + 0.0;
+            float km = kn_run;
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) km = fmaxf(km, __shfl_xor(km, o));
+            // an upper bound: the fp32 sums low by at most 130 * 2^-23
+            // relative, squares below 2^-126 flushed
+            const double kbv = sqrt((double)km * (1.0 + 0x1p-15) + 0x1p-119) * (1.0 + 1e-12);
+            if (j < a.n_spans) {
+                if (kb == 0 && n < a.NH) {
+                    a.out[(h0 + n) * a.n_spans + j] = sm;
+                    a.kbar[(h0 + n) * a.n_spans + j] = kbv;
+                }
+                gmax = fmax(gmax, sm);
+                gkmax = fmax(gkmax, kbv);
+            }
+            run = -INFINITY;
+            kn_run = 0.f;
+            if (sig + kWavesM >= kGroupH) {      // this wave's last slot of the group
+                if (kb == 0 && n < a.NH) {
+                    gsl[grp & 1][wave][n] = gmax;
+                    gsk[grp & 1][wave][n] = gkmax;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                if (wave == 0 && kb == 0 && n < a.NH) {
+                    double m1 = gsl[grp & 1][0][n], m2 = gsk[grp & 1][0][n];
+#pragma unroll
+                    for (int w = 1; w < kWavesM; ++w) {
+                        m1 = fmax(m1, gsl[grp & 1][w][n]);
+                        m2 = fmax(m2, gsk[grp & 1][w][n]);
+                    }
+                    a.gmx[(h0 + n) * ng + grp] = m1;
+                    a.gkb[(h0 + n) * ng + grp] = m2;
+                }
+                gmax = -INFINITY;
+                gkmax = 0.0;
+            }
+        }
     }
 }
 
@@ -505,6 +746,11 @@ struct CertArgs {
     int32_t *gcand;     // [pairs][kCCap] candidate span indices, ascending
     uint32_t *gncand;   // [pairs] candidates
     uint32_t *gover;    // [pairs] 1: too many candidates, the exact fallback selects
+    // queries per pair: 64 (blocks; re-scored by k_rescore from qeff) or 1 (a
+    // decode step per query head; re-scored in k_certify_tail from q1)
+    int qpb;
+    const uint16_t *q1;     // [Hsel][D] bf16 (qpb == 1)
+    const double *gmx, *gkb;    // [pairs][groups] group maxima (k_cert_candidates_g)
 };
 
 // Span index of the pair's ranked span at position c.
@@ -530,6 +776,7 @@ struct CertShared {
     uint32_t count, above, nd, nx;
     int32_t bstar, cut_j;
     double cut_v;
+    double q1[kD];                  // the pair's query in fp64 (one query per pair)
 };
 
 __device__ __forceinline__ int c_bin(double x, double mn, double inv) {
@@ -885,6 +1132,51 @@ __device__ __forceinline__ void cert_rescore(const CertArgs &a, Sh &sh, int64_t 
     }
 }
 
+// One query per pair: the exact (fp64) scores of the nx uncertain spans into
+// sh.xv, a wave per span; lane (token tl of a 32-token chunk, channel half kb)
+// takes 64 products of its token (bf16 values are exact in fp64), the halves
+// are added across lane^32 and the maximum taken over the 32 token lanes.
+__device__ __forceinline__ void cert_rescore_one(const CertArgs &a, CertShared &sh, int64_t bh,
+                                                 uint32_t nx) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = (int)(bh % a.Hkv);
+    const uint16_t *qh = a.q1 + (int64_t)h * kD;
+    for (int c = tid; c < kD; c += kCThreads) sh.q1[c] = bf16_to_f64(qh[c]);
+    __syncthreads();
+    const int tl = lane & 31, kb = lane >> 5;
+    const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
+    for (uint32_t x = wave; x < nx; x += kCWaves) {
+        const int64_t j = span_at(a, bh, sh.xs[x]);
+        const int64_t tb = a.mid_lo + j * a.S, te = min(tb + (int64_t)a.S, a.mid_hi);
+        double best = -INFINITY;
+        for (int64_t c0 = tb; c0 < te; c0 += 32) {
+            const int64_t t = c0 + tl;
+            const bool ok = t < te;
+            const unsigned char *krow = kh + (ok ? t : tb) * a.st_bytes + kb * (kD / 2) * 2;
+            uint4 kr[8];
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) kr[cc] = ld16(krow + cc * 16);
+            double acc = 0.0;
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+                const uint32_t w4[4] = {kr[cc].x, kr[cc].y, kr[cc].z, kr[cc].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = kb * (kD / 2) + cc * 8 + 2 * e;
+                    acc = fma(sh.q1[c], (double)__uint_as_float(w4[e] << 16), acc);
+                    acc = fma(sh.q1[c + 1], (double)__uint_as_float(w4[e] & 0xffff0000u), acc);
+                }
+            }
+            acc += __shfl_xor(acc, 32);
+            if (ok) best = fmax(best, acc);
+        }
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) best = fmax(best, __shfl_xor(best, o));
+        if (lane == 0) sh.xv[x] = best + 0.0;
+    }
+    __syncthreads();
+}
+
 // sh.xv from the per-item sums of the re-scoring, in a fixed order: the two
 // parts of a span, then the two query halves.
 __device__ __forceinline__ void cert_gather_xv(CertShared &sh, const double *gpart, uint32_t nx) {
@@ -957,6 +1249,211 @@ __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, i
             }
             for (int64_t i = (int64_t)kk + tid; i < a.topk; i += kCThreads) sel[i] = -1;
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_cert_candidates_g: grid (pairs), 512 threads; the candidate spans of a
+// pair with more than kCCap spans from the group maxima the scoring kernel
+// wrote (largest approximate score and largest key-norm bound of every 32
+// spans).  The (kk+1)-th largest group maximum tau is a lower bound of the
+// (kk+1)-th largest score c' (the kk+1 best groups hold kk+1 distinct spans at
+// or above it), so theta = tau - 2 eps_max <= c' - 2 eps_max and every span
+// scoring below theta is certainly out (see k_cert_candidates).  Only the
+// groups whose maximum reaches theta are read; their spans at or above theta,
+// ascending, are the candidates.  More than kGCand such groups or kCCap such
+// spans flag the pair for the exact fallback.
+// ---------------------------------------------------------------------------
+constexpr int kGThreads = 512;
+constexpr int kGPT = 8;                       // group maxima per thread
+constexpr int kGMaxGroups = kGThreads * kGPT; // 4096 groups (131,072 spans)
+constexpr int kGCand = 256;                   // candidate groups
+
+__global__ __launch_bounds__(kGThreads) void k_cert_candidates_g(CertArgs a) {
+    __shared__ uint32_t hist[kCBins];
+    __shared__ double red[3][kGThreads / 64];
+    __shared__ uint32_t wsum[kGThreads / 64];
+    __shared__ int32_t cgrp[kGCand];
+    __shared__ uint32_t cword[kGCand];
+    __shared__ int32_t s_bstar;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NW = kGThreads / 64;
+    const int64_t bh = blockIdx.x;
+    const int64_t n = a.n_spans;
+    const int64_t m = (n + kGroupH - 1) / kGroupH;
+    const int kk = a.kk;
+    auto flag_over = [&]() {
+        if (tid == 0) {
+            a.gncand[bh] = 0;
+            a.gover[bh] = 1;
+        }
+    };
+    if (kk == 0 || kk >= n) {
+        if (tid == 0) {
+            a.gncand[bh] = 0;
+            a.gover[bh] = 0;
+        }
+        return;
+    }
+    if (m > kGMaxGroups || (int64_t)kk + 1 > m) {
+        flag_over();
+        return;
+    }
+    const double *gm = a.gmx + bh * m;
+    const double *gk = a.gkb + bh * m;
+    double gv[kGPT];
+    double mn = INFINITY, mx = -INFINITY, km = 0.0;
+#pragma unroll
+    for (int r = 0; r < kGPT; ++r) {
+        const int64_t g = (int64_t)r * kGThreads + tid;
+        gv[r] = g < m ? gm[g] : -INFINITY;
+        km = fmax(km, g < m ? gk[g] : 0.0);
+    }
+#pragma unroll
+    for (int r = 0; r < kGPT; ++r)
+        if ((int64_t)r * kGThreads + tid < m) {
+            mn = fmin(mn, gv[r]);
+            mx = fmax(mx, gv[r]);
+        }
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fmin(mn, __shfl_xor(mn, o));
+        mx = fmax(mx, __shfl_xor(mx, o));
+        km = fmax(km, __shfl_xor(km, o));
+    }
+    if (lane == 0) {
+        red[0][wave] = mn;
+        red[1][wave] = mx;
+        red[2][wave] = km;
+    }
+    for (int i = tid; i < kCBins; i += kGThreads) hist[i] = 0u;
+    __syncthreads();
+    mn = INFINITY;
+    mx = -INFINITY;
+    km = 0.0;
+    for (int w = 0; w < NW; ++w) {
+        mn = fmin(mn, red[0][w]);
+        mx = fmax(mx, red[1][w]);
+        km = fmax(km, red[2][w]);
+    }
+    // tau: the smallest group maximum in the bins at or above the bin that
+    // holds the (kk+1)-th largest (every maximum equal: tau = that value)
+    double tau = mn;
+    if (mn < mx) {
+        const double inv = (double)kCBins / (mx - mn);
+#pragma unroll
+        for (int r = 0; r < kGPT; ++r)
+            if ((int64_t)r * kGThreads + tid < m) atomicAdd(&hist[c_bin(gv[r], mn, inv)], 1u);
+        __syncthreads();
+        if (wave == 0) {
+            constexpr int bpl = kCBins / 64;
+            const int64_t need = (int64_t)kk + 1;
+            uint32_t own = 0;
+            for (int i = 0; i < bpl; ++i) own += hist[lane * bpl + i];
+            uint32_t suf = own;
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_down(suf, o);
+                if (lane + o < 64) suf += y;
+            }
+            const uint32_t after = suf - own;
+            if ((int64_t)after < need && need <= (int64_t)suf) {
+                uint32_t above = after;
+                int bb = lane * bpl + bpl - 1;
+                for (; bb > lane * bpl; --bb) {
+                    if ((int64_t)(above + hist[bb]) >= need) break;
+                    above += hist[bb];
+                }
+                s_bstar = bb;
+            }
+        }
+        __syncthreads();
+        const int bstar = s_bstar;
+        double lo = INFINITY;
+#pragma unroll
+        for (int r = 0; r < kGPT; ++r)
+            if ((int64_t)r * kGThreads + tid < m && c_bin(gv[r], mn, inv) >= bstar) lo = fmin(lo, gv[r]);
+        for (int o = 32; o > 0; o >>= 1) lo = fmin(lo, __shfl_xor(lo, o));
+        __syncthreads();
+        if (lane == 0) red[0][wave] = lo;
+        __syncthreads();
+        tau = INFINITY;
+        for (int w = 0; w < NW; ++w) tau = fmin(tau, red[0][w]);
+    }
+    // eps_max bounds every span's cert_eps: E * Kbar with the largest key
+    // norm, and the relative term with a magnitude that covers every span
+    // at or above theta (spans below it stay below theta + eps_max)
+    const double Eb = a.E[bh];
+    const double eb = Eb * km * (1.0 + 1e-9) * (1.0 + 1e-9) + 1e-300;
+    const double A = fabs(tau) + fmax(fabs(mn), fabs(mx)) + 4.0 * eb;
+    const double eps_max = eb + 1e-12 * (A + eb) + 1e-300;
+    double theta = tau - 2.0 * eps_max;
+    theta -= 4e-16 * fabs(theta) + 1e-300;
+
+    // candidate groups: maximum >= theta, ascending
+    uint32_t ncg = 0;
+#pragma unroll
+    for (int r = 0; r < kGPT; ++r) {
+        const int64_t g = (int64_t)r * kGThreads + tid;
+        const bool keep = g < m && gv[r] >= theta;
+        const uint64_t bal = __ballot(keep);
+        const uint32_t before = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        __syncthreads();
+        if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t off = 0, tot = 0;
+        for (int w = 0; w < NW; ++w) {
+            off += w < wave ? wsum[w] : 0u;
+            tot += wsum[w];
+        }
+        const uint32_t pos = ncg + off + before;
+        if (keep && pos < (uint32_t)kGCand) cgrp[pos] = (int32_t)g;
+        ncg += tot;
+    }
+    if (ncg > (uint32_t)kGCand) {
+        flag_over();
+        return;
+    }
+    // their spans >= theta: half a wave per group, one 32-bit word each
+    const int half = tid >> 5, hl = tid & 31;
+    constexpr int NH2 = kGThreads / 32;           // groups per round
+    for (uint32_t c0 = 0; c0 < ncg; c0 += NH2) {
+        const uint32_t c = c0 + half;
+        const int64_t jj = c < ncg ? (int64_t)cgrp[c] * kGroupH + hl : 0;
+        const bool keep = c < ncg && jj < n && a.shat[bh * n + jj] >= theta;
+        const uint64_t bal = __ballot(keep);
+        if (hl == 0 && c < ncg) cword[c] = (uint32_t)(bal >> (lane & 32));
+    }
+    __syncthreads();
+    // ordered compaction of the words (ncg <= 256 <= threads)
+    const uint32_t wv = tid < (int)ncg ? cword[tid] : 0u;
+    uint32_t x = __popc(wv);
+    const uint32_t v0 = x;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
+    for (int w = 0; w < NW; ++w) {
+        base += w < wave ? wsum[w] : 0u;
+        total += wsum[w];
+    }
+    if (total > (uint32_t)kCCap) {
+        flag_over();
+        return;
+    }
+    uint32_t pos = base + x - v0;
+    int32_t *cand = a.gcand + bh * kCCap;
+    uint32_t w = wv;
+    while (w) {
+        const int bit = __ffs(w) - 1;
+        w &= w - 1;
+        cand[pos++] = cgrp[tid] * kGroupH + bit;
+    }
+    if (tid == 0) {
+        a.gncand[bh] = total;
+        a.gover[bh] = 0;
     }
 }
 
@@ -1168,6 +1665,20 @@ __global__ __launch_bounds__(kRThreads, 3) void k_rescore(CertArgs a) {
                             a.gpart + bh * 2 * kCCap);
 }
 
+// One query per pair (a decode step per query head): classification, fp64
+// re-scoring of the uncertain spans and ranking in one workgroup per pair.
+__global__ __launch_bounds__(kCThreads) void k_certify_one(CertArgs a) {
+    __shared__ CertShared sh;
+    const int64_t bh = blockIdx.x;
+    if (a.gover && a.gover[bh]) return;      // too many candidates: the exact fallback selects
+    uint32_t nx, nd;
+    if (!cert_classify(a, sh, bh, nx, nd)) return;
+    const int64_t need = (int64_t)a.kk - nd;
+    if (need > 0) cert_rescore_one(a, sh, bh, nx);
+    __syncthreads();
+    cert_finish(a, sh, bh, nx, need);
+}
+
 __global__ __launch_bounds__(kCThreads) void k_certify_tail(CertArgs a) {
     __shared__ CertShared sh;
     const int64_t bh = blockIdx.x;
@@ -1180,7 +1691,10 @@ __global__ __launch_bounds__(kCThreads) void k_certify_tail(CertArgs a) {
     if (need > 0) {
         for (uint32_t i = threadIdx.x; i < nx; i += kCThreads) sh.xs[i] = a.gxs[bh * kCCap + i];
         __syncthreads();
-        cert_gather_xv(sh, a.gpart + bh * 2 * kCCap, nx);
+        if (a.qpb == 1)
+            cert_rescore_one(a, sh, bh, nx);
+        else
+            cert_gather_xv(sh, a.gpart + bh * 2 * kCCap, nx);
     }
     __syncthreads();
     cert_finish(a, sh, bh, nx, need);
@@ -1296,6 +1810,10 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     ca.kk = g.k_sel;
     ca.topk = g.topk;
     ca.R = cert_ways(g);
+    ca.qpb = kQB;
+    ca.q1 = nullptr;
+    ca.gmx = nullptr;
+    ca.gkb = nullptr;
     const unsigned pairs = (unsigned)(g.n_blk * g.Hkv);
     ca.gxs = (int32_t *)p;
     p += al((size_t)pairs * kCCap * sizeof(int32_t));
@@ -1332,6 +1850,109 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     // pairs flagged in gover: exact fp64 span scores on the VALU (overwriting
     // their approximations) and the ordinary top-k; the other pairs' workgroups
     // return at once
+    if ((e = launch_score(g, q, k, span_scores, fb_gmax, num_cu, s, nullptr, nullptr, ca.gover)) !=
+        hipSuccess)
+        return e;
+    return launch_topk(g, span_scores, fb_gmax, sel, n_sel, s, ca.gover);
+}
+
+bool heads_mfma_path(const Geom &g) {
+    return g.dtype == 0 && g.d == kD && g.block_q == 1 && g.n_q == 1 && g.g == 1 &&
+           g.rep >= 2 && g.rep <= 32 && g.S % kTile == 0 && g.n_spans > 0 && !g.lens && !g.seg;
+}
+
+size_t heads_ws_bytes(const Geom &g) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t ng = (size_t)((g.n_spans + kGroupH - 1) / kGroupH);
+    return al((size_t)g.Hkv * g.n_spans * sizeof(double)) +            // key-norm bounds
+           al((size_t)g.Hkv * sizeof(double)) +                        // E
+           2 * al((size_t)g.Hkv * ng * sizeof(double)) +               // group maxima
+           cert_many_bytes(g);                                         // candidates, fallback
+}
+
+hipError_t launch_score_select_heads(const Geom &g, const void *q, const void *k,
+                                     double *span_scores, int32_t *sel, int32_t *n_sel,
+                                     void *ws, int num_cu, hipStream_t s,
+                                     hipEvent_t ev_begin, hipEvent_t ev_end) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t ng = (size_t)((g.n_spans + kGroupH - 1) / kGroupH);
+    char *p = (char *)ws;
+    double *kbar = (double *)p;
+    p += al((size_t)g.Hkv * g.n_spans * sizeof(double));
+    double *E = (double *)p;
+    p += al((size_t)g.Hkv * sizeof(double));
+    double *gmx = (double *)p;
+    p += al((size_t)g.Hkv * ng * sizeof(double));
+    double *gkb = (double *)p;
+    p += al((size_t)g.Hkv * ng * sizeof(double));
+
+    HeadsArgs ha;
+    ha.k = (const unsigned char *)k;
+    ha.q = (const uint16_t *)q;
+    ha.out = span_scores;
+    ha.kbar = kbar;
+    ha.E = E;
+    ha.gmx = gmx;
+    ha.gkb = gkb;
+    ha.sh_bytes = g.sh * g.esize;
+    ha.st_bytes = g.st * g.esize;
+    ha.mid_lo = g.mid_lo;
+    ha.mid_hi = g.mid_hi;
+    ha.n_spans = g.n_spans;
+    ha.S = g.S;
+    ha.NH = g.rep;
+    ha.Hp = g.Hkv / g.rep;
+    // one workgroup per CU, split evenly over the KV heads (runs of whole groups)
+    int64_t P = ((int64_t)(num_cu > 0 ? num_cu : 256) + ha.Hp - 1) / ha.Hp;
+    if (P > (int64_t)ng) P = (int64_t)ng;
+    if (P < 1) P = 1;
+    ha.P = (int)P;
+    hipError_t e = launch_struct(k_score_heads_mfma, dim3((unsigned)(ha.Hp * P)), dim3(256), 0, s,
+                                 ha, ev_begin, ev_end);
+    if (e != hipSuccess) return e;
+
+    CertArgs ca = {};
+    ca.shat = span_scores;
+    ca.kbar = kbar;
+    ca.E = E;
+    ca.qeff = nullptr;
+    ca.k = (const unsigned char *)k;
+    ca.sel = sel;
+    ca.nsel = n_sel;
+    ca.sh_bytes = ha.sh_bytes;
+    ca.st_bytes = ha.st_bytes;
+    ca.mid_lo = g.mid_lo;
+    ca.mid_hi = g.mid_hi;
+    ca.n_spans = g.n_spans;
+    ca.S = g.S;
+    ca.Hkv = g.Hkv;
+    ca.rep = g.rep;
+    ca.n_q = 1;
+    ca.kk = g.k_sel;
+    ca.topk = g.topk;
+    ca.qpb = 1;
+    ca.q1 = (const uint16_t *)q;
+    ca.gmx = gmx;
+    ca.gkb = gkb;
+    const unsigned pairs = (unsigned)(g.n_blk * g.Hkv);
+    const bool many = g.n_spans > kCCap;
+    double *fb_gmax = nullptr;
+    if (many) {
+        ca.gcand = (int32_t *)p;
+        p += al((size_t)pairs * kCCap * sizeof(int32_t));
+        ca.gncand = (uint32_t *)p;
+        p += al((size_t)pairs * sizeof(uint32_t));
+        ca.gover = (uint32_t *)p;
+        p += al((size_t)pairs * sizeof(uint32_t));
+        fb_gmax = (double *)p;
+        if ((e = launch_struct(k_cert_candidates_g, dim3(pairs), dim3(kGThreads), 0, s, ca)) !=
+            hipSuccess)
+            return e;
+    }
+    if ((e = launch_struct(k_certify_one, dim3(pairs), dim3(kCThreads), 0, s, ca)) != hipSuccess)
+        return e;
+    if (!many) return hipSuccess;
+    // flagged pairs: exact fp64 scores on the VALU, then the ordinary top-k
     if ((e = launch_score(g, q, k, span_scores, fb_gmax, num_cu, s, nullptr, nullptr, ca.gover)) !=
         hipSuccess)
         return e;

@@ -15,7 +15,10 @@
 //      k-th largest score from below (the k best groups hold k distinct
 //      scores), so every selected span scores >= tau and lies in a group
 //      whose maximum is >= tau; at most 256 such groups are accepted (more
-//      only with massive ties).
+//      only with massive ties).  With at most 4096 spans the same level is
+//      taken over the span scores themselves (read with the group maxima):
+//      when k is close to the group count the group bound keeps most spans,
+//      the span bound about k of them.
 //   2. the spans of those groups with score >= tau (all spans scoring >= tau)
 //      are loaded into LDS;
 //   3. with at most 192 of them, each one's rank among them (score desc,
@@ -50,6 +53,7 @@ constexpr int kBins = 2048;
 constexpr int kRankMax = 64;
 constexpr int kMaxCandGroups = kCandCap / kGroup;        // 256
 constexpr int kPairCap = 192;       // candidates ranked pairwise (else histogram levels)
+constexpr int kSmallPer = 8;        // spans per thread below which tau comes from the spans
 
 struct FastShared {
     double val[kCandCap];
@@ -784,7 +788,46 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         //    b* holding the kk-th largest, and tau is the smallest maximum in
         //    bins >= b* (bins are monotone in the value).
         double tau = -INFINITY;
-        if (kk <= m) {
+        if (n <= (int64_t)kThreads * kSmallPer) {
+            // few spans: the bound from one histogram level over the span
+            // scores themselves (the group maxima bound little when k is
+            // close to the group count): tau = the smallest score in the bins
+            // at or above the bin holding the kk-th largest
+            double sr[kSmallPer];
+#pragma unroll
+            for (int e = 0; e < kSmallPer; ++e) {
+                const int64_t i = tid + (int64_t)e * kThreads;
+                sr[e] = sc[i < n ? i : n - 1];
+            }
+            for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
+            double mn = INFINITY, mx = -INFINITY;
+            uint32_t dummy = 0;
+#pragma unroll
+            for (int e = 0; e < kSmallPer; ++e)
+                if (tid + (int64_t)e * kThreads < n) {
+                    mn = fmin(mn, sr[e]);
+                    mx = fmax(mx, sr[e]);
+                }
+            block_minmax_count(cm, mn, mx, dummy);
+            if (mn == mx) {
+                tau = mn;
+            } else {
+                const double inv = (double)kBins / (mx - mn);
+#pragma unroll
+                for (int e = 0; e < kSmallPer; ++e)
+                    if (tid + (int64_t)e * kThreads < n) atomicAdd(&f.hist[bin_of(sr[e], mn, inv, kBins)], 1u);
+                __syncthreads();
+                find_bin(cm, f.hist, kBins, kk);
+                const int bstar = cm.bstar;
+                double lo = INFINITY, unused = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < kSmallPer; ++e)
+                    if (tid + (int64_t)e * kThreads < n && bin_of(sr[e], mn, inv, kBins) >= bstar)
+                        lo = fmin(lo, sr[e]);
+                block_minmax_count(cm, lo, unused, dummy);
+                tau = lo;
+            }
+        } else if (kk <= m) {
             for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
             double mn = INFINITY, mx = -INFINITY;
             uint32_t dummy = 0;
