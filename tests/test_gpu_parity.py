@@ -360,6 +360,52 @@ def test_deterministic():
     assert np.array_equal(a["sel_step"], b["sel_step"])
 
 
+def test_reused_workspace_two_lengths():
+    """Decode steps and score-selects at two context lengths with the same
+    heads share one workspace, so every call starts from what the one before
+    left in it: each must give every span score (the caller's array starts as
+    NaN) and the selection the oracle gives, and a repeated step the same
+    output."""
+    import top_kv_cache_amd as rea
+    shapes = {"A": S(Hq=8, Hkv=2, d=128, T=300_000, S=32, topk=40, L=256, needles=2,
+                     kv_scaled=True),
+              "B": S(Hq=8, Hkv=2, d=128, T=120_000, S=32, topk=40, L=256, needles=2, seed=11)}
+    runs = {}
+    for key, w in shapes.items():
+        q, K, V = device_inputs(w)
+        st = rea.Step(q, K, V, w.G, w.S, w.topk, w.L, w.block_q, rope_theta=w.rope_theta)
+        q64 = synth.to_f32(w.q(0), w.dtype).astype(np.float64)
+        runs[key] = (w, st, [oracle_head(w, 0, h, q64) for h in range(w.Hkv)])
+    nbytes = max(max(st.sizes.ws_decode_step, st.sizes.ws_score_select)
+                 for _, st, _ in runs.values())
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+    ws = ws[(-ws.data_ptr()) % 256:]
+    first_out = {}
+    for i, key in enumerate(["A", "A", "B", "B", "A", "B"]):
+        w, st, ora = runs[key]
+        log(f"[reuse] call {i}: T={w.T} ({'score_select' if i % 2 else 'decode_step'})")
+        if i % 2:
+            sel, nsel, sc = st.score_select(span_scores=True, ws=ws)
+            sc = sc.cpu().numpy()
+            for h in range(w.Hkv):
+                ref = ora[h]["sc"][0]
+                assert not np.isnan(sc[0, h]).any(), ("unwritten span scores", key, h)
+                assert np.abs(sc[0, h] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+        else:
+            nb, cap = st.sizes.n_blocks, w.sel_cap
+            sel = torch.full((nb, w.Hkv, cap), -7, dtype=torch.int32, device="cuda")
+            nsel = torch.empty((nb, w.Hkv), dtype=torch.int32, device="cuda")
+            out = st.decode_step(sel=sel, nsel=nsel, ws=ws).cpu().numpy()
+            if key in first_out:
+                assert np.array_equal(out, first_out[key])
+            first_out.setdefault(key, out)
+        sel, nsel = sel.cpu().numpy(), nsel.cpu().numpy()
+        for h in range(w.Hkv):
+            exp = ora[h]["sel"][0]
+            assert int(nsel[0, h]) == len(exp)
+            assert sel[0, h, :len(exp)].tolist() == exp, (i, key, h)
+
+
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_config_one_layer(cfg):
     w = synth.config(cfg)

@@ -246,15 +246,19 @@ class Step:
         p = self.prob
         return p.n_q, p.n_q_heads, self.sizes.n_sel_heads, p.head_dim
 
-    def score_select(self, span_scores=False, stream=None):
+    def score_select(self, span_scores=False, stream=None, ws=None):
+        """rea_score_select; span scores (if asked for) start as NaN, so an
+        entry the library did not write shows.  ws: an aligned workspace of at
+        least sizes.ws_score_select bytes to reuse, else a new one."""
         torch = _torch()
         n_q, Hq, Hkv, d = self.shape
         nb, topk = self.sizes.n_blocks, self.sel_cap
         sel = torch.empty((nb, Hkv, max(topk, 1)), dtype=torch.int32, device=self.device)
         nsel = torch.empty((nb, Hkv), dtype=torch.int32, device=self.device)
-        sc = (torch.empty((nb, Hkv, max(self.sizes.n_spans, 1)), dtype=torch.float64,
-                          device=self.device) if span_scores else None)
-        ws = _aligned(_ws(self.sizes.ws_score_select, self.device))
+        sc = (torch.full((nb, Hkv, max(self.sizes.n_spans, 1)), float("nan"), dtype=torch.float64,
+                         device=self.device) if span_scores else None)
+        if ws is None:
+            ws = _aligned(_ws(self.sizes.ws_score_select, self.device))
         _check(lib().rea_score_select(ctypes.byref(self.prob), ctypes.byref(self.par),
                                       _ptr(sel), _ptr(nsel), _ptr(sc), _ptr(ws),
                                       ws.numel(), _stream(stream)))

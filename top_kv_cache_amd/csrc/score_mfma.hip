@@ -515,7 +515,7 @@ struct HeadsArgs {
     const unsigned char *k;     // K cache (bf16)
     const uint16_t *q;          // [Hq][D]: the step's one query
     double *out;                // [Hsel][n_spans] approximate span scores
-    double *kbar;               // [Hsel][n_spans] key-norm bounds
+    double *kbar;               // [Hp][n_spans] key-norm bounds (one per KV head)
     double *E;                  // [Hsel]
     double *gmx, *gkb;          // [Hsel][groups]: per 32 spans, largest score / norm bound
     int64_t sh_bytes, st_bytes, mid_lo, mid_hi, n_spans;
@@ -525,6 +525,9 @@ struct HeadsArgs {
 __global__ __launch_bounds__(256, 1) void k_score_heads_mfma(HeadsArgs a) {
     __shared__ __align__(16) unsigned char ring[kWavesM][kQNB][kTileBytes];
     __shared__ double gsl[2][kWavesM][32], gsk[2][kWavesM][32];
+    // a group's span scores and key-norm bounds, written out together after
+    // the group barrier (double-buffered by group parity)
+    __shared__ double sto[2][32][kGroupH + 1], skb[2][kGroupH];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hp = blockIdx.x / a.P, p = blockIdx.x % a.P;
@@ -680,10 +683,8 @@ __global__ __launch_bounds__(256, 1) void k_score_heads_mfma(HeadsArgs a) {
             // relative, squares below 2^-126 flushed
             const double kbv = sqrt((double)km * (1.0 + 0x1p-15) + 0x1p-119) * (1.0 + 1e-12);
             if (j < a.n_spans) {
-                if (kb == 0 && n < a.NH) {
-                    a.out[(h0 + n) * a.n_spans + j] = sm;
-                    a.kbar[(h0 + n) * a.n_spans + j] = kbv;
-                }
+                if (kb == 0 && n < a.NH) sto[grp & 1][n][sig] = sm;
+                if (lane == 0) skb[grp & 1][sig] = kbv;
                 gmax = fmax(gmax, sm);
                 gkmax = fmax(gkmax, kbv);
             }
@@ -707,6 +708,19 @@ __global__ __launch_bounds__(256, 1) void k_score_heads_mfma(HeadsArgs a) {
                     a.gmx[(h0 + n) * ng + grp] = m1;
                     a.gkb[(h0 + n) * ng + grp] = m2;
                 }
+                // the group's scores as 256 contiguous bytes per query head
+                // (one partial line per head at the middle's end), its
+                // key-norm bounds once for the KV head
+                const int64_t jb = grp * kGroupH;
+#pragma unroll
+                for (int r = 0; r < 32 * kGroupH / 256; ++r) {
+                    const int e = threadIdx.x + r * 256;
+                    const int n2 = e / kGroupH, sj = e % kGroupH;
+                    if (n2 < a.NH && jb + sj < a.n_spans)
+                        a.out[(h0 + n2) * a.n_spans + jb + sj] = sto[grp & 1][n2][sj];
+                }
+                if (threadIdx.x < kGroupH && jb + threadIdx.x < a.n_spans)
+                    a.kbar[(int64_t)hp * a.n_spans + jb + threadIdx.x] = skb[grp & 1][threadIdx.x];
                 gmax = -INFINITY;
                 gkmax = 0.0;
             }
@@ -751,6 +765,9 @@ struct CertArgs {
     int qpb;
     const uint16_t *q1;     // [Hsel][D] bf16 (qpb == 1)
     const double *gmx, *gkb;    // [pairs][groups] group maxima (k_cert_candidates_g)
+    // selection heads per kbar row: 1 (blocks: kbar per KV head and pair), or
+    // the query heads per KV head (decode per query head: one row per KV head)
+    int kbar_div;
 };
 
 // Span index of the pair's ranked span at position c.
@@ -930,7 +947,7 @@ __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh,
     const int64_t n = a.n_spans;
     const int kk = a.kk;
     const double *shat = a.shat + bh * n;
-    const double *kbar = a.kbar + (int64_t)h * n;
+    const double *kbar = a.kbar + (int64_t)(h / (a.kbar_div > 1 ? a.kbar_div : 1)) * n;
     const double Eb = a.E[bh];
     int32_t *sel = a.sel ? a.sel + bh * a.topk : nullptr;
     if (tid == 0) a.nsel[bh] = kk;
@@ -1494,7 +1511,7 @@ __global__ __launch_bounds__(kPThreads) void k_cert_candidates(CertArgs a) {
         return;
     }
     const double *shat = a.shat + bh * n;
-    const double *kbar = a.kbar + (int64_t)h * n;
+    const double *kbar = a.kbar + (int64_t)(h / (a.kbar_div > 1 ? a.kbar_div : 1)) * n;
 
     // range of the scores, largest key norm
     double mn = INFINITY, mx = -INFINITY, km = 0.0;
@@ -1812,6 +1829,7 @@ hipError_t launch_score_select_mfma(const Geom &g, const void *q, const void *k,
     ca.R = cert_ways(g);
     ca.qpb = kQB;
     ca.q1 = nullptr;
+    ca.kbar_div = 1;
     ca.gmx = nullptr;
     ca.gkb = nullptr;
     const unsigned pairs = (unsigned)(g.n_blk * g.Hkv);
@@ -1864,7 +1882,7 @@ bool heads_mfma_path(const Geom &g) {
 size_t heads_ws_bytes(const Geom &g) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t ng = (size_t)((g.n_spans + kGroupH - 1) / kGroupH);
-    return al((size_t)g.Hkv * g.n_spans * sizeof(double)) +            // key-norm bounds
+    return al((size_t)(g.Hkv / g.rep) * g.n_spans * sizeof(double)) + // key-norm bounds, per KV head
            al((size_t)g.Hkv * sizeof(double)) +                        // E
            2 * al((size_t)g.Hkv * ng * sizeof(double)) +               // group maxima
            cert_many_bytes(g);                                         // candidates, fallback
@@ -1878,7 +1896,7 @@ hipError_t launch_score_select_heads(const Geom &g, const void *q, const void *k
     const size_t ng = (size_t)((g.n_spans + kGroupH - 1) / kGroupH);
     char *p = (char *)ws;
     double *kbar = (double *)p;
-    p += al((size_t)g.Hkv * g.n_spans * sizeof(double));
+    p += al((size_t)(g.Hkv / g.rep) * g.n_spans * sizeof(double));
     double *E = (double *)p;
     p += al((size_t)g.Hkv * sizeof(double));
     double *gmx = (double *)p;
@@ -1934,6 +1952,7 @@ hipError_t launch_score_select_heads(const Geom &g, const void *q, const void *k
     ca.q1 = (const uint16_t *)q;
     ca.gmx = gmx;
     ca.gkb = gkb;
+    ca.kbar_div = g.rep;
     const unsigned pairs = (unsigned)(g.n_blk * g.Hkv);
     const bool many = g.n_spans > kCCap;
     double *fb_gmax = nullptr;
