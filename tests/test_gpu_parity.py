@@ -88,6 +88,10 @@ SMALL = {
     # path streams the group maxima instead of holding them in registers
     "bf16_token_level_33k_groups": S(Hq=2, Hkv=1, d=64, T=1_060_000, S=1, topk=300, L=64,
                                      needles=2),
+    # 65536 spans in 2048 groups, k = 256, needles stretching the score
+    # range: the top-k's first bound keeps more groups than it can hold, so
+    # the bound becomes the 256-th largest group maximum
+    "bf16_k256_2048_groups": S(Hq=2, Hkv=1, d=64, T=262_144, S=4, topk=256, L=64, needles=4),
     # token segments: the best tokens, each widened to S tokens
     "seg_bf16_d64": S(S=8, topk=6, T=700, token_segments=True),
     "seg_bf16_d128_pqh": S(Hq=8, Hkv=2, d=128, T=2048, S=32, topk=12, L=256, needles=2,

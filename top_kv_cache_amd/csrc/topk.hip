@@ -857,20 +857,49 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             }
         }
         // candidate groups: maximum >= tau
-        if (tid == 0) cm.count = 0;
-        __syncthreads();
-        // (about k appends: one LDS atomic each is cheaper than the ballots)
+        uint32_t ncg = 0;
+        for (int pass = 0;; ++pass) {
+            if (tid == 0) cm.count = 0;
+            __syncthreads();
+            // (about k appends: one LDS atomic each is cheaper than the ballots)
 #pragma unroll
-        for (int e = 0; e < GPT; ++e) {
-            const int i = tid + e * kThreads;
-            if (i < m && gr[e] >= tau) {
-                const uint32_t slot = atomicAdd(&cm.count, 1u);
-                if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
+            for (int e = 0; e < GPT; ++e) {
+                const int i = tid + e * kThreads;
+                if (i < m && gr[e] >= tau) {
+                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
+                }
             }
+            __syncthreads();
+            ncg = cm.count;
+            __syncthreads();
+            if (pass > 0 || ncg <= (uint32_t)kMaxCandGroups || n <= (int64_t)kThreads * kSmallPer ||
+                kk > m)
+                break;
+            // One histogram level left every group of the kk-th largest
+            // maximum's bin above tau, more than the candidate capacity (a
+            // wide bin: a few far larger maxima stretch the range).  tau
+            // becomes the kk-th largest group maximum itself, ranked among
+            // the groups at or above the first bound; it still bounds the
+            // kk-th largest span score from below (the kk best groups each
+            // hold a span at their maximum).
+            if (tid == 0) cm.count = 0;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < GPT; ++e) {
+                const int i = tid + e * kThreads;
+                if (i < m && gr[e] >= tau) {
+                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    f.val[slot] = gr[e];
+                    f.idx[slot] = i;
+                }
+            }
+            __syncthreads();
+            const uint32_t cnt = cm.count;
+            __syncthreads();
+            find_kth(cm, f.hist, f.val, f.idx, cnt, kk);
+            tau = cm.cut_v;
         }
-        __syncthreads();
-        const uint32_t ncg = cm.count;
-        __syncthreads();
         if (ncg <= (uint32_t)kMaxCandGroups) {
             // 2. their spans with score >= tau; half a wave per group, every
             //    load issued before any is used (addresses clamped in range)
