@@ -497,17 +497,19 @@ __global__ __launch_bounds__(256, 2) void k_score_mfma(MfmaArgs a) {
 // decides the top-k exactly (one query per pair: its fp64 re-scoring runs in
 // k_certify_one).
 //
-// grid (Hp * P), 256 threads, one workgroup per CU: workgroup (hp, p) takes a
+// grid (Hp * P), 256 threads, two workgroups per CU: workgroup (hp, p) takes a
 // contiguous run of KV head hp's groups of 32 spans.  Within a group, wave w
 // scores spans w, w + 4, ..., so the four waves stream adjacent spans, each
 // through its own LDS ring of kQNB tiles filled by DMA (global_load_lds;
 // 16-byte chunk c of token row m at slot c ^ (m % 16), as in k_score_mfma).
-// The only barrier is one per group, where the waves' group maxima are
-// combined in LDS.  The DMA loads carry the non-temporal cache policy: the
-// keys are read once, and keeping them out of the caches' normal replacement
-// raises the read rate markedly on this pattern.
+// No barrier couples the waves: each writes its own spans' results and its
+// own maxima of each group (gmx / gkb hold one per wave; the candidate pass
+// takes their maximum), so a wave never stops issuing loads to wait for the
+// others.  The DMA loads carry the non-temporal cache policy: the keys are
+// read once, and keeping them out of the caches' normal replacement raises
+// the read rate markedly on this pattern.
 // ---------------------------------------------------------------------------
-constexpr int kQNB = 3;
+constexpr int kQNB = 2;
 constexpr int kGroupH = 32;         // spans per group
 constexpr double kGammaHeads = 128.0 * 1.1920928955078125e-07 * (1.0 + 1e-4);   // 128 * 2^-23
 
@@ -517,17 +519,13 @@ struct HeadsArgs {
     double *out;                // [Hsel][n_spans] approximate span scores
     double *kbar;               // [Hp][n_spans] key-norm bounds (one per KV head)
     double *E;                  // [Hsel]
-    double *gmx, *gkb;          // [Hsel][groups]: per 32 spans, largest score / norm bound
+    double *gmx, *gkb;          // [Hsel][groups][4]: per 32 spans and wave, largest score / norm bound
     int64_t sh_bytes, st_bytes, mid_lo, mid_hi, n_spans;
     int S, NH, Hp, P;
 };
 
-__global__ __launch_bounds__(256, 1) void k_score_heads_mfma(HeadsArgs a) {
+__global__ __launch_bounds__(256, 2) void k_score_heads_mfma(HeadsArgs a) {
     __shared__ __align__(16) unsigned char ring[kWavesM][kQNB][kTileBytes];
-    __shared__ double gsl[2][kWavesM][32], gsk[2][kWavesM][32];
-    // a group's span scores and key-norm bounds, written out together after
-    // the group barrier (double-buffered by group parity)
-    __shared__ double sto[2][32][kGroupH + 1], skb[2][kGroupH];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hp = blockIdx.x / a.P, p = blockIdx.x % a.P;
@@ -565,8 +563,9 @@ __global__ __launch_bounds__(256, 1) void k_score_heads_mfma(HeadsArgs a) {
     const int64_t first = g0;
     const int64_t n_grp = g1 - g0;
     const int tps = a.S / kTile;
-    // every wave runs the same number of group steps (8 span slots per group,
-    // slots past the middle's last span masked) so the group barrier matches
+    // every wave runs 8 span slots of every group (slots past the middle's
+    // last span read a clamped row and are masked), so it writes its maxima
+    // slot of every group
     const int64_t n_tiles = n_grp * (kGroupH / kWavesM) * tps;
     const unsigned char *kh = a.k + (int64_t)hp * a.sh_bytes;
     unsigned char *rw = &ring[wave][0][0];
@@ -683,8 +682,8 @@ __global__ __launch_bounds__(256, 1) void k_score_heads_mfma(HeadsArgs a) {
             // relative, squares below 2^-126 flushed
             const double kbv = sqrt((double)km * (1.0 + 0x1p-15) + 0x1p-119) * (1.0 + 1e-12);
             if (j < a.n_spans) {
-                if (kb == 0 && n < a.NH) sto[grp & 1][n][sig] = sm;
-                if (lane == 0) skb[grp & 1][sig] = kbv;
+                if (kb == 0 && n < a.NH) a.out[(h0 + n) * a.n_spans + j] = sm;
+                if (lane == 0) a.kbar[(int64_t)hp * a.n_spans + j] = kbv;
                 gmax = fmax(gmax, sm);
                 gkmax = fmax(gkmax, kbv);
             }
@@ -692,35 +691,9 @@ __global__ __launch_bounds__(256, 1) void k_score_heads_mfma(HeadsArgs a) {
             kn_run = 0.f;
             if (sig + kWavesM >= kGroupH) {      // this wave's last slot of the group
                 if (kb == 0 && n < a.NH) {
-                    gsl[grp & 1][wave][n] = gmax;
-                    gsk[grp & 1][wave][n] = gkmax;
+                    a.gmx[((h0 + n) * ng + grp) * kWavesM + wave] = gmax;
+                    a.gkb[((h0 + n) * ng + grp) * kWavesM + wave] = gkmax;
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-                if (wave == 0 && kb == 0 && n < a.NH) {
-                    double m1 = gsl[grp & 1][0][n], m2 = gsk[grp & 1][0][n];
-#pragma unroll
-                    for (int w = 1; w < kWavesM; ++w) {
-                        m1 = fmax(m1, gsl[grp & 1][w][n]);
-                        m2 = fmax(m2, gsk[grp & 1][w][n]);
-                    }
-                    a.gmx[(h0 + n) * ng + grp] = m1;
-                    a.gkb[(h0 + n) * ng + grp] = m2;
-                }
-                // the group's scores as 256 contiguous bytes per query head
-                // (one partial line per head at the middle's end), its
-                // key-norm bounds once for the KV head
-                const int64_t jb = grp * kGroupH;
-#pragma unroll
-                for (int r = 0; r < 32 * kGroupH / 256; ++r) {
-                    const int e = threadIdx.x + r * 256;
-                    const int n2 = e / kGroupH, sj = e % kGroupH;
-                    if (n2 < a.NH && jb + sj < a.n_spans)
-                        a.out[(h0 + n2) * a.n_spans + jb + sj] = sto[grp & 1][n2][sj];
-                }
-                if (threadIdx.x < kGroupH && jb + threadIdx.x < a.n_spans)
-                    a.kbar[(int64_t)hp * a.n_spans + jb + threadIdx.x] = skb[grp & 1][threadIdx.x];
                 gmax = -INFINITY;
                 gkmax = 0.0;
             }
@@ -1281,6 +1254,7 @@ __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, i
 // ascending, are the candidates.  More than kGCand such groups or kCCap such
 // spans flag the pair for the exact fallback.
 // ---------------------------------------------------------------------------
+typedef double double4v __attribute__((ext_vector_type(4)));
 constexpr int kGThreads = 512;
 constexpr int kGPT = 8;                       // group maxima per thread
 constexpr int kGMaxGroups = kGThreads * kGPT; // 4096 groups (131,072 spans)
@@ -1316,15 +1290,21 @@ __global__ __launch_bounds__(kGThreads) void k_cert_candidates_g(CertArgs a) {
         flag_over();
         return;
     }
-    const double *gm = a.gmx + bh * m;
-    const double *gk = a.gkb + bh * m;
+    const double *gm = a.gmx + bh * m * kWavesM;      // [groups][4 waves]
+    const double *gk = a.gkb + bh * m * kWavesM;
     double gv[kGPT];
     double mn = INFINITY, mx = -INFINITY, km = 0.0;
 #pragma unroll
     for (int r = 0; r < kGPT; ++r) {
         const int64_t g = (int64_t)r * kGThreads + tid;
-        gv[r] = g < m ? gm[g] : -INFINITY;
-        km = fmax(km, g < m ? gk[g] : 0.0);
+        if (g < m) {
+            const double4v x = *(const double4v *)(gm + g * kWavesM);
+            const double4v y = *(const double4v *)(gk + g * kWavesM);
+            gv[r] = fmax(fmax(x[0], x[1]), fmax(x[2], x[3]));
+            km = fmax(km, fmax(fmax(y[0], y[1]), fmax(y[2], y[3])));
+        } else {
+            gv[r] = -INFINITY;
+        }
     }
 #pragma unroll
     for (int r = 0; r < kGPT; ++r)
@@ -1884,7 +1864,7 @@ size_t heads_ws_bytes(const Geom &g) {
     const size_t ng = (size_t)((g.n_spans + kGroupH - 1) / kGroupH);
     return al((size_t)(g.Hkv / g.rep) * g.n_spans * sizeof(double)) + // key-norm bounds, per KV head
            al((size_t)g.Hkv * sizeof(double)) +                        // E
-           2 * al((size_t)g.Hkv * ng * sizeof(double)) +               // group maxima
+           2 * al((size_t)g.Hkv * ng * kWavesM * sizeof(double)) +     // group maxima per wave
            cert_many_bytes(g);                                         // candidates, fallback
 }
 
@@ -1900,9 +1880,9 @@ hipError_t launch_score_select_heads(const Geom &g, const void *q, const void *k
     double *E = (double *)p;
     p += al((size_t)g.Hkv * sizeof(double));
     double *gmx = (double *)p;
-    p += al((size_t)g.Hkv * ng * sizeof(double));
+    p += al((size_t)g.Hkv * ng * kWavesM * sizeof(double));
     double *gkb = (double *)p;
-    p += al((size_t)g.Hkv * ng * sizeof(double));
+    p += al((size_t)g.Hkv * ng * kWavesM * sizeof(double));
 
     HeadsArgs ha;
     ha.k = (const unsigned char *)k;
@@ -1920,8 +1900,8 @@ hipError_t launch_score_select_heads(const Geom &g, const void *q, const void *k
     ha.S = g.S;
     ha.NH = g.rep;
     ha.Hp = g.Hkv / g.rep;
-    // one workgroup per CU, split evenly over the KV heads (runs of whole groups)
-    int64_t P = ((int64_t)(num_cu > 0 ? num_cu : 256) + ha.Hp - 1) / ha.Hp;
+    // two workgroups per CU, split evenly over the KV heads (runs of whole groups)
+    int64_t P = ((int64_t)(num_cu > 0 ? num_cu : 256) * 2 + ha.Hp - 1) / ha.Hp;
     if (P > (int64_t)ng) P = (int64_t)ng;
     if (P < 1) P = 1;
     ha.P = (int)P;
