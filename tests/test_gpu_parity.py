@@ -355,6 +355,40 @@ def test_mfma_blocks_massive_ties_past_4096_spans():
         compare_head(w, gpu, ora, h)
 
 
+def test_per_query_head_massive_ties_past_4096_spans():
+    """One selection per query head, beyond 4096 spans, every span but 20 per
+    KV head scoring exactly alike: the candidate spans near the k-th score
+    would be nearly all of them, so every pair takes the exact fallback (fp64
+    scores on the VALU, then the ordinary top-k); the raised spans and the
+    lowest indices of the tie must be selected for each query head."""
+    rng = np.random.default_rng(5151)
+    w = S(Hq=8, Hkv=2, d=128, T=140000, S=32, topk=50, L=128, needles=0, per_q_head=True)
+    assert w.n_spans > 4096
+    qn = rng.integers(0, 2, size=(w.n_q, w.Hq, w.d)).astype(np.float32)
+    qn[..., 0] = 1.0                            # every query head sums above zero
+    pattern = rng.integers(0, 3, size=(w.S, w.d)).astype(np.float32)
+    Kn = np.zeros((w.Hkv, w.T, w.d), np.float32)
+    lo, hi = w.mid
+    n_full = (hi - lo) // w.S
+    Kn[:, lo:lo + n_full * w.S] = np.tile(pattern, (n_full, 1))[None]
+    for h in range(w.Hkv):
+        for j in rng.choice(w.n_spans - 1, size=20, replace=False):
+            Kn[h, lo + j * w.S:lo + (j + 1) * w.S] = pattern + 1.0
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    gpu = run_library(w, to_bf(qn), to_bf(Kn), to_bf(Vn))
+    q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
+    for h in range(w.Hq):
+        hp = h // w.g
+        ora = oracle_head(w, 0, h, q64, K64[hp:hp + 1], V64[hp:hp + 1])
+        sc = ora["sc"][0]
+        kth = np.sort(sc)[::-1][w.topk - 1]
+        assert int((sc > kth).sum()) == 20 and int((sc == kth).sum()) > 4096
+        compare_head(w, gpu, ora, h)
+
+
 def test_deterministic():
     w = SMALL["bf16_many_heads"]
     q, K, V = device_inputs(w)

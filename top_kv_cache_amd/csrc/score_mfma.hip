@@ -737,7 +737,7 @@ struct CertArgs {
     // decode step per query head; re-scored in k_certify_tail from q1)
     int qpb;
     const uint16_t *q1;     // [Hsel][D] bf16 (qpb == 1)
-    const double *gmx, *gkb;    // [pairs][groups] group maxima (k_cert_candidates_g)
+    const double *gmx, *gkb;    // [pairs][groups][4] per-wave group maxima (k_certify_heads)
     // selection heads per kbar row: 1 (blocks: kbar per KV head and pair), or
     // the query heads per KV head (decode per query head: one row per KV head)
     int kbar_div;
@@ -767,7 +767,23 @@ struct CertShared {
     int32_t bstar, cut_j;
     double cut_v;
     double q1[kD];                  // the pair's query in fp64 (one query per pair)
+    int32_t cand[kCCap];            // k_certify_heads: the pair's candidate spans, ascending
+    uint32_t ncand;
 };
+
+// Span index of ranked position c, and the number of ranked spans: from the
+// candidate list in LDS (L, k_certify_heads) or as span_at / ranked.
+template <bool L>
+__device__ __forceinline__ int32_t span_of(const CertArgs &a, const CertShared &sh, int64_t bh,
+                                           int64_t c) {
+    if constexpr (L) return sh.cand[c];
+    return span_at(a, bh, c);
+}
+template <bool L>
+__device__ __forceinline__ int64_t ranked_of(const CertArgs &a, const CertShared &sh, int64_t bh) {
+    if constexpr (L) return (int64_t)sh.ncand;
+    return ranked(a, bh);
+}
 
 __device__ __forceinline__ int c_bin(double x, double mn, double inv) {
     const double f = floor((x - mn) * inv);
@@ -913,6 +929,7 @@ __device__ __forceinline__ double cert_eps(double Eb, double kb, double s) {
 // certainly in (sh.bitmap, nd of them), certainly out, or uncertain (sh.xs,
 // nx of them).  Returns false when the pair needs no ranking at all (kk == 0
 // or kk >= n_spans; sel is then written).
+template <bool L = false>
 __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh, int64_t bh,
                                               uint32_t &nx_out, uint32_t &nd_out) {
     const int tid = threadIdx.x;
@@ -933,7 +950,7 @@ __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh,
     // their approximate scores and error bounds, every load in flight
     // together (kCPer per thread), kept in registers for the three passes
     // below; position c holds span jv
-    const int64_t m = ranked(a, bh);
+    const int64_t m = ranked_of<L>(a, sh, bh);
     double sv[kCPer], ev[kCPer];
     int32_t jv[kCPer];
     {
@@ -941,7 +958,7 @@ __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh,
 #pragma unroll
         for (int e = 0; e < kCPer; ++e) {
             const int64_t c = tid + (int64_t)e * kCThreads;
-            jv[e] = c < m ? span_at(a, bh, c) : 0;
+            jv[e] = c < m ? span_of<L>(a, sh, bh, c) : 0;
         }
 #pragma unroll
         for (int e = 0; e < kCPer; ++e) {
@@ -1126,6 +1143,7 @@ __device__ __forceinline__ void cert_rescore(const CertArgs &a, Sh &sh, int64_t 
 // sh.xv, a wave per span; lane (token tl of a 32-token chunk, channel half kb)
 // takes 64 products of its token (bf16 values are exact in fp64), the halves
 // are added across lane^32 and the maximum taken over the 32 token lanes.
+template <bool L = false>
 __device__ __forceinline__ void cert_rescore_one(const CertArgs &a, CertShared &sh, int64_t bh,
                                                  uint32_t nx) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1136,7 +1154,7 @@ __device__ __forceinline__ void cert_rescore_one(const CertArgs &a, CertShared &
     const int tl = lane & 31, kb = lane >> 5;
     const unsigned char *kh = a.k + (int64_t)(h / a.rep) * a.sh_bytes;
     for (uint32_t x = wave; x < nx; x += kCWaves) {
-        const int64_t j = span_at(a, bh, sh.xs[x]);
+        const int64_t j = span_of<L>(a, sh, bh, sh.xs[x]);
         const int64_t tb = a.mid_lo + j * a.S, te = min(tb + (int64_t)a.S, a.mid_hi);
         double best = -INFINITY;
         for (int64_t c0 = tb; c0 < te; c0 += 32) {
@@ -1185,17 +1203,18 @@ __device__ __forceinline__ void cert_gather_xv(CertShared &sh, const double *gpa
 
 // The need best uncertain spans (sh.xv, sh.xs) join the certain ones in
 // sh.bitmap, and the bitmap is compacted in span order into sel.
+template <bool L = false>
 __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, int64_t bh,
                                             uint32_t nx, int64_t need) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kk = a.kk;
-    const int nwords = (int)((ranked(a, bh) + 31) / 32);
+    const int nwords = (int)((ranked_of<L>(a, sh, bh) + 31) / 32);
     int32_t *sel = a.sel ? a.sel + bh * a.topk : nullptr;
     if (need > 0) {
         // ranked by exact score, then span index
         for (uint32_t x = tid; x < nx; x += kCThreads) {
             sh.val[x] = sh.xv[x];
-            sh.idx[x] = span_at(a, bh, sh.xs[x]);
+            sh.idx[x] = span_of<L>(a, sh, bh, sh.xs[x]);
         }
         __syncthreads();
         c_find_kth(sh, nx, need);
@@ -1234,7 +1253,7 @@ __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, i
             while (w) {
                 const int bit = __ffs(w) - 1;
                 w &= w - 1;
-                if (pos < (uint32_t)a.topk) sel[pos] = span_at(a, bh, tid * 32 + bit);
+                if (pos < (uint32_t)a.topk) sel[pos] = span_of<L>(a, sh, bh, tid * 32 + bit);
                 ++pos;
             }
             for (int64_t i = (int64_t)kk + tid; i < a.topk; i += kCThreads) sel[i] = -1;
@@ -1243,10 +1262,10 @@ __device__ __forceinline__ void cert_finish(const CertArgs &a, CertShared &sh, i
 }
 
 // ---------------------------------------------------------------------------
-// k_cert_candidates_g: grid (pairs), 512 threads; the candidate spans of a
-// pair with more than kCCap spans from the group maxima the scoring kernel
-// wrote (largest approximate score and largest key-norm bound of every 32
-// spans).  The (kk+1)-th largest group maximum tau is a lower bound of the
+// Candidates of a decode pair with one selection per query head and more than
+// kCCap spans (k_certify_heads, first part), from the group maxima the
+// scoring kernel wrote (largest approximate score and largest key-norm bound
+// of every 32 spans, one of each per wave).  The (kk+1)-th largest group maximum tau is a lower bound of the
 // (kk+1)-th largest score c' (the kk+1 best groups hold kk+1 distinct spans at
 // or above it), so theta = tau - 2 eps_max <= c' - 2 eps_max and every span
 // scoring below theta is certainly out (see k_cert_candidates).  Only the
@@ -1260,10 +1279,19 @@ constexpr int kGPT = 8;                       // group maxima per thread
 constexpr int kGMaxGroups = kGThreads * kGPT; // 4096 groups (131,072 spans)
 constexpr int kGCand = 256;                   // candidate groups
 
-__global__ __launch_bounds__(kGThreads) void k_cert_candidates_g(CertArgs a) {
+// k_certify_heads: grid (pairs), 512 threads (kCThreads == kGThreads): the
+// candidates as above, then k_certify_one's steps.  The candidate spans go to
+// LDS (sh.cand) and
+// the classification, re-scoring and output read them there, so neither the
+// list nor its count makes a round trip through global memory.  The pair's
+// gover flag is written as before; a flagged pair returns at once (the exact
+// fallback selects it).
+__global__ __launch_bounds__(kCThreads) void k_certify_heads(CertArgs a) {
+    __shared__ CertShared sh;
     __shared__ uint32_t hist[kCBins];
     __shared__ double red[3][kGThreads / 64];
     __shared__ uint32_t wsum[kGThreads / 64];
+    __shared__ uint32_t wsum8[kGPT][kGThreads / 64];
     __shared__ int32_t cgrp[kGCand];
     __shared__ uint32_t cword[kGCand];
     __shared__ int32_t s_bstar;
@@ -1274,22 +1302,18 @@ __global__ __launch_bounds__(kGThreads) void k_cert_candidates_g(CertArgs a) {
     const int64_t m = (n + kGroupH - 1) / kGroupH;
     const int kk = a.kk;
     auto flag_over = [&]() {
-        if (tid == 0) {
-            a.gncand[bh] = 0;
-            a.gover[bh] = 1;
-        }
+        if (tid == 0) a.gover[bh] = 1;
     };
+    bool listed = false;         // candidates in sh.cand (else nothing to rank)
     if (kk == 0 || kk >= n) {
-        if (tid == 0) {
-            a.gncand[bh] = 0;
-            a.gover[bh] = 0;
-        }
-        return;
-    }
-    if (m > kGMaxGroups || (int64_t)kk + 1 > m) {
+        if (tid == 0) a.gover[bh] = 0;
+    } else if (m > kGMaxGroups || (int64_t)kk + 1 > m) {
         flag_over();
         return;
+    } else {
+        listed = true;
     }
+    if (listed) {
     const double *gm = a.gmx + bh * m * kWavesM;      // [groups][4 waves]
     const double *gk = a.gkb + bh * m * kWavesM;
     double gv[kGPT];
@@ -1386,25 +1410,29 @@ __global__ __launch_bounds__(kGThreads) void k_cert_candidates_g(CertArgs a) {
     theta -= 4e-16 * fabs(theta) + 1e-300;
 
     // candidate groups: maximum >= theta, ascending
-    uint32_t ncg = 0;
+    // (every batch's ballots first, then one barrier for all their counts)
+    uint64_t bal[kGPT];
 #pragma unroll
     for (int r = 0; r < kGPT; ++r) {
         const int64_t g = (int64_t)r * kGThreads + tid;
-        const bool keep = g < m && gv[r] >= theta;
-        const uint64_t bal = __ballot(keep);
-        const uint32_t before = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        __syncthreads();
-        if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
-        __syncthreads();
+        bal[r] = __ballot(g < m && gv[r] >= theta);
+        if (lane == 0) wsum8[r][wave] = (uint32_t)__popcll(bal[r]);
+    }
+    __syncthreads();
+    uint32_t ncg = 0;
+#pragma unroll
+    for (int r = 0; r < kGPT; ++r) {
         uint32_t off = 0, tot = 0;
         for (int w = 0; w < NW; ++w) {
-            off += w < wave ? wsum[w] : 0u;
-            tot += wsum[w];
+            off += w < wave ? wsum8[r][w] : 0u;
+            tot += wsum8[r][w];
         }
-        const uint32_t pos = ncg + off + before;
-        if (keep && pos < (uint32_t)kGCand) cgrp[pos] = (int32_t)g;
+        const uint32_t pos = ncg + off + (uint32_t)__popcll(bal[r] & ((1ull << lane) - 1ull));
+        if (((bal[r] >> lane) & 1ull) && pos < (uint32_t)kGCand)
+            cgrp[pos] = (int32_t)((int64_t)r * kGThreads + tid);
         ncg += tot;
     }
+    __syncthreads();
     if (ncg > (uint32_t)kGCand) {
         flag_over();
         return;
@@ -1441,17 +1469,24 @@ __global__ __launch_bounds__(kGThreads) void k_cert_candidates_g(CertArgs a) {
         return;
     }
     uint32_t pos = base + x - v0;
-    int32_t *cand = a.gcand + bh * kCCap;
     uint32_t w = wv;
     while (w) {
         const int bit = __ffs(w) - 1;
         w &= w - 1;
-        cand[pos++] = cgrp[tid] * kGroupH + bit;
+        sh.cand[pos++] = cgrp[tid] * kGroupH + bit;
     }
     if (tid == 0) {
-        a.gncand[bh] = total;
+        sh.ncand = total;
         a.gover[bh] = 0;
     }
+    }   // listed
+    __syncthreads();
+    uint32_t nx, nd;
+    if (!cert_classify<true>(a, sh, bh, nx, nd)) return;
+    const int64_t need = (int64_t)a.kk - nd;
+    if (need > 0) cert_rescore_one<true>(a, sh, bh, nx);
+    __syncthreads();
+    cert_finish<true>(a, sh, bh, nx, need);
 }
 
 // ---------------------------------------------------------------------------
@@ -1944,12 +1979,13 @@ hipError_t launch_score_select_heads(const Geom &g, const void *q, const void *k
         ca.gover = (uint32_t *)p;
         p += al((size_t)pairs * sizeof(uint32_t));
         fb_gmax = (double *)p;
-        if ((e = launch_struct(k_cert_candidates_g, dim3(pairs), dim3(kGThreads), 0, s, ca)) !=
+        if ((e = launch_struct(k_certify_heads, dim3(pairs), dim3(kCThreads), 0, s, ca)) !=
             hipSuccess)
             return e;
-    }
-    if ((e = launch_struct(k_certify_one, dim3(pairs), dim3(kCThreads), 0, s, ca)) != hipSuccess)
+    } else if ((e = launch_struct(k_certify_one, dim3(pairs), dim3(kCThreads), 0, s, ca)) !=
+               hipSuccess) {
         return e;
+    }
     if (!many) return hipSuccess;
     // flagged pairs: exact fp64 scores on the VALU, then the ordinary top-k
     if ((e = launch_score(g, q, k, span_scores, fb_gmax, num_cu, s, nullptr, nullptr, ca.gover)) !=
