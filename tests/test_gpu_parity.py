@@ -45,6 +45,10 @@ SMALL = {
     "f32_L1": S(dtype="f32", L=1, T=400, topk=4),
     "bf16_many_heads": S(Hq=32, Hkv=8, d=128, T=2048, S=32, topk=12, L=256, needles=2,
                          kv_scaled=True),
+    # 3 query heads per KV head (the 3B shape's group): 3 query rows in the
+    # fused decode attention
+    "bf16_g3_d128": S(Hq=6, Hkv=2, d=128, T=3000, S=32, topk=12, L=256, needles=2,
+                      kv_scaled=True),
     # blocks of 64 bf16 queries, d 128: scored on MFMA, certified top-k
     "bf16_mfma_blocks": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,
                           L=128, needles=0),

@@ -534,6 +534,9 @@ template <typename TIn, int D>
 hipError_t launch_qr(const Geom &g, const FusedArgs &a, hipStream_t s) {
     if (a.QR == 1) return launch_typed<TIn, D, 1>(g, a, s);
     if (a.QR == 2) return launch_typed<TIn, D, 2>(g, a, s);
+    // 3 query rows (e.g. 24 query heads over 8 KV heads): a fourth row would be
+    // a quarter more logit and P.V work for nothing
+    if (a.QR == 3) return launch_typed<TIn, D, 3>(g, a, s);
     return a.QR <= 4 ? launch_typed<TIn, D, 4>(g, a, s) : launch_typed<TIn, D, 8>(g, a, s);
 }
 
