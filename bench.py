@@ -281,7 +281,8 @@ def batch_main(args):
 
 def read_ceiling_main(args):
     """HBM read ceiling: rea_probe_stream_read (the scoring kernel's load
-    instruction and nothing else) over a 2 GiB buffer, for 1-8 workgroups per
+    instruction and nothing else) over a 2 GiB buffer (or --read-mib reads
+    rotating over buffers totalling 2 GiB), for 1-8 workgroups per
     CU and 4-16 loads in flight per wave; every shape timed with HIP events
     on the launch stream over args.steps launches after args.warmup.  One
     JSON line with the best rate and the table."""
@@ -289,21 +290,24 @@ def read_ceiling_main(args):
     import top_kv_cache_amd as rea
 
     dev = torch.device("cuda:0")
-    nbytes = 2 << 30
-    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    # one read of nbytes per launch; launches rotate over a pool of at least
+    # 2 GiB, so that no read finds its buffer in the 256 MB Infinity Cache
+    nbytes = (args.read_mib << 20) if args.read_mib > 0 else (2 << 30)
+    n_buf = max(1, -(-(2 << 30) // nbytes))
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(n_buf)]
     cu = rea.lib().rea_probe_cu_count()
     sink = torch.empty(16 * cu, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     table = []
     for wpc in (1, 2, 4, 8):
         for lif in (4, 8, 16):
-            for _ in range(args.warmup):
-                rea.probe_stream_read(buf, wpc, lif, sink, stream)
+            for i in range(args.warmup):
+                rea.probe_stream_read(bufs[i % n_buf], wpc, lif, sink, stream)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for _ in range(args.steps):
-                rea.probe_stream_read(buf, wpc, lif, sink, stream)
+            for i in range(args.steps):
+                rea.probe_stream_read(bufs[i % n_buf], wpc, lif, sink, stream)
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / args.steps
@@ -318,7 +322,8 @@ def read_ceiling_main(args):
         "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
         "dtype": "u32", "data": "synthetic", "peak": HBM_PEAK_GBS,
         "frac": best["GBps"] / HBM_PEAK_GBS, "bytes": nbytes, "best": best, "table": table,
-        "config": {"workload": "stream-read-2GiB", "cu": cu}}), flush=True)
+        "config": {"workload": f"stream-read-{nbytes >> 20}MiB", "buffers": n_buf, "cu": cu}}),
+        flush=True)
 
 
 def main():
@@ -343,6 +348,9 @@ def main():
                     help="with --batch: lengths spread over [context/2, context]")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="instead: the HBM read ceiling of the scoring kernel's load pattern")
+    ap.add_argument("--read-mib", type=int, default=0,
+                    help="with --read-ceiling: MiB per read (default 2048; smaller reads rotate "
+                         "over buffers totalling 2 GiB)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="with --config: context before the queries (T = tokens + queries)")
     ap.add_argument("--queries", type=int, default=0,

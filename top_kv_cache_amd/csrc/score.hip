@@ -21,7 +21,9 @@
 // rows, contiguous; loads are non-temporal (the cache is touched once); up to
 // 32 rows per wave are loaded before any arithmetic.  Partial dot products
 // are summed across a row's lanes with DPP quad-permute and mirror moves
-// (symmetric pairings, so every lane ends with identical bits).  Each
+// (symmetric pairings, so every lane of a row ends with identical bits); for
+// bf16 rows of 128 elements the two halves of the 16 lanes load different
+// rows in each instruction, which halves those moves (kPairRows).  Each
 // workgroup owns a contiguous run of 32-span groups of one (block, KV head);
 // its four waves take adjacent spans, so the workgroup reads 32 KB
 // contiguous per step.  About two workgroups per compute unit run: more
@@ -94,6 +96,20 @@ template <int CTRL> __device__ __forceinline__ double dpp_add(double v) {
     y.y = __builtin_amdgcn_mov_dpp(x.y, CTRL, 0xF, 0xF, false);
     return v + *reinterpret_cast<const double *>(&y);
 }
+
+// a + (b from the lane chosen by DPP control CTRL), on the two halves of a double
+template <int CTRL> __device__ __forceinline__ double dpp_add2(double a, double b) {
+    const int2 x = *reinterpret_cast<const int2 *>(&b);
+    int2 y;
+    y.x = __builtin_amdgcn_mov_dpp(x.x, CTRL, 0xF, 0xF, false);
+    y.y = __builtin_amdgcn_mov_dpp(x.y, CTRL, 0xF, 0xF, false);
+    return a + *reinterpret_cast<const double *>(&y);
+}
+
+// The decode scorer's paired-row layout: bf16 rows of 128 elements (16 lanes of
+// 16 bytes), 8 load instructions (32 rows) per batch.
+template <typename TIn, int D, int R>
+constexpr bool kPairRows = sizeof(TIn) == 2 && D == 128 && R == 8;
 
 // Sum over the LPR consecutive lanes that share a key row.  Every step pairs
 // lanes symmetrically: quad-permute xor 1, xor 2, half-row mirror, row mirror.
@@ -180,6 +196,46 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
             const int64_t tb = un.sg.mid_lo + j * a.S;
             const int64_t te = min(tb + (int64_t)a.S, un.sg.mid_hi);
             double best = -INFINITY;
+            if constexpr (kPairRows<TIn, D, R>) {
+                // instruction r of a batch: lanes of the row's first half
+                // (chunks 0-7) load row 4r + rs, lanes of the second half row
+                // 4(r ^ 4) + rs (every instruction still reads whole 128-byte
+                // half rows), so one mirror step turns the partial sums of
+                // instructions r and r + 4 into two rows' sums over a half
+                // each, and three steps within 8 lanes finish them
+                const int hb = (lane >> 3) & 1;
+                for (int64_t r0 = tb; r0 < te; r0 += (int64_t)R * RPI) {
+                    uint4 buf[R];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const int64_t t = r0 + (r ^ (hb * 4)) * RPI + rs;
+                        buf[r] = t < te ? load_nt(kh + t * a.st_bytes) : make_uint4(0u, 0u, 0u, 0u);
+                    }
+                    double acc[R];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        double x[EPL];
+                        unpack(buf[r], x);
+                        double v = 0.0;
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) v = fma(qr[e], x[e], v);
+                        acc[r] = v;
+                    }
+#pragma unroll
+                    for (int r = 0; r < R / 2; ++r) {
+                        // this lane's row: 4r + rs (first half) or 4(r + 4) + rs
+                        double v = dpp_add2<0x140>(acc[r], acc[r + R / 2]);
+                        v = dpp_add<0xB1>(v);
+                        v = dpp_add<0x4E>(v);
+                        v = dpp_add<0x141>(v);
+                        const int64_t t = r0 + (r + hb * (R / 2)) * RPI + rs;
+                        if (t < te) best = fmax(best, v);
+                    }
+                }
+                // rows of a half-row group: max over the halves and the 4 row groups
+                best = fmax(best, __shfl_xor(best, 8));
+                best = rows_max<LPR>(best) + 0.0;       // -0 -> +0
+            } else {
             for (int64_t r0 = tb; r0 < te; r0 += (int64_t)R * RPI) {
                 uint4 buf[R];
                 bool ok[R];
@@ -201,6 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
                 }
             }
             best = rows_max<LPR>(best) + 0.0;       // -0 -> +0
+            }
             if (lane == 0) a.out[(int64_t)bh * a.n_spans + j] = best;
             gbest = fmax(gbest, best);
         }

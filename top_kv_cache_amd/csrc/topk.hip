@@ -10,8 +10,9 @@
 // wrote the maximum of every group of 32 consecutive spans.  Fast path (at
 // most 2048 groups):
 //   1. tau, a lower bound of the k-th largest group maximum, from one
-//      histogram level over the group maxima: the smallest maximum in the
-//      bins at or above the bin holding the k-th largest.  It also bounds the
+//      histogram level over the group maxima: the lower edge of the bin
+//      holding the k-th largest (lowered by far more than the binning's
+//      rounding), below every maximum in that bin and the ones above.  It also bounds the
 //      k-th largest score from below (the k best groups hold k distinct
 //      scores), so every selected span scores >= tau and lies in a group
 //      whose maximum is >= tau; at most 256 such groups are accepted (more
@@ -157,6 +158,34 @@ __device__ __forceinline__ void block_minmax_count(Common &cm, double &mn, doubl
         cnt += cm.red_u[w];
     }
     __syncthreads();
+}
+
+// Workgroup min / max with one barrier (the LDS slots must not be written
+// again before a later barrier).
+__device__ __forceinline__ void block_minmax1(Common &cm, double &mn, double &mx) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fmin(mn, __shfl_xor(mn, o));
+        mx = fmax(mx, __shfl_xor(mx, o));
+    }
+    if (lane == 0) {
+        cm.red_d[0][wave] = mn;
+        cm.red_d[1][wave] = mx;
+    }
+    __syncthreads();
+    mn = INFINITY;
+    mx = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) {
+        mn = fmin(mn, cm.red_d[0][w]);
+        mx = fmax(mx, cm.red_d[1][w]);
+    }
+}
+
+// A value at or below every x with bin_of(x, mn, inv, kBins) >= b: the bin's
+// lower edge, lowered by far more than the rounding of the binning.
+__device__ __forceinline__ double bin_floor(double mn, double mx, int b) {
+    const double e = mn + (mx - mn) * ((double)b / (double)kBins);
+    return e - 1e-12 * (fabs(mn) + fabs(mx) + fabs(e)) - 1e-300;
 }
 
 // Exclusive prefix sum of v over the workgroup in thread order.
@@ -785,14 +814,15 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         }
         // 1. tau <= the kk-th largest group maximum (every span competes if
         //    kk > m): one histogram level over the group maxima finds the bin
-        //    b* holding the kk-th largest, and tau is the smallest maximum in
-        //    bins >= b* (bins are monotone in the value).
+        //    b* holding the kk-th largest, and tau is b*'s lower edge (bins
+        //    are monotone in the value, so every maximum in bins >= b* is at
+        //    or above it).
         double tau = -INFINITY;
         if (n <= (int64_t)kThreads * kSmallPer) {
             // few spans: the bound from one histogram level over the span
             // scores themselves (the group maxima bound little when k is
-            // close to the group count): tau = the smallest score in the bins
-            // at or above the bin holding the kk-th largest
+            // close to the group count): tau = the lower edge of the bin
+            // holding the kk-th largest
             double sr[kSmallPer];
 #pragma unroll
             for (int e = 0; e < kSmallPer; ++e) {
@@ -801,14 +831,13 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             }
             for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
             double mn = INFINITY, mx = -INFINITY;
-            uint32_t dummy = 0;
 #pragma unroll
             for (int e = 0; e < kSmallPer; ++e)
                 if (tid + (int64_t)e * kThreads < n) {
                     mn = fmin(mn, sr[e]);
                     mx = fmax(mx, sr[e]);
                 }
-            block_minmax_count(cm, mn, mx, dummy);
+            block_minmax1(cm, mn, mx);
             if (mn == mx) {
                 tau = mn;
             } else {
@@ -818,26 +847,18 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
                     if (tid + (int64_t)e * kThreads < n) atomicAdd(&f.hist[bin_of(sr[e], mn, inv, kBins)], 1u);
                 __syncthreads();
                 find_bin(cm, f.hist, kBins, kk);
-                const int bstar = cm.bstar;
-                double lo = INFINITY, unused = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < kSmallPer; ++e)
-                    if (tid + (int64_t)e * kThreads < n && bin_of(sr[e], mn, inv, kBins) >= bstar)
-                        lo = fmin(lo, sr[e]);
-                block_minmax_count(cm, lo, unused, dummy);
-                tau = lo;
+                tau = bin_floor(mn, mx, cm.bstar);
             }
         } else if (kk <= m) {
             for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
             double mn = INFINITY, mx = -INFINITY;
-            uint32_t dummy = 0;
 #pragma unroll
             for (int e = 0; e < GPT; ++e)
                 if (tid + e * kThreads < m) {
                     mn = fmin(mn, gr[e]);
                     mx = fmax(mx, gr[e]);
                 }
-            block_minmax_count(cm, mn, mx, dummy);
+            block_minmax1(cm, mn, mx);
             if (mn == mx) {
                 tau = mn;
             } else {
@@ -847,13 +868,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
                     if (tid + e * kThreads < m) atomicAdd(&f.hist[bin_of(gr[e], mn, inv, kBins)], 1u);
                 __syncthreads();
                 find_bin(cm, f.hist, kBins, kk);
-                const int bstar = cm.bstar;
-                double lo = INFINITY, unused = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < GPT; ++e)
-                    if (tid + e * kThreads < m && bin_of(gr[e], mn, inv, kBins) >= bstar) lo = fmin(lo, gr[e]);
-                block_minmax_count(cm, lo, unused, dummy);
-                tau = lo;
+                tau = bin_floor(mn, mx, cm.bstar);
             }
         }
         // candidate groups: maximum >= tau
