@@ -152,12 +152,18 @@ size_t group_max_bytes(const rea::Geom &g) {
     return (size_t)g.n_blk * g.Hkv * (size_t)rea::score_groups(g) * sizeof(double);
 }
 
+// The token scorer (spans of one token, one query per block) also records
+// each group's second largest score and where its maximum lies.
+bool token_groups(const rea::Geom &g) { return g.S == 1 && g.block_q == 1; }
+
 // score_select workspace: [span scores unless the caller keeps them][group
-// maxima, or the MFMA path's query rows / bounds]
+// maxima (+ second maxima and offsets of the maxima for the token scorer), or
+// the MFMA path's query rows / bounds]
 size_t select_aux_bytes(const rea::Geom &g) {
     if (rea::mfma_block_path(g)) return align256(rea::mfma_ws_bytes(g));
     if (rea::heads_mfma_path(g)) return align256(rea::heads_ws_bytes(g));
-    return align256(group_max_bytes(g));
+    const size_t gm = align256(group_max_bytes(g));
+    return token_groups(g) ? 2 * gm + align256(group_max_bytes(g) / 2) : gm;
 }
 
 // token segments: the best tokens before widening, [n_blk][Hkv][k_tok] + counts
@@ -184,11 +190,19 @@ hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, doubl
         return rea::launch_score_select_heads(g, q, k, scores, sel, n_sel, aux, num_cu, s,
                                               timing ? (hipEvent_t)timing->score_begin : nullptr,
                                               timing ? (hipEvent_t)timing->score_end : nullptr);
+    double *gsec = nullptr;
+    int32_t *garg = nullptr;
+    if (token_groups(g)) {
+        gsec = (double *)((char *)aux + align256(group_max_bytes(g)));
+        garg = (int32_t *)((char *)gsec + align256(group_max_bytes(g)));
+    }
     hipError_t e = rea::launch_score(g, q, k, scores, (double *)aux, num_cu, s,
                                      timing ? (hipEvent_t)timing->score_begin : nullptr,
-                                     timing ? (hipEvent_t)timing->score_end : nullptr);
+                                     timing ? (hipEvent_t)timing->score_end : nullptr, nullptr,
+                                     gsec, garg);
     if (e != hipSuccess) return e;
-    if (!g.seg) return rea::launch_topk(g, scores, (const double *)aux, sel, n_sel, s);
+    if (!g.seg)
+        return rea::launch_topk(g, scores, (const double *)aux, sel, n_sel, s, nullptr, gsec, garg);
     // token segments: the k_tok best tokens, then their widened union
     rea::Geom gt = g;
     gt.topk = g.k_tok;
@@ -196,7 +210,7 @@ hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, doubl
     Carve c{(char *)seg_ws, 0};
     int32_t *sel_tok = c.take<int32_t>((size_t)g.n_blk * g.Hkv * g.k_tok * sizeof(int32_t));
     int32_t *nsel_tok = c.take<int32_t>((size_t)g.n_blk * g.Hkv * sizeof(int32_t));
-    e = rea::launch_topk(gt, scores, (const double *)aux, sel_tok, nsel_tok, s);
+    e = rea::launch_topk(gt, scores, (const double *)aux, sel_tok, nsel_tok, s, nullptr, gsec, garg);
     if (e != hipSuccess) return e;
     return rea::launch_widen(g, sel_tok, nsel_tok, sel, n_sel, s);
 }

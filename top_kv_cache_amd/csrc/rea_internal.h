@@ -104,10 +104,14 @@ hipError_t launch_struct(void (*kern)(A), dim3 grid, dim3 block, size_t lds, hip
 // null, or one flag per (block, KV head) in device memory; then only the
 // flagged pairs are scored.
 int64_t score_groups(const Geom &g);
+// group_second / group_arg (token level, S = 1, only): null, or arrays like
+// group_max receiving each group's second largest score (a tied maximum
+// counts twice) and the offset of a maximum within the group.
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
                         double *group_max, int num_cu, hipStream_t s,
                         hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr,
-                        const uint32_t *only = nullptr);
+                        const uint32_t *only = nullptr, double *group_second = nullptr,
+                        int32_t *group_arg = nullptr);
 
 // Token segments: widen each selected token (sel_tok [n_blk*Hkv][k_tok],
 // middle-relative, ascending) to g.seg tokens and write the union, ascending,
@@ -117,9 +121,12 @@ hipError_t launch_widen(const Geom &g, const int32_t *sel_tok, const int32_t *ns
 
 // Step 1b: top-k per (block, KV head) from the span scores and group maxima;
 // only: null, or device flags per (block, KV head) selecting the pairs to run.
+// group_second / group_arg: null, or the scorer's arrays above (the large
+// path then reads only the groups with two or more candidates).
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
                        int32_t *sel, int32_t *n_sel, hipStream_t s,
-                       const uint32_t *only = nullptr);
+                       const uint32_t *only = nullptr, const double *group_second = nullptr,
+                       const int32_t *group_arg = nullptr);
 
 // Step 1 for blocks of 64 queries on MFMA (bf16, d 128, S a multiple of 32):
 // approximate span scores with a proven error bound, then an exact top-k that

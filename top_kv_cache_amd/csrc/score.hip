@@ -48,6 +48,10 @@ struct ScoreArgs {
     const unsigned char *k;
     double *out;                // [n_blk][Hkv][n_spans]
     double *gmax;               // [n_blk][Hkv][n_groups]
+    // k_score_tokens: null, or the second largest score of every group (a
+    // tied maximum counts twice) and the offset of a maximum in the group
+    double *gsec;               // [n_blk][Hkv][n_groups]
+    int32_t *garg;              // [n_blk][Hkv][n_groups]
     int64_t sh_bytes, st_bytes;
     int64_t mid_lo, mid_hi, n_spans, n_groups;   // n_spans, n_groups: also the row strides
     int S, Hq, Hkv, g, block_q, P, rep;
@@ -659,8 +663,36 @@ __global__ __launch_bounds__(kThreads) void k_score_tokens(ScoreArgs a) {
                 if (ok[r]) best = fmax(best, v[m][r]);
             }
             if (wr) a.out[(bh0 + m) * a.n_spans + (tw - un.sg.mid_lo)] = mine;
-            best = rows_max<LPR>(best);
-            if (lane == 0) a.gmax[(bh0 + m) * a.n_groups + grp] = best;
+            if (a.gsec) {
+                // (largest, second largest) over the 32 token lanes, pairwise:
+                // lanes ch < R of each row slot, then the 4 row slots
+                double b1 = wr ? mine : -INFINITY, b2 = -INFINITY;
+#pragma unroll
+                for (int o = 1; o < LPR; o <<= 1) {
+                    if (o >= R) break;
+                    const double c1 = __shfl_xor(b1, o), c2 = __shfl_xor(b2, o);
+                    b2 = fmax(fmin(b1, c1), fmax(b2, c2));
+                    b1 = fmax(b1, c1);
+                }
+#pragma unroll
+                for (int o = LPR; o < 64; o <<= 1) {
+                    const double c1 = __shfl_xor(b1, o), c2 = __shfl_xor(b2, o);
+                    b2 = fmax(fmin(b1, c1), fmax(b2, c2));
+                    b1 = fmax(b1, c1);
+                }
+                // a lane holding the maximum: its token's offset in the group
+                // (the only one when the second largest is smaller)
+                const uint64_t hit = __ballot(wr && mine == b1);
+                const int hl = hit ? __ffsll((long long)hit) - 1 : 0;
+                if (lane == 0) {
+                    a.gmax[(bh0 + m) * a.n_groups + grp] = b1 + 0.0;
+                    a.gsec[(bh0 + m) * a.n_groups + grp] = b2 + 0.0;
+                    a.garg[(bh0 + m) * a.n_groups + grp] = (hl % LPR) * RPI + hl / LPR;
+                }
+            } else {
+                best = rows_max<LPR>(best);
+                if (lane == 0) a.gmax[(bh0 + m) * a.n_groups + grp] = best;
+            }
         }
     }
 }
@@ -800,10 +832,13 @@ int64_t score_groups(const Geom &g) { return (g.n_spans + kGroup - 1) / kGroup; 
 
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
                         double *group_max, int num_cu, hipStream_t s, hipEvent_t ev_begin,
-                        hipEvent_t ev_end, const uint32_t *only) {
+                        hipEvent_t ev_end, const uint32_t *only, double *group_second,
+                        int32_t *group_arg) {
     if (g.n_spans == 0) return hipSuccess;
     ScoreArgs a;
     a.only = only;
+    a.gsec = group_second;
+    a.garg = group_arg;
     a.q = q;
     a.k = (const unsigned char *)k;
     a.out = span_scores;

@@ -516,38 +516,107 @@ __device__ __forceinline__ uint32_t large_tau_groups(Common &cm, LargeShared &L,
 }
 
 __device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const double *sc,
-                                           const double *gm, int64_t n, int64_t m, int kk,
-                                           int topk, int32_t *sel) {
+                                           const double *gm, const double *gs, const int32_t *ga,
+                                           int64_t n, int64_t m, int kk, int topk, int32_t *sel) {
     const int tid = threadIdx.x, lane = tid & 63;
     double tau;
     const uint32_t ncg = m <= (int64_t)kGReg * kThreads ? large_tau_groups<true>(cm, L, gm, m, kk, tau)
                                                         : large_tau_groups<false>(cm, L, gm, m, kk, tau);
     if (ncg > (uint32_t)kLGroups) return false;
-    if (tid == 0) cm.count = 0;
+    if (tid == 0) {
+        cm.count = 0;
+        cm.above = 0;
+    }
     __syncthreads();
-    // 3. their spans scoring >= tau (half a wave per group, U groups in
-    //    flight).  A candidate is recorded by its position p = c * 32 + lane
-    //    in the ascending candidate groups, which orders like its span index.
-    constexpr int U = 32;
+    // 3. their spans scoring >= tau.  A candidate is recorded by its position
+    //    p = c * 32 + o (o: its offset in candidate group c, the groups
+    //    ascending), which orders like its span index.
+    //    With the scorer's second largest scores: a group whose second
+    //    largest is below tau holds exactly one candidate, its maximum (at
+    //    the offset the scorer recorded), appended here without reading the
+    //    group; the others are listed (mlist, over the histogram's LDS) and
+    //    read span by span below.  More of them than the list holds: every
+    //    group is read.
+    int32_t *mlist = reinterpret_cast<int32_t *>(L.hist);
+    constexpr uint32_t kMList = kBins;
+    constexpr int U = 32;                  // groups in flight per half wave below
+    constexpr int GPI = kThreads / 32;     // groups per pass (16)
+    uint32_t nread = ncg;                  // groups read span by span
+    bool listed = false;
+    // (a single pass of reads, at most GPI * U groups, is no slower than the
+    // pass over the second maxima that would replace it)
+    if (gs && ncg > (uint32_t)(GPI * U)) {
+        constexpr int V = 8;               // candidate groups per thread and pass
+        for (uint32_t c0 = 0; c0 < ncg; c0 += kThreads * V) {
+            int32_t gi[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const uint32_t c = c0 + e * kThreads + tid;
+                gi[e] = L.cgrp[c < ncg ? c : ncg - 1];
+            }
+            double v1[V], v2[V];
+            int32_t off[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                v1[e] = gm[gi[e]];
+                v2[e] = gs[gi[e]];
+                off[e] = ga[gi[e]];
+            }
+            bool single[V];
+            uint32_t slot[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const uint32_t c = c0 + e * kThreads + tid;
+                // (the maxima tau was taken from are rounded up: check)
+                single[e] = c < ncg && v2[e] < tau && v1[e] >= tau;
+                if (c < ncg && !(v2[e] < tau)) {
+                    const uint32_t k2 = atomicAdd(&cm.above, 1u);
+                    if (k2 < kMList) mlist[k2] = (int32_t)c;
+                }
+            }
+            wave_append(&cm.count, single, slot);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                if (single[e] && slot[e] < (uint32_t)kCandCap) {
+                    L.val[slot[e]] = v1[e];
+                    L.idx[slot[e]] = (int32_t)((c0 + e * kThreads + tid) * kGroup + off[e]);
+                }
+            }
+        }
+        __syncthreads();
+        nread = cm.above;
+        listed = nread <= kMList;
+        if (!listed) {
+            // too many groups to list: read them all, from no candidates
+            nread = ncg;
+            __syncthreads();
+            if (tid == 0) cm.count = 0;
+        }
+        __syncthreads();
+    }
+    // half a wave per group read, U groups in flight
     const int half = tid >> 5, hl = tid & 31;
-    constexpr int GPI = kThreads / 32;                 // groups per pass (16)
-    for (uint32_t c0 = 0; c0 < ncg; c0 += GPI * U) {
+    for (uint32_t c0 = 0; c0 < nread; c0 += GPI * U) {
         double x[U];
         bool ok[U];
         // (the group index is read unconditionally, clamped, so the LDS reads
         // are issued together and the loads follow without a wait per read)
+        uint32_t cv[U];
         int32_t gi[U];
 #pragma unroll
         for (int e = 0; e < U; ++e) {
-            const uint32_t c = c0 + e * GPI + half;
-            gi[e] = L.cgrp[c < ncg ? c : ncg - 1];
+            const uint32_t r = c0 + e * GPI + half;
+            const uint32_t rc = r < nread ? r : nread - 1;
+            cv[e] = listed ? (uint32_t)mlist[rc] : rc;
         }
+#pragma unroll
+        for (int e = 0; e < U; ++e) gi[e] = L.cgrp[cv[e]];
 #pragma unroll
         for (int e = 0; e < U; ++e) {
             // (span indices are below 2^31: 32-bit offsets from one base)
-            const uint32_t c = c0 + e * GPI + half;
+            const uint32_t r = c0 + e * GPI + half;
             const uint32_t j = (uint32_t)gi[e] * kGroup + hl;
-            ok[e] = c < ncg && j < (uint64_t)n;
+            ok[e] = r < nread && j < (uint64_t)n;
             x[e] = sc[j < (uint64_t)n ? j : (uint32_t)(n - 1)];
         }
         bool keep[U];
@@ -559,7 +628,7 @@ __device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const dou
         for (int e = 0; e < U; ++e) {
             if (keep[e] && slot[e] < (uint32_t)kCandCap) {
                 L.val[slot[e]] = x[e];
-                L.idx[slot[e]] = (int32_t)((c0 + e * GPI + half) * kGroup + hl);
+                L.idx[slot[e]] = (int32_t)(cv[e] * kGroup + hl);
             }
         }
     }
@@ -770,6 +839,11 @@ struct TopkArgs {
     int64_t T, G, L;
     // null, or one flag per (block, head): only the flagged pairs are selected
     const uint32_t *only;
+    // null, or per group the second largest score and the offset of a maximum
+    // (token-level scorer): the large path then reads only the candidate
+    // groups with two or more spans at or above its bound
+    const double *gsec;
+    const int32_t *garg;
 };
 
 __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
@@ -1050,7 +1124,9 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         __syncthreads();
     }
 
-    if (kk <= m && large_path(cm, u.l, sc, gm, n, m, kk, topk, sel)) return;
+    if (kk <= m && large_path(cm, u.l, sc, gm, ta.gsec ? ta.gsec + bh * ta.m_stride : nullptr,
+                              ta.garg ? ta.garg + bh * ta.m_stride : nullptr, n, m, kk, topk, sel))
+        return;
 
     generic_cutoff(cm, u.g, sc, n, kk);
     if (sel) {
@@ -1158,10 +1234,13 @@ hipError_t launch_widen(const Geom &g, const int32_t *sel_tok, const int32_t *ns
 }
 
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
-                       int32_t *sel, int32_t *n_sel, hipStream_t s, const uint32_t *only) {
+                       int32_t *sel, int32_t *n_sel, hipStream_t s, const uint32_t *only,
+                       const double *group_second, const int32_t *group_arg) {
     const int nbh = g.n_blk * g.Hkv;
     TopkArgs ta;
     ta.only = only;
+    ta.gsec = group_second;
+    ta.garg = group_arg;
     ta.scores = span_scores;
     ta.gmax = group_max;
     ta.sel = sel;
