@@ -81,14 +81,14 @@ struct GenericShared {
 
 // large path state (many groups, or many candidate groups)
 constexpr int kLGroups = 8192;      // candidate groups held, ascending
-static_assert(8 * kWaves == 64, "one wave scans the slice counts");
+static_assert(8 * kWaves == 64, "one wave scans the slice counts of a batch");
 struct LargeShared {
     double val[kCandCap];
     int32_t idx[kCandCap];
     uint32_t hist[kBins];
     int32_t cgrp[kLGroups];
-    uint32_t wcnt[8 * kWaves];
-    uint32_t wpre[8 * kWaves + 1];
+    uint32_t wcnt[64 * kWaves];         // per (register or batch slot, wave)
+    uint32_t wpre[64 * kWaves + 1];
 };
 
 struct Common {
@@ -440,16 +440,14 @@ __device__ __forceinline__ uint32_t large_tau_groups(Common &cm, LargeShared &L,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     GmaxSource<kRegs> src{gm, m, {}};
     src.load();
-    // 1. tau: the smallest group maximum in the histogram bins at or above the
-    //    one holding the kk-th largest maximum (a lower bound of the kk-th
-    //    largest span score)
+    // 1. tau: the lower edge of the histogram bin holding the kk-th largest
+    //    maximum (a lower bound of the kk-th largest span score)
     double mn = INFINITY, mx = -INFINITY;
-    uint32_t dummy = 0;
     src.each([&](int64_t, double x) {
         mn = fmin(mn, x);
         mx = fmax(mx, x);
     });
-    block_minmax_count(cm, mn, mx, dummy);
+    block_minmax1(cm, mn, mx);
     double tau = mn;
     if (mn != mx) {
         const double inv = (double)kBins / (mx - mn);
@@ -458,18 +456,74 @@ __device__ __forceinline__ uint32_t large_tau_groups(Common &cm, LargeShared &L,
         src.each([&](int64_t, double x) { atomicAdd(&L.hist[bin_of(x, mn, inv, kBins)], 1u); });
         __syncthreads();
         find_bin(cm, L.hist, kBins, kk);
-        const int bstar = cm.bstar;
-        double lo = INFINITY, unused = -INFINITY;
-        src.each([&](int64_t, double x) {
-            if (bin_of(x, mn, inv, kBins) >= bstar) lo = fmin(lo, x);
-        });
-        block_minmax_count(cm, lo, unused, dummy);
-        tau = lo;
+        tau = bin_floor(mn, mx, cm.bstar);
     }
     if constexpr (kRegs) tau = (double)nextafterf((float)tau, -INFINITY);
     tau_out = tau;
-    // 2. candidate groups (maximum >= tau) in ascending order: per batch of
-    //    8 * kThreads groups, the count of every (e, wave) slice orders the writes
+    // 2. candidate groups (maximum >= tau) in ascending order
+    if constexpr (kRegs) {
+        // the counts of every (batch slot, wave) slice first, one prefix over
+        // all of them, then the writes (two barriers instead of two per batch)
+#pragma unroll
+        for (int bb = 0; bb < kGReg / 8; ++bb) {
+            const int64_t b0 = (int64_t)bb * 8 * kThreads;
+            double x[8];
+            src.batch(b0, bb, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t i = b0 + e * kThreads + tid;
+                const unsigned long long b = __ballot(i < m && x[e] >= tau);
+                if (lane == 0) L.wcnt[(bb * 8 + e) * kWaves + wave] = (uint32_t)__popcll(b);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {                 // exclusive prefix over the 512 slices, 8 per lane
+            constexpr int PL = kGReg * kWaves / 64;
+            uint32_t v[PL], own = 0;
+#pragma unroll
+            for (int j = 0; j < PL; ++j) {
+                v[j] = L.wcnt[lane * PL + j];
+                own += v[j];
+            }
+            uint32_t incl = own;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            uint32_t run = incl - own;
+#pragma unroll
+            for (int j = 0; j < PL; ++j) {
+                L.wpre[lane * PL + j] = run;
+                run += v[j];
+            }
+            if (lane == 63) L.wpre[kGReg * kWaves] = incl;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int bb = 0; bb < kGReg / 8; ++bb) {
+            const int64_t b0 = (int64_t)bb * 8 * kThreads;
+            double x[8];
+            src.batch(b0, bb, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t i = b0 + e * kThreads + tid;
+                const bool keep = i < m && x[e] >= tau;
+                const unsigned long long b = __ballot(keep);
+                if (keep) {
+                    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                        (uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+                    const uint32_t slot = L.wpre[(bb * 8 + e) * kWaves + wave] + below;
+                    if (slot < (uint32_t)kLGroups) L.cgrp[slot] = (int32_t)i;
+                }
+            }
+        }
+        const uint32_t total = L.wpre[kGReg * kWaves];
+        __syncthreads();
+        return total;
+    }
+    // per batch of 8 * kThreads groups, the count of every (e, wave) slice
+    // orders the writes
     uint32_t ncg = 0;
     constexpr int kMaxBatches = kRegs ? kGReg / 8 : 1 << 30;
 #pragma unroll kRegs ? kGReg / 8 : 1
