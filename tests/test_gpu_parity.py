@@ -183,6 +183,36 @@ def test_exact_ties_many_candidates(T, S_, k):
     assert split >= 1 and (crowded >= 1 or T == 40000)
 
 
+def test_token_level_many_two_candidate_groups():
+    """Token level, 3000 groups of 32 tokens holding two equal high tokens each
+    (every other token scores 0) and k = 3000: every candidate group has its
+    second largest score at the bound, more of them than the list of groups to
+    read holds, so the top-k reads every candidate group; the 3000 selected
+    are the lowest indices of the 6000 tied tokens."""
+    rng = np.random.default_rng(4242)
+    w = S(Hq=2, Hkv=2, d=64, T=200000, S=1, topk=3000, L=64, needles=0)
+    lo, hi = w.mid
+    n_groups = (hi - lo) // 32
+    qn = np.ones((1, w.Hq, w.d), np.float32)
+    Kn = np.zeros((w.Hkv, w.T, w.d), np.float32)
+    for h in range(w.Hkv):
+        for gi in rng.choice(n_groups, size=3000, replace=False):
+            a, b = rng.choice(32, size=2, replace=False)
+            Kn[h, lo + gi * 32 + a] = 1.0
+            Kn[h, lo + gi * 32 + b] = 1.0
+    Vn = rng.standard_normal((w.Hkv, w.T, w.d)).astype(np.float32)
+    to_bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    bf = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    gpu = run_library(w, to_bf(qn), to_bf(Kn), to_bf(Vn))
+    q64, K64, V64 = bf(qn), bf(Kn), bf(Vn)
+    for h in range(w.Hkv):
+        ora = oracle_head(w, 0, h, q64, K64[h:h + 1], V64[h:h + 1])
+        sc = ora["sc"][0]
+        assert int((sc == sc.max()).sum()) == 6000
+        compare_head(w, gpu, ora, h)
+
+
 def test_token_order_below_fp32_resolution():
     """fp32 inputs whose token scores differ only below fp32 resolution
     (score = level + 2^-30 * noise): the top-k's large path bounds the k-th
