@@ -83,6 +83,14 @@ SMALL = {
     "pqh_bf16_mfma_blocks": S(Hq=8, Hkv=2, d=128, T=3000, n_q=128, block_q=64, S=32, topk=12,
                               L=128, needles=0, per_q_head=True),
     "f32_token_level_S1_g1": S(dtype="f32", Hq=2, Hkv=2, d=128, S=1, topk=100, T=1200, L=50),
+    # bf16 rows of 128: the token scorer's paired-row layout (half rows of two
+    # rows per load), 1446 middle tokens (a last group of 6); one, three and
+    # four query heads scored per read of a key row
+    "bf16_d128_token_level": S(Hq=8, Hkv=2, d=128, S=1, topk=60, T=1500, L=50, needles=2),
+    "pqh_bf16_d128_g3_token_level": S(Hq=6, Hkv=2, d=128, S=1, topk=60, T=1500, L=50,
+                                      needles=2, per_q_head=True),
+    "pqh_bf16_d128_g4_token_level": S(Hq=8, Hkv=2, d=128, S=1, topk=60, T=1500, L=50,
+                                      needles=2, per_q_head=True),
     # 9..64 query rows per (block, selection head): 2-wave MFMA attention
     "bf16_blocks_of_16_rows_S24": S(Hq=8, Hkv=2, d=128, T=1900, n_q=8, block_q=4, S=24, topk=9,
                                     L=96, needles=0, kv_scaled=True),

@@ -595,7 +595,38 @@ __global__ __launch_bounds__(kThreads, 2) void k_score_heads_lds(ScoreArgs a) {
 // selection head; the group maximum needs no exchange between waves.  NH > 1
 // scores the NH query heads of a KV head from one read of each row (one
 // selection per query head); NH == 1 scores selection head u with the summed
-// queries of its group.
+// queries of its group.  After the row sums every lane holds the scores of
+// all the rows its lanes share (bf16 rows of 128 elements: paired rows, as in
+// k_score_decode, so each half row holds half of them), so a group's two
+// largest scores are formed in registers first and then merged across the
+// half rows (DPP rotate by 8) and the row slots (permlane swaps, no LDS).
+template <bool X16> __device__ __forceinline__ void swap_halves(double v, double &x, double &y) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t l = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const auto lo2 = X16 ? __builtin_amdgcn_permlane16_swap(l, l, false, false)
+                         : __builtin_amdgcn_permlane32_swap(l, l, false, false);
+    const auto hi2 = X16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                         : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    x = __longlong_as_double((long long)(((uint64_t)hi2[0] << 32) | lo2[0]));
+    y = __longlong_as_double((long long)(((uint64_t)hi2[1] << 32) | lo2[1]));
+}
+
+// (b1, b2) <- the two largest of the multiset {b1, b2, c1, c2} (a tie counts twice)
+__device__ __forceinline__ void top2_merge(double &b1, double &b2, double c1, double c2) {
+    b2 = fmax(fmin(b1, c1), fmax(b2, c2));
+    b1 = fmax(b1, c1);
+}
+
+// Merge with lane l ^ 16 (X16) or l ^ 32: the swap returns this lane's pair and
+// the partner's in either order, and the merge is symmetric in the two.
+template <bool X16> __device__ __forceinline__ void top2_xlane(double &b1, double &b2) {
+    double p1, q1, p2, q2;
+    swap_halves<X16>(b1, p1, q1);
+    swap_halves<X16>(b2, p2, q2);
+    b1 = p1, b2 = p2;
+    top2_merge(b1, b2, q1, q2);
+}
+
 template <typename TIn, int D, int NH>
 __global__ __launch_bounds__(kThreads) void k_score_tokens(ScoreArgs a) {
     constexpr int ESZ = sizeof(TIn);
@@ -603,9 +634,15 @@ __global__ __launch_bounds__(kThreads) void k_score_tokens(ScoreArgs a) {
     constexpr int RPI = 64 / LPR;
     constexpr int EPL = 16 / ESZ;
     constexpr int R = kGroup / RPI;              // load instructions per group
+    constexpr bool PAIR = kPairRows<TIn, D, R>;
+    constexpr int NV = PAIR ? R / 2 : R;         // token scores a lane holds
     static_assert(R <= LPR, "one lane per row slot writes the group's scores");
+    static_assert(LPR >= 8 && LPR <= 32, "rows of 8 to 32 lanes");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rs = lane / LPR, ch = lane % LPR;
+    // paired rows: the second half of a row's lanes holds rows NV.. of the group
+    const int hb = PAIR ? (lane >> 3) & 1 : 0;
+    const int c = PAIR ? ch & 7 : ch;            // writer lanes: c < NV
     const int Hu = a.Hkv / NH;
     const int bu = blockIdx.x / a.P, p = blockIdx.x % a.P;
     const int b = bu / Hu, u = bu % Hu;
@@ -630,68 +667,83 @@ __global__ __launch_bounds__(kThreads) void k_score_tokens(ScoreArgs a) {
     const GroupRange gr = group_range(a, p, un.sg.n_groups);
     for (int64_t grp = gr.g0 + wave; grp < gr.g1; grp += kWaves) {
         const int64_t t0 = un.sg.mid_lo + grp * kGroup;
+        // v[.][i] below is the score of token tl + i * RPI
+        const int64_t tl = t0 + hb * NV * RPI + rs;
         uint4 buf[R];
-        bool ok[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int64_t t = t0 + r * RPI + rs;
-            ok[r] = t < un.sg.mid_hi;
-            buf[r] = ok[r] ? load_nt(kh + t * a.st_bytes) : make_uint4(0u, 0u, 0u, 0u);
+            const int64_t t = t0 + (PAIR ? (r ^ (hb * NV)) : r) * RPI + rs;
+            buf[r] = t < un.sg.mid_hi ? load_nt(kh + t * a.st_bytes) : make_uint4(0u, 0u, 0u, 0u);
         }
-        double v[NH][R];
+        double acc[NH][R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             double x[EPL];
             unpack(buf[r], x);
 #pragma unroll
             for (int m = 0; m < NH; ++m) {
-                double acc = 0.0;
+                double s = 0.0;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) acc = fma(qr[m][e], x[e], acc);
-                v[m][r] = row_sum<LPR>(acc) + 0.0;          // -0 -> +0
+                for (int e = 0; e < EPL; ++e) s = fma(qr[m][e], x[e], s);
+                acc[m][r] = s;
             }
         }
-        // lane (rs, ch < R) stores the score of token t0 + ch*RPI + rs
-        const int64_t tw = t0 + ch * RPI + rs;
-        const bool wr = ch < R && tw < un.sg.mid_hi;
+        double v[NH][NV];
+#pragma unroll
+        for (int m = 0; m < NH; ++m)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                if constexpr (PAIR) {
+                    // instruction i of this half and i + NV of the mirrored half
+                    // read the same row: one mirror step, then 8 lanes
+                    double s = dpp_add2<0x140>(acc[m][i], acc[m][i + NV]);
+                    s = dpp_add<0xB1>(s);
+                    s = dpp_add<0x4E>(s);
+                    s = dpp_add<0x141>(s);
+                    v[m][i] = s + 0.0;                  // -0 -> +0
+                } else {
+                    v[m][i] = row_sum<LPR>(acc[m][i]) + 0.0;
+                }
+            }
+        // lane (rs, c < NV) stores the score of token tl + c * RPI
+        const int64_t tw = tl + c * RPI;
+        const bool wr = c < NV && tw < un.sg.mid_hi;
 #pragma unroll
         for (int m = 0; m < NH; ++m) {
-            double mine = v[m][0], best = ok[0] ? v[m][0] : -INFINITY;
+            double mine = v[m][0], b1 = -INFINITY, b2 = -INFINITY;
 #pragma unroll
-            for (int r = 1; r < R; ++r) {
-                if (ch == r) mine = v[m][r];
-                if (ok[r]) best = fmax(best, v[m][r]);
+            for (int i = 0; i < NV; ++i) {
+                if (i > 0 && c == i) mine = v[m][i];
+                const double x = tl + i * RPI < un.sg.mid_hi ? v[m][i] : -INFINITY;
+                if (a.gsec) {
+                    top2_merge(b1, b2, x, -INFINITY);
+                } else {
+                    b1 = fmax(b1, x);
+                }
             }
             if (wr) a.out[(bh0 + m) * a.n_spans + (tw - un.sg.mid_lo)] = mine;
             if (a.gsec) {
-                // (largest, second largest) over the 32 token lanes, pairwise:
-                // lanes ch < R of each row slot, then the 4 row slots
-                double b1 = wr ? mine : -INFINITY, b2 = -INFINITY;
-#pragma unroll
-                for (int o = 1; o < LPR; o <<= 1) {
-                    if (o >= R) break;
-                    const double c1 = __shfl_xor(b1, o), c2 = __shfl_xor(b2, o);
-                    b2 = fmax(fmin(b1, c1), fmax(b2, c2));
-                    b1 = fmax(b1, c1);
-                }
-#pragma unroll
-                for (int o = LPR; o < 64; o <<= 1) {
-                    const double c1 = __shfl_xor(b1, o), c2 = __shfl_xor(b2, o);
-                    b2 = fmax(fmin(b1, c1), fmax(b2, c2));
-                    b1 = fmax(b1, c1);
-                }
+                // lane l ^ 8 (the other half row, or with 8-lane rows the next
+                // row slot), then l ^ 16 where it holds another row slot, then l ^ 32
+                if constexpr (PAIR || LPR == 8)
+                    top2_merge(b1, b2, dpp_mov<0x128>(b1), dpp_mov<0x128>(b2));
+                if constexpr (LPR <= 16) top2_xlane<true>(b1, b2);
+                top2_xlane<false>(b1, b2);
                 // a lane holding the maximum: its token's offset in the group
                 // (the only one when the second largest is smaller)
                 const uint64_t hit = __ballot(wr && mine == b1);
                 const int hl = hit ? __ffsll((long long)hit) - 1 : 0;
                 if (lane == 0) {
+                    const int hch = hl % LPR;
+                    const int hc = PAIR ? hch & 7 : hch, hh = PAIR ? (hch >> 3) & 1 : 0;
                     a.gmax[(bh0 + m) * a.n_groups + grp] = b1 + 0.0;
                     a.gsec[(bh0 + m) * a.n_groups + grp] = b2 + 0.0;
-                    a.garg[(bh0 + m) * a.n_groups + grp] = (hl % LPR) * RPI + hl / LPR;
+                    a.garg[(bh0 + m) * a.n_groups + grp] = (hh * NV + hc) * RPI + hl / LPR;
                 }
             } else {
-                best = rows_max<LPR>(best);
-                if (lane == 0) a.gmax[(bh0 + m) * a.n_groups + grp] = best;
+                if constexpr (PAIR) b1 = fmax(b1, dpp_mov<0x128>(b1));
+                b1 = rows_max<LPR>(b1);
+                if (lane == 0) a.gmax[(bh0 + m) * a.n_groups + grp] = b1;
             }
         }
     }
