@@ -675,9 +675,17 @@ __global__ __launch_bounds__(256, 2) void k_score_heads_mfma(HeadsArgs a) {
             // span done: query n's maximum (lanes n and n + 32 hold the two
             // row halves), the largest key norm over the 32 row lanes
             const double sm = (double)pair_max(run) + 0.0;
+            // largest of the 32 rows' norms: DPP within each 16-lane row, then
+            // the two rows of a half wave (lanes l and l ^ 32 hold the same row)
             float km = kn_run;
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) km = fmaxf(km, __shfl_xor(km, o));
+            km = fmaxf(km, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(km), 0xB1, 0xF, 0xF, false)));
+            km = fmaxf(km, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(km), 0x4E, 0xF, 0xF, false)));
+            km = fmaxf(km, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(km), 0x141, 0xF, 0xF, false)));
+            km = fmaxf(km, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(km), 0x140, 0xF, 0xF, false)));
+            {
+                const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(km), __float_as_uint(km), false, false);
+                km = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+            }
             // an upper bound: the fp32 sums low by at most 130 * 2^-23
             // relative, squares below 2^-126 flushed
             const double kbv = sqrt((double)km * (1.0 + 0x1p-15) + 0x1p-119) * (1.0 + 1e-12);
