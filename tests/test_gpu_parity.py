@@ -104,6 +104,10 @@ SMALL = {
     # range: the top-k's first bound keeps more groups than it can hold, so
     # the bound becomes the 256-th largest group maximum
     "bf16_k256_2048_groups": S(Hq=2, Hkv=1, d=64, T=262_144, S=4, topk=256, L=64, needles=4),
+    # at most 4096 spans (2185 here) with k = 300: the top-k holds every
+    # span score in registers, and more than 192 of them reach its bound, so
+    # the cutoff comes from histogram levels and the output from a bitmap
+    "bf16_k300_2185_spans": S(Hq=4, Hkv=2, d=64, T=70_000, S=32, topk=300, L=64, needles=2),
     # token segments: the best tokens, each widened to S tokens
     "seg_bf16_d64": S(S=8, topk=6, T=700, token_segments=True),
     "seg_bf16_d128_pqh": S(Hq=8, Hkv=2, d=128, T=2048, S=32, topk=12, L=256, needles=2,

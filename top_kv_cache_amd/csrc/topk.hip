@@ -16,10 +16,11 @@
 //      k-th largest score from below (the k best groups hold k distinct
 //      scores), so every selected span scores >= tau and lies in a group
 //      whose maximum is >= tau; at most 256 such groups are accepted (more
-//      only with massive ties).  With at most 4096 spans the same level is
-//      taken over the span scores themselves (read with the group maxima):
-//      when k is close to the group count the group bound keeps most spans,
-//      the span bound about k of them.
+//      only with massive ties).  With at most 4096 spans every span score is
+//      held in registers instead: the same level is taken over the span
+//      scores themselves (when k is close to the group count the group bound
+//      keeps most spans, the span bound about k of them), and the spans
+//      scoring >= tau are the candidates of step 3 without step 2;
 //   2. the spans of those groups with score >= tau (all spans scoring >= tau)
 //      are loaded into LDS;
 //   3. with at most 192 of them, each one's rank among them (score desc,
@@ -880,6 +881,107 @@ __device__ __forceinline__ void generic_emit(Common &cm, const double *sc, int64
     }
 }
 
+// With every span scoring >= tau in (f.val, f.idx)[0..count), count <=
+// kPairCap: a candidate's rank among them (score desc, index asc) is its
+// global rank, so ranks < kk are kept and each kept span is written at the
+// count of kept indices below its own.  Both counts are split into slices of
+// the compared range, one thread per (entry, slice), summed through LDS.
+__device__ __forceinline__ void rank_pairwise_emit(Common &cm, FastShared &f, uint32_t count, int kk,
+                                                   int topk, int32_t *sel) {
+    const int tid = threadIdx.x;
+    // 3'. every span scoring >= tau is a candidate, so a candidate's
+    //     rank among them (score desc, index asc) is its rank among
+    //     all spans: rank every candidate pairwise, keep ranks < kk,
+    //     and place each kept span by the kept indices below it.
+    //     Both counts are split into slices of the compared range,
+    //     one thread per (entry, slice), summed through LDS.
+    if (tid == 0) cm.count = 0;
+    const uint32_t ns = count ? kThreads / count : 1;         // >= 2
+    if (tid < ns * count) {
+        const uint32_t c = tid % count, sl = tid / count;
+        const uint32_t o0 = sl * count / ns, o1 = (sl + 1) * count / ns;
+        const double x = f.val[c];
+        const int32_t jc = f.idx[c];
+        uint32_t rank = 0, o = o0;
+        for (; o + 8 <= o1; o += 8) {
+            double y[8];
+            int32_t yi[8];
+#pragma unroll
+            for (int u2 = 0; u2 < 8; ++u2) {
+                y[u2] = f.val[o + u2];
+                yi[u2] = f.idx[o + u2];
+            }
+#pragma unroll
+            for (int u2 = 0; u2 < 8; ++u2) rank += (y[u2] > x) || (y[u2] == x && yi[u2] < jc);
+        }
+        for (; o < o1; ++o) rank += (f.val[o] > x) || (f.val[o] == x && f.idx[o] < jc);
+        f.hist[tid] = rank;
+    }
+    __syncthreads();
+    for (uint32_t c = tid; c < count; c += kThreads) {
+        uint32_t rank = 0;
+        for (uint32_t sl = 0; sl < ns; ++sl) rank += f.hist[sl * count + c];
+        if (rank < (uint32_t)kk) f.gidx[atomicAdd(&cm.count, 1u)] = f.idx[c];
+    }
+    __syncthreads();
+    if (sel) {
+        const uint32_t nk = (uint32_t)kk, ns2 = kThreads / nk;  // >= 2
+        if (tid < ns2 * nk) {
+            const uint32_t t = tid % nk, sl = tid / nk;
+            const uint32_t o0 = sl * nk / ns2, o1 = (sl + 1) * nk / ns2;
+            const int32_t jt = f.gidx[t];
+            uint32_t pos = 0, o = o0;
+            for (; o + 8 <= o1; o += 8) {
+                int32_t yi[8];
+#pragma unroll
+                for (int u2 = 0; u2 < 8; ++u2) yi[u2] = f.gidx[o + u2];
+#pragma unroll
+                for (int u2 = 0; u2 < 8; ++u2) pos += yi[u2] < jt;
+            }
+            for (; o < o1; ++o) pos += f.gidx[o] < jt;
+            f.hist[tid] = pos;
+        }
+        __syncthreads();
+        for (uint32_t t = tid; t < nk; t += kThreads) {
+            uint32_t pos = 0;
+            for (uint32_t sl = 0; sl < ns2; ++sl) pos += f.hist[sl * nk + t];
+            sel[pos] = f.gidx[t];
+        }
+        for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
+    }
+}
+
+// The selection bitmap f.bitmap[0..m) (one word per 32 spans) compacted in
+// ascending span order into sel, padded with -1 after kk entries.
+__device__ __forceinline__ void emit_bitmap(Common &cm, FastShared &f, int64_t m, int kk, int topk,
+                                            int32_t *sel) {
+    const int tid = threadIdx.x;
+    constexpr int WPT = kMaxGroups / kThreads;      // 4 words per thread
+    uint32_t words[WPT];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+        const int wi = tid * WPT + i;
+        words[i] = wi < m ? f.bitmap[wi] : 0u;
+        mine += __popc(words[i]);
+    }
+    uint32_t tot;
+    uint32_t pos = block_excl_sum(cm, mine, &tot);
+    if (sel) {
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            uint32_t w = words[i];
+            while (w) {
+                const int bit = __ffs(w) - 1;
+                w &= w - 1;
+                if (pos < (uint32_t)topk) sel[pos] = (tid * WPT + i) * kGroup + bit;
+                ++pos;
+            }
+        }
+        for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
+    }
+}
+
 struct TopkArgs {
     const double *scores;       // [n_blk * Hkv][n_stride]
     const double *gmax;         // [n_blk * Hkv][m_stride]
@@ -931,6 +1033,74 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         return;
     }
 
+    if (n <= (int64_t)kThreads * kSmallPer) {
+        // few spans (at most 128 groups): every span score is held in
+        // registers.  tau = the lower edge of the histogram bin holding the
+        // kk-th largest score; the candidates are the spans scoring >= tau,
+        // taken straight from the registers (the group maxima bound little
+        // when k is close to the group count).
+        FastShared &f = u.f;
+        double sr[kSmallPer];
+#pragma unroll
+        for (int e = 0; e < kSmallPer; ++e) {
+            const int64_t i = tid + (int64_t)e * kThreads;
+            sr[e] = sc[i < n ? i : n - 1];
+        }
+        for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
+        double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kSmallPer; ++e)
+            if (tid + (int64_t)e * kThreads < n) {
+                mn = fmin(mn, sr[e]);
+                mx = fmax(mx, sr[e]);
+            }
+        block_minmax1(cm, mn, mx);
+        double tau = mn;
+        if (mn < mx) {
+            const double inv = (double)kBins / (mx - mn);
+#pragma unroll
+            for (int e = 0; e < kSmallPer; ++e)
+                if (tid + (int64_t)e * kThreads < n) atomicAdd(&f.hist[bin_of(sr[e], mn, inv, kBins)], 1u);
+            __syncthreads();
+            find_bin(cm, f.hist, kBins, kk);
+            tau = bin_floor(mn, mx, cm.bstar);
+        }
+        if (tid == 0) cm.count = 0;
+        __syncthreads();
+        bool keep[kSmallPer];
+        uint32_t slot[kSmallPer];
+#pragma unroll
+        for (int e = 0; e < kSmallPer; ++e) keep[e] = tid + (int64_t)e * kThreads < n && sr[e] >= tau;
+        wave_append(&cm.count, keep, slot);
+#pragma unroll
+        for (int e = 0; e < kSmallPer; ++e)
+            if (keep[e]) {
+                f.val[slot[e]] = sr[e];
+                f.idx[slot[e]] = tid + e * kThreads;
+            }
+        __syncthreads();
+        const uint32_t count = cm.count;
+        __syncthreads();
+        if (count <= (uint32_t)kPairCap) {
+            rank_pairwise_emit(cm, f, count, kk, topk, sel);
+            return;
+        }
+        // the cutoff among the candidates, then a bitmap over the spans
+        find_kth(cm, f.hist, f.val, f.idx, count, kk);
+        const double cv = cm.cut_v;
+        const int64_t cj = cm.cut_j;
+        for (int i = tid; i < m; i += kThreads) f.bitmap[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kSmallPer; ++e) {
+            const int32_t j = tid + e * kThreads;
+            if (keep[e] && (sr[e] > cv || (sr[e] == cv && j <= cj))) atomicOr(&f.bitmap[j >> 5], 1u << (j & 31));
+        }
+        __syncthreads();
+        emit_bitmap(cm, f, m, kk, topk, sel);
+        return;
+    }
+
     if (m <= kMaxGroups) {
         FastShared &f = u.f;
         constexpr int GPT = kMaxGroups / kThreads;         // group maxima per thread (4)
@@ -946,38 +1116,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         //    are monotone in the value, so every maximum in bins >= b* is at
         //    or above it).
         double tau = -INFINITY;
-        if (n <= (int64_t)kThreads * kSmallPer) {
-            // few spans: the bound from one histogram level over the span
-            // scores themselves (the group maxima bound little when k is
-            // close to the group count): tau = the lower edge of the bin
-            // holding the kk-th largest
-            double sr[kSmallPer];
-#pragma unroll
-            for (int e = 0; e < kSmallPer; ++e) {
-                const int64_t i = tid + (int64_t)e * kThreads;
-                sr[e] = sc[i < n ? i : n - 1];
-            }
-            for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
-            double mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < kSmallPer; ++e)
-                if (tid + (int64_t)e * kThreads < n) {
-                    mn = fmin(mn, sr[e]);
-                    mx = fmax(mx, sr[e]);
-                }
-            block_minmax1(cm, mn, mx);
-            if (mn == mx) {
-                tau = mn;
-            } else {
-                const double inv = (double)kBins / (mx - mn);
-#pragma unroll
-                for (int e = 0; e < kSmallPer; ++e)
-                    if (tid + (int64_t)e * kThreads < n) atomicAdd(&f.hist[bin_of(sr[e], mn, inv, kBins)], 1u);
-                __syncthreads();
-                find_bin(cm, f.hist, kBins, kk);
-                tau = bin_floor(mn, mx, cm.bstar);
-            }
-        } else if (kk <= m) {
+        if (kk <= m) {
             for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
             double mn = INFINITY, mx = -INFINITY;
 #pragma unroll
@@ -1016,9 +1155,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             __syncthreads();
             ncg = cm.count;
             __syncthreads();
-            if (pass > 0 || ncg <= (uint32_t)kMaxCandGroups || n <= (int64_t)kThreads * kSmallPer ||
-                kk > m)
-                break;
+            if (pass > 0 || ncg <= (uint32_t)kMaxCandGroups || kk > m) break;
             // One histogram level left every group of the kk-th largest
             // maximum's bin above tau, more than the candidate capacity (a
             // wide bin: a few far larger maxima stretch the range).  tau
@@ -1071,66 +1208,8 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             const uint32_t count = cm.count;
             __syncthreads();
             if (count <= (uint32_t)kPairCap) {
-                // 3'. every span scoring >= tau is a candidate, so a candidate's
-                //     rank among them (score desc, index asc) is its rank among
-                //     all spans: rank every candidate pairwise, keep ranks < kk,
-                //     and place each kept span by the kept indices below it.
-                //     Both counts are split into slices of the compared range,
-                //     one thread per (entry, slice), summed through LDS.
-                if (tid == 0) cm.count = 0;
-                const uint32_t ns = count ? kThreads / count : 1;         // >= 2
-                if (tid < ns * count) {
-                    const uint32_t c = tid % count, sl = tid / count;
-                    const uint32_t o0 = sl * count / ns, o1 = (sl + 1) * count / ns;
-                    const double x = f.val[c];
-                    const int32_t jc = f.idx[c];
-                    uint32_t rank = 0, o = o0;
-                    for (; o + 8 <= o1; o += 8) {
-                        double y[8];
-                        int32_t yi[8];
-#pragma unroll
-                        for (int u2 = 0; u2 < 8; ++u2) {
-                            y[u2] = f.val[o + u2];
-                            yi[u2] = f.idx[o + u2];
-                        }
-#pragma unroll
-                        for (int u2 = 0; u2 < 8; ++u2) rank += (y[u2] > x) || (y[u2] == x && yi[u2] < jc);
-                    }
-                    for (; o < o1; ++o) rank += (f.val[o] > x) || (f.val[o] == x && f.idx[o] < jc);
-                    f.hist[tid] = rank;
-                }
-                __syncthreads();
-                for (uint32_t c = tid; c < count; c += kThreads) {
-                    uint32_t rank = 0;
-                    for (uint32_t sl = 0; sl < ns; ++sl) rank += f.hist[sl * count + c];
-                    if (rank < (uint32_t)kk) f.gidx[atomicAdd(&cm.count, 1u)] = f.idx[c];
-                }
-                __syncthreads();
-                if (sel) {
-                    const uint32_t nk = (uint32_t)kk, ns2 = kThreads / nk;  // >= 2
-                    if (tid < ns2 * nk) {
-                        const uint32_t t = tid % nk, sl = tid / nk;
-                        const uint32_t o0 = sl * nk / ns2, o1 = (sl + 1) * nk / ns2;
-                        const int32_t jt = f.gidx[t];
-                        uint32_t pos = 0, o = o0;
-                        for (; o + 8 <= o1; o += 8) {
-                            int32_t yi[8];
-#pragma unroll
-                            for (int u2 = 0; u2 < 8; ++u2) yi[u2] = f.gidx[o + u2];
-#pragma unroll
-                            for (int u2 = 0; u2 < 8; ++u2) pos += yi[u2] < jt;
-                        }
-                        for (; o < o1; ++o) pos += f.gidx[o] < jt;
-                        f.hist[tid] = pos;
-                    }
-                    __syncthreads();
-                    for (uint32_t t = tid; t < nk; t += kThreads) {
-                        uint32_t pos = 0;
-                        for (uint32_t sl = 0; sl < ns2; ++sl) pos += f.hist[sl * nk + t];
-                        sel[pos] = f.gidx[t];
-                    }
-                    for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
-                }
+                // 3'. every span scoring >= tau is a candidate: rank them pairwise
+                rank_pairwise_emit(cm, f, count, kk, topk, sel);
                 return;
             }
             // 3. cutoff, bitmap words of the candidate groups, ordered output
@@ -1147,30 +1226,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
                 if (hl == 0 && c < ncg) f.bitmap[f.cgrp[c]] = (uint32_t)(bal >> (lane & 32));
             }
             __syncthreads();
-            constexpr int WPT = kMaxGroups / kThreads;      // 4 words per thread
-            uint32_t words[WPT];
-            uint32_t mine = 0;
-#pragma unroll
-            for (int i = 0; i < WPT; ++i) {
-                const int wi = tid * WPT + i;
-                words[i] = wi < m ? f.bitmap[wi] : 0u;
-                mine += __popc(words[i]);
-            }
-            uint32_t tot;
-            uint32_t pos = block_excl_sum(cm, mine, &tot);
-            if (sel) {
-#pragma unroll
-                for (int i = 0; i < WPT; ++i) {
-                    uint32_t w = words[i];
-                    while (w) {
-                        const int bit = __ffs(w) - 1;
-                        w &= w - 1;
-                        if (pos < (uint32_t)topk) sel[pos] = (tid * WPT + i) * kGroup + bit;
-                        ++pos;
-                    }
-                }
-                for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
-            }
+            emit_bitmap(cm, f, m, kk, topk, sel);
             (void)wave;
             return;
         }
