@@ -307,6 +307,30 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
         snt[p] = (RT)tab[c0 + p][3];
     }
 
+    // (cos, sin) of (kSub - kSL) theta_c: a stream's next sub-split starts that
+    // many rows after the row its per-row steps reach, so one complex step
+    // carries the rotation over instead of evaluating it again (fp64 powers of
+    // the per-row step, rounded to RT)
+    RT cj[PPL], sj[PPL];
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+        double rc = 1.0, rs = 0.0, bc = tab[c0 + p][2], bs = tab[c0 + p][3];
+        for (int e = kSub - kSL; e > 0; e >>= 1) {
+            if (e & 1) {
+                const double t = rc * bc - rs * bs;
+                rs = rs * bc + rc * bs;
+                rc = t;
+            }
+            const double t = bc * bc - bs * bs;
+            bs = 2.0 * bc * bs;
+            bc = t;
+        }
+        cj[p] = (RT)rc;
+        sj[p] = (RT)rs;
+    }
+    RT cs_run[PPL], sn_run[PPL];        // rotation of the row after the last consumed one
+    bool started = false;
+
     // the stream's running softmax state over its rows
     float m[QRM], l[QRM], acc[QRM][NA];
 #pragma unroll
@@ -321,15 +345,26 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     auto consume = [&](int sub, const RowsKV<TIn, PPL> &rk) {
         const int64_t wf = w0 + (int64_t)sub * kSub + soff;
         const int wfi = (int)wf;
-        // rotation of the stream's first row, then one step per row (bf16
-        // inputs step in fp32: 3 steps add a few fp32 ulps; fp32 inputs in fp64)
+        // rotation of the stream's first row (evaluated for the first
+        // sub-split, carried over from the previous one by one complex step
+        // after that), then one step per row (bf16 inputs step in fp32, a few
+        // fp32 ulps per sub-split; fp32 inputs in fp64)
         RT cs[PPL], sn[PPL];
+        if (!started) {
 #pragma unroll
-        for (int p = 0; p < PPL; ++p) {
-            float c1, s1;
-            rope_cs(wf, tab[c0 + p][0], tab[c0 + p][1], c1, s1);
-            cs[p] = c1;
-            sn[p] = s1;
+            for (int p = 0; p < PPL; ++p) {
+                float c1, s1;
+                rope_cs(wf, tab[c0 + p][0], tab[c0 + p][1], c1, s1);
+                cs[p] = c1;
+                sn[p] = s1;
+            }
+            started = true;
+        } else {
+#pragma unroll
+            for (int p = 0; p < PPL; ++p) {
+                cs[p] = cs_run[p] * cj[p] - sn_run[p] * sj[p];
+                sn[p] = sn_run[p] * cj[p] + cs_run[p] * sj[p];
+            }
         }
         // logits of the rows, in log2 units (the scale carries log2 e)
         float lg[kSL][QRM];
@@ -360,6 +395,11 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
                 const int pos = Wi - a.n_q + b * a.block_q + r / a.g;
                 lg[i][r] = (wfi + i < Wi && wfi + i <= pos && r < a.QR) ? d : -INFINITY;
             }
+        }
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) {
+            cs_run[p] = cs[p];
+            sn_run[p] = sn[p];
         }
         // online softmax: rescale the state to the new maximum, add the rows
 #pragma unroll
