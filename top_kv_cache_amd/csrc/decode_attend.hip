@@ -283,8 +283,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
                 const int64_t i = (int64_t)b * a.block_q + r / a.g;
                 float co, sn;
                 rope_cs(Wbh - a.n_q + i, tab[c][0], tab[c][1], co, sn);
-                y1 = qx1[j] * co - qx2[j] * sn;
-                y2 = qx2[j] * co + qx1[j] * sn;
+                // (the softmax scale, in log2 units, is folded in here)
+                y1 = (qx1[j] * co - qx2[j] * sn) * a.scale_log2;
+                y2 = (qx2[j] * co + qx1[j] * sn) * a.scale_log2;
             }
             qs[r][c] = y1;
             qs[r][c + HALF] = y2;
@@ -331,11 +332,15 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     RT cs_run[PPL], sn_run[PPL];        // rotation of the row after the last consumed one
     bool started = false;
 
-    // the stream's running softmax state over its rows
+    // the stream's running softmax state over its rows.  The running maximum
+    // starts at the lowest finite float, not -inf: every finite logit reaches
+    // it, and a masked row (logit -inf) then gets weight exp2(-inf) = 0 with
+    // no test (while every row so far is masked the state stays 0 and rescales
+    // by exp2(0)).
     float m[QRM], l[QRM], acc[QRM][NA];
 #pragma unroll
     for (int r = 0; r < QRM; ++r) {
-        m[r] = -INFINITY;
+        m[r] = -__FLT_MAX__;
         l[r] = 0.f;
 #pragma unroll
         for (int e = 0; e < NA; ++e) acc[r][e] = 0.f;
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
                     d = fmaf(q1[r][p], y1[p], d);
                     d = fmaf(q2[r][p], y2[p], d);
                 }
-                d = row_sum16f(d) * a.scale_log2;
+                d = row_sum16f(d);
                 const int pos = Wi - a.n_q + b * a.block_q + r / a.g;
                 lg[i][r] = (wfi + i < Wi && wfi + i <= pos && r < a.QR) ? d : -INFINITY;
             }
@@ -407,8 +412,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
             float mx = m[r];
 #pragma unroll
             for (int i = 0; i < kSL; ++i) mx = fmaxf(mx, lg[i][r]);
-            if (mx == -INFINITY) continue;          // every row so far masked
-            const float f = __builtin_amdgcn_exp2f(m[r] - mx);   // 0 when m was -inf
+            const float f = __builtin_amdgcn_exp2f(m[r] - mx);   // 0 from the floor to a real maximum
             l[r] *= f;
 #pragma unroll
             for (int e = 0; e < NA; ++e) acc[r][e] *= f;
@@ -422,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
 #pragma unroll
             for (int r = 0; r < QRM; ++r) {
                 // exp2(-inf) = 0 covers masked rows
-                const float p = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[i][r] - m[r]);
+                const float p = __builtin_amdgcn_exp2f(lg[i][r] - m[r]);
                 l[r] += p;
 #pragma unroll
                 for (int e = 0; e < PPL; ++e) {
