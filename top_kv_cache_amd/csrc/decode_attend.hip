@@ -347,6 +347,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
     }
     const int Wi = (int)Wbh;
 
+    const int64_t pos_min = Wbh - a.n_q + (int64_t)b * a.block_q;   // the first query row's position
     auto consume = [&](int sub, const RowsKV<TIn, PPL> &rk) {
         const int64_t wf = w0 + (int64_t)sub * kSub + soff;
         const int wfi = (int)wf;
@@ -371,13 +372,20 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
                 sn[p] = sn_run[p] * cj[p] + cs_run[p] * sj[p];
             }
         }
-        // logits of the rows, in log2 units (the scale carries log2 e)
+        // logits of the rows, in log2 units (the scale carries log2 e).  A row
+        // past the window adds -inf; a row after a query row's own position
+        // is masked per query row, tested only where the sub-split reaches
+        // the first query row's position (the same test for the workgroup).
+        // Query rows r >= QR need no mask: their staged query is 0 and their
+        // results are never written.
+        const bool causal = w0 + (int64_t)(sub + 1) * kSub - 1 > pos_min;
         float lg[kSL][QRM];
 #pragma unroll
         for (int i = 0; i < kSL; ++i) {
             float x1[PPL], x2[PPL];
             rk.k1[i].get(x1);
             rk.k2[i].get(x2);
+            const float madd = wfi + i < Wi ? 0.f : -INFINITY;
             float y1[PPL], y2[PPL];
 #pragma unroll
             for (int p = 0; p < PPL; ++p) {
@@ -396,9 +404,12 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
                     d = fmaf(q1[r][p], y1[p], d);
                     d = fmaf(q2[r][p], y2[p], d);
                 }
-                d = row_sum16f(d);
-                const int pos = Wi - a.n_q + b * a.block_q + r / a.g;
-                lg[i][r] = (wfi + i < Wi && wfi + i <= pos && r < a.QR) ? d : -INFINITY;
+                d = row_sum16f(d) + madd;
+                if (causal) {
+                    const int pos = Wi - a.n_q + b * a.block_q + r / a.g;
+                    if (wfi + i > pos) d = -INFINITY;
+                }
+                lg[i][r] = d;
             }
         }
 #pragma unroll
