@@ -245,6 +245,25 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
         const int64_t o0 = wf - sg.Gp;
         const uint32_t oc = (uint32_t)(o0 > 0 ? o0 : 0);
         int oq = (int)(oc / (uint32_t)a.S), orr = (int)(oc - (uint32_t)oq * (uint32_t)a.S);
+        // the usual case: the stream's kSL rows are consecutive cache rows
+        // (inside the window, in one region, within one selected span), so
+        // the first row's source and the row stride address them all
+        const bool run = wf + kSL <= Wbh &&
+                         (o0 + kSL <= 0 || o0 >= sel_len || (o0 >= 0 && o0 + kSL <= sel_len && orr + kSL <= a.S));
+        if (run) {
+            const int64_t src = o0 < 0 ? wf
+                              : o0 < sel_len ? sg.mid_lo + (int64_t)ssel[oq - slot0] * a.S + orr
+                                             : sg.T - sg.Lp + (o0 - sel_len);
+            const TIn *kp = kb + src * a.st + c0, *vp = vb + src * a.st + c0;
+#pragma unroll
+            for (int i = 0; i < kSL; ++i) {
+                rk.k1[i].load(kp + i * a.st);
+                rk.k2[i].load(kp + i * a.st + HALF);
+                rk.v1[i].load(vp + i * a.st);
+                rk.v2[i].load(vp + i * a.st + HALF);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < kSL; ++i) {
             const int64_t w = wf + i, o = o0 + i;
