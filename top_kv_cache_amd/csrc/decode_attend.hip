@@ -436,17 +436,23 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
             cs_run[p] = cs[p];
             sn_run[p] = sn[p];
         }
-        // online softmax: rescale the state to the new maximum, add the rows
+        // online softmax: the state is rescaled to a new maximum only when a
+        // row exceeds the current one by more than 2^8 (weights up to 2^8
+        // stay far inside fp32), and only when some stream of the wave needs
+        // it; the first real row always does (from the floor)
 #pragma unroll
         for (int r = 0; r < QRM; ++r) {
             float mx = m[r];
 #pragma unroll
             for (int i = 0; i < kSL; ++i) mx = fmaxf(mx, lg[i][r]);
-            const float f = __builtin_amdgcn_exp2f(m[r] - mx);   // 0 from the floor to a real maximum
-            l[r] *= f;
+            const bool grow = mx > m[r] + 8.f;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float f = grow ? __builtin_amdgcn_exp2f(m[r] - mx) : 1.f;   // 0 from the floor
+                l[r] *= f;
 #pragma unroll
-            for (int e = 0; e < NA; ++e) acc[r][e] *= f;
-            m[r] = mx;
+                for (int e = 0; e < NA; ++e) acc[r][e] *= f;
+                if (grow) m[r] = mx;
+            }
         }
 #pragma unroll
         for (int i = 0; i < kSL; ++i) {
