@@ -773,7 +773,7 @@ struct CertShared {
     uint32_t scan[kCWaves + 1];
     uint32_t count, above, nd, nx;
     int32_t bstar, cut_j;
-    double cut_v;
+    double cut_v, cut_u;
     double q1[kD];                  // the pair's query in fp64 (one query per pair)
     int32_t cand[kCCap];            // k_certify_heads: the pair's candidate spans, ascending
     uint32_t ncand;
@@ -820,6 +820,15 @@ __device__ __forceinline__ void c_minmax(CertShared &sh, double &mn, double &mx)
     __syncthreads();
 }
 
+// Slices a pairwise ranking of count entries is split into: as many as the
+// workgroup's threads allow, but each covering at least 16 entries (the
+// slices' counts are summed one LDS read each afterwards).
+__device__ __forceinline__ uint32_t c_slices(uint32_t count) {
+    uint32_t ns = count ? kCThreads / count : 1;
+    if (ns > count / 16) ns = count / 16;
+    return ns ? ns : 1u;
+}
+
 // need-th best of (val, idx)[0..count) under (val desc, idx asc) -> cut_v/cut_j.
 // Reorders and shrinks val/idx.
 __device__ __forceinline__ void c_find_kth(CertShared &sh, uint32_t count, int64_t need) {
@@ -827,14 +836,18 @@ __device__ __forceinline__ void c_find_kth(CertShared &sh, uint32_t count, int64
     bool by_index = false;
     for (;;) {
         if (count <= (uint32_t)kCRank) {
-            // pairwise ranks, 8 entries read per step so the LDS latency is
-            // paid once per 8 comparisons
-            for (uint32_t c = tid; c < count; c += kCThreads) {
+            // pairwise ranks: one thread per (entry, slice of the compared
+            // entries), so every thread of the workgroup takes part; 8
+            // entries are read per step so the LDS latency is paid once per 8
+            // comparisons, and the slices' counts are summed through LDS
+            const uint32_t ns = c_slices(count);
+            if ((uint32_t)tid < ns * count) {
+                const uint32_t c = (uint32_t)tid % count, sl = (uint32_t)tid / count;
+                const uint32_t o1 = (sl + 1) * count / ns;
                 const double x = sh.val[c];
                 const int32_t jc = sh.idx[c];
-                int64_t rank = 0;
-                uint32_t o = 0;
-                for (; o + 8 <= count; o += 8) {
+                uint32_t rank = 0, o = sl * count / ns;
+                for (; o + 8 <= o1; o += 8) {
                     double y[8];
                     int32_t yi[8];
 #pragma unroll
@@ -845,13 +858,19 @@ __device__ __forceinline__ void c_find_kth(CertShared &sh, uint32_t count, int64
 #pragma unroll
                     for (int u = 0; u < 8; ++u) rank += (y[u] > x) || (y[u] == x && yi[u] < jc);
                 }
-                for (; o < count; ++o) {
+                for (; o < o1; ++o) {
                     const double y = sh.val[o];
                     rank += (y > x) || (y == x && sh.idx[o] < jc);
                 }
+                sh.hist[tid] = rank;
+            }
+            __syncthreads();
+            for (uint32_t c = tid; c < count; c += kCThreads) {
+                int64_t rank = 0;
+                for (uint32_t sl = 0; sl < ns; ++sl) rank += sh.hist[sl * count + c];
                 if (rank == need - 1) {
-                    sh.cut_v = x;
-                    sh.cut_j = jc;
+                    sh.cut_v = sh.val[c];
+                    sh.cut_j = sh.idx[c];
                 }
             }
             __syncthreads();
@@ -928,6 +947,59 @@ __device__ __forceinline__ void c_find_kth(CertShared &sh, uint32_t count, int64
     }
 }
 
+// With count <= kCRank: the needL-th best of (val, idx) and the needU-th best
+// of (xv, idx) under (value desc, idx asc) -> cut_v and cut_u, from one
+// pairwise pass (one thread per (entry, slice of the compared entries), the
+// slices' counts summed through LDS).  val, xv and idx are left unchanged.
+__device__ __forceinline__ void c_find_kth_pair(CertShared &sh, uint32_t count, int64_t needL,
+                                                int64_t needU) {
+    const int tid = threadIdx.x;
+    const uint32_t ns = c_slices(count);
+    if ((uint32_t)tid < ns * count) {
+        const uint32_t c = (uint32_t)tid % count, sl = (uint32_t)tid / count;
+        const uint32_t o1 = (sl + 1) * count / ns;
+        const double xl = sh.val[c], xu = sh.xv[c];
+        const int32_t jc = sh.idx[c];
+        uint32_t rl = 0, ru = 0, o = sl * count / ns;
+        for (; o + 8 <= o1; o += 8) {
+            double yl[8], yu[8];
+            int32_t yi[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                yl[u] = sh.val[o + u];
+                yu[u] = sh.xv[o + u];
+                yi[u] = sh.idx[o + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                rl += (yl[u] > xl) || (yl[u] == xl && yi[u] < jc);
+                ru += (yu[u] > xu) || (yu[u] == xu && yi[u] < jc);
+            }
+        }
+        for (; o < o1; ++o) {
+            const int32_t yi = sh.idx[o];
+            rl += (sh.val[o] > xl) || (sh.val[o] == xl && yi < jc);
+            ru += (sh.xv[o] > xu) || (sh.xv[o] == xu && yi < jc);
+        }
+        sh.hist[tid] = rl;
+        sh.hist[kCThreads + tid] = ru;
+    }
+    __syncthreads();
+    for (uint32_t c = tid; c < count; c += kCThreads) {
+        int64_t rl = 0, ru = 0;
+        for (uint32_t sl = 0; sl < ns; ++sl) {
+            rl += sh.hist[sl * count + c];
+            ru += sh.hist[kCThreads + sl * count + c];
+        }
+        if (rl == needL - 1) {
+            sh.cut_v = sh.val[c];
+            sh.cut_j = sh.idx[c];
+        }
+        if (ru == needU - 1) sh.cut_u = sh.xv[c];
+    }
+    __syncthreads();
+}
+
 __device__ __forceinline__ double cert_eps(double Eb, double kb, double s) {
     const double e = Eb * kb;
     return e * (1.0 + 1e-9) + 1e-12 * (fabs(s) + e) + 1e-300;
@@ -977,28 +1049,48 @@ __device__ __forceinline__ bool cert_classify(const CertArgs &a, CertShared &sh,
         for (int e = 0; e < kCPer; ++e) ev[e] = cert_eps(Eb, kv[e], sv[e]);
     }
     // tau_L = kk-th largest lower end, tau_U = (kk+1)-th largest upper end
+    // (order: value desc, span index asc).  Up to kCRank ranked spans both
+    // come from one pairwise pass (lower ends in val, upper ends in xv, which
+    // the re-scoring fills only later); beyond that, histogram levels each.
+    double tauL, tauU;
+    if (m <= kCRank) {
 #pragma unroll
-    for (int e = 0; e < kCPer; ++e) {
-        const int64_t c = tid + (int64_t)e * kCThreads;
-        if (c < m) {
-            sh.val[c] = sv[e] - ev[e];
-            sh.idx[c] = jv[e];
+        for (int e = 0; e < kCPer; ++e) {
+            const int64_t c = tid + (int64_t)e * kCThreads;
+            if (c < m) {
+                sh.val[c] = sv[e] - ev[e];
+                sh.xv[c] = sv[e] + ev[e];
+                sh.idx[c] = jv[e];
+            }
         }
-    }
-    __syncthreads();
-    c_find_kth(sh, (uint32_t)m, kk);
-    const double tauL = sh.cut_v;
+        __syncthreads();
+        c_find_kth_pair(sh, (uint32_t)m, kk, kk + 1);
+        tauL = sh.cut_v;
+        tauU = sh.cut_u;
+    } else {
 #pragma unroll
-    for (int e = 0; e < kCPer; ++e) {
-        const int64_t c = tid + (int64_t)e * kCThreads;
-        if (c < m) {
-            sh.val[c] = sv[e] + ev[e];
-            sh.idx[c] = jv[e];
+        for (int e = 0; e < kCPer; ++e) {
+            const int64_t c = tid + (int64_t)e * kCThreads;
+            if (c < m) {
+                sh.val[c] = sv[e] - ev[e];
+                sh.idx[c] = jv[e];
+            }
         }
+        __syncthreads();
+        c_find_kth(sh, (uint32_t)m, kk);
+        tauL = sh.cut_v;
+#pragma unroll
+        for (int e = 0; e < kCPer; ++e) {
+            const int64_t c = tid + (int64_t)e * kCThreads;
+            if (c < m) {
+                sh.val[c] = sv[e] + ev[e];
+                sh.idx[c] = jv[e];
+            }
+        }
+        __syncthreads();
+        c_find_kth(sh, (uint32_t)m, kk + 1);
+        tauU = sh.cut_v;
     }
-    __syncthreads();
-    c_find_kth(sh, (uint32_t)m, kk + 1);
-    const double tauU = sh.cut_v;
     // certainly in: lower end above tau_U.  Possibly in: upper end >= tau_L.
     // Bits and uncertain entries are by position.
     const int nwords = (int)((m + 31) / 32);
