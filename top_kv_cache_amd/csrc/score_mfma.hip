@@ -829,6 +829,40 @@ __device__ __forceinline__ uint32_t c_slices(uint32_t count) {
     return ns ? ns : 1u;
 }
 
+// Called by the 64 lanes of one wave: the bin of hist[0..kCBins) holding the
+// need-th largest entry (bins counted from the top) and the count in the bins
+// above it (1 <= need <= the histogram's total).  Each lane sums a run of
+// kCBins / 64 bins, read in a lane-rotated order so that the lanes hit
+// distinct banks; a suffix scan over the lanes picks the run, and a prefix
+// scan over that run's bins, one per lane, picks the bin.
+__device__ __forceinline__ void c_find_bin(const uint32_t *hist, int64_t need, int &bstar,
+                                           uint32_t &above) {
+    const int lane = threadIdx.x & 63;
+    constexpr int bpl = kCBins / 64;
+    static_assert(bpl <= 64 && (bpl & (bpl - 1)) == 0, "one run's bins fit the wave");
+    uint32_t own = 0;
+    for (int i = 0; i < bpl; ++i) own += hist[lane * bpl + ((i + lane) & (bpl - 1))];
+    uint32_t suf = own;                          // count in bins >= lane * bpl
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_down(suf, o);
+        if (lane + o < 64) suf += y;
+    }
+    const uint32_t after = suf - own;            // count in the runs above this lane's
+    const uint64_t hit = __ballot((int64_t)after < need && need <= (int64_t)suf);
+    const int L = hit ? __ffsll((long long)hit) - 1 : 0;
+    const uint32_t aboveL = __shfl(after, L);
+    const uint32_t c = lane < bpl ? hist[L * bpl + bpl - 1 - lane] : 0u;   // run L, top first
+    uint32_t pre = c;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(pre, o);
+        if (lane >= o) pre += y;
+    }
+    const uint64_t at = __ballot(lane < bpl && (int64_t)(aboveL + pre) >= need);
+    const int i = at ? __ffsll((long long)at) - 1 : 0;
+    bstar = L * bpl + bpl - 1 - i;
+    above = aboveL + __shfl(pre - c, i);
+}
+
 // need-th best of (val, idx)[0..count) under (val desc, idx asc) -> cut_v/cut_j.
 // Reorders and shrinks val/idx.
 __device__ __forceinline__ void c_find_kth(CertShared &sh, uint32_t count, int64_t need) {
@@ -896,22 +930,10 @@ __device__ __forceinline__ void c_find_kth(CertShared &sh, uint32_t count, int64
         }
         __syncthreads();
         if ((tid >> 6) == 0) {
-            constexpr int bpl = kCBins / 64;
-            uint32_t own = 0;
-            for (int i = 0; i < bpl; ++i) own += sh.hist[lane * bpl + i];
-            uint32_t suf = own;
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_down(suf, o);
-                if (lane + o < 64) suf += y;
-            }
-            const uint32_t after = suf - own;
-            if ((int64_t)after < need && need <= (int64_t)suf) {
-                uint32_t above = after;
-                int bb = lane * bpl + bpl - 1;
-                for (; bb > lane * bpl; --bb) {
-                    if ((int64_t)(above + sh.hist[bb]) >= need) break;
-                    above += sh.hist[bb];
-                }
+            int bb;
+            uint32_t above;
+            c_find_bin(sh.hist, need, bb, above);
+            if (lane == 0) {
                 sh.bstar = bb;
                 sh.above = above;
             }
@@ -1466,25 +1488,10 @@ __global__ __launch_bounds__(kCThreads) void k_certify_heads(CertArgs a) {
             if ((int64_t)r * kGThreads + tid < m) atomicAdd(&hist[c_bin(gv[r], mn, inv)], 1u);
         __syncthreads();
         if (wave == 0) {
-            constexpr int bpl = kCBins / 64;
-            const int64_t need = (int64_t)kk + 1;
-            uint32_t own = 0;
-            for (int i = 0; i < bpl; ++i) own += hist[lane * bpl + i];
-            uint32_t suf = own;
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_down(suf, o);
-                if (lane + o < 64) suf += y;
-            }
-            const uint32_t after = suf - own;
-            if ((int64_t)after < need && need <= (int64_t)suf) {
-                uint32_t above = after;
-                int bb = lane * bpl + bpl - 1;
-                for (; bb > lane * bpl; --bb) {
-                    if ((int64_t)(above + hist[bb]) >= need) break;
-                    above += hist[bb];
-                }
-                s_bstar = bb;
-            }
+            int bb;
+            uint32_t above;
+            c_find_bin(hist, (int64_t)kk + 1, bb, above);
+            if (lane == 0) s_bstar = bb;
         }
         __syncthreads();
         const int bstar = s_bstar;
@@ -1673,25 +1680,10 @@ __global__ __launch_bounds__(kPThreads) void k_cert_candidates(CertArgs a) {
     for (int64_t j = tid; j < n; j += kPThreads) atomicAdd(&hist[c_bin(shat[j], mn, inv)], 1u);
     __syncthreads();
     if (wave == 0) {
-        constexpr int bpl = kCBins / 64;
-        const int64_t need = (int64_t)kk + 1;
-        uint32_t own = 0;
-        for (int i = 0; i < bpl; ++i) own += hist[lane * bpl + i];
-        uint32_t suf = own;                       // count in bins >= lane * bpl
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_down(suf, o);
-            if (lane + o < 64) suf += y;
-        }
-        const uint32_t after = suf - own;         // count in bins above this lane's
-        if ((int64_t)after < need && need <= (int64_t)suf) {
-            uint32_t above = after;
-            int bb = lane * bpl + bpl - 1;
-            for (; bb > lane * bpl; --bb) {
-                if ((int64_t)(above + hist[bb]) >= need) break;
-                above += hist[bb];
-            }
-            s_bstar = bb;
-        }
+        int bb;
+        uint32_t above;
+        c_find_bin(hist, (int64_t)kk + 1, bb, above);
+        if (lane == 0) s_bstar = bb;
     }
     __syncthreads();
     const int bstar = s_bstar;
