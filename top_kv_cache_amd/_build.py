@@ -2,9 +2,11 @@
 
     python -m top_kv_cache_amd._build
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -23,17 +25,32 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra=()) -> str:
+    """Compile every source to an object in parallel, then link the library."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", LIB + ".tmp", *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building librea.so")
-    if verbose and r.stderr.strip():
-        sys.stderr.write(r.stderr)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="rea_build_") as tmp:
+        def compile_one(src):
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [hipcc, *compile_flags, *extra, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+        jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8"))))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            results = list(pool.map(compile_one, SOURCES))
+        for _, r in results:
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError("hipcc failed building librea.so")
+        cmd = [hipcc, *FLAGS, *extra, "-o", LIB + ".tmp", *[o for o, _ in results]]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking librea.so")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 
