@@ -85,6 +85,13 @@ __device__ __forceinline__ SeqOf seq_of(const int64_t *lens, int h, int hps, int
 
 constexpr int kMaxHalfDim = 64;   // head_dim <= 128
 
+// 1 when (y, yi) ranks before (x, xi) in the selection order (higher score
+// first, the lower index first among equal scores), else 0.  Bitwise, not
+// short-circuit, so that ranking loops compile without branches.
+__device__ __forceinline__ uint32_t outranks(double y, int32_t yi, double x, int32_t xi) {
+    return (uint32_t)(y > x) | ((uint32_t)(y == x) & (uint32_t)(yi < xi));
+}
+
 // ---- launchers (each returns hipGetLastError() of its launches) ----------
 
 // Launches a kernel whose one parameter is an argument struct.  Non-null

@@ -890,11 +890,11 @@ __device__ __forceinline__ void c_find_kth(CertShared &sh, uint32_t count, int64
                         yi[u] = sh.idx[o + u];
                     }
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) rank += (y[u] > x) || (y[u] == x && yi[u] < jc);
+                    for (int u = 0; u < 8; ++u) rank += outranks(y[u], yi[u], x, jc);
                 }
                 for (; o < o1; ++o) {
                     const double y = sh.val[o];
-                    rank += (y > x) || (y == x && sh.idx[o] < jc);
+                    rank += outranks(y, sh.idx[o], x, jc);
                 }
                 sh.hist[tid] = rank;
             }
@@ -994,14 +994,14 @@ __device__ __forceinline__ void c_find_kth_pair(CertShared &sh, uint32_t count, 
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                rl += (yl[u] > xl) || (yl[u] == xl && yi[u] < jc);
-                ru += (yu[u] > xu) || (yu[u] == xu && yi[u] < jc);
+                rl += outranks(yl[u], yi[u], xl, jc);
+                ru += outranks(yu[u], yi[u], xu, jc);
             }
         }
         for (; o < o1; ++o) {
             const int32_t yi = sh.idx[o];
-            rl += (sh.val[o] > xl) || (sh.val[o] == xl && yi < jc);
-            ru += (sh.xv[o] > xu) || (sh.xv[o] == xu && yi < jc);
+            rl += outranks(sh.val[o], yi, xl, jc);
+            ru += outranks(sh.xv[o], yi, xu, jc);
         }
         sh.hist[tid] = rl;
         sh.hist[kCThreads + tid] = ru;

@@ -281,9 +281,9 @@ __device__ __forceinline__ void find_kth(Common &cm, uint32_t *hist, double *val
                         yi[u] = idx[o + u];
                     }
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) rank += (y[u] > x) || (y[u] == x && yi[u] < jc);
+                    for (int u = 0; u < 8; ++u) rank += outranks(y[u], yi[u], x, jc);
                 }
-                for (; o < count; ++o) rank += (val[o] > x) || (val[o] == x && idx[o] < jc);
+                for (; o < count; ++o) rank += outranks(val[o], idx[o], x, jc);
                 if (rank == need - 1) {
                     cm.cut_v = x;
                     cm.cut_j = jc;
@@ -792,7 +792,7 @@ __device__ __forceinline__ void generic_cutoff(Common &cm, GenericShared &gs, co
                 int64_t rank = 0;
                 for (uint32_t o = 0; o < m; ++o) {
                     const double y = gs.cand_v[o];
-                    rank += (y > x) || (y == x && gs.cand_j[o] < jc);
+                    rank += outranks(y, gs.cand_j[o], x, jc);
                 }
                 if (rank == need - 1) {
                     cm.cut_v = x;
@@ -912,9 +912,9 @@ __device__ __forceinline__ void rank_pairwise_emit(Common &cm, FastShared &f, ui
                 yi[u2] = f.idx[o + u2];
             }
 #pragma unroll
-            for (int u2 = 0; u2 < 8; ++u2) rank += (y[u2] > x) || (y[u2] == x && yi[u2] < jc);
+            for (int u2 = 0; u2 < 8; ++u2) rank += outranks(y[u2], yi[u2], x, jc);
         }
-        for (; o < o1; ++o) rank += (f.val[o] > x) || (f.val[o] == x && f.idx[o] < jc);
+        for (; o < o1; ++o) rank += outranks(f.val[o], f.idx[o], x, jc);
         f.hist[tid] = rank;
     }
     __syncthreads();
