@@ -98,14 +98,17 @@ class Hip:
         self.L.hipEventDestroy(e)
 
 
-def traffic_for(score_bytes):
+def traffic_for(workload, score_bytes):
     """Measured HBM traffic per scoring launch from the committed rocprofv3 PMC
-    summary, if it was taken on the current scoring kernel source."""
+    summary, if it was taken on this workload (same name and algorithmic bytes)
+    and on the current scoring kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         src = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
-        if t.get("score_src_sha256") != src:
+        if t.get("score_src_sha256") != src or t.get("workload") != workload:
+            return None
+        if t.get("algorithmic_bytes_per_launch") != score_bytes:
             return None
         return t["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
@@ -475,7 +478,7 @@ def main():
                        + n_scores * w.H_sel * 8 + w.Hq * w.d * (2 if w.dtype == "bf16" else 4))
         achieved = score_bytes / (k1_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(score_bytes),
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(w.name, score_bytes),
                     "kernel": ("k_score_tokens" if (w.S == 1 or w.token_segments) else
                                "k_score_heads_mfma" if w.per_q_head else "k_score_decode"),
                     "algorithmic_bytes_per_launch": score_bytes,
