@@ -97,6 +97,9 @@ struct Common {
     uint32_t red_u[kWaves];
     uint32_t scan[kWaves + 1];
     uint32_t count;
+    // candidate counters of the fast paths, cleared before a barrier that
+    // comes anyway, so that no barrier is spent on clearing them
+    uint32_t cgroups, cspans;
     uint32_t above;
     int32_t bstar;
     int32_t found;
@@ -1047,6 +1050,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             sr[e] = sc[i < n ? i : n - 1];
         }
         for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
+        if (tid == 0) cm.cspans = 0;       // ordered by block_minmax1's barrier
         double mn = INFINITY, mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < kSmallPer; ++e)
@@ -1065,13 +1069,11 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             find_bin(cm, f.hist, kBins, kk);
             tau = bin_floor(mn, mx, cm.bstar);
         }
-        if (tid == 0) cm.count = 0;
-        __syncthreads();
         bool keep[kSmallPer];
         uint32_t slot[kSmallPer];
 #pragma unroll
         for (int e = 0; e < kSmallPer; ++e) keep[e] = tid + (int64_t)e * kThreads < n && sr[e] >= tau;
-        wave_append(&cm.count, keep, slot);
+        wave_append(&cm.cspans, keep, slot);
 #pragma unroll
         for (int e = 0; e < kSmallPer; ++e)
             if (keep[e]) {
@@ -1079,8 +1081,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
                 f.idx[slot[e]] = tid + e * kThreads;
             }
         __syncthreads();
-        const uint32_t count = cm.count;
-        __syncthreads();
+        const uint32_t count = cm.cspans;   // not cleared again in this call
         if (count <= (uint32_t)kPairCap) {
             rank_pairwise_emit(cm, f, count, kk, topk, sel);
             return;
@@ -1116,6 +1117,11 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         //    are monotone in the value, so every maximum in bins >= b* is at
         //    or above it).
         double tau = -INFINITY;
+        if (tid == 0) {
+            cm.cgroups = 0;
+            cm.cspans = 0;
+        }
+        if (kk > m) __syncthreads();         // else ordered by block_minmax1's barrier
         if (kk <= m) {
             for (int i = tid; i < kBins; i += kThreads) f.hist[i] = 0u;
             double mn = INFINITY, mx = -INFINITY;
@@ -1141,21 +1147,25 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         // candidate groups: maximum >= tau
         uint32_t ncg = 0;
         for (int pass = 0;; ++pass) {
-            if (tid == 0) cm.count = 0;
-            __syncthreads();
+            if (pass > 0) {
+                // (the first pass's counter was cleared before the bound)
+                if (tid == 0) cm.cgroups = 0;
+                __syncthreads();
+            }
             // (about k appends: one LDS atomic each is cheaper than the ballots)
 #pragma unroll
             for (int e = 0; e < GPT; ++e) {
                 const int i = tid + e * kThreads;
                 if (i < m && gr[e] >= tau) {
-                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    const uint32_t slot = atomicAdd(&cm.cgroups, 1u);
                     if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
                 }
             }
             __syncthreads();
-            ncg = cm.count;
-            __syncthreads();
+            ncg = cm.cgroups;
             if (pass > 0 || ncg <= (uint32_t)kMaxCandGroups || kk > m) break;
+            // (every thread has read ncg before the clear at the loop's top:
+            // the barriers below come first)
             // One histogram level left every group of the kk-th largest
             // maximum's bin above tau, more than the candidate capacity (a
             // wide bin: a few far larger maxima stretch the range).  tau
@@ -1194,19 +1204,16 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
                 cjx[it] = (c < ncg && j < n) ? (int32_t)j : -1;
                 cx[it] = sc[j < n ? j : n - 1];
             }
-            if (tid == 0) cm.count = 0;
-            __syncthreads();
 #pragma unroll
             for (int it = 0; it < CPT; ++it) {
                 if (cjx[it] >= 0 && cx[it] >= tau) {
-                    const uint32_t slot = atomicAdd(&cm.count, 1u);
+                    const uint32_t slot = atomicAdd(&cm.cspans, 1u);
                     f.val[slot] = cx[it];
                     f.idx[slot] = cjx[it];
                 }
             }
             __syncthreads();
-            const uint32_t count = cm.count;
-            __syncthreads();
+            const uint32_t count = cm.cspans;   // not cleared again in this call
             if (count <= (uint32_t)kPairCap) {
                 // 3'. every span scoring >= tau is a candidate: rank them pairwise
                 rank_pairwise_emit(cm, f, count, kk, topk, sel);
