@@ -157,13 +157,16 @@ size_t group_max_bytes(const rea::Geom &g) {
 bool token_groups(const rea::Geom &g) { return g.S == 1 && g.block_q == 1; }
 
 // score_select workspace: [span scores unless the caller keeps them][group
-// maxima (+ second maxima and offsets of the maxima for the token scorer), or
-// the MFMA path's query rows / bounds]
+// maxima (+ second maxima and offsets of the maxima for the token scorer, or
+// second and third maxima and the spans of the first two for the decode
+// scorer), or the MFMA path's query rows / bounds]
 size_t select_aux_bytes(const rea::Geom &g) {
     if (rea::mfma_block_path(g)) return align256(rea::mfma_ws_bytes(g));
     if (rea::heads_mfma_path(g)) return align256(rea::heads_ws_bytes(g));
     const size_t gm = align256(group_max_bytes(g));
-    return token_groups(g) ? 2 * gm + align256(group_max_bytes(g) / 2) : gm;
+    if (token_groups(g)) return 2 * gm + align256(group_max_bytes(g) / 2);
+    if (rea::score_decode_path(g)) return gm + align256(2 * group_max_bytes(g)) + align256(group_max_bytes(g));
+    return gm;
 }
 
 // token segments: the best tokens before widening, [n_blk][Hkv][k_tok] + counts
@@ -190,19 +193,23 @@ hipError_t launch_select(const rea::Geom &g, const void *q, const void *k, doubl
         return rea::launch_score_select_heads(g, q, k, scores, sel, n_sel, aux, num_cu, s,
                                               timing ? (hipEvent_t)timing->score_begin : nullptr,
                                               timing ? (hipEvent_t)timing->score_end : nullptr);
-    double *gsec = nullptr;
-    int32_t *garg = nullptr;
+    double *gsec = nullptr, *gtop = nullptr;
+    int32_t *garg = nullptr, *gtopi = nullptr;
     if (token_groups(g)) {
         gsec = (double *)((char *)aux + align256(group_max_bytes(g)));
         garg = (int32_t *)((char *)gsec + align256(group_max_bytes(g)));
+    } else if (rea::score_decode_path(g)) {
+        gtop = (double *)((char *)aux + align256(group_max_bytes(g)));
+        gtopi = (int32_t *)((char *)gtop + align256(2 * group_max_bytes(g)));
     }
     hipError_t e = rea::launch_score(g, q, k, scores, (double *)aux, num_cu, s,
                                      timing ? (hipEvent_t)timing->score_begin : nullptr,
                                      timing ? (hipEvent_t)timing->score_end : nullptr, nullptr,
-                                     gsec, garg);
+                                     gsec, garg, gtop, gtopi);
     if (e != hipSuccess) return e;
     if (!g.seg)
-        return rea::launch_topk(g, scores, (const double *)aux, sel, n_sel, s, nullptr, gsec, garg);
+        return rea::launch_topk(g, scores, (const double *)aux, sel, n_sel, s, nullptr, gsec, garg,
+                                gtop, gtopi);
     // token segments: the k_tok best tokens, then their widened union
     rea::Geom gt = g;
     gt.topk = g.k_tok;

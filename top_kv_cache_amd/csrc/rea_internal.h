@@ -118,7 +118,14 @@ hipError_t launch_score(const Geom &g, const void *q, const void *k, double *spa
                         double *group_max, int num_cu, hipStream_t s,
                         hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr,
                         const uint32_t *only = nullptr, double *group_second = nullptr,
-                        int32_t *group_arg = nullptr);
+                        int32_t *group_arg = nullptr, double *group_top = nullptr,
+                        int32_t *group_top_idx = nullptr);
+// Whether launch_score takes the plain decode scorer (one query, spans of
+// S > 1, each selection head scored on its own): only that scorer fills
+// group_top ([..][groups][2] doubles: each group's second and third largest
+// span scores) and group_top_idx ([..][groups][2]: the spans holding its
+// largest and second largest), when both are given.
+bool score_decode_path(const Geom &g);
 
 // Token segments: widen each selected token (sel_tok [n_blk*Hkv][k_tok],
 // middle-relative, ascending) to g.seg tokens and write the union, ascending,
@@ -130,10 +137,14 @@ hipError_t launch_widen(const Geom &g, const int32_t *sel_tok, const int32_t *ns
 // only: null, or device flags per (block, KV head) selecting the pairs to run.
 // group_second / group_arg: null, or the scorer's arrays above (the large
 // path then reads only the groups with two or more candidates).
+// group_top / group_top_idx: null, or the decode scorer's arrays above (a
+// candidate group whose third largest score is below the bound then gives its
+// candidates from them, without its span scores being read).
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
                        int32_t *sel, int32_t *n_sel, hipStream_t s,
                        const uint32_t *only = nullptr, const double *group_second = nullptr,
-                       const int32_t *group_arg = nullptr);
+                       const int32_t *group_arg = nullptr, const double *group_top = nullptr,
+                       const int32_t *group_top_idx = nullptr);
 
 // Step 1 for blocks of 64 queries on MFMA (bf16, d 128, S a multiple of 32):
 // approximate span scores with a proven error bound, then an exact top-k that

@@ -63,6 +63,11 @@ struct ScoreArgs {
     // per-query-head decode scorers score only the flagged pairs (the exact
     // fallback of the MFMA paths)
     const uint32_t *only;
+    // null, or (k_score_decode) per group the second and third largest span
+    // scores [n_groups][2] and the spans holding the largest and the second
+    // largest [n_groups][2] (a tied score counts again)
+    double *gtop;
+    int32_t *gtopi;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -165,6 +170,77 @@ __device__ __forceinline__ void publish_group_max(const ScoreArgs &a, double (&s
     }
 }
 
+// The three largest span scores of a wave's spans in a group, with the spans
+// of the first two; a score equal to one held counts again.
+struct Top3 {
+    double v1, v2, v3;
+    int32_t i1, i2;
+    __device__ void init() {
+        v1 = v2 = v3 = -INFINITY;
+        i1 = i2 = -1;
+    }
+    __device__ void add(double v, int32_t j) {
+        if (v > v1) {
+            v3 = v2;
+            v2 = v1;
+            i2 = i1;
+            v1 = v;
+            i1 = j;
+        } else if (v > v2) {
+            v3 = v2;
+            v2 = v;
+            i2 = j;
+        } else if (v > v3) {
+            v3 = v;
+        }
+    }
+};
+
+// Group maximum and the group's top three (a.gtop set).  The waves' lists go
+// to LDS; after the barrier twelve lanes of one wave (a different one for
+// each group, so no wave is held back every time) take the twelve entries,
+// rank each against the others (value descending, then list position: a
+// wave's third value, which has no span, ranks after its first two) and the
+// lanes ranked 0-2 write the results.
+__device__ __forceinline__ void publish_group_top(const ScoreArgs &a, double (&slot)[2][kWaves],
+                                                  double (&tv)[2][kWaves][2], int32_t (&ti)[2][kWaves][2],
+                                                  int64_t bh, int64_t grp, const Top3 &w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int pb = (int)(grp & 1);
+    if (lane == 0) {
+        slot[pb][wave] = w.v1;
+        tv[pb][wave][0] = w.v2;
+        tv[pb][wave][1] = w.v3;
+        ti[pb][wave][0] = w.i1;
+        ti[pb][wave][1] = w.i2;
+    }
+    __syncthreads();
+    if (wave == (int)(grp & (kWaves - 1)) && lane < 3 * kWaves) {
+        double e[3 * kWaves];
+#pragma unroll
+        for (int q = 0; q < kWaves; ++q) {
+            e[3 * q] = slot[pb][q];
+            e[3 * q + 1] = tv[pb][q][0];
+            e[3 * q + 2] = tv[pb][q][1];
+        }
+        const int q = lane / 3, k = lane % 3;
+        const double v = k == 0 ? slot[pb][q] : tv[pb][q][k - 1];
+        uint32_t rank = 0;
+#pragma unroll
+        for (int o = 0; o < 3 * kWaves; ++o) rank += (uint32_t)(e[o] > v) | ((uint32_t)(e[o] == v) & (uint32_t)(o < lane));
+        const int64_t og = bh * a.n_groups + grp;
+        if (rank == 0) {
+            a.gmax[og] = v;
+            a.gtopi[2 * og] = ti[pb][q][k < 2 ? k : 1];
+        } else if (rank == 1) {
+            a.gtop[2 * og] = v;
+            a.gtopi[2 * og + 1] = ti[pb][q][k < 2 ? k : 1];
+        } else if (rank == 2) {
+            a.gtop[2 * og + 1] = v;
+        }
+    }
+}
+
 // Decode: one query per block; the group-summed query lives in registers.
 // R = load instructions per batch (each instruction covers RPI rows).
 template <typename TIn, int D, int R>
@@ -174,6 +250,8 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
     constexpr int RPI = 64 / LPR;              // rows per load instruction
     constexpr int EPL = 16 / ESZ;              // elements per lane
     __shared__ double slot[2][kWaves];
+    __shared__ double tv[2][kWaves][2];
+    __shared__ int32_t ti[2][kWaves][2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rs = lane / LPR, ch = lane % LPR;
     const int bh = blockIdx.x / a.P, p = blockIdx.x % a.P;
@@ -196,6 +274,8 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
     for (int64_t grp = gr.g0; grp < gr.g1; ++grp) {
         const int64_t jend = min((grp + 1) * kGroup, un.sg.n_spans);
         double gbest = -INFINITY;
+        Top3 top;
+        top.init();
         for (int64_t j = grp * kGroup + wave; j < jend; j += kWaves) {
             const int64_t tb = un.sg.mid_lo + j * a.S;
             const int64_t te = min(tb + (int64_t)a.S, un.sg.mid_hi);
@@ -264,8 +344,12 @@ __global__ __launch_bounds__(kThreads) void k_score_decode(ScoreArgs a) {
             }
             if (lane == 0) a.out[(int64_t)bh * a.n_spans + j] = best;
             gbest = fmax(gbest, best);
+            top.add(best, (int32_t)j);
         }
-        publish_group_max(a, slot, bh, grp, gbest);
+        if (a.gtop)
+            publish_group_top(a, slot, tv, ti, bh, grp, top);
+        else
+            publish_group_max(a, slot, bh, grp, gbest);
     }
 }
 
@@ -882,13 +966,18 @@ hipError_t launch_typed(const Geom &g, const ScoreArgs &a, int nblocks, hipStrea
 
 int64_t score_groups(const Geom &g) { return (g.n_spans + kGroup - 1) / kGroup; }
 
+bool score_decode_path(const Geom &g) { return g.block_q == 1 && g.S > 1 && multi_heads(g) == 0; }
+
 hipError_t launch_score(const Geom &g, const void *q, const void *k, double *span_scores,
                         double *group_max, int num_cu, hipStream_t s, hipEvent_t ev_begin,
                         hipEvent_t ev_end, const uint32_t *only, double *group_second,
-                        int32_t *group_arg) {
+                        int32_t *group_arg, double *group_top, int32_t *group_top_idx) {
     if (g.n_spans == 0) return hipSuccess;
     ScoreArgs a;
     a.only = only;
+    const bool top = score_decode_path(g) && group_top && group_top_idx;
+    a.gtop = top ? group_top : nullptr;
+    a.gtopi = top ? group_top_idx : nullptr;
     a.gsec = group_second;
     a.garg = group_arg;
     a.q = q;

@@ -65,6 +65,7 @@ struct FastShared {
     uint32_t hist[kBins];
     uint32_t bitmap[kMaxGroups];
     int32_t cgrp[kMaxCandGroups];
+    int32_t cxgrp[kMaxCandGroups];      // candidate groups whose span scores are read
 };
 
 // generic path state
@@ -99,7 +100,7 @@ struct Common {
     uint32_t count;
     // candidate counters of the fast paths, cleared before a barrier that
     // comes anyway, so that no barrier is spent on clearing them
-    uint32_t cgroups, cspans;
+    uint32_t cgroups, cspans, cxgroups;
     uint32_t above;
     int32_t bstar;
     int32_t found;
@@ -1003,6 +1004,12 @@ struct TopkArgs {
     // groups with two or more spans at or above its bound
     const double *gsec;
     const int32_t *garg;
+    // null, or per group its second and third largest span scores and the
+    // spans holding its largest and second largest (decode scorer): a
+    // candidate group whose third largest is below the bound then gives its
+    // one or two candidates without its span scores being read
+    const double *gtop;
+    const int32_t *gtopi;
 };
 
 __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
@@ -1106,10 +1113,18 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         FastShared &f = u.f;
         constexpr int GPT = kMaxGroups / kThreads;         // group maxima per thread (4)
         double gr[GPT];
+        double2 g23[GPT];              // second and third largest of the group
+        int2 gij[GPT];                 // spans of the largest and second largest
+        const bool tops = ta.gtop != nullptr;
 #pragma unroll
         for (int e = 0; e < GPT; ++e) {
             const int i = tid + e * kThreads;
-            gr[e] = gm[i < m ? i : m - 1];
+            const int64_t ic = i < m ? i : m - 1;
+            gr[e] = gm[ic];
+            if (tops) {
+                g23[e] = *(const double2 *)(ta.gtop + 2 * (bh * ta.m_stride + ic));
+                gij[e] = *(const int2 *)(ta.gtopi + 2 * (bh * ta.m_stride + ic));
+            }
         }
         // 1. tau <= the kk-th largest group maximum (every span competes if
         //    kk > m): one histogram level over the group maxima finds the bin
@@ -1120,6 +1135,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         if (tid == 0) {
             cm.cgroups = 0;
             cm.cspans = 0;
+            cm.cxgroups = 0;
         }
         if (kk > m) __syncthreads();         // else ordered by block_minmax1's barrier
         if (kk <= m) {
@@ -1144,35 +1160,48 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
                 tau = bin_floor(mn, mx, cm.bstar);
             }
         }
-        // candidate groups: maximum >= tau
-        uint32_t ncg = 0;
-        for (int pass = 0;; ++pass) {
-            if (pass > 0) {
-                // (the first pass's counter was cleared before the bound)
-                if (tid == 0) cm.cgroups = 0;
-                __syncthreads();
-            }
-            // (about k appends: one LDS atomic each is cheaper than the ballots)
+        // candidate groups: maximum >= tau (about k appends: one LDS atomic
+        // each is cheaper than the ballots).  With the groups' top three, a
+        // group whose third largest score is below tau holds at most two
+        // spans at or above it, its largest and maybe its second, appended
+        // here; the others are listed in cxgrp and their span scores read
+        // below.
 #pragma unroll
-            for (int e = 0; e < GPT; ++e) {
-                const int i = tid + e * kThreads;
-                if (i < m && gr[e] >= tau) {
-                    const uint32_t slot = atomicAdd(&cm.cgroups, 1u);
-                    if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
+        for (int e = 0; e < GPT; ++e) {
+            const int i = tid + e * kThreads;
+            if (i < m && gr[e] >= tau) {
+                const uint32_t slot = atomicAdd(&cm.cgroups, 1u);
+                if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
+                if (tops) {
+                    if (g23[e].y < tau) {
+                        const bool two = g23[e].x >= tau;
+                        const uint32_t s = atomicAdd(&cm.cspans, two ? 2u : 1u);
+                        f.val[s] = gr[e];
+                        f.idx[s] = gij[e].x;
+                        if (two) {
+                            f.val[s + 1] = g23[e].x;
+                            f.idx[s + 1] = gij[e].y;
+                        }
+                    } else {
+                        const uint32_t s = atomicAdd(&cm.cxgroups, 1u);
+                        if (s < (uint32_t)kMaxCandGroups) f.cxgrp[s] = i;
+                    }
                 }
             }
-            __syncthreads();
-            ncg = cm.cgroups;
-            if (pass > 0 || ncg <= (uint32_t)kMaxCandGroups || kk > m) break;
-            // (every thread has read ncg before the clear at the loop's top:
-            // the barriers below come first)
+        }
+        __syncthreads();
+        uint32_t ncg = cm.cgroups;
+        bool split = tops;              // candidates in place but for the cxgrp groups'
+        if (ncg > (uint32_t)kMaxCandGroups && kk <= m) {
             // One histogram level left every group of the kk-th largest
             // maximum's bin above tau, more than the candidate capacity (a
             // wide bin: a few far larger maxima stretch the range).  tau
             // becomes the kk-th largest group maximum itself, ranked among
             // the groups at or above the first bound; it still bounds the
             // kk-th largest span score from below (the kk best groups each
-            // hold a span at their maximum).
+            // hold a span at their maximum).  (Every thread has read ncg
+            // before the counters are cleared again: barriers come first.)
+            split = false;
             if (tid == 0) cm.count = 0;
             __syncthreads();
 #pragma unroll
@@ -1189,12 +1218,67 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
             __syncthreads();
             find_kth(cm, f.hist, f.val, f.idx, cnt, kk);
             tau = cm.cut_v;
+            if (tid == 0) {
+                cm.cgroups = 0;
+                cm.cspans = 0;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < GPT; ++e) {
+                const int i = tid + e * kThreads;
+                if (i < m && gr[e] >= tau) {
+                    const uint32_t slot = atomicAdd(&cm.cgroups, 1u);
+                    if (slot < (uint32_t)kMaxCandGroups) f.cgrp[slot] = i;
+                }
+            }
+            __syncthreads();
+            ncg = cm.cgroups;
+        }
+        constexpr int CPT = kMaxCandGroups / (kThreads / 32);   // 16
+        const int half = tid >> 5, hl = tid & 31;
+        if (split && ncg <= (uint32_t)kMaxCandGroups) {
+            // 2'. the spans scoring >= tau of the groups listed in cxgrp
+            //     (usually none or a few); the others are in place already
+            const uint32_t ncx = cm.cxgroups;
+            if (ncx > 0) {
+                double cx[CPT];
+                int32_t cjx[CPT];
+#pragma unroll
+                for (int it = 0; it < CPT; ++it) {
+                    const uint32_t c = half + it * (kThreads / 32);
+                    cjx[it] = -1;
+                    cx[it] = -INFINITY;
+                    if (c < ncx) {
+                        const int64_t j = (int64_t)f.cxgrp[c] * kGroup + hl;
+                        if (j < n) {
+                            cjx[it] = (int32_t)j;
+                            cx[it] = sc[j];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int it = 0; it < CPT; ++it) {
+                    if (cjx[it] >= 0 && cx[it] >= tau) {
+                        const uint32_t slot = atomicAdd(&cm.cspans, 1u);
+                        f.val[slot] = cx[it];
+                        f.idx[slot] = cjx[it];
+                    }
+                }
+                __syncthreads();
+            }
+            const uint32_t count = cm.cspans;
+            if (count <= (uint32_t)kPairCap) {
+                rank_pairwise_emit(cm, f, count, kk, topk, sel);
+                return;
+            }
+            // too many candidates to rank pairwise: the full pass below
+            __syncthreads();
+            if (tid == 0) cm.cspans = 0;
+            __syncthreads();
         }
         if (ncg <= (uint32_t)kMaxCandGroups) {
             // 2. their spans with score >= tau; half a wave per group, every
             //    load issued before any is used (addresses clamped in range)
-            constexpr int CPT = kMaxCandGroups / (kThreads / 32);   // 16
-            const int half = tid >> 5, hl = tid & 31;
             double cx[CPT];
             int32_t cjx[CPT];            // span index, -1 where (group, lane) is not a span
 #pragma unroll
@@ -1352,12 +1436,15 @@ hipError_t launch_widen(const Geom &g, const int32_t *sel_tok, const int32_t *ns
 
 hipError_t launch_topk(const Geom &g, const double *span_scores, const double *group_max,
                        int32_t *sel, int32_t *n_sel, hipStream_t s, const uint32_t *only,
-                       const double *group_second, const int32_t *group_arg) {
+                       const double *group_second, const int32_t *group_arg,
+                       const double *group_top, const int32_t *group_top_idx) {
     const int nbh = g.n_blk * g.Hkv;
     TopkArgs ta;
     ta.only = only;
     ta.gsec = group_second;
     ta.garg = group_arg;
+    ta.gtop = group_top_idx ? group_top : nullptr;
+    ta.gtopi = group_top ? group_top_idx : nullptr;
     ta.scores = span_scores;
     ta.gmax = group_max;
     ta.sel = sel;
