@@ -8,7 +8,9 @@
 // pseudocode: score = query @ key[G:-L]^T).  A span's score is the maximum of
 // its token scores; a block of queries sums its queries' maxima.  Token scores
 // are never written out: only span scores leave the kernel, together with the
-// maximum of every group of 32 consecutive spans (used by the top-k step).
+// maximum of every group of 32 consecutive spans (used by the top-k step) and,
+// from the decode scorer, each group's second and third largest and the spans
+// holding its top two (so the top-k need not read most groups' spans).
 //
 // Arithmetic: the group-summed query is formed in fp64 (exact for bf16 and,
 // in practice, fp32 inputs), every product with a bf16/fp32 key element is

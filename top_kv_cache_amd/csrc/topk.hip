@@ -22,7 +22,11 @@
 //      keeps most spans, the span bound about k of them), and the spans
 //      scoring >= tau are the candidates of step 3 without step 2;
 //   2. the spans of those groups with score >= tau (all spans scoring >= tau)
-//      are loaded into LDS;
+//      are loaded into LDS; when the decode scorer also wrote each group's
+//      second and third largest scores and the spans of its top two, a
+//      candidate group whose third largest is below tau holds at most those
+//      two, taken from registers, and only the other groups' span scores
+//      are read (usually none: no second round trip to memory);
 //   3. with at most 192 of them, each one's rank among them (score desc,
 //      index asc) is its global rank: ranks < k are kept and each kept span is
 //      written at the count of kept indices below its own.  Otherwise the
