@@ -105,6 +105,7 @@ struct Common {
     // candidate counters of the fast paths, cleared before a barrier that
     // comes anyway, so that no barrier is spent on clearing them
     uint32_t cgroups, cspans, cxgroups;
+    uint32_t nkept, ndrop;              // pairwise ranking: kept / dropped candidates
     uint32_t above;
     int32_t bstar;
     int32_t found;
@@ -897,20 +898,25 @@ __device__ __forceinline__ void generic_emit(Common &cm, const double *sc, int64
 __device__ __forceinline__ void rank_pairwise_emit(Common &cm, FastShared &f, uint32_t count, int kk,
                                                    int topk, int32_t *sel) {
     const int tid = threadIdx.x;
-    // 3'. every span scoring >= tau is a candidate, so a candidate's
-    //     rank among them (score desc, index asc) is its rank among
-    //     all spans: rank every candidate pairwise, keep ranks < kk,
-    //     and place each kept span by the kept indices below it.
-    //     Both counts are split into slices of the compared range,
-    //     one thread per (entry, slice), summed through LDS.
-    if (tid == 0) cm.count = 0;
-    const uint32_t ns = count ? kThreads / count : 1;         // >= 2
+    // 3'. every span scoring >= tau is a candidate, so a candidate's rank
+    //     among them (score desc, index asc) is its rank among all spans:
+    //     rank every candidate pairwise and keep ranks < kk.  The same pass
+    //     counts the candidates of lower index, so a kept span's output
+    //     position is that count less the dropped candidates below it (or
+    //     the kept ones below it, whichever list is shorter).  The counts
+    //     are split into slices of the compared range, one thread per
+    //     (entry, slice), summed through LDS.
+    if (tid == 0) {
+        cm.nkept = 0;
+        cm.ndrop = 0;
+    }
+    const uint32_t ns = count ? kThreads / count : 1;         // >= 2 (count <= kPairCap)
     if (tid < ns * count) {
         const uint32_t c = tid % count, sl = tid / count;
         const uint32_t o0 = sl * count / ns, o1 = (sl + 1) * count / ns;
         const double x = f.val[c];
         const int32_t jc = f.idx[c];
-        uint32_t rank = 0, o = o0;
+        uint32_t rank = 0, lt = 0, o = o0;
         for (; o + 8 <= o1; o += 8) {
             double y[8];
             int32_t yi[8];
@@ -920,40 +926,51 @@ __device__ __forceinline__ void rank_pairwise_emit(Common &cm, FastShared &f, ui
                 yi[u2] = f.idx[o + u2];
             }
 #pragma unroll
-            for (int u2 = 0; u2 < 8; ++u2) rank += outranks(y[u2], yi[u2], x, jc);
+            for (int u2 = 0; u2 < 8; ++u2) {
+                rank += outranks(y[u2], yi[u2], x, jc);
+                lt += (uint32_t)(yi[u2] < jc);
+            }
         }
-        for (; o < o1; ++o) rank += outranks(f.val[o], f.idx[o], x, jc);
+        for (; o < o1; ++o) {
+            const int32_t yi = f.idx[o];
+            rank += outranks(f.val[o], yi, x, jc);
+            lt += (uint32_t)(yi < jc);
+        }
         f.hist[tid] = rank;
+        f.hist[kThreads + tid] = lt;
     }
     __syncthreads();
-    for (uint32_t c = tid; c < count; c += kThreads) {
-        uint32_t rank = 0;
-        for (uint32_t sl = 0; sl < ns; ++sl) rank += f.hist[sl * count + c];
-        if (rank < (uint32_t)kk) f.gidx[atomicAdd(&cm.count, 1u)] = f.idx[c];
+    uint32_t rank = 0, lt = 0;
+    int32_t jt = 0;
+    if ((uint32_t)tid < count) {
+        for (uint32_t sl = 0; sl < ns; ++sl) {
+            rank += f.hist[sl * count + tid];
+            lt += f.hist[kThreads + sl * count + tid];
+        }
+        jt = f.idx[tid];
+        // kept indices from the front of gidx, dropped ones from the back
+        if (rank < (uint32_t)kk)
+            f.gidx[atomicAdd(&cm.nkept, 1u)] = jt;
+        else
+            f.gidx[kMaxGroups - 1 - atomicAdd(&cm.ndrop, 1u)] = jt;
     }
     __syncthreads();
     if (sel) {
-        const uint32_t nk = (uint32_t)kk, ns2 = kThreads / nk;  // >= 2
-        if (tid < ns2 * nk) {
-            const uint32_t t = tid % nk, sl = tid / nk;
-            const uint32_t o0 = sl * nk / ns2, o1 = (sl + 1) * nk / ns2;
-            const int32_t jt = f.gidx[t];
-            uint32_t pos = 0, o = o0;
-            for (; o + 8 <= o1; o += 8) {
+        if ((uint32_t)tid < count && rank < (uint32_t)kk) {
+            const uint32_t nk = cm.nkept, nd = cm.ndrop;
+            const bool by_drop = nd <= nk;
+            const int32_t *lst = by_drop ? &f.gidx[kMaxGroups - nd] : &f.gidx[0];
+            const uint32_t nl = by_drop ? nd : nk;
+            uint32_t below = 0, o = 0;
+            for (; o + 8 <= nl; o += 8) {
                 int32_t yi[8];
 #pragma unroll
-                for (int u2 = 0; u2 < 8; ++u2) yi[u2] = f.gidx[o + u2];
+                for (int u2 = 0; u2 < 8; ++u2) yi[u2] = lst[o + u2];
 #pragma unroll
-                for (int u2 = 0; u2 < 8; ++u2) pos += yi[u2] < jt;
+                for (int u2 = 0; u2 < 8; ++u2) below += (uint32_t)(yi[u2] < jt);
             }
-            for (; o < o1; ++o) pos += f.gidx[o] < jt;
-            f.hist[tid] = pos;
-        }
-        __syncthreads();
-        for (uint32_t t = tid; t < nk; t += kThreads) {
-            uint32_t pos = 0;
-            for (uint32_t sl = 0; sl < ns2; ++sl) pos += f.hist[sl * nk + t];
-            sel[pos] = f.gidx[t];
+            for (; o < nl; ++o) below += (uint32_t)(lst[o] < jt);
+            sel[by_drop ? lt - below : below] = jt;
         }
         for (int64_t i = (int64_t)kk + tid; i < topk; i += kThreads) sel[i] = -1;
     }
