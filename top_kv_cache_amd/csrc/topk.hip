@@ -1136,7 +1136,10 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
         double gr[GPT];
         double2 g23[GPT];              // second and third largest of the group
         int2 gij[GPT];                 // spans of the largest and second largest
-        const bool tops = ta.gtop != nullptr;
+        // (with k above half the candidate-group capacity the first bound
+        // usually keeps too many groups and the second bound lists them
+        // again, so the top three are not worth loading)
+        const bool tops = ta.gtop != nullptr && kk <= kMaxCandGroups / 2;
 #pragma unroll
         for (int e = 0; e < GPT; ++e) {
             const int i = tid + e * kThreads;
@@ -1292,7 +1295,29 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkArgs ta) {
                 rank_pairwise_emit(cm, f, count, kk, topk, sel);
                 return;
             }
-            // too many candidates to rank pairwise: the full pass below
+            if (count <= (uint32_t)kMaxGroups) {
+                // 3''. the cutoff among the candidates (find_kth reorders
+                //      val / idx, so they are copied first), then a bitmap over
+                //      the spans and the ordered output
+                for (uint32_t c = tid; c < count; c += kThreads) {
+                    f.gval[c] = f.val[c];
+                    f.gidx[c] = f.idx[c];
+                }
+                for (int i = tid; i < m; i += kThreads) f.bitmap[i] = 0u;
+                __syncthreads();
+                find_kth(cm, f.hist, f.val, f.idx, count, kk);
+                const double cv = cm.cut_v;
+                const int64_t cj = cm.cut_j;
+                for (uint32_t c = tid; c < count; c += kThreads) {
+                    const double x = f.gval[c];
+                    const int32_t j = f.gidx[c];
+                    if (x > cv || (x == cv && j <= cj)) atomicOr(&f.bitmap[j >> 5], 1u << (j & 31));
+                }
+                __syncthreads();
+                emit_bitmap(cm, f, m, kk, topk, sel);
+                return;
+            }
+            // more candidates than that: the full pass below
             __syncthreads();
             if (tid == 0) cm.cspans = 0;
             __syncthreads();
