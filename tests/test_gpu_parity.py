@@ -158,7 +158,8 @@ def test_exact_ties_lower_index_wins():
 
 
 @pytest.mark.parametrize("T,S_,k", [(40000, 16, 40), (60000, 8, 300), (200000, 4, 600),
-                                    (150000, 2, 2000), (200000, 1, 600), (300000, 1, 3000)])
+                                    (150000, 2, 2000), (200000, 1, 600), (300000, 1, 3000),
+                                    (100000, 16, 100), (90000, 12, 64)])
 def test_exact_ties_many_candidates(T, S_, k):
     """Binary inputs over thousands of spans, the k-th boundary cutting a tie
     group, through each way the top-k step can go: under 192 candidates
@@ -167,7 +168,11 @@ def test_exact_ties_many_candidates(T, S_, k):
     (the generic path over global memory).  Token level (S = 1): the groups
     with one token at or above the bound are taken from the scorer's second
     largest score and the offset of the maximum, the others (two or more, or
-    a tied maximum) read token by token."""
+    a tied maximum) read token by token.  Spans with k <= 128 over more than
+    4096 spans (the last two cases): candidate groups whose third largest score
+    is below the bound give their spans from the scorer's top three, the
+    others (tied tops) are read, and with more than 192 candidates the cutoff
+    and a span bitmap give the output."""
     rng = np.random.default_rng(T + k)
     w = S(Hq=2, Hkv=2, d=64, T=T, S=S_, topk=k, L=64, needles=0)
     qn = rng.integers(0, 2, size=(1, w.Hq, w.d)).astype(np.float32)
