@@ -417,13 +417,15 @@ __global__ __launch_bounds__(kThreads) void k_fused_split(FusedArgs a) {
             }
 #pragma unroll
             for (int r = 0; r < QRM; ++r) {
-                float d = 0.f;
+                // each of the row's 16 lanes starts from the row's mask term
+                // (0, or -inf past the window), so their sum carries it
+                float d = madd;
 #pragma unroll
                 for (int p = 0; p < PPL; ++p) {
                     d = fmaf(q1[r][p], y1[p], d);
                     d = fmaf(q2[r][p], y2[p], d);
                 }
-                d = row_sum16f(d) + madd;
+                d = row_sum16f(d);
                 if (causal) {
                     const int pos = Wi - a.n_q + b * a.block_q + r / a.g;
                     if (wfi + i > pos) d = -INFINITY;
