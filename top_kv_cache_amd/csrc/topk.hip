@@ -93,8 +93,8 @@ struct LargeShared {
     int32_t idx[kCandCap];
     uint32_t hist[kBins];
     int32_t cgrp[kLGroups];
-    uint32_t wcnt[64 * kWaves];         // per (register or batch slot, wave)
-    uint32_t wpre[64 * kWaves + 1];
+    uint32_t wcnt[8 * kWaves];          // per (batch slot, wave), or per wave
+    uint32_t wpre[8 * kWaves + 1];
 };
 
 struct Common {
@@ -386,26 +386,31 @@ __device__ __forceinline__ void for_each_gmax(const double *gm, int64_t m, F f) 
 // The group maxima as steps 1-2 of the large path read them: streamed from
 // global memory (16 loads in flight per thread) each time, or, when there are
 // at most kGReg * kThreads of them, loaded once into registers as fp32 values
-// rounded up (reg[k] = gm[k * kThreads + tid] rounded toward +inf).  Rounding
-// up is monotone, so with the rounded values step 1 finds a tau_r <= the
-// rounded kk-th largest maximum, and the fp32 value just below tau_r is <= the
-// exact kk-th largest maximum: a valid bound.  Step 2 then keeps every group
-// whose rounded maximum reaches it, a superset of the groups whose exact
-// maximum does.
+// rounded up.  In registers wave w holds the contiguous chunk of kGReg * 64
+// groups from w * kGReg * 64 on, lane l of it the groups chunk + k * 64 + l
+// (k < kGReg): every load is coalesced, and ascending group order is (wave,
+// k, lane) order.  Rounding up is monotone, so with the rounded values step 1
+// finds a tau_r <= the rounded kk-th largest maximum, and the fp32 value just
+// below tau_r is <= the exact kk-th largest maximum: a valid bound.  Step 2
+// then keeps every group whose rounded maximum reaches it, a superset of the
+// groups whose exact maximum does.
 constexpr int kGReg = 64;
 template <bool kRegs> struct GmaxSource {
     const double *gm;
     int64_t m;
     float reg[kRegs ? kGReg : 1];
+    __device__ static int64_t chunk() { return (int64_t)(threadIdx.x >> 6) * (kGReg * 64); }
     __device__ void load() {
         if constexpr (kRegs) {
             constexpr int C = 16;                   // loads in flight per thread
+            const int64_t c0 = chunk() + (threadIdx.x & 63);
 #pragma unroll
             for (int k0 = 0; k0 < kGReg; k0 += C) {
+                if (chunk() + (int64_t)k0 * 64 >= m) break;   // (wave-uniform) past the end
                 double x[C];
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
-                    const int64_t i = (int64_t)(k0 + k) * kThreads + threadIdx.x;
+                    const int64_t i = c0 + (int64_t)(k0 + k) * 64;
                     x[k] = gm[i < m ? i : m - 1];
                 }
 #pragma unroll
@@ -415,9 +420,10 @@ template <bool kRegs> struct GmaxSource {
     }
     template <typename F> __device__ void each(F f) const {
         if constexpr (kRegs) {
+            const int64_t c0 = chunk() + (threadIdx.x & 63);
 #pragma unroll
             for (int k = 0; k < kGReg; ++k) {
-                const int64_t i = (int64_t)k * kThreads + threadIdx.x;
+                const int64_t i = c0 + (int64_t)k * 64;
                 // (an empty asm pins the widening to this pass; hoisted out of
                 // the passes, 64 doubles would not fit in registers)
                 float v = reg[k];
@@ -428,18 +434,13 @@ template <bool kRegs> struct GmaxSource {
             for_each_gmax(gm, m, f);
         }
     }
-    // batch bb of 8 * kThreads groups: x[e] = gm[bb * 8 * kThreads + e * kThreads + tid]
-    __device__ void batch(int64_t b0, int bb, double (&x)[8]) const {
+    // (streamed only) batch of 8 * kThreads groups from b0:
+    // x[e] = gm[b0 + e * kThreads + tid]
+    __device__ void batch(int64_t b0, double (&x)[8]) const {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            if constexpr (kRegs) {
-                float v = reg[bb * 8 + e];
-                __asm__ volatile("" : "+v"(v));
-                x[e] = (double)v;
-            } else {
-                const int64_t i = b0 + e * kThreads + threadIdx.x;
-                x[e] = gm[i < m ? i : m - 1];
-            }
+            const int64_t i = b0 + e * kThreads + threadIdx.x;
+            x[e] = gm[i < m ? i : m - 1];
         }
     }
 };
@@ -472,76 +473,46 @@ __device__ __forceinline__ uint32_t large_tau_groups(Common &cm, LargeShared &L,
     tau_out = tau;
     // 2. candidate groups (maximum >= tau) in ascending order
     if constexpr (kRegs) {
-        // the counts of every (batch slot, wave) slice first, one prefix over
-        // all of them, then the writes (two barriers instead of two per batch)
+        // each wave counts its chunk's candidates (per lane, then summed over
+        // the wave), one prefix over the kWaves counts places the
+        // chunks, then each wave writes its candidates in (k, lane) order
+        const float tf = (float)tau;          // exact: tau is an fp32 value here
+        const int64_t c0 = GmaxSource<true>::chunk() + lane;
+        uint32_t cnt = 0;
 #pragma unroll
-        for (int bb = 0; bb < kGReg / 8; ++bb) {
-            const int64_t b0 = (int64_t)bb * 8 * kThreads;
-            double x[8];
-            src.batch(b0, bb, x);
+        for (int k = 0; k < kGReg; ++k) cnt += (c0 + (int64_t)k * 64 < m && src.reg[k] >= tf) ? 1u : 0u;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t i = b0 + e * kThreads + tid;
-                const unsigned long long b = __ballot(i < m && x[e] >= tau);
-                if (lane == 0) L.wcnt[(bb * 8 + e) * kWaves + wave] = (uint32_t)__popcll(b);
-            }
-        }
+        for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+        if (lane == 0) L.wcnt[wave] = cnt;
         __syncthreads();
-        if (wave == 0) {                 // exclusive prefix over the 512 slices, 8 per lane
-            constexpr int PL = kGReg * kWaves / 64;
-            uint32_t v[PL], own = 0;
+        uint32_t off = 0, total = 0;
 #pragma unroll
-            for (int j = 0; j < PL; ++j) {
-                v[j] = L.wcnt[lane * PL + j];
-                own += v[j];
-            }
-            uint32_t incl = own;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_up(incl, o);
-                if (lane >= o) incl += y;
-            }
-            uint32_t run = incl - own;
-#pragma unroll
-            for (int j = 0; j < PL; ++j) {
-                L.wpre[lane * PL + j] = run;
-                run += v[j];
-            }
-            if (lane == 63) L.wpre[kGReg * kWaves] = incl;
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t v = L.wcnt[w];
+            off += w < wave ? v : 0u;
+            total += v;
         }
-        __syncthreads();
 #pragma unroll
-        for (int bb = 0; bb < kGReg / 8; ++bb) {
-            const int64_t b0 = (int64_t)bb * 8 * kThreads;
-            double x[8];
-            src.batch(b0, bb, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t i = b0 + e * kThreads + tid;
-                const bool keep = i < m && x[e] >= tau;
-                const unsigned long long b = __ballot(keep);
-                if (keep) {
-                    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-                        (uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-                    const uint32_t slot = L.wpre[(bb * 8 + e) * kWaves + wave] + below;
-                    if (slot < (uint32_t)kLGroups) L.cgrp[slot] = (int32_t)i;
-                }
+        for (int k = 0; k < kGReg; ++k) {
+            const int64_t i = c0 + (int64_t)k * 64;
+            const bool keep = i < m && src.reg[k] >= tf;
+            const unsigned long long bk = __ballot(keep);
+            if (keep) {
+                const uint32_t slot = off + __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(bk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bk, 0u));
+                if (slot < (uint32_t)kLGroups) L.cgrp[slot] = (int32_t)i;
             }
+            off += (uint32_t)__popcll(bk);
         }
-        const uint32_t total = L.wpre[kGReg * kWaves];
         __syncthreads();
         return total;
     }
     // per batch of 8 * kThreads groups, the count of every (e, wave) slice
     // orders the writes
     uint32_t ncg = 0;
-    constexpr int kMaxBatches = kRegs ? kGReg / 8 : 1 << 30;
-#pragma unroll kRegs ? kGReg / 8 : 1
-    for (int bb = 0; bb < kMaxBatches; ++bb) {
-        const int64_t b0 = (int64_t)bb * 8 * kThreads;
-        if (b0 >= m) break;
+    for (int64_t b0 = 0; b0 < m; b0 += 8 * kThreads) {
         double x[8];
-        src.batch(b0, bb, x);
+        src.batch(b0, x);
         unsigned long long bal[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
