@@ -100,6 +100,11 @@ SMALL = {
     # path streams the group maxima instead of holding them in registers
     "bf16_token_level_33k_groups": S(Hq=2, Hkv=1, d=64, T=1_060_000, S=1, topk=300, L=64,
                                      needles=2),
+    # token level with 32,498 groups: the group maxima held in registers, a
+    # contiguous chunk of 4096 per wave; the last wave's chunk holds 3826 (its
+    # last lanes ragged) and the last group 28 tokens
+    "bf16_token_level_32k_groups": S(Hq=2, Hkv=1, d=64, T=1_040_000, S=1, topk=300, L=64,
+                                     needles=2),
     # 65536 spans in 2048 groups, k = 256, needles stretching the score
     # range: the top-k's first bound keeps more groups than it can hold, so
     # the bound becomes the 256-th largest group maximum

@@ -267,11 +267,13 @@ __device__ __forceinline__ void find_bin(Common &cm, const uint32_t *hist, int n
 
 // The need-th best of `count` (<= kCandCap) LDS entries (val, idx) under
 // (val desc, idx asc); result in cm.cut_v / cm.cut_j.  Reorders and shrinks
-// the arrays.
+// the arrays.  With lo0 < hi0 (every value known to lie in [lo0, hi0]) the
+// first histogram level spans that range instead of a min / max pass.
 __device__ __forceinline__ void find_kth(Common &cm, uint32_t *hist, double *val, int32_t *idx,
-                         uint32_t count, int64_t need) {
+                         uint32_t count, int64_t need, double lo0 = 0.0, double hi0 = -1.0) {
     const int tid = threadIdx.x;
     bool by_index = false;
+    bool given = lo0 < hi0;
     for (;;) {
         if (count <= (uint32_t)kRankMax) {
             // pairwise ranks; 8 entries are read per step so the LDS latency
@@ -301,24 +303,37 @@ __device__ __forceinline__ void find_kth(Common &cm, uint32_t *hist, double *val
             __syncthreads();
             return;
         }
-        double mn = INFINITY, mx = -INFINITY;
-        uint32_t dummy = 0;
-        for (uint32_t c = tid; c < count; c += kThreads) {
-            const double k = by_index ? -(double)idx[c] : val[c];
-            mn = fmin(mn, k);
-            mx = fmax(mx, k);
+        double mn = lo0, mx = hi0;
+        if (!given) {
+            mn = INFINITY;
+            mx = -INFINITY;
+            uint32_t dummy = 0;
+            for (uint32_t c = tid; c < count; c += kThreads) {
+                const double k = by_index ? -(double)idx[c] : val[c];
+                mn = fmin(mn, k);
+                mx = fmax(mx, k);
+            }
+            block_minmax_count(cm, mn, mx, dummy);
+            if (mn == mx) {      // every survivor has this score: order by index
+                by_index = true;
+                continue;
+            }
         }
-        block_minmax_count(cm, mn, mx, dummy);
-        if (mn == mx) {          // every survivor has this score: order by index
-            by_index = true;
-            continue;
-        }
+        given = false;
         const double inv = (double)kBins / (mx - mn);
         for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
         __syncthreads();
-        for (uint32_t c = tid; c < count; c += kThreads) {
-            const double k = by_index ? -(double)idx[c] : val[c];
-            atomicAdd(&hist[bin_of(k, mn, inv, kBins)], 1u);
+        for (uint32_t c0 = 0; c0 < count; c0 += 4 * kThreads) {
+            double k[4];             // (4 reads issued before the atomics)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t c = c0 + e * kThreads + tid;
+                const uint32_t cc = c < count ? c : 0u;
+                k[e] = by_index ? -(double)idx[cc] : val[cc];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c0 + e * kThreads + tid < count) atomicAdd(&hist[bin_of(k[e], mn, inv, kBins)], 1u);
         }
         __syncthreads();
         find_bin(cm, hist, kBins, need);
@@ -447,7 +462,8 @@ template <bool kRegs> struct GmaxSource {
 
 template <bool kRegs>
 __device__ __forceinline__ uint32_t large_tau_groups(Common &cm, LargeShared &L, const double *gm,
-                                                     int64_t m, int kk, double &tau_out) {
+                                                     int64_t m, int kk, double &tau_out,
+                                                     double &max_out) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     GmaxSource<kRegs> src{gm, m, {}};
     src.load();
@@ -459,6 +475,7 @@ __device__ __forceinline__ uint32_t large_tau_groups(Common &cm, LargeShared &L,
         mx = fmax(mx, x);
     });
     block_minmax1(cm, mn, mx);
+    max_out = mx;
     double tau = mn;
     if (mn != mx) {
         const double inv = (double)kBins / (mx - mn);
@@ -554,9 +571,10 @@ __device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const dou
                                            const double *gm, const double *gs, const int32_t *ga,
                                            int64_t n, int64_t m, int kk, int topk, int32_t *sel) {
     const int tid = threadIdx.x, lane = tid & 63;
-    double tau;
-    const uint32_t ncg = m <= (int64_t)kGReg * kThreads ? large_tau_groups<true>(cm, L, gm, m, kk, tau)
-                                                        : large_tau_groups<false>(cm, L, gm, m, kk, tau);
+    double tau, gmx;
+    const uint32_t ncg = m <= (int64_t)kGReg * kThreads
+                             ? large_tau_groups<true>(cm, L, gm, m, kk, tau, gmx)
+                             : large_tau_groups<false>(cm, L, gm, m, kk, tau, gmx);
     if (ncg > (uint32_t)kLGroups) return false;
     if (tid == 0) {
         cm.count = 0;
@@ -682,8 +700,10 @@ __device__ __forceinline__ bool large_path(Common &cm, LargeShared &L, const dou
         rp[e] = c < count ? L.idx[c] : -1;
     }
     __syncthreads();
-    // 4. the kk-th best candidate = the cutoff
-    find_kth(cm, L.hist, L.val, L.idx, count, kk);
+    // 4. the kk-th best candidate = the cutoff (every candidate lies in
+    //    [tau, the largest group maximum]: its score is >= tau and <= its
+    //    group's maximum, rounded up or exact)
+    find_kth(cm, L.hist, L.val, L.idx, count, kk, tau, gmx);
     const double cv = cm.cut_v;
     const int64_t cj = cm.cut_j;
     // 5. one selection word per candidate group (over the candidate values,
