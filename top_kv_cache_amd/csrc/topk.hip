@@ -35,13 +35,19 @@
 //      each candidate group becomes one 32-bit word of a bitmap over the
 //      spans, and one block scan over the words writes the indices in
 //      ascending order.
-// Histogram level: 2048 equal-width bins between the candidates' min and max,
-// bin = floor((x - min) * (2048 / (max - min))) in fp64 -- monotone in x, so
-// bins are ordered; only the bin holding the k-th best survives.  Once all
-// survivors share one score the order is by index, so the level key becomes
-// the negated index.  At most 64 survivors are ranked pairwise.
-// Otherwise a generic path makes the same decisions with passes over all
-// scores in global memory.
+// More groups (token level), or more candidate groups than the fast path
+// holds: the large path takes the same steps with the group maxima held in
+// registers (up to 32,768 groups, fp32 rounded up) or streamed, up to 8192
+// candidate groups and 8192 candidate spans, the cutoff always by histogram
+// levels and the output from one selection word per candidate group.
+// Histogram level: 2048 equal-width bins between the candidates' min and max
+// (on the large path's first level: between tau and the largest group
+// maximum, which hold every candidate), bin = floor((x - min) * (2048 /
+// (max - min))) in fp64 -- monotone in x, so bins are ordered; only the bin
+// holding the k-th best survives.  Once all survivors share one score the
+// order is by index, so the level key becomes the negated index.  At most 64
+// survivors are ranked pairwise.  Otherwise a generic path makes the same
+// decisions with passes over all scores in global memory.
 #include "rea_internal.h"
 
 #include <math.h>
