@@ -3,7 +3,8 @@
   * 3B-shaped decode at 4,194,304 tokens: every KV head checked against the
     oracle (selection exact, span scores, window rows, output).
   * 8B-shaped token-level decode at 1,048,576 tokens (3840 single tokens
-    selected per KV head): every KV head checked the same way.
+    selected per KV head): every KV head checked the same way; and the
+    per-query-head and token-segment selections at the same size.
   * 8B-shaped chunked prefill (4096 queries appended at 131072, blocks of 64):
     every (block, KV head) selection and every output checked; and one
     512-query chunk at 140,000 tokens (more than 4,096 spans per block).
@@ -75,6 +76,30 @@ def test_decode_1m_token_level():
     w = dataclasses.replace(synth.config(3), S=1, topk=3840)
     w.name = f"{w.name}-token-level"
     _one_layer(3, w, needles=False)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("variant", ["per_q_head", "token_segments"])
+def test_decode_1m_selection_variants(variant):
+    """The other selection variants the bench runs at 1,048,576 tokens (8B
+    shape, one layer): one selection per query head (8 of the 32 selection
+    heads checked, one per KV head at every position in its group), and the
+    120 best tokens each widened to 32 (every KV head checked)."""
+    w = dataclasses.replace(synth.config(3), **{variant: True})
+    w.name = f"{w.name}-{variant.replace('_', '-')}"
+    log(f"[variant] {w.name}: generating + uploading")
+    q, K, V = device_inputs(w)
+    gpu = run_library(w, q, K, V)
+    del K, V
+    torch.cuda.empty_cache()
+    q64 = synth.to_f32(w.q(0), w.dtype).astype(np.float64)
+    heads = [u * w.g + u % w.g for u in range(w.Hkv)] if w.per_q_head else list(range(w.H_sel))
+    errs = []
+    for h in heads:
+        ora = oracle_head(w, 0, h, q64)
+        errs.append(compare_head(w, gpu, ora, h))
+        log(f"  selection head {h}: parity ok, out err {errs[-1]:.2e}")
+    log(f"  max-abs out err {max(errs):.3e} (tolerance {TOL[w.dtype]})")
 
 
 @pytest.mark.timeout(900)
