@@ -78,14 +78,22 @@ def test_decode_1m_token_level():
     _one_layer(3, w, needles=False)
 
 
+VARIANTS_1M = {
+    "per_q_head": dict(per_q_head=True),
+    "token_segments": dict(token_segments=True),
+    "pages_k127": dict(topk=127),
+}
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("variant", ["per_q_head", "token_segments"])
+@pytest.mark.parametrize("variant", list(VARIANTS_1M))
 def test_decode_1m_selection_variants(variant):
     """The other selection variants the bench runs at 1,048,576 tokens (8B
     shape, one layer): one selection per query head (8 of the 32 selection
-    heads checked, one per KV head at every position in its group), and the
-    120 best tokens each widened to 32 (every KV head checked)."""
-    w = dataclasses.replace(synth.config(3), **{variant: True})
+    heads checked, one per KV head at every position in its group), the 120
+    best tokens each widened to 32, and the pages' LLaMA3-8B-8K selection of
+    127 spans (window exactly 8192; every KV head checked)."""
+    w = dataclasses.replace(synth.config(3), **VARIANTS_1M[variant])
     w.name = f"{w.name}-{variant.replace('_', '-')}"
     log(f"[variant] {w.name}: generating + uploading")
     q, K, V = device_inputs(w)
