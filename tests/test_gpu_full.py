@@ -8,6 +8,8 @@
   * 8B-shaped chunked prefill (4096 queries appended at 131072, blocks of 64):
     every (block, KV head) selection and every output checked; and one
     512-query chunk at 140,000 tokens (more than 4,096 spans per block).
+  * 8B-shaped batched decode of 32 sequences at 32K tokens (equal and ragged
+    lengths) as the batched bench builds it: every sequence checked.
   * 8B-shaped decode at 1,048,576 tokens with all 32 layers resident, run
     exactly as bench.py runs it (one shared workspace, rea_decode_step per
     layer): two layers checked in full against the oracle, every layer checked
@@ -19,6 +21,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle.rea_oracle as O
 import synth
 import top_kv_cache_amd as rea
 from synth import torch_io
@@ -155,6 +158,57 @@ def test_prefill_block_at_1m_tokens():
         err = compare_head(w, gpu, ora, h)
         log(f"  head {h}: selection exact, worst |s_hat - s| / eps_j {ora['eps_used']:.3g}, "
             f"out err {err:.2e}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ragged", [False, True])
+def test_decode_batch_32x32k_as_benchmarked(ragged):
+    """The batched decode as `bench.py --batch 32 --context 32768 [--ragged]`
+    builds it (8B shape, sequence b seeded seed + 1000 b; ragged lengths spread
+    over [16384, 32768]), one layer, one rea_decode_batch: every sequence's
+    selection compared bit-exactly with the oracle run on that sequence alone,
+    and its output within tolerance."""
+    B, T = 32, 32768
+    base = synth.small(name="llama8b-bf16-decode-batch32-32k", seed=240715190, dtype="bf16",
+                       Hq=32, Hkv=8, d=128, T=T, n_q=1, block_q=1, G=32, S=32, topk=120,
+                       L=4096, needles=4, kv_scaled=True, layers=1)
+    lens = [T - (i * (T // 2)) // (B - 1) for i in range(B)] if ragged else [T] * B
+    dev = torch.device("cuda:0")
+    q = torch.empty((B, base.Hq, base.d), dtype=torch.bfloat16, device=dev)
+    K = torch.empty((B, base.Hkv, T, base.d), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    seqs = [dataclasses.replace(base, seed=base.seed + 1000 * b) for b in range(B)]
+    for b, wb in enumerate(seqs):
+        q[b] = torch_io.q_device(wb, 0, dev)[0]
+        torch_io.kv_device(wb, 0, "k", out=K[b], device=dev)
+        torch_io.kv_device(wb, 0, "v", out=V[b], device=dev)
+    lengths = torch.tensor(lens, dtype=torch.int64, device=dev)
+    db = rea.DecodeBatch(q, K, V, lengths, base.G, base.S, base.topk, base.L,
+                         rope_theta=base.rope_theta)
+    sel = torch.full((B, base.Hkv, base.topk), -7, dtype=torch.int32, device=dev)
+    nsel = torch.empty((B, base.Hkv), dtype=torch.int32, device=dev)
+    log(f"[batch] 32 x 32K ({'ragged' if ragged else 'equal'} lengths {lens[-1]}..{lens[0]})")
+    out = db.run(sel=sel, nsel=nsel)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    sel_h, nsel_h = sel.cpu().numpy(), nsel.cpu().numpy()
+
+    def f64(t):                         # the device's bf16 values, exactly
+        return t.float().cpu().numpy().astype(np.float64)
+
+    err = 0.0
+    for b in range(B):
+        Tb = lens[b]
+        qb, Kb, Vb = f64(q[b:b + 1]), f64(K[b, :, :Tb]), f64(V[b, :, :Tb])
+        ref, rsel = O.step(qb, Kb, Vb, base.G, base.S, base.topk, base.L, 1, base.rope_theta)
+        for u in range(base.Hkv):
+            ns = int(nsel_h[b, u])
+            assert ns == len(rsel[0][u]), (b, u, ns)
+            assert sel_h[b, u, :ns].tolist() == rsel[0][u], (b, u)
+        e = float(np.abs(got[b] - ref[0]).max())
+        err = max(err, e)
+        assert e <= TOL["bf16"], (b, Tb, e)
+    log(f"  32 sequences: selections exact, max-abs out err {err:.3e} (tolerance {TOL['bf16']})")
 
 
 @pytest.mark.timeout(1100)
